@@ -1,0 +1,335 @@
+"""Plain float64 reference for the MTP verify step and the end-to-end TV loss.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  One row at a time,
+NumPy float64, every quantity from its definition; no blocking, no fusion.
+
+Notation follows the pages: target distribution p (the policy), draft
+distribution q (an MTP head), gamma draft positions, vocabulary V.
+
+Readings taken where the pages leave a step open are marked READING.
+"""
+import numpy as np
+
+from .philox import verify_uniforms
+
+# Row status flags.  READING: the pages define no error handling; these name the
+# data conditions that make a row's result undefined or that change its rule.
+BAD_TOKEN = 1        # draft token outside [0, V): treated as a rejection
+BAD_TARGET = 2       # target row has no finite log-sum-exp (NaN, +inf, all -inf)
+BAD_DRAFT = 4        # same for the draft row
+RESIDUAL_EMPTY = 8   # max(0, p - q) sums to zero: the row samples from p instead
+
+
+def log_softmax(x):
+    """(log p, lse) of one logit row.
+
+    paperlayer Sec. 2 and App. A: p = softmax(target logits), q = softmax(draft
+    logits z).  lse = m + log sum_v exp(x_v - m) with m = max x.  Entries at -inf
+    give p = 0.  Returns (None, lse) when lse is not finite.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if np.isnan(x).any():
+        return None, float("nan")
+    m = x.max()
+    if not np.isfinite(m):
+        return None, float("nan")
+    lse = m + np.log(np.sum(np.exp(x - m)))
+    return x - lse, float(lse)
+
+
+def entropy(logp):
+    """H(p) = -sum_v p_v log p_v in nats, with 0 log 0 = 0.
+
+    rainbus prerequisite "Entropy" (H is the negated sum of p log p).
+    READING: natural logarithm.
+    """
+    p = np.exp(logp)
+    nz = p > 0
+    return float(-np.sum(p[nz] * logp[nz]))
+
+
+def overlap(p, q):
+    """alpha = sum_v min(p_v, q_v): the acceptance probability of rejection
+    sampling (paperlayer Sec. 3 "Rejection Sampling"; Sec. 8, alpha = 1 - d_TV)."""
+    return float(np.sum(np.minimum(p, q)))
+
+
+def tv_distance(p, q):
+    """d_TV(p, q) = 1/2 sum_v |p_v - q_v| (rainbus prerequisite "Total Variation
+    Distance")."""
+    return 0.5 * float(np.sum(np.abs(p - q)))
+
+
+def residual(p, q):
+    """r_v = max(0, p_v - q_v), the unnormalised residual distribution sampled on a
+    rejection (EntMTP page, Related Work "Speculative Decoding"; paperlayer
+    App. G.1)."""
+    return np.maximum(p - q, 0.0)
+
+
+def inverse_cdf(r, t):
+    """Smallest v (in vocabulary order) whose cumulative mass C_v = sum_{w<=v} r_w
+    exceeds t; if rounding leaves none, the last v with r_v > 0.
+
+    paperlayer App. G.1 samples the residual "by CDF inversion".  READING: the
+    cumulative sum runs in vocabulary index order and the comparison is strict,
+    so a token with r_v = 0 is never chosen.
+    Returns (token, lower boundary C_{v-1}, upper boundary C_v).
+    """
+    c = np.cumsum(r)
+    v = int(np.searchsorted(c, t, side="right"))
+    if v >= len(r):
+        pos = np.nonzero(r > 0)[0]
+        v = int(pos[-1])
+    lo = float(c[v - 1]) if v > 0 else 0.0
+    return v, lo, float(c[v])
+
+
+def accept_decision(u, logp_y, logq_y):
+    """Accept iff u < min(1, p(y)/q(y)) (paperlayer Sec. 2 "Acceptance methods",
+    App. G.1; rainbus "Rejection Sampling").
+
+    The ratio is exp(log p(y) - log q(y)); q(y) = 0 < p(y) gives +inf (accept);
+    p(y) = q(y) = 0 gives NaN, taken as a rejection.  READING: strict '<', so a
+    ratio of exactly 1 always accepts (u < 1).  Returns (flag 0/1, ratio).
+    """
+    with np.errstate(invalid="ignore", over="ignore"):
+        ratio = float(np.exp(np.float64(logp_y) - np.float64(logq_y)))
+    if np.isnan(ratio):
+        return 0, 0.0
+    return (1 if u < min(1.0, ratio) else 0), ratio
+
+
+def row_sample(p, q, u_prime, cdf_tie_band=1e-6):
+    """The token a row emits when it is the first rejection (or the bonus row).
+
+    r = max(0, p - q) when q is given, else r = p (bonus row).  READING: if the
+    residual has no mass (p = q up to rounding) the row samples from p instead.
+    t = u' * sum r; the token is inverse_cdf(r, t).
+    Returns (token, residual_was_empty, near_tie).
+    """
+    empty = False
+    if q is None:
+        r = p
+    else:
+        r = residual(p, q)
+        if not np.sum(r) > 0:
+            empty = True
+            r = p
+    total = float(np.cumsum(r)[-1])
+    t = u_prime * total
+    tok, lo, hi = inverse_cdf(r, t)
+    band = cdf_tie_band * total
+    return tok, empty, (abs(t - lo) <= band) or (abs(t - hi) <= band)
+
+
+def verify(target, draft, tokens, seed, offset, tie_band=1e-6, cdf_tie_band=1e-6):
+    """Rejection-sampling verification of gamma drafted tokens per sequence.
+
+    target: float64 [B, gamma+1, V] -- target logits at the gamma draft positions
+            plus the bonus position.
+    draft:  float64 [B, gamma, V]   -- cached draft logits (q = softmax).
+    tokens: int [B, gamma]          -- draft tokens y_k, sampled from q_k.
+    seed, offset: Philox key and counter base (see philox.verify_uniforms).
+
+    Steps (paperlayer Sec. 2 "Acceptance methods", App. G.1; rainbus
+    "Rejection Sampling"; EntMTP Related Work):
+      1. p_k = softmax(target_k), q_k = softmax(draft_k).
+      2. H(p_k) for every row, k = 0..gamma.
+      3. alpha_k = sum min(p_k, q_k); TV_k = 1/2 sum |p_k - q_k|.
+      4. u_k, u'_k from Philox at position b*(gamma+1)+k.
+      5. accept_k = u_k < min(1, p_k(y_k) / q_k(y_k)).  READING: strict '<'; the
+         decision is reported for every k, the sequence stops at the first 0.
+      6. n_b = number of leading accepts (0..gamma).
+      7. Row sample: r = max(0, p_k - q_k) for k < gamma; r = p_gamma for the
+         bonus row (READING: when all gamma are accepted the next token comes
+         from the bonus target row).  If sum r = 0, r = p_k (READING; flagged).
+         t = u'_k * sum r; token = inverse_cdf(r, t).
+      8. next_token_b = row_token[b, n_b].
+
+    Near-ties: accept_tie marks |u - min(1, ratio)| <= tie_band; token_tie marks t
+    within cdf_tie_band * sum r of either boundary of the chosen token's interval.
+    There a float32 computation may legitimately decide the other way.
+    """
+    target = np.asarray(target, dtype=np.float64)
+    draft = np.asarray(draft, dtype=np.float64)
+    tokens = np.asarray(tokens, dtype=np.int64)
+    B, G1, V = target.shape
+    G = G1 - 1
+    assert draft.shape == (B, G, V) and tokens.shape == (B, G)
+
+    pos = np.arange(B * G1, dtype=np.uint64).reshape(B, G1)
+    u, up = verify_uniforms(seed, offset, pos)
+
+    out = dict(
+        accept=np.zeros((B, G), np.uint8), accepted_len=np.zeros(B, np.int32),
+        next_token=np.full(B, -1, np.int32), row_token=np.full((B, G1), -1, np.int32),
+        overlap=np.full((B, G), np.nan), tv=np.full((B, G), np.nan),
+        entropy=np.full((B, G1), np.nan), row_status=np.zeros((B, G1), np.int32),
+        ratio=np.full((B, G), np.nan), u=u, u_prime=up,
+        accept_tie=np.zeros((B, G), bool), token_tie=np.zeros((B, G1), bool),
+        lse_p=np.full((B, G1), np.nan), lse_q=np.full((B, G), np.nan),
+    )
+    for b in range(B):
+        for k in range(G1):
+            logp, lse_p = log_softmax(target[b, k])
+            out["lse_p"][b, k] = lse_p
+            if logp is None:
+                out["row_status"][b, k] |= BAD_TARGET
+            else:
+                out["entropy"][b, k] = entropy(logp)
+            if k == G:                                   # bonus row: r = p
+                if logp is not None:
+                    tok, _, tie = row_sample(np.exp(logp), None, up[b, k], cdf_tie_band)
+                    out["row_token"][b, k] = tok
+                    out["token_tie"][b, k] = tie
+                continue
+            logq, lse_q = log_softmax(draft[b, k])
+            out["lse_q"][b, k] = lse_q
+            y = int(tokens[b, k])
+            if logq is None:
+                out["row_status"][b, k] |= BAD_DRAFT
+            if not (0 <= y < V):
+                out["row_status"][b, k] |= BAD_TOKEN
+            if logp is None or logq is None:
+                continue
+            p, q = np.exp(logp), np.exp(logq)
+            out["overlap"][b, k] = overlap(p, q)
+            out["tv"][b, k] = tv_distance(p, q)
+            if 0 <= y < V:
+                flag, ratio = accept_decision(u[b, k], logp[y], logq[y])
+                out["ratio"][b, k] = ratio
+                out["accept"][b, k] = flag
+                out["accept_tie"][b, k] = abs(u[b, k] - min(1.0, ratio)) <= tie_band
+            tok, empty, tie = row_sample(p, q, up[b, k], cdf_tie_band)
+            if empty:
+                out["row_status"][b, k] |= RESIDUAL_EMPTY
+            out["row_token"][b, k] = tok
+            out["token_tie"][b, k] = tie
+        n = 0
+        while n < G and out["accept"][b, n] == 1:
+            n += 1
+        out["accepted_len"][b] = n
+        out["next_token"][b] = out["row_token"][b, n]
+    return out
+
+
+def _head_targets(target, G):
+    """Target rows per (position, head): a [T, V] target is shared by all heads."""
+    target = np.asarray(target, dtype=np.float64)
+    if target.ndim == 2:
+        return np.broadcast_to(target[:, None, :], (target.shape[0], G, target.shape[1]))
+    return target
+
+
+def tv_stats(target, draft):
+    """Per (position t, head k): lse_p, lse_q, alpha, S.
+
+    alpha_{t,k} = clamp(sum_v min(p_v, q_v), 0, 1)   (paperlayer App. F: the
+        forward pass accumulates the overlap; READING: tau_max = 1, so the clamp
+        only guards rounding).
+    S_{t,k} = sum_v 1[q_v <= p_v] q_v              (paperlayer App. A).
+    READING: the indicator is evaluated on log-probabilities, ties count as 1.
+    target: [T, V] (shared by all heads) or [T, gamma, V]; draft: [T, gamma, V].
+    Returns float64 [T, gamma, 4].
+    """
+    draft = np.asarray(draft, dtype=np.float64)
+    T, G, V = draft.shape
+    tgt = _head_targets(target, G)
+    saved = np.empty((T, G, 4))
+    for t in range(T):
+        for k in range(G):
+            logp, lse_p = log_softmax(tgt[t, k])
+            logq, lse_q = log_softmax(draft[t, k])
+            p, q = np.exp(logp), np.exp(logq)
+            alpha = min(max(overlap(p, q), 0.0), 1.0)
+            s = float(np.sum(q[logq <= logp]))
+            saved[t, k] = (lse_p, lse_q, alpha, s)
+    return saved
+
+
+def e2e_position_loss(alpha):
+    """l_t = -sum_{k=1..gamma} prod_{j<=k} alpha_{t,j}.
+
+    paperlayer Sec. 4 "End-to-end TV loss": the loss optimises the expected
+    acceptance length, which multiplies per-step acceptances, so earlier steps
+    weigh more; rainbus "Method steps" (first step) and "Technical novelty"
+    (fourth point).  READING: no normalising constant (any would only scale it).
+    alpha: [T, gamma] -> [T].
+    """
+    alpha = np.asarray(alpha, dtype=np.float64)
+    return -np.sum(np.cumprod(alpha, axis=1), axis=1)
+
+
+def tv_loss(target, draft):
+    """Mean over positions of the end-to-end multi-step TV loss.
+
+    Returns (loss, pos_loss [T], saved [T, gamma, 4] = (lse_p, lse_q, alpha, S)).
+    READING: the loss is averaged over the T positions.
+    """
+    saved = tv_stats(target, draft)
+    pos_loss = e2e_position_loss(saved[:, :, 2])
+    return float(np.mean(pos_loss)), pos_loss, saved
+
+
+def e2e_weights(alpha, g, T):
+    """w_{t,j} = dL/d alpha_{t,j} for L = (g/T) sum_t l_t.
+
+    d l_t / d alpha_j = -sum_{k>=j} prod_{i<=k, i != j} alpha_i, written as
+    products without division so that alpha = 0 is safe.
+    """
+    alpha = np.asarray(alpha, dtype=np.float64)
+    Tn, G = alpha.shape
+    w = np.zeros((Tn, G))
+    for t in range(Tn):
+        for j in range(G):
+            acc = 0.0
+            for k in range(j, G):
+                prod = 1.0
+                for i in range(k + 1):
+                    if i != j:
+                        prod *= alpha[t, i]
+                acc += prod
+            w[t, j] = -(g / T) * acc
+    return w
+
+
+def tv_loss_grad(target, draft, g=1.0):
+    """Gradient of g * tv_loss with respect to the draft logits.
+
+    paperlayer App. A: with p detached, d alpha / d z_v = q_v (1[q_v <= p_v] - S),
+    bounded by q_v; rainbus "Technical novelty": the TV gradient is -q times
+    (indicator - S).  Chained through the end-to-end weights:
+        grad_{t,j,v} = w_{t,j} q_v (1[q_v <= p_v] - S_{t,j}).
+    The target gets no gradient.  Returns float64 [T, gamma, V] and the
+    per-element indicator-tie mask is not computed here (see indicator_margin).
+    """
+    draft = np.asarray(draft, dtype=np.float64)
+    T, G, V = draft.shape
+    tgt = _head_targets(target, G)
+    saved = tv_stats(target, draft)
+    w = e2e_weights(saved[:, :, 2], g, T)
+    grad = np.empty((T, G, V))
+    for t in range(T):
+        for k in range(G):
+            logp, _ = log_softmax(tgt[t, k])
+            logq, _ = log_softmax(draft[t, k])
+            q = np.exp(logq)
+            ind = (logq <= logp).astype(np.float64)
+            grad[t, k] = w[t, k] * q * (ind - saved[t, k, 3])
+    return grad
+
+
+def indicator_margin(target, draft):
+    """|log q_v - log p_v| per element: where it is tiny, a float32 evaluation of
+    the indicator 1[q_v <= p_v] may legitimately flip.  [T, gamma, V]."""
+    draft = np.asarray(draft, dtype=np.float64)
+    T, G, V = draft.shape
+    tgt = _head_targets(target, G)
+    m = np.empty((T, G, V))
+    for t in range(T):
+        for k in range(G):
+            logp, _ = log_softmax(tgt[t, k])
+            logq, _ = log_softmax(draft[t, k])
+            m[t, k] = np.abs(logq - logp)
+    return m
