@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Benchmark of the MTP verify + end-to-end TV-loss hot path on one MI355X.
+
+Primary number (`value`): draft positions verified per second on the rollout
+workload (64 sequences x gamma = 3 draft positions + 1 bonus row, V = 151936,
+bfloat16 logits), inputs resident in HBM, four input sets rotated (545 MB, more
+than the 256 MB Infinity Cache).  One step = one mtp_verify call: softmax of both
+rows, acceptance tests, overlap / TV / entropy, inverse-CDF samples of every row,
+accepted lengths and next tokens.
+
+Also reported (`tv_loss`): end-to-end TV loss forward + backward on T = 8192
+positions x 3 heads, V = 151936 (bf16 in, bf16 gradient out), as algorithmic GB/s
+against the 8 TB/s HBM peak.
+
+`roofline` uses per-launch HIP events recorded on the stream the kernels run on;
+`cpu_baseline` times the float64 oracle on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "draft positions verified/sec at V=151936, γ=3; TV fwd+bwd GB/s vs HBM peak"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def verify_bytes(B, G, V, elem):
+    """Algorithmic bytes of one verify call: every logit read once (target B*(G+1)
+    rows, draft B*G rows), tokens read, per-row outputs written."""
+    logits = B * (2 * G + 1) * V * elem
+    small = B * G * 4 + B * G * 1 + 2 * B * 4 + B * (G + 1) * (4 + 4 + 4) + B * G * 8
+    return logits, logits + small
+
+
+def time_verify(mtp, torch, w, steps, warmup, nsets):
+    import synthetic
+    dev = "cuda:0"
+    B, G, V = w["B"], w["G"], w["V"]
+    plans = []
+    for i in range(nsets):
+        t, d, y = synthetic.verify_inputs(w, dev, seed=w["seed"] + i)
+        plans.append(mtp.VerifyPlan(t, d, y))
+    torch.cuda.synchronize()
+    rows = B * (G + 1)
+    for i in range(warmup):
+        plans[i % nsets].run(seed=w["seed"], offset=i * rows)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        evs[i][0].record()
+        plans[i % nsets].run(seed=w["seed"], offset=(warmup + i) * rows)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [a.elapsed_time(b) for a, b in evs]
+    return wall, kernel_ms, plans
+
+
+def time_tv(mtp, torch, w, steps, warmup):
+    import synthetic
+    dev = "cuda:0"
+    t, d = synthetic.tv_inputs(w, dev)
+    plan = mtp.TVPlan(t, d, grad_dtype=torch.bfloat16)
+    for _ in range(warmup):
+        plan.forward()
+        plan.backward()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record()
+        plan.forward()
+        ev[i][1].record()
+        plan.backward()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd = [a.elapsed_time(b) for a, b, _ in ev]
+    bwd = [b.elapsed_time(c) for _, b, c in ev]
+    loss = plan.loss.item()
+    del plan, t, d
+    torch.cuda.empty_cache()
+    return wall, fwd, bwd, loss
+
+
+def cpu_baseline(torch, w, seconds):
+    """The float64 oracle, untuned, on whole sequences of the rollout workload until
+    about `seconds` of CPU time: draft positions per second on this host."""
+    import numpy as np
+
+    import synthetic
+    from oracle import mtp as omtp
+    from oracle.bf16 import bf16_bits_to_f64
+    t, d, y = synthetic.verify_inputs(w, "cuda:0", B=16)
+    tb = bf16_bits_to_f64(t.cpu().view(torch.int16).numpy().view(np.uint16))
+    db = bf16_bits_to_f64(d.cpu().view(torch.int16).numpy().view(np.uint16))
+    yb = y.cpu().numpy()
+    G1 = w["G"] + 1
+    n = 0
+    t0 = time.process_time()
+    w0 = time.perf_counter()
+    while True:
+        b = n % tb.shape[0]
+        omtp.verify(tb[b:b + 1], db[b:b + 1], yb[b:b + 1], w["seed"], b * G1)
+        n += 1
+        if time.process_time() - t0 >= seconds:
+            break
+    wall = time.perf_counter() - w0
+    return n, wall
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--tv-steps", type=int, default=None, help="TV-loss steps (default: max(3, steps // 20))")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-tv", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this hot path is data-parallel and every run here uses a "
+              "single MI355X; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synthetic
+    import tv_loss_amd as mtp
+    mtp.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+
+    w = synthetic.VERIFY_WORKLOADS["rollout"]
+    B, G, V = w["B"], w["G"], w["V"]
+    nsets = 4
+    log(f"verify: rollout workload B={B} gamma={G} V={V} bf16, {nsets} input sets")
+    wall, kms, _ = time_verify(mtp, torch, w, args.steps, args.warmup, nsets)
+    positions = B * G * args.steps
+    value = positions / wall
+    logit_bytes, alg_bytes = verify_bytes(B, G, V, 2)
+    kmean = sum(kms) / len(kms)
+    ksorted = sorted(kms)
+    achieved = alg_bytes / (kmean * 1e-3) / 1e9
+    log(f"verify: {value / 1e6:.3f} M positions/s wall, kernel mean {kmean * 1e3:.2f} us "
+        f"(median {ksorted[len(ksorted) // 2] * 1e3:.2f} us), {achieved:.0f} GB/s")
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "draft positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "rollout verify: 64 sequences x gamma=3 draft positions (+1 bonus row), "
+                               "V=151936, bf16 logits, target N(0,1)/0.7, draft = target + N(0,0.3^2)",
+                   "batch": B, "gamma": G, "vocab": V, "storage": "bf16", "input_sets": nsets},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "verify_kernel<bf16>", "bytes_per_launch": alg_bytes,
+                     "kernel_us_mean": kmean * 1e3, "kernel_us_median": ksorted[len(ksorted) // 2] * 1e3},
+    }
+
+    if not args.no_tv:
+        tw = synthetic.TV_WORKLOADS["tv_loss"]
+        T, TG, TV = tw["T"], tw["G"], tw["V"]
+        tv_steps = args.tv_steps or max(3, args.steps // 20)
+        log(f"tv loss: T={T} gamma={TG} V={TV} bf16, {tv_steps} steps")
+        twall, fwd, bwd, loss = time_tv(mtp, torch, tw, tv_steps, max(1, min(3, args.warmup)))
+        fwd_bytes = T * (1 + TG) * TV * 2
+        bwd_bytes = T * (1 + TG) * TV * 2 + T * TG * TV * 2
+        fm, bm = sum(fwd) / len(fwd), sum(bwd) / len(bwd)
+        gbs = (fwd_bytes + bwd_bytes) / ((fm + bm) * 1e-3) / 1e9
+        result["tv_loss"] = {
+            "workload": "e2e TV loss fwd+bwd: T=8192 positions x gamma=3 heads, V=151936, bf16 in, bf16 grad "
+                        "out, target N(0,1)/0.8 shared by heads, head k = target + N(0,(0.2k)^2)",
+            "value": gbs, "unit": "GB/s", "frac_of_hbm_peak": gbs / HBM_PEAK_GBS,
+            "fwd_ms": fm, "bwd_ms": bm, "fwd_gbs": fwd_bytes / (fm * 1e-3) / 1e9,
+            "bwd_gbs": bwd_bytes / (bm * 1e-3) / 1e9, "bytes_fwd": fwd_bytes, "bytes_bwd": bwd_bytes,
+            "steps": tv_steps, "wall_ms_per_step": twall / tv_steps * 1e3, "loss": loss,
+        }
+        log(f"tv loss: fwd {fm:.3f} ms ({fwd_bytes / fm / 1e6:.0f} GB/s), bwd {bm:.3f} ms "
+            f"({bwd_bytes / bm / 1e6:.0f} GB/s), total {gbs:.0f} GB/s")
+
+    if not args.no_cpu_baseline:
+        n, cwall = cpu_baseline(torch, w, args.cpu_seconds)
+        cores = 1
+        result["cpu_baseline"] = {
+            "value": n * G / cwall, "unit": "draft positions/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} rollout sequences ({n * G} draft positions, {n * (2 * G + 1)} rows of V={V}) "
+                      f"through the float64 NumPy oracle, one thread, {cwall:.1f} s; host has "
+                      f"{os.cpu_count()} CPUs",
+        }
+        log(f"cpu oracle: {n * G / cwall:.1f} positions/s on one core")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,167 @@
+/*
+ * mtp.h -- C ABI of libmtp: MTP rejection-sampling verification and the
+ * end-to-end multi-step TV loss on AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one described on the pages about "Breaking Entropy Bounds:
+ * Accelerating RL Training via MTP with Rejection Sampling" (Bebop, arXiv
+ * 2606.12370): paperlayer.ai summary Sec. 2 "Acceptance methods", Sec. 3
+ * "Rejection Sampling", Sec. 4 "End-to-end TV loss", App. A "Derivation of TV
+ * Loss Gradient", App. F "Fused TV Loss Kernel", App. G.1 "Multinomial Draft
+ * Sampling (SGLang)"; paper.rainbus.top summary, prerequisites "Rejection
+ * Sampling", "Total Variation Distance", "Entropy", and "Method steps".
+ *
+ * Conventions for every entry point:
+ *  - Pointers named as device pointers refer to GPU memory owned by the caller.
+ *    The library never allocates, frees or keeps a pointer past the call.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL is the default stream)
+ *    and the call returns without synchronising.  Faults inside kernels surface
+ *    at the caller's next synchronisation.
+ *  - Argument errors are detected before any HIP call; the call then returns a
+ *    non-zero mtp_status, writes nothing and launches nothing.  mtp_last_error()
+ *    gives a thread-local description of the last failure.
+ *  - Logit rows are contiguous in the vocabulary dimension.  Row base addresses
+ *    must be 16-byte aligned (the pointer and stride * element size multiples of
+ *    16).  V need not be a multiple of anything.
+ *  - Logits may contain -inf (masked tokens).  Rows whose log-sum-exp is not
+ *    finite (all -inf, NaN, +inf) are reported through row_status, not as a
+ *    call failure.
+ *  - Workspaces: query the size, allocate it (256-byte aligned), and zero it
+ *    once before its first use.  Each call leaves its workspace zeroed again when
+ *    it completes, so one workspace can serve any sequence of calls on one
+ *    stream.  Calls that use the same workspace concurrently race.
+ */
+#ifndef MTP_H
+#define MTP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MTP_OK = 0,
+  MTP_ERR_NULL = 1,       /* a required pointer is NULL                          */
+  MTP_ERR_SHAPE = 2,      /* a size or stride is out of range                    */
+  MTP_ERR_DTYPE = 3,      /* unknown dtype code                                  */
+  MTP_ERR_ALIGN = 4,      /* a row base address is not 16-byte aligned           */
+  MTP_ERR_WORKSPACE = 5,  /* workspace NULL, misaligned or smaller than required */
+  MTP_ERR_DEVICE = 6,     /* a HIP device query failed                           */
+  MTP_ERR_LAUNCH = 7      /* a kernel launch failed                              */
+} mtp_status;
+
+typedef enum { MTP_F32 = 0, MTP_BF16 = 1 } mtp_dtype;
+
+/* row_status bits (per verify row) */
+#define MTP_ROW_BAD_TOKEN 1       /* draft token outside [0, V): counted as a rejection    */
+#define MTP_ROW_BAD_TARGET 2      /* target row has no finite log-sum-exp                 */
+#define MTP_ROW_BAD_DRAFT 4       /* draft row has no finite log-sum-exp                  */
+#define MTP_ROW_RESIDUAL_EMPTY 8  /* max(0, p - q) has no mass: the row sampled from p    */
+
+#define MTP_MAX_GAMMA 8
+
+/* ------------------------------------------------------------------------ */
+/* Verification (paperlayer Sec. 2 "Acceptance methods", App. G.1; rainbus
+ * "Rejection Sampling"; the EntMTP page, Related Work "Speculative Decoding").
+ *
+ * For sequence b and draft position k < gamma, with p = softmax(target row
+ * (b, k)) and q = softmax(draft row (b, k)):
+ *   accept[b, k]   = u < min(1, p(y) / q(y)),  y = draft_tokens[b, k]
+ *   overlap[b, k]  = sum_v min(p_v, q_v)
+ *   tv[b, k]       = sum_v max(0, p_v - q_v)        (= 1 - overlap)
+ *   entropy[b, k]  = -sum_v p_v ln p_v,  also for the bonus row k = gamma
+ *   row_token[b,k] = inverse-CDF sample in vocabulary order of
+ *                    r = max(0, p - q)  (k < gamma)  or  r = p  (k = gamma):
+ *                    the smallest v whose running sum of r exceeds u' * sum r
+ *   accepted_len[b] = n = number of leading accepts (0..gamma)
+ *   next_token[b]   = row_token[b, n]
+ * u and u' are Philox4x32-10 outputs (words 0 and 1, each (w >> 8) * 2^-24) with
+ * key = seed and 64-bit counter = offset + b * (gamma + 1) + k.  Advance `offset`
+ * by batch * (gamma + 1) between calls for fresh uniforms.
+ *
+ * target: device, dtype, rows (b, k) at target + (b*(gamma+1) + k) * target_row_stride
+ *         elements, k = 0..gamma.
+ * draft:  device, dtype, rows (b, k) at draft + (b*gamma + k) * draft_row_stride, k < gamma.
+ * draft_tokens: device int32 [batch, gamma].
+ * Required outputs (device): accept uint8 [batch, gamma], accepted_len int32 [batch],
+ *   next_token int32 [batch].
+ * Optional outputs (device, NULL to skip): row_token int32 [batch, gamma+1],
+ *   overlap, tv float [batch, gamma], entropy float [batch, gamma+1],
+ *   row_status int32 [batch, gamma+1] (MTP_ROW_* bits).
+ * Rows with MTP_ROW_BAD_TARGET / MTP_ROW_BAD_DRAFT give NaN statistics, token -1
+ * and a rejection.  batch == 0 is a no-op.
+ * Limits: 1 <= gamma <= MTP_MAX_GAMMA, 1 <= vocab <= 2^30, strides >= vocab.
+ */
+mtp_status mtp_verify_workspace_size(int32_t batch, int32_t gamma, int32_t vocab, mtp_dtype dtype,
+                                     size_t* bytes);
+
+mtp_status mtp_verify(const void* target, int64_t target_row_stride,
+                      const void* draft, int64_t draft_row_stride, mtp_dtype dtype,
+                      int32_t batch, int32_t gamma, int32_t vocab,
+                      const int32_t* draft_tokens, uint64_t seed, uint64_t offset,
+                      uint8_t* accept, int32_t* accepted_len, int32_t* next_token,
+                      int32_t* row_token, float* overlap, float* tv, float* entropy,
+                      int32_t* row_status,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* End-to-end TV loss, forward (paperlayer Sec. 4 "End-to-end TV loss", App. F;
+ * rainbus "Method steps").  For position t and head k (1-based in the formula):
+ *   alpha_{t,k} = clamp(sum_v min(p_v, q_v), 0, 1)
+ *   S_{t,k}     = sum_v 1[q_v <= p_v] q_v
+ *   pos_loss[t] = -sum_k prod_{j<=k} alpha_{t,j}
+ *   loss[0]     = mean_t pos_loss[t]
+ * with q = softmax(draft row (t, k)) and p = softmax(target row (t, k)).
+ *
+ * Row (t, k) of draft  starts at draft  + t*draft_pos_stride  + k*draft_head_stride.
+ * Row (t, k) of target starts at target + t*target_pos_stride + k*target_head_stride;
+ * target_head_stride = 0 shares one target row across the heads of a position.
+ * Outputs (device float): loss [1] (required), pos_loss [T] (optional),
+ *   saved [T, gamma, 4] = (ln-sum-exp of p, of q, alpha, S) (required; the
+ *   backward consumes it).
+ * Limits: T >= 1, 1 <= gamma <= MTP_MAX_GAMMA, 1 <= vocab <= 2^30.
+ */
+mtp_status mtp_tv_loss_workspace_size(int32_t T, int32_t gamma, int32_t vocab, mtp_dtype dtype,
+                                      int32_t shared_target, size_t* bytes);
+
+mtp_status mtp_tv_loss_fwd(const void* target, int64_t target_pos_stride, int64_t target_head_stride,
+                           const void* draft, int64_t draft_pos_stride, int64_t draft_head_stride,
+                           mtp_dtype dtype, int32_t T, int32_t gamma, int32_t vocab,
+                           float* loss, float* pos_loss, float* saved,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* End-to-end TV loss, backward (paperlayer App. A; rainbus "Technical novelty").
+ * p is detached: only the draft logits get a gradient.
+ *   grad[t, k, v] = w_{t,k} q_v (1[q_v <= p_v] - S_{t,k}),
+ *   w_{t,k} = -(g / T) sum_{m>=k} prod_{i<=m, i!=k} alpha_{t,i},   g = grad_loss[0].
+ * The indicator is evaluated as z_v - x_v <= lnZ_q - lnZ_p on the logits, with
+ * the forward's saved statistics.  grad_dtype MTP_BF16 rounds to nearest even;
+ * MTP_F32 keeps the float32 value.
+ * saved: device float [T, gamma, 4] from mtp_tv_loss_fwd on the same inputs.
+ * grad_loss: device float [1].
+ * grad: device, grad_dtype, row (t, k) at grad + t*grad_pos_stride + k*grad_head_stride,
+ *   16-byte aligned rows.  Needs no workspace.
+ */
+mtp_status mtp_tv_loss_bwd(const void* target, int64_t target_pos_stride, int64_t target_head_stride,
+                           const void* draft, int64_t draft_pos_stride, int64_t draft_head_stride,
+                           mtp_dtype dtype, int32_t T, int32_t gamma, int32_t vocab,
+                           const float* saved, const float* grad_loss,
+                           void* grad, int64_t grad_pos_stride, int64_t grad_head_stride,
+                           mtp_dtype grad_dtype, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Error word of a workspace: non-zero if a kernel that used it hit its bounded
+ * wait limit (the cluster exchange did not complete within one second).  Copies
+ * the 32-bit word to host memory, synchronising `stream`. */
+mtp_status mtp_workspace_error(const void* workspace, uint32_t* host_word, void* stream);
+
+const char* mtp_status_string(mtp_status s);
+const char* mtp_last_error(void);
+const char* mtp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MTP_H */

@@ -106,21 +106,26 @@ def row_sample(p, q, u_prime, cdf_tie_band=1e-6):
     r = max(0, p - q) when q is given, else r = p (bonus row).  READING: if the
     residual has no mass (p = q up to rounding) the row samples from p instead.
     t = u' * sum r; the token is inverse_cdf(r, t).
-    Returns (token, residual_was_empty, near_tie).
+    Returns (token, residual_was_empty, near_tie); near_tie is also set when the
+    residual mass is below cdf_tie_band (a float32 evaluation may find it empty).
     """
     empty = False
+    near_empty = False
     if q is None:
         r = p
     else:
         r = residual(p, q)
-        if not np.sum(r) > 0:
+        mass = float(np.sum(r))
+        # a float32 sum cannot tell a residual below ~1e-6 from an empty one
+        near_empty = mass < cdf_tie_band
+        if not mass > 0:
             empty = True
             r = p
     total = float(np.cumsum(r)[-1])
     t = u_prime * total
     tok, lo, hi = inverse_cdf(r, t)
     band = cdf_tie_band * total
-    return tok, empty, (abs(t - lo) <= band) or (abs(t - hi) <= band)
+    return tok, empty, near_empty or (abs(t - lo) <= band) or (abs(t - hi) <= band)
 
 
 def verify(target, draft, tokens, seed, offset, tie_band=1e-6, cdf_tie_band=1e-6):

@@ -1,0 +1,144 @@
+"""The C ABI without a GPU: libmtp.so loads, exports every function that
+include/mtp.h declares, and rejects bad arguments before any HIP call.
+
+Every call below fails argument validation, so no kernel is launched and no
+pointer is dereferenced, with or without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tv_loss_amd
+from tv_loss_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mtp.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libmtp.so not built")
+
+P = ctypes.c_void_p
+A16 = P(0x10000)      # an aligned fake address: validation fails before it is used
+MIS = P(0x10008)      # 8-byte aligned only
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mtp_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    lib = tv_loss_amd.load()
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, f"{n} has no ctypes signature"
+    assert set(_lib.SIGNATURES) == set(names)
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    for name, val in (("MTP_ROW_BAD_TOKEN", _lib.ROW_BAD_TOKEN), ("MTP_ROW_BAD_TARGET", _lib.ROW_BAD_TARGET),
+                      ("MTP_ROW_BAD_DRAFT", _lib.ROW_BAD_DRAFT),
+                      ("MTP_ROW_RESIDUAL_EMPTY", _lib.ROW_RESIDUAL_EMPTY), ("MTP_MAX_GAMMA", _lib.MAX_GAMMA)):
+        assert re.search(rf"#define {name} {val}\b", text), name
+    assert "MTP_F32 = 0" in text and "MTP_BF16 = 1" in text
+
+
+def test_status_strings():
+    lib = tv_loss_amd.load()
+    for code, name in _lib.STATUS.items():
+        assert lib.mtp_status_string(code).decode() == name
+    assert lib.mtp_version().decode().startswith("libmtp")
+
+
+def _verify(lib, **kw):
+    a = dict(target=A16, ts=151936, draft=A16, ds=151936, dt=1, B=64, G=3, V=151936, tok=A16, seed=0, off=0,
+             acc=A16, alen=A16, nxt=A16, rtok=None, ovl=None, tv=None, ent=None, rst=None, ws=A16,
+             wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.mtp_verify(a["target"], a["ts"], a["draft"], a["ds"], a["dt"], a["B"], a["G"], a["V"], a["tok"],
+                          a["seed"], a["off"], a["acc"], a["alen"], a["nxt"], a["rtok"], a["ovl"], a["tv"],
+                          a["ent"], a["rst"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(target=None), 1), (dict(draft=None), 1), (dict(tok=None), 1), (dict(acc=None), 1),
+    (dict(alen=None), 1), (dict(nxt=None), 1),
+    (dict(G=0), 2), (dict(G=9), 2), (dict(V=0), 2), (dict(V=-5), 2), (dict(B=-1), 2),
+    (dict(ts=151935), 2), (dict(ds=100), 2),
+    (dict(dt=2), 3), (dict(dt=-1), 3),
+    (dict(target=MIS), 4), (dict(draft=MIS), 4), (dict(ts=151937, ds=151944, V=151937), 4),
+    (dict(ws=None), 5), (dict(wsb=1024), 5), (dict(ws=P(0x10010)), 5),
+])
+def test_verify_rejects_bad_arguments(kw, code):
+    lib = tv_loss_amd.load()
+    assert _verify(lib, **kw) == code, lib.mtp_last_error()
+    assert lib.mtp_last_error()
+
+
+def test_verify_empty_batch_is_a_noop():
+    lib = tv_loss_amd.load()
+    assert _verify(lib, B=0, target=None, draft=None, ws=None, wsb=0) == 0
+    n = ctypes.c_size_t(123)
+    assert lib.mtp_verify_workspace_size(0, 3, 100, 1, ctypes.byref(n)) == 0 and n.value == 0
+
+
+def test_workspace_sizes_grow_with_the_problem():
+    lib = tv_loss_amd.load()
+    n = ctypes.c_size_t()
+    sizes = []
+    for B in (1, 64, 512):
+        assert lib.mtp_verify_workspace_size(B, 3, 151936, 1, ctypes.byref(n)) == 0
+        sizes.append(n.value)
+    assert sizes == sorted(sizes) and sizes[0] > 0 and all(s % 256 == 0 for s in sizes)
+    assert lib.mtp_verify_workspace_size(64, 3, 151936, 1, None) == 1
+    assert lib.mtp_tv_loss_workspace_size(0, 3, 100, 1, 1, ctypes.byref(n)) == 2
+    assert lib.mtp_tv_loss_workspace_size(8192, 3, 151936, 1, 1, ctypes.byref(n)) == 0 and n.value > 0
+
+
+def _fwd(lib, **kw):
+    a = dict(t=A16, tp=151936, th=0, d=A16, dp=3 * 151936, dh=151936, dt=1, T=8, G=3, V=151936, loss=A16,
+             pos=None, saved=A16, ws=A16, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.mtp_tv_loss_fwd(a["t"], a["tp"], a["th"], a["d"], a["dp"], a["dh"], a["dt"], a["T"], a["G"],
+                               a["V"], a["loss"], a["pos"], a["saved"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(t=None), 1), (dict(d=None), 1), (dict(loss=None), 1), (dict(saved=None), 1),
+    (dict(T=0), 2), (dict(G=0), 2), (dict(G=9), 2), (dict(V=0), 2), (dict(tp=-1), 2),
+    (dict(dt=5), 3),
+    (dict(t=MIS), 4), (dict(dp=3 * 151936 + 1), 4),
+    (dict(ws=None), 5), (dict(wsb=256), 5),
+])
+def test_tv_fwd_rejects_bad_arguments(kw, code):
+    lib = tv_loss_amd.load()
+    assert _fwd(lib, **kw) == code, lib.mtp_last_error()
+
+
+def _bwd(lib, **kw):
+    a = dict(t=A16, tp=151936, th=0, d=A16, dp=3 * 151936, dh=151936, dt=1, T=8, G=3, V=151936, saved=A16,
+             gl=A16, g=A16, gp=3 * 151936, gh=151936, gdt=1, stream=None)
+    a.update(kw)
+    return lib.mtp_tv_loss_bwd(a["t"], a["tp"], a["th"], a["d"], a["dp"], a["dh"], a["dt"], a["T"], a["G"],
+                               a["V"], a["saved"], a["gl"], a["g"], a["gp"], a["gh"], a["gdt"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(saved=None), 1), (dict(gl=None), 1), (dict(g=None), 1), (dict(d=None), 1),
+    (dict(T=0), 2), (dict(gp=-3), 2),
+    (dict(gdt=7), 3), (dict(dt=7), 3),
+    (dict(g=MIS), 4), (dict(gh=151937), 4),
+])
+def test_tv_bwd_rejects_bad_arguments(kw, code):
+    lib = tv_loss_amd.load()
+    assert _bwd(lib, **kw) == code, lib.mtp_last_error()
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    t = torch.zeros(1, 4, 16)
+    with pytest.raises(ValueError):
+        tv_loss_amd.verify(t, t[:, :3], torch.zeros(1, 3, dtype=torch.int32), 0)

@@ -1,0 +1,193 @@
+"""GPU parity of mtp_tv_loss_fwd / mtp_tv_loss_bwd against the float64 oracle.
+
+Forward: loss, per-position loss and the saved statistics (lse_p, lse_q, alpha, S)
+within the statistic tolerances.  Backward: the bfloat16 gradient within 1 bf16
+ulp of the oracle's value rounded to nearest even (indicator near-ties excepted),
+and the float32 gradient within 1e-3 norm-relative per (position, head) row.
+Sizes: the tiny float32 workload, ragged vocabularies over several chunks, shared
+and per-head targets, and sampled positions of the full T = 8192 workload.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synthetic
+import tv_loss_amd as mtp
+from oracle import mtp as omtp
+from parity import compare_grad_bf16, stat_close, to_f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mtp.load()
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+TIE_BAND = 1e-5   # |log q - log p| below which a float32 indicator may flip
+
+
+def _tie_mass(tf, df):
+    """Per (position, head): the draft mass q of elements whose indicator is within
+    TIE_BAND of flipping.  A float32 evaluation may count them on either side, so S
+    may legitimately differ from the oracle's by up to this mass."""
+    margin = omtp.indicator_margin(tf, df)
+    q = np.exp(df - np.log(np.sum(np.exp(df - df.max(-1, keepdims=True)), -1, keepdims=True))
+               - df.max(-1, keepdims=True))
+    return margin, q, np.where(margin < TIE_BAND, q, 0.0).sum(-1)
+
+
+def _check_forward(target, draft, loss, pos, saved, dtype, positions=None):
+    tf, df = to_f64(target), to_f64(draft)
+    if positions is not None:
+        tf, df = tf[positions], df[positions]
+    ref_loss, ref_pos, ref_saved = omtp.tv_loss(tf, df)
+    _, _, tie_mass = _tie_mass(tf, df)
+    sv = saved.cpu().numpy().astype(np.float64)
+    ps = pos.cpu().numpy().astype(np.float64)
+    if positions is not None:
+        sv, ps = sv[positions], ps[positions]
+    for i, name in enumerate(("lse_p", "lse_q", "alpha", "S")):
+        d = np.abs(sv[..., i] - ref_saved[..., i])
+        if name.startswith("lse"):   # compare log-sum-exp relative to its size
+            ok = d <= 1e-6 * np.abs(ref_saved[..., i]) + 1e-5
+        elif name == "S":
+            ok = stat_close(sv[..., i], ref_saved[..., i], dtype) | (d <= tie_mass * (1 + 1e-3) + 1e-6)
+        else:
+            ok = stat_close(sv[..., i], ref_saved[..., i], dtype)
+        assert ok.all(), f"saved {name}: max err {d.max()}"
+    assert stat_close(ps, ref_pos, dtype).all(), f"pos_loss max err {np.abs(ps - ref_pos).max()}"
+    if positions is None:
+        assert stat_close(loss.cpu().numpy(), [ref_loss], dtype).all()
+    return ref_saved
+
+
+def _check_backward(target, draft, saved, g, grad_bf16, grad_f32, positions=None):
+    tf, df = to_f64(target), to_f64(draft)
+    if positions is not None:
+        tf, df = tf[positions], df[positions]
+        grad_bf16, grad_f32 = grad_bf16[positions], grad_f32[positions]
+    # The oracle's gradient for the sampled positions, scaled as in the full mean.
+    T_full = saved.shape[0]
+    gs = g * tf.shape[0] / T_full
+    ref = omtp.tv_loss_grad(tf, df, gs)
+    margin, q, tie_mass = _tie_mass(tf, df)
+    _, _, ref_saved = omtp.tv_loss(tf, df)
+    w = omtp.e2e_weights(ref_saved[:, :, 2], gs, tf.shape[0])
+    # a shift of S by up to the tie mass moves every element by up to |w| q tie_mass
+    slack = np.abs(w)[..., None] * q * tie_mass[..., None] * 1.01
+    gb = to_f64(grad_bf16)
+    ties = compare_grad_bf16(grad_bf16, ref, np.where(np.abs(gb - ref) <= slack, 0.0, margin), TIE_BAND)
+    gf = grad_f32.cpu().numpy().astype(np.float64)
+    err = np.where(margin < TIE_BAND, 0.0, np.maximum(np.abs(gf - ref) - slack, 0.0))
+    den = np.linalg.norm(np.where(margin < TIE_BAND, 0.0, ref), axis=-1)
+    rel = np.linalg.norm(err, axis=-1) / np.maximum(den, 1e-30)
+    assert (rel <= 1e-3).all(), f"float32 gradient rel err {rel.max()}"
+    return ties
+
+
+def _run(target, draft, g=1.0):
+    loss, pos, saved = mtp.tv_loss_fwd(target, draft)
+    gl = torch.tensor([g], dtype=torch.float32, device=DEV)
+    gb = mtp.tv_loss_bwd(target, draft, saved, gl, grad_dtype=torch.bfloat16)
+    gf = mtp.tv_loss_bwd(target, draft, saved, gl, grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    return loss, pos, saved, gb, gf
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_tiny_float32(seed):
+    w = synthetic.TV_WORKLOADS["tiny"]
+    t, d = synthetic.tv_inputs(w, DEV, seed=seed)
+    _say("tiny tv seed", seed)
+    loss, pos, saved, gb, gf = _run(t, d, g=1.0 + 0.1 * seed)
+    _check_forward(t, d, loss, pos, saved, torch.float32)
+    _check_backward(t, d, saved, 1.0 + 0.1 * seed, gb, gf)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("shared", [True, False])
+@pytest.mark.parametrize("T,G,V", [(1, 1, 7), (5, 3, 1000), (3, 4, 8200), (17, 3, 50003), (2, 8, 20000),
+                                   (4, 2, 1)])
+def test_ragged(T, G, V, shared, dtype):
+    w = dict(T=T, G=G, V=V, dtype=dtype, scale=1.2, sigma=0.3, shared=shared, seed=3)
+    t, d = synthetic.tv_inputs(w, DEV, seed=T * 100 + V)
+    pad = (-V) % 8
+    if pad:
+        tp = torch.zeros(t.shape[:-1] + (V + pad,), dtype=dtype, device=DEV)
+        dp = torch.zeros(d.shape[:-1] + (V + pad,), dtype=dtype, device=DEV)
+        tp[..., :V] = t
+        dp[..., :V] = d
+        t, d = tp[..., :V], dp[..., :V]
+    _say("tv ragged", T, G, V, shared, dtype)
+    loss, pos, saved = mtp.tv_loss_fwd(t, d)
+    gl = torch.tensor([0.7], dtype=torch.float32, device=DEV)
+    gpad = torch.zeros((T, G, V + pad), dtype=torch.bfloat16, device=DEV)
+    gfpad = torch.zeros((T, G, V + pad), dtype=torch.float32, device=DEV)
+    gb = mtp.tv_loss_bwd(t, d, saved, gl, out=gpad[..., :V])
+    gf = mtp.tv_loss_bwd(t, d, saved, gl, out=gfpad[..., :V])
+    torch.cuda.synchronize()
+    _check_forward(t, d, loss, pos, saved, dtype)
+    _check_backward(t, d, saved, 0.7, gb, gf)
+    if pad:   # nothing written past the vocabulary
+        assert (gpad[..., V:] == 0).all() and (gfpad[..., V:] == 0).all()
+
+
+def test_full_workload_sampled_positions():
+    w = synthetic.TV_WORKLOADS["tv_loss"]
+    t, d = synthetic.tv_inputs(w, DEV)
+    _say("tv full workload")
+    loss, pos, saved, gb, gf = _run(t, d, g=1.0)
+    positions = [0, 1, 2, 1000, 4095, 4096, 8190, 8191]
+    ref_saved = _check_forward(t, d, loss, pos, saved, torch.bfloat16, positions)
+    ties = _check_backward(t, d, saved, 1.0, gb, gf, positions)
+    # the mean over all positions is the mean of the per-position losses
+    p = pos.double()
+    assert abs(loss.item() - p.mean().item()) <= 1e-6 * abs(p.mean().item()) + 1e-7
+    _say("alpha per head:", ref_saved[:, :, 2].mean(0), "indicator ties:", ties)
+
+
+def test_identical_heads_give_zero_gradient():
+    V, T, G = 30000, 3, 3
+    g = torch.Generator(device=DEV).manual_seed(5)
+    t = torch.randn((T, V), generator=g, device=DEV).to(torch.bfloat16)
+    d = t[:, None, :].expand(T, G, V).contiguous()
+    loss, pos, saved, gb, gf = _run(t, d)
+    assert torch.allclose(saved[:, :, 2], torch.ones_like(saved[:, :, 2]), atol=1e-3)
+    assert abs(loss.item() + G) < 3e-3
+    # every indicator is 1 and S = sum q, so the gradient is q (1 - S) ~ 1e-7 q
+    qmax = gf.abs().max().item()
+    assert qmax < 1e-5, qmax
+
+
+def test_autograd_function_matches_explicit_backward():
+    w = synthetic.TV_WORKLOADS["tiny"]
+    t, d = synthetic.tv_inputs(w, DEV, seed=9)
+    z = d.clone().requires_grad_(True)
+    loss = mtp.tv_loss(z, t)
+    (2.5 * loss).backward()
+    _, _, saved = mtp.tv_loss_fwd(t, d)
+    ref = mtp.tv_loss_bwd(t, d, saved, torch.tensor([2.5], device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(z.grad, ref)
+
+
+def test_forward_is_deterministic_and_reuses_workspace():
+    w = synthetic.TV_WORKLOADS["tv_loss"]
+    t, d = synthetic.tv_inputs(w, DEV, T=256)
+    small = synthetic.tv_inputs(dict(w, shared=False), DEV, T=5, V=5000)
+    a = mtp.tv_loss_fwd(t, d)
+    for _ in range(5):
+        mtp.tv_loss_fwd(*small)
+        b = mtp.tv_loss_fwd(t, d)
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
+    torch.cuda.synchronize()
+    assert mtp.workspace_error(mtp.workspace(DEV, 1)) == 0

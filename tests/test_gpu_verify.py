@@ -1,0 +1,218 @@
+"""GPU parity of mtp_verify against the float64 oracle, on identical seeded inputs.
+
+Sizes: the tiny float32 workload; ragged vocabularies spanning several 8192-element
+chunks with a partial last vector; the full rollout workload (64 x 4 rows of
+151936, every row checked); sampled sequences of the long-tail workload (512 x 5
+rows of 262144) and of all 15 entropy-sweep cells; edge cases; determinism and
+workspace reuse; and a chi-square test of the emitted token against p.
+"""
+import numpy as np
+import pytest
+import torch
+from scipy import stats
+
+import synthetic
+import tv_loss_amd as mtp
+from oracle import mtp as omtp
+from parity import compare_verify, oracle_verify, to_f64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mtp.load()
+
+
+def _run(target, draft, tokens, seed, offset):
+    out = mtp.verify(target, draft, tokens, seed, offset)
+    torch.cuda.synchronize()
+    return out
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_tiny_float32(seed):
+    w = synthetic.VERIFY_WORKLOADS["tiny"]
+    t, d, y = synthetic.verify_inputs(w, DEV, seed=seed)
+    _say("tiny seed", seed)
+    out = _run(t, d, y, seed=1000 + seed, offset=7 * seed)
+    ref = oracle_verify(t, d, y, 1000 + seed, 7 * seed)
+    compare_verify(out, ref, torch.float32)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("V,G,B", [(1, 1, 3), (7, 2, 2), (8, 3, 2), (1000, 3, 3), (8191, 1, 2), (8193, 3, 2),
+                                   (50003, 3, 3), (70000, 8, 2)])
+def test_ragged_vocab(V, G, B, dtype):
+    """Vocabulary sizes around vector and chunk boundaries; padded row strides."""
+    w = dict(B=B, G=G, V=V, dtype=dtype, kind="normal", scale=1.5, sigma=0.4, seed=11)
+    t, d, y = synthetic.verify_inputs(w, DEV, seed=V + G)
+    pad = (-V) % 8
+    if pad:   # rows must start 16-byte aligned: pad the vocabulary dimension
+        tp = torch.full((B, G + 1, V + pad), float("-inf"), dtype=dtype, device=DEV)
+        dp = torch.full((B, G, V + pad), float("-inf"), dtype=dtype, device=DEV)
+        tp[..., :V] = t
+        dp[..., :V] = d
+        t, d = tp[..., :V], dp[..., :V]
+    _say("ragged", V, G, B, dtype)
+    out = _run(t, d, y, seed=5, offset=123)
+    ref = oracle_verify(t, d, y, 5, 123)
+    compare_verify(out, ref, dtype)
+
+
+def test_rollout_full():
+    w = synthetic.VERIFY_WORKLOADS["rollout"]
+    t, d, y = synthetic.verify_inputs(w, DEV)
+    _say("rollout full")
+    out = _run(t, d, y, seed=2, offset=0)
+    ref = oracle_verify(t, d, y, 2, 0)
+    ties = compare_verify(out, ref, torch.bfloat16)
+    _say("rollout ties (accept, token):", ties, "mean overlap", ref["overlap"].mean())
+
+
+def test_long_tail_sampled():
+    w = synthetic.VERIFY_WORKLOADS["long_tail"]
+    t, d, y = synthetic.verify_inputs(w, DEV)
+    _say("long tail")
+    out = _run(t, d, y, seed=5, offset=0)
+    G1 = w["G"] + 1
+    rows = [0, 1, 2, 3, 255, 256, 400, 511]
+    for b in rows:
+        ref = oracle_verify(t[b:b + 1], d[b:b + 1], y[b:b + 1], 5, b * G1)
+        compare_verify(out, ref, torch.bfloat16, rows=[b])
+    # whole-batch properties
+    rt = out["row_token"].cpu().numpy()
+    assert rt.min() >= 0 and rt.max() < w["V"]
+    ov, tv = out["overlap"].cpu().numpy(), out["tv"].cpu().numpy()
+    np.testing.assert_allclose(ov + tv, 1.0, atol=2e-3)
+    assert (out["row_status"].cpu().numpy() == 0).all()
+
+
+@pytest.mark.parametrize("i_tau", range(5))
+@pytest.mark.parametrize("i_sigma", range(3))
+def test_entropy_sweep_cell(i_tau, i_sigma):
+    w = synthetic.sweep_cell(i_tau, i_sigma)
+    t, d, y = synthetic.verify_inputs(w, DEV)
+    seed = w["seed"]
+    _say("sweep cell", i_tau, i_sigma)
+    out = _run(t, d, y, seed=seed, offset=0)
+    G1 = w["G"] + 1
+    for b in (0, 37, 127):
+        ref = oracle_verify(t[b:b + 1], d[b:b + 1], y[b:b + 1], seed, b * G1)
+        compare_verify(out, ref, torch.bfloat16, rows=[b])
+    _say(f"tau={synthetic.SWEEP_TAUS[i_tau]} sigma={synthetic.SWEEP_SIGMAS[i_sigma]}: "
+         f"accept {out['accept'].float().mean().item():.4f}, mean n {out['accepted_len'].float().mean().item():.3f}, "
+         f"H {out['entropy'].mean().item():.3f}")
+
+
+def test_identical_rows_accept_everything():
+    w = synthetic.VERIFY_WORKLOADS["rollout"]
+    t, _, _ = synthetic.verify_inputs(w, DEV, B=8)
+    d = t[:, :3].clone()
+    y = synthetic.gumbel_tokens(d, torch.Generator(device=DEV).manual_seed(3))
+    out = _run(t, d, y, seed=4, offset=0)
+    assert out["accept"].all() and (out["accepted_len"] == 3).all()
+    assert (out["tv"] == 0).all()                       # same bytes -> same p, q bits
+    assert torch.allclose(out["overlap"], torch.ones_like(out["overlap"]), atol=1e-3)
+    assert (out["row_status"][:, :3] == mtp.ROW_RESIDUAL_EMPTY).all()
+    assert torch.equal(out["next_token"], out["row_token"][:, 3])
+    ref = oracle_verify(t, d, y, 4, 0)
+    compare_verify(out, ref, torch.bfloat16)
+
+
+def test_disjoint_supports_reject_everything():
+    B, G, V = 4, 3, 20000
+    g = torch.Generator(device=DEV).manual_seed(9)
+    t = torch.randn((B, G + 1, V), generator=g, device=DEV).to(torch.bfloat16)
+    d = torch.randn((B, G, V), generator=g, device=DEV).to(torch.bfloat16)
+    t[:, :, 0::2] = float("-inf")
+    d[:, :, 1::2] = float("-inf")
+    y = synthetic.gumbel_tokens(d, g)
+    out = _run(t, d, y, seed=1, offset=0)
+    assert not out["accept"].any() and (out["accepted_len"] == 0).all()
+    assert (out["overlap"] == 0).all()
+    assert torch.allclose(out["tv"], torch.ones_like(out["tv"]), atol=1e-3)
+    assert (out["next_token"] % 2 == 1).all()
+    compare_verify(out, oracle_verify(t, d, y, 1, 0), torch.bfloat16)
+
+
+def test_bad_rows_and_tokens():
+    w = dict(B=4, G=3, V=9000, dtype=torch.bfloat16, kind="normal", scale=1.0, sigma=0.3, seed=1)
+    t, d, y = synthetic.verify_inputs(w, DEV)
+    y[0, 1] = -1
+    y[1, 0] = 9000
+    t[2, 2, :] = float("-inf")
+    d[3, 0, 17] = float("nan")
+    out = _run(t, d, y, seed=8, offset=0)
+    st = out["row_status"].cpu().numpy()
+    assert st[0, 1] & mtp.ROW_BAD_TOKEN and out["accept"][0, 1] == 0
+    assert st[1, 0] & mtp.ROW_BAD_TOKEN and out["accepted_len"][1] == 0
+    assert st[2, 2] & mtp.ROW_BAD_TARGET and out["row_token"][2, 2] == -1
+    assert torch.isnan(out["entropy"][2, 2]) and torch.isnan(out["overlap"][2, 2])
+    assert st[3, 0] & mtp.ROW_BAD_DRAFT and out["accept"][3, 0] == 0 and out["row_token"][3, 0] == -1
+    compare_verify(out, oracle_verify(t, d, y, 8, 0), torch.bfloat16)
+
+
+def test_empty_batch():
+    t = torch.zeros((0, 4, 64), dtype=torch.bfloat16, device=DEV)
+    out = mtp.verify(t, t[:, :3], torch.zeros((0, 3), dtype=torch.int32, device=DEV), 0)
+    assert out["accepted_len"].numel() == 0
+
+
+def test_deterministic_and_workspace_reuse():
+    w = synthetic.VERIFY_WORKLOADS["rollout"]
+    t, d, y = synthetic.verify_inputs(w, DEV, B=16)
+    small = synthetic.verify_inputs(dict(w, B=3, V=9000), DEV)
+    first = _run(t, d, y, seed=3, offset=0)
+    for i in range(10):
+        # alternate shapes on the same workspace; every call must leave it clean
+        s_out = _run(*small, seed=1, offset=i)
+        again = _run(t, d, y, seed=3, offset=0)
+        for k in first:
+            assert torch.equal(torch.nan_to_num(first[k].float()), torch.nan_to_num(again[k].float())), k
+    ws = mtp.workspace(DEV, 1)
+    assert mtp.workspace_error(ws) == 0
+    compare_verify(s_out, oracle_verify(*small, 1, 9), torch.bfloat16)
+
+
+def test_offset_addresses_the_uniform_stream():
+    """Sequence b alone at offset + b*(gamma+1) reproduces its results in the batch."""
+    w = synthetic.VERIFY_WORKLOADS["rollout"]
+    t, d, y = synthetic.verify_inputs(w, DEV, B=6, V=30000)
+    full = _run(t, d, y, seed=77, offset=1000)
+    for b in range(6):
+        one = _run(t[b:b + 1], d[b:b + 1], y[b:b + 1], seed=77, offset=1000 + 4 * b)
+        for k in ("accept", "row_token", "accepted_len", "next_token"):
+            assert torch.equal(one[k][0], full[k][b]), (b, k)
+
+
+def test_chi_square_first_token_is_p():
+    """Rejection sampling emits tokens distributed as p (paperlayer Sec. 2): over
+    200000 sequences with fresh uniforms, the first emitted token against p."""
+    V, B = 16, 200000
+    g = torch.Generator(device=DEV).manual_seed(21)
+    base_t = 1.5 * torch.randn((1, 2, V), generator=g, device=DEV)
+    base_d = base_t[:, :1] + 0.9 * torch.randn((1, 1, V), generator=g, device=DEV)
+    t = base_t.expand(B, 2, V).contiguous()
+    d = base_d.expand(B, 1, V).contiguous()
+    y = synthetic.gumbel_tokens(d, g)
+    out = _run(t, d, y, seed=2024, offset=0)
+    first = torch.where(out["accept"][:, 0] == 1, y[:, 0], out["row_token"][:, 0])
+    counts = torch.bincount(first.long(), minlength=V).cpu().numpy()
+    p = np.exp(omtp.log_softmax(to_f64(base_t[0, 0]))[0])
+    assert stats.chisquare(counts, p * B).pvalue > 1e-4
+    q = np.exp(omtp.log_softmax(to_f64(base_d[0, 0]))[0])
+    alpha = omtp.overlap(p, q)
+    rate = out["accept"].float().mean().item()
+    assert abs(rate - alpha) < 5 * np.sqrt(alpha * (1 - alpha) / B)
+    # and every sample equals the oracle's on a slice
+    ref = oracle_verify(t[:2000], d[:2000], y[:2000], 2024, 0)
+    compare_verify({k: v[:2000] for k, v in out.items()}, ref, torch.float32)

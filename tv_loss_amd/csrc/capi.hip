@@ -1,0 +1,324 @@
+// C ABI of libmtp: argument validation, workspace layout, launch.
+//
+// Every argument check runs before the first HIP call, so a rejected call touches
+// neither the device nor any output.  The only global state is a per-device cache
+// of the compute-unit count and kernel occupancies, filled under a mutex.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
+
+#include "mtp.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+mtp_status fail(mtp_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+mtp_status ok() {
+  g_err[0] = 0;
+  return MTP_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int elem_bytes(mtp_dtype dt) { return dt == MTP_BF16 ? 2 : 4; }
+int per_vec(mtp_dtype dt) { return dt == MTP_BF16 ? 8 : 4; }
+
+constexpr int64_t kMaxVocab = int64_t(1) << 30;
+
+mtp_status check_common(mtp_dtype dt, int32_t gamma, int32_t vocab) {
+  if (dt != MTP_F32 && dt != MTP_BF16) return fail(MTP_ERR_DTYPE, "unknown dtype code %d", (int)dt);
+  if (gamma < 1 || gamma > MTP_MAX_GAMMA)
+    return fail(MTP_ERR_SHAPE, "gamma = %d outside [1, %d]", gamma, MTP_MAX_GAMMA);
+  if (vocab < 1 || vocab > kMaxVocab) return fail(MTP_ERR_SHAPE, "vocab = %d outside [1, 2^30]", vocab);
+  return MTP_OK;
+}
+
+mtp_status check_row_base(const void* p, int64_t stride_elems, mtp_dtype dt, const char* what) {
+  if (!aligned16(p)) return fail(MTP_ERR_ALIGN, "%s pointer is not 16-byte aligned", what);
+  if ((stride_elems * elem_bytes(dt)) % 16 != 0)
+    return fail(MTP_ERR_ALIGN, "%s stride of %lld elements is not a multiple of 16 bytes", what,
+                (long long)stride_elems);
+  return MTP_OK;
+}
+
+// ---- per-device limits --------------------------------------------------------
+struct DeviceInfo {
+  int cus = 0;
+  std::map<std::tuple<int, int, int, int>, int> occ;   // (kernel, dt, G, shared) -> blocks per CU
+};
+std::mutex g_dev_mu;
+std::map<int, DeviceInfo> g_dev;
+
+// Workgroups one XCD can hold for the given kernel (the cluster of a group must
+// fit, with margin, so that its members are co-resident).
+mtp_status cluster_capacity(int kernel, int dt, int G, int shared, int64_t* per_xcd) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(MTP_ERR_DEVICE, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DeviceInfo& info = g_dev[dev];
+  if (info.cus == 0) {
+    if (hipDeviceGetAttribute(&info.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return fail(MTP_ERR_DEVICE, "cannot query the compute-unit count");
+  }
+  const auto key = std::make_tuple(kernel, dt, G, shared);
+  auto it = info.occ.find(key);
+  if (it == info.occ.end()) {
+    int n = 0;
+    hipError_t e = kernel == 0 ? mtp::verify_occupancy(dt, &n) : mtp::tv_fwd_occupancy(dt, G, shared != 0, &n);
+    if (e != hipSuccess || n < 1) return fail(MTP_ERR_DEVICE, "occupancy query failed");
+    it = info.occ.emplace(key, n).first;
+  }
+  *per_xcd = (int64_t)it->second * info.cus / 8;
+  return MTP_OK;
+}
+
+// ---- workspace layouts --------------------------------------------------------
+struct VerifyLayout {
+  size_t err, grp, seq, part1, part2, rec, total;
+  mtp::RowSplit sp;
+  int64_t ngroups;
+};
+
+VerifyLayout verify_layout(int32_t B, int32_t G, int32_t V, mtp_dtype dt) {
+  VerifyLayout L{};
+  L.sp = mtp::make_split(V, per_vec(dt), mtp::verify_vec_per_thread(dt));
+  L.ngroups = (int64_t)B * (G + 1);
+  const int64_t C = L.sp.nchunks;
+  size_t off = 0;
+  L.err = off; off = align256(off + 4);
+  L.grp = off; off = align256(off + (size_t)L.ngroups * mtp::kCounterStride * 4);
+  L.seq = off; off = align256(off + (size_t)B * mtp::kCounterStride * 4);
+  L.part1 = off; off = align256(off + (size_t)L.ngroups * C * 8 * 4);
+  L.part2 = off; off = align256(off + (size_t)L.ngroups * C * 2 * 4);
+  L.rec = off; off = align256(off + (size_t)L.ngroups * 2 * 4);
+  L.total = off;
+  return L;
+}
+
+struct TvLayout {
+  size_t err, grp, glob, part1, part2, pos, total;
+  mtp::RowSplit sp;
+};
+
+TvLayout tv_layout(int32_t T, int32_t G, int32_t V, mtp_dtype dt, bool shared) {
+  TvLayout L{};
+  L.sp = mtp::make_split(V, per_vec(dt), mtp::tv_fwd_vec_per_thread(dt, G, shared));
+  const int64_t C = L.sp.nchunks;
+  size_t off = 0;
+  L.err = off; off = align256(off + 4);
+  L.grp = off; off = align256(off + (size_t)T * mtp::kCounterStride * 4);
+  L.glob = off; off = align256(off + 4);
+  L.part1 = off; off = align256(off + (size_t)T * C * mtp::tv_fwd_part1_stride(G, shared) * 4);
+  L.part2 = off; off = align256(off + (size_t)T * C * 2 * G * 4);
+  L.pos = off; off = align256(off + (size_t)T * 4);
+  L.total = off;
+  return L;
+}
+
+template <typename T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + off);
+}
+
+mtp_status check_workspace(void* ws, size_t have, size_t need) {
+  if (need == 0) return MTP_OK;
+  if (!ws) return fail(MTP_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (((uintptr_t)ws & 255u) != 0) return fail(MTP_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (have < need) return fail(MTP_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", have, need);
+  return MTP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mtp_status_string(mtp_status s) {
+  switch (s) {
+    case MTP_OK: return "MTP_OK";
+    case MTP_ERR_NULL: return "MTP_ERR_NULL";
+    case MTP_ERR_SHAPE: return "MTP_ERR_SHAPE";
+    case MTP_ERR_DTYPE: return "MTP_ERR_DTYPE";
+    case MTP_ERR_ALIGN: return "MTP_ERR_ALIGN";
+    case MTP_ERR_WORKSPACE: return "MTP_ERR_WORKSPACE";
+    case MTP_ERR_DEVICE: return "MTP_ERR_DEVICE";
+    case MTP_ERR_LAUNCH: return "MTP_ERR_LAUNCH";
+  }
+  return "MTP_ERR_UNKNOWN";
+}
+
+const char* mtp_last_error(void) { return g_err; }
+
+const char* mtp_version(void) { return "libmtp 0.1 (gfx950)"; }
+
+mtp_status mtp_verify_workspace_size(int32_t batch, int32_t gamma, int32_t vocab, mtp_dtype dtype,
+                                     size_t* bytes) {
+  if (!bytes) return fail(MTP_ERR_NULL, "bytes is NULL");
+  mtp_status s = check_common(dtype, gamma, vocab);
+  if (s) return s;
+  if (batch < 0) return fail(MTP_ERR_SHAPE, "batch = %d is negative", batch);
+  *bytes = batch == 0 ? 0 : verify_layout(batch, gamma, vocab, dtype).total;
+  return ok();
+}
+
+mtp_status mtp_verify(const void* target, int64_t target_row_stride, const void* draft,
+                      int64_t draft_row_stride, mtp_dtype dtype, int32_t batch, int32_t gamma,
+                      int32_t vocab, const int32_t* draft_tokens, uint64_t seed, uint64_t offset,
+                      uint8_t* accept, int32_t* accepted_len, int32_t* next_token, int32_t* row_token,
+                      float* overlap, float* tv, float* entropy, int32_t* row_status, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  mtp_status s = check_common(dtype, gamma, vocab);
+  if (s) return s;
+  if (batch < 0) return fail(MTP_ERR_SHAPE, "batch = %d is negative", batch);
+  if (batch == 0) return ok();
+  if (!target || !draft || !draft_tokens || !accept || !accepted_len || !next_token)
+    return fail(MTP_ERR_NULL, "a required pointer (target, draft, draft_tokens, accept, accepted_len, "
+                              "next_token) is NULL");
+  if (target_row_stride < vocab || draft_row_stride < vocab)
+    return fail(MTP_ERR_SHAPE, "row strides (%lld, %lld) must be >= vocab (%d)", (long long)target_row_stride,
+                (long long)draft_row_stride, vocab);
+  if ((s = check_row_base(target, target_row_stride, dtype, "target"))) return s;
+  if ((s = check_row_base(draft, draft_row_stride, dtype, "draft"))) return s;
+  const VerifyLayout L = verify_layout(batch, gamma, vocab, dtype);
+  if ((s = check_workspace(workspace, workspace_bytes, L.total))) return s;
+  const int64_t grid = (L.ngroups + 7) / 8 * 8 * (int64_t)L.sp.nchunks;
+  if (grid > 0x7fffffffLL) return fail(MTP_ERR_SHAPE, "batch * (gamma + 1) * chunks is too large");
+
+  // ---- device-dependent checks ---------------------------------------------
+  int64_t per_xcd = 0;
+  if ((s = cluster_capacity(0, dtype, 0, 0, &per_xcd))) return s;
+  if (2 * (int64_t)L.sp.nchunks > per_xcd)
+    return fail(MTP_ERR_SHAPE, "vocab %d needs %d co-resident workgroups per row; one XCD holds %lld", vocab,
+                L.sp.nchunks, (long long)per_xcd);
+
+  mtp::VerifyArgs a{};
+  a.target = target; a.t_stride = target_row_stride;
+  a.draft = draft; a.d_stride = draft_row_stride;
+  a.tokens = draft_tokens;
+  a.B = batch; a.G = gamma; a.V = vocab;
+  a.seed = seed; a.offset = offset;
+  a.accept = accept; a.accepted_len = accepted_len; a.next_token = next_token;
+  a.row_token = row_token; a.overlap = overlap; a.tv = tv; a.entropy = entropy; a.row_status = row_status;
+  a.err = at<uint32_t>(workspace, L.err);
+  a.grp_cnt = at<int>(workspace, L.grp);
+  a.seq_cnt = at<int>(workspace, L.seq);
+  a.part1 = at<float>(workspace, L.part1);
+  a.part2 = at<float>(workspace, L.part2);
+  a.rec = at<int>(workspace, L.rec);
+  a.sp = L.sp;
+  a.ngroups = (int)L.ngroups;
+  hipError_t e = mtp::launch_verify(a, dtype, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MTP_ERR_LAUNCH, "verify launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+mtp_status mtp_tv_loss_workspace_size(int32_t T, int32_t gamma, int32_t vocab, mtp_dtype dtype,
+                                      int32_t shared_target, size_t* bytes) {
+  if (!bytes) return fail(MTP_ERR_NULL, "bytes is NULL");
+  mtp_status s = check_common(dtype, gamma, vocab);
+  if (s) return s;
+  if (T < 1) return fail(MTP_ERR_SHAPE, "T = %d must be >= 1", T);
+  *bytes = tv_layout(T, gamma, vocab, dtype, shared_target != 0).total;
+  return ok();
+}
+
+static mtp_status check_tv_inputs(const void* target, int64_t tp, int64_t th, const void* draft, int64_t dp,
+                                  int64_t dh, mtp_dtype dtype, int32_t T, int32_t gamma, int32_t vocab) {
+  mtp_status s = check_common(dtype, gamma, vocab);
+  if (s) return s;
+  if (T < 1) return fail(MTP_ERR_SHAPE, "T = %d must be >= 1", T);
+  if (!target || !draft) return fail(MTP_ERR_NULL, "target or draft is NULL");
+  if (tp < 0 || th < 0 || dp < 0 || dh < 0) return fail(MTP_ERR_SHAPE, "negative stride");
+  if ((s = check_row_base(target, tp, dtype, "target position"))) return s;
+  if ((s = check_row_base(target, th, dtype, "target head"))) return s;
+  if ((s = check_row_base(draft, dp, dtype, "draft position"))) return s;
+  if ((s = check_row_base(draft, dh, dtype, "draft head"))) return s;
+  return MTP_OK;
+}
+
+mtp_status mtp_tv_loss_fwd(const void* target, int64_t target_pos_stride, int64_t target_head_stride,
+                           const void* draft, int64_t draft_pos_stride, int64_t draft_head_stride,
+                           mtp_dtype dtype, int32_t T, int32_t gamma, int32_t vocab, float* loss,
+                           float* pos_loss, float* saved, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  mtp_status s = check_tv_inputs(target, target_pos_stride, target_head_stride, draft, draft_pos_stride,
+                                 draft_head_stride, dtype, T, gamma, vocab);
+  if (s) return s;
+  if (!loss || !saved) return fail(MTP_ERR_NULL, "loss or saved is NULL");
+  const bool shared = target_head_stride == 0;
+  const TvLayout L = tv_layout(T, gamma, vocab, dtype, shared);
+  if ((s = check_workspace(workspace, workspace_bytes, L.total))) return s;
+  const int64_t grid = (int64_t)(T + 7) / 8 * 8 * L.sp.nchunks;
+  if (grid > 0x7fffffffLL) return fail(MTP_ERR_SHAPE, "T * chunks is too large");
+  int64_t per_xcd = 0;
+  if ((s = cluster_capacity(1, dtype, gamma, shared, &per_xcd))) return s;
+  if (2 * (int64_t)L.sp.nchunks > per_xcd)
+    return fail(MTP_ERR_SHAPE, "vocab %d needs %d co-resident workgroups per position; one XCD holds %lld",
+                vocab, L.sp.nchunks, (long long)per_xcd);
+  mtp::TvArgs a{};
+  a.target = target; a.t_pos = target_pos_stride; a.t_head = target_head_stride;
+  a.draft = draft; a.d_pos = draft_pos_stride; a.d_head = draft_head_stride;
+  a.T = T; a.G = gamma; a.V = vocab;
+  a.loss = loss; a.pos_loss = pos_loss; a.saved = saved;
+  a.err = at<uint32_t>(workspace, L.err);
+  a.grp_cnt = at<int>(workspace, L.grp);
+  a.glob_cnt = at<int>(workspace, L.glob);
+  a.part1 = at<float>(workspace, L.part1);
+  a.part2 = at<float>(workspace, L.part2);
+  a.pos_ws = at<float>(workspace, L.pos);
+  a.sp = L.sp;
+  hipError_t e = mtp::launch_tv_fwd(a, dtype, shared, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MTP_ERR_LAUNCH, "TV forward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+mtp_status mtp_tv_loss_bwd(const void* target, int64_t target_pos_stride, int64_t target_head_stride,
+                           const void* draft, int64_t draft_pos_stride, int64_t draft_head_stride,
+                           mtp_dtype dtype, int32_t T, int32_t gamma, int32_t vocab, const float* saved,
+                           const float* grad_loss, void* grad, int64_t grad_pos_stride,
+                           int64_t grad_head_stride, mtp_dtype grad_dtype, void* stream) {
+  mtp_status s = check_tv_inputs(target, target_pos_stride, target_head_stride, draft, draft_pos_stride,
+                                 draft_head_stride, dtype, T, gamma, vocab);
+  if (s) return s;
+  if (grad_dtype != MTP_F32 && grad_dtype != MTP_BF16)
+    return fail(MTP_ERR_DTYPE, "unknown grad dtype code %d", (int)grad_dtype);
+  if (!saved || !grad_loss || !grad) return fail(MTP_ERR_NULL, "saved, grad_loss or grad is NULL");
+  if (grad_pos_stride < 0 || grad_head_stride < 0) return fail(MTP_ERR_SHAPE, "negative grad stride");
+  if ((s = check_row_base(grad, grad_pos_stride, grad_dtype, "grad position"))) return s;
+  if ((s = check_row_base(grad, grad_head_stride, grad_dtype, "grad head"))) return s;
+  const bool shared = target_head_stride == 0;
+  mtp::TvArgs a{};
+  a.target = target; a.t_pos = target_pos_stride; a.t_head = target_head_stride;
+  a.draft = draft; a.d_pos = draft_pos_stride; a.d_head = draft_head_stride;
+  a.T = T; a.G = gamma; a.V = vocab;
+  a.saved_in = saved; a.grad_loss = grad_loss;
+  a.grad = grad; a.g_pos = grad_pos_stride; a.g_head = grad_head_stride; a.grad_dt = grad_dtype;
+  a.sp = mtp::make_split(vocab, per_vec(dtype), mtp::tv_bwd_vec_per_thread(dtype));
+  if ((int64_t)T * a.sp.nchunks > 0x7fffffffLL) return fail(MTP_ERR_SHAPE, "T * chunks is too large");
+  hipError_t e = mtp::launch_tv_bwd(a, dtype, shared, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MTP_ERR_LAUNCH, "TV backward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+mtp_status mtp_workspace_error(const void* workspace, uint32_t* host_word, void* stream) {
+  if (!workspace || !host_word) return fail(MTP_ERR_NULL, "workspace or host_word is NULL");
+  hipStream_t st = (hipStream_t)stream;
+  if (hipMemcpyAsync(host_word, workspace, 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return fail(MTP_ERR_DEVICE, "cannot read the workspace error word");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,320 @@
+// Device building blocks shared by the verify and TV-loss kernels (gfx950, wave64).
+//
+//  * 16-byte row streaming with bf16 -> fp32 unpacking (a bf16 is the top half of
+//    a binary32, so widening is a shift or a mask);
+//  * the online log-sum-exp partial (reference, sum, entropy moment) and its
+//    order-independent merge;
+//  * wave butterflies and 256-thread block reductions that leave every lane with
+//    bitwise-identical results (so every workgroup of a cluster derives the
+//    same row statistics from the same partials);
+//  * the cluster exchange: publish / arrive / bounded wait at agent scope;
+//  * Philox4x32-10 (Salmon et al., SC'11) for the verify uniforms.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mtp {
+
+constexpr int kBlock = 256;           // threads per workgroup: 4 wave64s
+constexpr int kWaves = kBlock / 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// dtype codes (match the C ABI)
+constexpr int kF32 = 0;
+constexpr int kBF16 = 1;
+
+template <int DT> struct Elem;
+template <> struct Elem<kF32> { static constexpr int kPerVec = 4; static constexpr int kBytes = 4; };
+template <> struct Elem<kBF16> { static constexpr int kPerVec = 8; static constexpr int kBytes = 2; };
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Geometry of one row split into `nchunks` chunks of whole 16-byte vectors.
+struct RowSplit {
+  int64_t nvec;        // vectors covering the row (the last may be partial)
+  int64_t nvec_full;   // vectors lying entirely inside the row
+  int64_t vec_per_chunk;
+  int nchunks;
+};
+
+__host__ __device__ inline RowSplit make_split(int64_t V, int per_vec, int vec_per_thread) {
+  RowSplit s;
+  s.nvec = (V + per_vec - 1) / per_vec;
+  s.nvec_full = V / per_vec;
+  const int64_t cap = (int64_t)kBlock * vec_per_thread;
+  s.nchunks = (int)((s.nvec + cap - 1) / cap);
+  s.vec_per_chunk = (s.nvec + s.nchunks - 1) / s.nchunks;
+  return s;
+}
+
+// Load this thread's NV vectors of one row chunk as floats.  Element (j, e) of the
+// thread is vocabulary index (vbeg + j*kBlock + tid) * PV + e.  Elements outside
+// the chunk or the row read as -inf.  Only whole vectors are read with 16-byte
+// loads; the row's partial last vector is read element by element.
+template <int DT, int NV>
+__device__ __forceinline__ void load_chunk(const void* __restrict__ row, int64_t vbeg, int64_t vend,
+                                           const RowSplit& sp, int64_t V,
+                                           float (&x)[NV * Elem<DT>::kPerVec]) {
+  constexpr int PV = Elem<DT>::kPerVec;
+  const int tid = threadIdx.x;
+  u32x4 raw[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int64_t vi = vbeg + (int64_t)j * kBlock + tid;
+    if (vi < vend && vi < sp.nvec_full) {
+      raw[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row) + vi);
+    } else {
+      raw[j] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int64_t vi = vbeg + (int64_t)j * kBlock + tid;
+    const bool full = vi < vend && vi < sp.nvec_full;
+    if constexpr (DT == kBF16) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        x[j * PV + 2 * w] = full ? bf16_lo(raw[j][w]) : kNegInf;
+        x[j * PV + 2 * w + 1] = full ? bf16_hi(raw[j][w]) : kNegInf;
+      }
+    } else {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) x[j * PV + w] = full ? __uint_as_float(raw[j][w]) : kNegInf;
+    }
+    if (!full && vi < vend) {   // the row's partial last vector
+#pragma unroll
+      for (int e = 0; e < PV; ++e) {
+        const int64_t idx = vi * PV + e;
+        if (idx < V) {
+          if constexpr (DT == kBF16) {
+            const uint16_t h = reinterpret_cast<const uint16_t*>(row)[idx];
+            x[j * PV + e] = __uint_as_float((uint32_t)h << 16);
+          } else {
+            x[j * PV + e] = reinterpret_cast<const float*>(row)[idx];
+          }
+        }
+      }
+    }
+  }
+}
+
+// Scalar load of one logit.
+template <int DT>
+__device__ __forceinline__ float load_one(const void* row, int64_t idx) {
+  if constexpr (DT == kBF16) {
+    return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(row)[idx] << 16);
+  } else {
+    return reinterpret_cast<const float*>(row)[idx];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Log-sum-exp partials.  A partial over a set of logits a_i, in base-2 units:
+//   ref = m * log2(e) rounded once (m = max a_i; -inf for an empty set),
+//   z   = sum_i 2^(a_i log2 e - ref),
+//   y   = sum_i 2^(a_i log2 e - ref) * (a_i log2 e - ref)   (entropy moment).
+// Then lse = (ref + log2 z) ln 2 and H = ln 2 (log2 z - y / z).
+struct Lse {
+  float ref, z, y;
+};
+
+__device__ __forceinline__ Lse lse_empty() { return Lse{kNegInf, 0.f, 0.f}; }
+
+// Merge two partials.  NaN anywhere gives NaN; an empty partial (z = 0) is the
+// identity.  Non-empty operands are put in a canonical order first, so the result
+// does not depend on which side each came from (bitwise), whatever the compiler
+// contracts into FMAs.
+__device__ __forceinline__ Lse lse_merge(Lse a, Lse b) {
+  if (a.z != a.z || b.z != b.z || a.ref != a.ref || b.ref != b.ref || a.y != a.y || b.y != b.y) {
+    const float nan = __builtin_nanf("");
+    return Lse{nan, nan, nan};
+  }
+  if (!(a.z > 0.f)) return (b.z > 0.f) ? b : lse_empty();
+  if (!(b.z > 0.f)) return a;
+  const bool swap = (b.ref > a.ref) || (b.ref == a.ref && (b.z > a.z || (b.z == a.z && b.y > a.y)));
+  if (swap) { Lse t = a; a = b; b = t; }
+  const float d = b.ref - a.ref;        // <= 0
+  const float f = fast_exp2(d);
+  const float z = a.z + b.z * f;
+  const float y = a.y + (b.y + d * b.z) * f;
+  return Lse{a.ref, z, y};
+}
+
+__device__ __forceinline__ float lse_log2(const Lse& s) { return s.ref + fast_log2(s.z); }
+
+// ---------------------------------------------------------------------------
+// Wave64 butterflies: every lane ends with the same bits.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ Lse wave_lse(Lse s) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    Lse t{__shfl_xor(s.ref, o, 64), __shfl_xor(s.z, o, 64), __shfl_xor(s.y, o, 64)};
+    s = lse_merge(s, t);
+  }
+  return s;
+}
+
+// Block (256-thread) reductions through LDS; results identical in every thread.
+// `scratch` holds at least kWaves * N floats.  Ends with a barrier-free read, so
+// callers must not reuse `scratch` before the next __syncthreads().
+template <int N>
+__device__ __forceinline__ void block_sum(float (&v)[N], float* scratch) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = wave_sum(v[i]);
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) scratch[i * kWaves + wave] = v[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float* s = scratch + i * kWaves;
+    v[i] = (s[0] + s[1]) + (s[2] + s[3]);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void block_lse(Lse (&v)[N], float* scratch) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = wave_lse(v[i]);
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      scratch[(i * kWaves + wave) * 3 + 0] = v[i].ref;
+      scratch[(i * kWaves + wave) * 3 + 1] = v[i].z;
+      scratch[(i * kWaves + wave) * 3 + 2] = v[i].y;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float* s = scratch + i * kWaves * 3;
+    Lse w0{s[0], s[1], s[2]}, w1{s[3], s[4], s[5]}, w2{s[6], s[7], s[8]}, w3{s[9], s[10], s[11]};
+    v[i] = lse_merge(lse_merge(w0, w1), lse_merge(w2, w3));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Cluster exchange.  Data shared between workgroups of one launch goes through
+// device-coherent accesses (relaxed agent-scope atomics: sc1 loads and stores on
+// gfx950), so no L2 writeback or invalidation is needed: a publisher writes its
+// partials with coherent stores, waits for them to complete (s_waitcnt), then
+// increments the cluster counter; a consumer polls the counter with coherent
+// loads and then reads the partials with coherent loads.  Waits are bounded by the
+// 100 MHz real-time counter so that no wave can spin forever; a timeout is
+// reported through `err` and the caller carries on.
+constexpr uint64_t kSpinLimitTicks = 100000000ull;   // 1 s
+constexpr uint32_t kErrSyncTimeout = 1u;
+
+__device__ __forceinline__ void st_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coherent(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_coherent(const int* p) {
+  return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait for this wave's outstanding memory operations (the coherent stores that
+// precede an arrival) to complete.  The signal fences keep the compiler from
+// moving memory operations across the wait.
+__device__ __forceinline__ void wait_stores() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Arrive on a counter after this thread's coherent stores; returns the old value.
+__device__ __forceinline__ int arrive(int* counter) {
+  wait_stores();
+  const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  return old;
+}
+
+// Thread 0 waits until *counter >= target; then the whole block is released.
+// Must be called by every thread of the block.
+__device__ __forceinline__ void block_wait(int* counter, int target, uint32_t* err) {
+  if (threadIdx.x == 0) {
+    if (ld_coherent(counter) < target) {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (ld_coherent(counter) < target) {
+        __builtin_amdgcn_s_sleep(2);
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimitTicks) {
+          __hip_atomic_fetch_or(err, kErrSyncTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+      }
+    }
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+}
+
+__device__ __forceinline__ void reset_counter(int* counter) { st_coherent(counter, 0); }
+
+// Zero n floats of workspace with the whole block (coherent stores).
+__device__ __forceinline__ void block_zero(float* p, int64_t n) {
+  for (int64_t i = threadIdx.x; i < n; i += kBlock) st_coherent(p + i, 0.f);
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10: ten rounds of the Philox S-box on four 32-bit words with a
+// two-word key advanced by the Weyl increments between rounds.
+struct P4 { uint32_t x[4]; };
+
+__device__ __forceinline__ P4 philox4x32_10(P4 c, uint32_t k0, uint32_t k1) {
+  constexpr uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+  constexpr uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) { k0 += W0; k1 += W1; }
+    const uint32_t lo0 = M0 * c.x[0], hi0 = __umulhi(M0, c.x[0]);
+    const uint32_t lo1 = M1 * c.x[2], hi1 = __umulhi(M1, c.x[2]);
+    P4 n;
+    n.x[0] = hi1 ^ c.x[1] ^ k0;
+    n.x[1] = lo1;
+    n.x[2] = hi0 ^ c.x[3] ^ k1;
+    n.x[3] = lo0;
+    c = n;
+  }
+  return c;
+}
+
+// The two verify uniforms of a row: counter = offset + position (64-bit, words 0-1),
+// key = seed; u from word 0, u' from word 1, each (w >> 8) * 2^-24.
+__device__ __forceinline__ void row_uniforms(uint64_t seed, uint64_t offset, uint64_t position,
+                                             float* u, float* u_prime) {
+  const uint64_t c = offset + position;
+  P4 in{{(uint32_t)c, (uint32_t)(c >> 32), 0u, 0u}};
+  P4 o = philox4x32_10(in, (uint32_t)seed, (uint32_t)(seed >> 32));
+  *u = (float)(o.x[0] >> 8) * 0x1p-24f;
+  *u_prime = (float)(o.x[1] >> 8) * 0x1p-24f;
+}
+
+}  // namespace mtp

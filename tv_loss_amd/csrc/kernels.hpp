@@ -1,0 +1,72 @@
+// Internal interface between the C ABI layer and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.hpp"
+
+namespace mtp {
+
+// Vectors of 16 bytes each thread keeps per row: verify keeps a target and a
+// draft chunk in registers (64 floats per thread either way).
+constexpr int kVerifyNVBf16 = 4;   // 32 bf16 per row per thread, 8192-element chunks
+constexpr int kVerifyNVF32 = 8;    // 32 fp32 per row per thread, 8192-element chunks
+
+// Counters sit 16 ints (64 bytes) apart so clusters do not share a line.
+constexpr int kCounterStride = 16;
+
+// Row status bits (same values as the public header's MTP_ROW_*).
+constexpr int kRowBadToken = 1;
+constexpr int kRowBadTarget = 2;
+constexpr int kRowBadDraft = 4;
+constexpr int kRowResidualEmpty = 8;
+
+struct VerifyArgs {
+  const void* target; int64_t t_stride;   // row (b, k) of [B, G+1, V] at (b*(G+1)+k)*t_stride
+  const void* draft;  int64_t d_stride;   // row (b, k) of [B, G, V]   at (b*G+k)*d_stride
+  const int32_t* tokens;                  // [B, G]
+  int B, G;
+  int64_t V;
+  uint64_t seed, offset;
+  uint8_t* accept; int32_t* accepted_len; int32_t* next_token;
+  int32_t* row_token; float* overlap; float* tv; float* entropy; int32_t* row_status;
+  // workspace sections
+  uint32_t* err; int* grp_cnt; int* seq_cnt; float* part1; float* part2; int* rec;
+  RowSplit sp;
+  int ngroups;
+};
+
+int verify_vec_per_thread(int dt);
+hipError_t launch_verify(const VerifyArgs& a, int dt, hipStream_t stream);
+hipError_t verify_occupancy(int dt, int* blocks_per_cu);
+
+// ---------------------------------------------------------------------------
+// End-to-end TV loss.  Head k of position t compares draft row
+// draft + t*d_pos + k*d_head with target row target + t*t_pos + k*t_head
+// (t_head = 0: one target row shared by all heads).
+struct TvArgs {
+  const void* target; int64_t t_pos, t_head;
+  const void* draft;  int64_t d_pos, d_head;
+  int T, G;
+  int64_t V;
+  // forward outputs
+  float* loss; float* pos_loss; float* saved;
+  // backward
+  const float* saved_in; const float* grad_loss;
+  void* grad; int64_t g_pos, g_head; int grad_dt;
+  // forward workspace
+  uint32_t* err; int* grp_cnt; int* glob_cnt; float* part1; float* part2; float* pos_ws;
+  RowSplit sp;
+};
+
+constexpr int kTvSavedStride = 4;   // saved[t, k, :] = (lse_p, lse_q, alpha, S)
+constexpr int kTvMaxHeads = 8;
+
+int tv_fwd_vec_per_thread(int dt, int G, bool shared);
+int tv_fwd_part1_stride(int G, bool shared);
+hipError_t launch_tv_fwd(const TvArgs& a, int dt, bool shared, hipStream_t stream);
+hipError_t tv_fwd_occupancy(int dt, int G, bool shared, int* blocks_per_cu);
+int tv_bwd_vec_per_thread(int dt);
+hipError_t launch_tv_bwd(const TvArgs& a, int dt, bool shared, hipStream_t stream);
+
+}  // namespace mtp

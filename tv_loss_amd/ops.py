@@ -1,0 +1,274 @@
+"""PyTorch-facing wrappers over the libmtp C ABI.
+
+Every computation runs in the HIP kernels behind include/mtp.h; this module only
+checks tensor layouts, allocates outputs with torch, passes pointers and the
+current stream, and caches one zero-initialised workspace per (device, stream).
+There is no CPU fallback: without libmtp.so or a GPU these functions raise.
+"""
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import MtpError, check, load
+
+_DTYPES = {torch.float32: _lib.MTP_F32, torch.bfloat16: _lib.MTP_BF16}
+_workspaces = {}
+
+
+def _dtype_code(t):
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}") from None
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def workspace(device, nbytes):
+    """A zero-filled workspace of at least nbytes for the current stream of device.
+    The kernels leave it zeroed after each call, so it is reused as is."""
+    device = torch.device(device)
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on a GPU")
+
+
+def verify(target, draft, draft_tokens, seed, offset=0, *, stats=True):
+    """Rejection-sampling verification (see mtp_verify in include/mtp.h).
+
+    target: [B, gamma+1, V], draft: [B, gamma, V] (float32 or bfloat16, same dtype,
+    unit stride along V, uniform row stride); draft_tokens: int32 [B, gamma].
+    Returns a dict of tensors: accept (uint8 [B, gamma]), accepted_len, next_token
+    (int32 [B]) and, with stats, row_token, row_status (int32 [B, gamma+1]),
+    overlap, tv (float [B, gamma]) and entropy (float [B, gamma+1]).
+    """
+    lib = load()
+    _require_cuda(target, draft, draft_tokens)
+    if target.dim() != 3 or draft.dim() != 3:
+        raise ValueError("target must be [B, gamma+1, V] and draft [B, gamma, V]")
+    B, G1, V = target.shape
+    G = G1 - 1
+    if tuple(draft.shape) != (B, G, V) or draft.dtype != target.dtype:
+        raise ValueError("draft must match target: [B, gamma, V], same dtype")
+    for name, t, rows in (("target", target, G1), ("draft", draft, G)):
+        if t.stride(2) != 1 or (B > 1 and t.stride(0) != rows * t.stride(1)):
+            raise ValueError(f"{name} needs unit stride along V and a uniform row stride")
+    if draft_tokens.dtype != torch.int32 or tuple(draft_tokens.shape) != (B, G):
+        raise ValueError("draft_tokens must be int32 [B, gamma]")
+    draft_tokens = draft_tokens.contiguous()
+    dev = target.device
+    dt = _dtype_code(target)
+    out = {
+        "accept": torch.empty((B, G), dtype=torch.uint8, device=dev),
+        "accepted_len": torch.empty(B, dtype=torch.int32, device=dev),
+        "next_token": torch.empty(B, dtype=torch.int32, device=dev),
+    }
+    if stats:
+        out.update(row_token=torch.empty((B, G1), dtype=torch.int32, device=dev),
+                   row_status=torch.empty((B, G1), dtype=torch.int32, device=dev),
+                   overlap=torch.empty((B, G), dtype=torch.float32, device=dev),
+                   tv=torch.empty((B, G), dtype=torch.float32, device=dev),
+                   entropy=torch.empty((B, G1), dtype=torch.float32, device=dev))
+    if B == 0:
+        return out
+    nbytes = ctypes.c_size_t()
+    check(lib.mtp_verify_workspace_size(B, G, V, dt, ctypes.byref(nbytes)))
+    ws = workspace(dev, nbytes.value)
+    with torch.cuda.device(dev):
+        check(lib.mtp_verify(
+            _ptr(target), target.stride(1), _ptr(draft), draft.stride(1), dt, B, G, V,
+            _ptr(draft_tokens), ctypes.c_uint64(seed), ctypes.c_uint64(offset),
+            _ptr(out["accept"]), _ptr(out["accepted_len"]), _ptr(out["next_token"]),
+            _ptr(out.get("row_token")), _ptr(out.get("overlap")), _ptr(out.get("tv")),
+            _ptr(out.get("entropy")), _ptr(out.get("row_status")),
+            _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+def _tv_layout(target, draft):
+    if draft.dim() != 3:
+        raise ValueError("draft must be [T, gamma, V]")
+    T, G, V = draft.shape
+    if target.dim() == 2:
+        if tuple(target.shape) != (T, V):
+            raise ValueError("a shared target must be [T, V]")
+        t_pos, t_head = target.stride(0), 0
+        if target.stride(1) != 1:
+            raise ValueError("target needs unit stride along V")
+    elif target.dim() == 3:
+        if tuple(target.shape) != (T, G, V):
+            raise ValueError("a per-head target must be [T, gamma, V]")
+        t_pos, t_head = target.stride(0), target.stride(1)
+        if target.stride(2) != 1:
+            raise ValueError("target needs unit stride along V")
+        if t_head == 0:
+            raise ValueError("a per-head target with head stride 0: pass the [T, V] row instead")
+    else:
+        raise ValueError("target must be [T, V] or [T, gamma, V]")
+    if draft.stride(2) != 1:
+        raise ValueError("draft needs unit stride along V")
+    if draft.dtype != target.dtype:
+        raise ValueError("target and draft must share a dtype")
+    return T, G, V, t_pos, t_head
+
+
+def tv_loss_fwd(target, draft):
+    """End-to-end TV loss forward (mtp_tv_loss_fwd).  target: [T, V] shared by the
+    heads or [T, gamma, V]; draft: [T, gamma, V].  Returns (loss [1], pos_loss [T],
+    saved [T, gamma, 4])."""
+    lib = load()
+    _require_cuda(target, draft)
+    T, G, V, t_pos, t_head = _tv_layout(target, draft)
+    dev = draft.device
+    dt = _dtype_code(draft)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    pos_loss = torch.empty(T, dtype=torch.float32, device=dev)
+    saved = torch.empty((T, G, 4), dtype=torch.float32, device=dev)
+    nbytes = ctypes.c_size_t()
+    check(lib.mtp_tv_loss_workspace_size(T, G, V, dt, int(t_head == 0), ctypes.byref(nbytes)))
+    ws = workspace(dev, nbytes.value)
+    with torch.cuda.device(dev):
+        check(lib.mtp_tv_loss_fwd(_ptr(target), t_pos, t_head, _ptr(draft), draft.stride(0), draft.stride(1),
+                                  dt, T, G, V, _ptr(loss), _ptr(pos_loss), _ptr(saved),
+                                  _ptr(ws), ws.numel(), _stream(dev)))
+    return loss, pos_loss, saved
+
+
+def tv_loss_bwd(target, draft, saved, grad_loss, grad_dtype=None, out=None):
+    """End-to-end TV loss backward (mtp_tv_loss_bwd): gradient w.r.t. the draft
+    logits, [T, gamma, V] in grad_dtype (default: the draft's dtype)."""
+    lib = load()
+    _require_cuda(target, draft, saved, grad_loss)
+    T, G, V, t_pos, t_head = _tv_layout(target, draft)
+    dev = draft.device
+    dt = _dtype_code(draft)
+    grad_dtype = grad_dtype or draft.dtype
+    if out is None:
+        out = torch.empty((T, G, V), dtype=grad_dtype, device=dev)
+    if out.stride(2) != 1 or tuple(out.shape) != (T, G, V):
+        raise ValueError("grad output must be [T, gamma, V] with unit stride along V")
+    gdt = _DTYPES[out.dtype]
+    saved = saved.contiguous()
+    grad_loss = grad_loss.reshape(1).to(torch.float32).contiguous()
+    with torch.cuda.device(dev):
+        check(lib.mtp_tv_loss_bwd(_ptr(target), t_pos, t_head, _ptr(draft), draft.stride(0), draft.stride(1),
+                                  dt, T, G, V, _ptr(saved), _ptr(grad_loss), _ptr(out), out.stride(0),
+                                  out.stride(1), gdt, _stream(dev)))
+    return out
+
+
+class TVLoss(torch.autograd.Function):
+    """L = mean_t -sum_k prod_{j<=k} alpha_{t,j}; gradient to the draft logits only
+    (the target distribution is detached)."""
+
+    @staticmethod
+    def forward(ctx, draft, target):
+        loss, _, saved = tv_loss_fwd(target.detach(), draft.detach())
+        ctx.save_for_backward(draft.detach(), target.detach(), saved)
+        return loss[0]
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        draft, target, saved = ctx.saved_tensors
+        grad = tv_loss_bwd(target, draft, saved, grad_out.reshape(1))
+        return grad, None
+
+
+def tv_loss(draft, target):
+    return TVLoss.apply(draft, target)
+
+
+def workspace_error(ws):
+    """The error word of a workspace (non-zero after a bounded-wait timeout)."""
+    lib = load()
+    word = ctypes.c_uint32()
+    check(lib.mtp_workspace_error(_ptr(ws), ctypes.byref(word), _stream(ws.device)))
+    return word.value
+
+
+
+
+class VerifyPlan:
+    """A verify call bound once to fixed input and output tensors, so that repeated
+    launches (a decode loop, a benchmark) only pay for the C call.  `run(seed,
+    offset)` enqueues mtp_verify on the current stream and returns the outputs
+    dict, whose tensors are overwritten by every run."""
+
+    def __init__(self, target, draft, draft_tokens):
+        self.lib = load()
+        draft_tokens = draft_tokens.contiguous()
+        self.inputs = (target, draft, draft_tokens)                   # keeps the pointers alive
+        self.out = verify(target, draft, draft_tokens, 0, 0)          # validates, allocates, warms
+        B, G1, V = target.shape
+        self.shape = (B, G1 - 1, V)
+        nbytes = ctypes.c_size_t()
+        check(self.lib.mtp_verify_workspace_size(B, G1 - 1, V, _dtype_code(target), ctypes.byref(nbytes)))
+        self.ws = workspace(target.device, nbytes.value)
+        o = self.out
+        self._head = (_ptr(target), target.stride(1), _ptr(draft), draft.stride(1), _dtype_code(target),
+                      B, G1 - 1, V, _ptr(draft_tokens))
+        self._tail = (_ptr(o["accept"]), _ptr(o["accepted_len"]), _ptr(o["next_token"]), _ptr(o["row_token"]),
+                      _ptr(o["overlap"]), _ptr(o["tv"]), _ptr(o["entropy"]), _ptr(o["row_status"]),
+                      _ptr(self.ws), self.ws.numel(), _stream(target.device))
+        self._fn = self.lib.mtp_verify
+
+    def run(self, seed, offset=0):
+        st = self._fn(*self._head, ctypes.c_uint64(seed), ctypes.c_uint64(offset), *self._tail)
+        if st:
+            check(st)
+        return self.out
+
+
+class TVPlan:
+    """Forward and backward TV-loss calls bound to fixed tensors (see VerifyPlan)."""
+
+    def __init__(self, target, draft, grad_dtype=None):
+        self.lib = load()
+        T, G, V, t_pos, t_head = _tv_layout(target, draft)
+        self.inputs = (target, draft)
+        dev = draft.device
+        dt = _dtype_code(draft)
+        self.loss, self.pos_loss, self.saved = tv_loss_fwd(target, draft)
+        self.grad_loss = torch.ones(1, dtype=torch.float32, device=dev)
+        self.grad = torch.empty((T, G, V), dtype=grad_dtype or draft.dtype, device=dev)
+        nbytes = ctypes.c_size_t()
+        check(self.lib.mtp_tv_loss_workspace_size(T, G, V, dt, int(t_head == 0), ctypes.byref(nbytes)))
+        self.ws = workspace(dev, nbytes.value)
+        s = _stream(dev)
+        common = (_ptr(target), t_pos, t_head, _ptr(draft), draft.stride(0), draft.stride(1), dt, T, G, V)
+        self._fwd = common + (_ptr(self.loss), _ptr(self.pos_loss), _ptr(self.saved), _ptr(self.ws),
+                              self.ws.numel(), s)
+        self._bwd = common + (_ptr(self.saved), _ptr(self.grad_loss), _ptr(self.grad), self.grad.stride(0),
+                              self.grad.stride(1), _DTYPES[self.grad.dtype], s)
+
+    def forward(self):
+        st = self.lib.mtp_tv_loss_fwd(*self._fwd)
+        if st:
+            check(st)
+        return self.loss
+
+    def backward(self):
+        st = self.lib.mtp_tv_loss_bwd(*self._bwd)
+        if st:
+            check(st)
+        return self.grad
+
+
+__all__ = ["verify", "tv_loss_fwd", "tv_loss_bwd", "tv_loss", "TVLoss", "MtpError", "workspace",
+           "workspace_error", "VerifyPlan", "TVPlan"]
