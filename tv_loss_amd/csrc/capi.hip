@@ -87,7 +87,7 @@ mtp_status cluster_capacity(int kernel, int dt, int G, int shared, int64_t* per_
 
 // ---- workspace layouts --------------------------------------------------------
 struct VerifyLayout {
-  size_t err, grp, seq, part1, part2, rec, total;
+  size_t err, part1, seg, total;
   mtp::RowSplit sp;
   int64_t ngroups;
 };
@@ -97,19 +97,17 @@ VerifyLayout verify_layout(int32_t B, int32_t G, int32_t V, mtp_dtype dt) {
   L.sp = mtp::make_split(V, per_vec(dt), mtp::verify_vec_per_thread(dt));
   L.ngroups = (int64_t)B * (G + 1);
   const int64_t C = L.sp.nchunks;
+  const int64_t nseg = (int64_t)mtp::verify_vec_per_thread(dt) * mtp::kWaves;
   size_t off = 0;
   L.err = off; off = align256(off + 4);
-  L.grp = off; off = align256(off + (size_t)L.ngroups * mtp::kCounterStride * 4);
-  L.seq = off; off = align256(off + (size_t)B * mtp::kCounterStride * 4);
-  L.part1 = off; off = align256(off + (size_t)L.ngroups * C * 8 * 4);
-  L.part2 = off; off = align256(off + (size_t)L.ngroups * C * 2 * 4);
-  L.rec = off; off = align256(off + (size_t)L.ngroups * 2 * 4);
+  L.part1 = off; off = align256(off + (size_t)L.ngroups * C * 3 * 8);
+  L.seg = off; off = align256(off + (size_t)L.ngroups * C * nseg * 4);
   L.total = off;
   return L;
 }
 
 struct TvLayout {
-  size_t err, grp, glob, part1, part2, pos, total;
+  size_t err, part1, part2, pos, total;
   mtp::RowSplit sp;
 };
 
@@ -119,13 +117,22 @@ TvLayout tv_layout(int32_t T, int32_t G, int32_t V, mtp_dtype dt, bool shared) {
   const int64_t C = L.sp.nchunks;
   size_t off = 0;
   L.err = off; off = align256(off + 4);
-  L.grp = off; off = align256(off + (size_t)T * mtp::kCounterStride * 4);
-  L.glob = off; off = align256(off + 4);
-  L.part1 = off; off = align256(off + (size_t)T * C * mtp::tv_fwd_part1_stride(G, shared) * 4);
+  L.part1 = off; off = align256(off + (size_t)T * C * mtp::tv_fwd_part1_words(G, shared) * 8);
   L.part2 = off; off = align256(off + (size_t)T * C * 2 * G * 4);
   L.pos = off; off = align256(off + (size_t)T * 4);
   L.total = off;
   return L;
+}
+
+// Persistent super-groups: C workgroups per super-group, at most per_xcd resident
+// workgroups per XCD, L groups per XCD.  Returns (super-groups per XCD, layers).
+void plan_layers(int64_t per_xcd, int C, int64_t L, int* sgroups, int* layers) {
+  int64_t smax = per_xcd / C;
+  if (smax < 1) smax = 1;
+  const int64_t k = (L + smax - 1) / smax;
+  const int64_t S = (L + k - 1) / k;
+  *sgroups = (int)S;
+  *layers = (int)k;
 }
 
 template <typename T>
@@ -193,15 +200,16 @@ mtp_status mtp_verify(const void* target, int64_t target_row_stride, const void*
   if ((s = check_row_base(draft, draft_row_stride, dtype, "draft"))) return s;
   const VerifyLayout L = verify_layout(batch, gamma, vocab, dtype);
   if ((s = check_workspace(workspace, workspace_bytes, L.total))) return s;
-  const int64_t grid = (L.ngroups + 7) / 8 * 8 * (int64_t)L.sp.nchunks;
-  if (grid > 0x7fffffffLL) return fail(MTP_ERR_SHAPE, "batch * (gamma + 1) * chunks is too large");
+  if (L.ngroups > 0x7fffffffLL / 8) return fail(MTP_ERR_SHAPE, "batch * (gamma + 1) is too large");
 
   // ---- device-dependent checks ---------------------------------------------
   int64_t per_xcd = 0;
   if ((s = cluster_capacity(0, dtype, 0, 0, &per_xcd))) return s;
-  if (2 * (int64_t)L.sp.nchunks > per_xcd)
+  if ((int64_t)L.sp.nchunks > per_xcd)
     return fail(MTP_ERR_SHAPE, "vocab %d needs %d co-resident workgroups per row; one XCD holds %lld", vocab,
                 L.sp.nchunks, (long long)per_xcd);
+  int sgroups = 0, layers = 0;
+  plan_layers(per_xcd, L.sp.nchunks, (L.ngroups + 7) / 8, &sgroups, &layers);
 
   mtp::VerifyArgs a{};
   a.target = target; a.t_stride = target_row_stride;
@@ -212,13 +220,12 @@ mtp_status mtp_verify(const void* target, int64_t target_row_stride, const void*
   a.accept = accept; a.accepted_len = accepted_len; a.next_token = next_token;
   a.row_token = row_token; a.overlap = overlap; a.tv = tv; a.entropy = entropy; a.row_status = row_status;
   a.err = at<uint32_t>(workspace, L.err);
-  a.grp_cnt = at<int>(workspace, L.grp);
-  a.seq_cnt = at<int>(workspace, L.seq);
-  a.part1 = at<float>(workspace, L.part1);
-  a.part2 = at<float>(workspace, L.part2);
-  a.rec = at<int>(workspace, L.rec);
+  a.part1 = at<uint64_t>(workspace, L.part1);
+  a.seg = at<float>(workspace, L.seg);
   a.sp = L.sp;
   a.ngroups = (int)L.ngroups;
+  a.sgroups = sgroups;
+  a.layers = layers;
   hipError_t e = mtp::launch_verify(a, dtype, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MTP_ERR_LAUNCH, "verify launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -260,25 +267,25 @@ mtp_status mtp_tv_loss_fwd(const void* target, int64_t target_pos_stride, int64_
   const bool shared = target_head_stride == 0;
   const TvLayout L = tv_layout(T, gamma, vocab, dtype, shared);
   if ((s = check_workspace(workspace, workspace_bytes, L.total))) return s;
-  const int64_t grid = (int64_t)(T + 7) / 8 * 8 * L.sp.nchunks;
-  if (grid > 0x7fffffffLL) return fail(MTP_ERR_SHAPE, "T * chunks is too large");
   int64_t per_xcd = 0;
   if ((s = cluster_capacity(1, dtype, gamma, shared, &per_xcd))) return s;
-  if (2 * (int64_t)L.sp.nchunks > per_xcd)
+  if ((int64_t)L.sp.nchunks > per_xcd)
     return fail(MTP_ERR_SHAPE, "vocab %d needs %d co-resident workgroups per position; one XCD holds %lld",
                 vocab, L.sp.nchunks, (long long)per_xcd);
+  int sgroups = 0, layers = 0;
+  plan_layers(per_xcd, L.sp.nchunks, ((int64_t)T + 7) / 8, &sgroups, &layers);
   mtp::TvArgs a{};
   a.target = target; a.t_pos = target_pos_stride; a.t_head = target_head_stride;
   a.draft = draft; a.d_pos = draft_pos_stride; a.d_head = draft_head_stride;
   a.T = T; a.G = gamma; a.V = vocab;
   a.loss = loss; a.pos_loss = pos_loss; a.saved = saved;
   a.err = at<uint32_t>(workspace, L.err);
-  a.grp_cnt = at<int>(workspace, L.grp);
-  a.glob_cnt = at<int>(workspace, L.glob);
-  a.part1 = at<float>(workspace, L.part1);
+  a.part1 = at<uint64_t>(workspace, L.part1);
   a.part2 = at<float>(workspace, L.part2);
   a.pos_ws = at<float>(workspace, L.pos);
   a.sp = L.sp;
+  a.sgroups = sgroups;
+  a.layers = layers;
   hipError_t e = mtp::launch_tv_fwd(a, dtype, shared, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MTP_ERR_LAUNCH, "TV forward launch failed: %s", hipGetErrorString(e));
   return ok();

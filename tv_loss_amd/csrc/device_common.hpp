@@ -55,55 +55,103 @@ __host__ __device__ inline RowSplit make_split(int64_t V, int per_vec, int vec_p
   return s;
 }
 
-// Load this thread's NV vectors of one row chunk as floats.  Element (j, e) of the
-// thread is vocabulary index (vbeg + j*kBlock + tid) * PV + e.  Elements outside
-// the chunk or the row read as -inf.  Only whole vectors are read with 16-byte
-// loads; the row's partial last vector is read element by element.
-template <int DT, int NV>
-__device__ __forceinline__ void load_chunk(const void* __restrict__ row, int64_t vbeg, int64_t vend,
-                                           const RowSplit& sp, int64_t V,
-                                           float (&x)[NV * Elem<DT>::kPerVec]) {
-  constexpr int PV = Elem<DT>::kPerVec;
+// Loading a chunk of R rows: this thread's NV 16-byte vectors per row.  Element
+// (j, e) of the thread is vocabulary index (vbeg + j*kBlock + tid) * PV + e.
+//
+// issue_rows() puts every load of every row in flight at once (unconditional, at
+// addresses clamped into the row), so a chunk costs one memory round trip and can
+// be prefetched while earlier data is processed.  unpack_rows() turns the raw
+// words into floats, -inf outside the chunk or the row; the row's partial last
+// vector, if the chunk holds it, is read element by element.
+template <int NV, int R>
+struct RawChunk {
+  u32x4 v[R][NV];
+};
+
+// Only the first `nrows` rows (a wave-uniform count, default R) are loaded.
+template <int DT, int NV, int R>
+__device__ __forceinline__ void issue_rows(RawChunk<NV, R>& raw, const char* const (&rows)[R], int64_t vbeg,
+                                           const RowSplit& sp, int nrows = R) {
   const int tid = threadIdx.x;
-  u32x4 raw[NV];
+  if (sp.nvec_full > 0) {
+    const int64_t last = sp.nvec_full - 1;
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int64_t vi = vbeg + (int64_t)j * kBlock + tid;
-    if (vi < vend && vi < sp.nvec_full) {
-      raw[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row) + vi);
-    } else {
-      raw[j] = u32x4{0u, 0u, 0u, 0u};
+    for (int r = 0; r < R; ++r) {
+      if (r >= nrows) break;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int64_t vi = min(vbeg + (int64_t)j * kBlock + tid, last);
+        raw.v[r][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rows[r]) + vi);
+      }
     }
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int j = 0; j < NV; ++j) raw.v[r][j] = u32x4{0u, 0u, 0u, 0u};
   }
+}
+
+template <int DT, int NV, int R>
+__device__ __forceinline__ void unpack_rows(const RawChunk<NV, R>& raw, const char* const (&rows)[R], int64_t vbeg,
+                                            int64_t vend, const RowSplit& sp, int64_t V,
+                                            float (&x)[R][NV * Elem<DT>::kPerVec], int nrows = R) {
+  constexpr int PV = Elem<DT>::kPerVec;
+  // a masked word reads as -inf in every element it holds
+  constexpr uint32_t kMasked = DT == kBF16 ? 0xFF80FF80u : 0xFF800000u;
+  const int tid = threadIdx.x;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int64_t vi = vbeg + (int64_t)j * kBlock + tid;
     const bool full = vi < vend && vi < sp.nvec_full;
-    if constexpr (DT == kBF16) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (r >= nrows) break;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        x[j * PV + 2 * w] = full ? bf16_lo(raw[j][w]) : kNegInf;
-        x[j * PV + 2 * w + 1] = full ? bf16_hi(raw[j][w]) : kNegInf;
+        const uint32_t word = full ? raw.v[r][j][w] : kMasked;
+        if constexpr (DT == kBF16) {
+          x[r][j * PV + 2 * w] = bf16_lo(word);
+          x[r][j * PV + 2 * w + 1] = bf16_hi(word);
+        } else {
+          x[r][j * PV + w] = __uint_as_float(word);
+        }
       }
-    } else {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) x[j * PV + w] = full ? __uint_as_float(raw[j][w]) : kNegInf;
     }
-    if (!full && vi < vend) {   // the row's partial last vector
+  }
+  // the row's partial last vector (V not a multiple of PV), if this chunk holds it
+  const int64_t tail = sp.nvec_full;
+  if (sp.nvec != sp.nvec_full && vbeg <= tail && tail < vend) {
 #pragma unroll
-      for (int e = 0; e < PV; ++e) {
-        const int64_t idx = vi * PV + e;
-        if (idx < V) {
-          if constexpr (DT == kBF16) {
-            const uint16_t h = reinterpret_cast<const uint16_t*>(row)[idx];
-            x[j * PV + e] = __uint_as_float((uint32_t)h << 16);
-          } else {
-            x[j * PV + e] = reinterpret_cast<const float*>(row)[idx];
+    for (int j = 0; j < NV; ++j) {
+      if (vbeg + (int64_t)j * kBlock + tid == tail) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          if (r >= nrows) break;
+#pragma unroll
+          for (int e = 0; e < PV; ++e) {
+            const int64_t idx = tail * PV + e;
+            if (idx < V) {
+              if constexpr (DT == kBF16) {
+                x[r][j * PV + e] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(rows[r])[idx] << 16);
+              } else {
+                x[r][j * PV + e] = reinterpret_cast<const float*>(rows[r])[idx];
+              }
+            }
           }
         }
       }
     }
   }
+}
+
+template <int DT, int NV, int R>
+__device__ __forceinline__ void load_rows(const char* const (&rows)[R], int64_t vbeg, int64_t vend,
+                                          const RowSplit& sp, int64_t V,
+                                          float (&x)[R][NV * Elem<DT>::kPerVec]) {
+  RawChunk<NV, R> raw;
+  issue_rows<DT, NV, R>(raw, rows, vbeg, sp);
+  unpack_rows<DT, NV, R>(raw, rows, vbeg, vend, sp, V, x);
 }
 
 // Scalar load of one logit.
@@ -257,23 +305,61 @@ __device__ __forceinline__ int arrive(int* counter) {
   return old;
 }
 
-// Thread 0 waits until *counter >= target; then the whole block is released.
-// Must be called by every thread of the block.
-__device__ __forceinline__ void block_wait(int* counter, int target, uint32_t* err) {
-  if (threadIdx.x == 0) {
-    if (ld_coherent(counter) < target) {
-      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-      while (ld_coherent(counter) < target) {
-        __builtin_amdgcn_s_sleep(2);
-        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimitTicks) {
-          __hip_atomic_fetch_or(err, kErrSyncTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-      }
+// ---- self-announcing records ------------------------------------------------
+// A record word is 64 bits written with one coherent atomic store, so a reader
+// sees either zero (not yet written: the workspace starts zeroed) or the whole
+// word.  Every encoding below is non-zero, so "non-zero" is the ready flag and a
+// consumer gets the data with the poll itself: no separate counter, no ordering
+// between a data store and a flag store.
+__device__ __forceinline__ uint64_t pack2(float lo, float hi) {
+  return (uint64_t)__float_as_uint(lo) | ((uint64_t)__float_as_uint(hi) << 32);
+}
+__device__ __forceinline__ float unpack_lo(uint64_t w) { return __uint_as_float((uint32_t)w); }
+__device__ __forceinline__ float unpack_hi(uint64_t w) { return __uint_as_float((uint32_t)(w >> 32)); }
+constexpr uint32_t kSign = 0x80000000u;
+// a non-negative float with its sign bit set as a marker (decode: clear the bit)
+__device__ __forceinline__ float mark(float nonneg) { return __uint_as_float(__float_as_uint(nonneg) | kSign); }
+__device__ __forceinline__ float unmark(float v) { return __uint_as_float(__float_as_uint(v) & ~kSign); }
+
+__device__ __forceinline__ void put_word(uint64_t* p, uint64_t w) {
+  __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t get_word(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One wave polls the W-word records of chunks [c0, c0 + 64) (lane l: chunk c0 + l,
+// if < C) until all are non-zero, and returns this lane's words.  Bounded: on
+// timeout it flags `err` and returns what it has.
+template <int W>
+__device__ __forceinline__ void wave_poll(const uint64_t* rec, int c0, int C, uint64_t (&w)[W], uint32_t* err) {
+  const int lane = threadIdx.x & 63;
+  const int c = c0 + lane;
+  bool ready = !(c < C);          // lanes without a chunk are ready; ready lanes stop loading
+#pragma unroll
+  for (int i = 0; i < W; ++i) w[i] = 0ull;
+  uint64_t t0 = 0;
+  for (int it = 0;; ++it) {
+    if (!ready) {
+#pragma unroll
+      for (int i = 0; i < W; ++i) w[i] = get_word(rec + (int64_t)c * W + i);
+      ready = true;
+#pragma unroll
+      for (int i = 0; i < W; ++i) ready = ready && (w[i] != 0ull);
+    }
+    if (__ballot(!ready) == 0ull) return;
+    if (it == 0) t0 = __builtin_amdgcn_s_memrealtime();
+    __builtin_amdgcn_s_sleep(2);
+    if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimitTicks) {
+      if (lane == 0) __hip_atomic_fetch_or(err, kErrSyncTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
     }
   }
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __syncthreads();
+}
+
+// Zero n 64-bit record words with the whole block.
+__device__ __forceinline__ void block_zero_words(uint64_t* p, int64_t n) {
+  for (int64_t i = threadIdx.x; i < n; i += kBlock) put_word(p + i, 0ull);
 }
 
 __device__ __forceinline__ void reset_counter(int* counter) { st_coherent(counter, 0); }

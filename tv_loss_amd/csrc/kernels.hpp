@@ -9,8 +9,15 @@ namespace mtp {
 
 // Vectors of 16 bytes each thread keeps per row: verify keeps a target and a
 // draft chunk in registers (64 floats per thread either way).
-constexpr int kVerifyNVBf16 = 4;   // 32 bf16 per row per thread, 8192-element chunks
-constexpr int kVerifyNVF32 = 8;    // 32 fp32 per row per thread, 8192-element chunks
+constexpr int kVerifyNVBf16 = 3;   // 24 bf16 per row per thread, 6144-element chunks
+constexpr int kVerifyNVF32 = 4;    // 16 fp32 per row per thread, 4096-element chunks
+constexpr int kMaxRowsPerSeq = 9;  // gamma + 1 with gamma <= 8
+// Workgroups per CU the layered main kernels are compiled for (one wave per SIMD
+// each), chosen so that one chunk in registers plus the next one in flight fit
+// without spilling: 4 (128 VGPRs) for verify's two rows, 3 (168 VGPRs) for the
+// TV forward's four.
+constexpr int kVerifyBlocksPerCU = 4;
+constexpr int kTvFwdBlocksPerCU = 3;
 
 // Counters sit 16 ints (64 bytes) apart so clusters do not share a line.
 constexpr int kCounterStride = 16;
@@ -30,10 +37,12 @@ struct VerifyArgs {
   uint64_t seed, offset;
   uint8_t* accept; int32_t* accepted_len; int32_t* next_token;
   int32_t* row_token; float* overlap; float* tv; float* entropy; int32_t* row_status;
-  // workspace sections
-  uint32_t* err; int* grp_cnt; int* seq_cnt; float* part1; float* part2; int* rec;
+  // workspace sections: error word, pass-1 records [group][chunk][3], segment
+  // masses [group][chunk][4 * NV]
+  uint32_t* err; uint64_t* part1; float* seg;
   RowSplit sp;
   int ngroups;
+  int sgroups, layers;   // super-groups per XCD, groups per super-group
 };
 
 int verify_vec_per_thread(int dt);
@@ -54,16 +63,18 @@ struct TvArgs {
   // backward
   const float* saved_in; const float* grad_loss;
   void* grad; int64_t g_pos, g_head; int grad_dt;
-  // forward workspace
-  uint32_t* err; int* grp_cnt; int* glob_cnt; float* part1; float* part2; float* pos_ws;
+  // forward workspace: error word, pass-1 records [t][chunk][rows], overlap and S
+  // partials [t][chunk][2 gamma], per-position losses [t]
+  uint32_t* err; uint64_t* part1; float* part2; float* pos_ws;
   RowSplit sp;
+  int sgroups, layers;
 };
 
 constexpr int kTvSavedStride = 4;   // saved[t, k, :] = (lse_p, lse_q, alpha, S)
 constexpr int kTvMaxHeads = 8;
 
 int tv_fwd_vec_per_thread(int dt, int G, bool shared);
-int tv_fwd_part1_stride(int G, bool shared);
+int tv_fwd_part1_words(int G, bool shared);
 hipError_t launch_tv_fwd(const TvArgs& a, int dt, bool shared, hipStream_t stream);
 hipError_t tv_fwd_occupancy(int dt, int G, bool shared, int* blocks_per_cu);
 int tv_bwd_vec_per_thread(int dt);

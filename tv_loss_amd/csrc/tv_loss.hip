@@ -9,12 +9,14 @@
 //   dL/dz_{t,j,v} = w_{t,j} q_v (1[q_v <= p_v] - S_{t,j}),
 //   w_{t,j} = -(g/T) sum_{k>=j} prod_{i<=k, i!=j} alpha_{t,i}.
 //
-// Forward: one cluster per position t.  Each workgroup keeps one vocabulary chunk
-// of the target row(s) and of the gamma draft rows in registers, publishes its
-// log-sum-exp partials, waits for the cluster, then computes its overlap and S
-// partials from registers.  The last workgroup of the cluster reduces them in a
-// fixed order and writes l_t and the saved statistics; the last position to
-// finish writes the mean.  Every logit is read from HBM once.
+// Forward: C workgroups split each position's rows along the vocabulary and sweep
+// the positions in layers (tv_fwd_main).  Per layer a workgroup keeps its chunk of
+// the target row(s) and of the gamma draft rows in registers while the next
+// layer's chunk is in flight, publishes its log-sum-exp partials as a
+// self-announcing record, polls its siblings' records, and computes its overlap
+// and S partials from registers.  tv_fwd_finish (one wave per position) sums the
+// partials in a fixed order and writes l_t and the saved statistics; tv_fwd_mean
+// writes the mean.  Every logit is read from HBM once.
 // Backward: pure streaming; each workgroup reads one chunk of the target and draft
 // rows of one position plus the saved statistics, and writes the gradient chunk.
 // The indicator is evaluated on logits, z_v - a_v <= lse_q - lse_p, so no
@@ -42,22 +44,29 @@ __device__ __forceinline__ Lse thread_lse_plain(float (&x)[NE]) {
   return Lse{ref, z, 0.f};
 }
 
-// Wave 0 merges the C chunk partials (ref, z) of NR rows with coherent loads in a
-// fixed order and broadcasts log2-sum-exp per row through LDS.
+// Wave 0 polls the C pass-1 records (NR words (ref, z) each) of the position and
+// merges them in one fixed order; log2-sum-exp per row is broadcast through LDS.
 template <int NR>
-__device__ __forceinline__ void merge_rows(const float* p1, int C, float (&lse2)[NR], float* lds) {
-  constexpr int P1S = 2 * NR;
+__device__ __forceinline__ void merge_rows(const uint64_t* p1, int C, float (&lse2)[NR], float* lds,
+                                           uint32_t* err) {
+  __syncthreads();
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
+    Lse acc[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) acc[r] = lse_empty();
+    for (int c0 = 0; c0 < C; c0 += 64) {
+      uint64_t w[NR];
+      wave_poll<NR>(p1, c0, C, w, err);
+      if (c0 + lane < C) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) acc[r] = lse_merge(acc[r], Lse{unpack_lo(w[r]), unmark(unpack_hi(w[r])), 0.f});
+      }
+    }
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-      Lse acc = lse_empty();
-      for (int c = lane; c < C; c += 64) {
-        const float* q = p1 + (int64_t)c * P1S + 2 * r;
-        acc = lse_merge(acc, Lse{ld_coherent(q), ld_coherent(q + 1), 0.f});
-      }
-      acc = wave_lse(acc);
-      if (lane == 0) lds[r] = lse_log2(acc);
+      const Lse m = wave_lse(acc[r]);
+      if (lane == 0) lds[r] = lse_log2(m);
     }
   }
   __syncthreads();
@@ -66,109 +75,150 @@ __device__ __forceinline__ void merge_rows(const float* p1, int C, float (&lse2)
   __syncthreads();
 }
 
+// Vectors per thread and row: about 64 bf16 or 32 fp32 values per thread in all
+// (their raw words for the next layer are in flight at the same time).
 template <int G>
 constexpr int fwd_nv(int per_vec, bool shared) {
   const int rows = (shared ? 1 : G) + G;
-  const int nv = 64 / (rows * per_vec);
+  const int budget = per_vec == 8 ? 64 : 32;
+  const int nv = budget / (rows * per_vec);
   return nv < 1 ? 1 : nv;
 }
 
+// Forward main kernel: super-groups of C workgroups sweep the positions of their
+// XCD in layers (position (sg + i * S) * 8 + xcd at layer i), prefetching the next
+// layer's chunk; per layer one record poll, then the chunk's overlap and S
+// partials from registers.
 template <int DT, int G, bool SHARED>
-__global__ __launch_bounds__(kBlock) void tv_fwd_kernel(TvArgs a) {
+__global__ __launch_bounds__(kBlock, kTvFwdBlocksPerCU) void tv_fwd_main(TvArgs a) {
   constexpr int PV = Elem<DT>::kPerVec;
   constexpr int NV = fwd_nv<G>(PV, SHARED);
   constexpr int NE = NV * PV;
   constexpr int NT = SHARED ? 1 : G;
   constexpr int NR = NT + G;
-  constexpr int P1S = 2 * NR;
   const int C = a.sp.nchunks;
   const int bid = blockIdx.x;
   const int xcd = bid & 7, slot = bid >> 3;
-  const int lg = slot / C, c = slot - lg * C;
-  const int t = lg * 8 + xcd;
-  if (t >= a.T) return;
+  const int sg = slot / C, c = slot - sg * C;
+  int nl = 0;
+  while (nl < a.layers && (int64_t)(sg + nl * a.sgroups) * 8 + xcd < a.T) ++nl;
+  if (nl == 0) return;
   const int64_t vbeg = (int64_t)c * a.sp.vec_per_chunk;
   const int64_t vend = min(vbeg + a.sp.vec_per_chunk, a.sp.nvec);
 
   __shared__ float lds[3 * kWaves * NR + 2 * kWaves * G];
-  __shared__ int last_in_cluster, last_position;
 
-  float xt[NT][NE], xd[G][NE];
-  const char* tb = reinterpret_cast<const char*>(a.target);
-  const char* db = reinterpret_cast<const char*>(a.draft);
+  auto rows_of = [&](int t, const char* (&rows)[NR]) {
+    const char* tb = reinterpret_cast<const char*>(a.target);
+    const char* db = reinterpret_cast<const char*>(a.draft);
 #pragma unroll
-  for (int r = 0; r < NT; ++r)
-    load_chunk<DT, NV>(tb + ((int64_t)t * a.t_pos + (int64_t)r * a.t_head) * Elem<DT>::kBytes,
-                       vbeg, vend, a.sp, a.V, xt[r]);
+    for (int r = 0; r < NT; ++r) rows[r] = tb + ((int64_t)t * a.t_pos + (int64_t)r * a.t_head) * Elem<DT>::kBytes;
 #pragma unroll
-  for (int k = 0; k < G; ++k)
-    load_chunk<DT, NV>(db + ((int64_t)t * a.d_pos + (int64_t)k * a.d_head) * Elem<DT>::kBytes,
-                       vbeg, vend, a.sp, a.V, xd[k]);
+    for (int k = 0; k < G; ++k) rows[NT + k] = db + ((int64_t)t * a.d_pos + (int64_t)k * a.d_head) * Elem<DT>::kBytes;
+  };
 
-  // ---- pass 1 ----------------------------------------------------------------
-  Lse parts[NR];
-  float refs[NR];
-#pragma unroll
-  for (int r = 0; r < NT; ++r) { parts[r] = thread_lse_plain<NE>(xt[r]); refs[r] = parts[r].ref; }
-#pragma unroll
-  for (int k = 0; k < G; ++k) { parts[NT + k] = thread_lse_plain<NE>(xd[k]); refs[NT + k] = parts[NT + k].ref; }
-  block_lse<NR>(parts, lds);
-  float* p1 = a.part1 + (int64_t)t * C * P1S;
-  int* cnt = a.grp_cnt + (int64_t)t * kCounterStride;
-  if (threadIdx.x == 0) {
-    float* mine = p1 + (int64_t)c * P1S;
-#pragma unroll
-    for (int r = 0; r < NR; ++r) { st_coherent(mine + 2 * r, parts[r].ref); st_coherent(mine + 2 * r + 1, parts[r].z); }
-    arrive(cnt);
+  RawChunk<NV, NR> raw;
+  {
+    const char* rows[NR];
+    rows_of(sg * 8 + xcd, rows);
+    issue_rows<DT, NV, NR>(raw, rows, vbeg, a.sp);
   }
-  block_wait(cnt, C, a.err);
-  float lse2[NR];
-  merge_rows<NR>(p1, C, lse2, lds);
+  for (int i = 0; i < nl; ++i) {
+    const int t = (sg + i * a.sgroups) * 8 + xcd;
+    const char* rows[NR];
+    rows_of(t, rows);
+    float x[NR][NE];
+    unpack_rows<DT, NV, NR>(raw, rows, vbeg, vend, a.sp, a.V, x);
+    if (i + 1 < nl) {   // prefetch the next layer's chunk
+      const char* nrows[NR];
+      rows_of((sg + (i + 1) * a.sgroups) * 8 + xcd, nrows);
+      issue_rows<DT, NV, NR>(raw, nrows, vbeg, a.sp);
+    }
 
-  // ---- pass 2: overlap and S from registers ----------------------------------
-  float s[NR];
+    // ---- pass 1 --------------------------------------------------------------
+    Lse parts[NR];
+    float refs[NR];
 #pragma unroll
-  for (int r = 0; r < NR; ++r) s[r] = fast_exp2(refs[r] - lse2[r]);
-  float acc[2 * G];
+    for (int r = 0; r < NR; ++r) { parts[r] = thread_lse_plain<NE>(x[r]); refs[r] = parts[r].ref; }
+    block_lse<NR>(parts, lds);
+    uint64_t* p1 = a.part1 + (int64_t)t * C * NR;
+    if (threadIdx.x == 0) {
 #pragma unroll
-  for (int k = 0; k < 2 * G; ++k) acc[k] = 0.f;
+      for (int r = 0; r < NR; ++r) put_word(p1 + (int64_t)c * NR + r, pack2(parts[r].ref, mark(parts[r].z)));
+    }
+    float lse2[NR];
+    merge_rows<NR>(p1, C, lse2, lds, a.err);
+
+    // ---- pass 2: overlap and S from registers ------------------------------
+    float s[NR];
 #pragma unroll
-  for (int i = 0; i < NE; ++i) {
-    const float p0 = xt[0][i] * s[0];
+    for (int r = 0; r < NR; ++r) s[r] = fast_exp2(refs[r] - lse2[r]);
+    float acc[2 * G];
 #pragma unroll
-    for (int k = 0; k < G; ++k) {
-      const float p = SHARED ? p0 : xt[SHARED ? 0 : k][i] * s[SHARED ? 0 : k];
-      const float q = xd[k][i] * s[NT + k];
-      const bool ind = q <= p;
-      acc[2 * k] += ind ? q : p;
-      acc[2 * k + 1] += ind ? q : 0.f;
+    for (int k = 0; k < 2 * G; ++k) acc[k] = 0.f;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      const float p0 = x[0][e] * s[0];
+#pragma unroll
+      for (int k = 0; k < G; ++k) {
+        const float p = SHARED ? p0 : x[SHARED ? 0 : k][e] * s[SHARED ? 0 : k];
+        const float q = x[NT + k][e] * s[NT + k];
+        const bool ind = q <= p;
+        acc[2 * k] += ind ? q : p;
+        acc[2 * k + 1] += ind ? q : 0.f;
+      }
+    }
+    block_sum<2 * G>(acc, lds);
+    if (threadIdx.x == 0) {
+      float* mine = a.part2 + ((int64_t)t * C + c) * 2 * G;
+#pragma unroll
+      for (int k = 0; k < 2 * G; ++k) st_coherent(mine + k, acc[k]);
     }
   }
-  block_sum<2 * G>(acc, lds);
-  float* p2 = a.part2 + (int64_t)t * C * 2 * G;
-  if (threadIdx.x == 0) {
-    float* mine = p2 + (int64_t)c * 2 * G;
-#pragma unroll
-    for (int k = 0; k < 2 * G; ++k) st_coherent(mine + k, acc[k]);
-    const int old = arrive(cnt);
-    last_in_cluster = old == 2 * C - 1;
-  }
-  __syncthreads();
-  if (!last_in_cluster) return;
+}
 
-  // ---- last workgroup of the cluster: position statistics --------------------
+// Forward finish: one wave per position sums the chunk partials in a fixed order
+// and writes the position's statistics, then clears the position's records.
+constexpr int kFinishWaves = 4;
+
+template <int G, bool SHARED>
+__global__ __launch_bounds__(64 * kFinishWaves) void tv_fwd_finish(TvArgs a) {
+  constexpr int NT = SHARED ? 1 : G;
+  constexpr int NR = NT + G;
   const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kFinishWaves + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const int C = a.sp.nchunks;
+  uint64_t* p1 = a.part1 + (int64_t)t * C * NR;
+  const float* p2 = a.part2 + (int64_t)t * C * 2 * G;
+  Lse acc[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) acc[r] = lse_empty();
   float tot[2 * G];
 #pragma unroll
-  for (int k = 0; k < 2 * G; ++k) {
-    float v = 0.f;
-    for (int cc = lane; cc < C; cc += 64) v += ld_coherent(p2 + (int64_t)cc * 2 * G + k);
-    tot[k] = wave_sum(v);
+  for (int k = 0; k < 2 * G; ++k) tot[k] = 0.f;
+  for (int c = lane; c < C; c += 64) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const uint64_t w = get_word(p1 + (int64_t)c * NR + r);
+      acc[r] = lse_merge(acc[r], Lse{unpack_lo(w), unmark(unpack_hi(w)), 0.f});
+    }
+#pragma unroll
+    for (int k = 0; k < 2 * G; ++k) tot[k] += ld_coherent(p2 + (int64_t)c * 2 * G + k);
   }
-  __syncthreads();   // every wave has read the partials: clear them for the next call
-  block_zero(p1, (int64_t)C * P1S);
-  block_zero(p2, (int64_t)C * 2 * G);
-  if (threadIdx.x == 0) {
+  float lse2[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) lse2[r] = lse_log2(wave_lse(acc[r]));
+#pragma unroll
+  for (int k = 0; k < 2 * G; ++k) tot[k] = wave_sum(tot[k]);
+  // a call leaves every workspace word it wrote at zero
+  for (int c = lane; c < C; c += 64) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) put_word(p1 + (int64_t)c * NR + r, 0ull);
+#pragma unroll
+    for (int k = 0; k < 2 * G; ++k) st_coherent(const_cast<float*>(p2) + (int64_t)c * 2 * G + k, 0.f);
+  }
+  if (lane == 0) {
     float prod = 1.f, l = 0.f;
     float* sv = a.saved + (int64_t)t * G * kTvSavedStride;
 #pragma unroll
@@ -183,20 +233,17 @@ __global__ __launch_bounds__(kBlock) void tv_fwd_kernel(TvArgs a) {
     }
     if (a.pos_loss) a.pos_loss[t] = l;
     st_coherent(a.pos_ws + t, l);
-    reset_counter(cnt);
-    const int old = arrive(a.glob_cnt);
-    last_position = old == a.T - 1;
   }
-  __syncthreads();
-  if (!last_position) return;
+}
+
+// The mean over positions, in one fixed order.
+__global__ __launch_bounds__(kBlock) void tv_fwd_mean(TvArgs a) {
+  __shared__ float lds[kWaves];
   float sum[1] = {0.f};
   for (int i = threadIdx.x; i < a.T; i += kBlock) sum[0] += ld_coherent(a.pos_ws + i);
   block_sum<1>(sum, lds);
-  block_zero(a.pos_ws, a.T);
-  if (threadIdx.x == 0) {
-    a.loss[0] = sum[0] / (float)a.T;
-    reset_counter(a.glob_cnt);
-  }
+  for (int i = threadIdx.x; i < a.T; i += kBlock) st_coherent(a.pos_ws + i, 0.f);
+  if (threadIdx.x == 0) a.loss[0] = sum[0] / (float)a.T;
 }
 
 // ---------------------------------------------------------------------------
@@ -265,14 +312,22 @@ __global__ __launch_bounds__(kBlock) void tv_bwd_kernel(TvArgs a) {
   const char* db = reinterpret_cast<const char*>(a.draft);
   char* gb = reinterpret_cast<char*>(a.grad);
   constexpr int gbytes = GDT == kBF16 ? 2 : 4;
-  float xt[NE], xd[NE], gr[NE];
-  if (SHARED) load_chunk<DT, NV>(tb + (int64_t)t * a.t_pos * Elem<DT>::kBytes, vbeg, vend, a.sp, a.V, xt);
+  float xv[2][NE], gr[NE];
+  float (&xt)[NE] = xv[0];
+  float (&xd)[NE] = xv[1];
+  if (SHARED) {
+    const char* const rows[1] = {tb + (int64_t)t * a.t_pos * Elem<DT>::kBytes};
+    load_rows<DT, NV, 1>(rows, vbeg, vend, a.sp, a.V, *reinterpret_cast<float(*)[1][NE]>(&xv[0]));
+  }
   for (int k = 0; k < G; ++k) {
-    if (!SHARED)
-      load_chunk<DT, NV>(tb + ((int64_t)t * a.t_pos + (int64_t)k * a.t_head) * Elem<DT>::kBytes, vbeg, vend,
-                         a.sp, a.V, xt);
-    load_chunk<DT, NV>(db + ((int64_t)t * a.d_pos + (int64_t)k * a.d_head) * Elem<DT>::kBytes, vbeg, vend,
-                       a.sp, a.V, xd);
+    const char* drow = db + ((int64_t)t * a.d_pos + (int64_t)k * a.d_head) * Elem<DT>::kBytes;
+    if (!SHARED) {
+      const char* const rows[2] = {tb + ((int64_t)t * a.t_pos + (int64_t)k * a.t_head) * Elem<DT>::kBytes, drow};
+      load_rows<DT, NV, 2>(rows, vbeg, vend, a.sp, a.V, xv);
+    } else {
+      const char* const rows[1] = {drow};
+      load_rows<DT, NV, 1>(rows, vbeg, vend, a.sp, a.V, *reinterpret_cast<float(*)[1][NE]>(&xv[1]));
+    }
     float wsum = 0.f;
     for (int kk = k; kk < G; ++kk) {
       float prod = 1.f;
@@ -304,9 +359,14 @@ __global__ __launch_bounds__(kBlock) void tv_bwd_kernel(TvArgs a) {
 // ---------------------------------------------------------------------------
 template <int DT, bool SHARED, int G>
 static hipError_t launch_fwd_g(const TvArgs& a, hipStream_t stream) {
-  const int C = a.sp.nchunks;
-  const int64_t grid = (int64_t)((a.T + 7) / 8) * C * 8;
-  hipLaunchKernelGGL((tv_fwd_kernel<DT, G, SHARED>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
+  const int64_t grid = (int64_t)a.sgroups * a.sp.nchunks * 8;
+  hipLaunchKernelGGL((tv_fwd_main<DT, G, SHARED>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((tv_fwd_finish<G, SHARED>), dim3((unsigned)((a.T + kFinishWaves - 1) / kFinishWaves)),
+                     dim3(64 * kFinishWaves), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(tv_fwd_mean, dim3(1), dim3(kBlock), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -331,17 +391,23 @@ hipError_t launch_tv_fwd(const TvArgs& a, int dt, bool shared, hipStream_t strea
 }
 
 int tv_fwd_vec_per_thread(int dt, int G, bool shared) {
-  const int pv = dt == kBF16 ? 8 : 4;
-  const int rows = (shared ? 1 : G) + G;
-  const int nv = 64 / (rows * pv);
-  return nv < 1 ? 1 : nv;
+  switch (G) {
+    case 1: return fwd_nv<1>(dt == kBF16 ? 8 : 4, shared);
+    case 2: return fwd_nv<2>(dt == kBF16 ? 8 : 4, shared);
+    case 3: return fwd_nv<3>(dt == kBF16 ? 8 : 4, shared);
+    case 4: return fwd_nv<4>(dt == kBF16 ? 8 : 4, shared);
+    case 5: return fwd_nv<5>(dt == kBF16 ? 8 : 4, shared);
+    case 6: return fwd_nv<6>(dt == kBF16 ? 8 : 4, shared);
+    case 7: return fwd_nv<7>(dt == kBF16 ? 8 : 4, shared);
+    default: return fwd_nv<8>(dt == kBF16 ? 8 : 4, shared);
+  }
 }
 
-int tv_fwd_part1_stride(int G, bool shared) { return 2 * ((shared ? 1 : G) + G); }
+int tv_fwd_part1_words(int G, bool shared) { return (shared ? 1 : G) + G; }
 
 template <int DT, bool SHARED, int G>
 static hipError_t occ_g(int* n) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, tv_fwd_kernel<DT, G, SHARED>, kBlock, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, tv_fwd_main<DT, G, SHARED>, kBlock, 0);
 }
 
 template <int DT, bool SHARED>

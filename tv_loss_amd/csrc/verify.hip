@@ -12,26 +12,33 @@
 // r = max(0, p - q) for k < gamma and r = p for the bonus row; the sequence emits
 // the sample of row n_b, n_b being the number of leading accepts.
 //
-// Layout of the work.  A "group" is one row of one sequence: (target row, draft
-// row) for k < gamma, or the bonus target row alone.  Each group is split along
-// the vocabulary into C chunks, one workgroup each; a chunk is read from HBM once
-// into registers.  The workgroups of a group form a cluster (all on one XCD:
-// workgroup i runs on XCD i mod 8) that exchanges partials through the workspace
-// with device-coherent loads and stores:
-//   1. every workgroup publishes its chunk's log-sum-exp partials (both rows, and
-//      the entropy moment of the target) and waits for the cluster -- the only
-//      wait; each then merges all C partials in one fixed order -> lse, H;
-//   2. pair groups: every workgroup publishes its chunk's overlap and residual
-//      mass from registers and leaves, except the last to publish, which scans
-//      the residual masses in chunk order, finds the chunk holding
-//      t = u' * sum r, and finishes the inverse CDF inside it (from its own
-//      registers, or by reading that chunk again);
-//      bonus groups: the masses of p per chunk come from step 1, so the chunk
-//      holding t finishes the inverse CDF from its registers;
-//   3. the row's finisher writes its outputs; the last row of a sequence to
-//      finish writes the accepted length and the next token.
-// The last user of every counter, partial and record slot clears it, so the
-// workspace is all zeros again when the kernel ends.
+// Two kernels.
+//
+// verify_main streams every logit once.  A "group" is one row of one sequence:
+// (target row, draft row) for k < gamma, or the bonus target row alone.  Each
+// group is split along the vocabulary into C chunks; C workgroups form a
+// super-group that processes one group after another ("layers") in lockstep,
+// chunk c of every group going to the same workgroup.  Per layer a workgroup
+//   - unpacks its chunk (loaded during the previous layer) and immediately puts
+//     the next layer's loads in flight,
+//   - computes its chunk's log-sum-exp partials (both rows, and the entropy
+//     moment of the target) and publishes them as one self-announcing record,
+//   - polls the C records of its group (the only wait; it overlaps the prefetch)
+//     and merges them in one fixed order,
+//   - computes from registers the residual masses r = max(0, p - q) (the masses
+//     of p for a bonus row) of its 4*NV segments (each 512 contiguous elements)
+//     and stores them.
+// All workgroups of a super-group sit on one XCD (workgroup i runs on XCD i mod 8)
+// and are dispatched together, so a super-group only needs its own C workgroups
+// to be co-resident.
+//
+// verify_finish runs one workgroup per sequence, one wave per row.  A wave merges
+// the row's records again (lse, entropy), scans the chunk masses and then the
+// segment masses of the owner chunk in vocabulary order, re-reads the single
+// 512-element segment holding t = u' * sum r and finishes the inverse CDF in it.
+// The row's acceptance flag needs p(y) and q(y) only.  The sequence's accepted
+// length and next token are then formed in LDS.  It also clears the records, so
+// the workspace is all zeros again when the call ends.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -59,32 +66,195 @@ __device__ __forceinline__ Lse thread_lse(float (&x)[NE]) {
   return Lse{ref, z, y};
 }
 
-// max(0, p - q) as p - min(p, q), with p = e_a * s_a and q = e_b * s_b.  FMA
-// contraction is off so that every evaluation (the pass-2 sums and the inverse
-// CDF, possibly in another workgroup) produces the same bits.
-__device__ __forceinline__ void pq_residual(float ea, float sa, float eb, float sb, float* p, float* mn,
-                                            float* r) {
+// max(0, p - q) with p = ea * sa and q = eb * sb, without FMA contraction.
+__device__ __forceinline__ float residual_of(float ea, float sa, float eb, float sb) {
 #pragma clang fp contract(off)
-  const float pp = ea * sa, qq = eb * sb;
-  const float m = fminf(pp, qq);
-  *p = pp;
-  *mn = m;
-  *r = pp - m;
+  const float p = ea * sa, q = eb * sb;
+  return fmaxf(p - q, 0.f);
 }
 
-// Prefix structure over per-chunk masses: lane l owns chunks [l*K, l*K + K).
-struct ChunkScan {
-  float total;     // sum of all masses
-  int owner;       // chunk holding t
-  float start;     // mass before the owner chunk
+// Chunk record of pass 1 (three words): (ref_p, z_p), (ref_q, z_q), (y_p, 1).
+__device__ __forceinline__ void put_p1(uint64_t* rec, const Lse& p, const Lse& q) {
+  put_word(rec + 0, pack2(p.ref, mark(p.z)));
+  put_word(rec + 1, pack2(q.ref, mark(q.z)));
+  put_word(rec + 2, pack2(p.y, 1.f));
+}
+
+__device__ __forceinline__ Lse rec_p(const uint64_t (&w)[3]) {
+  return Lse{unpack_lo(w[0]), unmark(unpack_hi(w[0])), unpack_lo(w[2])};
+}
+__device__ __forceinline__ Lse rec_q(const uint64_t (&w)[3]) {
+  return Lse{unpack_lo(w[1]), unmark(unpack_hi(w[1])), 0.f};
+}
+
+struct RowLse {
+  float lse2_p, lse2_q;
 };
 
-// Every lane computes the same result.  mass(c) supplies chunk c's mass.
-template <typename MassFn>
-__device__ __forceinline__ ChunkScan scan_chunks(int C, float u_prime, MassFn mass) {
+// Wave 0 polls the C pass-1 records of the group and merges them in one fixed
+// order; log2-sum-exp of both rows is broadcast through LDS.
+__device__ __forceinline__ RowLse merge_group(const uint64_t* p1, int C, bool pair, float* lds, uint32_t* err) {
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    Lse ap = lse_empty(), aq = lse_empty();
+    for (int c0 = 0; c0 < C; c0 += 64) {
+      uint64_t w[3];
+      wave_poll<3>(p1, c0, C, w, err);
+      if (c0 + lane < C) {
+        ap = lse_merge(ap, rec_p(w));
+        if (pair) aq = lse_merge(aq, rec_q(w));
+      }
+    }
+    ap = wave_lse(ap);
+    aq = wave_lse(aq);
+    if (lane == 0) {
+      lds[0] = lse_log2(ap);
+      lds[1] = pair ? lse_log2(aq) : 0.f;
+    }
+  }
+  __syncthreads();
+  RowLse r{lds[0], lds[1]};
+  __syncthreads();
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+template <int DT, int NV>
+__global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(VerifyArgs a) {
+  constexpr int PV = Elem<DT>::kPerVec;
+  constexpr int NE = NV * PV;
+  constexpr int NSEG = NV * kWaves;
+  const int C = a.sp.nchunks;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, slot = bid >> 3;
+  const int sg = slot / C, c = slot - sg * C;
+  const int G = a.G, G1 = G + 1;
+  // layer i of this super-group handles group (sg + i * S) * 8 + xcd
+  int nl = 0;
+  while (nl < a.layers && (int64_t)(sg + nl * a.sgroups) * 8 + xcd < a.ngroups) ++nl;
+  if (nl == 0) return;
+
+  __shared__ float lds[3 * kWaves * 2];
+  const int64_t vbeg = (int64_t)c * a.sp.vec_per_chunk;
+  const int64_t vend = min(vbeg + a.sp.vec_per_chunk, a.sp.nvec);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+
+  // the rows of group g: target (b, k) and, for k < gamma, draft (b, k)
+  auto trow_of = [&](int g) {
+    return reinterpret_cast<const char*>(a.target) + (int64_t)g * a.t_stride * Elem<DT>::kBytes;
+  };
+  auto drow_of = [&](int g) {
+    const int b = g / G1, k = g - b * G1;
+    return reinterpret_cast<const char*>(a.draft) + (int64_t)(b * G + (k < G ? k : 0)) * a.d_stride * Elem<DT>::kBytes;
+  };
+  auto is_pair = [&](int g) { return g % G1 < G; };
+  auto issue = [&](RawChunk<NV, 2>& raw, int g) {
+    const char* const rows[2] = {trow_of(g), drow_of(g)};
+    issue_rows<DT, NV, 2>(raw, rows, vbeg, a.sp, is_pair(g) ? 2 : 1);
+  };
+
+  RawChunk<NV, 2> raw;
+  issue(raw, sg * 8 + xcd);
+
+  for (int i = 0; i < nl; ++i) {
+    const int g = (sg + i * a.sgroups) * 8 + xcd;
+    const bool pair = is_pair(g);
+    float x[2][NE];
+    {
+      const char* const rows[2] = {trow_of(g), drow_of(g)};
+      unpack_rows<DT, NV, 2>(raw, rows, vbeg, vend, a.sp, a.V, x, pair ? 2 : 1);
+    }
+    if (i + 1 < nl) issue(raw, (sg + (i + 1) * a.sgroups) * 8 + xcd);   // prefetch the next layer
+
+    // ---- pass 1: chunk log-sum-exp partials, published as one record -------
+    Lse parts[2] = {thread_lse<NE, true>(x[0]), lse_empty()};
+    const float ref_a = parts[0].ref;
+    float ref_b = 0.f;
+    if (pair) {
+      parts[1] = thread_lse<NE, false>(x[1]);
+      ref_b = parts[1].ref;
+    }
+    block_lse<2>(parts, lds);
+    uint64_t* p1 = a.part1 + (int64_t)g * C * 3;
+    if (threadIdx.x == 0) put_p1(p1 + (int64_t)c * 3, parts[0], parts[1]);
+    const RowLse L = merge_group(p1, C, pair, lds, a.err);
+
+    // ---- pass 2: segment masses from registers -------------------------------
+    const float sa = fast_exp2(ref_a - L.lse2_p);
+    const float sb = pair ? fast_exp2(ref_b - L.lse2_q) : 0.f;
+    float segm[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < PV; ++e) {
+        const int idx = j * PV + e;
+        acc += pair ? residual_of(x[0][idx], sa, x[1][idx], sb) : x[0][idx] * sa;
+      }
+      segm[j] = wave_sum(acc);
+    }
+    if (lane == 0) {
+      float* seg = a.seg + ((int64_t)g * C + c) * NSEG;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) st_coherent(seg + j * kWaves + wave, segm[j]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// verify_finish: one workgroup per sequence, wave k handles row (b, k).
+
+// Inverse CDF of one segment held by a wave (PV values per lane, vocabulary order
+// lane-major): smallest index whose running mass exceeds t; if none, the last
+// index with positive mass; -1 if the segment has no mass.
+template <int PV>
+__device__ __forceinline__ int wave_inverse_cdf(const float (&v)[PV], float t) {
   const int lane = threadIdx.x & 63;
-  const int K = (C + 63) / 64;
-  const int c0 = lane * K, c1 = min(C, c0 + K);
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < PV; ++e) s += v[e];
+  float incl = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float n = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += n;
+  }
+  const float ex = __shfl_up(incl, 1, 64);
+  float cum = lane == 0 ? 0.f : ex;
+  int best = 0x7fffffff, lastpos = -1;
+#pragma unroll
+  for (int e = 0; e < PV; ++e) {
+    if (v[e] > 0.f) {
+      cum += v[e];
+      const int idx = lane * PV + e;
+      if (best == 0x7fffffff && cum > t) best = idx;
+      lastpos = idx;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    best = min(best, __shfl_xor(best, o, 64));
+    lastpos = max(lastpos, __shfl_xor(lastpos, o, 64));
+  }
+  return best != 0x7fffffff ? best : lastpos;
+}
+
+// Scan of masses m(0..n-1) in order: lane l owns [l*K, l*K + K).  Returns the
+// total, the first index whose running mass exceeds u' * total (else the last
+// index with mass, with start = -inf) and the mass before it.  Every lane of the
+// wave gets the same result.
+struct Scan {
+  float total;
+  int owner;
+  float start;
+};
+
+template <typename MassFn>
+__device__ __forceinline__ Scan wave_scan_owner(int n, float u_prime, MassFn mass) {
+  const int lane = threadIdx.x & 63;
+  const int K = (n + 63) / 64;
+  const int c0 = lane * K, c1 = min(n, c0 + K);
   float block = 0.f;
   int last_pos = -1;
   for (int c = c0; c < c1; ++c) {
@@ -92,364 +262,220 @@ __device__ __forceinline__ ChunkScan scan_chunks(int C, float u_prime, MassFn ma
     block += m;
     if (m > 0.f) last_pos = c;
   }
-  // inclusive scan over lanes (Hillis-Steele), deterministic
   float incl = block;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const float n = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += n;
+    const float v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
   }
-  const float excl_lane = __shfl_up(incl, 1, 64);
-  const float excl = lane == 0 ? 0.f : excl_lane;
-  ChunkScan r;
+  const float ex = __shfl_up(incl, 1, 64);
+  const float excl = lane == 0 ? 0.f : ex;
+  Scan r;
   r.total = __shfl(incl, 63, 64);
   const float t = u_prime * r.total;
+  r.owner = -1;
+  r.start = kNegInf;
   const uint64_t hit = __ballot(c0 < c1 && incl > t);
   if (hit != 0ull && r.total > 0.f) {
     const int l = __builtin_ctzll(hit);
-    // walk the winning lane's chunks, accumulating in the same order
-    const float lane_start = __shfl(excl, l, 64);
-    float run = lane_start;
-    int owner = -1;
-    float start = lane_start;
-    const int a0 = l * K, a1 = min(C, a0 + K);
+    float run = __shfl(excl, l, 64);
+    const int a0 = l * K, a1 = min(n, a0 + K);
     for (int c = a0; c < a1; ++c) {
       const float m = mass(c);
-      const float nxt = run + m;
-      if (owner < 0 && nxt > t) { owner = c; start = run; }
-      run = nxt;
+      if (r.owner < 0 && run + m > t) { r.owner = c; r.start = run; }
+      run += m;
     }
-    r.owner = owner;
-    r.start = start;
-    if (owner < 0) {   // rounding: the lane's last chunk with mass, from its end
-      int lastc = a0;
-      for (int c = a0; c < a1; ++c)
-        if (mass(c) > 0.f) lastc = c;
-      r.owner = lastc;
-      r.start = kNegInf;
-    }
-  } else {
-    // rounding left t past every boundary (or no mass): last chunk with mass
+  }
+  if (r.owner < 0) {   // rounding left t past every boundary: last index with mass
     const uint64_t pos = __ballot(last_pos >= 0);
-    if (pos != 0ull) {
-      const int l = 63 - __builtin_clzll(pos);
-      r.owner = __shfl(last_pos, l, 64);
-    } else {
-      r.owner = 0;
-    }
-    r.start = kNegInf;   // t_local = +inf: the owner takes its last positive element
+    r.owner = pos ? __shfl(last_pos, 63 - __builtin_clzll(pos), 64) : 0;
+    r.start = kNegInf;  // t - start = +inf: the owner takes its last positive element
   }
   return r;
-}
-
-// Inverse CDF inside the owner chunk: smallest local index whose running mass
-// exceeds t_local; if none, the last index with positive mass; -1 if no mass.
-// v holds this thread's NV*PV masses in (j, e) order.
-template <int NV, int PV>
-__device__ __forceinline__ int chunk_inverse_cdf(const float (&v)[NV * PV], float t_local, float* lds) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float s[NV];
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    float acc = 0.f;
-#pragma unroll
-    for (int e = 0; e < PV; ++e) acc += v[j * PV + e];
-    s[j] = acc;
-  }
-  // exclusive scan over threads, per iteration j
-  float incl[NV];
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    incl[j] = s[j];
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float n = __shfl_up(incl[j], o, 64);
-      if (lane >= o) incl[j] += n;
-    }
-  }
-  __syncthreads();
-  if (lane == 63) {
-#pragma unroll
-    for (int j = 0; j < NV; ++j) lds[j * kWaves + wave] = incl[j];
-  }
-  __syncthreads();
-  float off = 0.f;
-  int best = 0x7fffffff, lastpos = -1;
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const float* wt = lds + j * kWaves;
-    float woff = 0.f;
-    for (int w = 0; w < wave; ++w) woff += wt[w];
-    const float ex_lane = __shfl_up(incl[j], 1, 64);
-    const float start = off + (woff + (lane == 0 ? 0.f : ex_lane));
-    float cum = start;
-#pragma unroll
-    for (int e = 0; e < PV; ++e) {
-      const float val = v[j * PV + e];
-      if (val > 0.f) {
-        cum += val;
-        const int idx = (j * kBlock + tid) * PV + e;
-        if (best == 0x7fffffff && cum > t_local) best = idx;
-        lastpos = idx;
-      }
-    }
-    off += (wt[0] + wt[1]) + (wt[2] + wt[3]);
-  }
-  // block min of best, block max of lastpos
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    best = min(best, __shfl_xor(best, o, 64));
-    lastpos = max(lastpos, __shfl_xor(lastpos, o, 64));
-  }
-  __syncthreads();
-  int* li = reinterpret_cast<int*>(lds);
-  if (lane == 0) { li[wave] = best; li[kWaves + wave] = lastpos; }
-  __syncthreads();
-  best = min(min(li[0], li[1]), min(li[2], li[3]));
-  lastpos = max(max(li[4], li[5]), max(li[6], li[7]));
-  return best != 0x7fffffff ? best : lastpos;
-}
-
-// Workspace record per row, read by the sequence finaliser.
-struct RowRec { int flag; int token; };
-
-// Row statistics every workgroup of a group derives from the chunk partials.
-struct RowLse {
-  Lse p, q;
-  float lse2_p, lse2_q;
-  bool bad_p, bad_q;
-};
-
-// Wave 0 merges the C chunk partials (coherent loads) in a fixed order; the
-// result is broadcast through LDS.  Identical in every workgroup of the group.
-__device__ __forceinline__ RowLse merge_group(const float* p1, int C, bool pair, float* lds) {
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    Lse ap = lse_empty(), aq = lse_empty();
-    for (int c = lane; c < C; c += 64) {
-      const float* q = p1 + (int64_t)c * 8;
-      ap = lse_merge(ap, Lse{ld_coherent(q), ld_coherent(q + 1), ld_coherent(q + 2)});
-      if (pair) aq = lse_merge(aq, Lse{ld_coherent(q + 3), ld_coherent(q + 4), 0.f});
-    }
-    ap = wave_lse(ap);
-    aq = wave_lse(aq);
-    if (lane == 0) {
-      lds[0] = ap.ref; lds[1] = ap.z; lds[2] = ap.y;
-      lds[3] = aq.ref; lds[4] = aq.z; lds[5] = aq.y;
-    }
-  }
-  __syncthreads();
-  RowLse r;
-  r.p = Lse{lds[0], lds[1], lds[2]};
-  r.q = Lse{lds[3], lds[4], lds[5]};
-  __syncthreads();
-  r.lse2_p = lse_log2(r.p);
-  r.bad_p = !(__builtin_isfinite(r.lse2_p));
-  r.lse2_q = pair ? lse_log2(r.q) : 0.f;
-  r.bad_q = pair && !(__builtin_isfinite(r.lse2_q));
-  return r;
-}
-
-// The sequence finaliser: every row's finisher records (flag, token) and arrives
-// on the sequence counter; the last of the gamma+1 writes n_b and the next token,
-// then clears the records and the counter.  Called by one thread.
-__device__ __forceinline__ void finish_row(const VerifyArgs& a, int b, int g, int flag, int token) {
-  const int G = a.G, G1 = G + 1;
-  int* rec = a.rec;
-  st_coherent(rec + 2 * g, flag);
-  st_coherent(rec + 2 * g + 1, token);
-  int* scnt = a.seq_cnt + (int64_t)b * kCounterStride;
-  const int old = arrive(scnt);
-  if (old == G) {
-    int n = 0;
-    while (n < G && ld_coherent(rec + 2 * (b * G1 + n)) == 1) ++n;
-    a.accepted_len[b] = n;
-    a.next_token[b] = ld_coherent(rec + 2 * (b * G1 + n) + 1);
-    for (int k = 0; k < G1; ++k) {
-      st_coherent(rec + 2 * (b * G1 + k), 0);
-      st_coherent(rec + 2 * (b * G1 + k) + 1, 0);
-    }
-    reset_counter(scnt);
-  }
 }
 
 template <int DT, int NV>
-__global__ __launch_bounds__(kBlock) void verify_kernel(VerifyArgs a) {
+__global__ void verify_finish(VerifyArgs a) {
   constexpr int PV = Elem<DT>::kPerVec;
-  constexpr int NE = NV * PV;
+  constexpr int NSEG = NV * kWaves;
   const int C = a.sp.nchunks;
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7, slot = bid >> 3;
-  const int lg = slot / C, c = slot - lg * C;
-  const int g = lg * 8 + xcd;
-  if (g >= a.ngroups) return;
   const int G = a.G, G1 = G + 1;
-  const int b = g / G1, k = g - b * G1;
+  const int b = blockIdx.x;
+  const int k = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = b * G1 + k;
   const bool pair = k < G;
+  __shared__ int flag_sh[kMaxRowsPerSeq], token_sh[kMaxRowsPerSeq];
 
-  __shared__ float lds[64];
-  __shared__ int flag_sh;
-
-  float xa[NE], xb[NE];
   const char* trow = reinterpret_cast<const char*>(a.target) + (int64_t)g * a.t_stride * Elem<DT>::kBytes;
-  const char* drow = reinterpret_cast<const char*>(a.draft) + (int64_t)(b * G + k) * a.d_stride * Elem<DT>::kBytes;
-  {
-    const int64_t vbeg = (int64_t)c * a.sp.vec_per_chunk;
-    const int64_t vend = min(vbeg + a.sp.vec_per_chunk, a.sp.nvec);
-    load_chunk<DT, NV>(trow, vbeg, vend, a.sp, a.V, xa);
-    if (pair) load_chunk<DT, NV>(drow, vbeg, vend, a.sp, a.V, xb);
-  }
+  const char* drow = reinterpret_cast<const char*>(a.draft) + (int64_t)(b * G + (pair ? k : 0)) * a.d_stride * Elem<DT>::kBytes;
+  uint64_t* p1 = a.part1 + (int64_t)g * C * 3;
+  const float* seg = a.seg + (int64_t)g * C * NSEG;
 
-  // ---- pass 1: chunk log-sum-exp partials ----------------------------------
-  Lse parts[2] = {thread_lse<NE, true>(xa), lse_empty()};
-  const float ref_a = parts[0].ref;
-  float ref_b = 0.f;
-  if (pair) {
-    parts[1] = thread_lse<NE, false>(xb);
-    ref_b = parts[1].ref;
+  // ---- row statistics from the pass-1 records ---------------------------------
+  Lse ap = lse_empty(), aq = lse_empty();
+  for (int c = lane; c < C; c += 64) {
+    const uint64_t w[3] = {get_word(p1 + (int64_t)c * 3), get_word(p1 + (int64_t)c * 3 + 1),
+                           get_word(p1 + (int64_t)c * 3 + 2)};
+    ap = lse_merge(ap, rec_p(w));
+    if (pair) aq = lse_merge(aq, rec_q(w));
   }
-  block_lse<2>(parts, lds);
-  float* p1 = a.part1 + (int64_t)g * C * 8;
-  float* p2 = a.part2 + (int64_t)g * C * 2;
-  int* cnt = a.grp_cnt + (int64_t)g * kCounterStride;
-  if (threadIdx.x == 0) {
-    float* mine = p1 + (int64_t)c * 8;
-    st_coherent(mine + 0, parts[0].ref); st_coherent(mine + 1, parts[0].z); st_coherent(mine + 2, parts[0].y);
-    st_coherent(mine + 3, parts[1].ref); st_coherent(mine + 4, parts[1].z);
-    arrive(cnt);
-  }
-  block_wait(cnt, C, a.err);
-  const RowLse L = merge_group(p1, C, pair, lds);
-  const bool bad = L.bad_p || (pair && L.bad_q);
-  const float sa = fast_exp2(ref_a - L.lse2_p);            // p_i = xa[i] * sa
-  const float sb = pair ? fast_exp2(ref_b - L.lse2_q) : 0.f;
+  ap = wave_lse(ap);
+  aq = wave_lse(aq);
+  const float lse2_p = lse_log2(ap);
+  const float lse2_q = pair ? lse_log2(aq) : 0.f;
+  const bool bad_p = !(__builtin_isfinite(lse2_p));
+  const bool bad_q = pair && !(__builtin_isfinite(lse2_q));
+  const bool bad = bad_p || bad_q;
   float u, up;
   row_uniforms(a.seed, a.offset, (uint64_t)g, &u, &up);
-  auto pmass = [&](int cc) {                                // target mass of chunk cc
-    const float* q = p1 + (int64_t)cc * 8;
-    const float z = ld_coherent(q + 1);
-    return z > 0.f ? z * fast_exp2(ld_coherent(q) - L.lse2_p) : 0.f;
+
+  auto pmass = [&](int c) {   // mass of p in chunk c, from its record
+    const uint64_t w = get_word(p1 + (int64_t)c * 3);
+    const float z = unmark(unpack_hi(w));
+    return z > 0.f ? z * fast_exp2(unpack_lo(w) - lse2_p) : 0.f;
+  };
+  auto chunk_seg_mass = [&](int c) {
+    const float* s = seg + (int64_t)c * NSEG;
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < NSEG; ++i) m += ld_coherent(s + i);
+    return m;
   };
 
-  ChunkScan sc;
-  float alpha_tot = 0.f, r_tot = 0.f;
+  float alpha = 0.f;
   bool empty_res = false;
-  if (pair) {
-    // ---- pass 2: overlap and residual mass from registers -----------------
-    float acc[2] = {0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < NE; ++i) {
-      float p, mn, r;
-      pq_residual(xa[i], sa, xb[i], sb, &p, &mn, &r);
-      acc[0] += mn;
-      acc[1] += r;
+  Scan sc{0.f, 0, 0.f};
+  if (!bad) {
+    sc = wave_scan_owner(C, up, chunk_seg_mass);
+    if (pair) {
+      float pm = 0.f;
+      for (int c = lane; c < C; c += 64) pm += pmass(c);
+      alpha = wave_sum(pm) - sc.total;
+      if (!(sc.total > 0.f)) {   // the residual has no mass: sample from p
+        empty_res = true;
+        sc = wave_scan_owner(C, up, pmass);
+      }
     }
-    block_sum<2>(acc, lds);
-    if (threadIdx.x == 0) {
-      st_coherent(p2 + 2 * c, acc[0]);
-      st_coherent(p2 + 2 * c + 1, acc[1]);
-      flag_sh = arrive(cnt) == 2 * C - 1;
-    }
-    __syncthreads();
-    if (!flag_sh) return;
-    // ---- the last workgroup of the group finishes the row ------------------
-    const int lane = threadIdx.x & 63;
-    float al = 0.f;
-    for (int cc = lane; cc < C; cc += 64) al += ld_coherent(p2 + 2 * cc);
-    alpha_tot = wave_sum(al);
-    sc = scan_chunks(C, up, [&](int cc) { return ld_coherent(p2 + 2 * cc + 1); });
-    r_tot = sc.total;
-    if (!(r_tot > 0.f) && !bad) {
-      empty_res = true;
-      sc = scan_chunks(C, up, pmass);
-    }
-  } else {
-    sc = scan_chunks(C, up, pmass);
-    // departure: the last workgroup to leave clears the group's partials
-    if (threadIdx.x == 0) flag_sh = arrive(cnt) == 2 * C - 1;
-    __syncthreads();
-    if (flag_sh) {
-      block_zero(p1, (int64_t)C * 8);
-      if (threadIdx.x == 0) reset_counter(cnt);
-    }
-    if (bad) sc.owner = 0;
-    if (c != sc.owner) return;
   }
-  if (bad) sc.owner = 0;
+  const float r_tot = pair && !empty_res ? sc.total : 0.f;
 
-  // ---- inverse CDF inside the owner chunk -----------------------------------
+  // ---- owner segment inside the owner chunk, then the inverse CDF in it ------
   int token = -1;
   if (!bad) {
     const int oc = sc.owner;
     const int64_t obeg = (int64_t)oc * a.sp.vec_per_chunk;
-    if (pair && oc != c) {
-      // the owner chunk is another workgroup's: read it again and recompute the
-      // same per-thread values that workgroup summed
-      const int64_t oend = min(obeg + a.sp.vec_per_chunk, a.sp.nvec);
-      load_chunk<DT, NV>(trow, obeg, oend, a.sp, a.V, xa);
-      load_chunk<DT, NV>(drow, obeg, oend, a.sp, a.V, xb);
-      const Lse ta = thread_lse<NE, true>(xa);
-      const Lse tb = thread_lse<NE, false>(xb);
-      const float sa2 = fast_exp2(ta.ref - L.lse2_p), sb2 = fast_exp2(tb.ref - L.lse2_q);
+    const int64_t oend = min(obeg + a.sp.vec_per_chunk, a.sp.nvec);
+    // this lane's values in segment s (p, or max(0, p - q) for a non-empty residual)
+    auto seg_values = [&](int s, float (&v)[PV]) {
+      const int j = s / kWaves, w = s - j * kWaves;
+      const int64_t vi = obeg + (int64_t)j * kBlock + w * 64 + lane;
 #pragma unroll
-      for (int i = 0; i < NE; ++i) {
-        float p, mn, r;
-        pq_residual(xa[i], sa2, xb[i], sb2, &p, &mn, &r);
-        xa[i] = empty_res ? p : r;
+      for (int e = 0; e < PV; ++e) {
+        const int64_t idx = vi * PV + e;
+        float xa = kNegInf, xb = kNegInf;
+        if (vi < oend && idx < a.V) {
+          xa = load_one<DT>(trow, idx);
+          if (pair && !empty_res) xb = load_one<DT>(drow, idx);
+        }
+        const float p = fast_exp2(__builtin_fmaf(xa, kLog2e, -lse2_p));
+        if (pair && !empty_res) {
+          const float q = fast_exp2(__builtin_fmaf(xb, kLog2e, -lse2_q));
+          v[e] = fmaxf(p - q, 0.f);
+        } else {
+          v[e] = p;
+        }
       }
-    } else if (pair) {
+    };
+    const float tl = up * sc.total - sc.start;
+    int os = -1;
+    float seg_start = kNegInf;
+    if (empty_res) {
+      // segment masses of p are not recorded for a pair row: measure them (rare)
+      float run = 0.f;
+      for (int s = 0; s < NSEG && os < 0; ++s) {
+        float v[PV];
+        seg_values(s, v);
+        float m = 0.f;
 #pragma unroll
-      for (int i = 0; i < NE; ++i) {
-        float p, mn, r;
-        pq_residual(xa[i], sa, xb[i], sb, &p, &mn, &r);
-        xa[i] = empty_res ? p : r;
+        for (int e = 0; e < PV; ++e) m += v[e];
+        m = wave_sum(m);
+        if (run + m > tl) { os = s; seg_start = run; }
+        run += m;
       }
+      if (os < 0) os = NSEG - 1;
     } else {
-#pragma unroll
-      for (int i = 0; i < NE; ++i) xa[i] *= sa;
+      const float* s = seg + (int64_t)oc * NSEG;
+      float run = 0.f;
+      int lastpos = 0;
+      for (int i = 0; i < NSEG; ++i) {
+        const float m = ld_coherent(s + i);
+        if (m > 0.f) lastpos = i;
+        if (os < 0 && run + m > tl) { os = i; seg_start = run; }
+        run += m;
+      }
+      if (os < 0) os = lastpos;
     }
-    const float t_local = up * sc.total - sc.start;
-    const int loc = chunk_inverse_cdf<NV, PV>(xa, t_local, lds);
-    token = loc >= 0 ? (int)(obeg * PV + loc) : -1;
+    float v[PV];
+    seg_values(os, v);
+    const int loc = wave_inverse_cdf<PV>(v, tl - seg_start);
+    if (loc >= 0) {
+      const int j = os / kWaves, w = os - j * kWaves;
+      token = (int)((obeg + (int64_t)j * kBlock + w * 64) * PV + loc);
+    }
   }
-  if (pair) {   // the finishing workgroup clears the group's partials
-    block_zero(p1, (int64_t)C * 8);
-    block_zero(p2, (int64_t)C * 2);
-  }
-  if (threadIdx.x != 0) return;
-  if (pair) reset_counter(cnt);
 
-  int status = 0;
-  if (L.bad_p) status |= kRowBadTarget;
-  if (pair && L.bad_q) status |= kRowBadDraft;
-  if (empty_res) status |= kRowResidualEmpty;
-  int flag = 0;
-  const float nan = __builtin_nanf("");
-  if (pair) {
-    const int y = a.tokens[b * G + k];
-    if (y < 0 || y >= a.V) {
-      status |= kRowBadToken;
-    } else if (!bad) {
-      const float ay = load_one<DT>(trow, y), by = load_one<DT>(drow, y);
-      const float d = __builtin_fmaf(ay, kLog2e, -L.lse2_p) - __builtin_fmaf(by, kLog2e, -L.lse2_q);
-      if (d == d) flag = u < fminf(1.f, fast_exp2(d)) ? 1 : 0;
-    }
-    a.accept[b * G + k] = (uint8_t)flag;
-    if (a.overlap) a.overlap[b * G + k] = bad ? nan : alpha_tot;
-    if (a.tv) a.tv[b * G + k] = bad ? nan : r_tot;
+  // clear this row's records and segment masses for the next call (the wave has
+  // read them all): a call leaves every workspace word it wrote at zero
+  for (int c = lane; c < C; c += 64) {
+    put_word(p1 + (int64_t)c * 3, 0ull);
+    put_word(p1 + (int64_t)c * 3 + 1, 0ull);
+    put_word(p1 + (int64_t)c * 3 + 2, 0ull);
   }
-  if (a.entropy) a.entropy[g] = L.bad_p ? nan : kLn2 * (fast_log2(L.p.z) - L.p.y / L.p.z);
-  if (a.row_token) a.row_token[g] = token;
-  if (a.row_status) a.row_status[g] = status;
-  finish_row(a, b, g, flag, token);
+  for (int64_t i = lane; i < (int64_t)C * NSEG; i += 64) st_coherent(const_cast<float*>(seg) + i, 0.f);
+
+  if (lane == 0) {
+    int status = 0;
+    if (bad_p) status |= kRowBadTarget;
+    if (bad_q) status |= kRowBadDraft;
+    if (empty_res) status |= kRowResidualEmpty;
+    int flag = 0;
+    const float nan = __builtin_nanf("");
+    if (pair) {
+      const int y = a.tokens[b * G + k];
+      if (y < 0 || y >= a.V) {
+        status |= kRowBadToken;
+      } else if (!bad) {
+        const float ay = load_one<DT>(trow, y), by = load_one<DT>(drow, y);
+        const float d = __builtin_fmaf(ay, kLog2e, -lse2_p) - __builtin_fmaf(by, kLog2e, -lse2_q);
+        if (d == d) flag = u < fminf(1.f, fast_exp2(d)) ? 1 : 0;
+      }
+      a.accept[b * G + k] = (uint8_t)flag;
+      if (a.overlap) a.overlap[b * G + k] = bad ? nan : alpha;
+      if (a.tv) a.tv[b * G + k] = bad ? nan : r_tot;
+    }
+    if (a.entropy) a.entropy[g] = bad_p ? nan : kLn2 * (fast_log2(ap.z) - ap.y / ap.z);
+    if (a.row_token) a.row_token[g] = token;
+    if (a.row_status) a.row_status[g] = status;
+    flag_sh[k] = flag;
+    token_sh[k] = token;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int n = 0;
+    while (n < G && flag_sh[n] == 1) ++n;
+    a.accepted_len[b] = n;
+    a.next_token[b] = token_sh[n];
+  }
 }
 
+// ---------------------------------------------------------------------------
 template <int DT, int NV>
 static hipError_t launch(const VerifyArgs& a, hipStream_t stream) {
-  const int C = a.sp.nchunks;
-  const int64_t per_xcd = (a.ngroups + 7) / 8;
-  const int64_t grid = per_xcd * C * 8;
-  hipLaunchKernelGGL((verify_kernel<DT, NV>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
+  const int64_t grid = (int64_t)a.sgroups * a.sp.nchunks * 8;
+  hipLaunchKernelGGL((verify_main<DT, NV>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((verify_finish<DT, NV>), dim3((unsigned)a.B), dim3(64 * (a.G + 1)), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -462,8 +488,8 @@ hipError_t launch_verify(const VerifyArgs& a, int dt, hipStream_t stream) {
 
 hipError_t verify_occupancy(int dt, int* blocks_per_cu) {
   if (dt == kBF16)
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, verify_kernel<kBF16, kVerifyNVBf16>, kBlock, 0);
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, verify_kernel<kF32, kVerifyNVF32>, kBlock, 0);
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, verify_main<kBF16, kVerifyNVBf16>, kBlock, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, verify_main<kF32, kVerifyNVF32>, kBlock, 0);
 }
 
 }  // namespace mtp
