@@ -42,6 +42,14 @@ def verify_bytes(B, G, V, elem):
     return logits, logits + small
 
 
+def check_waits(mtp, ws):
+    """Stop if a bounded cluster wait timed out (the kernels set the workspace's
+    error word): the timings of such a run would mean nothing."""
+    word = mtp.workspace_error(ws)
+    if word:
+        sys.exit(f"bench: a cluster wait timed out (workspace error word {word:#x})")
+
+
 def time_verify(mtp, torch, w, steps, warmup, nsets):
     import synthetic
     dev = "cuda:0"
@@ -52,9 +60,12 @@ def time_verify(mtp, torch, w, steps, warmup, nsets):
         plans.append(mtp.VerifyPlan(t, d, y))
     torch.cuda.synchronize()
     rows = B * (G + 1)
+    plans[0].run(seed=w["seed"], offset=0)
+    check_waits(mtp, plans[0].ws)
     for i in range(warmup):
         plans[i % nsets].run(seed=w["seed"], offset=i * rows)
     torch.cuda.synchronize()
+    check_waits(mtp, plans[0].ws)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
@@ -72,6 +83,7 @@ def time_tv(mtp, torch, w, steps, warmup):
     dev = "cuda:0"
     t, d = synthetic.tv_inputs(w, dev)
     plan = mtp.TVPlan(t, d, grad_dtype=torch.bfloat16)
+    check_waits(mtp, plan.ws)
     for _ in range(warmup):
         plan.forward()
         plan.backward()

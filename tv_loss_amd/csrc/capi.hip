@@ -87,7 +87,7 @@ mtp_status cluster_capacity(int kernel, int dt, int G, int shared, int64_t* per_
 
 // ---- workspace layouts --------------------------------------------------------
 struct VerifyLayout {
-  size_t err, part1, seg, total;
+  size_t err, part1, part2, total;
   mtp::RowSplit sp;
   int64_t ngroups;
 };
@@ -97,11 +97,10 @@ VerifyLayout verify_layout(int32_t B, int32_t G, int32_t V, mtp_dtype dt) {
   L.sp = mtp::make_split(V, per_vec(dt), mtp::verify_vec_per_thread(dt));
   L.ngroups = (int64_t)B * (G + 1);
   const int64_t C = L.sp.nchunks;
-  const int64_t nseg = (int64_t)mtp::verify_vec_per_thread(dt) * mtp::kWaves;
   size_t off = 0;
   L.err = off; off = align256(off + 4);
   L.part1 = off; off = align256(off + (size_t)L.ngroups * C * 3 * 8);
-  L.seg = off; off = align256(off + (size_t)L.ngroups * C * nseg * 4);
+  L.part2 = off; off = align256(off + (size_t)L.ngroups * C * mtp::kWaves * 8);
   L.total = off;
   return L;
 }
@@ -221,7 +220,7 @@ mtp_status mtp_verify(const void* target, int64_t target_row_stride, const void*
   a.row_token = row_token; a.overlap = overlap; a.tv = tv; a.entropy = entropy; a.row_status = row_status;
   a.err = at<uint32_t>(workspace, L.err);
   a.part1 = at<uint64_t>(workspace, L.part1);
-  a.seg = at<float>(workspace, L.seg);
+  a.part2 = at<uint64_t>(workspace, L.part2);
   a.sp = L.sp;
   a.ngroups = (int)L.ngroups;
   a.sgroups = sgroups;

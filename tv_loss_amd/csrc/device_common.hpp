@@ -370,6 +370,229 @@ __device__ __forceinline__ void block_zero(float* p, int64_t n) {
 }
 
 // ---------------------------------------------------------------------------
+// Wave reductions with DPP (gfx9): prefix steps row_shr:1,2,4,8 inside each row of
+// 16 lanes, then row_bcast:15 and row_bcast:31 carry the row totals up, so lane 63
+// ends with the total; readlane hands its bits to every lane.  The order of the
+// operations is fixed, so equal inputs give equal bits in every kernel.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_mov(float old, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), kCtrl, kRowMask, 0xf, false));
+}
+__device__ __forceinline__ float lane63(float v) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63)); }
+
+__device__ __forceinline__ float wave_total(float v) {
+  v += dpp_mov<0x111, 0xf>(0.f, v);
+  v += dpp_mov<0x112, 0xf>(0.f, v);
+  v += dpp_mov<0x114, 0xf>(0.f, v);
+  v += dpp_mov<0x118, 0xf>(0.f, v);
+  v += dpp_mov<0x142, 0xa>(0.f, v);
+  v += dpp_mov<0x143, 0xc>(0.f, v);
+  return lane63(v);
+}
+
+// NaN-propagating maximum (IEEE maximum: no canonicalisation of the operands).
+__device__ __forceinline__ float fmaximum(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+__device__ __forceinline__ float wave_maximum(float v) {
+  v = fmaximum(v, dpp_mov<0x111, 0xf>(kNegInf, v));
+  v = fmaximum(v, dpp_mov<0x112, 0xf>(kNegInf, v));
+  v = fmaximum(v, dpp_mov<0x114, 0xf>(kNegInf, v));
+  v = fmaximum(v, dpp_mov<0x118, 0xf>(kNegInf, v));
+  v = fmaximum(v, dpp_mov<0x142, 0xa>(kNegInf, v));
+  v = fmaximum(v, dpp_mov<0x143, 0xc>(kNegInf, v));
+  return lane63(v);
+}
+
+__device__ __forceinline__ Lse lse_nan() {
+  const float nan = __builtin_nanf("");
+  return Lse{nan, nan, nan};
+}
+
+// Log-sum-exp partial of one row over a wave: the wave's largest logit M is the
+// reference (ref = M log2 e), x is overwritten with e = 2^(x log2 e - ref) and the
+// sums of e (and of e * (x log2 e - ref) with kY) are taken over the wave.  A wave
+// holding only -inf gives the empty partial (and e = 0); a NaN gives a NaN partial.
+// The entropy moment is accumulated without guarding 0 * (-inf); if that produced
+// a NaN it is summed again from the e values alone (e log2 e, e > 0).
+template <int NE, bool kY>
+__device__ __forceinline__ Lse wave_pass1(float (&x)[NE]) {
+  float m = x[0];
+#pragma unroll
+  for (int i = 1; i < NE; ++i) m = fmaximum(m, x[i]);
+  const float M = wave_maximum(m);
+  if (M != M) {
+#pragma unroll
+    for (int i = 0; i < NE; ++i) x[i] = 0.f;
+    return lse_nan();
+  }
+  if (!(M > kNegInf)) {
+#pragma unroll
+    for (int i = 0; i < NE; ++i) x[i] = 0.f;
+    return lse_empty();
+  }
+  const float ref = M * kLog2e;
+  float z = 0.f, y = 0.f;
+#pragma unroll
+  for (int i = 0; i < NE; ++i) {
+    const float t = __builtin_fmaf(x[i], kLog2e, -ref);
+    const float e = fast_exp2(t);
+    z += e;
+    if constexpr (kY) y = __builtin_fmaf(e, t, y);
+    x[i] = e;
+  }
+  const float Z = wave_total(z);
+  float Y = 0.f;
+  if constexpr (kY) {
+    Y = wave_total(y);
+    if (Y != Y && Z == Z) {
+      y = 0.f;
+#pragma unroll
+      for (int i = 0; i < NE; ++i)
+        if (x[i] > 0.f) y = __builtin_fmaf(x[i], fast_log2(x[i]), y);
+      Y = wave_total(y);
+    }
+  }
+  return Lse{ref, Z, Y};
+}
+
+// Merge of per-lane partials (lanes without one hold the empty partial) into one,
+// the same bits in every lane.  kY: also merge the entropy moment.
+template <bool kY>
+__device__ __forceinline__ Lse wave_merge(const Lse& s) {
+  const bool nan = s.z != s.z || s.ref != s.ref || (kY && s.y != s.y);
+  if (__ballot(nan) != 0ull) return lse_nan();
+  const bool live = s.z > 0.f;
+  const float R = wave_maximum(live ? s.ref : kNegInf);
+  if (!(R > kNegInf)) return lse_empty();
+  const float d = live ? s.ref - R : 0.f;
+  const float f = fast_exp2(d);
+  const float z = live ? s.z * f : 0.f;
+  float Y = 0.f;
+  if constexpr (kY) Y = wave_total(live ? __builtin_fmaf(d, s.z, s.y) * f : 0.f);
+  return Lse{R, wave_total(z), Y};
+}
+
+// Merge of N partials held in LDS (stride 3 floats), computed alike in every lane.
+template <int N, bool kY>
+__device__ __forceinline__ Lse merge_lds(const float* p) {
+  bool nan = false;
+  float R = kNegInf;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float ref = p[3 * i], z = p[3 * i + 1], y = p[3 * i + 2];
+    nan = nan || z != z || ref != ref || (kY && y != y);
+    if (z > 0.f) R = fmaxf(R, ref);
+  }
+  if (nan) return lse_nan();
+  if (!(R > kNegInf)) return lse_empty();
+  float Z = 0.f, Y = 0.f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float ref = p[3 * i], z = p[3 * i + 1], y = p[3 * i + 2];
+    if (z > 0.f) {
+      const float d = ref - R;
+      const float f = fast_exp2(d);
+      Z = __builtin_fmaf(z, f, Z);
+      if constexpr (kY) Y = __builtin_fmaf(__builtin_fmaf(d, z, y), f, Y);
+    }
+  }
+  return Lse{R, Z, Y};
+}
+
+// ---------------------------------------------------------------------------
+// Wave-segment streaming.  A chunk is split into kWaves contiguous segments of
+// NV*64 vectors, one per wave; lane l of a wave holds vectors s0 + j*64 + l
+// (j < NV), so each load instruction reads 1 KB contiguous per wave.
+// issue_seg() puts all loads in flight at once (addresses clamped into the row);
+// unpack_seg() widens them: when `full` (wave-uniform) every vector lies inside the
+// chunk and the row; otherwise vectors at or past `lim` read as -inf and the row's
+// partial last vector (index `tail`, if tail < `cend`) is read element by element.
+template <int DT, int NV, int R>
+__device__ __forceinline__ void issue_seg(RawChunk<NV, R>& raw, const char* const (&rows)[R], int64_t v0,
+                                          int64_t last, int nrows = R) {
+  if (last >= 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (r >= nrows) break;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int64_t vi = min(v0 + (int64_t)j * 64, last);
+        raw.v[r][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rows[r]) + vi);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int j = 0; j < NV; ++j) raw.v[r][j] = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+template <int DT, int NV, int R>
+__device__ __forceinline__ void unpack_seg(const RawChunk<NV, R>& raw, const char* const (&rows)[R], int64_t v0,
+                                           bool full, int64_t lim, int64_t tail, int64_t cend, int64_t V,
+                                           float (&x)[R][NV * Elem<DT>::kPerVec], int nrows = R) {
+  constexpr int PV = Elem<DT>::kPerVec;
+  constexpr uint32_t kMasked = DT == kBF16 ? 0xFF80FF80u : 0xFF800000u;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const bool ok = full || v0 + (int64_t)j * 64 < lim;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (r >= nrows) break;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t word = ok ? raw.v[r][j][w] : kMasked;
+        if constexpr (DT == kBF16) {
+          x[r][j * PV + 2 * w] = bf16_lo(word);
+          x[r][j * PV + 2 * w + 1] = bf16_hi(word);
+        } else {
+          x[r][j * PV + w] = __uint_as_float(word);
+        }
+      }
+    }
+  }
+  if (!full && tail < cend) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      if (v0 + (int64_t)j * 64 == tail) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          if (r >= nrows) break;
+#pragma unroll
+          for (int e = 0; e < PV; ++e) {
+            const int64_t idx = tail * PV + e;
+            if (idx < V) x[r][j * PV + e] = load_one<DT>(rows[r], idx);
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Cluster records through buffer instructions with an explicit cache policy:
+// device scope (sc1), so that a load never hits a stale copy in the CU's L1 (a
+// workgroup-scope load, sc0 alone, may) and a store is visible to every CU.
+#ifndef MTP_REC_CPOL
+#define MTP_REC_CPOL 16
+#endif
+constexpr int kRecCpol = MTP_REC_CPOL;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+}
+__device__ __forceinline__ uint64_t rec_load(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, kRecCpol);
+  return (uint64_t)v[0] | ((uint64_t)v[1] << 32);
+}
+__device__ __forceinline__ void rec_store(__amdgpu_buffer_rsrc_t r, int byte_off, uint64_t w) {
+  const u32x2 v = {(uint32_t)w, (uint32_t)(w >> 32)};
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, byte_off, 0, kRecCpol);
+}
+
+// ---------------------------------------------------------------------------
 // Philox4x32-10: ten rounds of the Philox S-box on four 32-bit words with a
 // two-word key advanced by the Weyl increments between rounds.
 struct P4 { uint32_t x[4]; };

@@ -7,10 +7,12 @@
 
 namespace mtp {
 
-// Vectors of 16 bytes each thread keeps per row: verify keeps a target and a
-// draft chunk in registers (64 floats per thread either way).
-constexpr int kVerifyNVBf16 = 3;   // 24 bf16 per row per thread, 6144-element chunks
-constexpr int kVerifyNVF32 = 4;    // 16 fp32 per row per thread, 4096-element chunks
+// Vectors of 16 bytes each thread holds per row and layer in the verify main
+// kernel: 16 values per row either way (a chunk is 4096 elements), so that the
+// current layer, the previous one (waiting for its row statistics) and the next
+// one in flight fit in 128 VGPRs.
+constexpr int kVerifyNVBf16 = 2;
+constexpr int kVerifyNVF32 = 4;
 constexpr int kMaxRowsPerSeq = 9;  // gamma + 1 with gamma <= 8
 // Workgroups per CU the layered main kernels are compiled for (one wave per SIMD
 // each), chosen so that one chunk in registers plus the next one in flight fit
@@ -37,9 +39,9 @@ struct VerifyArgs {
   uint64_t seed, offset;
   uint8_t* accept; int32_t* accepted_len; int32_t* next_token;
   int32_t* row_token; float* overlap; float* tv; float* entropy; int32_t* row_status;
-  // workspace sections: error word, pass-1 records [group][chunk][3], segment
-  // masses [group][chunk][4 * NV]
-  uint32_t* err; uint64_t* part1; float* seg;
+  // workspace sections: error word, pass-1 records [group][chunk][3], pass-2
+  // sums [group][chunk][wave] = (residual or p mass, overlap) as two floats
+  uint32_t* err; uint64_t* part1; uint64_t* part2;
   RowSplit sp;
   int ngroups;
   int sgroups, layers;   // super-groups per XCD, groups per super-group
