@@ -123,10 +123,11 @@ TvLayout tv_layout(int32_t T, int32_t G, int32_t V, mtp_dtype dt, bool shared) {
   return L;
 }
 
-// Persistent super-groups: C workgroups per super-group, at most per_xcd resident
-// workgroups per XCD, L groups per XCD.  Returns (super-groups per XCD, layers).
-void plan_layers(int64_t per_xcd, int C, int64_t L, int* sgroups, int* layers) {
-  int64_t smax = per_xcd / C;
+// Persistent super-groups of C workgroups, at most `cap` of them resident at once
+// (the workgroups that share the work), L groups to process.  Returns the number
+// of super-groups and of layers (groups per super-group), balanced.
+void plan_layers(int64_t cap, int C, int64_t L, int* sgroups, int* layers) {
+  int64_t smax = cap / C;
   if (smax < 1) smax = 1;
   const int64_t k = (L + smax - 1) / smax;
   const int64_t S = (L + k - 1) / k;
@@ -204,11 +205,12 @@ mtp_status mtp_verify(const void* target, int64_t target_row_stride, const void*
   // ---- device-dependent checks ---------------------------------------------
   int64_t per_xcd = 0;
   if ((s = cluster_capacity(0, dtype, 0, 0, &per_xcd))) return s;
-  if ((int64_t)L.sp.nchunks > per_xcd)
-    return fail(MTP_ERR_SHAPE, "vocab %d needs %d co-resident workgroups per row; one XCD holds %lld", vocab,
-                L.sp.nchunks, (long long)per_xcd);
+  const int64_t per_gpu = per_xcd * 8;
+  if ((int64_t)L.sp.nchunks > per_gpu)
+    return fail(MTP_ERR_SHAPE, "vocab %d needs %d co-resident workgroups per row; the GPU holds %lld", vocab,
+                L.sp.nchunks, (long long)per_gpu);
   int sgroups = 0, layers = 0;
-  plan_layers(per_xcd, L.sp.nchunks, (L.ngroups + 7) / 8, &sgroups, &layers);
+  plan_layers(per_gpu, L.sp.nchunks, L.ngroups, &sgroups, &layers);
 
   mtp::VerifyArgs a{};
   a.target = target; a.t_stride = target_row_stride;

@@ -408,93 +408,106 @@ __device__ __forceinline__ Lse lse_nan() {
   return Lse{nan, nan, nan};
 }
 
-// Log-sum-exp partial of one row over a wave: the wave's largest logit M is the
-// reference (ref = M log2 e), x is overwritten with e = 2^(x log2 e - ref) and the
-// sums of e (and of e * (x log2 e - ref) with kY) are taken over the wave.  A wave
-// holding only -inf gives the empty partial (and e = 0); a NaN gives a NaN partial.
-// The entropy moment is accumulated without guarding 0 * (-inf); if that produced
-// a NaN it is summed again from the e values alone (e log2 e, e > 0).
-template <int NE, bool kY>
-__device__ __forceinline__ Lse wave_pass1(float (&x)[NE]) {
-  float m = x[0];
+// Log-sum-exp partials of R rows over a wave, the rows interleaved so that their
+// dependency chains overlap.  For row r the wave's largest logit M is the reference
+// (ref = M log2 e; 0 when the wave holds only -inf), x[r] is overwritten with
+// e = 2^(x log2 e - ref) and the sums of e, and for r < RY of e * (x log2 e - ref)
+// (the entropy moment), are taken over the wave.  A wave holding only -inf gives
+// z = 0 (an empty partial, e = 0); a NaN gives z = NaN.  The entropy moment is
+// accumulated without guarding 0 * (-inf); if that produced a NaN it is summed again
+// from the e values alone (e log2 e over e > 0).
+template <int NE, int R, int RY>
+__device__ __forceinline__ void wave_pass1(float (&x)[R][NE], Lse (&out)[R]) {
+  float M[R];
 #pragma unroll
-  for (int i = 1; i < NE; ++i) m = fmaximum(m, x[i]);
-  const float M = wave_maximum(m);
-  if (M != M) {
+  for (int r = 0; r < R; ++r) {
+    float m = x[r][0];
 #pragma unroll
-    for (int i = 0; i < NE; ++i) x[i] = 0.f;
-    return lse_nan();
+    for (int i = 1; i < NE; ++i) m = fmaximum(m, x[r][i]);
+    M[r] = m;
   }
-  if (!(M > kNegInf)) {
 #pragma unroll
-    for (int i = 0; i < NE; ++i) x[i] = 0.f;
-    return lse_empty();
+  for (int r = 0; r < R; ++r) M[r] = wave_maximum(M[r]);
+  float ref[R], z0[R], z1[R], y0[R], y1[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    ref[r] = M[r] > kNegInf ? M[r] * kLog2e : 0.f;
+    z0[r] = z1[r] = y0[r] = y1[r] = 0.f;
   }
-  const float ref = M * kLog2e;
-  float z = 0.f, y = 0.f;
 #pragma unroll
   for (int i = 0; i < NE; ++i) {
-    const float t = __builtin_fmaf(x[i], kLog2e, -ref);
-    const float e = fast_exp2(t);
-    z += e;
-    if constexpr (kY) y = __builtin_fmaf(e, t, y);
-    x[i] = e;
-  }
-  const float Z = wave_total(z);
-  float Y = 0.f;
-  if constexpr (kY) {
-    Y = wave_total(y);
-    if (Y != Y && Z == Z) {
-      y = 0.f;
 #pragma unroll
-      for (int i = 0; i < NE; ++i)
-        if (x[i] > 0.f) y = __builtin_fmaf(x[i], fast_log2(x[i]), y);
-      Y = wave_total(y);
+    for (int r = 0; r < R; ++r) {
+      const float t = __builtin_fmaf(x[r][i], kLog2e, -ref[r]);
+      const float e = fast_exp2(t);
+      if (i & 1) z1[r] += e; else z0[r] += e;
+      if (r < RY) {
+        if (i & 1) y1[r] = __builtin_fmaf(e, t, y1[r]); else y0[r] = __builtin_fmaf(e, t, y0[r]);
+      }
+      x[r][i] = e;
     }
   }
-  return Lse{ref, Z, Y};
+  float Z[R], Y[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    Z[r] = wave_total(z0[r] + z1[r]);
+    Y[r] = r < RY ? wave_total(y0[r] + y1[r]) : 0.f;
+  }
+#pragma unroll
+  for (int r = 0; r < RY; ++r) {
+    if (Y[r] != Y[r] && Z[r] == Z[r]) {
+      float y = 0.f;
+#pragma unroll
+      for (int i = 0; i < NE; ++i)
+        if (x[r][i] > 0.f) y = __builtin_fmaf(x[r][i], fast_log2(x[r][i]), y);
+      Y[r] = wave_total(y);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) out[r] = Lse{ref[r], Z[r], Y[r]};
 }
 
-// Merge of per-lane partials (lanes without one hold the empty partial) into one,
-// the same bits in every lane.  kY: also merge the entropy moment.
-template <bool kY>
-__device__ __forceinline__ Lse wave_merge(const Lse& s) {
-  const bool nan = s.z != s.z || s.ref != s.ref || (kY && s.y != s.y);
-  if (__ballot(nan) != 0ull) return lse_nan();
-  const bool live = s.z > 0.f;
-  const float R = wave_maximum(live ? s.ref : kNegInf);
-  if (!(R > kNegInf)) return lse_empty();
-  const float d = live ? s.ref - R : 0.f;
-  const float f = fast_exp2(d);
-  const float z = live ? s.z * f : 0.f;
-  float Y = 0.f;
-  if constexpr (kY) Y = wave_total(live ? __builtin_fmaf(d, s.z, s.y) * f : 0.f);
-  return Lse{R, wave_total(z), Y};
+// Merge of per-lane partials of R rows into one per row, the same bits in every
+// lane; rows r < RY merge the entropy moment too.  A partial with z = 0 is empty;
+// a NaN z or ref propagates into the result (z != 0 keeps it live, the maximum
+// propagates a NaN reference); a row with no live partial gives ref = -inf, z = 0.
+template <int R, int RY>
+__device__ __forceinline__ void wave_merge(Lse (&s)[R]) {
+  float Rm[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) Rm[r] = wave_maximum(s[r].z != 0.f ? s[r].ref : kNegInf);
+  float zc[R], yc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const bool live = s[r].z != 0.f;
+    const float d = live ? s[r].ref - Rm[r] : 0.f;
+    const float f = fast_exp2(d);
+    zc[r] = live ? s[r].z * f : 0.f;
+    yc[r] = live && r < RY ? __builtin_fmaf(d, s[r].z, s[r].y) * f : 0.f;
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) s[r] = Lse{Rm[r], wave_total(zc[r]), r < RY ? wave_total(yc[r]) : 0.f};
 }
 
-// Merge of N partials held in LDS (stride 3 floats), computed alike in every lane.
+// Merge of N partials held in LDS (stride 3 floats), computed alike in every lane,
+// with the same conventions as wave_merge.
 template <int N, bool kY>
 __device__ __forceinline__ Lse merge_lds(const float* p) {
-  bool nan = false;
+  float ref[N], z[N], y[N];
   float R = kNegInf;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    const float ref = p[3 * i], z = p[3 * i + 1], y = p[3 * i + 2];
-    nan = nan || z != z || ref != ref || (kY && y != y);
-    if (z > 0.f) R = fmaxf(R, ref);
+    ref[i] = p[3 * i]; z[i] = p[3 * i + 1]; y[i] = kY ? p[3 * i + 2] : 0.f;
+    R = fmaximum(R, z[i] != 0.f ? ref[i] : kNegInf);
   }
-  if (nan) return lse_nan();
-  if (!(R > kNegInf)) return lse_empty();
   float Z = 0.f, Y = 0.f;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    const float ref = p[3 * i], z = p[3 * i + 1], y = p[3 * i + 2];
-    if (z > 0.f) {
-      const float d = ref - R;
-      const float f = fast_exp2(d);
-      Z = __builtin_fmaf(z, f, Z);
-      if constexpr (kY) Y = __builtin_fmaf(__builtin_fmaf(d, z, y), f, Y);
-    }
+    const bool live = z[i] != 0.f;
+    const float d = live ? ref[i] - R : 0.f;
+    const float f = fast_exp2(d);
+    Z = __builtin_fmaf(live ? z[i] : 0.f, f, Z);
+    if constexpr (kY) Y = __builtin_fmaf(live ? __builtin_fmaf(d, z[i], y[i]) : 0.f, f, Y);
   }
   return Lse{R, Z, Y};
 }
@@ -507,17 +520,21 @@ __device__ __forceinline__ Lse merge_lds(const float* p) {
 // unpack_seg() widens them: when `full` (wave-uniform) every vector lies inside the
 // chunk and the row; otherwise vectors at or past `lim` read as -inf and the row's
 // partial last vector (index `tail`, if tail < `cend`) is read element by element.
+// Streaming loads: non-temporal (each logit is read once).
+constexpr int kStreamCpol = 2;
+
 template <int DT, int NV, int R>
-__device__ __forceinline__ void issue_seg(RawChunk<NV, R>& raw, const char* const (&rows)[R], int64_t v0,
-                                          int64_t last, int nrows = R) {
+__device__ __forceinline__ void issue_seg(RawChunk<NV, R>& raw, const char* const (&rows)[R], int v0, int last,
+                                          int nrows = R) {
   if (last >= 0) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if (r >= nrows) break;
+    for (int j = 0; j < NV; ++j) {
+      const int off = min(v0 + j * 64, last) * 16;
 #pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        const int64_t vi = min(v0 + (int64_t)j * 64, last);
-        raw.v[r][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rows[r]) + vi);
+      for (int r = 0; r < R; ++r) {
+        if (r >= nrows) break;
+        raw.v[r][j] = __builtin_amdgcn_raw_buffer_load_b128(
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(rows[r]), 0, 0x7fffffff, 0x00020000), off, 0, kStreamCpol);
       }
     }
   } else {
@@ -528,40 +545,69 @@ __device__ __forceinline__ void issue_seg(RawChunk<NV, R>& raw, const char* cons
   }
 }
 
+// The same loads with a fixed count: all R rows (pass the same row twice when
+// there is only one) and, when `live` is false, a single 16-byte location for every
+// lane (rows[0] + 0) instead of the chunk.  A load count that does not depend on
+// the item lets the compiler wait for exactly the loads it needs.
 template <int DT, int NV, int R>
-__device__ __forceinline__ void unpack_seg(const RawChunk<NV, R>& raw, const char* const (&rows)[R], int64_t v0,
-                                           bool full, int64_t lim, int64_t tail, int64_t cend, int64_t V,
+__device__ __forceinline__ void issue_seg_fixed(RawChunk<NV, R>& raw, const char* const (&rows)[R], int v0,
+                                                int last, bool live) {
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int off = live ? min(v0 + j * 64, max(last, 0)) * 16 : 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      raw.v[r][j] = __builtin_amdgcn_raw_buffer_load_b128(
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(rows[r]), 0, 0x7fffffff, 0x00020000), off, 0, kStreamCpol);
+  }
+}
+
+template <int DT, int NV, int R>
+__device__ __forceinline__ void unpack_seg(const RawChunk<NV, R>& raw, const char* const (&rows)[R], int v0,
+                                           bool full, int lim, int tail, int cend, int V,
                                            float (&x)[R][NV * Elem<DT>::kPerVec], int nrows = R) {
   constexpr int PV = Elem<DT>::kPerVec;
   constexpr uint32_t kMasked = DT == kBF16 ? 0xFF80FF80u : 0xFF800000u;
+  auto put = [&](int r, int j, int w, uint32_t word) {
+    if constexpr (DT == kBF16) {
+      x[r][j * PV + 2 * w] = bf16_lo(word);
+      x[r][j * PV + 2 * w + 1] = bf16_hi(word);
+    } else {
+      x[r][j * PV + w] = __uint_as_float(word);
+    }
+  };
+  if (full) {   // wave-uniform: the whole segment lies inside the chunk and the row
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (r >= nrows) break;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) put(r, j, w, raw.v[r][j][w]);
+      }
+    return;
+  }
+  // also covers a bad (no valid data) case: last < 0 has raw = 0 but every vector masked
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const bool ok = full || v0 + (int64_t)j * 64 < lim;
+    const bool ok = v0 + j * 64 < lim;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       if (r >= nrows) break;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t word = ok ? raw.v[r][j][w] : kMasked;
-        if constexpr (DT == kBF16) {
-          x[r][j * PV + 2 * w] = bf16_lo(word);
-          x[r][j * PV + 2 * w + 1] = bf16_hi(word);
-        } else {
-          x[r][j * PV + w] = __uint_as_float(word);
-        }
-      }
+      for (int w = 0; w < 4; ++w) put(r, j, w, ok ? raw.v[r][j][w] : kMasked);
     }
   }
-  if (!full && tail < cend) {
+  if (tail < cend) {
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      if (v0 + (int64_t)j * 64 == tail) {
+      if (v0 + j * 64 == tail) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           if (r >= nrows) break;
 #pragma unroll
           for (int e = 0; e < PV; ++e) {
-            const int64_t idx = tail * PV + e;
+            const int idx = tail * PV + e;
             if (idx < V) x[r][j * PV + e] = load_one<DT>(rows[r], idx);
           }
         }

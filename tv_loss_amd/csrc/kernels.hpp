@@ -8,17 +8,16 @@
 namespace mtp {
 
 // Vectors of 16 bytes each thread holds per row and layer in the verify main
-// kernel: 16 values per row either way (a chunk is 4096 elements), so that the
+// kernel: 16 bf16 or 12 fp32 values per row (chunks of 4096 or 3072 elements), so that the
 // current layer, the previous one (waiting for its row statistics) and the next
 // one in flight fit in 128 VGPRs.
 constexpr int kVerifyNVBf16 = 2;
-constexpr int kVerifyNVF32 = 4;
+constexpr int kVerifyNVF32 = 3;
 constexpr int kMaxRowsPerSeq = 9;  // gamma + 1 with gamma <= 8
 // Workgroups per CU the layered main kernels are compiled for (one wave per SIMD
-// each), chosen so that one chunk in registers plus the next one in flight fit
-// without spilling: 4 (128 VGPRs) for verify's two rows, 3 (168 VGPRs) for the
-// TV forward's four.
-constexpr int kVerifyBlocksPerCU = 4;
+// each): 3 (168 VGPRs) for verify, which keeps one layer's e values in registers
+// and two chunks in flight, and for the TV forward's four rows.
+constexpr int kVerifyBlocksPerCU = 3;
 constexpr int kTvFwdBlocksPerCU = 3;
 
 // Counters sit 16 ints (64 bytes) apart so clusters do not share a line.
@@ -44,7 +43,7 @@ struct VerifyArgs {
   uint32_t* err; uint64_t* part1; uint64_t* part2;
   RowSplit sp;
   int ngroups;
-  int sgroups, layers;   // super-groups per XCD, groups per super-group
+  int sgroups, layers;   // super-groups (all co-resident), groups per super-group
 };
 
 int verify_vec_per_thread(int dt);

@@ -49,65 +49,70 @@ namespace mtp {
 // z's carry the sign bit as a marker so that no word of a published record is 0.
 constexpr int kRecWords = 3;
 
-__device__ __forceinline__ Lse rec_p(uint64_t w0, uint64_t w2) {
-  return Lse{unpack_lo(w0), unmark(unpack_hi(w0)), unpack_lo(w2)};
+// Row statistics from the C records of a group.  Lane l holds the partial of
+// record l and merges records l + 64, l + 128, ... into it in that order; the wave
+// then merges the lanes.  Both kernels use these functions, so both derive the same
+// bits for a row.
+__device__ __forceinline__ Lse lane_records(Lse acc, __amdgpu_buffer_rsrc_t rs, int C, int word, bool with_y) {
+  const int lane = threadIdx.x & 63;
+  for (int c = lane + 64; c < C; c += 64) {
+    const uint64_t w = rec_load(rs, c * 24 + word * 8);
+    const float y = with_y ? unpack_lo(rec_load(rs, c * 24 + 16)) : 0.f;
+    acc = lse_merge(acc, Lse{unpack_lo(w), unmark(unpack_hi(w)), y});
+  }
+  return acc;
 }
-__device__ __forceinline__ Lse rec_q(uint64_t w1) { return Lse{unpack_lo(w1), unmark(unpack_hi(w1)), 0.f}; }
 
-// Row statistics of a group from its C records: lane l merges records l, l + 64,
-// ... in that order, then the wave merges the lanes.  Used by both kernels, so
-// both derive the same bits.  `w` holds the words of record l (first batch).
 struct RowStats {
   Lse p, q;
 };
 
-template <bool kY>
-__device__ __forceinline__ RowStats merge_records(const uint64_t (&w)[kRecWords], __amdgpu_buffer_rsrc_t rs, int C,
-                                                  bool pair) {
+__device__ __forceinline__ RowStats merge_records(__amdgpu_buffer_rsrc_t rs, int C, bool pair) {
   const int lane = threadIdx.x & 63;
-  Lse ap = lse_empty(), aq = lse_empty();
+  Lse a[2] = {lse_empty(), lse_empty()};
   if (lane < C) {
-    ap = rec_p(w[0], w[2]);
-    if (pair) aq = rec_q(w[1]);
+    const uint64_t w0 = rec_load(rs, lane * 24), w1 = rec_load(rs, lane * 24 + 8), w2 = rec_load(rs, lane * 24 + 16);
+    a[0] = Lse{unpack_lo(w0), unmark(unpack_hi(w0)), unpack_lo(w2)};
+    if (pair) a[1] = Lse{unpack_lo(w1), unmark(unpack_hi(w1)), 0.f};
   }
-  for (int c = lane + 64; c < C; c += 64) {   // further batches: already known to be ready
-    const uint64_t w0 = rec_load(rs, c * 24), w1 = rec_load(rs, c * 24 + 8), w2 = rec_load(rs, c * 24 + 16);
-    ap = lse_merge(ap, rec_p(w0, w2));
-    if (pair) aq = lse_merge(aq, rec_q(w1));
-  }
-  RowStats s;
-  s.p = wave_merge<kY>(ap);
-  s.q = pair ? wave_merge<false>(aq) : lse_empty();
-  return s;
+  a[0] = lane_records(a[0], rs, C, 0, true);
+  if (pair) a[1] = lane_records(a[1], rs, C, 1, false);
+  wave_merge<2, 1>(a);
+  return RowStats{a[0], a[1]};
 }
 
-// Wait until every record of the group is published.  `w` holds this lane's words
-// of record `lane` as loaded earlier; lanes whose words are not all non-zero load
-// again.  Records beyond the first 64 are polled the same way.  Bounded by the
-// spin limit (a timeout sets the error word and returns).
-__device__ __forceinline__ void poll_records(uint64_t (&w)[kRecWords], __amdgpu_buffer_rsrc_t rs, int C,
-                                             uint32_t* err) {
+// Wait until word `word` of every record of the group is published (non-zero) and
+// return this row's merged log-sum-exp (no entropy moment).  `v` is this lane's
+// word of record `lane`, loaded earlier; lanes still seeing zero load again.
+// Bounded by the spin limit (a timeout sets the error word and carries on).
+__device__ __forceinline__ Lse poll_row(uint64_t v, __amdgpu_buffer_rsrc_t rs, int C, int word, uint32_t* err) {
   const int lane = threadIdx.x & 63;
   uint64_t t0 = 0;
+  Lse acc = lse_empty();
   for (int c0 = 0; c0 < C; c0 += 64) {
     const int c = c0 + lane;
-    uint64_t v0 = w[0], v1 = w[1], v2 = w[2];
-    if (c0 > 0 && c < C) { v0 = rec_load(rs, c * 24); v1 = rec_load(rs, c * 24 + 8); v2 = rec_load(rs, c * 24 + 16); }
-    bool ready = !(c < C) || (v0 != 0ull && v1 != 0ull && v2 != 0ull);
-    for (int it = 0; __ballot(!ready) != 0ull; ++it) {
+    if (c0 > 0 && c < C) v = rec_load(rs, c * 24 + word * 8);
+    bool ready = !(c < C) || v != 0ull;
+    while (__ballot(!ready) != 0ull) {
       if (t0 == 0) t0 = __builtin_amdgcn_s_memrealtime();
       __builtin_amdgcn_s_sleep(1);
       if (!ready) {
-        v0 = rec_load(rs, c * 24); v1 = rec_load(rs, c * 24 + 8); v2 = rec_load(rs, c * 24 + 16);
-        ready = v0 != 0ull && v1 != 0ull && v2 != 0ull;
+        v = rec_load(rs, c * 24 + word * 8);
+        ready = v != 0ull;
       }
       if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimitTicks) {
         if (lane == 0) __hip_atomic_fetch_or(err, kErrSyncTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
     }
-    if (c0 == 0) { w[0] = v0; w[1] = v1; w[2] = v2; }
+    if (c < C) {
+      const Lse r{unpack_lo(v), unmark(unpack_hi(v)), 0.f};
+      acc = c0 == 0 ? r : lse_merge(acc, r);
+    }
   }
+  Lse a[1] = {acc};
+  wave_merge<1, 0>(a);
+  return a[0];
 }
 
 // ---------------------------------------------------------------------------
@@ -118,129 +123,94 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
   constexpr int NQ = NE / 4;              // 16-byte LDS slots per row and thread
   constexpr int kSegVec = NV * 64;
   const int C = a.sp.nchunks;
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7, slot = bid >> 3;
+  const int slot = blockIdx.x;
   const int sg = slot / C, c = slot - sg * C;
   const int S = a.sgroups;
   const int B = a.B, G = a.G, G1 = G + 1;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int leader = (slot + c) & (kWaves - 1);   // spreads the leader role over the SIMDs
+  const int t = threadIdx.x;
+  // the p and q rows' bookkeeping (combining partials, publishing, polling) is
+  // done by two different waves, rotated over the workgroups so that it spreads
+  // over the SIMDs
+  const int wp = (slot + c) & (kWaves - 1), wq = wp ^ 1;
 
-  // item i of this super-group is w = (i S + sg) 8 + xcd; items run over rows
-  // k-major (all k = 0 rows first), so every stream sees the same mix of pair and
-  // bonus groups
-  const int64_t first = (int64_t)sg * 8 + xcd;
-  if (first >= a.ngroups) return;
-  const int nl = (int)((a.ngroups - 1 - first) / ((int64_t)S * 8)) + 1;
+  // item i of super-group sg is row w = sg + i S; rows are taken k-major (all
+  // k = 0 rows first), so every super-group sees the same mix of pair and bonus
+  // groups
+  if (sg >= a.ngroups) return;
+  const int nl = (a.ngroups - 1 - sg) / S + 1;
   auto group_of = [&](int i) {
-    const int w = (i * S + sg) * 8 + xcd;
+    const int w = sg + i * S;
     const int k = w / B;
     return (w - k * B) * G1 + k;
   };
-
-  const int64_t vbeg = (int64_t)c * a.sp.vec_per_chunk;
-  const int64_t vend = min(vbeg + a.sp.vec_per_chunk, a.sp.nvec);
-  const int64_t s0 = vbeg + (int64_t)wave * kSegVec;      // this wave's segment
-  const int64_t v0 = s0 + lane;
-  const int64_t lim = min(vend, a.sp.nvec_full);
-  const bool full = s0 + kSegVec <= lim;
-  const int64_t last = a.sp.nvec_full - 1;
-  const int64_t tail = a.sp.nvec_full;
-
-  // e values of the previous layer, waiting for their row statistics: thread t owns
-  // slots [row][q][t] (16 bytes each), so the accesses of a wave are contiguous
-  __shared__ float4 held[2][NQ][kBlock];
-  __shared__ float part_sh[2][kWaves * 3];
-  __shared__ float lse_sh[2];
-
+  auto is_pair = [&](int g) { return g % G1 < G; };
   auto trow_of = [&](int g) {
     return reinterpret_cast<const char*>(a.target) + (int64_t)g * a.t_stride * Elem<DT>::kBytes;
   };
-  auto drow_of = [&](int g) {
+  auto drow_of = [&](int g) {   // a bonus row has no draft row: its target row again
     const int b = g / G1, k = g - b * G1;
-    return reinterpret_cast<const char*>(a.draft) + (int64_t)(b * G + (k < G ? k : 0)) * a.d_stride * Elem<DT>::kBytes;
+    return k < G ? reinterpret_cast<const char*>(a.draft) + (int64_t)(b * G + k) * a.d_stride * Elem<DT>::kBytes
+                 : trow_of(g);
   };
-  auto is_pair = [&](int g) { return g % G1 < G; };
+  auto rsrc_rec = [&](int g) { return rsrc_of(a.part1 + (int64_t)g * C * kRecWords); };
 
-  RawChunk<NV, 2> raw;
-  {
-    const int g = group_of(0);
+  // vector indices fit in 32 bits (V <= 2^30)
+  const int vpc = (int)a.sp.vec_per_chunk, nvec = (int)a.sp.nvec, nfull = (int)a.sp.nvec_full;
+  const int vbeg = c * vpc;
+  const int vend = min(vbeg + vpc, nvec);
+  const int s0 = vbeg + wave * kSegVec;      // this wave's segment
+  const int v0 = s0 + lane;
+  const int lim = min(vend, nfull);
+  const bool full = s0 + kSegVec <= lim;
+  const int last = nfull - 1;
+  const int tail = nfull;
+  const int V = (int)a.V;
+
+  // e values of the item two layers back, waiting for their row statistics:
+  // thread t owns slots [row][q][t] (16 bytes each), so a wave's accesses are
+  // contiguous and no thread touches another's slots
+  __shared__ float4 held[2][NQ][kBlock];
+  // double-buffered by layer parity: a wave may run one layer ahead of another
+  __shared__ float part_sh[2][2][kWaves * 3];
+  __shared__ float lse_sh[2][2];
+
+  // the chunks of items i + 1 and i + 2 are in flight while item i is processed
+  // the chunks of items i + 1 and i + 2 are in flight while item i is processed;
+  // every prefetch issues the same number of loads (see issue_seg_fixed)
+  auto prefetch = [&](RawChunk<NV, 2>& rb, int g, bool live) {
     const char* const rows[2] = {trow_of(g), drow_of(g)};
-    issue_seg<DT, NV, 2>(raw, rows, v0, last, is_pair(g) ? 2 : 1);
-  }
+    issue_seg_fixed<DT, NV, 2>(rb, rows, v0, last, live);
+  };
+  RawChunk<NV, 2> rawA, rawB;
+  int g_0 = group_of(0), g_p1 = nl > 1 ? group_of(1) : g_0;
+  prefetch(rawA, g_0, true);
+  prefetch(rawB, g_p1, nl > 1);
+  int g_m2 = 0, g_m1 = 0;
+  uint64_t wpoll = 0ull;                     // this lane's polled record word
+  float x[2][NE];                            // item i - 1's e values between layers
+  float xref[2] = {0.f, 0.f};                // ... and this wave's references for them
+  float href[2] = {0.f, 0.f};                // references of the item held in LDS
 
-  uint64_t w[kRecWords] = {0ull, 0ull, 0ull};
-  float held_ref[2] = {kNegInf, kNegInf};   // this wave's references of the held layer
-  float x[2][NE];
-
-  for (int i = 0; i <= nl; ++i) {
-    const int gp = i >= 1 ? group_of(i - 1) : 0;
-    const bool pair_p = is_pair(gp);
-    const __amdgpu_buffer_rsrc_t rs_prev = rsrc_of(a.part1 + (int64_t)gp * C * kRecWords);
-    const int g = i < nl ? group_of(i) : 0;
-    const bool pair = is_pair(g);
-    if (i < nl) {
-      const char* const rows[2] = {trow_of(g), drow_of(g)};
-      unpack_seg<DT, NV, 2>(raw, rows, v0, full, lim, tail, vend, a.V, x, pair ? 2 : 1);
-    }
-    // the leader's poll of the previous item's records goes out before the
-    // prefetch, so that waiting for it does not wait for the prefetch
-    if (i >= 1 && wave == leader && lane < C) {
-      w[0] = rec_load(rs_prev, lane * 24);
-      w[1] = rec_load(rs_prev, lane * 24 + 8);
-      w[2] = rec_load(rs_prev, lane * 24 + 16);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (i + 1 < nl) {
-      const int gn = group_of(i + 1);
-      const char* const rows[2] = {trow_of(gn), drow_of(gn)};
-      issue_seg<DT, NV, 2>(raw, rows, v0, last, is_pair(gn) ? 2 : 1);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---- pass 1 of item i ----------------------------------------------------
-    float ref_a = kNegInf, ref_b = kNegInf;
-    if (i < nl) {
-      const Lse pa = wave_pass1<NE, true>(x[0]);
-      ref_a = pa.ref;
-      Lse pb = lse_empty();
-      if (pair) pb = wave_pass1<NE, false>(x[1]);
-      ref_b = pb.ref;
-      if (lane == 0) {
-        part_sh[0][wave * 3 + 0] = pa.ref; part_sh[0][wave * 3 + 1] = pa.z; part_sh[0][wave * 3 + 2] = pa.y;
-        part_sh[1][wave * 3 + 0] = pb.ref; part_sh[1][wave * 3 + 1] = pb.z; part_sh[1][wave * 3 + 2] = pb.y;
+  // Layer i: statistics and pass 2 of item i - 2 (held in LDS), item i - 1 moves
+  // from registers to LDS, item i is unpacked from buffer i & 1, the poll for item
+  // i - 1's records and the loads of item i + 2 (into the same buffer) go out, pass
+  // 1 of item i.
+  auto layer = [&](int i, RawChunk<NV, 2>& rb) __attribute__((always_inline)) {
+    // ---- row statistics of item i - 2 (polled a layer ago) ---------------------
+    if (i >= 2 && i - 2 < nl) {
+      const bool pair2 = is_pair(g_m2);
+      if (wave == wp || (wave == wq && pair2)) {
+        const int row = wave == wp ? 0 : 1;
+        const Lse st = poll_row(wpoll, rsrc_rec(g_m2), C, row, a.err);
+        if (lane == 0) lse_sh[i & 1][row] = lse_log2(st);
       }
-    }
-    __syncthreads();
-    if (wave == leader) {
-      if (i < nl) {
-        const Lse p = merge_lds<kWaves, true>(part_sh[0]);
-        const Lse q = pair ? merge_lds<kWaves, false>(part_sh[1]) : lse_empty();
-        if (lane == 0) {
-          const __amdgpu_buffer_rsrc_t rs = rsrc_of(a.part1 + (int64_t)g * C * kRecWords);
-          rec_store(rs, c * 24, pack2(p.ref, mark(p.z)));
-          rec_store(rs, c * 24 + 8, pack2(q.ref, mark(q.z)));
-          rec_store(rs, c * 24 + 16, pack2(p.y, 1.f));
-        }
-      }
-      if (i >= 1) {
-        poll_records(w, rs_prev, C, a.err);
-        const RowStats st = merge_records<false>(w, rs_prev, C, pair_p);
-        if (lane == 0) {
-          lse_sh[0] = lse_log2(st.p);
-          lse_sh[1] = pair_p ? lse_log2(st.q) : 0.f;
-        }
-      }
-    }
-    __syncthreads();
-
-    // ---- pass 2 of item i - 1, from LDS ----------------------------------------
-    const int t = threadIdx.x;
-    if (i >= 1) {
-      const float sa = fast_exp2(held_ref[0] - lse_sh[0]);
-      float rm = 0.f, om = 0.f;
-      if (pair_p) {
-        const float sb = fast_exp2(held_ref[1] - lse_sh[1]);
+      __syncthreads();
+      // ---- pass 2 of item i - 2 ------------------------------------------------
+      const float sa = fast_exp2(href[0] - lse_sh[i & 1][0]);
+      float rm0 = 0.f, rm1 = 0.f, om0 = 0.f, om1 = 0.f;
+      if (pair2) {
+        const float sb = fast_exp2(href[1] - lse_sh[i & 1][1]);
 #pragma unroll
         for (int qi = 0; qi < NQ; ++qi) {
           const float4 ea = held[0][qi][t], eb = held[1][qi][t];
@@ -250,37 +220,93 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
 #pragma clang fp contract(off)
             const float p = va[e] * sa, q = vb[e] * sb;
             const float m = fminf(p, q);
-            rm += p - m;   // = max(0, p - q) exactly
-            om += m;
+            if (e & 1) { rm1 += p - m; om1 += m; } else { rm0 += p - m; om0 += m; }   // p - m = max(0, p - q)
           }
         }
       } else {
 #pragma unroll
         for (int qi = 0; qi < NQ; ++qi) {
           const float4 ea = held[0][qi][t];
-          rm += ea.x * sa;
-          rm += ea.y * sa;
-          rm += ea.z * sa;
-          rm += ea.w * sa;
+          rm0 = __builtin_fmaf(ea.x, sa, rm0);
+          rm1 = __builtin_fmaf(ea.y, sa, rm1);
+          rm0 = __builtin_fmaf(ea.z, sa, rm0);
+          rm1 = __builtin_fmaf(ea.w, sa, rm1);
         }
       }
-      rm = wave_total(rm);
-      om = pair_p ? wave_total(om) : 0.f;
-      if (lane == 0) a.part2[((int64_t)gp * C + c) * kWaves + wave] = pack2(rm, om);
+      const float rm = wave_total(rm0 + rm1);
+      const float om = wave_total(om0 + om1);
+      if (lane == 0) a.part2[((int64_t)g_m2 * C + c) * kWaves + wave] = pack2(rm, pair2 ? om : 0.f);
     }
-    // ---- hold item i's e values for the next layer (own slots only) ------------
-    if (i < nl) {
+    // ---- item i - 1 moves to LDS (own slots only) ------------------------------
+    if (i >= 1 && i - 1 < nl) {
 #pragma unroll
-      for (int qi = 0; qi < NQ; ++qi)
+      for (int qi = 0; qi < NQ; ++qi) {
         held[0][qi][t] = make_float4(x[0][4 * qi], x[0][4 * qi + 1], x[0][4 * qi + 2], x[0][4 * qi + 3]);
-      if (pair) {
-#pragma unroll
-        for (int qi = 0; qi < NQ; ++qi)
-          held[1][qi][t] = make_float4(x[1][4 * qi], x[1][4 * qi + 1], x[1][4 * qi + 2], x[1][4 * qi + 3]);
+        held[1][qi][t] = make_float4(x[1][4 * qi], x[1][4 * qi + 1], x[1][4 * qi + 2], x[1][4 * qi + 3]);
       }
-      held_ref[0] = ref_a;
-      held_ref[1] = ref_b;
+      href[0] = xref[0];
+      href[1] = xref[1];
     }
+
+    // ---- item i: unpack, then the poll for item i - 1 and the loads of i + 2 ----
+    const bool pair = is_pair(g_0);
+    if (i < nl) {
+      const char* const rows[2] = {trow_of(g_0), drow_of(g_0)};
+      // both rows always (a bonus item's second row is its target row again), so
+      // that every load of the buffer is consumed before the buffer is refilled
+      unpack_seg<DT, NV, 2>(rb, rows, v0, full, lim, tail, vend, V, x, 2);
+    }
+    // the poll goes out before the prefetch, so that waiting for it (a layer
+    // later) does not wait for the prefetch
+    if (i >= 1 && i <= nl && (wave == wp || wave == wq) && lane < C)
+      wpoll = rec_load(rsrc_rec(g_m1), lane * 24 + (wave == wp ? 0 : 8));
+    __builtin_amdgcn_sched_barrier(0);
+    const int g_p2 = i + 2 < nl ? group_of(i + 2) : g_0;
+    prefetch(rb, g_p2, i + 2 < nl);
+    __builtin_amdgcn_sched_barrier(0);
+
+    if (i < nl) {
+      // ---- pass 1 of item i: wave partials, combined and published --------------
+      Lse pt[2];
+      if (pair) {
+        wave_pass1<NE, 2, 1>(x, pt);
+      } else {
+        wave_pass1<NE, 1, 1>(*reinterpret_cast<float(*)[1][NE]>(&x[0]), *reinterpret_cast<Lse(*)[1]>(&pt[0]));
+        pt[1] = lse_empty();
+      }
+      xref[0] = pt[0].ref;
+      xref[1] = pt[1].ref;
+      if (lane == 0) {
+        float* ps = part_sh[i & 1][0];
+        ps[wave * 3 + 0] = pt[0].ref; ps[wave * 3 + 1] = pt[0].z; ps[wave * 3 + 2] = pt[0].y;
+        ps = part_sh[i & 1][1];
+        ps[wave * 3 + 0] = pt[1].ref; ps[wave * 3 + 1] = pt[1].z; ps[wave * 3 + 2] = 0.f;
+      }
+      __syncthreads();
+      if (wave == wp) {
+        const Lse p = merge_lds<kWaves, true>(part_sh[i & 1][0]);
+        if (lane == 0) {
+          const __amdgpu_buffer_rsrc_t rs = rsrc_rec(g_0);
+          rec_store(rs, c * 24, pack2(p.ref, mark(p.z)));
+          rec_store(rs, c * 24 + 16, pack2(p.y, 1.f));
+        }
+      } else if (wave == wq) {
+        const Lse q = merge_lds<kWaves, false>(part_sh[i & 1][1]);
+        if (lane == 0) rec_store(rsrc_rec(g_0), c * 24 + 8, pack2(q.ref, mark(q.z)));
+      }
+    }
+    // ---- shift the item window -------------------------------------------------
+    g_m2 = g_m1;
+    g_m1 = g_0;
+    g_0 = g_p1;
+    g_p1 = g_p2;
+  };
+
+  // nl + 2 layers, rounded up to an even count so that both halves of the loop
+  // body always run (the buffers then keep their registers across iterations)
+  for (int i = 0; i < nl + 2; i += 2) {
+    layer(i, rawA);
+    layer(i + 1, rawB);
   }
 }
 
@@ -401,9 +427,7 @@ __global__ void verify_finish(VerifyArgs a) {
   uint64_t* p2 = a.part2 + (int64_t)g * C * kWaves;
 
   // ---- row statistics from the pass-1 records ---------------------------------
-  uint64_t w[kRecWords] = {0ull, 0ull, 0ull};
-  if (lane < C) { w[0] = rec_load(rs, lane * 24); w[1] = rec_load(rs, lane * 24 + 8); w[2] = rec_load(rs, lane * 24 + 16); }
-  const RowStats st = merge_records<true>(w, rs, C, pair);
+  const RowStats st = merge_records(rs, C, pair);
   const float lse2_p = lse_log2(st.p);
   const float lse2_q = pair ? lse_log2(st.q) : 0.f;
   const bool bad_p = !(__builtin_isfinite(lse2_p));
@@ -557,7 +581,7 @@ __global__ void verify_finish(VerifyArgs a) {
 // ---------------------------------------------------------------------------
 template <int DT, int NV>
 static hipError_t launch(const VerifyArgs& a, hipStream_t stream) {
-  const int64_t grid = (int64_t)a.sgroups * a.sp.nchunks * 8;
+  const int64_t grid = (int64_t)a.sgroups * a.sp.nchunks;
   hipLaunchKernelGGL((verify_main<DT, NV>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
