@@ -8,7 +8,6 @@
 #include <cstring>
 #include <map>
 #include <mutex>
-#include <tuple>
 
 #include "mtp.h"
 #include "kernels.hpp"
@@ -57,14 +56,15 @@ mtp_status check_row_base(const void* p, int64_t stride_elems, mtp_dtype dt, con
 // ---- per-device limits --------------------------------------------------------
 struct DeviceInfo {
   int cus = 0;
-  std::map<std::tuple<int, int, int, int>, int> occ;   // (kernel, dt, G, shared) -> blocks per CU
+  std::map<int, int> occ;   // dtype -> verify main workgroups per CU
 };
 std::mutex g_dev_mu;
 std::map<int, DeviceInfo> g_dev;
 
-// Workgroups one XCD can hold for the given kernel (the cluster of a group must
-// fit, with margin, so that its members are co-resident).
-mtp_status cluster_capacity(int kernel, int dt, int G, int shared, int64_t* per_xcd) {
+// Workgroups of the verify main kernel the current device holds at once: all of a
+// launch's workgroups must be resident together (a super-group waits on its
+// members' records).
+mtp_status verify_capacity(int dt, int64_t* per_gpu) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(MTP_ERR_DEVICE, "hipGetDevice failed");
   std::lock_guard<std::mutex> lk(g_dev_mu);
@@ -73,15 +73,14 @@ mtp_status cluster_capacity(int kernel, int dt, int G, int shared, int64_t* per_
     if (hipDeviceGetAttribute(&info.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return fail(MTP_ERR_DEVICE, "cannot query the compute-unit count");
   }
-  const auto key = std::make_tuple(kernel, dt, G, shared);
-  auto it = info.occ.find(key);
+  auto it = info.occ.find(dt);
   if (it == info.occ.end()) {
     int n = 0;
-    hipError_t e = kernel == 0 ? mtp::verify_occupancy(dt, &n) : mtp::tv_fwd_occupancy(dt, G, shared != 0, &n);
+    hipError_t e = mtp::verify_occupancy(dt, &n);
     if (e != hipSuccess || n < 1) return fail(MTP_ERR_DEVICE, "occupancy query failed");
-    it = info.occ.emplace(key, n).first;
+    it = info.occ.emplace(dt, n).first;
   }
-  *per_xcd = (int64_t)it->second * info.cus / 8;
+  *per_gpu = (int64_t)it->second * info.cus;
   return MTP_OK;
 }
 
@@ -203,9 +202,8 @@ mtp_status mtp_verify(const void* target, int64_t target_row_stride, const void*
   if (L.ngroups > 0x7fffffffLL / 8) return fail(MTP_ERR_SHAPE, "batch * (gamma + 1) is too large");
 
   // ---- device-dependent checks ---------------------------------------------
-  int64_t per_xcd = 0;
-  if ((s = cluster_capacity(0, dtype, 0, 0, &per_xcd))) return s;
-  const int64_t per_gpu = per_xcd * 8;
+  int64_t per_gpu = 0;
+  if ((s = verify_capacity(dtype, &per_gpu))) return s;
   if ((int64_t)L.sp.nchunks > per_gpu)
     return fail(MTP_ERR_SHAPE, "vocab %d needs %d co-resident workgroups per row; the GPU holds %lld", vocab,
                 L.sp.nchunks, (long long)per_gpu);
@@ -268,13 +266,7 @@ mtp_status mtp_tv_loss_fwd(const void* target, int64_t target_pos_stride, int64_
   const bool shared = target_head_stride == 0;
   const TvLayout L = tv_layout(T, gamma, vocab, dtype, shared);
   if ((s = check_workspace(workspace, workspace_bytes, L.total))) return s;
-  int64_t per_xcd = 0;
-  if ((s = cluster_capacity(1, dtype, gamma, shared, &per_xcd))) return s;
-  if ((int64_t)L.sp.nchunks > per_xcd)
-    return fail(MTP_ERR_SHAPE, "vocab %d needs %d co-resident workgroups per position; one XCD holds %lld",
-                vocab, L.sp.nchunks, (long long)per_xcd);
-  int sgroups = 0, layers = 0;
-  plan_layers(per_xcd, L.sp.nchunks, ((int64_t)T + 7) / 8, &sgroups, &layers);
+  if ((int64_t)T * L.sp.nchunks > 0x7fffffffLL) return fail(MTP_ERR_SHAPE, "T * chunks is too large");
   mtp::TvArgs a{};
   a.target = target; a.t_pos = target_pos_stride; a.t_head = target_head_stride;
   a.draft = draft; a.d_pos = draft_pos_stride; a.d_head = draft_head_stride;
@@ -285,8 +277,6 @@ mtp_status mtp_tv_loss_fwd(const void* target, int64_t target_pos_stride, int64_
   a.part2 = at<float>(workspace, L.part2);
   a.pos_ws = at<float>(workspace, L.pos);
   a.sp = L.sp;
-  a.sgroups = sgroups;
-  a.layers = layers;
   hipError_t e = mtp::launch_tv_fwd(a, dtype, shared, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MTP_ERR_LAUNCH, "TV forward launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -14,11 +14,10 @@ namespace mtp {
 constexpr int kVerifyNVBf16 = 2;
 constexpr int kVerifyNVF32 = 3;
 constexpr int kMaxRowsPerSeq = 9;  // gamma + 1 with gamma <= 8
-// Workgroups per CU the layered main kernels are compiled for (one wave per SIMD
-// each): 3 (168 VGPRs) for verify, which keeps one layer's e values in registers
-// and two chunks in flight, and for the TV forward's four rows.
+// Workgroups per CU the verify main kernel is compiled for (one wave per SIMD
+// each): 3 (168 VGPRs) keeps one layer's e values in registers and two chunks in
+// flight.
 constexpr int kVerifyBlocksPerCU = 3;
-constexpr int kTvFwdBlocksPerCU = 3;
 
 // Counters sit 16 ints (64 bytes) apart so clusters do not share a line.
 constexpr int kCounterStride = 16;
@@ -64,11 +63,10 @@ struct TvArgs {
   // backward
   const float* saved_in; const float* grad_loss;
   void* grad; int64_t g_pos, g_head; int grad_dt;
-  // forward workspace: error word, pass-1 records [t][chunk][rows], overlap and S
-  // partials [t][chunk][2 gamma], per-position losses [t]
+  // forward workspace: error word, log-sum-exp partials [t][chunk][rows] as
+  // (ref, z), overlap and S partials [t][chunk][2 gamma], per-position losses [t]
   uint32_t* err; uint64_t* part1; float* part2; float* pos_ws;
   RowSplit sp;
-  int sgroups, layers;
 };
 
 constexpr int kTvSavedStride = 4;   // saved[t, k, :] = (lse_p, lse_q, alpha, S)
@@ -77,7 +75,6 @@ constexpr int kTvMaxHeads = 8;
 int tv_fwd_vec_per_thread(int dt, int G, bool shared);
 int tv_fwd_part1_words(int G, bool shared);
 hipError_t launch_tv_fwd(const TvArgs& a, int dt, bool shared, hipStream_t stream);
-hipError_t tv_fwd_occupancy(int dt, int G, bool shared, int* blocks_per_cu);
 int tv_bwd_vec_per_thread(int dt);
 hipError_t launch_tv_bwd(const TvArgs& a, int dt, bool shared, hipStream_t stream);
 

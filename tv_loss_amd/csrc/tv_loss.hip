@@ -9,14 +9,16 @@
 //   dL/dz_{t,j,v} = w_{t,j} q_v (1[q_v <= p_v] - S_{t,j}),
 //   w_{t,j} = -(g/T) sum_{k>=j} prod_{i<=k, i!=j} alpha_{t,i}.
 //
-// Forward: C workgroups split each position's rows along the vocabulary and sweep
-// the positions in layers (tv_fwd_main).  Per layer a workgroup keeps its chunk of
-// the target row(s) and of the gamma draft rows in registers while the next
-// layer's chunk is in flight, publishes its log-sum-exp partials as a
-// self-announcing record, polls its siblings' records, and computes its overlap
-// and S partials from registers.  tv_fwd_finish (one wave per position) sums the
-// partials in a fixed order and writes l_t and the saved statistics; tv_fwd_mean
-// writes the mean.  Every logit is read from HBM once.
+// Forward: three streaming kernels, no cross-workgroup waits.  tv_fwd_lse reads
+// chunk c of every row of position t (one workgroup per (t, c)) and writes the
+// chunk's log-sum-exp partial of each row.  tv_fwd_stats merges the partials of its
+// position's rows (every workgroup of the position derives the same bits), reads
+// the chunk again and writes the chunk's overlap and S partials of every head; the
+// indicator and the minimum are taken on log-probabilities, min(p, q) =
+// 2^min(log2 p, log2 q), so one exponential per head and element suffices.
+// tv_fwd_finish (one wave per position) sums the partials in a fixed order and
+// writes l_t and the saved statistics; tv_fwd_mean writes the mean.  Every logit is
+// read twice; the partials take a few bytes per chunk.
 // Backward: pure streaming; each workgroup reads one chunk of the target and draft
 // rows of one position plus the saved statistics, and writes the gradient chunk.
 // The indicator is evaluated on logits, z_v - a_v <= lse_q - lse_p, so no
@@ -26,198 +28,185 @@
 
 namespace mtp {
 
-template <int NE>
-__device__ __forceinline__ Lse thread_lse_plain(float (&x)[NE]) {
-  float m = x[0];
-#pragma unroll
-  for (int i = 1; i < NE; ++i) m = fmaxf(m, x[i]);
-  const bool empty = !(m > kNegInf);
-  const float ref = empty ? 0.f : m * kLog2e;
-  float z = 0.f;
-#pragma unroll
-  for (int i = 0; i < NE; ++i) {
-    const float e = fast_exp2(__builtin_fmaf(x[i], kLog2e, -ref));
-    z += e;
-    x[i] = e;
-  }
-  if (empty && z == 0.f) return lse_empty();
-  return Lse{ref, z, 0.f};
-}
-
-// Wave 0 polls the C pass-1 records (NR words (ref, z) each) of the position and
-// merges them in one fixed order; log2-sum-exp per row is broadcast through LDS.
+// Vectors per thread and row for the forward kernels: 16 bf16 or 8 fp32 values
+// per row and thread for up to four rows, fewer vectors when there are more rows
+// (at least one).
 template <int NR>
-__device__ __forceinline__ void merge_rows(const uint64_t* p1, int C, float (&lse2)[NR], float* lds,
-                                           uint32_t* err) {
-  __syncthreads();
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    Lse acc[NR];
-#pragma unroll
-    for (int r = 0; r < NR; ++r) acc[r] = lse_empty();
-    for (int c0 = 0; c0 < C; c0 += 64) {
-      uint64_t w[NR];
-      wave_poll<NR>(p1, c0, C, w, err);
-      if (c0 + lane < C) {
-#pragma unroll
-        for (int r = 0; r < NR; ++r) acc[r] = lse_merge(acc[r], Lse{unpack_lo(w[r]), unmark(unpack_hi(w[r])), 0.f});
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const Lse m = wave_lse(acc[r]);
-      if (lane == 0) lds[r] = lse_log2(m);
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < NR; ++r) lse2[r] = lds[r];
-  __syncthreads();
-}
-
-// Vectors per thread and row: about 64 bf16 or 32 fp32 values per thread in all
-// (their raw words for the next layer are in flight at the same time).
-template <int G>
-constexpr int fwd_nv(int per_vec, bool shared) {
-  const int rows = (shared ? 1 : G) + G;
-  const int budget = per_vec == 8 ? 64 : 32;
-  const int nv = budget / (rows * per_vec);
+constexpr int fwd_nv(int per_vec) {
+  const int nv = (per_vec == 8 ? 64 : 32) / (NR * per_vec);
   return nv < 1 ? 1 : nv;
 }
 
-// Forward main kernel: super-groups of C workgroups sweep the positions of their
-// XCD in layers (position (sg + i * S) * 8 + xcd at layer i), prefetching the next
-// layer's chunk; per layer one record poll, then the chunk's overlap and S
-// partials from registers.
-template <int DT, int G, bool SHARED>
-__global__ __launch_bounds__(kBlock, kTvFwdBlocksPerCU) void tv_fwd_main(TvArgs a) {
-  constexpr int PV = Elem<DT>::kPerVec;
-  constexpr int NV = fwd_nv<G>(PV, SHARED);
-  constexpr int NE = NV * PV;
-  constexpr int NT = SHARED ? 1 : G;
-  constexpr int NR = NT + G;
-  const int C = a.sp.nchunks;
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7, slot = bid >> 3;
-  const int sg = slot / C, c = slot - sg * C;
-  int nl = 0;
-  while (nl < a.layers && (int64_t)(sg + nl * a.sgroups) * 8 + xcd < a.T) ++nl;
-  if (nl == 0) return;
-  const int64_t vbeg = (int64_t)c * a.sp.vec_per_chunk;
-  const int64_t vend = min(vbeg + a.sp.vec_per_chunk, a.sp.nvec);
+template <int G, bool SHARED>
+struct FwdShape {
+  static constexpr int NT = SHARED ? 1 : G;   // target rows
+  static constexpr int NR = NT + G;           // target rows, then the G draft rows
+};
 
-  __shared__ float lds[3 * kWaves * NR + 2 * kWaves * G];
-
-  auto rows_of = [&](int t, const char* (&rows)[NR]) {
-    const char* tb = reinterpret_cast<const char*>(a.target);
-    const char* db = reinterpret_cast<const char*>(a.draft);
+// Row bases of position t: targets first, then drafts.
+template <int DT, int NT, int G>
+__device__ __forceinline__ void fwd_rows(const TvArgs& a, int t, const char* (&rows)[NT + G]) {
+  const char* tb = reinterpret_cast<const char*>(a.target);
+  const char* db = reinterpret_cast<const char*>(a.draft);
 #pragma unroll
-    for (int r = 0; r < NT; ++r) rows[r] = tb + ((int64_t)t * a.t_pos + (int64_t)r * a.t_head) * Elem<DT>::kBytes;
+  for (int r = 0; r < NT; ++r) rows[r] = tb + ((int64_t)t * a.t_pos + (int64_t)r * a.t_head) * Elem<DT>::kBytes;
 #pragma unroll
-    for (int k = 0; k < G; ++k) rows[NT + k] = db + ((int64_t)t * a.d_pos + (int64_t)k * a.d_head) * Elem<DT>::kBytes;
-  };
+  for (int k = 0; k < G; ++k) rows[NT + k] = db + ((int64_t)t * a.d_pos + (int64_t)k * a.d_head) * Elem<DT>::kBytes;
+}
 
+// This workgroup's chunk of every row of position t, widened to fp32 (-inf outside
+// the chunk and the row).  Each wave owns a contiguous segment of NV * 64 vectors.
+template <int DT, int NV, int NR>
+__device__ __forceinline__ void fwd_load(const TvArgs& a, const char* const (&rows)[NR], int c,
+                                         float (&x)[NR][NV * Elem<DT>::kPerVec]) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int vpc = (int)a.sp.vec_per_chunk, nvec = (int)a.sp.nvec, nfull = (int)a.sp.nvec_full;
+  const int vbeg = c * vpc;
+  const int vend = min(vbeg + vpc, nvec);
+  const int s0 = vbeg + wave * NV * 64;
+  const int lim = min(vend, nfull);
   RawChunk<NV, NR> raw;
-  {
-    const char* rows[NR];
-    rows_of(sg * 8 + xcd, rows);
-    issue_rows<DT, NV, NR>(raw, rows, vbeg, a.sp);
+  issue_seg<DT, NV, NR>(raw, rows, s0 + lane, nfull - 1);
+  unpack_seg<DT, NV, NR>(raw, rows, s0 + lane, s0 + NV * 64 <= lim, lim, nfull, vend, (int)a.V, x);
+}
+
+// Pass 1: chunk log-sum-exp partials of every row, part1[t][c][r] = (ref, z).
+template <int DT, int G, bool SHARED>
+__global__ __launch_bounds__(kBlock) void tv_fwd_lse(TvArgs a) {
+  constexpr int NR = FwdShape<G, SHARED>::NR;
+  constexpr int NV = fwd_nv<NR>(Elem<DT>::kPerVec);
+  constexpr int NE = NV * Elem<DT>::kPerVec;
+  const int C = a.sp.nchunks;
+  const int t = blockIdx.x / C, c = blockIdx.x - t * C;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ float part_sh[NR][kWaves * 3];
+  const char* rows[NR];
+  fwd_rows<DT, FwdShape<G, SHARED>::NT, G>(a, t, rows);
+  float x[NR][NE];
+  fwd_load<DT, NV, NR>(a, rows, c, x);
+  Lse pt[NR];
+  wave_pass1<NE, NR, 0>(x, pt);
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      part_sh[r][wave * 3 + 0] = pt[r].ref;
+      part_sh[r][wave * 3 + 1] = pt[r].z;
+      part_sh[r][wave * 3 + 2] = 0.f;
+    }
   }
-  for (int i = 0; i < nl; ++i) {
-    const int t = (sg + i * a.sgroups) * 8 + xcd;
-    const char* rows[NR];
-    rows_of(t, rows);
-    float x[NR][NE];
-    unpack_rows<DT, NV, NR>(raw, rows, vbeg, vend, a.sp, a.V, x);
-    if (i + 1 < nl) {   // prefetch the next layer's chunk
-      const char* nrows[NR];
-      rows_of((sg + (i + 1) * a.sgroups) * 8 + xcd, nrows);
-      issue_rows<DT, NV, NR>(raw, nrows, vbeg, a.sp);
-    }
-
-    // ---- pass 1 --------------------------------------------------------------
-    Lse parts[NR];
-    float refs[NR];
-#pragma unroll
-    for (int r = 0; r < NR; ++r) { parts[r] = thread_lse_plain<NE>(x[r]); refs[r] = parts[r].ref; }
-    block_lse<NR>(parts, lds);
-    uint64_t* p1 = a.part1 + (int64_t)t * C * NR;
-    if (threadIdx.x == 0) {
-#pragma unroll
-      for (int r = 0; r < NR; ++r) put_word(p1 + (int64_t)c * NR + r, pack2(parts[r].ref, mark(parts[r].z)));
-    }
-    float lse2[NR];
-    merge_rows<NR>(p1, C, lse2, lds, a.err);
-
-    // ---- pass 2: overlap and S from registers ------------------------------
-    float s[NR];
-#pragma unroll
-    for (int r = 0; r < NR; ++r) s[r] = fast_exp2(refs[r] - lse2[r]);
-    float acc[2 * G];
-#pragma unroll
-    for (int k = 0; k < 2 * G; ++k) acc[k] = 0.f;
-#pragma unroll
-    for (int e = 0; e < NE; ++e) {
-      const float p0 = x[0][e] * s[0];
-#pragma unroll
-      for (int k = 0; k < G; ++k) {
-        const float p = SHARED ? p0 : x[SHARED ? 0 : k][e] * s[SHARED ? 0 : k];
-        const float q = x[NT + k][e] * s[NT + k];
-        const bool ind = q <= p;
-        acc[2 * k] += ind ? q : p;
-        acc[2 * k + 1] += ind ? q : 0.f;
-      }
-    }
-    block_sum<2 * G>(acc, lds);
-    if (threadIdx.x == 0) {
-      float* mine = a.part2 + ((int64_t)t * C + c) * 2 * G;
-#pragma unroll
-      for (int k = 0; k < 2 * G; ++k) st_coherent(mine + k, acc[k]);
-    }
+  __syncthreads();
+  if (threadIdx.x < NR) {
+    const Lse m = merge_lds<kWaves, false>(part_sh[threadIdx.x]);
+    reinterpret_cast<float2*>(a.part1)[((int64_t)t * C + c) * NR + threadIdx.x] = make_float2(m.ref, m.z);
   }
 }
 
-// Forward finish: one wave per position sums the chunk partials in a fixed order
-// and writes the position's statistics, then clears the position's records.
+// log2-sum-exp of row r of position t from its C chunk partials: lane l merges
+// chunks l, l + 64, ... in order, then the wave merges the lanes.  tv_fwd_stats and
+// tv_fwd_finish both use it, so both derive the same bits.
+template <int NR>
+__device__ __forceinline__ float fwd_row_lse2(const TvArgs& a, int t, int r) {
+  const int C = a.sp.nchunks;
+  const int lane = threadIdx.x & 63;
+  const float2* p1 = reinterpret_cast<const float2*>(a.part1) + (int64_t)t * C * NR + r;
+  Lse acc[1] = {lse_empty()};
+  for (int c = lane; c < C; c += 64) {
+    const float2 w = p1[(int64_t)c * NR];
+    const Lse v{w.x, w.y, 0.f};
+    acc[0] = c == lane ? v : lse_merge(acc[0], v);
+  }
+  wave_merge<1, 0>(acc);
+  return lse_log2(acc[0]);
+}
+
+// Pass 2: chunk partials of the overlap sum_v min(p, q) and of S = sum_v 1[q <= p] q
+// for every head, part2[t][c][2k] = overlap, [2k + 1] = S.
+template <int DT, int G, bool SHARED>
+__global__ __launch_bounds__(kBlock) void tv_fwd_stats(TvArgs a) {
+  constexpr int NT = FwdShape<G, SHARED>::NT;
+  constexpr int NR = FwdShape<G, SHARED>::NR;
+  constexpr int NV = fwd_nv<NR>(Elem<DT>::kPerVec);
+  constexpr int NE = NV * Elem<DT>::kPerVec;
+  const int C = a.sp.nchunks;
+  const int t = blockIdx.x / C, c = blockIdx.x - t * C;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ float lse_sh[NR];
+  __shared__ float acc_sh[2 * G][kWaves];
+  const char* rows[NR];
+  fwd_rows<DT, NT, G>(a, t, rows);
+  float x[NR][NE];
+  fwd_load<DT, NV, NR>(a, rows, c, x);
+  for (int r = wave; r < NR; r += kWaves) {
+    const float l = fwd_row_lse2<NR>(a, t, r);
+    if (lane == 0) lse_sh[r] = l;
+  }
+  __syncthreads();
+  float al[G], sk[G];
+#pragma unroll
+  for (int k = 0; k < G; ++k) al[k] = sk[k] = 0.f;
+#pragma unroll
+  for (int i = 0; i < NE; ++i) {
+    float u[NT];
+#pragma unroll
+    for (int r = 0; r < NT; ++r) u[r] = __builtin_fmaf(x[r][i], kLog2e, -lse_sh[r]);   // log2 p
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const float uk = u[SHARED ? 0 : k];
+      const float v = __builtin_fmaf(x[NT + k][i], kLog2e, -lse_sh[NT + k]);        // log2 q
+      const float m = fast_exp2(fminf(uk, v));                                        // min(p, q)
+      al[k] += m;
+      sk[k] += v <= uk ? m : 0.f;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < G; ++k) {
+    al[k] = wave_total(al[k]);
+    sk[k] = wave_total(sk[k]);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      acc_sh[2 * k][wave] = al[k];
+      acc_sh[2 * k + 1][wave] = sk[k];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 2 * G) {
+    const float* v = acc_sh[threadIdx.x];
+    a.part2[((int64_t)t * C + c) * 2 * G + threadIdx.x] = (v[0] + v[1]) + (v[2] + v[3]);
+  }
+}
+
+// One wave per position: row log-sum-exps, the overlap and S of every head, l_t and
+// the saved statistics.  Clears the partials it read, so the workspace is all
+// zeros again when the call ends.
 constexpr int kFinishWaves = 4;
 
 template <int G, bool SHARED>
 __global__ __launch_bounds__(64 * kFinishWaves) void tv_fwd_finish(TvArgs a) {
-  constexpr int NT = SHARED ? 1 : G;
-  constexpr int NR = NT + G;
+  constexpr int NT = FwdShape<G, SHARED>::NT;
+  constexpr int NR = FwdShape<G, SHARED>::NR;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * kFinishWaves + (threadIdx.x >> 6);
   if (t >= a.T) return;
   const int C = a.sp.nchunks;
-  uint64_t* p1 = a.part1 + (int64_t)t * C * NR;
-  const float* p2 = a.part2 + (int64_t)t * C * 2 * G;
-  Lse acc[NR];
+  float lse2[NR];
 #pragma unroll
-  for (int r = 0; r < NR; ++r) acc[r] = lse_empty();
+  for (int r = 0; r < NR; ++r) lse2[r] = fwd_row_lse2<NR>(a, t, r);
+  float* p2 = a.part2 + (int64_t)t * C * 2 * G;
   float tot[2 * G];
 #pragma unroll
   for (int k = 0; k < 2 * G; ++k) tot[k] = 0.f;
   for (int c = lane; c < C; c += 64) {
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const uint64_t w = get_word(p1 + (int64_t)c * NR + r);
-      acc[r] = lse_merge(acc[r], Lse{unpack_lo(w), unmark(unpack_hi(w)), 0.f});
-    }
-#pragma unroll
-    for (int k = 0; k < 2 * G; ++k) tot[k] += ld_coherent(p2 + (int64_t)c * 2 * G + k);
+    for (int k = 0; k < 2 * G; ++k) tot[k] += p2[(int64_t)c * 2 * G + k];
   }
-  float lse2[NR];
 #pragma unroll
-  for (int r = 0; r < NR; ++r) lse2[r] = lse_log2(wave_lse(acc[r]));
-#pragma unroll
-  for (int k = 0; k < 2 * G; ++k) tot[k] = wave_sum(tot[k]);
+  for (int k = 0; k < 2 * G; ++k) tot[k] = wave_total(tot[k]);
   // a call leaves every workspace word it wrote at zero
-  for (int c = lane; c < C; c += 64) {
-#pragma unroll
-    for (int r = 0; r < NR; ++r) put_word(p1 + (int64_t)c * NR + r, 0ull);
-#pragma unroll
-    for (int k = 0; k < 2 * G; ++k) st_coherent(const_cast<float*>(p2) + (int64_t)c * 2 * G + k, 0.f);
-  }
+  float2* p1 = reinterpret_cast<float2*>(a.part1) + (int64_t)t * C * NR;
+  for (int i = lane; i < C * NR; i += 64) p1[i] = make_float2(0.f, 0.f);
+  for (int i = lane; i < C * 2 * G; i += 64) p2[i] = 0.f;
   if (lane == 0) {
     float prod = 1.f, l = 0.f;
     float* sv = a.saved + (int64_t)t * G * kTvSavedStride;
@@ -232,17 +221,17 @@ __global__ __launch_bounds__(64 * kFinishWaves) void tv_fwd_finish(TvArgs a) {
       sv[k * kTvSavedStride + 3] = tot[2 * k + 1];
     }
     if (a.pos_loss) a.pos_loss[t] = l;
-    st_coherent(a.pos_ws + t, l);
+    a.pos_ws[t] = l;
   }
 }
 
-// The mean over positions, in one fixed order.
+// The mean over positions, in one fixed order; clears the per-position losses.
 __global__ __launch_bounds__(kBlock) void tv_fwd_mean(TvArgs a) {
   __shared__ float lds[kWaves];
   float sum[1] = {0.f};
-  for (int i = threadIdx.x; i < a.T; i += kBlock) sum[0] += ld_coherent(a.pos_ws + i);
+  for (int i = threadIdx.x; i < a.T; i += kBlock) sum[0] += a.pos_ws[i];
   block_sum<1>(sum, lds);
-  for (int i = threadIdx.x; i < a.T; i += kBlock) st_coherent(a.pos_ws + i, 0.f);
+  for (int i = threadIdx.x; i < a.T; i += kBlock) a.pos_ws[i] = 0.f;
   if (threadIdx.x == 0) a.loss[0] = sum[0] / (float)a.T;
 }
 
@@ -359,10 +348,12 @@ __global__ __launch_bounds__(kBlock) void tv_bwd_kernel(TvArgs a) {
 // ---------------------------------------------------------------------------
 template <int DT, bool SHARED, int G>
 static hipError_t launch_fwd_g(const TvArgs& a, hipStream_t stream) {
-  const int64_t grid = (int64_t)a.sgroups * a.sp.nchunks * 8;
-  hipLaunchKernelGGL((tv_fwd_main<DT, G, SHARED>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
+  const int64_t grid = (int64_t)a.T * a.sp.nchunks;
+  hipLaunchKernelGGL((tv_fwd_lse<DT, G, SHARED>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((tv_fwd_stats<DT, G, SHARED>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((tv_fwd_finish<G, SHARED>), dim3((unsigned)((a.T + kFinishWaves - 1) / kFinishWaves)),
                      dim3(64 * kFinishWaves), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -390,45 +381,26 @@ hipError_t launch_tv_fwd(const TvArgs& a, int dt, bool shared, hipStream_t strea
   return shared ? launch_fwd_dt<kF32, true>(a, stream) : launch_fwd_dt<kF32, false>(a, stream);
 }
 
+template <int G>
+static int nv_for(int dt, bool shared) {
+  const int pv = dt == kBF16 ? 8 : 4;
+  return shared ? fwd_nv<FwdShape<G, true>::NR>(pv) : fwd_nv<FwdShape<G, false>::NR>(pv);
+}
+
 int tv_fwd_vec_per_thread(int dt, int G, bool shared) {
   switch (G) {
-    case 1: return fwd_nv<1>(dt == kBF16 ? 8 : 4, shared);
-    case 2: return fwd_nv<2>(dt == kBF16 ? 8 : 4, shared);
-    case 3: return fwd_nv<3>(dt == kBF16 ? 8 : 4, shared);
-    case 4: return fwd_nv<4>(dt == kBF16 ? 8 : 4, shared);
-    case 5: return fwd_nv<5>(dt == kBF16 ? 8 : 4, shared);
-    case 6: return fwd_nv<6>(dt == kBF16 ? 8 : 4, shared);
-    case 7: return fwd_nv<7>(dt == kBF16 ? 8 : 4, shared);
-    default: return fwd_nv<8>(dt == kBF16 ? 8 : 4, shared);
+    case 1: return nv_for<1>(dt, shared);
+    case 2: return nv_for<2>(dt, shared);
+    case 3: return nv_for<3>(dt, shared);
+    case 4: return nv_for<4>(dt, shared);
+    case 5: return nv_for<5>(dt, shared);
+    case 6: return nv_for<6>(dt, shared);
+    case 7: return nv_for<7>(dt, shared);
+    default: return nv_for<8>(dt, shared);
   }
 }
 
 int tv_fwd_part1_words(int G, bool shared) { return (shared ? 1 : G) + G; }
-
-template <int DT, bool SHARED, int G>
-static hipError_t occ_g(int* n) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, tv_fwd_main<DT, G, SHARED>, kBlock, 0);
-}
-
-template <int DT, bool SHARED>
-static hipError_t occ_dt(int G, int* n) {
-  switch (G) {
-    case 1: return occ_g<DT, SHARED, 1>(n);
-    case 2: return occ_g<DT, SHARED, 2>(n);
-    case 3: return occ_g<DT, SHARED, 3>(n);
-    case 4: return occ_g<DT, SHARED, 4>(n);
-    case 5: return occ_g<DT, SHARED, 5>(n);
-    case 6: return occ_g<DT, SHARED, 6>(n);
-    case 7: return occ_g<DT, SHARED, 7>(n);
-    case 8: return occ_g<DT, SHARED, 8>(n);
-  }
-  return hipErrorInvalidValue;
-}
-
-hipError_t tv_fwd_occupancy(int dt, int G, bool shared, int* n) {
-  if (dt == kBF16) return shared ? occ_dt<kBF16, true>(G, n) : occ_dt<kBF16, false>(G, n);
-  return shared ? occ_dt<kF32, true>(G, n) : occ_dt<kF32, false>(G, n);
-}
 
 int tv_bwd_vec_per_thread(int dt) { return dt == kBF16 ? kBwdNVBf16 : kBwdNVF32; }
 
