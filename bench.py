@@ -34,6 +34,32 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def profiled_traffic(summary, sources):
+    """HBM bytes per call from a committed rocprofv3 summary (FETCH_SIZE and
+    WRITE_SIZE passes, scaled by a plain copy's reading), or None when the kernel
+    sources have changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", summary)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("|", " ")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip().split()[0] if v.strip() else ""
+    h = hashlib.sha256()
+    for f in sources:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("source_sha256") != h.hexdigest()[:16] or "traffic_bytes_per_call" not in fields:
+        return None
+    return float(fields["traffic_bytes_per_call"])
+
+
+VERIFY_SOURCES = ["tv_loss_amd/csrc/verify.hip", "tv_loss_amd/csrc/device_common.hpp", "tv_loss_amd/csrc/kernels.hpp"]
+TV_SOURCES = ["tv_loss_amd/csrc/tv_loss.hip", "tv_loss_amd/csrc/device_common.hpp", "tv_loss_amd/csrc/kernels.hpp"]
+
+
 def verify_bytes(B, G, V, elem):
     """Algorithmic bytes of one verify call: every logit read once (target B*(G+1)
     rows, draft B*G rows), tokens read, per-row outputs written."""
@@ -141,6 +167,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-tv", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="after the bench, copy BYTES of device memory three times with torch (a plain copy "
+                         "kernel of known size, to calibrate HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -189,8 +218,9 @@ def main():
                                "V=151936, bf16 logits, target N(0,1)/0.7, draft = target + N(0,0.3^2)",
                    "batch": B, "gamma": G, "vocab": V, "storage": "bf16", "input_sets": nsets},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "verify_kernel<bf16>", "bytes_per_launch": alg_bytes,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": profiled_traffic("verify_rollout_64x3_V151936_bf16.md", VERIFY_SOURCES),
+                     "kernel": "verify_main + verify_finish (one mtp_verify call)", "bytes_per_launch": alg_bytes,
                      "kernel_us_mean": kmean * 1e3, "kernel_us_median": ksorted[len(ksorted) // 2] * 1e3},
     }
 
@@ -211,6 +241,11 @@ def main():
             "fwd_ms": fm, "bwd_ms": bm, "fwd_gbs": fwd_bytes / (fm * 1e-3) / 1e9,
             "bwd_gbs": bwd_bytes / (bm * 1e-3) / 1e9, "bytes_fwd": fwd_bytes, "bytes_bwd": bwd_bytes,
             "steps": tv_steps, "wall_ms_per_step": twall / tv_steps * 1e3, "loss": loss,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": profiled_traffic("tv_loss_T8192x3_V151936_bf16.md", TV_SOURCES),
+                         "kernel": "tv_fwd_lse + tv_fwd_stats + tv_fwd_finish + tv_fwd_mean + tv_bwd_kernel",
+                         "bytes_per_launch": fwd_bytes + bwd_bytes},
         }
         log(f"tv loss: fwd {fm:.3f} ms ({fwd_bytes / fm / 1e6:.0f} GB/s), bwd {bm:.3f} ms "
             f"({bwd_bytes / bm / 1e6:.0f} GB/s), total {gbs:.0f} GB/s")
@@ -225,6 +260,14 @@ def main():
                       f"{os.cpu_count()} CPUs",
         }
         log(f"cpu oracle: {n * G / cwall:.1f} positions/s on one core")
+
+    if args.copy_probe > 0:
+        src = torch.ones(args.copy_probe, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     print(json.dumps(result), flush=True)
 

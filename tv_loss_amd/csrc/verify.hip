@@ -16,22 +16,24 @@
 //
 // verify_main streams every logit once.  A "group" is one row of one sequence:
 // (target row, draft row) for k < gamma, or the bonus target row alone.  Each
-// group is split along the vocabulary into C chunks of 4096 elements; C workgroups
-// form a super-group that walks a list of groups ("layers"), chunk c of every group
-// going to workgroup c, and each wave of a workgroup owns a contiguous segment of
-// 1024 elements of the chunk.  The two passes over a chunk are software-pipelined
-// across layers, so that no workgroup waits on its cluster:
-//   layer i:  unpack the chunk of group i (its loads were issued a layer earlier)
-//             and issue the loads of group i + 1;
+// group is split along the vocabulary into C chunks of 4096 elements (3072 for
+// fp32); C workgroups form a super-group that walks a list of groups ("layers"),
+// chunk c of every group going to workgroup c, and each wave of a workgroup owns a
+// contiguous segment of the chunk.  All super-groups are resident at once.  The two
+// passes over a chunk are software-pipelined across layers, so that no workgroup
+// waits on its cluster:
+//   layer i:  row statistics and pass 2 of group i - 2: its C records were polled
+//             a layer ago; merged in one fixed order they give the row
+//             log-sum-exps, and each wave sums r = p - min(p, q) and min(p, q)
+//             (p alone for a bonus row) over its segment from the e values held
+//             in LDS;
+//             group i - 1's e values move from registers to LDS;
+//             unpack the chunk of group i (its loads went out two layers ago),
+//             poll group i - 1's records and issue the loads of group i + 2;
 //             pass 1 on group i: per-wave log-sum-exp partials (both rows, plus
 //             the entropy moment of the target), combined over the workgroup and
-//             published as one self-announcing record;
-//             pass 2 on group i - 1, whose values are still in registers: the C
-//             records of that group were published a layer ago, so polling them
-//             finds them ready; merged (same order everywhere) they give the row
-//             log-sum-exps, and each wave sums r = p - min(p, q) and min(p, q)
-//             (p alone for a bonus row) over its segment.
-// A super-group's workgroups run on one XCD (workgroup i runs on XCD i mod 8).
+//             published as one self-announcing record.
+// Records use device-scope loads and stores, so a super-group may span XCDs.
 //
 // verify_finish runs one workgroup per sequence, one wave per row.  A wave merges
 // the row's records again (lse, entropy), scans the chunk masses, then the segment
