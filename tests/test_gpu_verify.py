@@ -68,6 +68,26 @@ def test_ragged_vocab(V, G, B, dtype):
     compare_verify(out, ref, dtype)
 
 
+@pytest.mark.parametrize("V", [262144, 400003])
+def test_many_chunks_float32(V):
+    """More than 64 (V = 262144) and more than 128 (V = 400003) chunks per row for
+    float32 rows: records beyond the first 64 per lane batch, and chunk masses the
+    finish kernel re-reads instead of keeping in registers."""
+    B, G = 2, 2
+    w = dict(B=B, G=G, V=V, dtype=torch.float32, kind="normal", scale=1.2, sigma=0.5, seed=13)
+    t, d, y = synthetic.verify_inputs(w, DEV, seed=V)
+    pad = (-V) % 4
+    if pad:
+        tp = torch.full((B, G + 1, V + pad), float("-inf"), dtype=torch.float32, device=DEV)
+        dp = torch.full((B, G, V + pad), float("-inf"), dtype=torch.float32, device=DEV)
+        tp[..., :V] = t
+        dp[..., :V] = d
+        t, d = tp[..., :V], dp[..., :V]
+    _say("many chunks", V)
+    out = _run(t, d, y, seed=8, offset=40)
+    compare_verify(out, oracle_verify(t, d, y, 8, 40), torch.float32)
+
+
 def test_rollout_full():
     w = synthetic.VERIFY_WORKLOADS["rollout"]
     t, d, y = synthetic.verify_inputs(w, DEV)

@@ -415,6 +415,7 @@ template <int DT, int NV>
 __global__ void verify_finish(VerifyArgs a) {
   constexpr int PV = Elem<DT>::kPerVec;
   constexpr int kSegVec = NV * 64;
+  constexpr int KC = 2;   // chunks per lane whose pass-2 words are kept in registers
   const int C = a.sp.nchunks;
   const int G = a.G, G1 = G + 1;
   const int b = blockIdx.x;
@@ -428,6 +429,34 @@ __global__ void verify_finish(VerifyArgs a) {
   const __amdgpu_buffer_rsrc_t rs = rsrc_of(a.part1 + (int64_t)g * C * kRecWords);
   uint64_t* p2 = a.part2 + (int64_t)g * C * kWaves;
 
+  // ---- everything that does not depend on the row statistics goes out first ----
+  // lane l owns chunks [l K, l K + K); the pass-2 words of its first KC are kept
+  const int K = (C + 63) / 64;
+  const int c0 = lane * K, c1 = min(C, c0 + K);
+  float seg[KC][kWaves], om_sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < KC; ++i)
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) seg[i][w] = 0.f;
+#pragma unroll
+  for (int i = 0; i < KC; ++i) {
+    if (c0 + i < c1) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const uint64_t v = p2[(int64_t)(c0 + i) * kWaves + w];
+        seg[i][w] = unpack_lo(v);
+        om_sum += unpack_hi(v);
+      }
+    }
+  }
+  for (int cc = c0 + KC; cc < c1; ++cc)
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) om_sum += unpack_hi(p2[(int64_t)cc * kWaves + w]);
+  const int y = pair ? a.tokens[b * G + k] : 0;
+  const bool y_ok = pair && y >= 0 && y < a.V;
+  const float ay = y_ok ? load_one<DT>(trow, y) : 0.f;
+  const float by = y_ok ? load_one<DT>(drow, y) : 0.f;
+
   // ---- row statistics from the pass-1 records ---------------------------------
   const RowStats st = merge_records(rs, C, pair);
   const float lse2_p = lse_log2(st.p);
@@ -438,11 +467,20 @@ __global__ void verify_finish(VerifyArgs a) {
   float u, up;
   row_uniforms(a.seed, a.offset, (uint64_t)g, &u, &up);
 
-  // chunk sums of the pass-2 words: (residual or p mass, overlap)
-  auto chunk_mass = [&](int cc) {
+  // chunk mass (residual, or p for a bonus row) and its segment masses
+  auto seg_mass = [&](int cc, int w) {   // any chunk, from memory
+    return unpack_lo(p2[(int64_t)cc * kWaves + w]);
+  };
+  auto chunk_mass_own = [&](int cc) {    // a chunk of this lane's block
+    const int i = cc - c0;
     float m = 0.f;
+    if (i < KC) {
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i) m += unpack_lo(p2[(int64_t)cc * kWaves + i]);
+      for (int w = 0; w < kWaves; ++w) m += seg[i][w];
+    } else {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) m += seg_mass(cc, w);
+    }
     return m;
   };
   auto pmass = [&](int cc) {   // mass of p in chunk cc, from its record
@@ -454,15 +492,65 @@ __global__ void verify_finish(VerifyArgs a) {
   float alpha = 0.f;
   bool empty_res = false;
   Scan sc{0.f, 0, 0.f};
+  float oseg[kWaves] = {0.f, 0.f, 0.f, 0.f};   // segment masses of the owner chunk
   if (!bad) {
-    sc = wave_scan_owner(C, up, chunk_mass);
-    if (pair) {
-      float om = 0.f;
-      for (int cc = lane; cc < C; cc += 64) {
+    // block sums in lane order, prefix over lanes, then the owner lane walks its block
+    float blk = 0.f;
+    int last_pos = -1;
+    for (int cc = c0; cc < c1; ++cc) {
+      const float m = chunk_mass_own(cc);
+      blk += m;
+      if (m > 0.f) last_pos = cc;
+    }
+    float incl = blk;
 #pragma unroll
-        for (int i = 0; i < kWaves; ++i) om += unpack_hi(p2[(int64_t)cc * kWaves + i]);
+    for (int o = 1; o < 64; o <<= 1) {
+      const float v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    const float ex = __shfl_up(incl, 1, 64);
+    const float excl = lane == 0 ? 0.f : ex;
+    sc.total = __shfl(incl, 63, 64);
+    const float tt = up * sc.total;
+    sc.owner = -1;
+    sc.start = kNegInf;
+    int ol = -1;
+    const uint64_t hit = __ballot(c0 < c1 && incl > tt);
+    if (hit != 0ull && sc.total > 0.f) {
+      ol = __builtin_ctzll(hit);
+      float run = excl;
+      int own = -1;
+      float st0 = kNegInf;
+      for (int cc = c0; cc < c1; ++cc) {
+        const float m = chunk_mass_own(cc);
+        if (own < 0 && run + m > tt) { own = cc; st0 = run; }
+        run += m;
       }
-      alpha = wave_total(om);
+      sc.owner = __shfl(own, ol, 64);
+      sc.start = __shfl(st0, ol, 64);
+    }
+    if (sc.owner < 0) {   // rounding left t past every boundary: last chunk with mass
+      const uint64_t pos = __ballot(last_pos >= 0);
+      ol = pos ? 63 - __builtin_clzll(pos) : 0;
+      sc.owner = pos ? __shfl(last_pos, ol, 64) : 0;
+      sc.start = kNegInf;
+    }
+    // the owner chunk's segment masses, from the lane that holds them
+    const int oi = sc.owner - ol * K;
+    if (oi >= 0 && oi < KC) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        float v = 0.f;
+#pragma unroll
+        for (int i = 0; i < KC; ++i) v = i == oi ? seg[i][w] : v;
+        oseg[w] = __shfl(v, ol, 64);
+      }
+    } else {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) oseg[w] = seg_mass(sc.owner, w);
+    }
+    if (pair) {
+      alpha = wave_total(om_sum);
       if (!(sc.total > 0.f)) {   // the residual has no mass: sample from p
         empty_res = true;
         sc = wave_scan_owner(C, up, pmass);
@@ -476,30 +564,30 @@ __global__ void verify_finish(VerifyArgs a) {
   int token = -1;
   if (!bad) {
     const int oc = sc.owner;
-    const int64_t obeg = (int64_t)oc * a.sp.vec_per_chunk;
-    const int64_t oend = min(obeg + a.sp.vec_per_chunk, a.sp.nvec);
+    const int vpc = (int)a.sp.vec_per_chunk, nvec = (int)a.sp.nvec, nfull = (int)a.sp.nvec_full;
+    const int obeg = oc * vpc;
+    const int oend = min(obeg + vpc, nvec);
+    const int lim = min(oend, nfull);
     // this lane's values of wave segment s: p, or max(0, p - q) for a non-empty residual
     auto seg_values = [&](int s, float (&v)[NV][PV]) {
+      const int s0 = obeg + s * kSegVec;
+      const char* const rows[2] = {trow, use_q ? drow : trow};
+      RawChunk<NV, 2> raw;
+      issue_seg<DT, NV, 2>(raw, rows, s0 + lane, nfull - 1);
+      float x[2][NV * PV];
+      unpack_seg<DT, NV, 2>(raw, rows, s0 + lane, s0 + kSegVec <= lim, lim, nfull, oend, (int)a.V, x);
 #pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        const int64_t vi = obeg + (int64_t)s * kSegVec + j * 64 + lane;
+      for (int j = 0; j < NV; ++j)
 #pragma unroll
         for (int e = 0; e < PV; ++e) {
-          const int64_t idx = vi * PV + e;
-          float xa = kNegInf, xb = kNegInf;
-          if (vi < oend && idx < a.V) {
-            xa = load_one<DT>(trow, idx);
-            if (use_q) xb = load_one<DT>(drow, idx);
-          }
-          const float p = fast_exp2(__builtin_fmaf(xa, kLog2e, -lse2_p));
+          const float p = fast_exp2(__builtin_fmaf(x[0][j * PV + e], kLog2e, -lse2_p));
           if (use_q) {
-            const float q = fast_exp2(__builtin_fmaf(xb, kLog2e, -lse2_q));
+            const float q = fast_exp2(__builtin_fmaf(x[1][j * PV + e], kLog2e, -lse2_q));
             v[j][e] = fmaxf(p - q, 0.f);
           } else {
             v[j][e] = p;
           }
         }
-      }
     };
     const float tl = up * sc.total - sc.start;
     int os = -1;
@@ -523,8 +611,9 @@ __global__ void verify_finish(VerifyArgs a) {
     } else {
       float run = 0.f;
       int lastpos = 0;
+#pragma unroll
       for (int i = 0; i < kWaves; ++i) {
-        const float m = unpack_lo(p2[(int64_t)oc * kWaves + i]);
+        const float m = oseg[i];
         if (m > 0.f) lastpos = i;
         if (os < 0 && run + m > tl) { os = i; seg_start = run; }
         run += m;
@@ -533,7 +622,7 @@ __global__ void verify_finish(VerifyArgs a) {
     }
     seg_values(os, v);
     const int loc = wave_inverse_cdf<NV, PV>(v, tl - seg_start);
-    if (loc >= 0) token = (int)((obeg + (int64_t)os * kSegVec) * PV + loc);
+    if (loc >= 0) token = (obeg + os * kSegVec) * PV + loc;
   }
 
   // clear this row's records and pass-2 words for the next call (the wave has read
@@ -543,7 +632,7 @@ __global__ void verify_finish(VerifyArgs a) {
     rec_store(rs, cc * 24 + 8, 0ull);
     rec_store(rs, cc * 24 + 16, 0ull);
   }
-  for (int64_t i = lane; i < (int64_t)C * kWaves; i += 64) p2[i] = 0ull;
+  for (int i = lane; i < C * kWaves; i += 64) p2[i] = 0ull;
 
   if (lane == 0) {
     int status = 0;
@@ -553,11 +642,9 @@ __global__ void verify_finish(VerifyArgs a) {
     int flag = 0;
     const float nan = __builtin_nanf("");
     if (pair) {
-      const int y = a.tokens[b * G + k];
-      if (y < 0 || y >= a.V) {
+      if (!y_ok) {
         status |= kRowBadToken;
       } else if (!bad) {
-        const float ay = load_one<DT>(trow, y), by = load_one<DT>(drow, y);
         const float d = __builtin_fmaf(ay, kLog2e, -lse2_p) - __builtin_fmaf(by, kLog2e, -lse2_q);
         if (d == d) flag = u < fminf(1.f, fast_exp2(d)) ? 1 : 0;
       }
