@@ -93,7 +93,7 @@ struct VerifyLayout {
 
 VerifyLayout verify_layout(int32_t B, int32_t G, int32_t V, mtp_dtype dt) {
   VerifyLayout L{};
-  L.sp = mtp::make_split(V, per_vec(dt), mtp::verify_vec_per_thread(dt));
+  L.sp = mtp::make_split(V, per_vec(dt), mtp::verify_vec_per_thread(dt), false);
   L.ngroups = (int64_t)B * (G + 1);
   const int64_t C = L.sp.nchunks;
   size_t off = 0;
@@ -111,7 +111,7 @@ struct TvLayout {
 
 TvLayout tv_layout(int32_t T, int32_t G, int32_t V, mtp_dtype dt, bool shared) {
   TvLayout L{};
-  L.sp = mtp::make_split(V, per_vec(dt), mtp::tv_fwd_vec_per_thread(dt, G, shared));
+  L.sp = mtp::make_split(V, per_vec(dt), mtp::tv_fwd_vec_per_thread(dt, G, shared), false);
   const int64_t C = L.sp.nchunks;
   size_t off = 0;
   L.err = off; off = align256(off + 4);

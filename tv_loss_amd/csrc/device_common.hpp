@@ -45,13 +45,16 @@ struct RowSplit {
   int nchunks;
 };
 
-__host__ __device__ inline RowSplit make_split(int64_t V, int per_vec, int vec_per_thread) {
+// balanced: chunks of equal size (each a little under the capacity); otherwise
+// every chunk but the last is full, so that only the last chunk has partly filled
+// wave segments.
+__host__ __device__ inline RowSplit make_split(int64_t V, int per_vec, int vec_per_thread, bool balanced = true) {
   RowSplit s;
   s.nvec = (V + per_vec - 1) / per_vec;
   s.nvec_full = V / per_vec;
   const int64_t cap = (int64_t)kBlock * vec_per_thread;
   s.nchunks = (int)((s.nvec + cap - 1) / cap);
-  s.vec_per_chunk = (s.nvec + s.nchunks - 1) / s.nchunks;
+  s.vec_per_chunk = balanced ? (s.nvec + s.nchunks - 1) / s.nchunks : cap;
   return s;
 }
 
@@ -393,13 +396,15 @@ __device__ __forceinline__ float wave_total(float v) {
 // NaN-propagating maximum (IEEE maximum: no canonicalisation of the operands).
 __device__ __forceinline__ float fmaximum(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
+// A lane whose DPP source is out of range (or whose row is masked off) gets its own
+// value back, which leaves the maximum unchanged.
 __device__ __forceinline__ float wave_maximum(float v) {
-  v = fmaximum(v, dpp_mov<0x111, 0xf>(kNegInf, v));
-  v = fmaximum(v, dpp_mov<0x112, 0xf>(kNegInf, v));
-  v = fmaximum(v, dpp_mov<0x114, 0xf>(kNegInf, v));
-  v = fmaximum(v, dpp_mov<0x118, 0xf>(kNegInf, v));
-  v = fmaximum(v, dpp_mov<0x142, 0xa>(kNegInf, v));
-  v = fmaximum(v, dpp_mov<0x143, 0xc>(kNegInf, v));
+  v = fmaximum(v, dpp_mov<0x111, 0xf>(v, v));
+  v = fmaximum(v, dpp_mov<0x112, 0xf>(v, v));
+  v = fmaximum(v, dpp_mov<0x114, 0xf>(v, v));
+  v = fmaximum(v, dpp_mov<0x118, 0xf>(v, v));
+  v = fmaximum(v, dpp_mov<0x142, 0xa>(v, v));
+  v = fmaximum(v, dpp_mov<0x143, 0xc>(v, v));
   return lane63(v);
 }
 
@@ -410,10 +415,10 @@ __device__ __forceinline__ Lse lse_nan() {
 
 // Log-sum-exp partials of R rows over a wave, the rows interleaved so that their
 // dependency chains overlap.  For row r the wave's largest logit M is the reference
-// (ref = M log2 e; 0 when the wave holds only -inf), x[r] is overwritten with
-// e = 2^(x log2 e - ref) and the sums of e, and for r < RY of e * (x log2 e - ref)
-// (the entropy moment), are taken over the wave.  A wave holding only -inf gives
-// z = 0 (an empty partial, e = 0); a NaN gives z = NaN.  The entropy moment is
+// (ref = M log2 e), x[r] is overwritten with e = 2^(x log2 e - ref) and the sums of
+// e, and for r < RY of e * (x log2 e - ref) (the entropy moment), are taken over the
+// wave.  A wave holding only -inf gives the empty partial (ref = -inf, z = 0, e = 0);
+// a NaN gives z = NaN.  The entropy moment is
 // accumulated without guarding 0 * (-inf); if that produced a NaN it is summed again
 // from the e values alone (e log2 e over e > 0).
 template <int NE, int R, int RY>
@@ -431,7 +436,7 @@ __device__ __forceinline__ void wave_pass1(float (&x)[R][NE], Lse (&out)[R]) {
   float ref[R], z0[R], z1[R], y0[R], y1[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    ref[r] = M[r] > kNegInf ? M[r] * kLog2e : 0.f;
+    ref[r] = M[r] > kNegInf ? M[r] * kLog2e : 0.f;   // 0 keeps -inf - ref = -inf
     z0[r] = z1[r] = y0[r] = y1[r] = 0.f;
   }
 #pragma unroll
@@ -464,26 +469,26 @@ __device__ __forceinline__ void wave_pass1(float (&x)[R][NE], Lse (&out)[R]) {
     }
   }
 #pragma unroll
-  for (int r = 0; r < R; ++r) out[r] = Lse{ref[r], Z[r], Y[r]};
+  for (int r = 0; r < R; ++r) out[r] = Lse{M[r] * kLog2e, Z[r], Y[r]};   // ref -inf when empty
 }
 
 // Merge of per-lane partials of R rows into one per row, the same bits in every
-// lane; rows r < RY merge the entropy moment too.  A partial with z = 0 is empty;
-// a NaN z or ref propagates into the result (z != 0 keeps it live, the maximum
-// propagates a NaN reference); a row with no live partial gives ref = -inf, z = 0.
+// lane; rows r < RY merge the entropy moment too.  An empty partial is (ref = -inf,
+// z = 0, y = 0) and weighs 2^(-inf) = 0; a row with only empty partials gives the
+// empty partial; a NaN reference or sum propagates.
+__device__ __forceinline__ float finite_ref(float R) { return R == kNegInf ? -__FLT_MAX__ : R; }
+
 template <int R, int RY>
 __device__ __forceinline__ void wave_merge(Lse (&s)[R]) {
-  float Rm[R];
+  float Rm[R], zc[R], yc[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) Rm[r] = wave_maximum(s[r].z != 0.f ? s[r].ref : kNegInf);
-  float zc[R], yc[R];
+  for (int r = 0; r < R; ++r) Rm[r] = wave_maximum(s[r].ref);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const bool live = s[r].z != 0.f;
-    const float d = live ? s[r].ref - Rm[r] : 0.f;
+    const float d = s[r].ref - finite_ref(Rm[r]);
     const float f = fast_exp2(d);
-    zc[r] = live ? s[r].z * f : 0.f;
-    yc[r] = live && r < RY ? __builtin_fmaf(d, s[r].z, s[r].y) * f : 0.f;
+    zc[r] = s[r].z * f;
+    yc[r] = r < RY ? __builtin_fmaf(fmaxf(d, -1e30f), s[r].z, s[r].y) * f : 0.f;
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) s[r] = Lse{Rm[r], wave_total(zc[r]), r < RY ? wave_total(yc[r]) : 0.f};
@@ -498,16 +503,16 @@ __device__ __forceinline__ Lse merge_lds(const float* p) {
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     ref[i] = p[3 * i]; z[i] = p[3 * i + 1]; y[i] = kY ? p[3 * i + 2] : 0.f;
-    R = fmaximum(R, z[i] != 0.f ? ref[i] : kNegInf);
+    R = fmaximum(R, ref[i]);
   }
+  const float Rf = finite_ref(R);
   float Z = 0.f, Y = 0.f;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    const bool live = z[i] != 0.f;
-    const float d = live ? ref[i] - R : 0.f;
+    const float d = ref[i] - Rf;
     const float f = fast_exp2(d);
-    Z = __builtin_fmaf(live ? z[i] : 0.f, f, Z);
-    if constexpr (kY) Y = __builtin_fmaf(live ? __builtin_fmaf(d, z[i], y[i]) : 0.f, f, Y);
+    Z = __builtin_fmaf(z[i], f, Z);
+    if constexpr (kY) Y = __builtin_fmaf(__builtin_fmaf(fmaxf(d, -1e30f), z[i], y[i]), f, Y);
   }
   return Lse{R, Z, Y};
 }
@@ -546,19 +551,21 @@ __device__ __forceinline__ void issue_seg(RawChunk<NV, R>& raw, const char* cons
 }
 
 // The same loads with a fixed count: all R rows (pass the same row twice when
-// there is only one) and, when `live` is false, a single 16-byte location for every
-// lane (rows[0] + 0) instead of the chunk.  A load count that does not depend on
-// the item lets the compiler wait for exactly the loads it needs.
+// there is only one), every row read through a buffer descriptor bounded by the
+// row's `row_bytes` (a read past it returns zeros); when `live` is false, or the row
+// has no full vector, every lane reads offset 0.  A load count that does not depend
+// on the item lets the compiler wait for exactly the loads it needs.
 template <int DT, int NV, int R>
 __device__ __forceinline__ void issue_seg_fixed(RawChunk<NV, R>& raw, const char* const (&rows)[R], int v0,
-                                                int last, bool live) {
+                                                int last, bool live, int row_bytes) {
+  const bool ok = live && last >= 0;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const int off = live ? min(v0 + j * 64, max(last, 0)) * 16 : 0;
+    const int off = ok ? min(v0 + j * 64, last) * 16 : 0;
 #pragma unroll
     for (int r = 0; r < R; ++r)
       raw.v[r][j] = __builtin_amdgcn_raw_buffer_load_b128(
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(rows[r]), 0, 0x7fffffff, 0x00020000), off, 0, kStreamCpol);
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(rows[r]), 0, row_bytes, 0x00020000), off, 0, kStreamCpol);
   }
 }
 

@@ -177,18 +177,22 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
   __shared__ float part_sh[2][2][kWaves * 3];
   __shared__ float lse_sh[2][2];
 
-  // the chunks of items i + 1 and i + 2 are in flight while item i is processed
   // the chunks of items i + 1 and i + 2 are in flight while item i is processed;
-  // every prefetch issues the same number of loads (see issue_seg_fixed)
+  // every prefetch issues the same number of loads (see issue_seg_fixed).  A
+  // prefetch past the end of the list (live false) names an item of the list (the
+  // window below only ever holds such items) and reads at offset 0.
+  const int row_bytes = (int)min(a.V * Elem<DT>::kBytes, (int64_t)0x7fffffff);
   auto prefetch = [&](RawChunk<NV, 2>& rb, int g, bool live) {
     const char* const rows[2] = {trow_of(g), drow_of(g)};
-    issue_seg_fixed<DT, NV, 2>(rb, rows, v0, last, live);
+    issue_seg_fixed<DT, NV, 2>(rb, rows, v0, last, live, row_bytes);
   };
   RawChunk<NV, 2> rawA, rawB;
+  // groups of items i, i + 1 of the current layer (past the end: an earlier item)
   int g_0 = group_of(0), g_p1 = nl > 1 ? group_of(1) : g_0;
   prefetch(rawA, g_0, true);
   prefetch(rawB, g_p1, nl > 1);
-  int g_m2 = 0, g_m1 = 0;
+  int g_m2 = 0, g_m1 = 0;          // groups of items i - 2 and i - 1
+  bool pair_m2 = false, pair_m1 = false;
   uint64_t wpoll = 0ull;                     // this lane's polled record word
   float x[2][NE];                            // item i - 1's e values between layers
   float xref[2] = {0.f, 0.f};                // ... and this wave's references for them
@@ -201,7 +205,7 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
   auto layer = [&](int i, RawChunk<NV, 2>& rb) __attribute__((always_inline)) {
     // ---- row statistics of item i - 2 (polled a layer ago) ---------------------
     if (i >= 2 && i - 2 < nl) {
-      const bool pair2 = is_pair(g_m2);
+      const bool pair2 = pair_m2;
       if (wave == wp || (wave == wq && pair2)) {
         const int row = wave == wp ? 0 : 1;
         const Lse st = poll_row(wpoll, rsrc_rec(g_m2), C, row, a.err);
@@ -209,34 +213,38 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
       }
       __syncthreads();
       // ---- pass 2 of item i - 2 ------------------------------------------------
-      const float sa = fast_exp2(href[0] - lse_sh[i & 1][0]);
+      // in this wave's e units: p = sa e_p, q = sa rho e_q with rho = sb / sa, so
+      // min(p, q) = sa min(e_p, rho e_q) and max(0, p - q) = sa (e_p - min(...))
+      const float la = href[0] - lse_sh[i & 1][0];   // log2 of sa (-inf: no p mass here)
+      const float sa = fast_exp2(la);
       float rm0 = 0.f, rm1 = 0.f, om0 = 0.f, om1 = 0.f;
       if (pair2) {
-        const float sb = fast_exp2(href[1] - lse_sh[i & 1][1]);
+        if (la != kNegInf) {
+          const float rho = fast_exp2(href[1] - lse_sh[i & 1][1] - la);
 #pragma unroll
-        for (int qi = 0; qi < NQ; ++qi) {
-          const float4 ea = held[0][qi][t], eb = held[1][qi][t];
-          const float va[4] = {ea.x, ea.y, ea.z, ea.w}, vb[4] = {eb.x, eb.y, eb.z, eb.w};
+          for (int qi = 0; qi < NQ; ++qi) {
+            const float4 ea = held[0][qi][t], eb = held[1][qi][t];
+            const float va[4] = {ea.x, ea.y, ea.z, ea.w}, vb[4] = {eb.x, eb.y, eb.z, eb.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
+            for (int e = 0; e < 4; ++e) {
 #pragma clang fp contract(off)
-            const float p = va[e] * sa, q = vb[e] * sb;
-            const float m = fminf(p, q);
-            if (e & 1) { rm1 += p - m; om1 += m; } else { rm0 += p - m; om0 += m; }   // p - m = max(0, p - q)
+              const float m = __builtin_elementwise_minimum(va[e], vb[e] * rho);
+              if (e & 1) { rm1 += va[e] - m; om1 += m; } else { rm0 += va[e] - m; om0 += m; }
+            }
           }
         }
       } else {
 #pragma unroll
         for (int qi = 0; qi < NQ; ++qi) {
           const float4 ea = held[0][qi][t];
-          rm0 = __builtin_fmaf(ea.x, sa, rm0);
-          rm1 = __builtin_fmaf(ea.y, sa, rm1);
-          rm0 = __builtin_fmaf(ea.z, sa, rm0);
-          rm1 = __builtin_fmaf(ea.w, sa, rm1);
+          rm0 += ea.x;
+          rm1 += ea.y;
+          rm0 += ea.z;
+          rm1 += ea.w;
         }
       }
-      const float rm = wave_total(rm0 + rm1);
-      const float om = wave_total(om0 + om1);
+      const float rm = sa * wave_total(rm0 + rm1);
+      const float om = sa * wave_total(om0 + om1);
       if (lane == 0) a.part2[((int64_t)g_m2 * C + c) * kWaves + wave] = pack2(rm, pair2 ? om : 0.f);
     }
     // ---- item i - 1 moves to LDS (own slots only) ------------------------------
@@ -299,7 +307,9 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
     }
     // ---- shift the item window -------------------------------------------------
     g_m2 = g_m1;
+    pair_m2 = pair_m1;
     g_m1 = g_0;
+    pair_m1 = pair;
     g_0 = g_p1;
     g_p1 = g_p2;
   };
