@@ -197,6 +197,7 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
   float x[2][NE];                            // item i - 1's e values between layers
   float xref[2] = {0.f, 0.f};                // ... and this wave's references for them
   float href[2] = {0.f, 0.f};                // references of the item held in LDS
+  float xz = 0.f, hz = 0.f;                  // this wave's p mass (e units) of each
 
   // Layer i: statistics and pass 2 of item i - 2 (held in LDS), item i - 1 moves
   // from registers to LDS, item i is unpacked from buffer i & 1, the poll for item
@@ -213,39 +214,53 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
       }
       __syncthreads();
       // ---- pass 2 of item i - 2 ------------------------------------------------
-      // in this wave's e units: p = sa e_p, q = sa rho e_q with rho = sb / sa, so
-      // min(p, q) = sa min(e_p, rho e_q) and max(0, p - q) = sa (e_p - min(...))
+      // In this wave's e units p = sa e_p and q = sb e_q.  While rho = sb / sa is at
+      // most 2^64, max(0, p - q) = sa max(0, e_p - rho e_q) (one rounding) and the
+      // overlap is the wave's p mass minus the residual, both summed in pass 1's
+      // order, so disjoint supports give an overlap of exactly 0.  A larger rho (q
+      // outweighs p here by more than 2^64) works in q's units instead.
       const float la = href[0] - lse_sh[i & 1][0];   // log2 of sa (-inf: no p mass here)
       const float sa = fast_exp2(la);
-      float rm0 = 0.f, rm1 = 0.f, om0 = 0.f, om1 = 0.f;
-      if (pair2) {
-        if (la != kNegInf) {
-          const float rho = fast_exp2(href[1] - lse_sh[i & 1][1] - la);
+      float rm = 0.f, om = 0.f;
+      if (!pair2) {
+        rm = sa * hz;
+      } else if (la != kNegInf) {
+        const float lr = href[1] - lse_sh[i & 1][1] - la;   // log2 of rho
+        float r0 = 0.f, r1 = 0.f;
+        if (!(lr > 64.f)) {
+          const float rho = fast_exp2(lr);
 #pragma unroll
           for (int qi = 0; qi < NQ; ++qi) {
             const float4 ea = held[0][qi][t], eb = held[1][qi][t];
             const float va[4] = {ea.x, ea.y, ea.z, ea.w}, vb[4] = {eb.x, eb.y, eb.z, eb.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-#pragma clang fp contract(off)
-              const float m = __builtin_elementwise_minimum(va[e], vb[e] * rho);
-              if (e & 1) { rm1 += va[e] - m; om1 += m; } else { rm0 += va[e] - m; om0 += m; }
+              const float d = fmaxf(__builtin_fmaf(-rho, vb[e], va[e]), 0.f);
+              if (e & 1) r1 += d; else r0 += d;
             }
           }
-        }
-      } else {
+          const float rw = wave_total(r0 + r1);
+          rm = sa * rw;
+          om = sa * fmaxf(hz - rw, 0.f);
+        } else {
+          const float rr = fast_exp2(-lr), sb = fast_exp2(href[1] - lse_sh[i & 1][1]);   // rr = 1 / rho
+          float o0 = 0.f, o1 = 0.f;
+#pragma unroll 1
+          for (int qi = 0; qi < NQ; ++qi) {
+            const float4 ea = held[0][qi][t], eb = held[1][qi][t];
+            const float va[4] = {ea.x, ea.y, ea.z, ea.w}, vb[4] = {eb.x, eb.y, eb.z, eb.w};
 #pragma unroll
-        for (int qi = 0; qi < NQ; ++qi) {
-          const float4 ea = held[0][qi][t];
-          rm0 += ea.x;
-          rm1 += ea.y;
-          rm0 += ea.z;
-          rm1 += ea.w;
+            for (int e = 0; e < 4; ++e) {
+              const float d = fmaxf(__builtin_fmaf(rr, va[e], -vb[e]), 0.f);
+              const float m = __builtin_elementwise_minimum(rr * va[e], vb[e]);
+              if (e & 1) { r1 += d; o1 += m; } else { r0 += d; o0 += m; }
+            }
+          }
+          rm = sb * wave_total(r0 + r1);
+          om = sb * wave_total(o0 + o1);
         }
       }
-      const float rm = sa * wave_total(rm0 + rm1);
-      const float om = sa * wave_total(om0 + om1);
-      if (lane == 0) a.part2[((int64_t)g_m2 * C + c) * kWaves + wave] = pack2(rm, pair2 ? om : 0.f);
+      if (lane == 0) a.part2[((int64_t)g_m2 * C + c) * kWaves + wave] = pack2(rm, om);
     }
     // ---- item i - 1 moves to LDS (own slots only) ------------------------------
     if (i >= 1 && i - 1 < nl) {
@@ -256,6 +271,7 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
       }
       href[0] = xref[0];
       href[1] = xref[1];
+      hz = xz;
     }
 
     // ---- item i: unpack, then the poll for item i - 1 and the loads of i + 2 ----
@@ -286,6 +302,7 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
       }
       xref[0] = pt[0].ref;
       xref[1] = pt[1].ref;
+      xz = pt[0].z;
       if (lane == 0) {
         float* ps = part_sh[i & 1][0];
         ps[wave * 3 + 0] = pt[0].ref; ps[wave * 3 + 1] = pt[0].z; ps[wave * 3 + 2] = pt[0].y;
