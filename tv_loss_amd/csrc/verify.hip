@@ -131,10 +131,11 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
   const int B = a.B, G = a.G, G1 = G + 1;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = threadIdx.x;
-  // the p and q rows' bookkeeping (combining partials, publishing, polling) is
-  // done by two different waves, rotated over the workgroups so that it spreads
-  // over the SIMDs
-  const int wp = (slot + c) & (kWaves - 1), wq = wp ^ 1;
+  // the rows' bookkeeping is one task per wave (combine and publish p, the same for
+  // q, poll p's records, poll q's), so that none of it runs back to back on one
+  // wave; the roles rotate over the workgroups so that they spread over the SIMDs
+  const int wp = (slot + c) & (kWaves - 1), wq = wp ^ 1;   // combine and publish p / q
+  const int rp = wp ^ 2, rq = wp ^ 3;                     // poll p / q records
 
   // item i of super-group sg is row w = sg + i S; rows are taken k-major (all
   // k = 0 rows first), so every super-group sees the same mix of pair and bonus
@@ -207,8 +208,8 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
     // ---- row statistics of item i - 2 (polled a layer ago) ---------------------
     if (i >= 2 && i - 2 < nl) {
       const bool pair2 = pair_m2;
-      if (wave == wp || (wave == wq && pair2)) {
-        const int row = wave == wp ? 0 : 1;
+      if (wave == rp || (wave == rq && pair2)) {
+        const int row = wave == rp ? 0 : 1;
         const Lse st = poll_row(wpoll, rsrc_rec(g_m2), C, row, a.err);
         if (lane == 0) lse_sh[i & 1][row] = lse_log2(st);
       }
@@ -284,8 +285,8 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
     }
     // the poll goes out before the prefetch, so that waiting for it (a layer
     // later) does not wait for the prefetch
-    if (i >= 1 && i <= nl && (wave == wp || wave == wq) && lane < C)
-      wpoll = rec_load(rsrc_rec(g_m1), lane * 24 + (wave == wp ? 0 : 8));
+    if (i >= 1 && i <= nl && (wave == rp || wave == rq) && lane < C)
+      wpoll = rec_load(rsrc_rec(g_m1), lane * 24 + (wave == rp ? 0 : 8));
     __builtin_amdgcn_sched_barrier(0);
     const int g_p2 = i + 2 < nl ? group_of(i + 2) : g_0;
     prefetch(rb, g_p2, i + 2 < nl);
