@@ -129,7 +129,7 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
   const int sg = slot / C, c = slot - sg * C;
   const int S = a.sgroups;
   const int B = a.B, G = a.G, G1 = G + 1;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int t = threadIdx.x;
   // the rows' bookkeeping is one task per wave (combine and publish p, the same for
   // q, poll p's records, poll q's), so that none of it runs back to back on one
@@ -281,7 +281,11 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
       const char* const rows[2] = {trow_of(g_0), drow_of(g_0)};
       // both rows always (a bonus item's second row is its target row again), so
       // that every load of the buffer is consumed before the buffer is refilled
-      unpack_seg<DT, NV, 2>(rb, rows, v0, full, lim, tail, vend, V, x, 2);
+      // the bounds pass through an empty asm so that the masks of the partial
+      // segment path are derived there, not kept live across the loop
+      int lim_l = lim, tail_l = tail, vend_l = vend, V_l = V;
+      asm volatile("" : "+s"(lim_l), "+s"(tail_l), "+s"(vend_l), "+s"(V_l));
+      unpack_seg<DT, NV, 2>(rb, rows, v0, full, lim_l, tail_l, vend_l, V_l, x, 2);
     }
     // the poll goes out before the prefetch, so that waiting for it (a layer
     // later) does not wait for the prefetch
