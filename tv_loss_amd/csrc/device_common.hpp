@@ -373,39 +373,77 @@ __device__ __forceinline__ void block_zero(float* p, int64_t n) {
 }
 
 // ---------------------------------------------------------------------------
-// Wave reductions with DPP (gfx9): prefix steps row_shr:1,2,4,8 inside each row of
-// 16 lanes, then row_bcast:15 and row_bcast:31 carry the row totals up, so lane 63
-// ends with the total; readlane hands its bits to every lane.  The order of the
-// operations is fixed, so equal inputs give equal bits in every kernel.
-template <int kCtrl, int kRowMask>
-__device__ __forceinline__ float dpp_mov(float old, float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), kCtrl, kRowMask, 0xf, false));
-}
+// Wave reductions as in-place DPP chains: each step is one fused VALU op
+// v = op(v[source lane], v) over row_shr 1, 2, 4, 8, then row_bcast 15 (rows 1 and
+// 3) and row_bcast 31 (rows 2 and 3), so lane 63 ends with the result.  A lane
+// whose source is out of range or whose row is masked off is not written and keeps
+// its own value (the identity of both operations).  N independent values run
+// interleaved, so that their steps fill each other's DPP read delay (a VALU write
+// must be two wait states ahead of a DPP read of the same register); s_nop covers
+// what they do not, and the leading s_nop covers an EXEC write just before.  All
+// lanes must be active.
+#define MTP_DPP_STEP(OP, R, CTRL, MASK) "v_" OP "_f32_dpp " R ", " R ", " R " " CTRL " row_mask:" MASK " bank_mask:0xf\n\t"
+#define MTP_DPP_CHAIN1(OP)                                                                                  \
+  "s_nop 4\n\t" MTP_DPP_STEP(OP, "%0", "row_shr:1", "0xf") "s_nop 1\n\t" MTP_DPP_STEP(OP, "%0", "row_shr:2", "0xf") \
+  "s_nop 1\n\t" MTP_DPP_STEP(OP, "%0", "row_shr:4", "0xf") "s_nop 1\n\t" MTP_DPP_STEP(OP, "%0", "row_shr:8", "0xf") \
+  "s_nop 1\n\t" MTP_DPP_STEP(OP, "%0", "row_bcast:15", "0xa") "s_nop 1\n\t"                                     \
+  MTP_DPP_STEP(OP, "%0", "row_bcast:31", "0xc") "s_nop 1"
+#define MTP_DPP_PAIR(OP, CTRL, MASK) MTP_DPP_STEP(OP, "%0", CTRL, MASK) MTP_DPP_STEP(OP, "%1", CTRL, MASK)
+#define MTP_DPP_CHAIN2(OP)                                                                              \
+  "s_nop 4\n\t" MTP_DPP_PAIR(OP, "row_shr:1", "0xf") "s_nop 0\n\t" MTP_DPP_PAIR(OP, "row_shr:2", "0xf")   \
+  "s_nop 0\n\t" MTP_DPP_PAIR(OP, "row_shr:4", "0xf") "s_nop 0\n\t" MTP_DPP_PAIR(OP, "row_shr:8", "0xf")   \
+  "s_nop 0\n\t" MTP_DPP_PAIR(OP, "row_bcast:15", "0xa") "s_nop 0\n\t" MTP_DPP_PAIR(OP, "row_bcast:31", "0xc") \
+  "s_nop 1"
+#define MTP_DPP_TRIPLE(OP, CTRL, MASK) MTP_DPP_PAIR(OP, CTRL, MASK) MTP_DPP_STEP(OP, "%2", CTRL, MASK)
+#define MTP_DPP_CHAIN3(OP)                                                                                    \
+  "s_nop 4\n\t" MTP_DPP_TRIPLE(OP, "row_shr:1", "0xf") MTP_DPP_TRIPLE(OP, "row_shr:2", "0xf")                  \
+  MTP_DPP_TRIPLE(OP, "row_shr:4", "0xf") MTP_DPP_TRIPLE(OP, "row_shr:8", "0xf")                               \
+  MTP_DPP_TRIPLE(OP, "row_bcast:15", "0xa") MTP_DPP_TRIPLE(OP, "row_bcast:31", "0xc") "s_nop 1"
+
 __device__ __forceinline__ float lane63(float v) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63)); }
 
+// In place: v[i] becomes the wave's sum (kMax false) or maximum (kMax true) of
+// v[i], in every lane's copy of the returned value.  The maximum ignores a NaN
+// operand (v_max_f32); callers propagate NaNs through the sums instead.
+template <bool kMax, int N>
+__device__ __forceinline__ void wave_reduce(float (&v)[N]) {
+  static_assert(N >= 1, "at least one value");
+  if constexpr (N > 3) {   // groups of three
+    float a[3] = {v[0], v[1], v[2]}, b[N - 3];
+#pragma unroll
+    for (int i = 3; i < N; ++i) b[i - 3] = v[i];
+    wave_reduce<kMax, 3>(a);
+    wave_reduce<kMax, N - 3>(b);
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = i < 3 ? a[i] : b[i - 3];
+    return;
+  } else if constexpr (N == 1) {
+    if constexpr (kMax) asm volatile(MTP_DPP_CHAIN1("max") : "+v"(v[0]));
+    else asm volatile(MTP_DPP_CHAIN1("add") : "+v"(v[0]));
+  } else if constexpr (N == 2) {
+    if constexpr (kMax) asm volatile(MTP_DPP_CHAIN2("max") : "+v"(v[0]), "+v"(v[1]));
+    else asm volatile(MTP_DPP_CHAIN2("add") : "+v"(v[0]), "+v"(v[1]));
+  } else {
+    if constexpr (kMax) asm volatile(MTP_DPP_CHAIN3("max") : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]));
+    else asm volatile(MTP_DPP_CHAIN3("add") : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]));
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = lane63(v[i]);
+}
+
 __device__ __forceinline__ float wave_total(float v) {
-  v += dpp_mov<0x111, 0xf>(0.f, v);
-  v += dpp_mov<0x112, 0xf>(0.f, v);
-  v += dpp_mov<0x114, 0xf>(0.f, v);
-  v += dpp_mov<0x118, 0xf>(0.f, v);
-  v += dpp_mov<0x142, 0xa>(0.f, v);
-  v += dpp_mov<0x143, 0xc>(0.f, v);
-  return lane63(v);
+  float a[1] = {v};
+  wave_reduce<false, 1>(a);
+  return a[0];
 }
 
 // NaN-propagating maximum (IEEE maximum: no canonicalisation of the operands).
 __device__ __forceinline__ float fmaximum(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
-// A lane whose DPP source is out of range (or whose row is masked off) gets its own
-// value back, which leaves the maximum unchanged.
 __device__ __forceinline__ float wave_maximum(float v) {
-  v = fmaximum(v, dpp_mov<0x111, 0xf>(v, v));
-  v = fmaximum(v, dpp_mov<0x112, 0xf>(v, v));
-  v = fmaximum(v, dpp_mov<0x114, 0xf>(v, v));
-  v = fmaximum(v, dpp_mov<0x118, 0xf>(v, v));
-  v = fmaximum(v, dpp_mov<0x142, 0xa>(v, v));
-  v = fmaximum(v, dpp_mov<0x143, 0xc>(v, v));
-  return lane63(v);
+  float a[1] = {v};
+  wave_reduce<true, 1>(a);
+  return a[0];
 }
 
 __device__ __forceinline__ Lse lse_nan() {
@@ -431,8 +469,7 @@ __device__ __forceinline__ void wave_pass1(float (&x)[R][NE], Lse (&out)[R]) {
     for (int i = 1; i < NE; ++i) m = fmaximum(m, x[r][i]);
     M[r] = m;
   }
-#pragma unroll
-  for (int r = 0; r < R; ++r) M[r] = wave_maximum(M[r]);
+  wave_reduce<true, R>(M);
   float ref[R], z0[R], z1[R], y0[R], y1[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -452,11 +489,17 @@ __device__ __forceinline__ void wave_pass1(float (&x)[R][NE], Lse (&out)[R]) {
       x[r][i] = e;
     }
   }
-  float Z[R], Y[R];
+  // the R + RY sums in one interleaved chain
+  float zy[R + RY], Z[R], Y[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) zy[r] = z0[r] + z1[r];
+#pragma unroll
+  for (int r = 0; r < RY; ++r) zy[R + r] = y0[r] + y1[r];
+  wave_reduce<false, R + RY>(zy);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    Z[r] = wave_total(z0[r] + z1[r]);
-    Y[r] = r < RY ? wave_total(y0[r] + y1[r]) : 0.f;
+    Z[r] = zy[r];
+    Y[r] = r < RY ? zy[R + r] : 0.f;
   }
 #pragma unroll
   for (int r = 0; r < RY; ++r) {
@@ -482,7 +525,8 @@ template <int R, int RY>
 __device__ __forceinline__ void wave_merge(Lse (&s)[R]) {
   float Rm[R], zc[R], yc[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) Rm[r] = wave_maximum(s[r].ref);
+  for (int r = 0; r < R; ++r) Rm[r] = s[r].ref;
+  wave_reduce<true, R>(Rm);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const float d = s[r].ref - finite_ref(Rm[r]);
@@ -490,8 +534,14 @@ __device__ __forceinline__ void wave_merge(Lse (&s)[R]) {
     zc[r] = s[r].z * f;
     yc[r] = r < RY ? __builtin_fmaf(fmaxf(d, -1e30f), s[r].z, s[r].y) * f : 0.f;
   }
+  float zy[R + RY];
 #pragma unroll
-  for (int r = 0; r < R; ++r) s[r] = Lse{Rm[r], wave_total(zc[r]), r < RY ? wave_total(yc[r]) : 0.f};
+  for (int r = 0; r < R; ++r) zy[r] = zc[r];
+#pragma unroll
+  for (int r = 0; r < RY; ++r) zy[R + r] = yc[r];
+  wave_reduce<false, R + RY>(zy);
+#pragma unroll
+  for (int r = 0; r < R; ++r) s[r] = Lse{Rm[r], zy[r], r < RY ? zy[R + r] : 0.f};
 }
 
 // Merge of N partials held in LDS (stride 3 floats), computed alike in every lane,
