@@ -10,7 +10,10 @@ accepted lengths and next tokens.
 
 Also reported (`tv_loss`): end-to-end TV loss forward + backward on T = 8192
 positions x 3 heads, V = 151936 (bf16 in, bf16 gradient out), as algorithmic GB/s
-against the 8 TB/s HBM peak.
+against the 8 TB/s HBM peak; (`long_tail`) verify on 512 x 4 positions at V = 2^18
+with Zipf-like logits; (`entropy_sweep`) verify on the 15 temperature x noise cells
+(128 sequences each), with each cell's acceptance rate, mean accepted length and
+mean target entropy.
 
 `roofline` uses per-launch HIP events recorded on the stream the kernels run on;
 `cpu_baseline` times the float64 oracle on a bounded sample of the same workload.
@@ -167,6 +170,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-tv", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the long-tail and entropy-sweep verify lines")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="after the bench, copy BYTES of device memory three times with torch (a plain copy "
                          "kernel of known size, to calibrate HBM byte counters)")
@@ -249,6 +253,56 @@ def main():
         }
         log(f"tv loss: fwd {fm:.3f} ms ({fwd_bytes / fm / 1e6:.0f} GB/s), bwd {bm:.3f} ms "
             f"({bwd_bytes / bm / 1e6:.0f} GB/s), total {gbs:.0f} GB/s")
+
+    if not args.no_extra:
+        # the long-tail workload (Zipf-like logits, V = 2^18, gamma = 4) and the 15
+        # cells of the entropy sweep, each timed like the rollout workload
+        lw = synthetic.VERIFY_WORKLOADS["long_tail"]
+        lsteps = max(5, args.steps // 10)
+        log(f"verify: long-tail workload B={lw['B']} gamma={lw['G']} V={lw['V']} bf16, {lsteps} steps")
+        lwall, lkms, plans = time_verify(mtp, torch, lw, lsteps, 2, 1)
+        del plans
+        torch.cuda.empty_cache()
+        lmean = sum(lkms) / len(lkms)
+        _, lbytes = verify_bytes(lw["B"], lw["G"], lw["V"], 2)
+        lpos = lw["B"] * lw["G"]
+        result["long_tail"] = {
+            "workload": "long-tail verify: 512 sequences x gamma=4 (+1 bonus row), V=262144, bf16, Zipf-like "
+                        "logits -1.1 ln(rank) + N(0,0.5^2), draft = target + N(0,0.4^2)",
+            "value": lpos / (lmean * 1e-3), "unit": "draft positions/s", "kernel_us_mean": lmean * 1e3,
+            "roofline": {"bound": "hbm", "achieved": lbytes / (lmean * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": lbytes / (lmean * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "bytes_per_launch": lbytes},
+        }
+        log(f"verify long tail: {lpos / lmean / 1e3:.3f} M positions/s, {lmean * 1e3:.1f} us per call, "
+            f"{lbytes / lmean / 1e6:.0f} GB/s")
+        cells = []
+        for it in range(len(synthetic.SWEEP_TAUS)):
+            for isg in range(len(synthetic.SWEEP_SIGMAS)):
+                cw = synthetic.sweep_cell(it, isg)
+                cwall_, ckms, plans = time_verify(mtp, torch, cw, max(5, args.steps // 10), 2, 3)
+                out = plans[0].run(seed=cw["seed"], offset=0)
+                acc = out["accept"].float().mean().item()
+                mean_n = out["accepted_len"].float().mean().item()
+                ent = out["entropy"].float().mean().item()
+                del plans, out
+                cm = sum(ckms) / len(ckms)
+                cells.append({"tau": synthetic.SWEEP_TAUS[it], "sigma": synthetic.SWEEP_SIGMAS[isg],
+                              "us_per_call": cm * 1e3, "positions_per_s": cw["B"] * cw["G"] / (cm * 1e-3),
+                              "accept_rate": acc, "mean_accepted_len": mean_n, "mean_entropy": ent})
+        torch.cuda.empty_cache()
+        _, cbytes = verify_bytes(128, 3, 151936, 2)
+        cmean = sum(c["us_per_call"] for c in cells) / len(cells)
+        result["entropy_sweep"] = {
+            "workload": "entropy sweep: 15 cells tau x sigma, 128 sequences x gamma=3 (+1 bonus row), V=151936, "
+                        "bf16, target N(0,1)/tau, draft = target + N(0,sigma^2), 3 input sets per cell",
+            "value": 128 * 3 / (cmean * 1e-6), "unit": "draft positions/s", "kernel_us_mean": cmean,
+            "roofline": {"bound": "hbm", "achieved": cbytes / (cmean * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": cbytes / (cmean * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                         "bytes_per_launch": cbytes},
+            "cells": cells,
+        }
+        log(f"verify entropy sweep: {cmean:.1f} us per call on average over 15 cells")
 
     if not args.no_cpu_baseline:
         n, cwall = cpu_baseline(torch, w, args.cpu_seconds)
