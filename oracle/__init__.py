@@ -24,7 +24,8 @@ Rejection Sampling" (Bebop; arXiv 2606.12370), cited by page and section:
 Modules
   philox   Philox4x32-10 counter-based generator (Salmon et al., SC'11).
   bf16     exact bfloat16 <-> float64 conversion (round to nearest even).
-  mtp      verification, overlap / TV / entropy, residual sampling, the
+  mtp      verification (rejection sampling and target-only), overlap / TV /
+           entropy, residual sampling, the
            end-to-end TV loss, its gradient.
 
 Parity status: every function is pinned by a ``-m "not gpu"`` test against a

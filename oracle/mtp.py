@@ -219,6 +219,125 @@ def verify(target, draft, tokens, seed, offset, tie_band=1e-6, cdf_tie_band=1e-6
     return out
 
 
+def greedy_draft_token(draft_logits):
+    """yhat = argmax_y q(y): the draft token chosen greedily (paperlayer Sec. 2
+    "Preliminaries", acceptance methods; App. D.2 "Target-Only Sampling").  q is a
+    softmax of the draft logits, so this is the argmax of the logits.  READING:
+    among equal maxima the smallest index."""
+    return int(np.argmax(np.asarray(draft_logits, dtype=np.float64)))
+
+
+def target_only_row_sample(p, yhat, u_prime, cdf_tie_band=1e-6):
+    """The token a rejected target-only row emits.
+
+    READING: the pages give target-only acceptance (probability p(yhat)) but not the
+    token emitted on a rejection.  Target-only sampling is rejection sampling whose
+    draft distribution is the point mass at yhat: the acceptance probability
+    min(1, p(yhat)/1) is the pages' p(yhat), and the residual max(0, p - delta_yhat)
+    is p with yhat removed, which keeps the emitted token's law exactly p.  If that
+    residual has no mass (p(yhat) = 1) the row samples from p (flagged, as in
+    row_sample).  t = u' * sum r; the token is inverse_cdf(r, t).
+    Returns (token, residual_was_empty, near_tie).
+    """
+    r = np.array(p, dtype=np.float64)
+    r[yhat] = 0.0
+    mass = float(np.sum(r))
+    near_empty = mass < cdf_tie_band
+    empty = not mass > 0
+    if empty:
+        r = np.asarray(p, dtype=np.float64)
+    total = float(np.cumsum(r)[-1])
+    t = u_prime * total
+    tok, lo, hi = inverse_cdf(r, t)
+    band = cdf_tie_band * total
+    return tok, empty, near_empty or (abs(t - lo) <= band) or (abs(t - hi) <= band)
+
+
+def verify_target_only(target, draft, seed, offset, tie_band=1e-6, cdf_tie_band=1e-6):
+    """Target-only verification of gamma draft positions per sequence, with the
+    rejection-sampling statistics and the RS/TO diagnostic.
+
+    target: float64 [B, gamma+1, V]; draft: float64 [B, gamma, V]; no draft tokens:
+    each draft position proposes its greedy token.
+
+    Steps (paperlayer Sec. 2 "Preliminaries", acceptance methods; Sec. 7
+    "Discussion", robustness of acceptance methods; App. D.2 "Target-Only
+    Sampling"):
+      1. p_k = softmax(target_k), q_k = softmax(draft_k); H(p_k) for every row.
+      2. yhat_k = greedy_draft_token(draft_k).
+      3. accept_k = u_k < p_k(yhat_k).  READING: strict '<' as for rejection
+         sampling, with the same position-addressed uniforms.
+      4. n_b = number of leading accepts; next_token_b = row_token[b, n_b].
+      5. Row sample: target_only_row_sample(p_k, yhat_k, u'_k) for k < gamma;
+         p_gamma for the bonus row.
+      6. alpha_k = sum min(p_k, q_k) and TV_k = d_TV(p_k, q_k) as for rejection
+         sampling; rs_better_k = TV_k < 1 - p_k(yhat_k), the boundary below which
+         rejection sampling accepts more often than target-only sampling
+         (1 - TV_k > p_k(yhat_k)).
+    Near-ties as in verify; rs_tie marks |TV_k - (1 - p_k(yhat_k))| <= tie_band.
+    """
+    target = np.asarray(target, dtype=np.float64)
+    draft = np.asarray(draft, dtype=np.float64)
+    B, G1, V = target.shape
+    G = G1 - 1
+    assert draft.shape == (B, G, V)
+
+    pos = np.arange(B * G1, dtype=np.uint64).reshape(B, G1)
+    u, up = verify_uniforms(seed, offset, pos)
+
+    out = dict(
+        accept=np.zeros((B, G), np.uint8), accepted_len=np.zeros(B, np.int32),
+        next_token=np.full(B, -1, np.int32), row_token=np.full((B, G1), -1, np.int32),
+        draft_token=np.full((B, G), -1, np.int32), p_yhat=np.full((B, G), np.nan),
+        rs_better=np.zeros((B, G), np.uint8), rs_tie=np.zeros((B, G), bool),
+        overlap=np.full((B, G), np.nan), tv=np.full((B, G), np.nan),
+        entropy=np.full((B, G1), np.nan), row_status=np.zeros((B, G1), np.int32),
+        u=u, u_prime=up,
+        accept_tie=np.zeros((B, G), bool), token_tie=np.zeros((B, G1), bool),
+    )
+    for b in range(B):
+        for k in range(G1):
+            logp, _ = log_softmax(target[b, k])
+            if logp is None:
+                out["row_status"][b, k] |= BAD_TARGET
+            else:
+                out["entropy"][b, k] = entropy(logp)
+            if k == G:                                   # bonus row: r = p
+                if logp is not None:
+                    tok, _, tie = row_sample(np.exp(logp), None, up[b, k], cdf_tie_band)
+                    out["row_token"][b, k] = tok
+                    out["token_tie"][b, k] = tie
+                continue
+            logq, _ = log_softmax(draft[b, k])
+            if logq is None:
+                out["row_status"][b, k] |= BAD_DRAFT
+            if logp is None or logq is None:
+                continue
+            p, q = np.exp(logp), np.exp(logq)
+            yhat = greedy_draft_token(draft[b, k])
+            py = float(p[yhat])
+            out["draft_token"][b, k] = yhat
+            out["p_yhat"][b, k] = py
+            out["accept"][b, k] = 1 if u[b, k] < py else 0
+            out["accept_tie"][b, k] = abs(u[b, k] - py) <= tie_band
+            out["overlap"][b, k] = overlap(p, q)
+            tv = tv_distance(p, q)
+            out["tv"][b, k] = tv
+            out["rs_better"][b, k] = 1 if tv < 1.0 - py else 0
+            out["rs_tie"][b, k] = abs(tv - (1.0 - py)) <= tie_band
+            tok, empty, tie = target_only_row_sample(p, yhat, up[b, k], cdf_tie_band)
+            if empty:
+                out["row_status"][b, k] |= RESIDUAL_EMPTY
+            out["row_token"][b, k] = tok
+            out["token_tie"][b, k] = tie
+        n = 0
+        while n < G and out["accept"][b, n] == 1:
+            n += 1
+        out["accepted_len"][b] = n
+        out["next_token"][b] = out["row_token"][b, n]
+    return out
+
+
 def _head_targets(target, G):
     """Target rows per (position, head): a [T, V] target is shared by all heads."""
     target = np.asarray(target, dtype=np.float64)
