@@ -106,6 +106,40 @@ mtp_status mtp_verify(const void* target, int64_t target_row_stride,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Target-only verification with the rejection-sampling / target-only diagnostic
+ * (paperlayer Sec. 2 "Preliminaries", acceptance methods; Sec. 7 "Discussion",
+ * robustness of acceptance methods; App. D.2 "Target-Only Sampling").
+ *
+ * Each draft position proposes its greedy token instead of a sampled one:
+ *   draft_token[b, k] = yhat = argmax_v q_v   (the smallest index among equal maxima)
+ *   accept[b, k]      = u < p(yhat)
+ *   p_yhat[b, k]      = p(yhat)
+ *   rs_better[b, k]   = tv[b, k] < 1 - p(yhat): rejection sampling (acceptance
+ *                       1 - TV) would accept more often than target-only sampling
+ *   row_token[b, k]   = inverse-CDF sample of r = p with r_yhat = 0 (the residual of
+ *                       the point-mass draft at yhat, so the emitted token's law is
+ *                       p); if that has no mass (p(yhat) = 1), a sample of p with
+ *                       MTP_ROW_RESIDUAL_EMPTY set; the bonus row samples p
+ * and overlap, tv, entropy, accepted_len, next_token, row_status, u, u' exactly as
+ * for mtp_verify.  Arguments as for mtp_verify without draft_tokens; draft_token
+ * (device int32 [batch, gamma]) is a required output, p_yhat (float) and
+ * rs_better (uint8) [batch, gamma] are optional.  Bad rows give draft_token -1, NaN
+ * p_yhat, rs_better 0 and a rejection.  The workspace size differs from mtp_verify's.
+ */
+mtp_status mtp_verify_target_only_workspace_size(int32_t batch, int32_t gamma, int32_t vocab, mtp_dtype dtype,
+                                                 size_t* bytes);
+
+mtp_status mtp_verify_target_only(const void* target, int64_t target_row_stride,
+                                  const void* draft, int64_t draft_row_stride, mtp_dtype dtype,
+                                  int32_t batch, int32_t gamma, int32_t vocab,
+                                  uint64_t seed, uint64_t offset,
+                                  uint8_t* accept, int32_t* accepted_len, int32_t* next_token,
+                                  int32_t* draft_token, float* p_yhat, uint8_t* rs_better,
+                                  int32_t* row_token, float* overlap, float* tv, float* entropy,
+                                  int32_t* row_status,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* End-to-end TV loss, forward (paperlayer Sec. 4 "End-to-end TV loss", App. F;
  * rainbus "Method steps").  For position t and head k (1-based in the formula):
  *   alpha_{t,k} = clamp(sum_v min(p_v, q_v), 0, 1)

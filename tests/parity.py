@@ -77,6 +77,34 @@ def compare_verify(out, ref, dtype, rows=None):
     return int(acc_tie.sum()), int(tok_tie.sum())
 
 
+def oracle_target_only(target, draft, seed, offset):
+    return omtp.verify_target_only(to_f64(target), to_f64(draft), seed, offset)
+
+
+# The RS/TO flag compares a float32 TV with 1 - p(yhat); rows whose float64 values
+# lie within this band of the boundary may flip.
+RS_FLAG_BAND = 1e-4
+
+
+def compare_target_only(out, ref, dtype, rows=None):
+    """compare_verify's checks for a target-only call, plus the greedy tokens (exact:
+    both sides compare the same input values), p(yhat) within the statistic
+    tolerance and the RS/TO flags away from the boundary.  Returns tie counts."""
+    ties = compare_verify(out, ref, dtype, rows)
+
+    def g(name):
+        v = out[name].cpu().numpy()
+        return v if rows is None else v[rows]
+
+    np.testing.assert_array_equal(g("draft_token"), ref["draft_token"])
+    ok = stat_close(g("p_yhat"), ref["p_yhat"], dtype)
+    assert ok.all(), f"p_yhat: {g('p_yhat')[~ok][:5]} vs {ref['p_yhat'][~ok][:5]}"
+    near = np.abs(ref["tv"] - (1.0 - ref["p_yhat"])) <= RS_FLAG_BAND
+    bad = (g("rs_better") != ref["rs_better"]) & ~near
+    assert not bad.any(), f"rs_better mismatch at {np.argwhere(bad)[:10]}"
+    return ties
+
+
 def bf16_ulp_distance(a_bits, b_bits):
     """|a - b| in units of bfloat16 spacing (ordered-integer distance)."""
     def ordered(x):

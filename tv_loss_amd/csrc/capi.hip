@@ -56,7 +56,7 @@ mtp_status check_row_base(const void* p, int64_t stride_elems, mtp_dtype dt, con
 // ---- per-device limits --------------------------------------------------------
 struct DeviceInfo {
   int cus = 0;
-  std::map<int, int> occ;   // dtype -> verify main workgroups per CU
+  std::map<int, int> occ;   // (dtype, target-only) -> verify main workgroups per CU
 };
 std::mutex g_dev_mu;
 std::map<int, DeviceInfo> g_dev;
@@ -64,7 +64,7 @@ std::map<int, DeviceInfo> g_dev;
 // Workgroups of the verify main kernel the current device holds at once: all of a
 // launch's workgroups must be resident together (a super-group waits on its
 // members' records).
-mtp_status verify_capacity(int dt, int64_t* per_gpu) {
+mtp_status verify_capacity(int dt, bool target_only, int64_t* per_gpu) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(MTP_ERR_DEVICE, "hipGetDevice failed");
   std::lock_guard<std::mutex> lk(g_dev_mu);
@@ -73,12 +73,13 @@ mtp_status verify_capacity(int dt, int64_t* per_gpu) {
     if (hipDeviceGetAttribute(&info.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return fail(MTP_ERR_DEVICE, "cannot query the compute-unit count");
   }
-  auto it = info.occ.find(dt);
+  const int key = dt * 2 + (target_only ? 1 : 0);
+  auto it = info.occ.find(key);
   if (it == info.occ.end()) {
     int n = 0;
-    hipError_t e = mtp::verify_occupancy(dt, &n);
+    hipError_t e = mtp::verify_occupancy(dt, target_only, &n);
     if (e != hipSuccess || n < 1) return fail(MTP_ERR_DEVICE, "occupancy query failed");
-    it = info.occ.emplace(dt, n).first;
+    it = info.occ.emplace(key, n).first;
   }
   *per_gpu = (int64_t)it->second * info.cus;
   return MTP_OK;
@@ -86,20 +87,22 @@ mtp_status verify_capacity(int dt, int64_t* per_gpu) {
 
 // ---- workspace layouts --------------------------------------------------------
 struct VerifyLayout {
-  size_t err, part1, part2, total;
+  size_t err, part1, part2, part3, total;
   mtp::RowSplit sp;
   int64_t ngroups;
 };
 
-VerifyLayout verify_layout(int32_t B, int32_t G, int32_t V, mtp_dtype dt) {
+VerifyLayout verify_layout(int32_t B, int32_t G, int32_t V, mtp_dtype dt, bool target_only) {
   VerifyLayout L{};
   L.sp = mtp::make_split(V, per_vec(dt), mtp::verify_vec_per_thread(dt), false);
   L.ngroups = (int64_t)B * (G + 1);
   const int64_t C = L.sp.nchunks;
   size_t off = 0;
   L.err = off; off = align256(off + 4);
-  L.part1 = off; off = align256(off + (size_t)L.ngroups * C * 3 * 8);
+  L.part1 = off; off = align256(off + (size_t)L.ngroups * C * mtp::verify_record_words(target_only) * 8);
   L.part2 = off; off = align256(off + (size_t)L.ngroups * C * mtp::kWaves * 8);
+  L.part3 = off;
+  if (target_only) off = align256(off + (size_t)L.ngroups * C * mtp::kWaves * 4);
   L.total = off;
   return L;
 }
@@ -175,35 +178,52 @@ mtp_status mtp_verify_workspace_size(int32_t batch, int32_t gamma, int32_t vocab
   mtp_status s = check_common(dtype, gamma, vocab);
   if (s) return s;
   if (batch < 0) return fail(MTP_ERR_SHAPE, "batch = %d is negative", batch);
-  *bytes = batch == 0 ? 0 : verify_layout(batch, gamma, vocab, dtype).total;
+  *bytes = batch == 0 ? 0 : verify_layout(batch, gamma, vocab, dtype, false).total;
   return ok();
 }
 
-mtp_status mtp_verify(const void* target, int64_t target_row_stride, const void* draft,
-                      int64_t draft_row_stride, mtp_dtype dtype, int32_t batch, int32_t gamma,
-                      int32_t vocab, const int32_t* draft_tokens, uint64_t seed, uint64_t offset,
-                      uint8_t* accept, int32_t* accepted_len, int32_t* next_token, int32_t* row_token,
-                      float* overlap, float* tv, float* entropy, int32_t* row_status, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+mtp_status mtp_verify_target_only_workspace_size(int32_t batch, int32_t gamma, int32_t vocab, mtp_dtype dtype,
+                                                 size_t* bytes) {
+  if (!bytes) return fail(MTP_ERR_NULL, "bytes is NULL");
+  mtp_status s = check_common(dtype, gamma, vocab);
+  if (s) return s;
+  if (batch < 0) return fail(MTP_ERR_SHAPE, "batch = %d is negative", batch);
+  *bytes = batch == 0 ? 0 : verify_layout(batch, gamma, vocab, dtype, true).total;
+  return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+// Both verify entry points: rejection sampling (draft_tokens given) or target-only
+// (draft_token out).  Argument errors return before any HIP call.
+mtp_status verify_impl(bool target_only, const void* target, int64_t target_row_stride, const void* draft,
+                       int64_t draft_row_stride, mtp_dtype dtype, int32_t batch, int32_t gamma, int32_t vocab,
+                       const int32_t* draft_tokens, uint64_t seed, uint64_t offset, uint8_t* accept,
+                       int32_t* accepted_len, int32_t* next_token, int32_t* draft_token, float* p_yhat,
+                       uint8_t* rs_better, int32_t* row_token, float* overlap, float* tv, float* entropy,
+                       int32_t* row_status, void* workspace, size_t workspace_bytes, void* stream) {
   mtp_status s = check_common(dtype, gamma, vocab);
   if (s) return s;
   if (batch < 0) return fail(MTP_ERR_SHAPE, "batch = %d is negative", batch);
   if (batch == 0) return ok();
-  if (!target || !draft || !draft_tokens || !accept || !accepted_len || !next_token)
-    return fail(MTP_ERR_NULL, "a required pointer (target, draft, draft_tokens, accept, accepted_len, "
-                              "next_token) is NULL");
+  if (!target || !draft || !accept || !accepted_len || !next_token)
+    return fail(MTP_ERR_NULL, "a required pointer (target, draft, accept, accepted_len, next_token) is NULL");
+  if (!target_only && !draft_tokens) return fail(MTP_ERR_NULL, "draft_tokens is NULL");
+  if (target_only && !draft_token) return fail(MTP_ERR_NULL, "draft_token is NULL");
   if (target_row_stride < vocab || draft_row_stride < vocab)
     return fail(MTP_ERR_SHAPE, "row strides (%lld, %lld) must be >= vocab (%d)", (long long)target_row_stride,
                 (long long)draft_row_stride, vocab);
   if ((s = check_row_base(target, target_row_stride, dtype, "target"))) return s;
   if ((s = check_row_base(draft, draft_row_stride, dtype, "draft"))) return s;
-  const VerifyLayout L = verify_layout(batch, gamma, vocab, dtype);
+  const VerifyLayout L = verify_layout(batch, gamma, vocab, dtype, target_only);
   if ((s = check_workspace(workspace, workspace_bytes, L.total))) return s;
   if (L.ngroups > 0x7fffffffLL / 8) return fail(MTP_ERR_SHAPE, "batch * (gamma + 1) is too large");
 
   // ---- device-dependent checks ---------------------------------------------
   int64_t per_gpu = 0;
-  if ((s = verify_capacity(dtype, &per_gpu))) return s;
+  if ((s = verify_capacity(dtype, target_only, &per_gpu))) return s;
   if ((int64_t)L.sp.nchunks > per_gpu)
     return fail(MTP_ERR_SHAPE, "vocab %d needs %d co-resident workgroups per row; the GPU holds %lld", vocab,
                 L.sp.nchunks, (long long)per_gpu);
@@ -213,21 +233,50 @@ mtp_status mtp_verify(const void* target, int64_t target_row_stride, const void*
   mtp::VerifyArgs a{};
   a.target = target; a.t_stride = target_row_stride;
   a.draft = draft; a.d_stride = draft_row_stride;
-  a.tokens = draft_tokens;
+  a.tokens = target_only ? nullptr : draft_tokens;
   a.B = batch; a.G = gamma; a.V = vocab;
   a.seed = seed; a.offset = offset;
   a.accept = accept; a.accepted_len = accepted_len; a.next_token = next_token;
   a.row_token = row_token; a.overlap = overlap; a.tv = tv; a.entropy = entropy; a.row_status = row_status;
+  a.draft_token = draft_token; a.p_yhat = p_yhat; a.rs_better = rs_better;
   a.err = at<uint32_t>(workspace, L.err);
   a.part1 = at<uint64_t>(workspace, L.part1);
   a.part2 = at<uint64_t>(workspace, L.part2);
+  a.part3 = target_only ? at<float>(workspace, L.part3) : nullptr;
   a.sp = L.sp;
   a.ngroups = (int)L.ngroups;
   a.sgroups = sgroups;
   a.layers = layers;
-  hipError_t e = mtp::launch_verify(a, dtype, (hipStream_t)stream);
+  hipError_t e = mtp::launch_verify(a, dtype, target_only, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MTP_ERR_LAUNCH, "verify launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+mtp_status mtp_verify(const void* target, int64_t target_row_stride, const void* draft,
+                      int64_t draft_row_stride, mtp_dtype dtype, int32_t batch, int32_t gamma,
+                      int32_t vocab, const int32_t* draft_tokens, uint64_t seed, uint64_t offset,
+                      uint8_t* accept, int32_t* accepted_len, int32_t* next_token, int32_t* row_token,
+                      float* overlap, float* tv, float* entropy, int32_t* row_status, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return verify_impl(false, target, target_row_stride, draft, draft_row_stride, dtype, batch, gamma, vocab,
+                     draft_tokens, seed, offset, accept, accepted_len, next_token, nullptr, nullptr, nullptr,
+                     row_token, overlap, tv, entropy, row_status, workspace, workspace_bytes, stream);
+}
+
+mtp_status mtp_verify_target_only(const void* target, int64_t target_row_stride, const void* draft,
+                                  int64_t draft_row_stride, mtp_dtype dtype, int32_t batch, int32_t gamma,
+                                  int32_t vocab, uint64_t seed, uint64_t offset, uint8_t* accept,
+                                  int32_t* accepted_len, int32_t* next_token, int32_t* draft_token, float* p_yhat,
+                                  uint8_t* rs_better, int32_t* row_token, float* overlap, float* tv,
+                                  float* entropy, int32_t* row_status, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  return verify_impl(true, target, target_row_stride, draft, draft_row_stride, dtype, batch, gamma, vocab,
+                     nullptr, seed, offset, accept, accepted_len, next_token, draft_token, p_yhat, rs_better,
+                     row_token, overlap, tv, entropy, row_status, workspace, workspace_bytes, stream);
 }
 
 mtp_status mtp_tv_loss_workspace_size(int32_t T, int32_t gamma, int32_t vocab, mtp_dtype dtype,

@@ -446,6 +446,20 @@ __device__ __forceinline__ float wave_maximum(float v) {
   return a[0];
 }
 
+// Wave minimum of unsigned integers with the same chain (v_min_u32), every lane.
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  asm volatile(
+      "s_nop 4\n\t"
+      "v_min_u32_dpp %0, %0, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\ts_nop 1\n\t"
+      "v_min_u32_dpp %0, %0, %0 row_shr:2 row_mask:0xf bank_mask:0xf\n\ts_nop 1\n\t"
+      "v_min_u32_dpp %0, %0, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\ts_nop 1\n\t"
+      "v_min_u32_dpp %0, %0, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\ts_nop 1\n\t"
+      "v_min_u32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\ts_nop 1\n\t"
+      "v_min_u32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf\n\ts_nop 1"
+      : "+v"(v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 __device__ __forceinline__ Lse lse_nan() {
   const float nan = __builtin_nanf("");
   return Lse{nan, nan, nan};

@@ -31,23 +31,28 @@ constexpr int kRowResidualEmpty = 8;
 struct VerifyArgs {
   const void* target; int64_t t_stride;   // row (b, k) of [B, G+1, V] at (b*(G+1)+k)*t_stride
   const void* draft;  int64_t d_stride;   // row (b, k) of [B, G, V]   at (b*G+k)*d_stride
-  const int32_t* tokens;                  // [B, G]
+  const int32_t* tokens;                  // [B, G]; unused by target-only verify
   int B, G;
   int64_t V;
   uint64_t seed, offset;
   uint8_t* accept; int32_t* accepted_len; int32_t* next_token;
   int32_t* row_token; float* overlap; float* tv; float* entropy; int32_t* row_status;
-  // workspace sections: error word, pass-1 records [group][chunk][3], pass-2
-  // sums [group][chunk][wave] = (residual or p mass, overlap) as two floats
-  uint32_t* err; uint64_t* part1; uint64_t* part2;
+  // target-only verify: greedy draft tokens [B, G], p at them, RS/TO boundary flags
+  int32_t* draft_token; float* p_yhat; uint8_t* rs_better;
+  // workspace sections: error word, pass-1 records [group][chunk][3 or 4 words],
+  // pass-2 sums [group][chunk][wave] = (residual or p mass, overlap) as two floats,
+  // target-only: p mass without the greedy token [group][chunk][wave]
+  uint32_t* err; uint64_t* part1; uint64_t* part2; float* part3;
   RowSplit sp;
   int ngroups;
   int sgroups, layers;   // super-groups (all co-resident), groups per super-group
 };
 
 int verify_vec_per_thread(int dt);
-hipError_t launch_verify(const VerifyArgs& a, int dt, hipStream_t stream);
-hipError_t verify_occupancy(int dt, int* blocks_per_cu);
+// target_only selects target-only verification (greedy draft tokens, no tokens input)
+hipError_t launch_verify(const VerifyArgs& a, int dt, bool target_only, hipStream_t stream);
+hipError_t verify_occupancy(int dt, bool target_only, int* blocks_per_cu);
+int verify_record_words(bool target_only);
 
 // ---------------------------------------------------------------------------
 // End-to-end TV loss.  Head k of position t compares draft row

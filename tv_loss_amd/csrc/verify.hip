@@ -47,19 +47,24 @@
 
 namespace mtp {
 
-// Chunk record of pass 1 (three words): (ref_p, z_p), (ref_q, z_q), (y_p, 1); the
-// z's carry the sign bit as a marker so that no word of a published record is 0.
-constexpr int kRecWords = 3;
+// Chunk record of pass 1: (ref_p, z_p), (ref_q, z_q), (y_p, 1), and for target-only
+// verify a fourth word, the chunk's largest draft logit and its vocabulary index + 1.
+// The z's carry the sign bit as a marker (and the index is at least 1), so no word of
+// a published record is 0.  rec_bytes is the record stride.
+template <bool TO>
+constexpr int rec_bytes() { return TO ? 32 : 24; }
+constexpr int kArgmaxWord = 3;
 
 // Row statistics from the C records of a group.  Lane l holds the partial of
 // record l and merges records l + 64, l + 128, ... into it in that order; the wave
 // then merges the lanes.  Both kernels use these functions, so both derive the same
 // bits for a row.
-__device__ __forceinline__ Lse lane_records(Lse acc, __amdgpu_buffer_rsrc_t rs, int C, int word, bool with_y) {
+__device__ __forceinline__ Lse lane_records(Lse acc, __amdgpu_buffer_rsrc_t rs, int C, int st, int word,
+                                            bool with_y) {
   const int lane = threadIdx.x & 63;
   for (int c = lane + 64; c < C; c += 64) {
-    const uint64_t w = rec_load(rs, c * 24 + word * 8);
-    const float y = with_y ? unpack_lo(rec_load(rs, c * 24 + 16)) : 0.f;
+    const uint64_t w = rec_load(rs, c * st + word * 8);
+    const float y = with_y ? unpack_lo(rec_load(rs, c * st + 16)) : 0.f;
     acc = lse_merge(acc, Lse{unpack_lo(w), unmark(unpack_hi(w)), y});
   }
   return acc;
@@ -69,37 +74,39 @@ struct RowStats {
   Lse p, q;
 };
 
-__device__ __forceinline__ RowStats merge_records(__amdgpu_buffer_rsrc_t rs, int C, bool pair) {
+__device__ __forceinline__ RowStats merge_records(__amdgpu_buffer_rsrc_t rs, int C, int st, bool pair) {
   const int lane = threadIdx.x & 63;
   Lse a[2] = {lse_empty(), lse_empty()};
   if (lane < C) {
-    const uint64_t w0 = rec_load(rs, lane * 24), w1 = rec_load(rs, lane * 24 + 8), w2 = rec_load(rs, lane * 24 + 16);
+    const uint64_t w0 = rec_load(rs, lane * st), w1 = rec_load(rs, lane * st + 8), w2 = rec_load(rs, lane * st + 16);
     a[0] = Lse{unpack_lo(w0), unmark(unpack_hi(w0)), unpack_lo(w2)};
     if (pair) a[1] = Lse{unpack_lo(w1), unmark(unpack_hi(w1)), 0.f};
   }
-  a[0] = lane_records(a[0], rs, C, 0, true);
-  if (pair) a[1] = lane_records(a[1], rs, C, 1, false);
+  a[0] = lane_records(a[0], rs, C, st, 0, true);
+  if (pair) a[1] = lane_records(a[1], rs, C, st, 1, false);
   wave_merge<2, 1>(a);
   return RowStats{a[0], a[1]};
 }
 
-// Wait until word `word` of every record of the group is published (non-zero) and
-// return this row's merged log-sum-exp (no entropy moment).  `v` is this lane's
-// word of record `lane`, loaded earlier; lanes still seeing zero load again.
-// Bounded by the spin limit (a timeout sets the error word and carries on).
-__device__ __forceinline__ Lse poll_row(uint64_t v, __amdgpu_buffer_rsrc_t rs, int C, int word, uint32_t* err) {
+// Wait until word `word` of every record of the group is published (non-zero):
+// `v` is this lane's word of record `lane`, loaded earlier, and lanes still seeing
+// zero load again; records past the first 64 are loaded here.  `merge` folds each
+// lane's words in record order (first record, then l + 64, ...).  Bounded by the
+// spin limit (a timeout sets the error word and carries on).
+template <typename Fold>
+__device__ __forceinline__ void poll_words(uint64_t v, __amdgpu_buffer_rsrc_t rs, int C, int st, int word,
+                                           uint32_t* err, Fold fold) {
   const int lane = threadIdx.x & 63;
   uint64_t t0 = 0;
-  Lse acc = lse_empty();
   for (int c0 = 0; c0 < C; c0 += 64) {
     const int c = c0 + lane;
-    if (c0 > 0 && c < C) v = rec_load(rs, c * 24 + word * 8);
+    if (c0 > 0 && c < C) v = rec_load(rs, c * st + word * 8);
     bool ready = !(c < C) || v != 0ull;
     while (__ballot(!ready) != 0ull) {
       if (t0 == 0) t0 = __builtin_amdgcn_s_memrealtime();
       __builtin_amdgcn_s_sleep(1);
       if (!ready) {
-        v = rec_load(rs, c * 24 + word * 8);
+        v = rec_load(rs, c * st + word * 8);
         ready = v != 0ull;
       }
       if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimitTicks) {
@@ -107,18 +114,72 @@ __device__ __forceinline__ Lse poll_row(uint64_t v, __amdgpu_buffer_rsrc_t rs, i
         break;
       }
     }
-    if (c < C) {
-      const Lse r{unpack_lo(v), unmark(unpack_hi(v)), 0.f};
-      acc = c0 == 0 ? r : lse_merge(acc, r);
-    }
+    if (c < C) fold(c0 == 0, v);
   }
+}
+
+// The row's merged log-sum-exp (no entropy moment) from word `word` of the records.
+__device__ __forceinline__ Lse poll_row(uint64_t v, __amdgpu_buffer_rsrc_t rs, int C, int st, int word,
+                                        uint32_t* err) {
+  Lse acc = lse_empty();
+  poll_words(v, rs, C, st, word, err, [&](bool first, uint64_t w) {
+    const Lse r{unpack_lo(w), unmark(unpack_hi(w)), 0.f};
+    acc = first ? r : lse_merge(acc, r);
+  });
   Lse a[1] = {acc};
   wave_merge<1, 0>(a);
   return a[0];
 }
 
+// ---- argmax of the draft logits (target-only verify) --------------------------
+__device__ __forceinline__ uint64_t pack_argmax(float m, uint32_t idx) {
+  return pack2(m, __uint_as_float(min(idx, 0xfffffffeu) + 1u));
+}
+__device__ __forceinline__ uint32_t argmax_index(uint64_t w) { return __float_as_uint(unpack_hi(w)) - 1u; }
+
+// (m, idx) absorbs (m2, idx2) if m2 is larger, or equal with a smaller index; a NaN
+// m2 never wins.
+__device__ __forceinline__ void argmax_fold(float& m, uint32_t& idx, float m2, uint32_t idx2) {
+  const bool take = m2 > m || (m2 == m && idx2 < idx);
+  m = take ? m2 : m;
+  idx = take ? idx2 : idx;
+}
+
+// Wave argmax: the largest m over the lanes (NaN ignored), the smallest idx among
+// the lanes that hold it.  The same bits in every lane.
+__device__ __forceinline__ void wave_argmax(float& m, uint32_t& idx) {
+  const float M = wave_maximum(m);
+  const uint32_t cand = m == M ? idx : 0xffffffffu;
+  m = M;
+  idx = wave_min_u32(cand);
+}
+
+// The chunk argmax words of a group merged over its C records, in record order per
+// lane then over the wave: the vocabulary index of the largest draft logit.
+__device__ __forceinline__ uint32_t poll_argmax(uint64_t v, __amdgpu_buffer_rsrc_t rs, int C, int st,
+                                                uint32_t* err) {
+  float m = kNegInf;
+  uint32_t idx = 0xffffffffu;
+  poll_words(v, rs, C, st, kArgmaxWord, err,
+             [&](bool, uint64_t w) { argmax_fold(m, idx, unpack_lo(w), argmax_index(w)); });
+  wave_argmax(m, idx);
+  return idx;
+}
+
+__device__ __forceinline__ uint32_t merge_argmax(__amdgpu_buffer_rsrc_t rs, int C, int st) {
+  const int lane = threadIdx.x & 63;
+  float m = kNegInf;
+  uint32_t idx = 0xffffffffu;
+  for (int c = lane; c < C; c += 64) {
+    const uint64_t w = rec_load(rs, c * st + kArgmaxWord * 8);
+    argmax_fold(m, idx, unpack_lo(w), argmax_index(w));
+  }
+  wave_argmax(m, idx);
+  return idx;
+}
+
 // ---------------------------------------------------------------------------
-template <int DT, int NV>
+template <int DT, int NV, bool TO>
 __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(VerifyArgs a) {
   constexpr int PV = Elem<DT>::kPerVec;
   constexpr int NE = NV * PV;
@@ -156,7 +217,8 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
     return k < G ? reinterpret_cast<const char*>(a.draft) + (int64_t)(b * G + k) * a.d_stride * Elem<DT>::kBytes
                  : trow_of(g);
   };
-  auto rsrc_rec = [&](int g) { return rsrc_of(a.part1 + (int64_t)g * C * kRecWords); };
+  constexpr int kSt = rec_bytes<TO>();
+  auto rsrc_rec = [&](int g) { return rsrc_of(a.part1 + (int64_t)g * C * (kSt / 8)); };
 
   // vector indices fit in 32 bits (V <= 2^30)
   const int vpc = (int)a.sp.vec_per_chunk, nvec = (int)a.sp.nvec, nfull = (int)a.sp.nvec_full;
@@ -177,6 +239,10 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
   // double-buffered by layer parity: a wave may run one layer ahead of another
   __shared__ float part_sh[2][2][kWaves * 3];
   __shared__ float lse_sh[2][2];
+  // target-only: per-wave argmax of the draft logits (pass 1), the row's argmax (pass 2)
+  __shared__ float am_sh[2][kWaves];
+  __shared__ uint32_t ai_sh[2][kWaves];
+  __shared__ uint32_t yhat_sh[2];
 
   // the chunks of items i + 1 and i + 2 are in flight while item i is processed;
   // every prefetch issues the same number of loads (see issue_seg_fixed).  A
@@ -195,6 +261,7 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
   int g_m2 = 0, g_m1 = 0;          // groups of items i - 2 and i - 1
   bool pair_m2 = false, pair_m1 = false;
   uint64_t wpoll = 0ull;                     // this lane's polled record word
+  uint64_t wpoll_am = 0ull;                  // ... and its argmax word (target-only)
   float x[2][NE];                            // item i - 1's e values between layers
   float xref[2] = {0.f, 0.f};                // ... and this wave's references for them
   float href[2] = {0.f, 0.f};                // references of the item held in LDS
@@ -210,8 +277,12 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
       const bool pair2 = pair_m2;
       if (wave == rp || (wave == rq && pair2)) {
         const int row = wave == rp ? 0 : 1;
-        const Lse st = poll_row(wpoll, rsrc_rec(g_m2), C, row, a.err);
+        const Lse st = poll_row(wpoll, rsrc_rec(g_m2), C, kSt, row, a.err);
         if (lane == 0) lse_sh[i & 1][row] = lse_log2(st);
+        if (TO && row == 1) {
+          const uint32_t yh = poll_argmax(wpoll_am, rsrc_rec(g_m2), C, kSt, a.err);
+          if (lane == 0) yhat_sh[i & 1] = yh;
+        }
       }
       __syncthreads();
       // ---- pass 2 of item i - 2 ------------------------------------------------
@@ -262,6 +333,32 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
         }
       }
       if (lane == 0) a.part2[((int64_t)g_m2 * C + c) * kWaves + wave] = pack2(rm, om);
+      if constexpr (TO) {
+        if (pair2) {
+          // target-only: this wave's p mass without the greedy draft token (the
+          // residual a rejected row samples), re-summed only by the wave holding it
+          const uint32_t yh = yhat_sh[i & 1];
+          const uint32_t ylo = (uint32_t)s0 * PV;
+          float pex = sa * hz;
+          if (la != kNegInf && yh >= ylo && yh - ylo < (uint32_t)(kSegVec * PV)) {
+            float m0 = 0.f, m1 = 0.f;
+#pragma unroll
+            for (int qi = 0; qi < NQ; ++qi) {
+              const float4 ea = held[0][qi][t];
+              const float va[4] = {ea.x, ea.y, ea.z, ea.w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int ii = 4 * qi + e;
+                const uint32_t gi = (uint32_t)(v0 + (ii / PV) * 64) * PV + ii % PV;
+                const float v = gi == yh ? 0.f : va[e];
+                if (e & 1) m1 += v; else m0 += v;
+              }
+            }
+            pex = sa * wave_total(m0 + m1);
+          }
+          if (lane == 0) a.part3[((int64_t)g_m2 * C + c) * kWaves + wave] = pex;
+        }
+      }
     }
     // ---- item i - 1 moves to LDS (own slots only) ------------------------------
     if (i >= 1 && i - 1 < nl) {
@@ -289,8 +386,11 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
     }
     // the poll goes out before the prefetch, so that waiting for it (a layer
     // later) does not wait for the prefetch
-    if (i >= 1 && i <= nl && (wave == rp || wave == rq) && lane < C)
-      wpoll = rec_load(rsrc_rec(g_m1), lane * 24 + (wave == rp ? 0 : 8));
+    if (i >= 1 && i <= nl && (wave == rp || wave == rq) && lane < C) {
+      const __amdgpu_buffer_rsrc_t rs = rsrc_rec(g_m1);
+      wpoll = rec_load(rs, lane * kSt + (wave == rp ? 0 : 8));
+      if (TO && wave == rq) wpoll_am = rec_load(rs, lane * kSt + kArgmaxWord * 8);
+    }
     __builtin_amdgcn_sched_barrier(0);
     const int g_p2 = i + 2 < nl ? group_of(i + 2) : g_0;
     prefetch(rb, g_p2, i + 2 < nl);
@@ -299,6 +399,21 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
     if (i < nl) {
       // ---- pass 1 of item i: wave partials, combined and published --------------
       Lse pt[2];
+      float am = 0.f;   // target-only: this wave's largest draft logit and its index
+      uint32_t ai = 0;
+      if (TO && pair) {
+        float bm = x[1][NE - 1];
+        int bi = NE - 1;
+#pragma unroll
+        for (int ii = NE - 2; ii >= 0; --ii) {   // downwards with >=: the smallest index wins ties
+          const bool tk = x[1][ii] >= bm;
+          bm = tk ? x[1][ii] : bm;
+          bi = tk ? ii : bi;
+        }
+        am = bm;
+        ai = (uint32_t)(v0 + (bi / PV) * 64) * PV + bi % PV;
+        wave_argmax(am, ai);
+      }
       if (pair) {
         wave_pass1<NE, 2, 1>(x, pt);
       } else {
@@ -313,18 +428,32 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
         ps[wave * 3 + 0] = pt[0].ref; ps[wave * 3 + 1] = pt[0].z; ps[wave * 3 + 2] = pt[0].y;
         ps = part_sh[i & 1][1];
         ps[wave * 3 + 0] = pt[1].ref; ps[wave * 3 + 1] = pt[1].z; ps[wave * 3 + 2] = 0.f;
+        if (TO) {
+          am_sh[i & 1][wave] = am;
+          ai_sh[i & 1][wave] = ai;
+        }
       }
       __syncthreads();
       if (wave == wp) {
         const Lse p = merge_lds<kWaves, true>(part_sh[i & 1][0]);
         if (lane == 0) {
           const __amdgpu_buffer_rsrc_t rs = rsrc_rec(g_0);
-          rec_store(rs, c * 24, pack2(p.ref, mark(p.z)));
-          rec_store(rs, c * 24 + 16, pack2(p.y, 1.f));
+          rec_store(rs, c * kSt, pack2(p.ref, mark(p.z)));
+          rec_store(rs, c * kSt + 16, pack2(p.y, 1.f));
         }
       } else if (wave == wq) {
         const Lse q = merge_lds<kWaves, false>(part_sh[i & 1][1]);
-        if (lane == 0) rec_store(rsrc_rec(g_0), c * 24 + 8, pack2(q.ref, mark(q.z)));
+        if (lane == 0) {
+          const __amdgpu_buffer_rsrc_t rs = rsrc_rec(g_0);
+          rec_store(rs, c * kSt + 8, pack2(q.ref, mark(q.z)));
+          if (TO && pair) {   // the chunk's argmax over the four waves
+            float m = am_sh[i & 1][0];
+            uint32_t idx = ai_sh[i & 1][0];
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w) argmax_fold(m, idx, am_sh[i & 1][w], ai_sh[i & 1][w]);
+            rec_store(rs, c * kSt + kArgmaxWord * 8, pack_argmax(m, idx));
+          }
+        }
       }
     }
     // ---- shift the item window -------------------------------------------------
@@ -443,7 +572,7 @@ __device__ __forceinline__ Scan wave_scan_owner(int n, float u_prime, MassFn mas
   return r;
 }
 
-template <int DT, int NV>
+template <int DT, int NV, bool TO>
 __global__ void verify_finish(VerifyArgs a) {
   constexpr int PV = Elem<DT>::kPerVec;
   constexpr int kSegVec = NV * 64;
@@ -458,14 +587,18 @@ __global__ void verify_finish(VerifyArgs a) {
 
   const char* trow = reinterpret_cast<const char*>(a.target) + (int64_t)g * a.t_stride * Elem<DT>::kBytes;
   const char* drow = reinterpret_cast<const char*>(a.draft) + (int64_t)(b * G + (pair ? k : 0)) * a.d_stride * Elem<DT>::kBytes;
-  const __amdgpu_buffer_rsrc_t rs = rsrc_of(a.part1 + (int64_t)g * C * kRecWords);
+  constexpr int kSt = rec_bytes<TO>();
+  const __amdgpu_buffer_rsrc_t rs = rsrc_of(a.part1 + (int64_t)g * C * (kSt / 8));
   uint64_t* p2 = a.part2 + (int64_t)g * C * kWaves;
+  // target-only pair rows sample p without the greedy token: its per-wave masses
+  float* p3 = TO ? a.part3 + (int64_t)g * C * kWaves : nullptr;
+  const bool to_pair = TO && pair;
 
   // ---- everything that does not depend on the row statistics goes out first ----
   // lane l owns chunks [l K, l K + K); the pass-2 words of its first KC are kept
   const int K = (C + 63) / 64;
   const int c0 = lane * K, c1 = min(C, c0 + K);
-  float seg[KC][kWaves], om_sum = 0.f;
+  float seg[KC][kWaves], om_sum = 0.f, tv_sum = 0.f;
 #pragma unroll
   for (int i = 0; i < KC; ++i)
 #pragma unroll
@@ -476,21 +609,27 @@ __global__ void verify_finish(VerifyArgs a) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
         const uint64_t v = p2[(int64_t)(c0 + i) * kWaves + w];
-        seg[i][w] = unpack_lo(v);
+        seg[i][w] = to_pair ? p3[(int64_t)(c0 + i) * kWaves + w] : unpack_lo(v);
         om_sum += unpack_hi(v);
+        tv_sum += unpack_lo(v);
       }
     }
   }
   for (int cc = c0 + KC; cc < c1; ++cc)
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) om_sum += unpack_hi(p2[(int64_t)cc * kWaves + w]);
-  const int y = pair ? a.tokens[b * G + k] : 0;
+    for (int w = 0; w < kWaves; ++w) {
+      const uint64_t v = p2[(int64_t)cc * kWaves + w];
+      om_sum += unpack_hi(v);
+      tv_sum += unpack_lo(v);
+    }
+  // the draft token: given (rejection sampling) or the greedy one (target-only)
+  const int y = !pair ? 0 : TO ? (int)merge_argmax(rs, C, kSt) : a.tokens[b * G + k];
   const bool y_ok = pair && y >= 0 && y < a.V;
   const float ay = y_ok ? load_one<DT>(trow, y) : 0.f;
-  const float by = y_ok ? load_one<DT>(drow, y) : 0.f;
+  const float by = y_ok && !TO ? load_one<DT>(drow, y) : 0.f;
 
   // ---- row statistics from the pass-1 records ---------------------------------
-  const RowStats st = merge_records(rs, C, pair);
+  const RowStats st = merge_records(rs, C, kSt, pair);
   const float lse2_p = lse_log2(st.p);
   const float lse2_q = pair ? lse_log2(st.q) : 0.f;
   const bool bad_p = !(__builtin_isfinite(lse2_p));
@@ -501,7 +640,7 @@ __global__ void verify_finish(VerifyArgs a) {
 
   // chunk mass (residual, or p for a bonus row) and its segment masses
   auto seg_mass = [&](int cc, int w) {   // any chunk, from memory
-    return unpack_lo(p2[(int64_t)cc * kWaves + w]);
+    return to_pair ? p3[(int64_t)cc * kWaves + w] : unpack_lo(p2[(int64_t)cc * kWaves + w]);
   };
   auto chunk_mass_own = [&](int cc) {    // a chunk of this lane's block
     const int i = cc - c0;
@@ -516,7 +655,7 @@ __global__ void verify_finish(VerifyArgs a) {
     return m;
   };
   auto pmass = [&](int cc) {   // mass of p in chunk cc, from its record
-    const uint64_t w0 = rec_load(rs, cc * 24);
+    const uint64_t w0 = rec_load(rs, cc * kSt);
     const float z = unmark(unpack_hi(w0));
     return z > 0.f ? z * fast_exp2(unpack_lo(w0) - lse2_p) : 0.f;
   };
@@ -582,15 +721,20 @@ __global__ void verify_finish(VerifyArgs a) {
       for (int w = 0; w < kWaves; ++w) oseg[w] = seg_mass(sc.owner, w);
     }
     if (pair) {
-      alpha = wave_total(om_sum);
+      float ot[2] = {om_sum, tv_sum};
+      wave_reduce<false, 2>(ot);
+      alpha = ot[0];
+      tv_sum = ot[1];
       if (!(sc.total > 0.f)) {   // the residual has no mass: sample from p
         empty_res = true;
         sc = wave_scan_owner(C, up, pmass);
       }
     }
   }
-  const float r_tot = pair && !empty_res ? sc.total : 0.f;
-  const bool use_q = pair && !empty_res;
+  // TV: the residual mass (the scan's total for rejection sampling)
+  const float r_tot = TO ? tv_sum : pair && !empty_res ? sc.total : 0.f;
+  const bool use_q = !TO && pair && !empty_res;
+  const bool drop_y = to_pair && !empty_res && y_ok;   // target-only residual: p without y
 
   // ---- owner segment inside the owner chunk, then the inverse CDF in it ------
   int token = -1;
@@ -617,7 +761,7 @@ __global__ void verify_finish(VerifyArgs a) {
             const float q = fast_exp2(__builtin_fmaf(x[1][j * PV + e], kLog2e, -lse2_q));
             v[j][e] = fmaxf(p - q, 0.f);
           } else {
-            v[j][e] = p;
+            v[j][e] = drop_y && (s0 + lane + j * 64) * PV + e == y ? 0.f : p;
           }
         }
     };
@@ -660,11 +804,12 @@ __global__ void verify_finish(VerifyArgs a) {
   // clear this row's records and pass-2 words for the next call (the wave has read
   // them all): a call leaves every workspace word it wrote at zero
   for (int cc = lane; cc < C; cc += 64) {
-    rec_store(rs, cc * 24, 0ull);
-    rec_store(rs, cc * 24 + 8, 0ull);
-    rec_store(rs, cc * 24 + 16, 0ull);
+#pragma unroll
+    for (int w = 0; w < kSt / 8; ++w) rec_store(rs, cc * kSt + w * 8, 0ull);
   }
   for (int i = lane; i < C * kWaves; i += 64) p2[i] = 0ull;
+  if (to_pair)
+    for (int i = lane; i < C * kWaves; i += 64) p3[i] = 0.f;
 
   if (lane == 0) {
     int status = 0;
@@ -674,7 +819,15 @@ __global__ void verify_finish(VerifyArgs a) {
     int flag = 0;
     const float nan = __builtin_nanf("");
     if (pair) {
-      if (!y_ok) {
+      if (TO) {
+        // target-only: accept the greedy token with probability p(y); the RS/TO
+        // boundary TV < 1 - p(y)
+        const float py = y_ok && !bad ? fast_exp2(__builtin_fmaf(ay, kLog2e, -lse2_p)) : nan;
+        if (y_ok && !bad) flag = u < py ? 1 : 0;
+        a.draft_token[b * G + k] = y_ok && !bad ? y : -1;
+        if (a.p_yhat) a.p_yhat[b * G + k] = py;
+        if (a.rs_better) a.rs_better[b * G + k] = (uint8_t)(y_ok && !bad && r_tot < 1.f - py ? 1 : 0);
+      } else if (!y_ok) {
         status |= kRowBadToken;
       } else if (!bad) {
         const float d = __builtin_fmaf(ay, kLog2e, -lse2_p) - __builtin_fmaf(by, kLog2e, -lse2_q);
@@ -700,27 +853,37 @@ __global__ void verify_finish(VerifyArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-template <int DT, int NV>
+template <int DT, int NV, bool TO>
 static hipError_t launch(const VerifyArgs& a, hipStream_t stream) {
   const int64_t grid = (int64_t)a.sgroups * a.sp.nchunks;
-  hipLaunchKernelGGL((verify_main<DT, NV>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
+  hipLaunchKernelGGL((verify_main<DT, NV, TO>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((verify_finish<DT, NV>), dim3((unsigned)a.B), dim3(64 * (a.G + 1)), 0, stream, a);
+  hipLaunchKernelGGL((verify_finish<DT, NV, TO>), dim3((unsigned)a.B), dim3(64 * (a.G + 1)), 0, stream, a);
   return hipGetLastError();
 }
 
 int verify_vec_per_thread(int dt) { return dt == kBF16 ? kVerifyNVBf16 : kVerifyNVF32; }
 
-hipError_t launch_verify(const VerifyArgs& a, int dt, hipStream_t stream) {
-  if (dt == kBF16) return launch<kBF16, kVerifyNVBf16>(a, stream);
-  return launch<kF32, kVerifyNVF32>(a, stream);
+int verify_record_words(bool target_only) { return (target_only ? rec_bytes<true>() : rec_bytes<false>()) / 8; }
+
+hipError_t launch_verify(const VerifyArgs& a, int dt, bool target_only, hipStream_t stream) {
+  if (dt == kBF16)
+    return target_only ? launch<kBF16, kVerifyNVBf16, true>(a, stream) : launch<kBF16, kVerifyNVBf16, false>(a, stream);
+  return target_only ? launch<kF32, kVerifyNVF32, true>(a, stream) : launch<kF32, kVerifyNVF32, false>(a, stream);
 }
 
-hipError_t verify_occupancy(int dt, int* blocks_per_cu) {
+template <int DT, int NV, bool TO>
+static hipError_t occupancy(int* n) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, verify_main<DT, NV, TO>, kBlock, 0);
+}
+
+hipError_t verify_occupancy(int dt, bool target_only, int* blocks_per_cu) {
   if (dt == kBF16)
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, verify_main<kBF16, kVerifyNVBf16>, kBlock, 0);
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, verify_main<kF32, kVerifyNVF32>, kBlock, 0);
+    return target_only ? occupancy<kBF16, kVerifyNVBf16, true>(blocks_per_cu)
+                       : occupancy<kBF16, kVerifyNVBf16, false>(blocks_per_cu);
+  return target_only ? occupancy<kF32, kVerifyNVF32, true>(blocks_per_cu)
+                     : occupancy<kF32, kVerifyNVF32, false>(blocks_per_cu);
 }
 
 }  // namespace mtp

@@ -49,6 +49,19 @@ def _require_cuda(*ts):
             raise ValueError("tensors must be on a GPU")
 
 
+def _verify_shape(target, draft):
+    if target.dim() != 3 or draft.dim() != 3:
+        raise ValueError("target must be [B, gamma+1, V] and draft [B, gamma, V]")
+    B, G1, V = target.shape
+    G = G1 - 1
+    if tuple(draft.shape) != (B, G, V) or draft.dtype != target.dtype:
+        raise ValueError("draft must match target: [B, gamma, V], same dtype")
+    for name, t, rows in (("target", target, G1), ("draft", draft, G)):
+        if t.stride(2) != 1 or (B > 1 and t.stride(0) != rows * t.stride(1)):
+            raise ValueError(f"{name} needs unit stride along V and a uniform row stride")
+    return B, G1, V
+
+
 def verify(target, draft, draft_tokens, seed, offset=0, *, stats=True):
     """Rejection-sampling verification (see mtp_verify in include/mtp.h).
 
@@ -60,15 +73,8 @@ def verify(target, draft, draft_tokens, seed, offset=0, *, stats=True):
     """
     lib = load()
     _require_cuda(target, draft, draft_tokens)
-    if target.dim() != 3 or draft.dim() != 3:
-        raise ValueError("target must be [B, gamma+1, V] and draft [B, gamma, V]")
-    B, G1, V = target.shape
+    B, G1, V = _verify_shape(target, draft)
     G = G1 - 1
-    if tuple(draft.shape) != (B, G, V) or draft.dtype != target.dtype:
-        raise ValueError("draft must match target: [B, gamma, V], same dtype")
-    for name, t, rows in (("target", target, G1), ("draft", draft, G)):
-        if t.stride(2) != 1 or (B > 1 and t.stride(0) != rows * t.stride(1)):
-            raise ValueError(f"{name} needs unit stride along V and a uniform row stride")
     if draft_tokens.dtype != torch.int32 or tuple(draft_tokens.shape) != (B, G):
         raise ValueError("draft_tokens must be int32 [B, gamma]")
     draft_tokens = draft_tokens.contiguous()
@@ -95,6 +101,49 @@ def verify(target, draft, draft_tokens, seed, offset=0, *, stats=True):
             _ptr(target), target.stride(1), _ptr(draft), draft.stride(1), dt, B, G, V,
             _ptr(draft_tokens), ctypes.c_uint64(seed), ctypes.c_uint64(offset),
             _ptr(out["accept"]), _ptr(out["accepted_len"]), _ptr(out["next_token"]),
+            _ptr(out.get("row_token")), _ptr(out.get("overlap")), _ptr(out.get("tv")),
+            _ptr(out.get("entropy")), _ptr(out.get("row_status")),
+            _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+def verify_target_only(target, draft, seed, offset=0, *, stats=True):
+    """Target-only verification with the RS/TO diagnostic (see
+    mtp_verify_target_only in include/mtp.h): every draft position proposes its
+    greedy token argmax q.  Same inputs as verify() without draft_tokens; the dict
+    adds draft_token (int32 [B, gamma]) and, with stats, p_yhat (float) and
+    rs_better (uint8) [B, gamma]."""
+    lib = load()
+    _require_cuda(target, draft)
+    B, G1, V = _verify_shape(target, draft)
+    G = G1 - 1
+    dev = target.device
+    dt = _dtype_code(target)
+    out = {
+        "accept": torch.empty((B, G), dtype=torch.uint8, device=dev),
+        "accepted_len": torch.empty(B, dtype=torch.int32, device=dev),
+        "next_token": torch.empty(B, dtype=torch.int32, device=dev),
+        "draft_token": torch.empty((B, G), dtype=torch.int32, device=dev),
+    }
+    if stats:
+        out.update(row_token=torch.empty((B, G1), dtype=torch.int32, device=dev),
+                   row_status=torch.empty((B, G1), dtype=torch.int32, device=dev),
+                   overlap=torch.empty((B, G), dtype=torch.float32, device=dev),
+                   tv=torch.empty((B, G), dtype=torch.float32, device=dev),
+                   entropy=torch.empty((B, G1), dtype=torch.float32, device=dev),
+                   p_yhat=torch.empty((B, G), dtype=torch.float32, device=dev),
+                   rs_better=torch.empty((B, G), dtype=torch.uint8, device=dev))
+    if B == 0:
+        return out
+    nbytes = ctypes.c_size_t()
+    check(lib.mtp_verify_target_only_workspace_size(B, G, V, dt, ctypes.byref(nbytes)))
+    ws = workspace(dev, nbytes.value)
+    with torch.cuda.device(dev):
+        check(lib.mtp_verify_target_only(
+            _ptr(target), target.stride(1), _ptr(draft), draft.stride(1), dt, B, G, V,
+            ctypes.c_uint64(seed), ctypes.c_uint64(offset),
+            _ptr(out["accept"]), _ptr(out["accepted_len"]), _ptr(out["next_token"]), _ptr(out["draft_token"]),
+            _ptr(out.get("p_yhat")), _ptr(out.get("rs_better")),
             _ptr(out.get("row_token")), _ptr(out.get("overlap")), _ptr(out.get("tv")),
             _ptr(out.get("entropy")), _ptr(out.get("row_status")),
             _ptr(ws), ws.numel(), _stream(dev)))
@@ -210,23 +259,34 @@ class VerifyPlan:
     offset)` enqueues mtp_verify on the current stream and returns the outputs
     dict, whose tensors are overwritten by every run."""
 
-    def __init__(self, target, draft, draft_tokens):
+    def __init__(self, target, draft, draft_tokens=None, target_only=False):
         self.lib = load()
-        draft_tokens = draft_tokens.contiguous()
-        self.inputs = (target, draft, draft_tokens)                   # keeps the pointers alive
-        self.out = verify(target, draft, draft_tokens, 0, 0)          # validates, allocates, warms
         B, G1, V = target.shape
         self.shape = (B, G1 - 1, V)
         nbytes = ctypes.c_size_t()
-        check(self.lib.mtp_verify_workspace_size(B, G1 - 1, V, _dtype_code(target), ctypes.byref(nbytes)))
+        dt = _dtype_code(target)
+        if target_only:                                               # greedy draft tokens
+            self.inputs = (target, draft)                             # keeps the pointers alive
+            self.out = verify_target_only(target, draft, 0, 0)        # validates, allocates, warms
+            check(self.lib.mtp_verify_target_only_workspace_size(B, G1 - 1, V, dt, ctypes.byref(nbytes)))
+            self._head = (_ptr(target), target.stride(1), _ptr(draft), draft.stride(1), dt, B, G1 - 1, V)
+            o = self.out
+            mid = (_ptr(o["accept"]), _ptr(o["accepted_len"]), _ptr(o["next_token"]), _ptr(o["draft_token"]),
+                   _ptr(o["p_yhat"]), _ptr(o["rs_better"]))
+            self._fn = self.lib.mtp_verify_target_only
+        else:
+            draft_tokens = draft_tokens.contiguous()
+            self.inputs = (target, draft, draft_tokens)
+            self.out = verify(target, draft, draft_tokens, 0, 0)
+            check(self.lib.mtp_verify_workspace_size(B, G1 - 1, V, dt, ctypes.byref(nbytes)))
+            self._head = (_ptr(target), target.stride(1), _ptr(draft), draft.stride(1), dt, B, G1 - 1, V,
+                          _ptr(draft_tokens))
+            o = self.out
+            mid = (_ptr(o["accept"]), _ptr(o["accepted_len"]), _ptr(o["next_token"]))
+            self._fn = self.lib.mtp_verify
         self.ws = workspace(target.device, nbytes.value)
-        o = self.out
-        self._head = (_ptr(target), target.stride(1), _ptr(draft), draft.stride(1), _dtype_code(target),
-                      B, G1 - 1, V, _ptr(draft_tokens))
-        self._tail = (_ptr(o["accept"]), _ptr(o["accepted_len"]), _ptr(o["next_token"]), _ptr(o["row_token"]),
-                      _ptr(o["overlap"]), _ptr(o["tv"]), _ptr(o["entropy"]), _ptr(o["row_status"]),
-                      _ptr(self.ws), self.ws.numel(), _stream(target.device))
-        self._fn = self.lib.mtp_verify
+        self._tail = mid + (_ptr(o["row_token"]), _ptr(o["overlap"]), _ptr(o["tv"]), _ptr(o["entropy"]),
+                            _ptr(o["row_status"]), _ptr(self.ws), self.ws.numel(), _stream(target.device))
 
     def run(self, seed, offset=0):
         st = self._fn(*self._head, ctypes.c_uint64(seed), ctypes.c_uint64(offset), *self._tail)
