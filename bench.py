@@ -13,7 +13,7 @@ positions x 3 heads, V = 151936 (bf16 in, bf16 gradient out), as algorithmic GB/
 against the 8 TB/s HBM peak; (`long_tail`) verify on 512 x 4 positions at V = 2^18
 with Zipf-like logits; (`entropy_sweep`) verify on the 15 temperature x noise cells
 (128 sequences each), with each cell's acceptance rate, mean accepted length and
-mean target entropy.
+mean target entropy; (`target_only`) target-only verify of the rollout workload.
 
 `roofline` uses per-launch HIP events recorded on the stream the kernels run on;
 `cpu_baseline` times the float64 oracle on a bounded sample of the same workload.
@@ -79,14 +79,14 @@ def check_waits(mtp, ws):
         sys.exit(f"bench: a cluster wait timed out (workspace error word {word:#x})")
 
 
-def time_verify(mtp, torch, w, steps, warmup, nsets):
+def time_verify(mtp, torch, w, steps, warmup, nsets, target_only=False):
     import synthetic
     dev = "cuda:0"
     B, G, V = w["B"], w["G"], w["V"]
     plans = []
     for i in range(nsets):
         t, d, y = synthetic.verify_inputs(w, dev, seed=w["seed"] + i)
-        plans.append(mtp.VerifyPlan(t, d, y))
+        plans.append(mtp.VerifyPlan(t, d, None, target_only=True) if target_only else mtp.VerifyPlan(t, d, y))
     torch.cuda.synchronize()
     rows = B * (G + 1)
     plans[0].run(seed=w["seed"], offset=0)
@@ -255,6 +255,25 @@ def main():
             f"({bwd_bytes / bm / 1e6:.0f} GB/s), total {gbs:.0f} GB/s")
 
     if not args.no_extra:
+        # target-only verify of the rollout workload (greedy draft tokens, the RS/TO flag)
+        log("verify: target-only on the rollout workload")
+        owall, okms, plans = time_verify(mtp, torch, w, args.steps, args.warmup, nsets, target_only=True)
+        out = plans[0].run(seed=w["seed"], offset=0)
+        to_acc = out["accept"].float().mean().item()
+        rs_share = out["rs_better"].float().mean().item()
+        del plans, out
+        omean = sum(okms) / len(okms)
+        result["target_only"] = {
+            "workload": "target-only verify of the rollout workload (greedy draft tokens argmax q, accept with "
+                        "p(yhat), RS/TO boundary TV < 1 - p(yhat))",
+            "value": positions / owall, "unit": "draft positions/s", "kernel_us_mean": omean * 1e3,
+            "accept_rate": to_acc, "rs_better_share": rs_share,
+            "roofline": {"bound": "hbm", "achieved": alg_bytes / (omean * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": alg_bytes / (omean * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "bytes_per_launch": alg_bytes},
+        }
+        log(f"verify target-only: {omean * 1e3:.2f} us per call, accept rate {to_acc:.3f}, "
+            f"RS better on {rs_share:.3f} of positions")
         # the long-tail workload (Zipf-like logits, V = 2^18, gamma = 4) and the 15
         # cells of the entropy sweep, each timed like the rollout workload
         lw = synthetic.VERIFY_WORKLOADS["long_tail"]
