@@ -15,9 +15,9 @@ constexpr int kVerifyNVBf16 = 2;
 constexpr int kVerifyNVF32 = 3;
 constexpr int kMaxRowsPerSeq = 9;  // gamma + 1 with gamma <= 8
 // Workgroups per CU the verify main kernel is compiled for (one wave per SIMD
-// each): 3 (168 VGPRs) keeps one layer's e values in registers and two chunks in
-// flight.
-constexpr int kVerifyBlocksPerCU = 3;
+// each): 4 (128 VGPRs) keeps one layer's e values in registers and two chunks in
+// flight, for both dtypes and both acceptance rules, without spilling.
+constexpr int kVerifyBlocksPerCU = 4;
 
 // Counters sit 16 ints (64 bytes) apart so clusters do not share a line.
 constexpr int kCounterStride = 16;
