@@ -275,7 +275,9 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
     // ---- row statistics of item i - 2 (polled a layer ago) ---------------------
     if (i >= 2 && i - 2 < nl) {
       const bool pair2 = pair_m2;
+      // the bookkeeping waves run at raised priority: the layer waits for them
       if (wave == rp || (wave == rq && pair2)) {
+        __builtin_amdgcn_s_setprio(3);
         const int row = wave == rp ? 0 : 1;
         const Lse st = poll_row(wpoll, rsrc_rec(g_m2), C, kSt, row, a.err);
         if (lane == 0) lse_sh[i & 1][row] = lse_log2(st);
@@ -283,6 +285,7 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
           const uint32_t yh = poll_argmax(wpoll_am, rsrc_rec(g_m2), C, kSt, a.err);
           if (lane == 0) yhat_sh[i & 1] = yh;
         }
+        __builtin_amdgcn_s_setprio(0);
       }
       __syncthreads();
       // ---- pass 2 of item i - 2 ------------------------------------------------
@@ -434,6 +437,7 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
         }
       }
       __syncthreads();
+      if (wave == wp || wave == wq) __builtin_amdgcn_s_setprio(3);
       if (wave == wp) {
         const Lse p = merge_lds<kWaves, true>(part_sh[i & 1][0]);
         if (lane == 0) {
@@ -455,6 +459,7 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
           }
         }
       }
+      __builtin_amdgcn_s_setprio(0);
     }
     // ---- shift the item window -------------------------------------------------
     g_m2 = g_m1;
