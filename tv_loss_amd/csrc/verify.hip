@@ -401,6 +401,8 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
 
     if (i < nl) {
       // ---- pass 1 of item i: wave partials, combined and published --------------
+      // (raised priority up to the barrier: the combine and the next layer wait on it)
+      __builtin_amdgcn_s_setprio(1);
       Lse pt[2];
       float am = 0.f;   // target-only: this wave's largest draft logit and its index
       uint32_t ai = 0;
@@ -436,6 +438,7 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
           ai_sh[i & 1][wave] = ai;
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       __syncthreads();
       if (wave == wp || wave == wq) __builtin_amdgcn_s_setprio(3);
       if (wave == wp) {
