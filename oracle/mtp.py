@@ -10,7 +10,7 @@ Readings taken where the pages leave a step open are marked READING.
 """
 import numpy as np
 
-from .philox import verify_uniforms
+from .philox import element_uniforms, verify_uniforms
 
 # Row status flags.  READING: the pages define no error handling; these name the
 # data conditions that make a row's result undefined or that change its rule.
@@ -334,6 +334,82 @@ def verify_target_only(target, draft, seed, offset, tie_band=1e-6, cdf_tie_band=
         while n < G and out["accept"][b, n] == 1:
             n += 1
         out["accepted_len"][b] = n
+        out["next_token"][b] = out["row_token"][b, n]
+    return out
+
+
+def gumbel_argmax(logw, U, gap_band=1e-4):
+    """argmax_v (log w_v + G_v) with G_v = -log(-log U_v): the Gumbel-max trick, a
+    sample from w / sum w (paperlayer App. G.2 "Gumbel-Max Trick (vLLM)").  Entries
+    with w_v = 0 (log w_v = -inf) never win.  READING: ties go to the smallest index.
+    Returns (token, near_tie): near_tie marks a runner-up key within gap_band of the
+    winner's, where a float32 evaluation of the keys may choose the other token.
+    """
+    keys = np.asarray(logw, dtype=np.float64) - np.log(-np.log(np.asarray(U, dtype=np.float64)))
+    tok = int(np.argmax(keys))
+    top = keys[tok]
+    rest = np.delete(keys, tok)
+    near = bool(rest.size) and bool(np.max(rest) >= top - gap_band)
+    return tok, near
+
+
+def gumbel_draft_tokens(draft, seed, offset, temperature=1.0):
+    """Draft tokens by the Gumbel-max trick at temperature T: y = argmax_v
+    (z_v / T + G_v) for each row of draft logits z [..., V] (App. G.2: argmax of
+    log q / T + G, and log q differs from z / T by a constant).  Row r (in
+    row-major order) uses element_uniforms(seed, offset, r, V).  Returns (tokens,
+    near_tie) of the leading shape."""
+    z = np.asarray(draft, dtype=np.float64)
+    lead, V = z.shape[:-1], z.shape[-1]
+    flat = z.reshape(-1, V)
+    tok = np.zeros(flat.shape[0], np.int32)
+    tie = np.zeros(flat.shape[0], bool)
+    for r in range(flat.shape[0]):
+        tok[r], tie[r] = gumbel_argmax(flat[r] / temperature, element_uniforms(seed, offset, r, V))
+    return tok.reshape(lead), tie.reshape(lead)
+
+
+def verify_gumbel(target, draft, tokens, seed, offset, temperature=1.0, tie_band=1e-6, cdf_tie_band=1e-6):
+    """Rejection-sampling verification at temperature T with Gumbel-max sampling of
+    the emitted tokens (paperlayer App. G.2, "Gumbel-Max Trick (vLLM)").
+
+    Steps as in verify, except:
+      1. p_k = softmax(target_k / T), q_k = softmax(draft_k / T).  READING: the
+         temperature scales both the target and the cached draft logits.
+      7. Row sample: r = max(0, p_k - q_k) (k < gamma) or p_gamma (bonus row); the
+         token is gumbel_argmax(log r, U) with U = element_uniforms(seed, offset,
+         b*(gamma+1) + k, V); an empty residual samples p the same way (flagged).
+    Acceptance uses the same u as verify; token_tie marks a near-tie of the keys
+    (or a residual below cdf_tie_band, as in row_sample).
+    """
+    target = np.asarray(target, dtype=np.float64) / temperature
+    draft = np.asarray(draft, dtype=np.float64) / temperature
+    out = verify(target, draft, tokens, seed, offset, tie_band, cdf_tie_band)
+    B, G1, V = target.shape
+    G = G1 - 1
+    for b in range(B):
+        for k in range(G1):
+            logp, _ = log_softmax(target[b, k])
+            if logp is None:
+                continue
+            U = element_uniforms(seed, offset, b * G1 + k, V)
+            p = np.exp(logp)
+            near_empty = False
+            w = p
+            if k < G:
+                logq, _ = log_softmax(draft[b, k])
+                if logq is None:
+                    continue
+                r = residual(p, np.exp(logq))
+                mass = float(np.sum(r))
+                near_empty = mass < cdf_tie_band
+                if mass > 0:
+                    w = r
+            with np.errstate(divide="ignore"):
+                tok, near = gumbel_argmax(np.log(w), U)
+            out["row_token"][b, k] = tok
+            out["token_tie"][b, k] = near or near_empty
+        n = out["accepted_len"][b]
         out["next_token"][b] = out["row_token"][b, n]
     return out
 

@@ -81,3 +81,22 @@ def verify_uniforms(seed, offset, positions):
     u = (out[..., 0] >> np.uint32(8)).astype(np.float64) * scale
     up = (out[..., 1] >> np.uint32(8)).astype(np.float64) * scale
     return u, up
+
+
+def element_uniforms(seed, offset, position, V):
+    """Per-element uniforms U_v, v < V, of one row, for Gumbel-max sampling.
+
+    READING (the pages name the Gumbel-max trick but no generator layout): key as
+    in verify_uniforms; counter = (c low 32, c high 32, 1 + v // 4, 0) with
+    c = offset + position, output word v % 4; U = ((word >> 8) + 1/2) * 2**-24, in
+    (0, 1) strictly, so that -log(-log U) is finite.  Counter word 2 is at least 1,
+    so these never coincide with the row's (u, u') (word 2 = 0).
+    Returns a float64 array [V].
+    """
+    c = int(offset) + int(position)
+    groups = np.arange((V + 3) // 4, dtype=np.uint64)
+    ctr = np.stack([np.full_like(groups, c & 0xFFFFFFFF), np.full_like(groups, (c >> 32) & 0xFFFFFFFF),
+                    groups + np.uint64(1), np.zeros_like(groups)], axis=-1)
+    seed = int(seed) & ((1 << 64) - 1)
+    out = philox4x32_10(ctr, (seed & 0xFFFFFFFF, seed >> 32)).reshape(-1)[:V]
+    return ((out >> np.uint32(8)).astype(np.float64) + 0.5) * 2.0 ** -24
