@@ -140,6 +140,48 @@ mtp_status mtp_verify_target_only(const void* target, int64_t target_row_stride,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Verification at a temperature with Gumbel-max sampling (paperlayer App. G.2
+ * "Gumbel-Max Trick (vLLM)"; Sec. 2 acceptance methods).
+ *
+ * As mtp_verify with p = softmax(target row / T) and q = softmax(draft row / T)
+ * (the temperature scales both), except for the row samples:
+ *   row_token[b, k] = argmax_v (log r_v + g_v), r as for mtp_verify (an empty
+ *                     residual samples p, MTP_ROW_RESIDUAL_EMPTY set), the smallest
+ *                     index among equal keys;
+ *   g_v = -log(-log U_v), U_v = ((w >> 8) + 1/2) * 2^-24 with w word v % 4 of the
+ *         Philox4x32-10 block at key = seed, counter words (lo(c), hi(c),
+ *         v / 4 + 1, 0), c = offset + b * (gamma + 1) + k.
+ * u keeps mtp_verify's counter (third word 0), so acceptance uses the same
+ * uniforms.  temperature must be positive and finite (else MTP_ERR_SHAPE);
+ * T = 1 gives mtp_verify's accept flags and statistics.  Other arguments as for
+ * mtp_verify; its own workspace size.
+ */
+mtp_status mtp_verify_gumbel_workspace_size(int32_t batch, int32_t gamma, int32_t vocab, mtp_dtype dtype,
+                                            size_t* bytes);
+
+mtp_status mtp_verify_gumbel(const void* target, int64_t target_row_stride,
+                             const void* draft, int64_t draft_row_stride, mtp_dtype dtype,
+                             int32_t batch, int32_t gamma, int32_t vocab,
+                             const int32_t* draft_tokens, float temperature, uint64_t seed, uint64_t offset,
+                             uint8_t* accept, int32_t* accepted_len, int32_t* next_token,
+                             int32_t* row_token, float* overlap, float* tv, float* entropy,
+                             int32_t* row_status,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Gumbel-max draft sampling (paperlayer App. G.2): for each of `rows` logit rows x
+ * (device, dtype, row r at logits + r * row_stride elements),
+ *   tokens[r] = argmax_v (x_v / T + g_v)   (a sample of softmax(x / T)),
+ * g_v as for mtp_verify_gumbel with c = offset + r; the smallest index among
+ * equal keys, -1 for a row with no finite key (all -inf or NaN logits).  tokens:
+ * device int32 [rows].  No workspace; rows == 0 is a no-op.  Sampling draft rows
+ * (b, k) in row-major order with offset o and verifying with an offset whose
+ * counters do not overlap [o, o + batch * gamma) keeps the two noises independent.
+ */
+mtp_status mtp_gumbel_sample(const void* logits, int64_t row_stride, mtp_dtype dtype, int32_t rows,
+                             int32_t vocab, float temperature, uint64_t seed, uint64_t offset,
+                             int32_t* tokens, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* End-to-end TV loss, forward (paperlayer Sec. 4 "End-to-end TV loss", App. F;
  * rainbus "Method steps").  For position t and head k (1-based in the formula):
  *   alpha_{t,k} = clamp(sum_v min(p_v, q_v), 0, 1)

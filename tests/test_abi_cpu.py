@@ -98,6 +98,55 @@ def test_workspace_sizes_grow_with_the_problem():
     assert lib.mtp_tv_loss_workspace_size(8192, 3, 151936, 1, 1, ctypes.byref(n)) == 0 and n.value > 0
 
 
+def _verify_gumbel(lib, **kw):
+    a = dict(target=A16, ts=151936, draft=A16, ds=151936, dt=1, B=64, G=3, V=151936, tok=A16, T=0.8, seed=0,
+             off=0, acc=A16, alen=A16, nxt=A16, ws=A16, wsb=1 << 30)
+    a.update(kw)
+    return lib.mtp_verify_gumbel(a["target"], a["ts"], a["draft"], a["ds"], a["dt"], a["B"], a["G"], a["V"],
+                                 a["tok"], a["T"], a["seed"], a["off"], a["acc"], a["alen"], a["nxt"], None, None,
+                                 None, None, None, a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(tok=None), 1), (dict(acc=None), 1), (dict(G=9), 2), (dict(ds=7), 2),
+    (dict(T=0.0), 2), (dict(T=-1.0), 2), (dict(T=float("inf")), 2), (dict(T=float("nan")), 2),
+    (dict(dt=3), 3), (dict(draft=MIS), 4), (dict(ws=None), 5), (dict(wsb=4096), 5),
+])
+def test_verify_gumbel_rejects_bad_arguments(kw, code):
+    lib = tv_loss_amd.load()
+    assert _verify_gumbel(lib, **kw) == code, lib.mtp_last_error()
+    assert lib.mtp_last_error()
+
+
+def _sample(lib, **kw):
+    a = dict(x=A16, rs=151936, dt=1, rows=64, V=151936, T=1.0, seed=0, off=0, tok=A16)
+    a.update(kw)
+    return lib.mtp_gumbel_sample(a["x"], a["rs"], a["dt"], a["rows"], a["V"], a["T"], a["seed"], a["off"],
+                                 a["tok"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), 1), (dict(tok=None), 1),
+    (dict(rows=-1), 2), (dict(V=0), 2), (dict(V=(1 << 30) + 1), 2), (dict(rs=151935), 2),
+    (dict(T=0.0), 2), (dict(T=float("nan")), 2), (dict(T=float("-inf")), 2),
+    (dict(dt=9), 3), (dict(x=MIS), 4), (dict(rs=151937, V=151937), 4),
+])
+def test_gumbel_sample_rejects_bad_arguments(kw, code):
+    lib = tv_loss_amd.load()
+    assert _sample(lib, **kw) == code, lib.mtp_last_error()
+
+
+def test_gumbel_entries_empty_inputs_and_workspace():
+    lib = tv_loss_amd.load()
+    assert _sample(lib, rows=0, x=None, tok=None) == 0
+    assert _verify_gumbel(lib, B=0, target=None, draft=None, tok=None, ws=None, wsb=0) == 0
+    n_rs, n_gm = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.mtp_verify_workspace_size(64, 3, 151936, 1, ctypes.byref(n_rs)) == 0
+    assert lib.mtp_verify_gumbel_workspace_size(64, 3, 151936, 1, ctypes.byref(n_gm)) == 0
+    assert n_gm.value > n_rs.value and n_gm.value % 256 == 0   # adds the per-wave key words
+    assert lib.mtp_verify_gumbel_workspace_size(0, 3, 151936, 1, ctypes.byref(n_gm)) == 0 and n_gm.value == 0
+
+
 def _fwd(lib, **kw):
     a = dict(t=A16, tp=151936, th=0, d=A16, dp=3 * 151936, dh=151936, dt=1, T=8, G=3, V=151936, loss=A16,
              pos=None, saved=A16, ws=A16, wsb=1 << 30, stream=None)

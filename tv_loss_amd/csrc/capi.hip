@@ -36,6 +36,7 @@ int elem_bytes(mtp_dtype dt) { return dt == MTP_BF16 ? 2 : 4; }
 int per_vec(mtp_dtype dt) { return dt == MTP_BF16 ? 8 : 4; }
 
 constexpr int64_t kMaxVocab = int64_t(1) << 30;
+constexpr float kLog2e = 1.4426950408889634f;
 
 mtp_status check_common(mtp_dtype dt, int32_t gamma, int32_t vocab) {
   if (dt != MTP_F32 && dt != MTP_BF16) return fail(MTP_ERR_DTYPE, "unknown dtype code %d", (int)dt);
@@ -56,7 +57,7 @@ mtp_status check_row_base(const void* p, int64_t stride_elems, mtp_dtype dt, con
 // ---- per-device limits --------------------------------------------------------
 struct DeviceInfo {
   int cus = 0;
-  std::map<int, int> occ;   // (dtype, target-only) -> verify main workgroups per CU
+  std::map<int, int> occ;   // (dtype, verify mode) -> verify main workgroups per CU
 };
 std::mutex g_dev_mu;
 std::map<int, DeviceInfo> g_dev;
@@ -64,7 +65,7 @@ std::map<int, DeviceInfo> g_dev;
 // Workgroups of the verify main kernel the current device holds at once: all of a
 // launch's workgroups must be resident together (a super-group waits on its
 // members' records).
-mtp_status verify_capacity(int dt, bool target_only, int64_t* per_gpu) {
+mtp_status verify_capacity(int dt, int mode, int64_t* per_gpu) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(MTP_ERR_DEVICE, "hipGetDevice failed");
   std::lock_guard<std::mutex> lk(g_dev_mu);
@@ -73,11 +74,11 @@ mtp_status verify_capacity(int dt, bool target_only, int64_t* per_gpu) {
     if (hipDeviceGetAttribute(&info.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return fail(MTP_ERR_DEVICE, "cannot query the compute-unit count");
   }
-  const int key = dt * 2 + (target_only ? 1 : 0);
+  const int key = dt * 4 + mode;
   auto it = info.occ.find(key);
   if (it == info.occ.end()) {
     int n = 0;
-    hipError_t e = mtp::verify_occupancy(dt, target_only, &n);
+    hipError_t e = mtp::verify_occupancy(dt, mode, &n);
     if (e != hipSuccess || n < 1) return fail(MTP_ERR_DEVICE, "occupancy query failed");
     it = info.occ.emplace(key, n).first;
   }
@@ -87,22 +88,24 @@ mtp_status verify_capacity(int dt, bool target_only, int64_t* per_gpu) {
 
 // ---- workspace layouts --------------------------------------------------------
 struct VerifyLayout {
-  size_t err, part1, part2, part3, total;
+  size_t err, part1, part2, part3, gkeys, total;
   mtp::RowSplit sp;
   int64_t ngroups;
 };
 
-VerifyLayout verify_layout(int32_t B, int32_t G, int32_t V, mtp_dtype dt, bool target_only) {
+VerifyLayout verify_layout(int32_t B, int32_t G, int32_t V, mtp_dtype dt, int mode) {
   VerifyLayout L{};
   L.sp = mtp::make_split(V, per_vec(dt), mtp::verify_vec_per_thread(dt), false);
   L.ngroups = (int64_t)B * (G + 1);
   const int64_t C = L.sp.nchunks;
   size_t off = 0;
   L.err = off; off = align256(off + 4);
-  L.part1 = off; off = align256(off + (size_t)L.ngroups * C * mtp::verify_record_words(target_only) * 8);
+  L.part1 = off; off = align256(off + (size_t)L.ngroups * C * mtp::verify_record_words(mode) * 8);
   L.part2 = off; off = align256(off + (size_t)L.ngroups * C * mtp::kWaves * 8);
   L.part3 = off;
-  if (target_only) off = align256(off + (size_t)L.ngroups * C * mtp::kWaves * 4);
+  if (mode == mtp::kVerifyTargetOnly) off = align256(off + (size_t)L.ngroups * C * mtp::kWaves * 4);
+  L.gkeys = off;
+  if (mode == mtp::kVerifyGumbel) off = align256(off + (size_t)L.ngroups * C * mtp::kWaves * 2 * 8);
   L.total = off;
   return L;
 }
@@ -178,7 +181,7 @@ mtp_status mtp_verify_workspace_size(int32_t batch, int32_t gamma, int32_t vocab
   mtp_status s = check_common(dtype, gamma, vocab);
   if (s) return s;
   if (batch < 0) return fail(MTP_ERR_SHAPE, "batch = %d is negative", batch);
-  *bytes = batch == 0 ? 0 : verify_layout(batch, gamma, vocab, dtype, false).total;
+  *bytes = batch == 0 ? 0 : verify_layout(batch, gamma, vocab, dtype, mtp::kVerifyRejection).total;
   return ok();
 }
 
@@ -188,7 +191,17 @@ mtp_status mtp_verify_target_only_workspace_size(int32_t batch, int32_t gamma, i
   mtp_status s = check_common(dtype, gamma, vocab);
   if (s) return s;
   if (batch < 0) return fail(MTP_ERR_SHAPE, "batch = %d is negative", batch);
-  *bytes = batch == 0 ? 0 : verify_layout(batch, gamma, vocab, dtype, true).total;
+  *bytes = batch == 0 ? 0 : verify_layout(batch, gamma, vocab, dtype, mtp::kVerifyTargetOnly).total;
+  return ok();
+}
+
+mtp_status mtp_verify_gumbel_workspace_size(int32_t batch, int32_t gamma, int32_t vocab, mtp_dtype dtype,
+                                            size_t* bytes) {
+  if (!bytes) return fail(MTP_ERR_NULL, "bytes is NULL");
+  mtp_status s = check_common(dtype, gamma, vocab);
+  if (s) return s;
+  if (batch < 0) return fail(MTP_ERR_SHAPE, "batch = %d is negative", batch);
+  *bytes = batch == 0 ? 0 : verify_layout(batch, gamma, vocab, dtype, mtp::kVerifyGumbel).total;
   return ok();
 }
 
@@ -196,9 +209,12 @@ mtp_status mtp_verify_target_only_workspace_size(int32_t batch, int32_t gamma, i
 
 namespace {
 
-// Both verify entry points: rejection sampling (draft_tokens given) or target-only
-// (draft_token out).  Argument errors return before any HIP call.
-mtp_status verify_impl(bool target_only, const void* target, int64_t target_row_stride, const void* draft,
+bool bad_temperature(float T) { return !(T > 0.f) || T == __builtin_inff(); }
+
+// The verify entry points: rejection sampling (draft_tokens given), target-only
+// (draft_token out) or rejection sampling at a temperature with Gumbel-max row
+// samples.  Argument errors return before any HIP call.
+mtp_status verify_impl(int mode, float temperature, const void* target, int64_t target_row_stride, const void* draft,
                        int64_t draft_row_stride, mtp_dtype dtype, int32_t batch, int32_t gamma, int32_t vocab,
                        const int32_t* draft_tokens, uint64_t seed, uint64_t offset, uint8_t* accept,
                        int32_t* accepted_len, int32_t* next_token, int32_t* draft_token, float* p_yhat,
@@ -210,6 +226,7 @@ mtp_status verify_impl(bool target_only, const void* target, int64_t target_row_
   if (batch == 0) return ok();
   if (!target || !draft || !accept || !accepted_len || !next_token)
     return fail(MTP_ERR_NULL, "a required pointer (target, draft, accept, accepted_len, next_token) is NULL");
+  const bool target_only = mode == mtp::kVerifyTargetOnly;
   if (!target_only && !draft_tokens) return fail(MTP_ERR_NULL, "draft_tokens is NULL");
   if (target_only && !draft_token) return fail(MTP_ERR_NULL, "draft_token is NULL");
   if (target_row_stride < vocab || draft_row_stride < vocab)
@@ -217,13 +234,15 @@ mtp_status verify_impl(bool target_only, const void* target, int64_t target_row_
                 (long long)draft_row_stride, vocab);
   if ((s = check_row_base(target, target_row_stride, dtype, "target"))) return s;
   if ((s = check_row_base(draft, draft_row_stride, dtype, "draft"))) return s;
-  const VerifyLayout L = verify_layout(batch, gamma, vocab, dtype, target_only);
+  if (mode == mtp::kVerifyGumbel && bad_temperature(temperature))
+    return fail(MTP_ERR_SHAPE, "temperature %g is not a positive finite number", (double)temperature);
+  const VerifyLayout L = verify_layout(batch, gamma, vocab, dtype, mode);
   if ((s = check_workspace(workspace, workspace_bytes, L.total))) return s;
   if (L.ngroups > 0x7fffffffLL / 8) return fail(MTP_ERR_SHAPE, "batch * (gamma + 1) is too large");
 
   // ---- device-dependent checks ---------------------------------------------
   int64_t per_gpu = 0;
-  if ((s = verify_capacity(dtype, target_only, &per_gpu))) return s;
+  if ((s = verify_capacity(dtype, mode, &per_gpu))) return s;
   if ((int64_t)L.sp.nchunks > per_gpu)
     return fail(MTP_ERR_SHAPE, "vocab %d needs %d co-resident workgroups per row; the GPU holds %lld", vocab,
                 L.sp.nchunks, (long long)per_gpu);
@@ -243,11 +262,13 @@ mtp_status verify_impl(bool target_only, const void* target, int64_t target_row_
   a.part1 = at<uint64_t>(workspace, L.part1);
   a.part2 = at<uint64_t>(workspace, L.part2);
   a.part3 = target_only ? at<float>(workspace, L.part3) : nullptr;
+  a.gkeys = mode == mtp::kVerifyGumbel ? at<uint64_t>(workspace, L.gkeys) : nullptr;
+  a.inv_temp = mode == mtp::kVerifyGumbel ? 1.f / temperature : 1.f;
   a.sp = L.sp;
   a.ngroups = (int)L.ngroups;
   a.sgroups = sgroups;
   a.layers = layers;
-  hipError_t e = mtp::launch_verify(a, dtype, target_only, (hipStream_t)stream);
+  hipError_t e = mtp::launch_verify(a, dtype, mode, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MTP_ERR_LAUNCH, "verify launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -262,7 +283,7 @@ mtp_status mtp_verify(const void* target, int64_t target_row_stride, const void*
                       uint8_t* accept, int32_t* accepted_len, int32_t* next_token, int32_t* row_token,
                       float* overlap, float* tv, float* entropy, int32_t* row_status, void* workspace,
                       size_t workspace_bytes, void* stream) {
-  return verify_impl(false, target, target_row_stride, draft, draft_row_stride, dtype, batch, gamma, vocab,
+  return verify_impl(mtp::kVerifyRejection, 1.f, target, target_row_stride, draft, draft_row_stride, dtype, batch, gamma, vocab,
                      draft_tokens, seed, offset, accept, accepted_len, next_token, nullptr, nullptr, nullptr,
                      row_token, overlap, tv, entropy, row_status, workspace, workspace_bytes, stream);
 }
@@ -274,9 +295,40 @@ mtp_status mtp_verify_target_only(const void* target, int64_t target_row_stride,
                                   uint8_t* rs_better, int32_t* row_token, float* overlap, float* tv,
                                   float* entropy, int32_t* row_status, void* workspace, size_t workspace_bytes,
                                   void* stream) {
-  return verify_impl(true, target, target_row_stride, draft, draft_row_stride, dtype, batch, gamma, vocab,
+  return verify_impl(mtp::kVerifyTargetOnly, 1.f, target, target_row_stride, draft, draft_row_stride, dtype, batch, gamma, vocab,
                      nullptr, seed, offset, accept, accepted_len, next_token, draft_token, p_yhat, rs_better,
                      row_token, overlap, tv, entropy, row_status, workspace, workspace_bytes, stream);
+}
+
+mtp_status mtp_verify_gumbel(const void* target, int64_t target_row_stride, const void* draft,
+                             int64_t draft_row_stride, mtp_dtype dtype, int32_t batch, int32_t gamma,
+                             int32_t vocab, const int32_t* draft_tokens, float temperature, uint64_t seed,
+                             uint64_t offset, uint8_t* accept, int32_t* accepted_len, int32_t* next_token,
+                             int32_t* row_token, float* overlap, float* tv, float* entropy, int32_t* row_status,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return verify_impl(mtp::kVerifyGumbel, temperature, target, target_row_stride, draft, draft_row_stride, dtype,
+                     batch, gamma, vocab, draft_tokens, seed, offset, accept, accepted_len, next_token, nullptr,
+                     nullptr, nullptr, row_token, overlap, tv, entropy, row_status, workspace, workspace_bytes,
+                     stream);
+}
+
+mtp_status mtp_gumbel_sample(const void* logits, int64_t row_stride, mtp_dtype dtype, int32_t rows, int32_t vocab,
+                             float temperature, uint64_t seed, uint64_t offset, int32_t* tokens, void* stream) {
+  if (dtype != MTP_F32 && dtype != MTP_BF16) return fail(MTP_ERR_DTYPE, "unknown dtype code %d", (int)dtype);
+  if (rows < 0) return fail(MTP_ERR_SHAPE, "rows = %d is negative", rows);
+  if (vocab < 1 || vocab > kMaxVocab) return fail(MTP_ERR_SHAPE, "vocab = %d outside [1, 2^30]", vocab);
+  if (bad_temperature(temperature))
+    return fail(MTP_ERR_SHAPE, "temperature %g is not a positive finite number", (double)temperature);
+  if (rows == 0) return ok();
+  if (!logits || !tokens) return fail(MTP_ERR_NULL, "logits or tokens is NULL");
+  if (row_stride < vocab)
+    return fail(MTP_ERR_SHAPE, "row stride %lld must be >= vocab (%d)", (long long)row_stride, vocab);
+  mtp_status s = check_row_base(logits, row_stride, dtype, "logits");
+  if (s) return s;
+  hipError_t e = mtp::launch_gumbel_sample(logits, row_stride, dtype, rows, vocab, kLog2e / temperature,
+                                           seed, offset, tokens, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MTP_ERR_LAUNCH, "Gumbel sample launch failed: %s", hipGetErrorString(e));
+  return ok();
 }
 
 mtp_status mtp_tv_loss_workspace_size(int32_t T, int32_t gamma, int32_t vocab, mtp_dtype dtype,

@@ -466,15 +466,16 @@ __device__ __forceinline__ Lse lse_nan() {
 }
 
 // Log-sum-exp partials of R rows over a wave, the rows interleaved so that their
-// dependency chains overlap.  For row r the wave's largest logit M is the reference
-// (ref = M log2 e), x[r] is overwritten with e = 2^(x log2 e - ref) and the sums of
-// e, and for r < RY of e * (x log2 e - ref) (the entropy moment), are taken over the
+// dependency chains overlap.  L converts logits to base-2 exponents: log2 e, or
+// log2 e / T for temperature T.  For row r the wave's largest logit M is the
+// reference (ref = M L), x[r] is overwritten with e = 2^(x L - ref) and the sums of
+// e, and for r < RY of e * (x L - ref) (the entropy moment), are taken over the
 // wave.  A wave holding only -inf gives the empty partial (ref = -inf, z = 0, e = 0);
 // a NaN gives z = NaN.  The entropy moment is
 // accumulated without guarding 0 * (-inf); if that produced a NaN it is summed again
 // from the e values alone (e log2 e over e > 0).
 template <int NE, int R, int RY>
-__device__ __forceinline__ void wave_pass1(float (&x)[R][NE], Lse (&out)[R]) {
+__device__ __forceinline__ void wave_pass1(float (&x)[R][NE], Lse (&out)[R], float L = kLog2e) {
   float M[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -487,14 +488,14 @@ __device__ __forceinline__ void wave_pass1(float (&x)[R][NE], Lse (&out)[R]) {
   float ref[R], z0[R], z1[R], y0[R], y1[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    ref[r] = M[r] > kNegInf ? M[r] * kLog2e : 0.f;   // 0 keeps -inf - ref = -inf
+    ref[r] = M[r] > kNegInf ? M[r] * L : 0.f;   // 0 keeps -inf - ref = -inf
     z0[r] = z1[r] = y0[r] = y1[r] = 0.f;
   }
 #pragma unroll
   for (int i = 0; i < NE; ++i) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const float t = __builtin_fmaf(x[r][i], kLog2e, -ref[r]);
+      const float t = __builtin_fmaf(x[r][i], L, -ref[r]);
       const float e = fast_exp2(t);
       if (i & 1) z1[r] += e; else z0[r] += e;
       if (r < RY) {
@@ -526,7 +527,7 @@ __device__ __forceinline__ void wave_pass1(float (&x)[R][NE], Lse (&out)[R]) {
     }
   }
 #pragma unroll
-  for (int r = 0; r < R; ++r) out[r] = Lse{M[r] * kLog2e, Z[r], Y[r]};   // ref -inf when empty
+  for (int r = 0; r < R; ++r) out[r] = Lse{M[r] * L, Z[r], Y[r]};   // ref -inf when empty
 }
 
 // Merge of per-lane partials of R rows into one per row, the same bits in every
@@ -741,6 +742,27 @@ __device__ __forceinline__ void row_uniforms(uint64_t seed, uint64_t offset, uin
   P4 o = philox4x32_10(in, (uint32_t)seed, (uint32_t)(seed >> 32));
   *u = (float)(o.x[0] >> 8) * 0x1p-24f;
   *u_prime = (float)(o.x[1] >> 8) * 0x1p-24f;
+}
+
+// Gumbel noise for four consecutive elements 4 v4 .. 4 v4 + 3 of a row, in base-2
+// key units: argmax_v (ln w_v + G_v), G = -ln(-ln U), equals argmax_v (log2 w_v +
+// g_v) with g = -log2(-ln U) (the keys differ by the factor 1/ln 2 and a constant).
+// U = (k + 1/2) 2^-24 with k = word >> 8 of Philox at counter (c, 1 + v4, 0), key =
+// seed.  -ln U is formed from whichever of U and 1 - U is exact in float32: log2 of
+// U = (2k + 1) 2^-25 below 1/2, log1p(-e) with e = 1 - U = (2^25 - 2k - 1) 2^-25 from
+// 1/2 up, so the largest noise values (U near 1, the likely winners) keep their
+// accuracy.
+__device__ __forceinline__ void gumbel4(uint64_t seed, uint64_t c, uint32_t v4, float (&g)[4]) {
+  const P4 in{{(uint32_t)c, (uint32_t)(c >> 32), v4 + 1u, 0u}};
+  const P4 o = philox4x32_10(in, (uint32_t)seed, (uint32_t)(seed >> 32));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t k = o.x[j] >> 8;
+    const float lo = -fast_log2((float)(2u * k + 1u) * 0x1p-25f) * kLn2;   // -ln U, U < 1/2
+    const float e = (float)((1u << 25) - 2u * k - 1u) * 0x1p-25f;                          // 1 - U, exact
+    const float hi = -log1pf(-e);                                                            // -ln U, U >= 1/2
+    g[j] = -fast_log2(k < (1u << 23) ? lo : hi);
+  }
 }
 
 }  // namespace mtp

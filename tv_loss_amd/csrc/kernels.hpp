@@ -39,20 +39,32 @@ struct VerifyArgs {
   int32_t* row_token; float* overlap; float* tv; float* entropy; int32_t* row_status;
   // target-only verify: greedy draft tokens [B, G], p at them, RS/TO boundary flags
   int32_t* draft_token; float* p_yhat; uint8_t* rs_better;
+  // Gumbel-max verify: 1 / temperature (1 otherwise)
+  float inv_temp;
   // workspace sections: error word, pass-1 records [group][chunk][3 or 4 words],
   // pass-2 sums [group][chunk][wave] = (residual or p mass, overlap) as two floats,
-  // target-only: p mass without the greedy token [group][chunk][wave]
-  uint32_t* err; uint64_t* part1; uint64_t* part2; float* part3;
+  // target-only: p mass without the greedy token [group][chunk][wave]; Gumbel-max:
+  // each wave's (largest key, index + 1) of the residual and of p [group][chunk][wave][2]
+  uint32_t* err; uint64_t* part1; uint64_t* part2; float* part3; uint64_t* gkeys;
   RowSplit sp;
   int ngroups;
   int sgroups, layers;   // super-groups (all co-resident), groups per super-group
 };
 
+// Verify modes: rejection sampling with inverse-CDF samples; target-only (greedy
+// draft tokens, no tokens input); rejection sampling at a temperature with
+// Gumbel-max samples.
+constexpr int kVerifyRejection = 0;
+constexpr int kVerifyTargetOnly = 1;
+constexpr int kVerifyGumbel = 2;
+
 int verify_vec_per_thread(int dt);
-// target_only selects target-only verification (greedy draft tokens, no tokens input)
-hipError_t launch_verify(const VerifyArgs& a, int dt, bool target_only, hipStream_t stream);
-hipError_t verify_occupancy(int dt, bool target_only, int* blocks_per_cu);
-int verify_record_words(bool target_only);
+hipError_t launch_verify(const VerifyArgs& a, int dt, int mode, hipStream_t stream);
+hipError_t verify_occupancy(int dt, int mode, int* blocks_per_cu);
+int verify_record_words(int mode);
+// Gumbel-max tokens of `rows` logit rows: argmax_v (x_v L + g_v), one workgroup per row.
+hipError_t launch_gumbel_sample(const void* logits, int64_t row_stride, int dt, int rows, int64_t V, float L,
+                                uint64_t seed, uint64_t offset, int32_t* tokens, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // End-to-end TV loss.  Head k of position t compares draft row

@@ -179,8 +179,9 @@ __device__ __forceinline__ uint32_t merge_argmax(__amdgpu_buffer_rsrc_t rs, int 
 }
 
 // ---------------------------------------------------------------------------
-template <int DT, int NV, bool TO>
+template <int DT, int NV, int MODE>
 __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(VerifyArgs a) {
+  constexpr bool TO = MODE == kVerifyTargetOnly, GM = MODE == kVerifyGumbel;
   constexpr int PV = Elem<DT>::kPerVec;
   constexpr int NE = NV * PV;
   constexpr int NQ = NE / 4;              // 16-byte LDS slots per row and thread
@@ -219,6 +220,7 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
   };
   constexpr int kSt = rec_bytes<TO>();
   auto rsrc_rec = [&](int g) { return rsrc_of(a.part1 + (int64_t)g * C * (kSt / 8)); };
+  const float L = GM ? kLog2e * a.inv_temp : kLog2e;   // logit -> base-2 exponent scale
 
   // vector indices fit in 32 bits (V <= 2^30)
   const int vpc = (int)a.sp.vec_per_chunk, nvec = (int)a.sp.nvec, nfull = (int)a.sp.nvec_full;
@@ -336,6 +338,50 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
         }
       }
       if (lane == 0) a.part2[((int64_t)g_m2 * C + c) * kWaves + wave] = pack2(rm, om);
+      if constexpr (GM) {
+        // Gumbel-max keys of this wave's segment in base-2 units, key = log2 w + g:
+        // w = the residual (pair rows) and w = p, g the element's Gumbel noise; the
+        // wave keeps the largest of each with its vocabulary index
+        float kr = kNegInf, kp = kNegInf;
+        uint32_t ir = 0xffffffffu, ip = 0xffffffffu;
+        if (la != kNegInf) {
+          const uint64_t crow = a.offset + (uint64_t)g_m2;
+          const float lb = href[1] - lse_sh[i & 1][1];
+          const bool p_units = !(lb - la > 64.f);
+          const float fq = p_units ? fast_exp2(lb - la) : 1.f, fp = p_units ? 1.f : fast_exp2(la - lb);
+          const float lr = p_units ? la : lb;   // log2 of the residual's unit
+          // one 16-byte slot at a time: the Philox rounds would otherwise hold the
+          // registers that the items in flight need
+#pragma unroll 1
+          for (int qi = 0; qi < NQ; ++qi) {
+            const float4 ea = held[0][qi][t];
+            const float va[4] = {ea.x, ea.y, ea.z, ea.w};
+            float vb[4] = {0.f, 0.f, 0.f, 0.f};
+            if (pair2) {
+              const float4 eb = held[1][qi][t];
+              vb[0] = eb.x; vb[1] = eb.y; vb[2] = eb.z; vb[3] = eb.w;
+            }
+            const uint32_t gi0 = (uint32_t)(v0 + (4 * qi / PV) * 64) * PV + (4 * qi) % PV;   // 4-aligned
+            float gm[4];
+            gumbel4(a.seed, crow, gi0 >> 2, gm);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              argmax_fold(kp, ip, la + fast_log2(va[e]) + gm[e], gi0 + e);
+              if (pair2) {
+                const float d = fmaxf(__builtin_fmaf(-fq, vb[e], fp * va[e]), 0.f);
+                argmax_fold(kr, ir, lr + fast_log2(d) + gm[e], gi0 + e);
+              }
+            }
+          }
+        }
+        wave_argmax(kp, ip);
+        if (pair2) wave_argmax(kr, ir);
+        if (lane == 0) {
+          uint64_t* gk = a.gkeys + (((int64_t)g_m2 * C + c) * kWaves + wave) * 2;
+          gk[0] = pack_argmax(kr, ir);
+          gk[1] = pack_argmax(kp, ip);
+        }
+      }
       if constexpr (TO) {
         if (pair2) {
           // target-only: this wave's p mass without the greedy draft token (the
@@ -420,9 +466,9 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
         wave_argmax(am, ai);
       }
       if (pair) {
-        wave_pass1<NE, 2, 1>(x, pt);
+        wave_pass1<NE, 2, 1>(x, pt, L);
       } else {
-        wave_pass1<NE, 1, 1>(*reinterpret_cast<float(*)[1][NE]>(&x[0]), *reinterpret_cast<Lse(*)[1]>(&pt[0]));
+        wave_pass1<NE, 1, 1>(*reinterpret_cast<float(*)[1][NE]>(&x[0]), *reinterpret_cast<Lse(*)[1]>(&pt[0]), L);
         pt[1] = lse_empty();
       }
       xref[0] = pt[0].ref;
@@ -580,8 +626,9 @@ __device__ __forceinline__ Scan wave_scan_owner(int n, float u_prime, MassFn mas
   return r;
 }
 
-template <int DT, int NV, bool TO>
+template <int DT, int NV, int MODE>
 __global__ void verify_finish(VerifyArgs a) {
+  constexpr bool TO = MODE == kVerifyTargetOnly, GM = MODE == kVerifyGumbel;
   constexpr int PV = Elem<DT>::kPerVec;
   constexpr int kSegVec = NV * 64;
   constexpr int KC = 2;   // chunks per lane whose pass-2 words are kept in registers
@@ -596,6 +643,7 @@ __global__ void verify_finish(VerifyArgs a) {
   const char* trow = reinterpret_cast<const char*>(a.target) + (int64_t)g * a.t_stride * Elem<DT>::kBytes;
   const char* drow = reinterpret_cast<const char*>(a.draft) + (int64_t)(b * G + (pair ? k : 0)) * a.d_stride * Elem<DT>::kBytes;
   constexpr int kSt = rec_bytes<TO>();
+  const float L = GM ? kLog2e * a.inv_temp : kLog2e;   // logit -> base-2 exponent scale
   const __amdgpu_buffer_rsrc_t rs = rsrc_of(a.part1 + (int64_t)g * C * (kSt / 8));
   uint64_t* p2 = a.part2 + (int64_t)g * C * kWaves;
   // target-only pair rows sample p without the greedy token: its per-wave masses
@@ -672,7 +720,7 @@ __global__ void verify_finish(VerifyArgs a) {
   bool empty_res = false;
   Scan sc{0.f, 0, 0.f};
   float oseg[kWaves] = {0.f, 0.f, 0.f, 0.f};   // segment masses of the owner chunk
-  if (!bad) {
+  if (!bad && !GM) {
     // block sums in lane order, prefix over lanes, then the owner lane walks its block
     float blk = 0.f;
     int last_pos = -1;
@@ -728,25 +776,47 @@ __global__ void verify_finish(VerifyArgs a) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) oseg[w] = seg_mass(sc.owner, w);
     }
-    if (pair) {
-      float ot[2] = {om_sum, tv_sum};
-      wave_reduce<false, 2>(ot);
-      alpha = ot[0];
-      tv_sum = ot[1];
-      if (!(sc.total > 0.f)) {   // the residual has no mass: sample from p
-        empty_res = true;
-        sc = wave_scan_owner(C, up, pmass);
-      }
+  }
+  if (!bad && pair) {
+    float ot[2] = {om_sum, tv_sum};
+    wave_reduce<false, 2>(ot);
+    alpha = ot[0];
+    tv_sum = ot[1];
+    if (GM ? !(tv_sum > 0.f) : !(sc.total > 0.f)) {   // the residual has no mass: sample from p
+      empty_res = true;
+      if (!GM) sc = wave_scan_owner(C, up, pmass);
     }
   }
   // TV: the residual mass (the scan's total for rejection sampling)
-  const float r_tot = TO ? tv_sum : pair && !empty_res ? sc.total : 0.f;
+  const float r_tot = TO || GM ? tv_sum : pair && !empty_res ? sc.total : 0.f;
   const bool use_q = !TO && pair && !empty_res;
   const bool drop_y = to_pair && !empty_res && y_ok;   // target-only residual: p without y
 
   // ---- owner segment inside the owner chunk, then the inverse CDF in it ------
   int token = -1;
-  if (!bad) {
+  if (GM && !bad) {
+    // Gumbel-max: the largest key over the row's waves, of the residual unless it is
+    // empty (or no residual key is finite), else of p (a bonus row's keys are p's)
+    const uint64_t* gk = a.gkeys + (int64_t)g * C * kWaves * 2;
+    float m = kNegInf;
+    uint32_t idx = 0xffffffffu;
+    auto best = [&](int slot) {
+      m = kNegInf;
+      idx = 0xffffffffu;
+      for (int i = lane; i < C * kWaves; i += 64) {
+        const uint64_t w = gk[i * 2 + slot];
+        argmax_fold(m, idx, unpack_lo(w), argmax_index(w));
+      }
+      wave_argmax(m, idx);
+    };
+    if (pair && !empty_res) {
+      best(0);
+      empty_res = !(m > kNegInf);
+    }
+    if (!pair || empty_res) best(1);
+    token = m > kNegInf && idx < (uint32_t)a.V ? (int)idx : -1;
+  }
+  if (!bad && !GM) {
     const int oc = sc.owner;
     const int vpc = (int)a.sp.vec_per_chunk, nvec = (int)a.sp.nvec, nfull = (int)a.sp.nvec_full;
     const int obeg = oc * vpc;
@@ -764,9 +834,9 @@ __global__ void verify_finish(VerifyArgs a) {
       for (int j = 0; j < NV; ++j)
 #pragma unroll
         for (int e = 0; e < PV; ++e) {
-          const float p = fast_exp2(__builtin_fmaf(x[0][j * PV + e], kLog2e, -lse2_p));
+          const float p = fast_exp2(__builtin_fmaf(x[0][j * PV + e], L, -lse2_p));
           if (use_q) {
-            const float q = fast_exp2(__builtin_fmaf(x[1][j * PV + e], kLog2e, -lse2_q));
+            const float q = fast_exp2(__builtin_fmaf(x[1][j * PV + e], L, -lse2_q));
             v[j][e] = fmaxf(p - q, 0.f);
           } else {
             v[j][e] = drop_y && (s0 + lane + j * 64) * PV + e == y ? 0.f : p;
@@ -818,6 +888,8 @@ __global__ void verify_finish(VerifyArgs a) {
   for (int i = lane; i < C * kWaves; i += 64) p2[i] = 0ull;
   if (to_pair)
     for (int i = lane; i < C * kWaves; i += 64) p3[i] = 0.f;
+  if (GM)
+    for (int i = lane; i < C * kWaves * 2; i += 64) a.gkeys[(int64_t)g * C * kWaves * 2 + i] = 0ull;
 
   if (lane == 0) {
     int status = 0;
@@ -830,7 +902,7 @@ __global__ void verify_finish(VerifyArgs a) {
       if (TO) {
         // target-only: accept the greedy token with probability p(y); the RS/TO
         // boundary TV < 1 - p(y)
-        const float py = y_ok && !bad ? fast_exp2(__builtin_fmaf(ay, kLog2e, -lse2_p)) : nan;
+        const float py = y_ok && !bad ? fast_exp2(__builtin_fmaf(ay, L, -lse2_p)) : nan;
         if (y_ok && !bad) flag = u < py ? 1 : 0;
         a.draft_token[b * G + k] = y_ok && !bad ? y : -1;
         if (a.p_yhat) a.p_yhat[b * G + k] = py;
@@ -838,7 +910,7 @@ __global__ void verify_finish(VerifyArgs a) {
       } else if (!y_ok) {
         status |= kRowBadToken;
       } else if (!bad) {
-        const float d = __builtin_fmaf(ay, kLog2e, -lse2_p) - __builtin_fmaf(by, kLog2e, -lse2_q);
+        const float d = __builtin_fmaf(ay, L, -lse2_p) - __builtin_fmaf(by, L, -lse2_q);
         if (d == d) flag = u < fminf(1.f, fast_exp2(d)) ? 1 : 0;
       }
       a.accept[b * G + k] = (uint8_t)flag;
@@ -861,37 +933,118 @@ __global__ void verify_finish(VerifyArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-template <int DT, int NV, bool TO>
+// Gumbel-max tokens of logit rows (draft sampling at a temperature): row r emits
+// argmax_v (x_v L + g_v) with g the element's Gumbel noise (counter offset + r), the
+// smallest index among equal keys, -1 if no key is finite.  One workgroup per row;
+// thread t walks the 16-byte vectors t, t + 256, ...; four elements share a Philox
+// call.
+template <int DT>
+__global__ __launch_bounds__(kBlock) void gumbel_sample(const char* logits, int64_t row_bytes, int64_t V, float L,
+                                                        uint64_t seed, uint64_t offset, int32_t* tokens) {
+  constexpr int PV = Elem<DT>::kPerVec;
+  const int r = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const char* row = logits + (int64_t)r * row_bytes;
+  const int64_t nvec = (V + PV - 1) / PV;
+  const uint64_t crow = offset + (uint64_t)r;
+  float km = kNegInf;
+  uint32_t ki = 0xffffffffu;
+  for (int64_t v = threadIdx.x; v < nvec; v += kBlock) {
+    float x[PV];
+    if ((v + 1) * PV <= V) {
+      const u32x4 w = reinterpret_cast<const u32x4*>(row)[v];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        if constexpr (DT == kBF16) {
+          x[2 * h] = bf16_lo(w[h]);
+          x[2 * h + 1] = bf16_hi(w[h]);
+        } else {
+          x[h] = __uint_as_float(w[h]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < PV; ++e) x[e] = v * PV + e < V ? load_one<DT>(row, v * PV + e) : kNegInf;
+    }
+#pragma unroll
+    for (int h = 0; h < PV / 4; ++h) {
+      float gm[4];
+      gumbel4(seed, crow, (uint32_t)(v * PV / 4 + h), gm);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        argmax_fold(km, ki, __builtin_fmaf(x[4 * h + e], L, gm[e]), (uint32_t)(v * PV + 4 * h + e));
+    }
+  }
+  wave_argmax(km, ki);
+  __shared__ float m_sh[kWaves];
+  __shared__ uint32_t i_sh[kWaves];
+  if (lane == 0) {
+    m_sh[wave] = km;
+    i_sh[wave] = ki;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = m_sh[0];
+    uint32_t idx = i_sh[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) argmax_fold(m, idx, m_sh[w], i_sh[w]);
+    tokens[r] = m > kNegInf && idx < (uint32_t)V ? (int32_t)idx : -1;
+  }
+}
+
+hipError_t launch_gumbel_sample(const void* logits, int64_t row_stride, int dt, int rows, int64_t V, float L,
+                                uint64_t seed, uint64_t offset, int32_t* tokens, hipStream_t stream) {
+  const char* base = reinterpret_cast<const char*>(logits);
+  if (dt == kBF16)
+    hipLaunchKernelGGL(gumbel_sample<kBF16>, dim3((unsigned)rows), dim3(kBlock), 0, stream, base, row_stride * 2, V, L,
+                       seed, offset, tokens);
+  else
+    hipLaunchKernelGGL(gumbel_sample<kF32>, dim3((unsigned)rows), dim3(kBlock), 0, stream, base, row_stride * 4, V, L,
+                       seed, offset, tokens);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+template <int DT, int NV, int MODE>
 static hipError_t launch(const VerifyArgs& a, hipStream_t stream) {
   const int64_t grid = (int64_t)a.sgroups * a.sp.nchunks;
-  hipLaunchKernelGGL((verify_main<DT, NV, TO>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
+  hipLaunchKernelGGL((verify_main<DT, NV, MODE>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((verify_finish<DT, NV, TO>), dim3((unsigned)a.B), dim3(64 * (a.G + 1)), 0, stream, a);
+  hipLaunchKernelGGL((verify_finish<DT, NV, MODE>), dim3((unsigned)a.B), dim3(64 * (a.G + 1)), 0, stream, a);
   return hipGetLastError();
 }
 
 int verify_vec_per_thread(int dt) { return dt == kBF16 ? kVerifyNVBf16 : kVerifyNVF32; }
 
-int verify_record_words(bool target_only) { return (target_only ? rec_bytes<true>() : rec_bytes<false>()) / 8; }
+int verify_record_words(int mode) { return (mode == kVerifyTargetOnly ? rec_bytes<true>() : rec_bytes<false>()) / 8; }
 
-hipError_t launch_verify(const VerifyArgs& a, int dt, bool target_only, hipStream_t stream) {
-  if (dt == kBF16)
-    return target_only ? launch<kBF16, kVerifyNVBf16, true>(a, stream) : launch<kBF16, kVerifyNVBf16, false>(a, stream);
-  return target_only ? launch<kF32, kVerifyNVF32, true>(a, stream) : launch<kF32, kVerifyNVF32, false>(a, stream);
+template <int MODE>
+static hipError_t launch_mode(const VerifyArgs& a, int dt, hipStream_t stream) {
+  return dt == kBF16 ? launch<kBF16, kVerifyNVBf16, MODE>(a, stream) : launch<kF32, kVerifyNVF32, MODE>(a, stream);
 }
 
-template <int DT, int NV, bool TO>
-static hipError_t occupancy(int* n) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, verify_main<DT, NV, TO>, kBlock, 0);
+hipError_t launch_verify(const VerifyArgs& a, int dt, int mode, hipStream_t stream) {
+  switch (mode) {
+    case kVerifyTargetOnly: return launch_mode<kVerifyTargetOnly>(a, dt, stream);
+    case kVerifyGumbel: return launch_mode<kVerifyGumbel>(a, dt, stream);
+    default: return launch_mode<kVerifyRejection>(a, dt, stream);
+  }
 }
 
-hipError_t verify_occupancy(int dt, bool target_only, int* blocks_per_cu) {
-  if (dt == kBF16)
-    return target_only ? occupancy<kBF16, kVerifyNVBf16, true>(blocks_per_cu)
-                       : occupancy<kBF16, kVerifyNVBf16, false>(blocks_per_cu);
-  return target_only ? occupancy<kF32, kVerifyNVF32, true>(blocks_per_cu)
-                     : occupancy<kF32, kVerifyNVF32, false>(blocks_per_cu);
+template <int MODE>
+static hipError_t occupancy_mode(int dt, int* n) {
+  return dt == kBF16
+             ? hipOccupancyMaxActiveBlocksPerMultiprocessor(n, verify_main<kBF16, kVerifyNVBf16, MODE>, kBlock, 0)
+             : hipOccupancyMaxActiveBlocksPerMultiprocessor(n, verify_main<kF32, kVerifyNVF32, MODE>, kBlock, 0);
+}
+
+hipError_t verify_occupancy(int dt, int mode, int* blocks_per_cu) {
+  switch (mode) {
+    case kVerifyTargetOnly: return occupancy_mode<kVerifyTargetOnly>(dt, blocks_per_cu);
+    case kVerifyGumbel: return occupancy_mode<kVerifyGumbel>(dt, blocks_per_cu);
+    default: return occupancy_mode<kVerifyRejection>(dt, blocks_per_cu);
+  }
 }
 
 }  // namespace mtp

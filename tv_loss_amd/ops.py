@@ -252,6 +252,87 @@ def workspace_error(ws):
 
 
 
+def _check_temperature(temperature):
+    t = float(temperature)
+    if not (t > 0.0) or t == float("inf"):
+        raise ValueError(f"temperature must be positive and finite, got {temperature}")
+    return t
+
+
+def verify_gumbel(target, draft, draft_tokens, temperature, seed, offset=0, *, stats=True):
+    """Rejection-sampling verification at a temperature with Gumbel-max row samples
+    (see mtp_verify_gumbel in include/mtp.h).  Inputs and outputs as for verify();
+    p and q are the softmax of the logits divided by `temperature`."""
+    lib = load()
+    _require_cuda(target, draft, draft_tokens)
+    B, G1, V = _verify_shape(target, draft)
+    G = G1 - 1
+    if draft_tokens.dtype != torch.int32 or tuple(draft_tokens.shape) != (B, G):
+        raise ValueError("draft_tokens must be int32 [B, gamma]")
+    T = _check_temperature(temperature)
+    draft_tokens = draft_tokens.contiguous()
+    dev = target.device
+    dt = _dtype_code(target)
+    out = {
+        "accept": torch.empty((B, G), dtype=torch.uint8, device=dev),
+        "accepted_len": torch.empty(B, dtype=torch.int32, device=dev),
+        "next_token": torch.empty(B, dtype=torch.int32, device=dev),
+    }
+    if stats:
+        out.update(row_token=torch.empty((B, G1), dtype=torch.int32, device=dev),
+                   row_status=torch.empty((B, G1), dtype=torch.int32, device=dev),
+                   overlap=torch.empty((B, G), dtype=torch.float32, device=dev),
+                   tv=torch.empty((B, G), dtype=torch.float32, device=dev),
+                   entropy=torch.empty((B, G1), dtype=torch.float32, device=dev))
+    if B == 0:
+        return out
+    nbytes = ctypes.c_size_t()
+    check(lib.mtp_verify_gumbel_workspace_size(B, G, V, dt, ctypes.byref(nbytes)))
+    ws = workspace(dev, nbytes.value)
+    with torch.cuda.device(dev):
+        check(lib.mtp_verify_gumbel(
+            _ptr(target), target.stride(1), _ptr(draft), draft.stride(1), dt, B, G, V,
+            _ptr(draft_tokens), ctypes.c_float(T), ctypes.c_uint64(seed), ctypes.c_uint64(offset),
+            _ptr(out["accept"]), _ptr(out["accepted_len"]), _ptr(out["next_token"]),
+            _ptr(out.get("row_token")), _ptr(out.get("overlap")), _ptr(out.get("tv")),
+            _ptr(out.get("entropy")), _ptr(out.get("row_status")),
+            _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+def gumbel_sample(logits, temperature, seed, offset=0):
+    """Gumbel-max samples of softmax(logits / temperature) over the last dimension
+    (see mtp_gumbel_sample in include/mtp.h): row r of the flattened leading
+    dimensions uses Philox counter offset + r.  logits: float32 or bfloat16 [..., V]
+    with unit stride along V and a uniform row stride.  Returns int32 [...]."""
+    lib = load()
+    _require_cuda(logits)
+    if logits.dim() < 1:
+        raise ValueError("logits must have a vocabulary dimension")
+    V = logits.shape[-1]
+    lead = tuple(logits.shape[:-1])
+    flat = logits.reshape(-1, V)
+    if flat.stride(-1) != 1:
+        flat = flat.contiguous()
+    rows = flat.shape[0]
+    T = _check_temperature(temperature)
+    dt = _dtype_code(logits)
+    tokens = torch.empty(rows, dtype=torch.int32, device=logits.device)
+    if rows:
+        pv = 16 // flat.element_size()
+        vp = -(-V // pv) * pv                     # V rounded up to whole 16-byte vectors
+        stride = flat.stride(0) if rows > 1 else vp
+        if (stride * flat.element_size()) % 16 or flat.data_ptr() % 16:
+            # rows must start 16-byte aligned: copy into a padded buffer
+            padded = torch.empty((rows, vp), dtype=flat.dtype, device=flat.device)
+            padded[:, :V] = flat
+            flat, stride = padded, vp
+        with torch.cuda.device(logits.device):
+            check(lib.mtp_gumbel_sample(_ptr(flat), stride, dt, rows, V, ctypes.c_float(T),
+                                        ctypes.c_uint64(seed), ctypes.c_uint64(offset), _ptr(tokens),
+                                        _stream(logits.device)))
+    return tokens.reshape(lead)
+
 
 class VerifyPlan:
     """A verify call bound once to fixed input and output tensors, so that repeated
@@ -259,7 +340,7 @@ class VerifyPlan:
     offset)` enqueues mtp_verify on the current stream and returns the outputs
     dict, whose tensors are overwritten by every run."""
 
-    def __init__(self, target, draft, draft_tokens=None, target_only=False):
+    def __init__(self, target, draft, draft_tokens=None, target_only=False, temperature=None):
         self.lib = load()
         B, G1, V = target.shape
         self.shape = (B, G1 - 1, V)
@@ -274,6 +355,16 @@ class VerifyPlan:
             mid = (_ptr(o["accept"]), _ptr(o["accepted_len"]), _ptr(o["next_token"]), _ptr(o["draft_token"]),
                    _ptr(o["p_yhat"]), _ptr(o["rs_better"]))
             self._fn = self.lib.mtp_verify_target_only
+        elif temperature is not None:                                 # Gumbel-max row samples
+            draft_tokens = draft_tokens.contiguous()
+            self.inputs = (target, draft, draft_tokens)
+            self.out = verify_gumbel(target, draft, draft_tokens, temperature, 0, 0)
+            check(self.lib.mtp_verify_gumbel_workspace_size(B, G1 - 1, V, dt, ctypes.byref(nbytes)))
+            self._head = (_ptr(target), target.stride(1), _ptr(draft), draft.stride(1), dt, B, G1 - 1, V,
+                          _ptr(draft_tokens), ctypes.c_float(_check_temperature(temperature)))
+            o = self.out
+            mid = (_ptr(o["accept"]), _ptr(o["accepted_len"]), _ptr(o["next_token"]))
+            self._fn = self.lib.mtp_verify_gumbel
         else:
             draft_tokens = draft_tokens.contiguous()
             self.inputs = (target, draft, draft_tokens)
