@@ -13,7 +13,9 @@ positions x 3 heads, V = 151936 (bf16 in, bf16 gradient out), as algorithmic GB/
 against the 8 TB/s HBM peak; (`long_tail`) verify on 512 x 4 positions at V = 2^18
 with Zipf-like logits; (`entropy_sweep`) verify on the 15 temperature x noise cells
 (128 sequences each), with each cell's acceptance rate, mean accepted length and
-mean target entropy; (`target_only`) target-only verify of the rollout workload.
+mean target entropy; (`target_only`) target-only verify of the rollout workload;
+(`gumbel`) verify at temperature 0.7 with Gumbel-max row samples, and the
+Gumbel-max draft sampler on the rollout's draft rows.
 
 `roofline` uses per-launch HIP events recorded on the stream the kernels run on;
 `cpu_baseline` times the float64 oracle on a bounded sample of the same workload.
@@ -79,14 +81,17 @@ def check_waits(mtp, ws):
         sys.exit(f"bench: a cluster wait timed out (workspace error word {word:#x})")
 
 
-def time_verify(mtp, torch, w, steps, warmup, nsets, target_only=False):
+def time_verify(mtp, torch, w, steps, warmup, nsets, target_only=False, temperature=None):
     import synthetic
     dev = "cuda:0"
     B, G, V = w["B"], w["G"], w["V"]
     plans = []
     for i in range(nsets):
         t, d, y = synthetic.verify_inputs(w, dev, seed=w["seed"] + i)
-        plans.append(mtp.VerifyPlan(t, d, None, target_only=True) if target_only else mtp.VerifyPlan(t, d, y))
+        if target_only:
+            plans.append(mtp.VerifyPlan(t, d, None, target_only=True))
+        else:
+            plans.append(mtp.VerifyPlan(t, d, y, temperature=temperature))
     torch.cuda.synchronize()
     rows = B * (G + 1)
     plans[0].run(seed=w["seed"], offset=0)
@@ -274,6 +279,40 @@ def main():
         }
         log(f"verify target-only: {omean * 1e3:.2f} us per call, accept rate {to_acc:.3f}, "
             f"RS better on {rs_share:.3f} of positions")
+        # rejection sampling at temperature 0.7 with Gumbel-max row samples, and the
+        # Gumbel-max draft sampler on the rollout's draft rows
+        log("verify: Gumbel-max at T=0.7 on the rollout workload")
+        gwall, gkms, plans = time_verify(mtp, torch, w, args.steps, args.warmup, nsets, temperature=0.7)
+        out = plans[0].run(seed=w["seed"], offset=0)
+        g_acc = out["accept"].float().mean().item()
+        drafts = [p.inputs[1] for p in plans]
+        del out
+        gmean = sum(gkms) / len(gkms)
+        sevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(args.steps)]
+        for i in range(args.warmup):
+            mtp.gumbel_sample(drafts[i % nsets], 0.7, seed=1, offset=i * B * G)
+        for i in range(args.steps):
+            sevs[i][0].record()
+            mtp.gumbel_sample(drafts[i % nsets], 0.7, seed=1, offset=i * B * G)
+            sevs[i][1].record()
+        torch.cuda.synchronize()
+        smean = sum(a.elapsed_time(b) for a, b in sevs) / args.steps
+        sbytes = B * G * V * 2 + B * G * 4
+        del plans, drafts
+        result["gumbel"] = {
+            "workload": "rejection-sampling verify of the rollout workload at temperature 0.7 (p, q tempered), "
+                        "row tokens by the Gumbel-max trick with per-element Philox noise; draft sampler on "
+                        "its 192 draft rows",
+            "value": positions / gwall, "unit": "draft positions/s", "kernel_us_mean": gmean * 1e3,
+            "accept_rate": g_acc,
+            "roofline": {"bound": "hbm", "achieved": alg_bytes / (gmean * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": alg_bytes / (gmean * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "bytes_per_launch": alg_bytes},
+            "sampler_us_mean": smean * 1e3, "sampler_gbs": sbytes / (smean * 1e-3) / 1e9,
+        }
+        log(f"verify Gumbel-max: {gmean * 1e3:.2f} us per call, accept rate {g_acc:.3f}; sampler "
+            f"{smean * 1e3:.2f} us per call ({sbytes / smean / 1e6:.0f} GB/s)")
         # the long-tail workload (Zipf-like logits, V = 2^18, gamma = 4) and the 15
         # cells of the entropy sweep, each timed like the rollout workload
         lw = synthetic.VERIFY_WORKLOADS["long_tail"]

@@ -173,13 +173,20 @@ mtp_status mtp_verify_gumbel(const void* target, int64_t target_row_stride,
  *   tokens[r] = argmax_v (x_v / T + g_v)   (a sample of softmax(x / T)),
  * g_v as for mtp_verify_gumbel with c = offset + r; the smallest index among
  * equal keys, -1 for a row with no finite key (all -inf or NaN logits).  tokens:
- * device int32 [rows].  No workspace; rows == 0 is a no-op.  Sampling draft rows
- * (b, k) in row-major order with offset o and verifying with an offset whose
- * counters do not overlap [o, o + batch * gamma) keeps the two noises independent.
+ * device int32 [rows].  workspace: device, 256-byte aligned, at least
+ * mtp_gumbel_sample_workspace_size bytes (per-chunk partial maxima), left zeroed
+ * on return like the verify workspaces, so one zeroed buffer serves both.
+ * rows == 0 is a no-op.
+ * Sampling draft rows (b, k) in row-major order with offset o and verifying with
+ * an offset whose counters do not overlap [o, o + batch * gamma) keeps the two
+ * noises independent.  rows * ceil(vocab / 8192) (bfloat16; / 4096 for float32)
+ * must stay below 2^24.
  */
+mtp_status mtp_gumbel_sample_workspace_size(int32_t rows, int32_t vocab, mtp_dtype dtype, size_t* bytes);
+
 mtp_status mtp_gumbel_sample(const void* logits, int64_t row_stride, mtp_dtype dtype, int32_t rows,
                              int32_t vocab, float temperature, uint64_t seed, uint64_t offset,
-                             int32_t* tokens, void* stream);
+                             int32_t* tokens, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* End-to-end TV loss, forward (paperlayer Sec. 4 "End-to-end TV loss", App. F;

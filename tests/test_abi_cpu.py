@@ -119,10 +119,10 @@ def test_verify_gumbel_rejects_bad_arguments(kw, code):
 
 
 def _sample(lib, **kw):
-    a = dict(x=A16, rs=151936, dt=1, rows=64, V=151936, T=1.0, seed=0, off=0, tok=A16)
+    a = dict(x=A16, rs=151936, dt=1, rows=64, V=151936, T=1.0, seed=0, off=0, tok=A16, ws=A16, wsb=1 << 30)
     a.update(kw)
     return lib.mtp_gumbel_sample(a["x"], a["rs"], a["dt"], a["rows"], a["V"], a["T"], a["seed"], a["off"],
-                                 a["tok"], None)
+                                 a["tok"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -130,6 +130,8 @@ def _sample(lib, **kw):
     (dict(rows=-1), 2), (dict(V=0), 2), (dict(V=(1 << 30) + 1), 2), (dict(rs=151935), 2),
     (dict(T=0.0), 2), (dict(T=float("nan")), 2), (dict(T=float("-inf")), 2),
     (dict(dt=9), 3), (dict(x=MIS), 4), (dict(rs=151937, V=151937), 4),
+    (dict(rows=1 << 20, rs=1 << 20, V=1 << 20), 2),             # 2^20 rows x 128 chunks: too many
+    (dict(ws=None), 5), (dict(wsb=64 * 19 * 8 - 8), 5), (dict(ws=P(0x10080)), 5),
 ])
 def test_gumbel_sample_rejects_bad_arguments(kw, code):
     lib = tv_loss_amd.load()
@@ -138,7 +140,13 @@ def test_gumbel_sample_rejects_bad_arguments(kw, code):
 
 def test_gumbel_entries_empty_inputs_and_workspace():
     lib = tv_loss_amd.load()
-    assert _sample(lib, rows=0, x=None, tok=None) == 0
+    assert _sample(lib, rows=0, x=None, tok=None, ws=None, wsb=0) == 0
+    n = ctypes.c_size_t()
+    assert lib.mtp_gumbel_sample_workspace_size(64, 151936, 1, ctypes.byref(n)) == 0
+    assert n.value == -(-64 * 19 * 8 // 256) * 256                  # 19 chunks of 8192 bf16 per row
+    assert lib.mtp_gumbel_sample_workspace_size(64, 151936, 0, ctypes.byref(n)) == 0 and n.value >= 64 * 38 * 8
+    assert lib.mtp_gumbel_sample_workspace_size(0, 151936, 1, ctypes.byref(n)) == 0 and n.value == 0
+    assert lib.mtp_gumbel_sample_workspace_size(-1, 151936, 1, ctypes.byref(n)) == 2
     assert _verify_gumbel(lib, B=0, target=None, draft=None, tok=None, ws=None, wsb=0) == 0
     n_rs, n_gm = ctypes.c_size_t(), ctypes.c_size_t()
     assert lib.mtp_verify_workspace_size(64, 3, 151936, 1, ctypes.byref(n_rs)) == 0

@@ -272,3 +272,30 @@ def test_chi_square_sampler_and_first_token():
     n = 2000
     _compare_sampler(y[:n], d[:n], T, 99, 1 << 33)
     compare_verify({k: v[:n] for k, v in out.items()}, _oracle(t[:n], d[:n], y[:n], T, 2026, 0), torch.float32)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_sampler_equal_logits_pick_the_largest_noise(dtype):
+    """Equal logits: the token is the element with the largest Gumbel noise (U
+    nearest 1), where the exponential variate is smallest; checks the noise's
+    accuracy in its upper tail against the float64 oracle."""
+    rows, V = 24, 262144
+    x = torch.full((rows, V), 0.25, dtype=dtype, device=DEV)
+    toks = mtp.gumbel_sample(x, 1.0, seed=1234, offset=55)
+    torch.cuda.synchronize()
+    assert _compare_sampler(toks, x, 1.0, 1234, 55) <= 2
+
+
+def test_sampler_leaves_the_shared_workspace_zeroed():
+    """The sampler's partial maxima are cleared by its second kernel, so a verify
+    call on the same (shared) workspace right after it sees a clean one."""
+    w = synthetic.VERIFY_WORKLOADS["rollout"]
+    t, d, y = synthetic.verify_inputs(w, DEV, B=6, V=50000)
+    toks = mtp.gumbel_sample(d, 0.9, seed=8, offset=1 << 36)
+    torch.cuda.synchronize()
+    ws = mtp.workspace(DEV, 1)
+    assert int(torch.count_nonzero(ws)) == 0
+    out = _run(t, d, toks, 0.9, seed=8, offset=0)
+    assert mtp.workspace_error(ws) == 0 and int(torch.count_nonzero(ws)) == 0
+    _compare_sampler(toks, d, 0.9, 8, 1 << 36)
+    compare_verify(out, _oracle(t, d, toks, 0.9, 8, 0), torch.bfloat16)

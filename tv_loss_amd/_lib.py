@@ -36,8 +36,10 @@ SIGNATURES = {
     "mtp_verify_gumbel": (_c.c_int, [_P, _c.c_int64, _P, _c.c_int64, _c.c_int, _c.c_int32, _c.c_int32,
                                      _c.c_int32, _P, _c.c_float, _c.c_uint64, _c.c_uint64, _P, _P, _P, _P, _P,
                                      _P, _P, _P, _P, _c.c_size_t, _P]),
+    "mtp_gumbel_sample_workspace_size": (_c.c_int, [_c.c_int32, _c.c_int32, _c.c_int,
+                                                    _c.POINTER(_c.c_size_t)]),
     "mtp_gumbel_sample": (_c.c_int, [_P, _c.c_int64, _c.c_int, _c.c_int32, _c.c_int32, _c.c_float, _c.c_uint64,
-                                     _c.c_uint64, _P, _P]),
+                                     _c.c_uint64, _P, _P, _c.c_size_t, _P]),
     "mtp_tv_loss_workspace_size": (_c.c_int, [_c.c_int32, _c.c_int32, _c.c_int32, _c.c_int, _c.c_int32,
                                               _c.POINTER(_c.c_size_t)]),
     "mtp_tv_loss_fwd": (_c.c_int, [_P, _c.c_int64, _c.c_int64, _P, _c.c_int64, _c.c_int64, _c.c_int,

@@ -312,8 +312,18 @@ mtp_status mtp_verify_gumbel(const void* target, int64_t target_row_stride, cons
                      stream);
 }
 
+mtp_status mtp_gumbel_sample_workspace_size(int32_t rows, int32_t vocab, mtp_dtype dtype, size_t* bytes) {
+  if (!bytes) return fail(MTP_ERR_NULL, "bytes is NULL");
+  if (dtype != MTP_F32 && dtype != MTP_BF16) return fail(MTP_ERR_DTYPE, "unknown dtype code %d", (int)dtype);
+  if (rows < 0) return fail(MTP_ERR_SHAPE, "rows = %d is negative", rows);
+  if (vocab < 1 || vocab > kMaxVocab) return fail(MTP_ERR_SHAPE, "vocab = %d outside [1, 2^30]", vocab);
+  *bytes = rows == 0 ? 0 : align256((size_t)rows * mtp::gumbel_sample_chunks_per_row(dtype, vocab) * 8);
+  return ok();
+}
+
 mtp_status mtp_gumbel_sample(const void* logits, int64_t row_stride, mtp_dtype dtype, int32_t rows, int32_t vocab,
-                             float temperature, uint64_t seed, uint64_t offset, int32_t* tokens, void* stream) {
+                             float temperature, uint64_t seed, uint64_t offset, int32_t* tokens, void* workspace,
+                             size_t workspace_bytes, void* stream) {
   if (dtype != MTP_F32 && dtype != MTP_BF16) return fail(MTP_ERR_DTYPE, "unknown dtype code %d", (int)dtype);
   if (rows < 0) return fail(MTP_ERR_SHAPE, "rows = %d is negative", rows);
   if (vocab < 1 || vocab > kMaxVocab) return fail(MTP_ERR_SHAPE, "vocab = %d outside [1, 2^30]", vocab);
@@ -325,8 +335,13 @@ mtp_status mtp_gumbel_sample(const void* logits, int64_t row_stride, mtp_dtype d
     return fail(MTP_ERR_SHAPE, "row stride %lld must be >= vocab (%d)", (long long)row_stride, vocab);
   mtp_status s = check_row_base(logits, row_stride, dtype, "logits");
   if (s) return s;
-  hipError_t e = mtp::launch_gumbel_sample(logits, row_stride, dtype, rows, vocab, kLog2e / temperature,
-                                           seed, offset, tokens, (hipStream_t)stream);
+  const int64_t nch = mtp::gumbel_sample_chunks_per_row(dtype, vocab);
+  if ((int64_t)rows * nch * mtp::kBlock > 0xffffffffLL)
+    return fail(MTP_ERR_SHAPE, "rows * vocab is too large for one launch");
+  if ((s = check_workspace(workspace, workspace_bytes, align256((size_t)rows * nch * 8)))) return s;
+  hipError_t e = mtp::launch_gumbel_sample(logits, row_stride, dtype, rows, vocab, kLog2e / temperature, seed,
+                                           offset, tokens, reinterpret_cast<uint64_t*>(workspace),
+                                           (hipStream_t)stream);
   if (e != hipSuccess) return fail(MTP_ERR_LAUNCH, "Gumbel sample launch failed: %s", hipGetErrorString(e));
   return ok();
 }

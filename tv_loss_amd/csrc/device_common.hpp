@@ -721,13 +721,13 @@ __device__ __forceinline__ P4 philox4x32_10(P4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     if (r) { k0 += W0; k1 += W1; }
-    const uint32_t lo0 = M0 * c.x[0], hi0 = __umulhi(M0, c.x[0]);
-    const uint32_t lo1 = M1 * c.x[2], hi1 = __umulhi(M1, c.x[2]);
+    // each 32 x 32 -> 64-bit product is one v_mad_u64_u32
+    const uint64_t p0 = (uint64_t)M0 * c.x[0], p1 = (uint64_t)M1 * c.x[2];
     P4 n;
-    n.x[0] = hi1 ^ c.x[1] ^ k0;
-    n.x[1] = lo1;
-    n.x[2] = hi0 ^ c.x[3] ^ k1;
-    n.x[3] = lo0;
+    n.x[0] = (uint32_t)(p1 >> 32) ^ c.x[1] ^ k0;
+    n.x[1] = (uint32_t)p1;
+    n.x[2] = (uint32_t)(p0 >> 32) ^ c.x[3] ^ k1;
+    n.x[3] = (uint32_t)p0;
     c = n;
   }
   return c;
@@ -744,25 +744,33 @@ __device__ __forceinline__ void row_uniforms(uint64_t seed, uint64_t offset, uin
   *u_prime = (float)(o.x[1] >> 8) * 0x1p-24f;
 }
 
-// Gumbel noise for four consecutive elements 4 v4 .. 4 v4 + 3 of a row, in base-2
-// key units: argmax_v (ln w_v + G_v), G = -ln(-ln U), equals argmax_v (log2 w_v +
-// g_v) with g = -log2(-ln U) (the keys differ by the factor 1/ln 2 and a constant).
-// U = (k + 1/2) 2^-24 with k = word >> 8 of Philox at counter (c, 1 + v4, 0), key =
-// seed.  -ln U is formed from whichever of U and 1 - U is exact in float32: log2 of
-// U = (2k + 1) 2^-25 below 1/2, log1p(-e) with e = 1 - U = (2^25 - 2k - 1) 2^-25 from
-// 1/2 up, so the largest noise values (U near 1, the likely winners) keep their
+// Exponential variates for four consecutive elements 4 v4 .. 4 v4 + 3 of a row, in
+// base-2 units: E = -log2 U = -ln U / ln 2, U = (k + 1/2) 2^-24 with k = word >> 8
+// of Philox at counter (c, 1 + v4, 0), key = seed.  The Gumbel noise is -ln(-ln U),
+// so argmax_v (ln w_v + G_v) = argmax_v w_v / E_v = argmax_v (log2 w_v - log2 E_v)
+// (the exponential race).  E is formed from whichever of U and 1 - U is exact in
+// float32: U = (2k + 1) 2^-25 below 1/2; from 1/2 up, e = 1 - U = (2^25 - 2k - 1)
+// 2^-25 and -log2(1 - e) = -log2(y) e / (1 - y) with y = 1 - e rounded (the log1p
+// identity of Goldberg, "What every computer scientist should know about
+// floating-point arithmetic", Theorem 4; 1 - y is exact), or e / ln 2 when y rounds
+// to 1.  The smallest E (U near 1, the likely winners) thus keeps full relative
 // accuracy.
-__device__ __forceinline__ void gumbel4(uint64_t seed, uint64_t c, uint32_t v4, float (&g)[4]) {
+__device__ __forceinline__ float expo_of_word(uint32_t w) {
+  const uint32_t k = w >> 8;
+  const bool low = k < (1u << 23);
+  const float e = (float)((1u << 25) - 2u * k - 1u) * 0x1p-25f;
+  const float y = 1.f - e;
+  const float z = low ? (float)(2u * k + 1u) * 0x1p-25f : y;
+  const float f = low ? 1.f : e * __builtin_amdgcn_rcpf(1.f - y);
+  const float E = -fast_log2(z) * f;
+  return !low && y == 1.f ? e * kLog2e : E;
+}
+
+__device__ __forceinline__ void expo4(uint64_t seed, uint64_t c, uint32_t v4, float (&E)[4]) {
   const P4 in{{(uint32_t)c, (uint32_t)(c >> 32), v4 + 1u, 0u}};
   const P4 o = philox4x32_10(in, (uint32_t)seed, (uint32_t)(seed >> 32));
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t k = o.x[j] >> 8;
-    const float lo = -fast_log2((float)(2u * k + 1u) * 0x1p-25f) * kLn2;   // -ln U, U < 1/2
-    const float e = (float)((1u << 25) - 2u * k - 1u) * 0x1p-25f;                          // 1 - U, exact
-    const float hi = -log1pf(-e);                                                            // -ln U, U >= 1/2
-    g[j] = -fast_log2(k < (1u << 23) ? lo : hi);
-  }
+  for (int j = 0; j < 4; ++j) E[j] = expo_of_word(o.x[j]);
 }
 
 }  // namespace mtp

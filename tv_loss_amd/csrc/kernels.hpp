@@ -62,9 +62,12 @@ int verify_vec_per_thread(int dt);
 hipError_t launch_verify(const VerifyArgs& a, int dt, int mode, hipStream_t stream);
 hipError_t verify_occupancy(int dt, int mode, int* blocks_per_cu);
 int verify_record_words(int mode);
-// Gumbel-max tokens of `rows` logit rows: argmax_v (x_v L + g_v), one workgroup per row.
+// Gumbel-max tokens of `rows` logit rows: argmax_v (x_v L - log2 E_v), E the
+// elements' exponential variates.  keys: [rows][gumbel_sample_chunks_per_row] words.
+int gumbel_sample_chunks_per_row(int dt, int64_t V);
 hipError_t launch_gumbel_sample(const void* logits, int64_t row_stride, int dt, int rows, int64_t V, float L,
-                                uint64_t seed, uint64_t offset, int32_t* tokens, hipStream_t stream);
+                                uint64_t seed, uint64_t offset, int32_t* tokens, uint64_t* keys,
+                                hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // End-to-end TV loss.  Head k of position t compares draft row

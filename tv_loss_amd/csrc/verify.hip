@@ -339,17 +339,20 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
       }
       if (lane == 0) a.part2[((int64_t)g_m2 * C + c) * kWaves + wave] = pack2(rm, om);
       if constexpr (GM) {
-        // Gumbel-max keys of this wave's segment in base-2 units, key = log2 w + g:
-        // w = the residual (pair rows) and w = p, g the element's Gumbel noise; the
-        // wave keeps the largest of each with its vocabulary index
-        float kr = kNegInf, kp = kNegInf;
-        uint32_t ir = 0xffffffffu, ip = 0xffffffffu;
+        // Gumbel-max keys of this wave's segment, key = w / E (the exponential race,
+        // E the element's exponential variate): w = the residual (pair rows) and w =
+        // p.  Each thread keeps its best of each as a (numerator, E) pair compared by
+        // cross-multiplication, in increasing index order (strict >, so the smaller
+        // index stays on equal keys); the wave then compares log2 keys.
+        float np = 0.f, ep = 1.f, nr = 0.f, er = 1.f;
+        uint32_t ip = 0xffffffffu, ir = 0xffffffffu;
+        float lr = la;   // log2 of the residual's unit
         if (la != kNegInf) {
           const uint64_t crow = a.offset + (uint64_t)g_m2;
           const float lb = href[1] - lse_sh[i & 1][1];
           const bool p_units = !(lb - la > 64.f);
           const float fq = p_units ? fast_exp2(lb - la) : 1.f, fp = p_units ? 1.f : fast_exp2(la - lb);
-          const float lr = p_units ? la : lb;   // log2 of the residual's unit
+          lr = p_units ? la : lb;
           // one 16-byte slot at a time: the Philox rounds would otherwise hold the
           // registers that the items in flight need
 #pragma unroll 1
@@ -362,18 +365,26 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
               vb[0] = eb.x; vb[1] = eb.y; vb[2] = eb.z; vb[3] = eb.w;
             }
             const uint32_t gi0 = (uint32_t)(v0 + (4 * qi / PV) * 64) * PV + (4 * qi) % PV;   // 4-aligned
-            float gm[4];
-            gumbel4(a.seed, crow, gi0 >> 2, gm);
+            float E[4];
+            expo4(a.seed, crow, gi0 >> 2, E);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              argmax_fold(kp, ip, la + fast_log2(va[e]) + gm[e], gi0 + e);
+              const bool tp = va[e] * ep > np * E[e];
+              np = tp ? va[e] : np;
+              ep = tp ? E[e] : ep;
+              ip = tp ? gi0 + e : ip;
               if (pair2) {
                 const float d = fmaxf(__builtin_fmaf(-fq, vb[e], fp * va[e]), 0.f);
-                argmax_fold(kr, ir, lr + fast_log2(d) + gm[e], gi0 + e);
+                const bool tr = d * er > nr * E[e];
+                nr = tr ? d : nr;
+                er = tr ? E[e] : er;
+                ir = tr ? gi0 + e : ir;
               }
             }
           }
         }
+        float kp = np > 0.f ? la + fast_log2(np) - fast_log2(ep) : kNegInf;
+        float kr = nr > 0.f ? lr + fast_log2(nr) - fast_log2(er) : kNegInf;
         wave_argmax(kp, ip);
         if (pair2) wave_argmax(kr, ir);
         if (lane == 0) {
@@ -934,32 +945,47 @@ __global__ void verify_finish(VerifyArgs a) {
 
 // ---------------------------------------------------------------------------
 // Gumbel-max tokens of logit rows (draft sampling at a temperature): row r emits
-// argmax_v (x_v L + g_v) with g the element's Gumbel noise (counter offset + r), the
-// smallest index among equal keys, -1 if no key is finite.  One workgroup per row;
-// thread t walks the 16-byte vectors t, t + 256, ...; four elements share a Philox
-// call.
+// argmax_v (x_v L - log2 E_v) with E the element's exponential variate (counter
+// offset + r; L = log2(e) / T), the smallest index among equal keys, -1 if no key
+// is finite.  A row is cut into chunks of kSampleVec 16-byte vectors, one
+// workgroup each (thread t takes vectors t, t + 256, ...), which writes its best
+// (key, index + 1) word; gumbel_sample_finish reduces a row's words, one wave per row.
+constexpr int kSampleVecPerThread = 4;
+constexpr int kSampleVec = kBlock * kSampleVecPerThread;
+
 template <int DT>
-__global__ __launch_bounds__(kBlock) void gumbel_sample(const char* logits, int64_t row_bytes, int64_t V, float L,
-                                                        uint64_t seed, uint64_t offset, int32_t* tokens) {
+__global__ __launch_bounds__(kBlock) void gumbel_sample_chunks(const char* logits, int64_t row_bytes, int64_t V,
+                                                               int nchunks, float L, uint64_t seed, uint64_t offset,
+                                                               uint64_t* keys) {
   constexpr int PV = Elem<DT>::kPerVec;
-  const int r = blockIdx.x;
+  const int r = blockIdx.x / nchunks, c = blockIdx.x - r * nchunks;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const char* row = logits + (int64_t)r * row_bytes;
   const int64_t nvec = (V + PV - 1) / PV;
   const uint64_t crow = offset + (uint64_t)r;
+  const int64_t vb = (int64_t)c * kSampleVec + threadIdx.x;
+  // all of this thread's loads first; a vector past the row's end stays unused
+  u32x4 w[kSampleVecPerThread];
+#pragma unroll
+  for (int j = 0; j < kSampleVecPerThread; ++j) {
+    const int64_t v = vb + (int64_t)j * kBlock;
+    if ((v + 1) * PV <= V) w[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row) + v);
+  }
   float km = kNegInf;
   uint32_t ki = 0xffffffffu;
-  for (int64_t v = threadIdx.x; v < nvec; v += kBlock) {
+#pragma unroll
+  for (int j = 0; j < kSampleVecPerThread; ++j) {
+    const int64_t v = vb + (int64_t)j * kBlock;
+    if (v >= nvec) break;
     float x[PV];
     if ((v + 1) * PV <= V) {
-      const u32x4 w = reinterpret_cast<const u32x4*>(row)[v];
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         if constexpr (DT == kBF16) {
-          x[2 * h] = bf16_lo(w[h]);
-          x[2 * h + 1] = bf16_hi(w[h]);
+          x[2 * h] = bf16_lo(w[j][h]);
+          x[2 * h + 1] = bf16_hi(w[j][h]);
         } else {
-          x[h] = __uint_as_float(w[h]);
+          x[h] = __uint_as_float(w[j][h]);
         }
       }
     } else {
@@ -968,11 +994,11 @@ __global__ __launch_bounds__(kBlock) void gumbel_sample(const char* logits, int6
     }
 #pragma unroll
     for (int h = 0; h < PV / 4; ++h) {
-      float gm[4];
-      gumbel4(seed, crow, (uint32_t)(v * PV / 4 + h), gm);
+      float E[4];
+      expo4(seed, crow, (uint32_t)(v * PV / 4 + h), E);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        argmax_fold(km, ki, __builtin_fmaf(x[4 * h + e], L, gm[e]), (uint32_t)(v * PV + 4 * h + e));
+        argmax_fold(km, ki, __builtin_fmaf(x[4 * h + e], L, -fast_log2(E[e])), (uint32_t)(v * PV + 4 * h + e));
     }
   }
   wave_argmax(km, ki);
@@ -987,20 +1013,51 @@ __global__ __launch_bounds__(kBlock) void gumbel_sample(const char* logits, int6
     float m = m_sh[0];
     uint32_t idx = i_sh[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) argmax_fold(m, idx, m_sh[w], i_sh[w]);
-    tokens[r] = m > kNegInf && idx < (uint32_t)V ? (int32_t)idx : -1;
+    for (int q = 1; q < kWaves; ++q) argmax_fold(m, idx, m_sh[q], i_sh[q]);
+    keys[blockIdx.x] = pack_argmax(m, idx);
   }
 }
 
+// Each wave clears its row's words after reading them: the workspace is left zeroed,
+// as the verify kernels leave theirs, so that the two can share one.
+__global__ __launch_bounds__(kBlock) void gumbel_sample_finish(uint64_t* keys, int rows, int nchunks, int64_t V,
+                                                               int32_t* tokens) {
+  const int r = blockIdx.x * kWaves + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (r >= rows) return;
+  float m = kNegInf;
+  uint32_t idx = 0xffffffffu;
+  for (int i = lane; i < nchunks; i += 64) {
+    uint64_t* const p = keys + (int64_t)r * nchunks + i;
+    const uint64_t w = *p;
+    *p = 0ull;
+    argmax_fold(m, idx, unpack_lo(w), argmax_index(w));
+  }
+  wave_argmax(m, idx);
+  if (lane == 0) tokens[r] = m > kNegInf && idx < (uint32_t)V ? (int32_t)idx : -1;
+}
+
+int gumbel_sample_chunks_per_row(int dt, int64_t V) {
+  const int pv = dt == kBF16 ? Elem<kBF16>::kPerVec : Elem<kF32>::kPerVec;
+  const int64_t nvec = (V + pv - 1) / pv;
+  return (int)((nvec + kSampleVec - 1) / kSampleVec);
+}
+
 hipError_t launch_gumbel_sample(const void* logits, int64_t row_stride, int dt, int rows, int64_t V, float L,
-                                uint64_t seed, uint64_t offset, int32_t* tokens, hipStream_t stream) {
+                                uint64_t seed, uint64_t offset, int32_t* tokens, uint64_t* keys,
+                                hipStream_t stream) {
   const char* base = reinterpret_cast<const char*>(logits);
+  const int nch = gumbel_sample_chunks_per_row(dt, V);
+  const dim3 grid((unsigned)((int64_t)rows * nch));
   if (dt == kBF16)
-    hipLaunchKernelGGL(gumbel_sample<kBF16>, dim3((unsigned)rows), dim3(kBlock), 0, stream, base, row_stride * 2, V, L,
-                       seed, offset, tokens);
+    hipLaunchKernelGGL(gumbel_sample_chunks<kBF16>, grid, dim3(kBlock), 0, stream, base, row_stride * 2, V, nch, L,
+                       seed, offset, keys);
   else
-    hipLaunchKernelGGL(gumbel_sample<kF32>, dim3((unsigned)rows), dim3(kBlock), 0, stream, base, row_stride * 4, V, L,
-                       seed, offset, tokens);
+    hipLaunchKernelGGL(gumbel_sample_chunks<kF32>, grid, dim3(kBlock), 0, stream, base, row_stride * 4, V, nch, L,
+                       seed, offset, keys);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gumbel_sample_finish, dim3((unsigned)((rows + kWaves - 1) / kWaves)), dim3(kBlock), 0, stream,
+                     keys, rows, nch, V, tokens);
   return hipGetLastError();
 }
 

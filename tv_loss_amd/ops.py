@@ -327,10 +327,13 @@ def gumbel_sample(logits, temperature, seed, offset=0):
             padded = torch.empty((rows, vp), dtype=flat.dtype, device=flat.device)
             padded[:, :V] = flat
             flat, stride = padded, vp
+        nbytes = ctypes.c_size_t()
+        check(lib.mtp_gumbel_sample_workspace_size(rows, V, dt, ctypes.byref(nbytes)))
+        ws = workspace(logits.device, nbytes.value)
         with torch.cuda.device(logits.device):
             check(lib.mtp_gumbel_sample(_ptr(flat), stride, dt, rows, V, ctypes.c_float(T),
                                         ctypes.c_uint64(seed), ctypes.c_uint64(offset), _ptr(tokens),
-                                        _stream(logits.device)))
+                                        _ptr(ws), ws.numel(), _stream(logits.device)))
     return tokens.reshape(lead)
 
 
