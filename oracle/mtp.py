@@ -71,7 +71,8 @@ def inverse_cdf(r, t):
     """Smallest v (in vocabulary order) whose cumulative mass C_v = sum_{w<=v} r_w
     exceeds t; if rounding leaves none, the last v with r_v > 0.
 
-    paperlayer App. G.1 samples the residual "by CDF inversion".  READING: the
+    paperlayer App. G.1 draws the residual sample by inverting its cumulative
+    distribution.  READING: the
     cumulative sum runs in vocabulary index order and the comparison is strict,
     so a token with r_v = 0 is never chosen.
     Returns (token, lower boundary C_{v-1}, upper boundary C_v).
