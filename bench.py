@@ -61,8 +61,36 @@ def profiled_traffic(summary, sources):
     return float(fields["traffic_bytes_per_call"])
 
 
+def profiled_valu_busy(kernels, weights=None):
+    """rocprofv3's VALUBusy (%) for the named kernels from the committed summary,
+    averaged with the given time weights, or None when the kernel sources have
+    changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "valu_busy_bench_kernels.md")
+    if not os.path.exists(path):
+        return None
+    sha, busy = None, {}
+    for line in open(path):
+        if line.startswith("source_sha256:"):
+            sha = line.split(":", 1)[1].split()[0]
+        elif line.startswith("| `"):
+            cells = [c.strip() for c in line.strip().strip("|").split("|")]
+            busy[cells[0].strip("`")] = float(cells[3])
+    h = hashlib.sha256()
+    for f in VALU_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    vals = [busy[k] for k in kernels if k in busy]
+    if sha != h.hexdigest()[:16] or len(vals) != len(kernels):
+        return None
+    weights = weights or [1.0] * len(vals)
+    return sum(v * w for v, w in zip(vals, weights)) / sum(weights)
+
+
 VERIFY_SOURCES = ["tv_loss_amd/csrc/verify.hip", "tv_loss_amd/csrc/device_common.hpp", "tv_loss_amd/csrc/kernels.hpp"]
 TV_SOURCES = ["tv_loss_amd/csrc/tv_loss.hip", "tv_loss_amd/csrc/device_common.hpp", "tv_loss_amd/csrc/kernels.hpp"]
+VALU_SOURCES = ["tv_loss_amd/csrc/verify.hip", "tv_loss_amd/csrc/tv_loss.hip", "tv_loss_amd/csrc/device_common.hpp",
+                "tv_loss_amd/csrc/kernels.hpp"]
 
 
 def verify_bytes(B, G, V, elem):
@@ -153,17 +181,52 @@ def cpu_baseline(torch, w, seconds):
     db = bf16_bits_to_f64(d.cpu().view(torch.int16).numpy().view(np.uint16))
     yb = y.cpu().numpy()
     G1 = w["G"] + 1
+    # one core: this thread pinned to a single CPU for the timed loop
+    old = os.sched_getaffinity(0) if hasattr(os, "sched_getaffinity") else None
+    if old:
+        os.sched_setaffinity(0, {min(old)})
     n = 0
     t0 = time.process_time()
     w0 = time.perf_counter()
-    while True:
-        b = n % tb.shape[0]
-        omtp.verify(tb[b:b + 1], db[b:b + 1], yb[b:b + 1], w["seed"], b * G1)
-        n += 1
-        if time.process_time() - t0 >= seconds:
-            break
-    wall = time.perf_counter() - w0
+    try:
+        while True:
+            b = n % tb.shape[0]
+            omtp.verify(tb[b:b + 1], db[b:b + 1], yb[b:b + 1], w["seed"], b * G1)
+            n += 1
+            if time.process_time() - t0 >= seconds:
+                break
+    finally:
+        wall = time.perf_counter() - w0
+        if old:
+            os.sched_setaffinity(0, old)
     return n, wall
+
+
+def stream_context(torch, nbytes=1 << 31, reps=10):
+    """Achievable-bandwidth context from plain torch kernels on the same GPU: a
+    device-to-device copy (bytes read + written) and a float32 sum (bytes read)."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    out = {}
+    for name, fn, moved in (("copy_gbs", lambda: dst.copy_(src), 2 * nbytes),
+                            ("read_sum_gbs", lambda: src.sum(), nbytes)):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        out[name] = moved * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
+def pct(xs, q):
+    s = sorted(xs)
+    return s[min(len(s) - 1, int(round(q * (len(s) - 1))))]
 
 
 def main():
@@ -230,7 +293,9 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": profiled_traffic("verify_rollout_64x3_V151936_bf16.md", VERIFY_SOURCES),
                      "kernel": "verify_main + verify_finish (one mtp_verify call)", "bytes_per_launch": alg_bytes,
-                     "kernel_us_mean": kmean * 1e3, "kernel_us_median": ksorted[len(ksorted) // 2] * 1e3},
+                     "kernel_us_mean": kmean * 1e3, "kernel_us_median": ksorted[len(ksorted) // 2] * 1e3,
+                     "kernel_us_p10": pct(kms, 0.1) * 1e3, "kernel_us_p90": pct(kms, 0.9) * 1e3,
+                     "valu_busy_pct": profiled_valu_busy(["void mtp::verify_main<1, 2, 0>(mtp::VerifyArgs)"])},
     }
 
     if not args.no_tv:
@@ -254,6 +319,10 @@ def main():
                          "frac": gbs / HBM_PEAK_GBS,
                          "traffic": profiled_traffic("tv_loss_T8192x3_V151936_bf16.md", TV_SOURCES),
                          "kernel": "tv_fwd_lse + tv_fwd_stats + tv_fwd_finish + tv_fwd_mean + tv_bwd_kernel",
+                         "valu_busy_pct": profiled_valu_busy(["void mtp::tv_fwd_lse<1, 3, true>(mtp::TvArgs)",
+                                                              "void mtp::tv_fwd_stats<1, 3, true>(mtp::TvArgs)",
+                                                              "void mtp::tv_bwd_kernel<1, 1, true>(mtp::TvArgs)"],
+                                                             [fm / 2, fm / 2, bm]),
                          "bytes_per_launch": fwd_bytes + bwd_bytes},
         }
         log(f"tv loss: fwd {fm:.3f} ms ({fwd_bytes / fm / 1e6:.0f} GB/s), bwd {bm:.3f} ms "
@@ -368,10 +437,15 @@ def main():
         result["cpu_baseline"] = {
             "value": n * G / cwall, "unit": "draft positions/s", "cores": cores, "kind": "oracle",
             "sample": f"{n} rollout sequences ({n * G} draft positions, {n * (2 * G + 1)} rows of V={V}) "
-                      f"through the float64 NumPy oracle, one thread, {cwall:.1f} s; host has "
+                      f"through the float64 NumPy oracle, pinned to one CPU, {cwall:.1f} s; host has "
                       f"{os.cpu_count()} CPUs",
         }
         log(f"cpu oracle: {n * G / cwall:.1f} positions/s on one core")
+
+    if not args.no_extra:
+        ctx = stream_context(torch)
+        result["roofline"]["stream_context"] = ctx
+        log(f"stream context: torch copy {ctx['copy_gbs']:.0f} GB/s, torch float32 sum {ctx['read_sum_gbs']:.0f} GB/s")
 
     if args.copy_probe > 0:
         src = torch.ones(args.copy_probe, dtype=torch.uint8, device="cuda:0")
