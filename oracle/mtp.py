@@ -534,3 +534,112 @@ def indicator_margin(target, draft):
             logq, _ = log_softmax(draft[t, k])
             m[t, k] = np.abs(logq - logp)
     return m
+
+
+def _head_topk(x, G):
+    """Top-K target entries per (position, head): a [T, K] input is shared by all heads."""
+    x = np.asarray(x)
+    if x.ndim == 2:
+        return np.broadcast_to(x[:, None, :], (x.shape[0], G, x.shape[1]))
+    return x
+
+
+def tv_topk_stats(idx, val, draft):
+    """Per (position t, head k) for the top-K path: lse_A, lse_q, alpha, S.
+
+    paperlayer App. F ("Fused TV Loss Kernel"): an optional top-K path keeps O(K)
+    of the target instead of O(V).  READING: the target is given by K entries per
+    row, vocabulary indices I_j and target logits A_j, and stands for the target
+    truncated to those entries and renormalised, p_j = exp(A_j - lse_A); the
+    draft stays the full softmax q = softmax(z) over V.  Then, entry by entry,
+        alpha = clamp(sum_j min(p_j, q_{I_j}), 0, 1),
+        S = sum_j 1[log q_{I_j} <= log p_j] q_{I_j},
+    which for distinct indices are the full path's alpha and S against the
+    truncated target (p = 0 off the K entries, where the indicator is 0).
+    READING: an entry whose index is outside [0, V) has no mass (as A_j = -inf);
+    repeated indices are taken entry by entry (each its own point mass), which is
+    no longer a distance between distributions over V.
+    idx: int [T, K] (shared by the heads) or [T, gamma, K]; val: the same shape;
+    draft: [T, gamma, V].  Returns float64 [T, gamma, 4].
+    """
+    draft = np.asarray(draft, dtype=np.float64)
+    T, G, V = draft.shape
+    I = _head_topk(idx, G)
+    A = _head_topk(np.asarray(val, dtype=np.float64), G)
+    saved = np.empty((T, G, 4))
+    for t in range(T):
+        for k in range(G):
+            ii = np.asarray(I[t, k], dtype=np.int64)
+            ok = (ii >= 0) & (ii < V)
+            a = np.where(ok, A[t, k], -np.inf)
+            logp, lse_a = log_softmax(a)
+            logq, lse_q = log_softmax(draft[t, k])
+            if logp is None or logq is None:
+                saved[t, k] = (lse_a, lse_q, np.nan, np.nan)
+                continue
+            lq = np.where(ok, logq[np.where(ok, ii, 0)], -np.inf)
+            qj, pj = np.exp(lq), np.exp(logp)
+            alpha = min(max(float(np.sum(np.minimum(pj, qj))), 0.0), 1.0)
+            s = float(np.sum(qj[lq <= logp]))
+            saved[t, k] = (lse_a, lse_q, alpha, s)
+    return saved
+
+
+def tv_topk_loss(idx, val, draft):
+    """Mean over positions of the end-to-end TV loss with top-K targets (the
+    position loss and the mean as in tv_loss).  Returns (loss, pos_loss, saved)."""
+    saved = tv_topk_stats(idx, val, draft)
+    pos_loss = e2e_position_loss(saved[:, :, 2])
+    return float(np.mean(pos_loss)), pos_loss, saved
+
+
+def tv_topk_loss_grad(idx, val, draft, g=1.0):
+    """Gradient of g * tv_topk_loss with respect to the draft logits (paperlayer
+    App. A with the truncated target): d alpha / d z_v = q_v (c_v - S) with c_v the
+    number of entries j with I_j = v and log q_v <= log p_j (0 or 1 for distinct
+    indices), chained through the end-to-end weights.  Returns float64 [T, gamma, V].
+    """
+    draft = np.asarray(draft, dtype=np.float64)
+    T, G, V = draft.shape
+    I = _head_topk(idx, G)
+    A = _head_topk(np.asarray(val, dtype=np.float64), G)
+    saved = tv_topk_stats(idx, val, draft)
+    w = e2e_weights(saved[:, :, 2], g, T)
+    grad = np.empty((T, G, V))
+    for t in range(T):
+        for k in range(G):
+            ii = np.asarray(I[t, k], dtype=np.int64)
+            ok = (ii >= 0) & (ii < V)
+            logp, _ = log_softmax(np.where(ok, A[t, k], -np.inf))
+            logq, _ = log_softmax(draft[t, k])
+            if logp is None or logq is None:
+                grad[t, k] = np.nan
+                continue
+            q = np.exp(logq)
+            c = np.zeros(V)
+            for j in np.flatnonzero(ok):
+                if logq[ii[j]] <= logp[j]:
+                    c[ii[j]] += 1.0
+            grad[t, k] = w[t, k] * q * (c - saved[t, k, 3])
+    return grad
+
+
+def tv_topk_indicator_margin(idx, val, draft):
+    """|log q_{I_j} - log p_j| per entry [T, gamma, K] (inf for entries out of
+    range): where it is tiny a float32 indicator may flip."""
+    draft = np.asarray(draft, dtype=np.float64)
+    T, G, V = draft.shape
+    I = _head_topk(idx, G)
+    A = _head_topk(np.asarray(val, dtype=np.float64), G)
+    K = I.shape[-1]
+    m = np.full((T, G, K), np.inf)
+    for t in range(T):
+        for k in range(G):
+            ii = np.asarray(I[t, k], dtype=np.int64)
+            ok = (ii >= 0) & (ii < V)
+            logp, _ = log_softmax(np.where(ok, A[t, k], -np.inf))
+            logq, _ = log_softmax(draft[t, k])
+            if logp is None or logq is None:
+                continue
+            m[t, k, ok] = np.abs(logq[ii[ok]] - logp[ok])
+    return m
