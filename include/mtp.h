@@ -234,6 +234,49 @@ mtp_status mtp_tv_loss_bwd(const void* target, int64_t target_pos_stride, int64_
                            mtp_dtype grad_dtype, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* End-to-end TV loss with top-K targets (paperlayer App. F "Fused TV Loss
+ * Kernel": an optional top-K path keeps O(K) of the target instead of O(V)).
+ *
+ * The target of head k at position t is given by K entries, vocabulary indices
+ * I_j = target_idx[t*topk_pos_stride + k*topk_head_stride + j] and logits
+ * A_j = target_val[same] (topk_head_stride = 0: one set shared by all heads).  It
+ * stands for the target truncated to those entries and renormalised,
+ * p_j = exp(A_j - lse_A); q = softmax(draft row (t, k)) over all V.  Then
+ *   alpha = clamp(sum_j min(p_j, q(I_j)), 0, 1),  S = sum_j 1[q(I_j) <= p_j] q(I_j),
+ * and the loss, per-position losses and the gradient are those of
+ * mtp_tv_loss_fwd / mtp_tv_loss_bwd with these alpha and S:
+ *   dL/dz_v = w_{t,k} q_v (c_v - S),  c_v = #{j : I_j = v, q_v <= p_j}.
+ * For distinct indices this is the full-vocabulary TV loss against the truncated
+ * target.  An index outside [0, V) carries no mass; repeated indices count entry
+ * by entry (each its own point mass).  saved[t, k, :] = (lse_A, lse_q, alpha, S).
+ * A row with no finite normaliser (no entry in range, or a NaN / all -inf draft
+ * row) gives NaN alpha and S.
+ *
+ * target_idx: device int32, target_val: device float32, both 4-byte aligned;
+ * strides in entries.  Draft, dtype, T, gamma, vocab, strides, loss, pos_loss,
+ * saved, grad and grad_dtype as for mtp_tv_loss_fwd / _bwd; 1 <= K <= 2^20.  The
+ * forward needs a workspace of mtp_tv_topk_workspace_size bytes (zeroed once,
+ * left zeroed); the backward needs none.  The forward reads the draft once
+ * (plus the K entries); the backward reads it once and writes the gradient.
+ */
+mtp_status mtp_tv_topk_workspace_size(int32_t T, int32_t gamma, int32_t vocab, mtp_dtype dtype, size_t* bytes);
+
+mtp_status mtp_tv_topk_fwd(const int32_t* target_idx, const float* target_val, int64_t topk_pos_stride,
+                           int64_t topk_head_stride, int32_t K,
+                           const void* draft, int64_t draft_pos_stride, int64_t draft_head_stride,
+                           mtp_dtype dtype, int32_t T, int32_t gamma, int32_t vocab,
+                           float* loss, float* pos_loss, float* saved,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+mtp_status mtp_tv_topk_bwd(const int32_t* target_idx, const float* target_val, int64_t topk_pos_stride,
+                           int64_t topk_head_stride, int32_t K,
+                           const void* draft, int64_t draft_pos_stride, int64_t draft_head_stride,
+                           mtp_dtype dtype, int32_t T, int32_t gamma, int32_t vocab,
+                           const float* saved, const float* grad_loss,
+                           void* grad, int64_t grad_pos_stride, int64_t grad_head_stride,
+                           mtp_dtype grad_dtype, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Error word of a workspace: non-zero if a kernel that used it hit its bounded
  * wait limit (the cluster exchange did not complete within one second).  Copies
  * the 32-bit word to host memory, synchronising `stream`. */

@@ -118,3 +118,13 @@ def tv_inputs(w, device="cpu", seed=None, T=None, V=None, chunk=256):
         target[s:e] = t.to(w["dtype"])
         draft[s:e] = d.to(w["dtype"])
     return target, draft
+
+
+def topk_inputs(w, K, device="cpu", seed=None, T=None, V=None):
+    """(target_idx int32, target_val float32, draft) for the top-K TV path: a TV
+    workload's target rows reduced to their K largest logits (indices and the
+    stored values, widened to float32), [T, K] when shared by the heads, else
+    [T, G, K]; the draft as in tv_inputs."""
+    target, draft = tv_inputs(w, device, seed=seed, T=T, V=V)
+    val, idx = torch.topk(target.to(torch.float32), K, dim=-1)
+    return idx.to(torch.int32).contiguous(), val.contiguous(), draft

@@ -194,6 +194,52 @@ def test_tv_bwd_rejects_bad_arguments(kw, code):
     assert _bwd(lib, **kw) == code, lib.mtp_last_error()
 
 
+def _topk_fwd(lib, **kw):
+    a = dict(i=A16, v=A16, kp=256, kh=0, K=256, d=A16, dp=3 * 151936, dh=151936, dt=1, T=8, G=3, V=151936,
+             loss=A16, pos=None, saved=A16, ws=A16, wsb=1 << 30)
+    a.update(kw)
+    return lib.mtp_tv_topk_fwd(a["i"], a["v"], a["kp"], a["kh"], a["K"], a["d"], a["dp"], a["dh"], a["dt"], a["T"],
+                               a["G"], a["V"], a["loss"], a["pos"], a["saved"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(i=None), 1), (dict(v=None), 1), (dict(d=None), 1), (dict(loss=None), 1), (dict(saved=None), 1),
+    (dict(K=0), 2), (dict(K=(1 << 20) + 1), 2), (dict(T=0), 2), (dict(G=9), 2), (dict(kp=-1), 2),
+    (dict(dt=4), 3), (dict(i=P(0x10002)), 4), (dict(v=P(0x10001)), 4), (dict(d=MIS), 4),
+    (dict(ws=None), 5), (dict(wsb=256), 5),
+])
+def test_tv_topk_fwd_rejects_bad_arguments(kw, code):
+    lib = tv_loss_amd.load()
+    assert _topk_fwd(lib, **kw) == code, lib.mtp_last_error()
+
+
+def _topk_bwd(lib, **kw):
+    a = dict(i=A16, v=A16, kp=256, kh=0, K=256, d=A16, dp=3 * 151936, dh=151936, dt=1, T=8, G=3, V=151936,
+             saved=A16, gl=A16, g=A16, gp=3 * 151936, gh=151936, gdt=1)
+    a.update(kw)
+    return lib.mtp_tv_topk_bwd(a["i"], a["v"], a["kp"], a["kh"], a["K"], a["d"], a["dp"], a["dh"], a["dt"], a["T"],
+                               a["G"], a["V"], a["saved"], a["gl"], a["g"], a["gp"], a["gh"], a["gdt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(saved=None), 1), (dict(gl=None), 1), (dict(g=None), 1), (dict(i=None), 1),
+    (dict(K=-3), 2), (dict(gh=-1), 2), (dict(gdt=2), 3), (dict(g=MIS), 4), (dict(gp=3 * 151936 + 1), 4),
+])
+def test_tv_topk_bwd_rejects_bad_arguments(kw, code):
+    lib = tv_loss_amd.load()
+    assert _topk_bwd(lib, **kw) == code, lib.mtp_last_error()
+
+
+def test_tv_topk_workspace_size():
+    lib = tv_loss_amd.load()
+    n = ctypes.c_size_t()
+    assert lib.mtp_tv_topk_workspace_size(8192, 3, 151936, 1, ctypes.byref(n)) == 0
+    full = ctypes.c_size_t()
+    assert lib.mtp_tv_loss_workspace_size(8192, 3, 151936, 1, 1, ctypes.byref(full)) == 0
+    assert 0 < n.value < full.value and n.value % 256 == 0
+    assert lib.mtp_tv_topk_workspace_size(0, 3, 151936, 1, ctypes.byref(n)) == 2
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     t = torch.zeros(1, 4, 16)

@@ -47,6 +47,13 @@ SIGNATURES = {
     "mtp_tv_loss_bwd": (_c.c_int, [_P, _c.c_int64, _c.c_int64, _P, _c.c_int64, _c.c_int64, _c.c_int,
                                    _c.c_int32, _c.c_int32, _c.c_int32, _P, _P, _P, _c.c_int64, _c.c_int64,
                                    _c.c_int, _P]),
+    "mtp_tv_topk_workspace_size": (_c.c_int, [_c.c_int32, _c.c_int32, _c.c_int32, _c.c_int,
+                                              _c.POINTER(_c.c_size_t)]),
+    "mtp_tv_topk_fwd": (_c.c_int, [_P, _P, _c.c_int64, _c.c_int64, _c.c_int32, _P, _c.c_int64, _c.c_int64, _c.c_int,
+                                   _c.c_int32, _c.c_int32, _c.c_int32, _P, _P, _P, _P, _c.c_size_t, _P]),
+    "mtp_tv_topk_bwd": (_c.c_int, [_P, _P, _c.c_int64, _c.c_int64, _c.c_int32, _P, _c.c_int64, _c.c_int64, _c.c_int,
+                                   _c.c_int32, _c.c_int32, _c.c_int32, _P, _P, _P, _c.c_int64, _c.c_int64, _c.c_int,
+                                   _P]),
     "mtp_workspace_error": (_c.c_int, [_P, _c.POINTER(_c.c_uint32), _P]),
     "mtp_status_string": (_c.c_char_p, [_c.c_int]),
     "mtp_last_error": (_c.c_char_p, []),

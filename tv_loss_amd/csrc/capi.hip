@@ -37,6 +37,7 @@ int per_vec(mtp_dtype dt) { return dt == MTP_BF16 ? 8 : 4; }
 
 constexpr int64_t kMaxVocab = int64_t(1) << 30;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int32_t kMaxTopK = 1 << 20;
 
 mtp_status check_common(mtp_dtype dt, int32_t gamma, int32_t vocab) {
   if (dt != MTP_F32 && dt != MTP_BF16) return fail(MTP_ERR_DTYPE, "unknown dtype code %d", (int)dt);
@@ -123,6 +124,21 @@ TvLayout tv_layout(int32_t T, int32_t G, int32_t V, mtp_dtype dt, bool shared) {
   L.err = off; off = align256(off + 4);
   L.part1 = off; off = align256(off + (size_t)T * C * mtp::tv_fwd_part1_words(G, shared) * 8);
   L.part2 = off; off = align256(off + (size_t)T * C * 2 * G * 4);
+  L.pos = off; off = align256(off + (size_t)T * 4);
+  L.total = off;
+  return L;
+}
+
+// top-K path: error word, draft log-sum-exp partials [t][chunk][gamma] as float2,
+// per-position losses [t]
+TvLayout topk_layout(int32_t T, int32_t G, int32_t V, mtp_dtype dt) {
+  TvLayout L{};
+  L.sp = mtp::make_split(V, per_vec(dt), mtp::tv_topk_fwd_vec_per_thread(dt, G), false);
+  const int64_t C = L.sp.nchunks;
+  size_t off = 0;
+  L.err = off; off = align256(off + 4);
+  L.part1 = off; off = align256(off + (size_t)T * C * G * 8);
+  L.part2 = off;
   L.pos = off; off = align256(off + (size_t)T * 4);
   L.total = off;
   return L;
@@ -395,6 +411,84 @@ mtp_status mtp_tv_loss_fwd(const void* target, int64_t target_pos_stride, int64_
   a.sp = L.sp;
   hipError_t e = mtp::launch_tv_fwd(a, dtype, shared, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MTP_ERR_LAUNCH, "TV forward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+static mtp_status check_topk_inputs(const int32_t* idx, const float* val, int64_t kp, int64_t kh, int32_t K,
+                                    const void* draft, int64_t dp, int64_t dh, mtp_dtype dtype, int32_t T,
+                                    int32_t gamma, int32_t vocab) {
+  mtp_status s = check_common(dtype, gamma, vocab);
+  if (s) return s;
+  if (T < 1) return fail(MTP_ERR_SHAPE, "T = %d must be >= 1", T);
+  if (K < 1 || K > kMaxTopK) return fail(MTP_ERR_SHAPE, "K = %d outside [1, %d]", K, kMaxTopK);
+  if (!idx || !val || !draft) return fail(MTP_ERR_NULL, "target_idx, target_val or draft is NULL");
+  if (kp < 0 || kh < 0 || dp < 0 || dh < 0) return fail(MTP_ERR_SHAPE, "negative stride");
+  if (((uintptr_t)idx & 3u) || ((uintptr_t)val & 3u))
+    return fail(MTP_ERR_ALIGN, "target_idx or target_val is not 4-byte aligned");
+  if ((s = check_row_base(draft, dp, dtype, "draft position"))) return s;
+  if ((s = check_row_base(draft, dh, dtype, "draft head"))) return s;
+  return MTP_OK;
+}
+
+mtp_status mtp_tv_topk_workspace_size(int32_t T, int32_t gamma, int32_t vocab, mtp_dtype dtype, size_t* bytes) {
+  if (!bytes) return fail(MTP_ERR_NULL, "bytes is NULL");
+  mtp_status s = check_common(dtype, gamma, vocab);
+  if (s) return s;
+  if (T < 1) return fail(MTP_ERR_SHAPE, "T = %d must be >= 1", T);
+  *bytes = topk_layout(T, gamma, vocab, dtype).total;
+  return ok();
+}
+
+mtp_status mtp_tv_topk_fwd(const int32_t* target_idx, const float* target_val, int64_t topk_pos_stride,
+                           int64_t topk_head_stride, int32_t K, const void* draft, int64_t draft_pos_stride,
+                           int64_t draft_head_stride, mtp_dtype dtype, int32_t T, int32_t gamma, int32_t vocab,
+                           float* loss, float* pos_loss, float* saved, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  mtp_status s = check_topk_inputs(target_idx, target_val, topk_pos_stride, topk_head_stride, K, draft,
+                                   draft_pos_stride, draft_head_stride, dtype, T, gamma, vocab);
+  if (s) return s;
+  if (!loss || !saved) return fail(MTP_ERR_NULL, "loss or saved is NULL");
+  const TvLayout L = topk_layout(T, gamma, vocab, dtype);
+  if ((s = check_workspace(workspace, workspace_bytes, L.total))) return s;
+  if ((int64_t)T * L.sp.nchunks > 0x7fffffffLL) return fail(MTP_ERR_SHAPE, "T * chunks is too large");
+  mtp::TvArgs a{};
+  a.idx = target_idx; a.val = target_val; a.k_pos = topk_pos_stride; a.k_head = topk_head_stride; a.K = K;
+  a.draft = draft; a.d_pos = draft_pos_stride; a.d_head = draft_head_stride;
+  a.T = T; a.G = gamma; a.V = vocab;
+  a.loss = loss; a.pos_loss = pos_loss; a.saved = saved;
+  a.err = at<uint32_t>(workspace, L.err);
+  a.part1 = at<uint64_t>(workspace, L.part1);
+  a.pos_ws = at<float>(workspace, L.pos);
+  a.sp = L.sp;
+  hipError_t e = mtp::launch_tv_topk_fwd(a, dtype, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MTP_ERR_LAUNCH, "top-K TV forward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+mtp_status mtp_tv_topk_bwd(const int32_t* target_idx, const float* target_val, int64_t topk_pos_stride,
+                           int64_t topk_head_stride, int32_t K, const void* draft, int64_t draft_pos_stride,
+                           int64_t draft_head_stride, mtp_dtype dtype, int32_t T, int32_t gamma, int32_t vocab,
+                           const float* saved, const float* grad_loss, void* grad, int64_t grad_pos_stride,
+                           int64_t grad_head_stride, mtp_dtype grad_dtype, void* stream) {
+  mtp_status s = check_topk_inputs(target_idx, target_val, topk_pos_stride, topk_head_stride, K, draft,
+                                   draft_pos_stride, draft_head_stride, dtype, T, gamma, vocab);
+  if (s) return s;
+  if (grad_dtype != MTP_F32 && grad_dtype != MTP_BF16)
+    return fail(MTP_ERR_DTYPE, "unknown grad dtype code %d", (int)grad_dtype);
+  if (!saved || !grad_loss || !grad) return fail(MTP_ERR_NULL, "saved, grad_loss or grad is NULL");
+  if (grad_pos_stride < 0 || grad_head_stride < 0) return fail(MTP_ERR_SHAPE, "negative grad stride");
+  if ((s = check_row_base(grad, grad_pos_stride, grad_dtype, "grad position"))) return s;
+  if ((s = check_row_base(grad, grad_head_stride, grad_dtype, "grad head"))) return s;
+  mtp::TvArgs a{};
+  a.idx = target_idx; a.val = target_val; a.k_pos = topk_pos_stride; a.k_head = topk_head_stride; a.K = K;
+  a.draft = draft; a.d_pos = draft_pos_stride; a.d_head = draft_head_stride;
+  a.T = T; a.G = gamma; a.V = vocab;
+  a.saved_in = saved; a.grad_loss = grad_loss;
+  a.grad = grad; a.g_pos = grad_pos_stride; a.g_head = grad_head_stride; a.grad_dt = grad_dtype;
+  a.sp = mtp::make_split(vocab, per_vec(dtype), mtp::tv_bwd_vec_per_thread(dtype));
+  if ((int64_t)T * a.sp.nchunks > 0x7fffffffLL) return fail(MTP_ERR_SHAPE, "T * chunks is too large");
+  hipError_t e = mtp::launch_tv_topk_bwd(a, dtype, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MTP_ERR_LAUNCH, "top-K TV backward launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -87,6 +87,9 @@ struct TvArgs {
   // (ref, z), overlap and S partials [t][chunk][2 gamma], per-position losses [t]
   uint32_t* err; uint64_t* part1; float* part2; float* pos_ws;
   RowSplit sp;
+  // top-K path: the target of head k at position t is given by K entries, indices
+  // idx and logits val at t*k_pos + k*k_head + j (k_head = 0: shared by the heads)
+  const int32_t* idx; const float* val; int64_t k_pos, k_head; int K;
 };
 
 constexpr int kTvSavedStride = 4;   // saved[t, k, :] = (lse_p, lse_q, alpha, S)
@@ -97,5 +100,10 @@ int tv_fwd_part1_words(int G, bool shared);
 hipError_t launch_tv_fwd(const TvArgs& a, int dt, bool shared, hipStream_t stream);
 int tv_bwd_vec_per_thread(int dt);
 hipError_t launch_tv_bwd(const TvArgs& a, int dt, bool shared, hipStream_t stream);
+// top-K path: forward (draft log-sum-exp partials, per-position finish over the K
+// entries, mean) and backward; the workspace holds part1 [t][chunk][gamma] and pos_ws
+int tv_topk_fwd_vec_per_thread(int dt, int G);
+hipError_t launch_tv_topk_fwd(const TvArgs& a, int dt, hipStream_t stream);
+hipError_t launch_tv_topk_bwd(const TvArgs& a, int dt, hipStream_t stream);
 
 }  // namespace mtp

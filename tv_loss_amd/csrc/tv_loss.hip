@@ -422,4 +422,258 @@ hipError_t launch_tv_bwd(const TvArgs& a, int dt, bool shared, hipStream_t strea
   return a.grad_dt == kBF16 ? launch_bwd2<kF32, kBF16>(a, shared, stream) : launch_bwd2<kF32, kF32>(a, shared, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Top-K path (paperlayer App. F: an optional top-K path keeps O(K) of the target).
+// The target of head k at position t is given by K entries (vocabulary index I_j,
+// logit A_j); it stands for the target truncated to them and renormalised,
+// p_j = 2^(A_j log2 e - lse2_A).  With q the full softmax of the draft row,
+//   alpha = clamp(sum_j min(p_j, q_{I_j}), 0, 1),  S = sum_j 1[q_{I_j} <= p_j] q_{I_j},
+//   dL/dz_v = w q_v (c_v - S),  c_v = #{j : I_j = v, q_v <= p_j},
+// entry by entry (an index outside [0, V) carries no mass; repeated indices count
+// separately).  Forward: topk_fwd_lse streams the draft rows once (chunk
+// log-sum-exp partials, one workgroup per (t, chunk)); topk_fwd_finish (one wave
+// per position) merges them, takes the K entries' log-sum-exp, gathers the K draft
+// logits and forms alpha and S; tv_fwd_mean averages.  Backward: one workgroup per
+// (t, chunk) counts the chunk's entries whose indicator holds in LDS, then streams
+// the draft chunk and writes the gradient.
+template <int DT, int G>
+__global__ __launch_bounds__(kBlock) void topk_fwd_lse(TvArgs a) {
+  constexpr int NV = fwd_nv<G>(Elem<DT>::kPerVec);
+  constexpr int NE = NV * Elem<DT>::kPerVec;
+  const int C = a.sp.nchunks;
+  const int t = blockIdx.x / C, c = blockIdx.x - t * C;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ float part_sh[G][kWaves * 3];
+  const char* db = reinterpret_cast<const char*>(a.draft);
+  const char* rows[G];
+#pragma unroll
+  for (int k = 0; k < G; ++k) rows[k] = db + ((int64_t)t * a.d_pos + (int64_t)k * a.d_head) * Elem<DT>::kBytes;
+  float x[G][NE];
+  fwd_load<DT, NV, G>(a, rows, c, x);
+  Lse pt[G];
+  wave_pass1<NE, G, 0>(x, pt);
+  if (lane == 0) {
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      part_sh[k][wave * 3 + 0] = pt[k].ref;
+      part_sh[k][wave * 3 + 1] = pt[k].z;
+      part_sh[k][wave * 3 + 2] = 0.f;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < G) {
+    const Lse m = merge_lds<kWaves, false>(part_sh[threadIdx.x]);
+    reinterpret_cast<float2*>(a.part1)[((int64_t)t * C + c) * G + threadIdx.x] = make_float2(m.ref, m.z);
+  }
+}
+
+template <int DT, int G>
+__global__ __launch_bounds__(64 * kFinishWaves) void topk_fwd_finish(TvArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kFinishWaves + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const int C = a.sp.nchunks;
+  const int K = a.K;
+  const int64_t V = a.V;
+  const char* db = reinterpret_cast<const char*>(a.draft);
+  float al[G], ss[G], l2a[G], l2q[G];
+#pragma unroll
+  for (int k = 0; k < G; ++k) {
+    l2q[k] = fwd_row_lse2<G>(a, t, k);
+    const int32_t* ii = a.idx + (int64_t)t * a.k_pos + (int64_t)k * a.k_head;
+    const float* vv = a.val + (int64_t)t * a.k_pos + (int64_t)k * a.k_head;
+    // log2-sum-exp of the K target logits (entries out of range count as -inf)
+    float m = kNegInf;
+    for (int j = lane; j < K; j += 64) {
+      const int32_t i = ii[j];
+      m = fmaxf(m, i >= 0 && i < V ? vv[j] : kNegInf);
+    }
+    m = wave_maximum(m);
+    const float ref = m * kLog2e;
+    float z = 0.f;
+    for (int j = lane; j < K; j += 64) {
+      const int32_t i = ii[j];
+      if (i >= 0 && i < V) z += fast_exp2(__builtin_fmaf(vv[j], kLog2e, -ref));
+    }
+    z = wave_total(z);
+    l2a[k] = ref + fast_log2(z);
+    // the entries' overlap and S, on base-2 log-probabilities
+    const char* drow = db + ((int64_t)t * a.d_pos + (int64_t)k * a.d_head) * Elem<DT>::kBytes;
+    float ov = 0.f, s = 0.f;
+    for (int j = lane; j < K; j += 64) {
+      const int32_t i = ii[j];
+      if (i >= 0 && i < V) {
+        const float lq = __builtin_fmaf(load_one<DT>(drow, i), kLog2e, -l2q[k]);
+        const float lp = __builtin_fmaf(vv[j], kLog2e, -l2a[k]);
+        ov += fast_exp2(fminf(lq, lp));
+        if (lq <= lp) s += fast_exp2(lq);
+      }
+    }
+    ov = wave_total(ov);
+    s = wave_total(s);
+    // no finite normaliser on either side (no entry in range, NaN or -inf rows)
+    const bool bad = !__builtin_isfinite(l2a[k]) || !__builtin_isfinite(l2q[k]);
+    al[k] = bad ? __builtin_nanf("") : fminf(fmaxf(ov, 0.f), 1.f);
+    ss[k] = bad ? __builtin_nanf("") : s;
+  }
+  // a call leaves every workspace word it wrote at zero
+  float2* p1 = reinterpret_cast<float2*>(a.part1) + (int64_t)t * C * G;
+  for (int i = lane; i < C * G; i += 64) p1[i] = make_float2(0.f, 0.f);
+  if (lane == 0) {
+    float prod = 1.f, l = 0.f;
+    float* sv = a.saved + (int64_t)t * G * kTvSavedStride;
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      prod *= al[k];
+      l -= prod;
+      sv[k * kTvSavedStride + 0] = l2a[k] * kLn2;
+      sv[k * kTvSavedStride + 1] = l2q[k] * kLn2;
+      sv[k * kTvSavedStride + 2] = al[k];
+      sv[k * kTvSavedStride + 3] = ss[k];
+    }
+    if (a.pos_loss) a.pos_loss[t] = l;
+    a.pos_ws[t] = l;
+  }
+}
+
+template <int DT, int GDT>
+__global__ __launch_bounds__(kBlock) void topk_bwd_kernel(TvArgs a) {
+  constexpr int PV = Elem<DT>::kPerVec;
+  constexpr int NV = DT == kBF16 ? kBwdNVBf16 : kBwdNVF32;
+  constexpr int NE = NV * PV;
+  constexpr int kMap = kBlock * NE;           // the largest chunk, in elements
+  __shared__ __align__(16) float cnt[kMap];   // indicator counts of the chunk's elements
+  const int C = a.sp.nchunks;
+  const int t = blockIdx.x / C, c = blockIdx.x - (blockIdx.x / C) * C;
+  const int G = a.G, K = a.K;
+  const int64_t vbeg = (int64_t)c * a.sp.vec_per_chunk;
+  const int64_t vend = min(vbeg + a.sp.vec_per_chunk, a.sp.nvec);
+  const int64_t ebeg = vbeg * PV, eend = min(vend * PV, a.V);
+  for (int i = threadIdx.x; i < kMap; i += kBlock) cnt[i] = 0.f;
+
+  const float* sv = a.saved_in + (int64_t)t * G * kTvSavedStride;
+  float alpha[kTvMaxHeads];
+  for (int k = 0; k < G; ++k) alpha[k] = sv[k * kTvSavedStride + 2];
+  const float gscale = -a.grad_loss[0] / (float)a.T;
+
+  const char* db = reinterpret_cast<const char*>(a.draft);
+  char* gb = reinterpret_cast<char*>(a.grad);
+  constexpr int gbytes = GDT == kBF16 ? 2 : 4;
+  for (int k = 0; k < G; ++k) {
+    const char* drow = db + ((int64_t)t * a.d_pos + (int64_t)k * a.d_head) * Elem<DT>::kBytes;
+    const char* const rows[1] = {drow};
+    RawChunk<NV, 1> raw;
+    issue_rows<DT, NV, 1>(raw, rows, vbeg, a.sp);   // the chunk's loads go out first
+    float wsum = 0.f;
+    for (int kk = k; kk < G; ++kk) {
+      float prod = 1.f;
+      for (int i = 0; i <= kk; ++i)
+        if (i != k) prod *= alpha[i];
+      wsum += prod;
+    }
+    const float w = gscale * wsum;
+    const float lse_a = sv[k * kTvSavedStride + 0], lse_q = sv[k * kTvSavedStride + 1];
+    const float S = sv[k * kTvSavedStride + 3];
+    const float dl = lse_q - lse_a;
+    const int32_t* ii = a.idx + (int64_t)t * a.k_pos + (int64_t)k * a.k_head;
+    const float* vv = a.val + (int64_t)t * a.k_pos + (int64_t)k * a.k_head;
+    __syncthreads();   // the map is clear (initial zeroing or the previous head's reset)
+    // log q_v <= log p_j  <=>  z_v - A_j <= lse_q - lse_A
+    for (int j = threadIdx.x; j < K; j += kBlock) {
+      const int64_t i = ii[j];
+      if (i >= ebeg && i < eend && load_one<DT>(drow, i) - vv[j] <= dl) atomicAdd(&cnt[i - ebeg], 1.f);
+    }
+    __syncthreads();
+    float x[1][NE], gr[NE];
+    unpack_rows<DT, NV, 1>(raw, rows, vbeg, vend, a.sp, a.V, x);
+    const float lq2 = lse_q * kLog2e;
+    const float c0 = -w * S;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      float cv[PV];
+      const float4* cp = reinterpret_cast<const float4*>(cnt + (j * kBlock + threadIdx.x) * PV);
+#pragma unroll
+      for (int h = 0; h < PV / 4; ++h) {
+        const float4 f = cp[h];
+        cv[4 * h] = f.x; cv[4 * h + 1] = f.y; cv[4 * h + 2] = f.z; cv[4 * h + 3] = f.w;
+      }
+#pragma unroll
+      for (int e = 0; e < PV; ++e) {
+        const float q = fast_exp2(__builtin_fmaf(x[0][j * PV + e], kLog2e, -lq2));
+        gr[j * PV + e] = q * __builtin_fmaf(w, cv[e], c0);
+      }
+    }
+    char* grow = gb + ((int64_t)t * a.g_pos + (int64_t)k * a.g_head) * gbytes;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int64_t vi = vbeg + (int64_t)j * kBlock + threadIdx.x;
+      if (vi < vend) store_grad<GDT, PV>(grow, vi, a.sp, a.V, gr + j * PV);
+    }
+    __syncthreads();   // every thread has read the map
+    for (int j = threadIdx.x; j < K; j += kBlock) {
+      const int64_t i = ii[j];
+      if (i >= ebeg && i < eend) cnt[i - ebeg] = 0.f;
+    }
+  }
+}
+
+template <int DT, int G>
+static hipError_t launch_topk_fwd_g(const TvArgs& a, hipStream_t stream) {
+  const int64_t grid = (int64_t)a.T * a.sp.nchunks;
+  hipLaunchKernelGGL((topk_fwd_lse<DT, G>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((topk_fwd_finish<DT, G>), dim3((unsigned)((a.T + kFinishWaves - 1) / kFinishWaves)),
+                     dim3(64 * kFinishWaves), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(tv_fwd_mean, dim3(1), dim3(kBlock), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int DT>
+static hipError_t launch_topk_fwd_dt(const TvArgs& a, hipStream_t stream) {
+  switch (a.G) {
+    case 1: return launch_topk_fwd_g<DT, 1>(a, stream);
+    case 2: return launch_topk_fwd_g<DT, 2>(a, stream);
+    case 3: return launch_topk_fwd_g<DT, 3>(a, stream);
+    case 4: return launch_topk_fwd_g<DT, 4>(a, stream);
+    case 5: return launch_topk_fwd_g<DT, 5>(a, stream);
+    case 6: return launch_topk_fwd_g<DT, 6>(a, stream);
+    case 7: return launch_topk_fwd_g<DT, 7>(a, stream);
+    case 8: return launch_topk_fwd_g<DT, 8>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_tv_topk_fwd(const TvArgs& a, int dt, hipStream_t stream) {
+  return dt == kBF16 ? launch_topk_fwd_dt<kBF16>(a, stream) : launch_topk_fwd_dt<kF32>(a, stream);
+}
+
+int tv_topk_fwd_vec_per_thread(int dt, int G) {
+  const int pv = dt == kBF16 ? 8 : 4;
+  switch (G) {
+    case 1: return fwd_nv<1>(pv);
+    case 2: return fwd_nv<2>(pv);
+    case 3: return fwd_nv<3>(pv);
+    case 4: return fwd_nv<4>(pv);
+    case 5: return fwd_nv<5>(pv);
+    case 6: return fwd_nv<6>(pv);
+    case 7: return fwd_nv<7>(pv);
+    default: return fwd_nv<8>(pv);
+  }
+}
+
+template <int DT, int GDT>
+static hipError_t launch_topk_bwd2(const TvArgs& a, hipStream_t stream) {
+  const int64_t grid = (int64_t)a.T * a.sp.nchunks;
+  hipLaunchKernelGGL((topk_bwd_kernel<DT, GDT>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_tv_topk_bwd(const TvArgs& a, int dt, hipStream_t stream) {
+  if (dt == kBF16)
+    return a.grad_dt == kBF16 ? launch_topk_bwd2<kBF16, kBF16>(a, stream) : launch_topk_bwd2<kBF16, kF32>(a, stream);
+  return a.grad_dt == kBF16 ? launch_topk_bwd2<kF32, kBF16>(a, stream) : launch_topk_bwd2<kF32, kF32>(a, stream);
+}
+
 }  // namespace mtp

@@ -243,6 +243,92 @@ def tv_loss(draft, target):
     return TVLoss.apply(draft, target)
 
 
+def _topk_layout(idx, val, draft):
+    if draft.dim() != 3:
+        raise ValueError("draft must be [T, gamma, V]")
+    T, G, V = draft.shape
+    if idx.dtype != torch.int32 or val.dtype != torch.float32:
+        raise ValueError("target_idx must be int32 and target_val float32")
+    if tuple(idx.shape) != tuple(val.shape) or idx.stride() != val.stride():
+        raise ValueError("target_idx and target_val must have the same shape and strides")
+    if idx.dim() == 2 and idx.shape[0] == T:
+        k_pos, k_head = idx.stride(0), 0
+    elif idx.dim() == 3 and tuple(idx.shape[:2]) == (T, G):
+        k_pos, k_head = idx.stride(0), idx.stride(1)
+    else:
+        raise ValueError("top-K targets must be [T, K] (shared by the heads) or [T, gamma, K]")
+    if idx.stride(-1) != 1:
+        raise ValueError("top-K targets need unit stride along K")
+    if draft.stride(2) != 1:
+        raise ValueError("draft needs unit stride along V")
+    return T, G, V, idx.shape[-1], k_pos, k_head
+
+
+def tv_topk_fwd(target_idx, target_val, draft):
+    """End-to-end TV loss forward with top-K targets (mtp_tv_topk_fwd).
+    target_idx int32 / target_val float32: [T, K] shared by the heads or
+    [T, gamma, K]; draft: [T, gamma, V].  Returns (loss [1], pos_loss [T],
+    saved [T, gamma, 4] = (lse_A, lse_q, alpha, S))."""
+    lib = load()
+    _require_cuda(target_idx, target_val, draft)
+    T, G, V, K, k_pos, k_head = _topk_layout(target_idx, target_val, draft)
+    dev = draft.device
+    dt = _dtype_code(draft)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    pos_loss = torch.empty(T, dtype=torch.float32, device=dev)
+    saved = torch.empty((T, G, 4), dtype=torch.float32, device=dev)
+    nbytes = ctypes.c_size_t()
+    check(lib.mtp_tv_topk_workspace_size(T, G, V, dt, ctypes.byref(nbytes)))
+    ws = workspace(dev, nbytes.value)
+    with torch.cuda.device(dev):
+        check(lib.mtp_tv_topk_fwd(_ptr(target_idx), _ptr(target_val), k_pos, k_head, K, _ptr(draft),
+                                  draft.stride(0), draft.stride(1), dt, T, G, V, _ptr(loss), _ptr(pos_loss),
+                                  _ptr(saved), _ptr(ws), ws.numel(), _stream(dev)))
+    return loss, pos_loss, saved
+
+
+def tv_topk_bwd(target_idx, target_val, draft, saved, grad_loss, grad_dtype=None, out=None):
+    """Backward of the top-K TV loss (mtp_tv_topk_bwd): gradient w.r.t. the draft
+    logits, [T, gamma, V] in grad_dtype (default: the draft's dtype)."""
+    lib = load()
+    _require_cuda(target_idx, target_val, draft, saved, grad_loss)
+    T, G, V, K, k_pos, k_head = _topk_layout(target_idx, target_val, draft)
+    dev = draft.device
+    dt = _dtype_code(draft)
+    grad_dtype = grad_dtype or draft.dtype
+    if out is None:
+        out = torch.empty((T, G, V), dtype=grad_dtype, device=dev)
+    if out.stride(2) != 1 or tuple(out.shape) != (T, G, V):
+        raise ValueError("grad output must be [T, gamma, V] with unit stride along V")
+    gdt = _DTYPES[out.dtype]
+    saved = saved.contiguous()
+    grad_loss = grad_loss.reshape(1).to(torch.float32).contiguous()
+    with torch.cuda.device(dev):
+        check(lib.mtp_tv_topk_bwd(_ptr(target_idx), _ptr(target_val), k_pos, k_head, K, _ptr(draft),
+                                  draft.stride(0), draft.stride(1), dt, T, G, V, _ptr(saved), _ptr(grad_loss),
+                                  _ptr(out), out.stride(0), out.stride(1), gdt, _stream(dev)))
+    return out
+
+
+class TVTopKLoss(torch.autograd.Function):
+    """The end-to-end TV loss against top-K targets; gradient to the draft logits only."""
+
+    @staticmethod
+    def forward(ctx, draft, target_idx, target_val):
+        loss, _, saved = tv_topk_fwd(target_idx, target_val, draft.detach())
+        ctx.save_for_backward(draft.detach(), target_idx, target_val, saved)
+        return loss[0]
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        draft, idx, val, saved = ctx.saved_tensors
+        return tv_topk_bwd(idx, val, draft, saved, grad_out.reshape(1)), None, None
+
+
+def tv_topk_loss(draft, target_idx, target_val):
+    return TVTopKLoss.apply(draft, target_idx, target_val)
+
+
 def workspace_error(ws):
     """The error word of a workspace (non-zero after a bounded-wait timeout)."""
     lib = load()
