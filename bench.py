@@ -15,7 +15,8 @@ with Zipf-like logits; (`entropy_sweep`) verify on the 15 temperature x noise ce
 (128 sequences each), with each cell's acceptance rate, mean accepted length and
 mean target entropy; (`target_only`) target-only verify of the rollout workload;
 (`gumbel`) verify at temperature 0.7 with Gumbel-max row samples, and the
-Gumbel-max draft sampler on the rollout's draft rows.
+Gumbel-max draft sampler on the rollout's draft rows; (`tv_topk`) the TV loss
+forward + backward with top-K targets (K = 256) on the TV workload.
 
 `roofline` uses per-launch HIP events recorded on the stream the kernels run on;
 `cpu_baseline` times the float64 oracle on a bounded sample of the same workload.
@@ -140,11 +141,16 @@ def time_verify(mtp, torch, w, steps, warmup, nsets, target_only=False, temperat
     return wall, kernel_ms, plans
 
 
-def time_tv(mtp, torch, w, steps, warmup):
+def time_tv(mtp, torch, w, steps, warmup, topk=None):
     import synthetic
     dev = "cuda:0"
-    t, d = synthetic.tv_inputs(w, dev)
-    plan = mtp.TVPlan(t, d, grad_dtype=torch.bfloat16)
+    if topk:
+        i, v, d = synthetic.topk_inputs(w, topk, dev)
+        plan = mtp.TVTopKPlan(i, v, d, grad_dtype=torch.bfloat16)
+        t = (i, v)
+    else:
+        t, d = synthetic.tv_inputs(w, dev)
+        plan = mtp.TVPlan(t, d, grad_dtype=torch.bfloat16)
     check_waits(mtp, plan.ws)
     for _ in range(warmup):
         plan.forward()
@@ -327,6 +333,30 @@ def main():
         }
         log(f"tv loss: fwd {fm:.3f} ms ({fwd_bytes / fm / 1e6:.0f} GB/s), bwd {bm:.3f} ms "
             f"({bwd_bytes / bm / 1e6:.0f} GB/s), total {gbs:.0f} GB/s")
+
+    if not args.no_extra and not args.no_tv:
+        # the top-K path on the same workload: each position's target reduced to its
+        # 256 largest logits (indices + float32 values, shared by the heads)
+        tw = synthetic.TV_WORKLOADS["tv_loss"]
+        T, TG, TV, TK = tw["T"], tw["G"], tw["V"], 256
+        tv_steps = args.tv_steps or max(3, args.steps // 20)
+        log(f"tv loss top-K: T={T} gamma={TG} V={TV} K={TK} bf16, {tv_steps} steps")
+        kwall, kf, kb, kloss = time_tv(mtp, torch, tw, tv_steps, 2, topk=TK)
+        kfm, kbm = sum(kf) / len(kf), sum(kb) / len(kb)
+        kfb = T * TG * TV * 2 + T * TK * 8
+        kbb = 2 * T * TG * TV * 2 + T * TK * 8
+        kgbs = (kfb + kbb) / ((kfm + kbm) * 1e-3) / 1e9
+        result["tv_topk"] = {
+            "workload": "e2e TV loss fwd+bwd with top-K targets: T=8192 x gamma=3 heads, V=151936, K=256 target "
+                        "entries per position (the tv_loss workload's target reduced to its 256 largest logits), "
+                        "bf16 draft in, bf16 grad out",
+            "value": kgbs, "unit": "GB/s", "fwd_ms": kfm, "bwd_ms": kbm, "bytes_fwd": kfb, "bytes_bwd": kbb,
+            "fwd_gbs": kfb / (kfm * 1e-3) / 1e9, "bwd_gbs": kbb / (kbm * 1e-3) / 1e9, "loss": kloss,
+            "roofline": {"bound": "hbm", "achieved": kgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": kgbs / HBM_PEAK_GBS, "bytes_per_launch": kfb + kbb},
+        }
+        log(f"tv loss top-K: fwd {kfm:.3f} ms ({kfb / kfm / 1e6:.0f} GB/s), bwd {kbm:.3f} ms "
+            f"({kbb / kbm / 1e6:.0f} GB/s), total {kgbs:.0f} GB/s")
 
     if not args.no_extra:
         # target-only verify of the rollout workload (greedy draft tokens, the RS/TO flag)

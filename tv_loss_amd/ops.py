@@ -510,5 +510,42 @@ class TVPlan:
         return self.grad
 
 
-__all__ = ["verify", "tv_loss_fwd", "tv_loss_bwd", "tv_loss", "TVLoss", "MtpError", "workspace",
-           "workspace_error", "VerifyPlan", "TVPlan"]
+class TVTopKPlan:
+    """Forward and backward top-K TV-loss calls bound to fixed tensors (see VerifyPlan)."""
+
+    def __init__(self, target_idx, target_val, draft, grad_dtype=None):
+        self.lib = load()
+        T, G, V, K, k_pos, k_head = _topk_layout(target_idx, target_val, draft)
+        self.inputs = (target_idx, target_val, draft)
+        dev = draft.device
+        dt = _dtype_code(draft)
+        self.loss, self.pos_loss, self.saved = tv_topk_fwd(target_idx, target_val, draft)
+        self.grad_loss = torch.ones(1, dtype=torch.float32, device=dev)
+        self.grad = torch.empty((T, G, V), dtype=grad_dtype or draft.dtype, device=dev)
+        nbytes = ctypes.c_size_t()
+        check(self.lib.mtp_tv_topk_workspace_size(T, G, V, dt, ctypes.byref(nbytes)))
+        self.ws = workspace(dev, nbytes.value)
+        s = _stream(dev)
+        common = (_ptr(target_idx), _ptr(target_val), k_pos, k_head, K, _ptr(draft), draft.stride(0),
+                  draft.stride(1), dt, T, G, V)
+        self._fwd = common + (_ptr(self.loss), _ptr(self.pos_loss), _ptr(self.saved), _ptr(self.ws),
+                              self.ws.numel(), s)
+        self._bwd = common + (_ptr(self.saved), _ptr(self.grad_loss), _ptr(self.grad), self.grad.stride(0),
+                              self.grad.stride(1), _DTYPES[self.grad.dtype], s)
+
+    def forward(self):
+        st = self.lib.mtp_tv_topk_fwd(*self._fwd)
+        if st:
+            check(st)
+        return self.loss
+
+    def backward(self):
+        st = self.lib.mtp_tv_topk_bwd(*self._bwd)
+        if st:
+            check(st)
+        return self.grad
+
+
+__all__ = ["verify", "verify_target_only", "verify_gumbel", "gumbel_sample", "tv_loss_fwd", "tv_loss_bwd",
+           "tv_loss", "TVLoss", "tv_topk_fwd", "tv_topk_bwd", "tv_topk_loss", "TVTopKLoss", "MtpError",
+           "workspace", "workspace_error", "VerifyPlan", "TVPlan", "TVTopKPlan"]
