@@ -284,6 +284,8 @@ mtp_status verify_impl(int mode, float temperature, const void* target, int64_t 
   a.ngroups = (int)L.ngroups;
   a.sgroups = sgroups;
   a.layers = layers;
+  a.div_b = mtp::make_fastdiv((uint32_t)batch);
+  a.div_g1 = mtp::make_fastdiv((uint32_t)(gamma + 1));
   hipError_t e = mtp::launch_verify(a, dtype, mode, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MTP_ERR_LAUNCH, "verify launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -28,6 +28,29 @@ constexpr int kRowBadTarget = 2;
 constexpr int kRowBadDraft = 4;
 constexpr int kRowResidualEmpty = 8;
 
+// Division by a runtime-invariant d >= 1 for numerators 0 <= n < 2^31 with one
+// high multiply (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994): n / d = (mulhi(n, lo) + n hi) >> s.  For d >= 2,
+// s = ceil(log2 d) - 1 and lo = ceil(2^(32+s) / d) < 2^32, hi = 0; the error term
+// n (lo d - 2^(32+s)) < 2^31 d <= 2^(32+s) keeps the floor exact.  d = 1: lo = 0,
+// hi = 1, s = 0.
+struct FastDiv {
+  uint32_t lo, hi, s;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  if (d <= 1) return FastDiv{0u, 1u, 0u};
+  int l = 0;
+  while ((1ull << l) < d) ++l;
+  const uint32_t s = (uint32_t)(l - 1);
+  const uint64_t m = ((1ull << (32 + s)) + d - 1) / d;
+  return FastDiv{(uint32_t)m, 0u, s};
+}
+
+__device__ __forceinline__ int fast_div(int n, const FastDiv& f) {
+  return (int)((__umulhi((uint32_t)n, f.lo) + (uint32_t)n * f.hi) >> f.s);
+}
+
 struct VerifyArgs {
   const void* target; int64_t t_stride;   // row (b, k) of [B, G+1, V] at (b*(G+1)+k)*t_stride
   const void* draft;  int64_t d_stride;   // row (b, k) of [B, G, V]   at (b*G+k)*d_stride
@@ -49,6 +72,7 @@ struct VerifyArgs {
   RowSplit sp;
   int ngroups;
   int sgroups, layers;   // super-groups (all co-resident), groups per super-group
+  FastDiv div_b, div_g1; // division by B and by gamma + 1
 };
 
 // Verify modes: rejection sampling with inverse-CDF samples; target-only (greedy

@@ -206,15 +206,15 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
   const int nl = (a.ngroups - 1 - sg) / S + 1;
   auto group_of = [&](int i) {
     const int w = sg + i * S;
-    const int k = w / B;
+    const int k = fast_div(w, a.div_b);
     return (w - k * B) * G1 + k;
   };
-  auto is_pair = [&](int g) { return g % G1 < G; };
+  auto is_pair = [&](int g) { return g - fast_div(g, a.div_g1) * G1 < G; };
   auto trow_of = [&](int g) {
     return reinterpret_cast<const char*>(a.target) + (int64_t)g * a.t_stride * Elem<DT>::kBytes;
   };
   auto drow_of = [&](int g) {   // a bonus row has no draft row: its target row again
-    const int b = g / G1, k = g - b * G1;
+    const int b = fast_div(g, a.div_g1), k = g - b * G1;
     return k < G ? reinterpret_cast<const char*>(a.draft) + (int64_t)(b * G + k) * a.d_stride * Elem<DT>::kBytes
                  : trow_of(g);
   };
