@@ -105,6 +105,14 @@ mtp_status mtp_verify(const void* target, int64_t target_row_stride,
                       int32_t* row_status,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* The largest vocab that the verify entry points (all three) accept for dtype on
+ * the current device: every row is cut into chunks of 4096 (bfloat16) or 3072
+ * (float32) logits, one workgroup each, and all workgroups of a row must be
+ * resident on the GPU at once.  Larger vocabularies return MTP_ERR_SHAPE from the
+ * verify calls.  Queries the device (MTP_ERR_DEVICE without one).
+ */
+mtp_status mtp_verify_max_vocab(mtp_dtype dtype, int32_t* vocab);
+
 /* ------------------------------------------------------------------------ */
 /* Target-only verification with the rejection-sampling / target-only diagnostic
  * (paperlayer Sec. 2 "Preliminaries", acceptance methods; Sec. 7 "Discussion",

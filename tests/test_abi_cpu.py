@@ -230,6 +230,15 @@ def test_tv_topk_bwd_rejects_bad_arguments(kw, code):
     assert _topk_bwd(lib, **kw) == code, lib.mtp_last_error()
 
 
+def test_verify_max_vocab_arguments():
+    lib = tv_loss_amd.load()
+    v = ctypes.c_int32(-1)
+    assert lib.mtp_verify_max_vocab(1, None) == 1
+    assert lib.mtp_verify_max_vocab(7, ctypes.byref(v)) == 3
+    st = lib.mtp_verify_max_vocab(1, ctypes.byref(v))   # needs a device: MTP_ERR_DEVICE without one
+    assert st in (0, 6) and (st != 0 or v.value >= 4096)
+
+
 def test_tv_topk_workspace_size():
     lib = tv_loss_amd.load()
     n = ctypes.c_size_t()

@@ -191,3 +191,35 @@ def test_forward_is_deterministic_and_reuses_workspace():
             assert torch.equal(x, y)
     torch.cuda.synchronize()
     assert mtp.workspace_error(mtp.workspace(DEV, 1)) == 0
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_largest_vocabulary_closed_form(dtype):
+    """V = 2^30 (the largest the API takes; a float32 row spans 4 GiB), T = 1,
+    gamma = 1: a uniform target and a draft that is uniform but for its last logit,
+    a = 30 (so that a misread last element would change every statistic).  With
+    n = V - 1 + e^a: q_o = 1/n < 1/V < q_j = e^a/n, alpha = (V - 1)/n + 1/V,
+    S = (V - 1)/n, lse_p = ln V, lse_q = ln n, and the gradient (g = 1) is
+    -q_o (1 - S) off j and q_j S at j."""
+    V, a = 1 << 30, 30.0
+    j = V - 1
+    t = torch.zeros((1, V), dtype=dtype, device=DEV)
+    d = torch.zeros((1, 1, V), dtype=dtype, device=DEV)
+    d[0, 0, j] = a
+    _say("tv largest vocabulary", dtype)
+    loss, pos, saved = mtp.tv_loss_fwd(t, d)
+    g = mtp.tv_loss_bwd(t, d, saved, torch.ones(1, device=DEV), grad_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    n = (V - 1) + np.exp(a)
+    alpha, S = (V - 1) / n + 1 / V, (V - 1) / n
+    sv = saved[0, 0].double().cpu().numpy()
+    assert abs(sv[0] - np.log(V)) < 1e-6 * np.log(V)
+    assert abs(sv[1] - np.log(n)) < 1e-6 * np.log(n)
+    assert abs(sv[2] - alpha) < 1e-4 * alpha and abs(sv[3] - S) < 1e-4 * S
+    assert abs(loss.item() + alpha) < 1e-4 * alpha
+    qo, qj = 1 / n, np.exp(a) / n
+    for v, ref in ((0, -qo * (1 - S)), (j - 1, -qo * (1 - S)), (V // 2, -qo * (1 - S)), (j, qj * S)):
+        got = g[0, 0, v].double().item()
+        assert abs(got - ref) <= 2 ** -7 * abs(ref), (v, got, ref)
+    del t, d, g
+    torch.cuda.empty_cache()

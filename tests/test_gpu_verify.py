@@ -236,3 +236,23 @@ def test_chi_square_first_token_is_p():
     # and every sample equals the oracle's on a slice
     ref = oracle_verify(t[:2000], d[:2000], y[:2000], 2024, 0)
     compare_verify({k: v[:2000] for k, v in out.items()}, ref, torch.float32)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_largest_vocabulary(dtype):
+    """The largest vocabulary one GPU verifies (every workgroup of the row resident
+    at once), checked against the oracle; one vector more is refused."""
+    V = mtp.verify_max_vocab(dtype)
+    per = 4096 if dtype == torch.bfloat16 else 3072
+    assert V % per == 0 and V >= 256 * per
+    w = dict(B=1, G=1, V=V, dtype=dtype, kind="normal", scale=1.5, sigma=0.5, seed=21)
+    t, d, y = synthetic.verify_inputs(w, DEV, seed=21)
+    _say("verify largest vocabulary", V, dtype)
+    out = _run(t, d, y, seed=4, offset=0)
+    compare_verify(out, oracle_verify(t, d, y, 4, 0), dtype)
+    pv = 16 // t.element_size()
+    big = torch.zeros((1, 2, V + pv), dtype=dtype, device=DEV)
+    with pytest.raises(mtp.MtpError, match="MTP_ERR_SHAPE"):
+        mtp.verify(big, big[:, :1], torch.zeros((1, 1), dtype=torch.int32, device=DEV), 0)
+    with pytest.raises(mtp.MtpError, match="MTP_ERR_SHAPE"):
+        mtp.verify_gumbel(big, big[:, :1], torch.zeros((1, 1), dtype=torch.int32, device=DEV), 1.0, 0)

@@ -26,6 +26,7 @@ SIGNATURES = {
     "mtp_verify": (_c.c_int, [_P, _c.c_int64, _P, _c.c_int64, _c.c_int, _c.c_int32, _c.c_int32, _c.c_int32,
                               _P, _c.c_uint64, _c.c_uint64, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                               _c.c_size_t, _P]),
+    "mtp_verify_max_vocab": (_c.c_int, [_c.c_int, _c.POINTER(_c.c_int32)]),
     "mtp_verify_target_only_workspace_size": (_c.c_int, [_c.c_int32, _c.c_int32, _c.c_int32, _c.c_int,
                                                          _c.POINTER(_c.c_size_t)]),
     "mtp_verify_target_only": (_c.c_int, [_P, _c.c_int64, _P, _c.c_int64, _c.c_int, _c.c_int32, _c.c_int32,

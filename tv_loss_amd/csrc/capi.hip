@@ -211,6 +211,23 @@ mtp_status mtp_verify_target_only_workspace_size(int32_t batch, int32_t gamma, i
   return ok();
 }
 
+mtp_status mtp_verify_max_vocab(mtp_dtype dtype, int32_t* vocab) {
+  if (!vocab) return fail(MTP_ERR_NULL, "vocab is NULL");
+  if (dtype != MTP_F32 && dtype != MTP_BF16) return fail(MTP_ERR_DTYPE, "unknown dtype code %d", (int)dtype);
+  int64_t cap = INT64_MAX;
+  for (int mode : {mtp::kVerifyRejection, mtp::kVerifyTargetOnly, mtp::kVerifyGumbel}) {
+    int64_t per_gpu = 0;
+    mtp_status s = verify_capacity(dtype, mode, &per_gpu);
+    if (s) return s;
+    cap = per_gpu < cap ? per_gpu : cap;
+  }
+  // every chunk holds kBlock * vec_per_thread vectors; the last may be partial
+  const int64_t per_chunk = (int64_t)mtp::kBlock * mtp::verify_vec_per_thread(dtype) * per_vec(dtype);
+  const int64_t v = cap * per_chunk;
+  *vocab = (int32_t)(v < kMaxVocab ? v : kMaxVocab);
+  return ok();
+}
+
 mtp_status mtp_verify_gumbel_workspace_size(int32_t batch, int32_t gamma, int32_t vocab, mtp_dtype dtype,
                                             size_t* bytes) {
   if (!bytes) return fail(MTP_ERR_NULL, "bytes is NULL");

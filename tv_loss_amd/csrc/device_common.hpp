@@ -593,18 +593,24 @@ __device__ __forceinline__ Lse merge_lds(const float* p) {
 // Streaming loads: non-temporal (each logit is read once).
 constexpr int kStreamCpol = 2;
 
+// v0 = the wave's first vector + lane.  The descriptors start at the wave's first
+// vector, so byte offsets stay within the segment for rows of any length (a row
+// may exceed the 2^31 bytes one descriptor spans); a vector clamped below that
+// start gives a negative offset, which the descriptor's bound turns into zeros.
 template <int DT, int NV, int R>
 __device__ __forceinline__ void issue_seg(RawChunk<NV, R>& raw, const char* const (&rows)[R], int v0, int last,
                                           int nrows = R) {
   if (last >= 0) {
+    const int vb = __builtin_amdgcn_readfirstlane(v0 - (int)(threadIdx.x & 63));
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      const int off = min(v0 + j * 64, last) * 16;
+      const int off = (min(v0 + j * 64, last) - vb) * 16;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         if (r >= nrows) break;
         raw.v[r][j] = __builtin_amdgcn_raw_buffer_load_b128(
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(rows[r]), 0, 0x7fffffff, 0x00020000), off, 0, kStreamCpol);
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(rows[r]) + (int64_t)vb * 16, 0, 0x7fffffff, 0x00020000),
+            off, 0, kStreamCpol);
       }
     }
   } else {

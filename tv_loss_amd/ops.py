@@ -107,6 +107,16 @@ def verify(target, draft, draft_tokens, seed, offset=0, *, stats=True):
     return out
 
 
+def verify_max_vocab(dtype, device=0):
+    """The largest vocabulary the verify calls accept for `dtype` on `device`
+    (mtp_verify_max_vocab)."""
+    lib = load()
+    v = ctypes.c_int32()
+    with torch.cuda.device(device):
+        check(lib.mtp_verify_max_vocab(_DTYPES[dtype], ctypes.byref(v)))
+    return v.value
+
+
 def verify_target_only(target, draft, seed, offset=0, *, stats=True):
     """Target-only verification with the RS/TO diagnostic (see
     mtp_verify_target_only in include/mtp.h): every draft position proposes its
@@ -546,6 +556,6 @@ class TVTopKPlan:
         return self.grad
 
 
-__all__ = ["verify", "verify_target_only", "verify_gumbel", "gumbel_sample", "tv_loss_fwd", "tv_loss_bwd",
+__all__ = ["verify", "verify_max_vocab", "verify_target_only", "verify_gumbel", "gumbel_sample", "tv_loss_fwd", "tv_loss_bwd",
            "tv_loss", "TVLoss", "tv_topk_fwd", "tv_topk_bwd", "tv_topk_loss", "TVTopKLoss", "MtpError",
            "workspace", "workspace_error", "VerifyPlan", "TVPlan", "TVTopKPlan"]
