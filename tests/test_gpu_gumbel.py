@@ -2,7 +2,7 @@
 
 Cases follow the other verify tests: the tiny float32 workload at three
 temperatures; ragged vocabularies (both dtypes, gamma up to 8); float32 rows of
-more than 64 chunks; every row of a rollout-shaped batch with draft tokens from
+more than 64 chunks; every row of the rollout workload with draft tokens from
 the GPU sampler; sampled sequences of the long-tail workload; temperature 1
 against the plain verify's flags and statistics; edge cases (p = q, a wave where
 q outweighs p by more than 2^64, bad rows); workspace reuse across the three
@@ -104,12 +104,12 @@ def test_many_chunks_float32():
     compare_verify(out, _oracle(t, d, y, 1.3, 10, 40), torch.float32)
 
 
-def test_rollout_shape_all_rows_with_gpu_draft_tokens():
+def test_rollout_all_rows_with_gpu_draft_tokens():
     """Draft tokens from the GPU sampler at T (its own counter range), then the
     tempered verify; both against the oracle on every row."""
     w = synthetic.VERIFY_WORKLOADS["rollout"]
     T = 0.7
-    t, d, _ = synthetic.verify_inputs(w, DEV, B=24)
+    t, d, _ = synthetic.verify_inputs(w, DEV)          # the full bench batch: 64 x (3 + 1) rows
     B, G = d.shape[0], d.shape[1]
     _say("gm rollout shape")
     y = mtp.gumbel_sample(d, T, seed=41, offset=1 << 40)

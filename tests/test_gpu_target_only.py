@@ -2,7 +2,7 @@
 
 Sizes and cases follow the rejection-sampling verify tests: the tiny float32
 workload; ragged vocabularies around vector and chunk boundaries (both dtypes,
-gamma up to 8); float32 rows of more than 64 chunks; every row of a rollout-shaped
+gamma up to 8); float32 rows of more than 64 chunks; every row of the rollout
 batch; sampled sequences of the long-tail workload; edge cases (equal maxima of q
 in different chunks and in the partial last vector, a one-hot target, bad rows);
 workspace reuse alternating with rejection-sampling calls; position-addressed
@@ -84,9 +84,9 @@ def test_many_chunks_float32():
     compare_target_only(out, oracle_target_only(t, d, 9, 17), torch.float32)
 
 
-def test_rollout_shape_all_rows():
+def test_rollout_all_rows():
     w = synthetic.VERIFY_WORKLOADS["rollout"]
-    t, d, _ = synthetic.verify_inputs(w, DEV, B=24)
+    t, d, _ = synthetic.verify_inputs(w, DEV)          # the full bench batch: 64 x (3 + 1) rows
     _say("to rollout shape")
     out = _run(t, d, seed=2, offset=0)
     ref = oracle_target_only(t, d, 2, 0)
