@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "draft positions verified/sec at V=151936, γ=3; TV fwd+bwd GB/s vs HBM peak"
 HBM_PEAK_GBS = 8000.0
+EXTRAS = ("tv_topk", "target_only", "gumbel", "long_tail", "entropy_sweep", "stream_context")
 
 
 def log(*a):
@@ -244,11 +245,16 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-tv", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the long-tail and entropy-sweep verify lines")
+    ap.add_argument("--no-extra", action="store_true", help="only the headline lines (rollout verify, TV loss)")
+    ap.add_argument("--extra", default=",".join(EXTRAS),
+                    help=f"comma-separated extra lines to run (default: all of {','.join(EXTRAS)})")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="after the bench, copy BYTES of device memory three times with torch (a plain copy "
                          "kernel of known size, to calibrate HBM byte counters)")
     args = ap.parse_args()
+    extras = set() if args.no_extra else {e for e in args.extra.split(",") if e}
+    if extras - set(EXTRAS):
+        ap.error(f"unknown extra lines: {sorted(extras - set(EXTRAS))}")
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this hot path is data-parallel and every run here uses a "
@@ -334,7 +340,7 @@ def main():
         log(f"tv loss: fwd {fm:.3f} ms ({fwd_bytes / fm / 1e6:.0f} GB/s), bwd {bm:.3f} ms "
             f"({bwd_bytes / bm / 1e6:.0f} GB/s), total {gbs:.0f} GB/s")
 
-    if not args.no_extra and not args.no_tv:
+    if "tv_topk" in extras:
         # the top-K path on the same workload: each position's target reduced to its
         # 256 largest logits (indices + float32 values, shared by the heads)
         tw = synthetic.TV_WORKLOADS["tv_loss"]
@@ -358,7 +364,7 @@ def main():
         log(f"tv loss top-K: fwd {kfm:.3f} ms ({kfb / kfm / 1e6:.0f} GB/s), bwd {kbm:.3f} ms "
             f"({kbb / kbm / 1e6:.0f} GB/s), total {kgbs:.0f} GB/s")
 
-    if not args.no_extra:
+    if "target_only" in extras:
         # target-only verify of the rollout workload (greedy draft tokens, the RS/TO flag)
         log("verify: target-only on the rollout workload")
         owall, okms, plans = time_verify(mtp, torch, w, args.steps, args.warmup, nsets, target_only=True)
@@ -378,6 +384,7 @@ def main():
         }
         log(f"verify target-only: {omean * 1e3:.2f} us per call, accept rate {to_acc:.3f}, "
             f"RS better on {rs_share:.3f} of positions")
+    if "gumbel" in extras:
         # rejection sampling at temperature 0.7 with Gumbel-max row samples, and the
         # Gumbel-max draft sampler on the rollout's draft rows
         log("verify: Gumbel-max at T=0.7 on the rollout workload")
@@ -412,8 +419,10 @@ def main():
         }
         log(f"verify Gumbel-max: {gmean * 1e3:.2f} us per call, accept rate {g_acc:.3f}; sampler "
             f"{smean * 1e3:.2f} us per call ({sbytes / smean / 1e6:.0f} GB/s)")
-        # the long-tail workload (Zipf-like logits, V = 2^18, gamma = 4) and the 15
-        # cells of the entropy sweep, each timed like the rollout workload
+
+    if "long_tail" in extras:
+        # the long-tail workload (Zipf-like logits, V = 2^18, gamma = 4), timed like
+        # the rollout workload
         lw = synthetic.VERIFY_WORKLOADS["long_tail"]
         lsteps = max(5, args.steps // 10)
         log(f"verify: long-tail workload B={lw['B']} gamma={lw['G']} V={lw['V']} bf16, {lsteps} steps")
@@ -433,6 +442,9 @@ def main():
         }
         log(f"verify long tail: {lpos / lmean / 1e3:.3f} M positions/s, {lmean * 1e3:.1f} us per call, "
             f"{lbytes / lmean / 1e6:.0f} GB/s")
+
+    if "entropy_sweep" in extras:
+        # the 15 cells of the entropy sweep
         cells = []
         for it in range(len(synthetic.SWEEP_TAUS)):
             for isg in range(len(synthetic.SWEEP_SIGMAS)):
@@ -472,7 +484,7 @@ def main():
         }
         log(f"cpu oracle: {n * G / cwall:.1f} positions/s on one core")
 
-    if not args.no_extra:
+    if "stream_context" in extras:
         ctx = stream_context(torch)
         result["roofline"]["stream_context"] = ctx
         log(f"stream context: torch copy {ctx['copy_gbs']:.0f} GB/s, torch float32 sum {ctx['read_sum_gbs']:.0f} GB/s")
