@@ -130,15 +130,21 @@ def time_verify(mtp, torch, w, steps, warmup, nsets, target_only=False, temperat
         plans[i % nsets].run(seed=w["seed"], offset=i * rows)
     torch.cuda.synchronize()
     check_waits(mtp, plans[0].ws)
+    # per-call GPU times: events around every call
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    t0 = time.perf_counter()
     for i in range(steps):
         evs[i][0].record()
         plans[i % nsets].run(seed=w["seed"], offset=(warmup + i) * rows)
         evs[i][1].record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     kernel_ms = [a.elapsed_time(b) for a, b in evs]
+    # throughput: the same calls back to back, without the event records in between
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        plans[i % nsets].run(seed=w["seed"], offset=(warmup + steps + i) * rows)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
     return wall, kernel_ms, plans
 
 
