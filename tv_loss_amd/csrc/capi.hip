@@ -58,15 +58,16 @@ mtp_status check_row_base(const void* p, int64_t stride_elems, mtp_dtype dt, con
 // ---- per-device limits --------------------------------------------------------
 struct DeviceInfo {
   int cus = 0;
-  std::map<int, int> occ;   // (dtype, verify mode) -> verify main workgroups per CU
+  std::map<int, int> occ;   // kernel key -> workgroups per CU
 };
 std::mutex g_dev_mu;
 std::map<int, DeviceInfo> g_dev;
 
-// Workgroups of the verify main kernel the current device holds at once: all of a
-// launch's workgroups must be resident together (a super-group waits on its
-// members' records).
-mtp_status verify_capacity(int dt, int mode, int64_t* per_gpu) {
+// Workgroups of a persistent kernel the current device holds at once (all of a
+// launch's workgroups must be resident together: a super-group waits on its
+// members' records), from the kernel's occupancy, cached per device and key.
+template <typename Occ>
+mtp_status capacity(int key, Occ occupancy, int64_t* per_gpu) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(MTP_ERR_DEVICE, "hipGetDevice failed");
   std::lock_guard<std::mutex> lk(g_dev_mu);
@@ -75,16 +76,24 @@ mtp_status verify_capacity(int dt, int mode, int64_t* per_gpu) {
     if (hipDeviceGetAttribute(&info.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return fail(MTP_ERR_DEVICE, "cannot query the compute-unit count");
   }
-  const int key = dt * 4 + mode;
   auto it = info.occ.find(key);
   if (it == info.occ.end()) {
     int n = 0;
-    hipError_t e = mtp::verify_occupancy(dt, mode, &n);
+    hipError_t e = occupancy(&n);
     if (e != hipSuccess || n < 1) return fail(MTP_ERR_DEVICE, "occupancy query failed");
     it = info.occ.emplace(key, n).first;
   }
   *per_gpu = (int64_t)it->second * info.cus;
   return MTP_OK;
+}
+
+mtp_status verify_capacity(int dt, int mode, int64_t* per_gpu) {
+  return capacity(dt * 4 + mode, [&](int* n) { return mtp::verify_occupancy(dt, mode, n); }, per_gpu);
+}
+
+mtp_status tv_pipe_capacity(int dt, int G, bool shared, int64_t* per_gpu) {
+  return capacity(1000 + dt * 64 + G * 2 + (shared ? 1 : 0),
+                  [&](int* n) { return mtp::tv_pipe_occupancy(dt, G, shared, n); }, per_gpu);
 }
 
 // ---- workspace layouts --------------------------------------------------------
@@ -116,9 +125,14 @@ struct TvLayout {
   mtp::RowSplit sp;
 };
 
-TvLayout tv_layout(int32_t T, int32_t G, int32_t V, mtp_dtype dt, bool shared) {
+// The forward's workspace: error word, part1 (two passes: (ref, z) float2 per
+// [t][chunk][row]; single read: one record word per [t][chunk][row]), part2
+// [t][chunk][2 gamma] floats, per-position losses [t].  `pipe` picks the single-read
+// forward's chunking.
+TvLayout tv_layout(int32_t T, int32_t G, int32_t V, mtp_dtype dt, bool shared, bool pipe) {
   TvLayout L{};
-  L.sp = mtp::make_split(V, per_vec(dt), mtp::tv_fwd_vec_per_thread(dt, G, shared), false);
+  const int nv = pipe ? mtp::tv_pipe_vec_per_thread(dt, G, shared) : mtp::tv_fwd_vec_per_thread(dt, G, shared);
+  L.sp = mtp::make_split(V, per_vec(dt), nv, false);
   const int64_t C = L.sp.nchunks;
   size_t off = 0;
   L.err = off; off = align256(off + 4);
@@ -127,6 +141,17 @@ TvLayout tv_layout(int32_t T, int32_t G, int32_t V, mtp_dtype dt, bool shared) {
   L.pos = off; off = align256(off + (size_t)T * 4);
   L.total = off;
   return L;
+}
+
+// Bytes a forward call may need: the larger of the two layouts (which forward runs
+// also depends on the device's co-residency).
+size_t tv_workspace_bytes(int32_t T, int32_t G, int32_t V, mtp_dtype dt, bool shared) {
+  size_t b = tv_layout(T, G, V, dt, shared, false).total;
+  if (mtp::tv_pipe_vec_per_thread(dt, G, shared) > 0) {
+    const size_t p = tv_layout(T, G, V, dt, shared, true).total;
+    b = p > b ? p : b;
+  }
+  return b;
 }
 
 // top-K path: error word, draft log-sum-exp partials [t][chunk][gamma] as float2,
@@ -387,7 +412,7 @@ mtp_status mtp_tv_loss_workspace_size(int32_t T, int32_t gamma, int32_t vocab, m
   mtp_status s = check_common(dtype, gamma, vocab);
   if (s) return s;
   if (T < 1) return fail(MTP_ERR_SHAPE, "T = %d must be >= 1", T);
-  *bytes = tv_layout(T, gamma, vocab, dtype, shared_target != 0).total;
+  *bytes = tv_workspace_bytes(T, gamma, vocab, dtype, shared_target != 0);
   return ok();
 }
 
@@ -415,8 +440,21 @@ mtp_status mtp_tv_loss_fwd(const void* target, int64_t target_pos_stride, int64_
   if (s) return s;
   if (!loss || !saved) return fail(MTP_ERR_NULL, "loss or saved is NULL");
   const bool shared = target_head_stride == 0;
-  const TvLayout L = tv_layout(T, gamma, vocab, dtype, shared);
-  if ((s = check_workspace(workspace, workspace_bytes, L.total))) return s;
+  if ((s = check_workspace(workspace, workspace_bytes, tv_workspace_bytes(T, gamma, vocab, dtype, shared)))) return s;
+  // the single-read forward when a position's rows fit it and every chunk of a row
+  // can be resident at once; otherwise the two streaming passes
+  bool pipe = false;
+  int sgroups = 0, layers = 0;
+  if (mtp::tv_pipe_vec_per_thread(dtype, gamma, shared) > 0) {
+    int64_t per_gpu = 0;
+    if ((s = tv_pipe_capacity(dtype, gamma, shared, &per_gpu))) return s;
+    const TvLayout Lp = tv_layout(T, gamma, vocab, dtype, shared, true);
+    if ((int64_t)Lp.sp.nchunks <= per_gpu) {
+      pipe = true;
+      plan_layers(per_gpu, Lp.sp.nchunks, T, &sgroups, &layers);
+    }
+  }
+  const TvLayout L = tv_layout(T, gamma, vocab, dtype, shared, pipe);
   if ((int64_t)T * L.sp.nchunks > 0x7fffffffLL) return fail(MTP_ERR_SHAPE, "T * chunks is too large");
   mtp::TvArgs a{};
   a.target = target; a.t_pos = target_pos_stride; a.t_head = target_head_stride;
@@ -428,7 +466,9 @@ mtp_status mtp_tv_loss_fwd(const void* target, int64_t target_pos_stride, int64_
   a.part2 = at<float>(workspace, L.part2);
   a.pos_ws = at<float>(workspace, L.pos);
   a.sp = L.sp;
-  hipError_t e = mtp::launch_tv_fwd(a, dtype, shared, (hipStream_t)stream);
+  a.sgroups = sgroups;
+  hipError_t e = pipe ? mtp::launch_tv_pipe_fwd(a, dtype, shared, (hipStream_t)stream)
+                      : mtp::launch_tv_fwd(a, dtype, shared, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MTP_ERR_LAUNCH, "TV forward launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -532,7 +572,7 @@ mtp_status mtp_tv_loss_bwd(const void* target, int64_t target_pos_stride, int64_
   a.T = T; a.G = gamma; a.V = vocab;
   a.saved_in = saved; a.grad_loss = grad_loss;
   a.grad = grad; a.g_pos = grad_pos_stride; a.g_head = grad_head_stride; a.grad_dt = grad_dtype;
-  a.sp = mtp::make_split(vocab, per_vec(dtype), mtp::tv_bwd_vec_per_thread(dtype));
+  a.sp = mtp::make_split(vocab, per_vec(dtype), mtp::tv_bwd_full_vec_per_thread(dtype, gamma, shared));
   if ((int64_t)T * a.sp.nchunks > 0x7fffffffLL) return fail(MTP_ERR_SHAPE, "T * chunks is too large");
   hipError_t e = mtp::launch_tv_bwd(a, dtype, shared, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MTP_ERR_LAUNCH, "TV backward launch failed: %s", hipGetErrorString(e));

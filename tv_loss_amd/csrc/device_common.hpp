@@ -716,6 +716,49 @@ __device__ __forceinline__ void rec_store(__amdgpu_buffer_rsrc_t r, int byte_off
   __builtin_amdgcn_raw_buffer_store_b64(v, r, byte_off, 0, kRecCpol);
 }
 
+// Wait until word `word` of every record of a row is published (non-zero):
+// `v` is this lane's word of record `lane`, loaded earlier, and lanes still seeing
+// zero load again; records past the first 64 are loaded here.  `merge` folds each
+// lane's words in record order (first record, then l + 64, ...).  Bounded by the
+// spin limit (a timeout sets the error word and carries on).
+template <typename Fold>
+__device__ __forceinline__ void poll_words(uint64_t v, __amdgpu_buffer_rsrc_t rs, int C, int st, int word,
+                                           uint32_t* err, Fold fold) {
+  const int lane = threadIdx.x & 63;
+  uint64_t t0 = 0;
+  for (int c0 = 0; c0 < C; c0 += 64) {
+    const int c = c0 + lane;
+    if (c0 > 0 && c < C) v = rec_load(rs, c * st + word * 8);
+    bool ready = !(c < C) || v != 0ull;
+    while (__ballot(!ready) != 0ull) {
+      if (t0 == 0) t0 = __builtin_amdgcn_s_memrealtime();
+      __builtin_amdgcn_s_sleep(1);
+      if (!ready) {
+        v = rec_load(rs, c * st + word * 8);
+        ready = v != 0ull;
+      }
+      if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimitTicks) {
+        if (lane == 0) __hip_atomic_fetch_or(err, kErrSyncTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+    if (c < C) fold(c0 == 0, v);
+  }
+}
+
+// The row's merged log-sum-exp (no entropy moment) from word `word` of the records.
+__device__ __forceinline__ Lse poll_row(uint64_t v, __amdgpu_buffer_rsrc_t rs, int C, int st, int word,
+                                        uint32_t* err) {
+  Lse acc = lse_empty();
+  poll_words(v, rs, C, st, word, err, [&](bool first, uint64_t w) {
+    const Lse r{unpack_lo(w), unmark(unpack_hi(w)), 0.f};
+    acc = first ? r : lse_merge(acc, r);
+  });
+  Lse a[1] = {acc};
+  wave_merge<1, 0>(a);
+  return a[0];
+}
+
 // ---------------------------------------------------------------------------
 // Philox4x32-10: ten rounds of the Philox S-box on four 32-bit words with a
 // two-word key advanced by the Weyl increments between rounds.

@@ -111,6 +111,7 @@ struct TvArgs {
   // (ref, z), overlap and S partials [t][chunk][2 gamma], per-position losses [t]
   uint32_t* err; uint64_t* part1; float* part2; float* pos_ws;
   RowSplit sp;
+  int sgroups;   // single-read forward: super-groups of sp.nchunks workgroups, all resident
   // top-K path: the target of head k at position t is given by K entries, indices
   // idx and logits val at t*k_pos + k*k_head + j (k_head = 0: shared by the heads)
   const int32_t* idx; const float* val; int64_t k_pos, k_head; int K;
@@ -122,7 +123,16 @@ constexpr int kTvMaxHeads = 8;
 int tv_fwd_vec_per_thread(int dt, int G, bool shared);
 int tv_fwd_part1_words(int G, bool shared);
 hipError_t launch_tv_fwd(const TvArgs& a, int dt, bool shared, hipStream_t stream);
-int tv_bwd_vec_per_thread(int dt);
+// single-read forward (rows held on chip between the two passes): applies when a
+// position has at most kTvPipeMaxRows rows; vectors per thread and row (0: does not
+// apply), main-kernel workgroups per CU, launch (main, finish, mean).  The workspace
+// holds the records part1 [t][chunk][rows] (64-bit words) and part2 [t][chunk][2 gamma].
+constexpr int kTvPipeMaxRows = 5;
+int tv_pipe_vec_per_thread(int dt, int G, bool shared);
+hipError_t tv_pipe_occupancy(int dt, int G, bool shared, int* blocks_per_cu);
+hipError_t launch_tv_pipe_fwd(const TvArgs& a, int dt, bool shared, hipStream_t stream);
+int tv_bwd_vec_per_thread(int dt);   // top-K backward
+int tv_bwd_full_vec_per_thread(int dt, int G, bool shared);
 hipError_t launch_tv_bwd(const TvArgs& a, int dt, bool shared, hipStream_t stream);
 // top-K path: forward (draft log-sum-exp partials, per-position finish over the K
 // entries, mean) and backward; the workspace holds part1 [t][chunk][gamma] and pos_ws

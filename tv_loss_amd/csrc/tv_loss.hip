@@ -236,6 +236,303 @@ __global__ __launch_bounds__(kBlock) void tv_fwd_mean(TvArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Single-read forward.  The two passes above read every logit twice; this path
+// reads it once.  Super-groups of C workgroups, all resident at once, walk their
+// positions t = sg, sg + S, ... in layers; workgroup c of a super-group takes chunk
+// c of every row of each of its positions, and each wave owns a contiguous segment
+// of the chunk.  Layer i:
+//   * the records of position i - 2 (polled a layer ago) give each row's base-2
+//     log-sum-exp; every wave forms the overlap and S partials of every head over
+//     its segment from the e values it holds in LDS;
+//   * the e values of position i - 1 move from registers to LDS;
+//   * the chunk of position i is unpacked (its loads went out two layers ago), the
+//     poll of position i - 1's records and the loads of position i + 2 go out;
+//   * pass 1 of position i: per-wave log-sum-exp partials of every row, merged over
+//     the workgroup and published as one self-announcing record word per row;
+//     the waves' overlap and S partials of position i - 2 are added up and stored.
+// In a wave's own units p = sa e_p and q = sb e_q (e <= 1, taken against the wave's
+// largest logit of the row).  For head k, with rho = sb / sa <= 1:
+//   min(p, q) = sa min(e_p, rho e_q),  1[q <= p] q = sa 1[rho e_q <= e_p] rho e_q,
+// and with rho > 1 the same in q's units (sb, e_q and e_p / rho), so no scale
+// overflows.  tv_pipe_finish (one wave per position) merges the records in the
+// order the poll used, sums the partials, writes the saved statistics and l_t, and
+// clears what it read.  Record words: (ref, z with the sign bit set), never zero.
+constexpr int kPipeFloats = 64;   // logits per thread and position (all rows) in flight
+
+template <int NR>
+constexpr int pipe_nv(int per_vec) {
+  const int nv = kPipeFloats / (NR * per_vec);
+  return nv < 1 ? 1 : nv;
+}
+
+template <int G, bool SHARED>
+constexpr bool pipe_fits() { return FwdShape<G, SHARED>::NR <= kTvPipeMaxRows; }
+
+template <int DT, int G, bool SHARED>
+__global__ __launch_bounds__(kBlock) void tv_pipe_main(TvArgs a) {
+  constexpr int NT = FwdShape<G, SHARED>::NT;
+  constexpr int NR = FwdShape<G, SHARED>::NR;
+  constexpr int PV = Elem<DT>::kPerVec;
+  constexpr int NV = pipe_nv<NR>(PV);
+  constexpr int NE = NV * PV;
+  constexpr int NQ = NE / 4;                       // 16-byte LDS slots per row and thread
+  constexpr int kSegVec = NV * 64;
+  constexpr int RW = (NR + kWaves - 1) / kWaves;   // rows whose records one wave polls / publishes
+  constexpr int kSt = NR * 8;                      // record stride (bytes) per chunk
+  const int C = a.sp.nchunks;
+  const int slot = blockIdx.x;
+  const int sg = slot / C, c = slot - sg * C;
+  const int S = a.sgroups;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  if (sg >= a.T) return;
+  const int nl = (a.T - 1 - sg) / S + 1;
+  auto pos_of = [&](int i) { return sg + i * S; };
+  auto rsrc_rec = [&](int t) { return rsrc_of(a.part1 + (int64_t)t * C * NR); };
+
+  const int vpc = (int)a.sp.vec_per_chunk, nvec = (int)a.sp.nvec, nfull = (int)a.sp.nvec_full;
+  const int vbeg = c * vpc;
+  const int vend = min(vbeg + vpc, nvec);
+  const int s0 = vbeg + wave * kSegVec;
+  const int v0 = s0 + lane;
+  const int lim = min(vend, nfull);
+  const bool full = s0 + kSegVec <= lim;
+  const int last = nfull - 1;
+  const int tail = nfull;
+  const int V = (int)a.V;
+  const int row_bytes = (int)min(a.V * Elem<DT>::kBytes, (int64_t)0x7fffffff);
+
+  __shared__ float4 held[NR][NQ][kBlock];      // e values of the position two layers back
+  __shared__ float part_sh[2][NR][kWaves * 3];  // pass-1 wave partials, by layer parity
+  __shared__ float lse_sh[2][NR];               // row log2-sum-exps of the position in pass 2
+  __shared__ float acc_sh[2][kWaves][2 * G];    // pass-2 wave partials (overlap, S per head)
+
+  auto prefetch = [&](RawChunk<NV, NR>& rb, int t, bool live) {
+    const char* rows[NR];
+    fwd_rows<DT, NT, G>(a, t, rows);
+    issue_seg_fixed<DT, NV, NR>(rb, rows, v0, last, live, row_bytes);
+  };
+  RawChunk<NV, NR> rawA, rawB;
+  int t_0 = pos_of(0), t_p1 = nl > 1 ? pos_of(1) : t_0;
+  prefetch(rawA, t_0, true);
+  prefetch(rawB, t_p1, nl > 1);
+  int t_m2 = 0, t_m1 = 0;
+  uint64_t wpoll[RW];
+#pragma unroll
+  for (int j = 0; j < RW; ++j) wpoll[j] = 0ull;
+  float x[NR][NE];
+  float xref[NR], href[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) xref[r] = href[r] = 0.f;
+
+  auto layer = [&](int i, RawChunk<NV, NR>& rb) __attribute__((always_inline)) {
+    const int par = i & 1;
+    const bool do2 = i >= 2 && i - 2 < nl;
+    // ---- row statistics of position i - 2 (polled a layer ago) ---------------
+    if (do2) {
+#pragma unroll
+      for (int j = 0; j < RW; ++j) {
+        const int r = wave + j * kWaves;
+        if (r < NR) {
+          __builtin_amdgcn_s_setprio(3);
+          const Lse st = poll_row(wpoll[j], rsrc_rec(t_m2), C, kSt, r, a.err);
+          if (lane == 0) lse_sh[par][r] = lse_log2(st);
+          __builtin_amdgcn_s_setprio(0);
+        }
+      }
+      __syncthreads();
+      // ---- pass 2 of position i - 2: overlap and S partials of every head ----
+      float res[2 * G];
+#pragma unroll
+      for (int k = 0; k < G; ++k) {
+        const int rt = SHARED ? 0 : k, rq = NT + k;
+        const float la = href[rt] - lse_sh[par][rt];   // log2 sa (-inf: no p mass here)
+        const float lb = href[rq] - lse_sh[par][rq];   // log2 sb
+        const float lr = lb - la;
+        float al0 = 0.f, al1 = 0.f, s0_ = 0.f, s1_ = 0.f, scale = 0.f;
+        if (la == kNegInf || lb == kNegInf) {
+          scale = 0.f;                                   // one of p, q has no mass here
+        } else if (lr <= 0.f) {                          // p units
+          const float rho = fast_exp2(lr);
+          scale = fast_exp2(la);
+#pragma unroll
+          for (int qi = 0; qi < NQ; ++qi) {
+            const float4 ep4 = held[rt][qi][tid], eq4 = held[rq][qi][tid];
+            const float ep[4] = {ep4.x, ep4.y, ep4.z, ep4.w}, eq[4] = {eq4.x, eq4.y, eq4.z, eq4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float tq = rho * eq[e];
+              const float m = __builtin_elementwise_minimum(ep[e], tq);
+              const float sv = tq <= ep[e] ? tq : 0.f;
+              if (e & 1) { al1 += m; s1_ += sv; } else { al0 += m; s0_ += sv; }
+            }
+          }
+        } else if (lr > 0.f) {                           // q units
+          const float rho = fast_exp2(-lr);
+          scale = fast_exp2(lb);
+#pragma unroll
+          for (int qi = 0; qi < NQ; ++qi) {
+            const float4 ep4 = held[rt][qi][tid], eq4 = held[rq][qi][tid];
+            const float ep[4] = {ep4.x, ep4.y, ep4.z, ep4.w}, eq[4] = {eq4.x, eq4.y, eq4.z, eq4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float tp = rho * ep[e];
+              const float m = __builtin_elementwise_minimum(tp, eq[e]);
+              const float sv = eq[e] <= tp ? eq[e] : 0.f;
+              if (e & 1) { al1 += m; s1_ += sv; } else { al0 += m; s0_ += sv; }
+            }
+          }
+        } else {
+          scale = __builtin_nanf("");                    // a NaN statistic propagates
+        }
+        res[2 * k] = (al0 + al1) * scale;
+        res[2 * k + 1] = (s0_ + s1_) * scale;
+      }
+      wave_reduce<false, 2 * G>(res);
+      if (lane == 0) {
+#pragma unroll
+        for (int k = 0; k < 2 * G; ++k) acc_sh[par][wave][k] = res[k];
+      }
+    }
+    // ---- position i - 1 moves to LDS (own slots only) --------------------------
+    if (i >= 1 && i - 1 < nl) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+#pragma unroll
+        for (int qi = 0; qi < NQ; ++qi)
+          held[r][qi][tid] = make_float4(x[r][4 * qi], x[r][4 * qi + 1], x[r][4 * qi + 2], x[r][4 * qi + 3]);
+        href[r] = xref[r];
+      }
+    }
+    // ---- position i: unpack, then the poll for i - 1 and the loads of i + 2 ------
+    if (i < nl) {
+      const char* rows[NR];
+      fwd_rows<DT, NT, G>(a, t_0, rows);
+      int lim_l = lim, tail_l = tail, vend_l = vend, V_l = V;
+      asm volatile("" : "+s"(lim_l), "+s"(tail_l), "+s"(vend_l), "+s"(V_l));
+      unpack_seg<DT, NV, NR>(rb, rows, v0, full, lim_l, tail_l, vend_l, V_l, x);
+    }
+    if (i >= 1 && i <= nl && lane < C) {
+      const __amdgpu_buffer_rsrc_t rs = rsrc_rec(t_m1);
+#pragma unroll
+      for (int j = 0; j < RW; ++j) {
+        const int r = wave + j * kWaves;
+        if (r < NR) wpoll[j] = rec_load(rs, lane * kSt + r * 8);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const int t_p2 = i + 2 < nl ? pos_of(i + 2) : t_0;
+    prefetch(rb, t_p2, i + 2 < nl);
+    __builtin_amdgcn_sched_barrier(0);
+
+    if (i < nl) {
+      // ---- pass 1 of position i ------------------------------------------------
+      __builtin_amdgcn_s_setprio(1);
+      Lse pt[NR];
+      wave_pass1<NE, NR, 0>(x, pt, kLog2e);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) xref[r] = pt[r].ref;
+      if (lane == 0) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          part_sh[par][r][wave * 3 + 0] = pt[r].ref;
+          part_sh[par][r][wave * 3 + 1] = pt[r].z;
+          part_sh[par][r][wave * 3 + 2] = 0.f;
+        }
+      }
+      __builtin_amdgcn_s_setprio(0);
+    }
+    if (i < nl || do2) __syncthreads();
+    if (i < nl) {
+      __builtin_amdgcn_s_setprio(3);
+      const __amdgpu_buffer_rsrc_t rs = rsrc_rec(t_0);
+#pragma unroll
+      for (int j = 0; j < RW; ++j) {
+        const int r = wave + j * kWaves;
+        if (r < NR) {
+          const Lse m = merge_lds<kWaves, false>(part_sh[par][r]);
+          if (lane == 0) rec_store(rs, c * kSt + r * 8, pack2(m.ref, mark(m.z)));
+        }
+      }
+      __builtin_amdgcn_s_setprio(0);
+    }
+    if (do2 && wave == kWaves - 1 && lane < 2 * G) {
+      // the chunk's overlap and S partials of position i - 2, summed in a fixed order
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        float sel = 0.f;
+#pragma unroll
+        for (int k = 0; k < 2 * G; ++k) sel = lane == k ? acc_sh[par][w][k] : sel;
+        v = w == 0 ? sel : v + sel;
+      }
+      a.part2[((int64_t)t_m2 * C + c) * 2 * G + lane] = v;
+    }
+    // ---- shift the position window ---------------------------------------------
+    t_m2 = t_m1;
+    t_m1 = t_0;
+    t_0 = t_p1;
+    t_p1 = t_p2;
+  };
+
+  // nl + 2 layers, rounded up to an even count so that both buffers keep their
+  // registers across iterations
+  for (int i = 0; i < nl + 2; i += 2) {
+    layer(i, rawA);
+    layer(i + 1, rawB);
+  }
+}
+
+// One wave per position: the row log-sum-exps from the records (merged as the poll
+// merged them), the overlap and S of every head from the chunk partials, l_t and the
+// saved statistics.  Clears the records and partials it read.
+template <int G, bool SHARED>
+__global__ __launch_bounds__(64 * kFinishWaves) void tv_pipe_finish(TvArgs a) {
+  constexpr int NT = FwdShape<G, SHARED>::NT;
+  constexpr int NR = FwdShape<G, SHARED>::NR;
+  constexpr int kSt = NR * 8;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kFinishWaves + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const int C = a.sp.nchunks;
+  const __amdgpu_buffer_rsrc_t rs = rsrc_of(a.part1 + (int64_t)t * C * NR);
+  float lse2[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const uint64_t v = lane < C ? rec_load(rs, lane * kSt + r * 8) : 0ull;
+    lse2[r] = lse_log2(poll_row(v, rs, C, kSt, r, a.err));
+  }
+  float* p2 = a.part2 + (int64_t)t * C * 2 * G;
+  float tot[2 * G];
+#pragma unroll
+  for (int k = 0; k < 2 * G; ++k) tot[k] = 0.f;
+  for (int cc = lane; cc < C; cc += 64) {
+#pragma unroll
+    for (int k = 0; k < 2 * G; ++k) tot[k] += p2[(int64_t)cc * 2 * G + k];
+  }
+  wave_reduce<false, 2 * G>(tot);
+  uint64_t* rec = a.part1 + (int64_t)t * C * NR;
+  for (int i = lane; i < C * NR; i += 64) rec[i] = 0ull;
+  for (int i = lane; i < C * 2 * G; i += 64) p2[i] = 0.f;
+  if (lane == 0) {
+    float prod = 1.f, l = 0.f;
+    float* sv = a.saved + (int64_t)t * G * kTvSavedStride;
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const float al = fminf(fmaxf(tot[2 * k], 0.f), 1.f);
+      prod *= al;
+      l -= prod;
+      sv[k * kTvSavedStride + 0] = lse2[SHARED ? 0 : k] * kLn2;
+      sv[k * kTvSavedStride + 1] = lse2[NT + k] * kLn2;
+      sv[k * kTvSavedStride + 2] = al;
+      sv[k * kTvSavedStride + 3] = tot[2 * k + 1];
+    }
+    if (a.pos_loss) a.pos_loss[t] = l;
+    a.pos_ws[t] = l;
+  }
+}
+
+// ---------------------------------------------------------------------------
 constexpr int kBwdNVBf16 = 4;
 constexpr int kBwdNVF32 = 8;
 
@@ -280,46 +577,57 @@ __device__ __forceinline__ void store_grad(char* row, int64_t vi, const RowSplit
   }
 }
 
-template <int DT, int GDT, bool SHARED>
+// Vectors per thread and row for the backward: 32 bf16 or 16 fp32 values per row
+// and thread for up to four rows (fewer with more rows, at least one vector).
+template <int NR>
+constexpr int bwd_nv(int per_vec) {
+  const int nv = (per_vec == 8 ? 128 : 64) / (NR * per_vec);
+  return nv < 1 ? 1 : nv;
+}
+
+template <int G>
+static int bwd_nv_for(int dt, bool shared) {
+  const int pv = dt == kBF16 ? 8 : 4;
+  return shared ? bwd_nv<FwdShape<G, true>::NR>(pv) : bwd_nv<FwdShape<G, false>::NR>(pv);
+}
+
+// One workgroup per (position, chunk).  The chunk of every row of the position
+// (target row(s), then the G draft rows) is put in flight at once, then the
+// gradient of each head is formed and stored: one memory round trip per
+// workgroup, and the stores of one head overlap the arithmetic of the next.
+template <int DT, int GDT, int G, bool SHARED>
 __global__ __launch_bounds__(kBlock) void tv_bwd_kernel(TvArgs a) {
+  constexpr int NT = FwdShape<G, SHARED>::NT;
+  constexpr int NR = FwdShape<G, SHARED>::NR;
   constexpr int PV = Elem<DT>::kPerVec;
-  constexpr int NV = DT == kBF16 ? kBwdNVBf16 : kBwdNVF32;
+  constexpr int NV = bwd_nv<NR>(PV);
   constexpr int NE = NV * PV;
   const int C = a.sp.nchunks;
   const int t = blockIdx.x / C, c = blockIdx.x - (blockIdx.x / C) * C;
-  const int G = a.G;
   const int64_t vbeg = (int64_t)c * a.sp.vec_per_chunk;
   const int64_t vend = min(vbeg + a.sp.vec_per_chunk, a.sp.nvec);
 
+  const char* rows[NR];
+  fwd_rows<DT, NT, G>(a, t, rows);
+  float x[NR][NE];
+  load_rows<DT, NV, NR>(rows, vbeg, vend, a.sp, a.V, x);
+
   // end-to-end weights of this position
   const float* sv = a.saved_in + (int64_t)t * G * kTvSavedStride;
-  float alpha[kTvMaxHeads];
+  float alpha[G];
+#pragma unroll
   for (int k = 0; k < G; ++k) alpha[k] = sv[k * kTvSavedStride + 2];
   const float gscale = -a.grad_loss[0] / (float)a.T;
 
-  const char* tb = reinterpret_cast<const char*>(a.target);
-  const char* db = reinterpret_cast<const char*>(a.draft);
   char* gb = reinterpret_cast<char*>(a.grad);
   constexpr int gbytes = GDT == kBF16 ? 2 : 4;
-  float xv[2][NE], gr[NE];
-  float (&xt)[NE] = xv[0];
-  float (&xd)[NE] = xv[1];
-  if (SHARED) {
-    const char* const rows[1] = {tb + (int64_t)t * a.t_pos * Elem<DT>::kBytes};
-    load_rows<DT, NV, 1>(rows, vbeg, vend, a.sp, a.V, *reinterpret_cast<float(*)[1][NE]>(&xv[0]));
-  }
+#pragma unroll
   for (int k = 0; k < G; ++k) {
-    const char* drow = db + ((int64_t)t * a.d_pos + (int64_t)k * a.d_head) * Elem<DT>::kBytes;
-    if (!SHARED) {
-      const char* const rows[2] = {tb + ((int64_t)t * a.t_pos + (int64_t)k * a.t_head) * Elem<DT>::kBytes, drow};
-      load_rows<DT, NV, 2>(rows, vbeg, vend, a.sp, a.V, xv);
-    } else {
-      const char* const rows[1] = {drow};
-      load_rows<DT, NV, 1>(rows, vbeg, vend, a.sp, a.V, *reinterpret_cast<float(*)[1][NE]>(&xv[1]));
-    }
     float wsum = 0.f;
+#pragma unroll
     for (int kk = k; kk < G; ++kk) {
       float prod = 1.f;
+#pragma unroll
       for (int i = 0; i <= kk; ++i)
         if (i != k) prod *= alpha[i];
       wsum += prod;
@@ -330,6 +638,9 @@ __global__ __launch_bounds__(kBlock) void tv_bwd_kernel(TvArgs a) {
     const float delta = lse_q - lse_p;
     const float lq2 = lse_q * kLog2e;
     const float c1 = w * (1.f - S), c0 = -w * S;
+    const float(&xt)[NE] = x[SHARED ? 0 : k];
+    const float(&xd)[NE] = x[NT + k];
+    float gr[NE];
 #pragma unroll
     for (int i = 0; i < NE; ++i) {
       const bool ind = (xd[i] - xt[i]) <= delta;
@@ -381,6 +692,67 @@ hipError_t launch_tv_fwd(const TvArgs& a, int dt, bool shared, hipStream_t strea
   return shared ? launch_fwd_dt<kF32, true>(a, stream) : launch_fwd_dt<kF32, false>(a, stream);
 }
 
+// ---- single-read forward: launch, vectors per thread, occupancy --------------
+template <int DT, bool SHARED, int G>
+static hipError_t launch_pipe_g(const TvArgs& a, hipStream_t stream) {
+  if constexpr (!pipe_fits<G, SHARED>()) {
+    return hipErrorInvalidValue;
+  } else {
+    const int64_t grid = (int64_t)a.sgroups * a.sp.nchunks;
+    hipLaunchKernelGGL((tv_pipe_main<DT, G, SHARED>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((tv_pipe_finish<G, SHARED>), dim3((unsigned)((a.T + kFinishWaves - 1) / kFinishWaves)),
+                       dim3(64 * kFinishWaves), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(tv_fwd_mean, dim3(1), dim3(kBlock), 0, stream, a);
+    return hipGetLastError();
+  }
+}
+
+template <int DT, bool SHARED, int G>
+static hipError_t occupancy_pipe_g(int* n) {
+  if constexpr (!pipe_fits<G, SHARED>()) {
+    *n = 0;
+    return hipErrorInvalidValue;
+  } else {
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, tv_pipe_main<DT, G, SHARED>, kBlock, 0);
+  }
+}
+
+template <int DT, bool SHARED>
+static hipError_t pipe_dispatch(int G, const TvArgs* a, hipStream_t stream, int* occ) {
+  switch (G) {
+#define MTP_PIPE_CASE(g) \
+    case g: return a ? launch_pipe_g<DT, SHARED, g>(*a, stream) : occupancy_pipe_g<DT, SHARED, g>(occ);
+    MTP_PIPE_CASE(1) MTP_PIPE_CASE(2) MTP_PIPE_CASE(3) MTP_PIPE_CASE(4)
+    MTP_PIPE_CASE(5) MTP_PIPE_CASE(6) MTP_PIPE_CASE(7) MTP_PIPE_CASE(8)
+#undef MTP_PIPE_CASE
+  }
+  return hipErrorInvalidValue;
+}
+
+static hipError_t pipe_any(int dt, bool shared, int G, const TvArgs* a, hipStream_t stream, int* occ) {
+  if (dt == kBF16) return shared ? pipe_dispatch<kBF16, true>(G, a, stream, occ) : pipe_dispatch<kBF16, false>(G, a, stream, occ);
+  return shared ? pipe_dispatch<kF32, true>(G, a, stream, occ) : pipe_dispatch<kF32, false>(G, a, stream, occ);
+}
+
+int tv_pipe_vec_per_thread(int dt, int G, bool shared) {
+  const int nr = (shared ? 1 : G) + G;
+  if (nr > kTvPipeMaxRows) return 0;
+  const int pv = dt == kBF16 ? 8 : 4;
+  const int nv = kPipeFloats / (nr * pv);
+  return nv < 1 ? 1 : nv;
+}
+
+hipError_t tv_pipe_occupancy(int dt, int G, bool shared, int* blocks_per_cu) {
+  return pipe_any(dt, shared, G, nullptr, nullptr, blocks_per_cu);
+}
+
+hipError_t launch_tv_pipe_fwd(const TvArgs& a, int dt, bool shared, hipStream_t stream) {
+  return pipe_any(dt, shared, a.G, &a, stream, nullptr);
+}
+
 template <int G>
 static int nv_for(int dt, bool shared) {
   const int pv = dt == kBF16 ? 8 : 4;
@@ -404,11 +776,39 @@ int tv_fwd_part1_words(int G, bool shared) { return (shared ? 1 : G) + G; }
 
 int tv_bwd_vec_per_thread(int dt) { return dt == kBF16 ? kBwdNVBf16 : kBwdNVF32; }
 
+int tv_bwd_full_vec_per_thread(int dt, int G, bool shared) {
+  switch (G) {
+    case 1: return bwd_nv_for<1>(dt, shared);
+    case 2: return bwd_nv_for<2>(dt, shared);
+    case 3: return bwd_nv_for<3>(dt, shared);
+    case 4: return bwd_nv_for<4>(dt, shared);
+    case 5: return bwd_nv_for<5>(dt, shared);
+    case 6: return bwd_nv_for<6>(dt, shared);
+    case 7: return bwd_nv_for<7>(dt, shared);
+    default: return bwd_nv_for<8>(dt, shared);
+  }
+}
+
+template <int DT, int GDT, bool SHARED, int G>
+static hipError_t launch_bwd_g(const TvArgs& a, hipStream_t stream) {
+  const int64_t grid = (int64_t)a.T * a.sp.nchunks;
+  hipLaunchKernelGGL((tv_bwd_kernel<DT, GDT, G, SHARED>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int DT, int GDT, bool SHARED>
 static hipError_t launch_bwd3(const TvArgs& a, hipStream_t stream) {
-  const int64_t grid = (int64_t)a.T * a.sp.nchunks;
-  hipLaunchKernelGGL((tv_bwd_kernel<DT, GDT, SHARED>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
-  return hipGetLastError();
+  switch (a.G) {
+    case 1: return launch_bwd_g<DT, GDT, SHARED, 1>(a, stream);
+    case 2: return launch_bwd_g<DT, GDT, SHARED, 2>(a, stream);
+    case 3: return launch_bwd_g<DT, GDT, SHARED, 3>(a, stream);
+    case 4: return launch_bwd_g<DT, GDT, SHARED, 4>(a, stream);
+    case 5: return launch_bwd_g<DT, GDT, SHARED, 5>(a, stream);
+    case 6: return launch_bwd_g<DT, GDT, SHARED, 6>(a, stream);
+    case 7: return launch_bwd_g<DT, GDT, SHARED, 7>(a, stream);
+    case 8: return launch_bwd_g<DT, GDT, SHARED, 8>(a, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int DT, int GDT>

@@ -88,49 +88,6 @@ __device__ __forceinline__ RowStats merge_records(__amdgpu_buffer_rsrc_t rs, int
   return RowStats{a[0], a[1]};
 }
 
-// Wait until word `word` of every record of the group is published (non-zero):
-// `v` is this lane's word of record `lane`, loaded earlier, and lanes still seeing
-// zero load again; records past the first 64 are loaded here.  `merge` folds each
-// lane's words in record order (first record, then l + 64, ...).  Bounded by the
-// spin limit (a timeout sets the error word and carries on).
-template <typename Fold>
-__device__ __forceinline__ void poll_words(uint64_t v, __amdgpu_buffer_rsrc_t rs, int C, int st, int word,
-                                           uint32_t* err, Fold fold) {
-  const int lane = threadIdx.x & 63;
-  uint64_t t0 = 0;
-  for (int c0 = 0; c0 < C; c0 += 64) {
-    const int c = c0 + lane;
-    if (c0 > 0 && c < C) v = rec_load(rs, c * st + word * 8);
-    bool ready = !(c < C) || v != 0ull;
-    while (__ballot(!ready) != 0ull) {
-      if (t0 == 0) t0 = __builtin_amdgcn_s_memrealtime();
-      __builtin_amdgcn_s_sleep(1);
-      if (!ready) {
-        v = rec_load(rs, c * st + word * 8);
-        ready = v != 0ull;
-      }
-      if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimitTicks) {
-        if (lane == 0) __hip_atomic_fetch_or(err, kErrSyncTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-    }
-    if (c < C) fold(c0 == 0, v);
-  }
-}
-
-// The row's merged log-sum-exp (no entropy moment) from word `word` of the records.
-__device__ __forceinline__ Lse poll_row(uint64_t v, __amdgpu_buffer_rsrc_t rs, int C, int st, int word,
-                                        uint32_t* err) {
-  Lse acc = lse_empty();
-  poll_words(v, rs, C, st, word, err, [&](bool first, uint64_t w) {
-    const Lse r{unpack_lo(w), unmark(unpack_hi(w)), 0.f};
-    acc = first ? r : lse_merge(acc, r);
-  });
-  Lse a[1] = {acc};
-  wave_merge<1, 0>(a);
-  return a[0];
-}
-
 // ---- argmax of the draft logits (target-only verify) --------------------------
 __device__ __forceinline__ uint64_t pack_argmax(float m, uint32_t idx) {
   return pack2(m, __uint_as_float(min(idx, 0xfffffffeu) + 1u));
