@@ -336,11 +336,10 @@ def main():
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS,
                          "traffic": profiled_traffic("tv_loss_T8192x3_V151936_bf16.md", TV_SOURCES),
-                         "kernel": "tv_fwd_lse + tv_fwd_stats + tv_fwd_finish + tv_fwd_mean + tv_bwd_kernel",
-                         "valu_busy_pct": profiled_valu_busy(["void mtp::tv_fwd_lse<1, 3, true>(mtp::TvArgs)",
-                                                              "void mtp::tv_fwd_stats<1, 3, true>(mtp::TvArgs)",
-                                                              "void mtp::tv_bwd_kernel<1, 1, true>(mtp::TvArgs)"],
-                                                             [fm / 2, fm / 2, bm]),
+                         "kernel": "tv_pipe_main + tv_pipe_finish + tv_fwd_mean + tv_bwd_kernel",
+                         "valu_busy_pct": profiled_valu_busy(["void mtp::tv_pipe_main<1, 3, true>(mtp::TvArgs)",
+                                                              "void mtp::tv_bwd_kernel<1, 1, 3, true>(mtp::TvArgs)"],
+                                                             [fm, bm]),
                          "bytes_per_launch": fwd_bytes + bwd_bytes},
         }
         log(f"tv loss: fwd {fm:.3f} ms ({fwd_bytes / fm / 1e6:.0f} GB/s), bwd {bm:.3f} ms "
