@@ -212,6 +212,13 @@ mtp_status mtp_gumbel_sample(const void* logits, int64_t row_stride, mtp_dtype d
  *   saved [T, gamma, 4] = (ln-sum-exp of p, of q, alpha, S) (required; the
  *   backward consumes it).
  * Limits: T >= 1, 1 <= gamma <= MTP_MAX_GAMMA, 1 <= vocab <= 2^30.
+ * Each logit is read once when a position has at most 5 rows (a shared target with
+ * gamma <= 4, or per-head targets with gamma <= 2) and the GPU can hold every chunk
+ * of a row at once (vocab up to ~2M bf16 logits on MI355X); otherwise twice (two
+ * streaming passes).  The results agree within the statistic tolerances either way;
+ * the indicator of S is then taken on float32 probabilities rather than logits.
+ * Workspace: mtp_tv_loss_workspace_size bytes for the same T, gamma, vocab, dtype
+ * and sharing (it covers both forms), zeroed once and left zeroed by every call.
  */
 mtp_status mtp_tv_loss_workspace_size(int32_t T, int32_t gamma, int32_t vocab, mtp_dtype dtype,
                                       int32_t shared_target, size_t* bytes);

@@ -223,3 +223,21 @@ def test_largest_vocabulary_closed_form(dtype):
         assert abs(got - ref) <= 2 ** -7 * abs(ref), (v, got, ref)
     del t, d, g
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("extra", [0, 8])
+def test_single_read_forward_at_the_co_residency_limit(extra):
+    """The single-read forward holds every chunk of a row on chip at once: the
+    largest vocabulary it takes is (co-resident workgroups) x 4096 bf16 logits, one
+    super-group for the whole call.  At that vocabulary it runs with a single
+    super-group; one vector more falls back to the two streaming passes.  Both must
+    match the oracle, and no bounded wait may time out."""
+    props = torch.cuda.get_device_properties(0)
+    V = 2 * props.multi_processor_count * 4096 + extra
+    w = dict(T=2, G=3, V=V, dtype=torch.bfloat16, scale=1.25, sigma=0.3, shared=True, seed=6)
+    t, d = synthetic.tv_inputs(w, DEV)
+    _say("tv co-residency limit", V)
+    loss, pos, saved, gb, gf = _run(t, d, g=1.0)
+    _check_forward(t, d, loss, pos, saved, torch.bfloat16)
+    _check_backward(t, d, saved, 1.0, gb, gf)
+    assert mtp.workspace_error(mtp.workspace(DEV, 1)) == 0
