@@ -212,6 +212,9 @@ mtp_status mtp_gumbel_sample(const void* logits, int64_t row_stride, mtp_dtype d
  *   saved [T, gamma, 4] = (ln-sum-exp of p, of q, alpha, S) (required; the
  *   backward consumes it).
  * Limits: T >= 1, 1 <= gamma <= MTP_MAX_GAMMA, 1 <= vocab <= 2^30.
+ * -inf logits are allowed (masking).  A head whose target or draft row has no
+ * finite normaliser (all -inf, or a NaN) is a data error: its alpha and S are NaN,
+ * and so are its position's loss and the mean.
  * Each logit is read once when a position has at most 5 rows (a shared target with
  * gamma <= 4, or per-head targets with gamma <= 2) and the GPU can hold every chunk
  * of a row at once (vocab up to ~2M bf16 logits on MI355X); otherwise twice (two

@@ -431,6 +431,9 @@ def tv_stats(target, draft):
         only guards rounding).
     S_{t,k} = sum_v 1[q_v <= p_v] q_v              (paperlayer App. A).
     READING: the indicator is evaluated on log-probabilities, ties count as 1.
+    READING: a row without a finite normaliser (all -inf, or a NaN) is a data error,
+    as in verify: that head's alpha and S are NaN (and so are the position's loss and
+    the mean).
     target: [T, V] (shared by all heads) or [T, gamma, V]; draft: [T, gamma, V].
     Returns float64 [T, gamma, 4].
     """
@@ -442,6 +445,9 @@ def tv_stats(target, draft):
         for k in range(G):
             logp, lse_p = log_softmax(tgt[t, k])
             logq, lse_q = log_softmax(draft[t, k])
+            if logp is None or logq is None:
+                saved[t, k] = (lse_p, lse_q, np.nan, np.nan)
+                continue
             p, q = np.exp(logp), np.exp(logq)
             alpha = min(max(overlap(p, q), 0.0), 1.0)
             s = float(np.sum(q[logq <= logp]))
@@ -515,6 +521,9 @@ def tv_loss_grad(target, draft, g=1.0):
         for k in range(G):
             logp, _ = log_softmax(tgt[t, k])
             logq, _ = log_softmax(draft[t, k])
+            if logp is None or logq is None:   # data error (see tv_stats)
+                grad[t, k] = np.nan
+                continue
             q = np.exp(logq)
             ind = (logq <= logp).astype(np.float64)
             grad[t, k] = w[t, k] * q * (ind - saved[t, k, 3])

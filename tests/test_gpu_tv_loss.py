@@ -241,3 +241,68 @@ def test_single_read_forward_at_the_co_residency_limit(extra):
     _check_forward(t, d, loss, pos, saved, torch.bfloat16)
     _check_backward(t, d, saved, 1.0, gb, gf)
     assert mtp.workspace_error(mtp.workspace(DEV, 1)) == 0
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("shared,G", [(True, 3), (False, 2), (False, 3)])
+def test_masked_supports(shared, G, dtype):
+    """-inf logits (masking) on both sides: partly overlapping windows, equal
+    supports, a head disjoint from the target (alpha = 0, S = 0, zero gradient),
+    a narrow target window (most wave segments hold no target mass) and narrow
+    draft windows (most hold no draft mass).  shared gamma = 3 and per-head gamma = 2
+    take the single-read forward, per-head gamma = 3 the two streaming passes."""
+    T, V = 4, 50000
+    w = dict(T=T, G=G, V=V, dtype=dtype, scale=1.2, sigma=0.3, shared=shared, seed=11)
+    t, d = synthetic.tv_inputs(w, DEV, seed=77)
+    t, d = t.clone(), d.clone()
+    ninf = float("-inf")
+
+    def keep(x, lo, hi):   # mask a row outside [lo, hi)
+        x[..., :lo] = ninf
+        x[..., hi:] = ninf
+
+    tgt = (lambda pos: [t[pos]]) if shared else (lambda pos: [t[pos, k] for k in range(G)])
+    for row in tgt(0):
+        keep(row, 1000, 30000)
+    keep(d[0, 0], 20000, 45000)           # partial overlap
+    keep(d[0, 1], 1000, 30000)            # the target's support
+    if G > 2:
+        keep(d[0, 2], 35000, V)           # disjoint from the target
+    for row in tgt(1):
+        keep(row, 12345, 12845)           # narrow target window
+    for k in range(G):
+        keep(d[2, k], 7000 + 3000 * k, 7300 + 3000 * k)   # narrow draft windows
+    _say("tv masked supports", shared, G, dtype)
+    loss, pos, saved, gb, gf = _run(t, d, g=0.9)
+    ref_saved = _check_forward(t, d, loss, pos, saved, dtype)
+    _check_backward(t, d, saved, 0.9, gb, gf)
+    if G > 2:   # the disjoint head
+        assert saved[0, 2, 2].item() == 0.0 and saved[0, 2, 3].item() == 0.0
+        assert ref_saved[0, 2, 2] == 0.0
+        assert (gf[0, 2] == 0).all() and (gb[0, 2] == 0).all()
+    # masked draft elements get no gradient
+    dm = torch.isinf(d.float())
+    assert (gf[dm] == 0).all() and (gb[dm] == 0).all()
+
+
+@pytest.mark.parametrize("shared,G", [(True, 3), (False, 3)])
+def test_position_without_a_finite_target_normaliser(shared, G):
+    """A target row of -inf only has no normaliser: its position's statistics are
+    NaN (a data error), and every other position still matches the oracle."""
+    T, V = 5, 20000
+    w = dict(T=T, G=G, V=V, dtype=torch.bfloat16, scale=1.2, sigma=0.3, shared=shared, seed=12)
+    t, d = synthetic.tv_inputs(w, DEV, seed=78)
+    t = t.clone()
+    t[2] = float("-inf")
+    loss, pos, saved = mtp.tv_loss_fwd(t, d)
+    torch.cuda.synchronize()
+    sv = saved.cpu()
+    assert torch.isnan(sv[2, :, 2]).all() and torch.isnan(sv[2, :, 3]).all()
+    assert torch.isnan(pos[2]).item() and torch.isnan(loss).item()
+    keep = [0, 1, 3, 4]
+    tf, df = to_f64(t)[keep], to_f64(d)[keep]
+    _, ref_pos, ref_saved = omtp.tv_loss(tf, df)
+    for i in (2, 3):
+        assert stat_close(sv[keep][..., i].double().numpy(), ref_saved[..., i], torch.bfloat16).all()
+    assert stat_close(pos.cpu()[keep].double().numpy(), ref_pos, torch.bfloat16).all()
+    assert mtp.workspace_error(mtp.workspace(DEV, 1)) == 0

@@ -129,3 +129,24 @@ def test_gradient_invariants():
     loss, pos, saved = mtp.tv_loss(xp, np.stack([xq] * 2, axis=1))
     assert loss == 0.0 and np.all(saved[:, :, 2] == 0.0)
     assert np.all(np.isfinite(mtp.e2e_weights(saved[:, :, 2], 1.0, 1)))
+
+
+def test_row_without_a_finite_normaliser_is_a_data_error():
+    """READING (as in verify): a target or draft row of -inf only, or one holding a
+    NaN, has no normaliser; that head's alpha and S are NaN, so are its position's
+    loss and the mean, and the other positions are unaffected."""
+    rng = np.random.default_rng(3)
+    t = rng.normal(size=(3, 40))
+    d = t[:, None, :] + 0.3 * rng.normal(size=(3, 2, 40))
+    t_bad, d_bad = t.copy(), d.copy()
+    t_bad[1] = -np.inf
+    d_bad[2, 1, 5] = np.nan
+    loss, pos, saved = mtp.tv_loss(t_bad, d_bad)
+    assert np.isnan(loss)
+    assert np.isnan(saved[1, :, 2:]).all() and np.isnan(pos[1])
+    assert np.isnan(saved[2, 1, 2:]).all() and np.isnan(pos[2])
+    assert np.isfinite(saved[2, 0]).all()
+    _, pos_ok, saved_ok = mtp.tv_loss(t, d)
+    assert np.allclose(saved[0], saved_ok[0]) and np.isclose(pos[0], pos_ok[0])
+    g = mtp.tv_loss_grad(t_bad, d_bad)
+    assert np.isnan(g[1]).all() and np.isfinite(g[0]).all()

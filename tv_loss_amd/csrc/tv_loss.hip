@@ -153,9 +153,11 @@ __global__ __launch_bounds__(kBlock) void tv_fwd_stats(TvArgs a) {
     for (int k = 0; k < G; ++k) {
       const float uk = u[SHARED ? 0 : k];
       const float v = __builtin_fmaf(x[NT + k][i], kLog2e, -lse_sh[NT + k]);        // log2 q
-      const float m = fast_exp2(fminf(uk, v));                                        // min(p, q)
+      // min(p, q) and 1[q <= p] q; a NaN log-probability (a row without a
+      // normaliser) propagates into both sums
+      const float m = fast_exp2(__builtin_elementwise_minimum(uk, v));
       al[k] += m;
-      sk[k] += v <= uk ? m : 0.f;
+      sk[k] += v > uk ? 0.f : m;
     }
   }
 #pragma unroll
@@ -212,7 +214,8 @@ __global__ __launch_bounds__(64 * kFinishWaves) void tv_fwd_finish(TvArgs a) {
     float* sv = a.saved + (int64_t)t * G * kTvSavedStride;
 #pragma unroll
     for (int k = 0; k < G; ++k) {
-      const float al = fminf(fmaxf(tot[2 * k], 0.f), 1.f);
+      const float ov = tot[2 * k];   // NaN (a row without a normaliser) stays NaN
+      const float al = ov != ov ? ov : fminf(fmaxf(ov, 0.f), 1.f);
       prod *= al;
       l -= prod;
       sv[k * kTvSavedStride + 0] = lse2[SHARED ? 0 : k] * kLn2;
@@ -519,7 +522,8 @@ __global__ __launch_bounds__(64 * kFinishWaves) void tv_pipe_finish(TvArgs a) {
     float* sv = a.saved + (int64_t)t * G * kTvSavedStride;
 #pragma unroll
     for (int k = 0; k < G; ++k) {
-      const float al = fminf(fmaxf(tot[2 * k], 0.f), 1.f);
+      const float ov = tot[2 * k];   // NaN (a row without a normaliser) stays NaN
+      const float al = ov != ov ? ov : fminf(fmaxf(ov, 0.f), 1.f);
       prod *= al;
       l -= prod;
       sv[k * kTvSavedStride + 0] = lse2[SHARED ? 0 : k] * kLn2;
