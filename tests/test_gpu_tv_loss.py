@@ -152,6 +152,9 @@ def test_full_workload_sampled_positions():
     p = pos.double()
     assert abs(loss.item() - p.mean().item()) <= 1e-6 * abs(p.mean().item()) + 1e-7
     _say("alpha per head:", ref_saved[:, :, 2].mean(0), "indicator ties:", ties)
+    # sum_v q_v (1[q_v <= p_v] - S) = S - S = 0: every gradient row sums to zero
+    rows = gf[positions].double()
+    assert (rows.sum(-1).abs() <= 1e-4 * rows.abs().sum(-1)).all()
 
 
 def test_identical_heads_give_zero_gradient():

@@ -270,6 +270,35 @@ def test_million_sequences_match_the_oracle_and_emit_p(V):
     assert abs(rate - alpha) < 5 * np.sqrt(alpha * (1 - alpha) / B)
 
 
+def test_mean_accepted_length_is_the_product_of_overlaps():
+    """The expected number of accepted drafts is sum_k prod_{j<=k} alpha_j for
+    independent positions (paperlayer Sec. 4: the acceptance length multiplies the
+    per-step overlaps): 200000 sequences of three fixed (p, q) pairs, each with its
+    own uniforms, against the overlaps of the oracle, within 5 sigma."""
+    B, G, V = 200000, 3, 16
+    g = torch.Generator(device=DEV).manual_seed(57)
+    base_t = 1.2 * torch.randn((1, G + 1, V), generator=g, device=DEV)
+    base_d = base_t[:, :G] + torch.tensor([0.3, 0.6, 1.0], device=DEV)[None, :, None] * torch.randn(
+        (1, G, V), generator=g, device=DEV)
+    t = base_t.expand(B, G + 1, V).contiguous()
+    d = base_d.expand(B, G, V).contiguous()
+    y = synthetic.gumbel_tokens(d, g)
+    out = _run(t, d, y, seed=99, offset=5)
+    n = out["accepted_len"].double().cpu().numpy()
+    alphas = []
+    for k in range(G):
+        lp, _ = omtp.log_softmax(to_f64(base_t[0, k]))
+        lq, _ = omtp.log_softmax(to_f64(base_d[0, k]))
+        alphas.append(omtp.overlap(np.exp(lp), np.exp(lq)))
+    expect = sum(np.prod(alphas[:k + 1]) for k in range(G))
+    _say("alphas", alphas, "E[n]", expect, "mean n", n.mean())
+    assert abs(n.mean() - expect) < 5 * n.std() / np.sqrt(B)
+    # each flag's rate is its overlap, independently of the others
+    rates = out["accept"].double().mean(0).cpu().numpy()
+    for k in range(G):
+        assert abs(rates[k] - alphas[k]) < 5 * np.sqrt(alphas[k] * (1 - alphas[k]) / B)
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_largest_vocabulary(dtype):
     """The largest vocabulary one GPU verifies (every workgroup of the row resident
