@@ -250,9 +250,11 @@ __global__ __launch_bounds__(kBlock) void tv_fwd_mean(TvArgs a) {
 //   * the e values of position i - 1 move from registers to LDS;
 //   * the chunk of position i is unpacked (its loads went out two layers ago), the
 //     poll of position i - 1's records and the loads of position i + 2 go out;
-//   * pass 1 of position i: per-wave log-sum-exp partials of every row, merged over
-//     the workgroup and published as one self-announcing record word per row;
-//     the waves' overlap and S partials of position i - 2 are added up and stored.
+//   * pass 1 of position i: every lane's sums of e against its wave's largest logit
+//     go to LDS; wave r merges row r over the workgroup (lanes first, across the
+//     waves, then one wave sum) and publishes it as one self-announcing record word;
+//     the lanes' overlap and S partials of position i - 2 are added up the same way,
+//     wave w taking the values w, w + 4, ...
 // In a wave's own units p = sa e_p and q = sb e_q (e <= 1, taken against the wave's
 // largest logit of the row).  For head k, with rho = sb / sa <= 1:
 //   min(p, q) = sa min(e_p, rho e_q),  1[q <= p] q = sa 1[rho e_q <= e_p] rho e_q,
@@ -261,6 +263,42 @@ __global__ __launch_bounds__(kBlock) void tv_fwd_mean(TvArgs a) {
 // order the poll used, sums the partials, writes the saved statistics and l_t, and
 // clears what it read.  Record words: (ref, z with the sign bit set), never zero.
 constexpr int kPipeFloats = 64;   // logits per thread and position (all rows) in flight
+
+// Pass 1 of R rows with the sums left per lane: row r's reference is the wave's
+// largest logit M (ref = M L; -inf for a wave holding only -inf), x[r] is
+// overwritten with e = 2^(x L - ref) and z[r] is this lane's sum of its e values.
+template <int NE, int R>
+__device__ __forceinline__ void lane_pass1(float (&x)[R][NE], float (&ref)[R], float (&z)[R], float L) {
+  float M[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float m = x[r][0];
+#pragma unroll
+    for (int i = 1; i < NE; ++i) m = fmaximum(m, x[r][i]);
+    M[r] = m;
+  }
+  wave_reduce<true, R>(M);
+  float sh[R], z0[R], z1[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    sh[r] = M[r] > kNegInf ? M[r] * L : 0.f;   // 0 keeps -inf - sh = -inf
+    z0[r] = z1[r] = 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < NE; ++i) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float e = fast_exp2(__builtin_fmaf(x[r][i], L, -sh[r]));
+      if (i & 1) z1[r] += e; else z0[r] += e;
+      x[r][i] = e;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    z[r] = z0[r] + z1[r];
+    ref[r] = M[r] * L;
+  }
+}
 
 template <int NR>
 constexpr int pipe_nv(int per_vec) {
@@ -305,10 +343,12 @@ __global__ __launch_bounds__(kBlock) void tv_pipe_main(TvArgs a) {
   const int V = (int)a.V;
   const int row_bytes = (int)min(a.V * Elem<DT>::kBytes, (int64_t)0x7fffffff);
 
+  constexpr int KW = (2 * G + kWaves - 1) / kWaves;   // pass-2 values each wave adds up
   __shared__ float4 held[NR][NQ][kBlock];      // e values of the position two layers back
-  __shared__ float part_sh[2][NR][kWaves * 3];  // pass-1 wave partials, by layer parity
+  __shared__ float ref_sh[2][NR][kWaves];       // pass-1 wave references, by layer parity
+  __shared__ float z_sh[2][NR][kBlock];         // pass-1 lane sums in their wave's units
   __shared__ float lse_sh[2][NR];               // row log2-sum-exps of the position in pass 2
-  __shared__ float acc_sh[2][kWaves][2 * G];    // pass-2 wave partials (overlap, S per head)
+  __shared__ float red_sh[2 * G][kBlock];       // pass-2 lane partials (overlap, S per head)
 
   auto prefetch = [&](RawChunk<NV, NR>& rb, int t, bool live) {
     const char* rows[NR];
@@ -391,11 +431,8 @@ __global__ __launch_bounds__(kBlock) void tv_pipe_main(TvArgs a) {
         res[2 * k] = (al0 + al1) * scale;
         res[2 * k + 1] = (s0_ + s1_) * scale;
       }
-      wave_reduce<false, 2 * G>(res);
-      if (lane == 0) {
 #pragma unroll
-        for (int k = 0; k < 2 * G; ++k) acc_sh[par][wave][k] = res[k];
-      }
+      for (int k = 0; k < 2 * G; ++k) red_sh[k][tid] = res[k];
     }
     // ---- position i - 1 moves to LDS (own slots only) --------------------------
     if (i >= 1 && i - 1 < nl) {
@@ -431,17 +468,13 @@ __global__ __launch_bounds__(kBlock) void tv_pipe_main(TvArgs a) {
     if (i < nl) {
       // ---- pass 1 of position i ------------------------------------------------
       __builtin_amdgcn_s_setprio(1);
-      Lse pt[NR];
-      wave_pass1<NE, NR, 0>(x, pt, kLog2e);
+      float zl[NR];
+      lane_pass1<NE, NR>(x, xref, zl, kLog2e);
 #pragma unroll
-      for (int r = 0; r < NR; ++r) xref[r] = pt[r].ref;
+      for (int r = 0; r < NR; ++r) z_sh[par][r][tid] = zl[r];
       if (lane == 0) {
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          part_sh[par][r][wave * 3 + 0] = pt[r].ref;
-          part_sh[par][r][wave * 3 + 1] = pt[r].z;
-          part_sh[par][r][wave * 3 + 2] = 0.f;
-        }
+        for (int r = 0; r < NR; ++r) ref_sh[par][r][wave] = xref[r];
       }
       __builtin_amdgcn_s_setprio(0);
     }
@@ -453,23 +486,41 @@ __global__ __launch_bounds__(kBlock) void tv_pipe_main(TvArgs a) {
       for (int j = 0; j < RW; ++j) {
         const int r = wave + j * kWaves;
         if (r < NR) {
-          const Lse m = merge_lds<kWaves, false>(part_sh[par][r]);
-          if (lane == 0) rec_store(rs, c * kSt + r * 8, pack2(m.ref, mark(m.z)));
+          // row r over the workgroup: each lane rescales its four waves' sums to the
+          // largest reference, then one wave sum
+          float rf[kWaves], R = kNegInf;
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w) {
+            rf[w] = ref_sh[par][r][w];
+            R = fmaximum(R, rf[w]);
+          }
+          const float Rf = finite_ref(R);
+          float zs = 0.f;
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w) zs = __builtin_fmaf(z_sh[par][r][w * 64 + lane], fast_exp2(rf[w] - Rf), zs);
+          const float Z = wave_total(zs);
+          if (lane == 0) rec_store(rs, c * kSt + r * 8, pack2(R, mark(Z)));
         }
       }
       __builtin_amdgcn_s_setprio(0);
     }
-    if (do2 && wave == kWaves - 1 && lane < 2 * G) {
-      // the chunk's overlap and S partials of position i - 2, summed in a fixed order
-      float v = 0.f;
+    if (do2) {
+      // the chunk's overlap and S partials of position i - 2: wave w adds up values
+      // w, w + 4, ... over the lanes (the four waves' lanes first), in a fixed order
+      float v[KW];
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        float sel = 0.f;
-#pragma unroll
-        for (int k = 0; k < 2 * G; ++k) sel = lane == k ? acc_sh[par][w][k] : sel;
-        v = w == 0 ? sel : v + sel;
+      for (int j = 0; j < KW; ++j) {
+        const int k = min(wave + j * kWaves, 2 * G - 1);
+        v[j] = (red_sh[k][lane] + red_sh[k][lane + 64]) + (red_sh[k][lane + 128] + red_sh[k][lane + 192]);
       }
-      a.part2[((int64_t)t_m2 * C + c) * 2 * G + lane] = v;
+      wave_reduce<false, KW>(v);
+      if (lane == 0) {
+#pragma unroll
+        for (int j = 0; j < KW; ++j) {
+          const int k = wave + j * kWaves;
+          if (k < 2 * G) a.part2[((int64_t)t_m2 * C + c) * 2 * G + k] = v[j];
+        }
+      }
     }
     // ---- shift the position window ---------------------------------------------
     t_m2 = t_m1;
