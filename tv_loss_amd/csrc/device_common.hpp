@@ -291,6 +291,11 @@ __device__ __forceinline__ int ld_coherent(const int* p) {
   return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Wait for every outstanding vector memory operation of this wave and nothing else:
+// s_waitcnt with vmcnt 0 and expcnt / lgkmcnt at their maxima (gfx9 encoding: vmcnt
+// in bits 3:0 and 15:14, expcnt in 6:4, lgkmcnt in 11:8).
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Wait for this wave's outstanding memory operations (the coherent stores that
 // precede an arrival) to complete.  The signal fences keep the compiler from
 // moving memory operations across the wait.
@@ -720,29 +725,36 @@ __device__ __forceinline__ void rec_store(__amdgpu_buffer_rsrc_t r, int byte_off
 // `v` is this lane's word of record `lane`, loaded earlier, and lanes still seeing
 // zero load again; records past the first 64 are loaded here.  `merge` folds each
 // lane's words in record order (first record, then l + 64, ...).  Bounded by the
-// spin limit (a timeout sets the error word and carries on).
+// spin limit (a timeout sets the error word and carries on).  The first 64 words are
+// tested before any load of this function is issued, so that test waits only for
+// the caller's load and not for the (in-order) loads the caller issued after it.
 template <typename Fold>
 __device__ __forceinline__ void poll_words(uint64_t v, __amdgpu_buffer_rsrc_t rs, int C, int st, int word,
                                            uint32_t* err, Fold fold) {
   const int lane = threadIdx.x & 63;
   uint64_t t0 = 0;
-  for (int c0 = 0; c0 < C; c0 += 64) {
-    const int c = c0 + lane;
-    if (c0 > 0 && c < C) v = rec_load(rs, c * st + word * 8);
-    bool ready = !(c < C) || v != 0ull;
+  auto settle = [&](int c, uint64_t& w) {
+    bool ready = !(c < C) || w != 0ull;
     while (__ballot(!ready) != 0ull) {
       if (t0 == 0) t0 = __builtin_amdgcn_s_memrealtime();
       __builtin_amdgcn_s_sleep(1);
       if (!ready) {
-        v = rec_load(rs, c * st + word * 8);
-        ready = v != 0ull;
+        w = rec_load(rs, c * st + word * 8);
+        ready = w != 0ull;
       }
       if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimitTicks) {
         if (lane == 0) __hip_atomic_fetch_or(err, kErrSyncTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
     }
-    if (c < C) fold(c0 == 0, v);
+  };
+  settle(lane, v);
+  if (lane < C) fold(true, v);
+  for (int c0 = 64; c0 < C; c0 += 64) {
+    const int c = c0 + lane;
+    if (c < C) v = rec_load(rs, c * st + word * 8);
+    settle(c, v);
+    if (c < C) fold(false, v);
   }
 }
 

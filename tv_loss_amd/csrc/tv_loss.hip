@@ -356,9 +356,11 @@ __global__ __launch_bounds__(kBlock) void tv_pipe_main(TvArgs a) {
     issue_seg_fixed<DT, NV, NR>(rb, rows, v0, last, live, row_bytes);
   };
   RawChunk<NV, NR> rawA, rawB;
-  int t_0 = pos_of(0), t_p1 = nl > 1 ? pos_of(1) : t_0;
-  prefetch(rawA, t_0, true);
-  prefetch(rawB, t_p1, nl > 1);
+  // Layers -2 and -1 only issue the loads of positions 0 and 1, from the same code
+  // as every later prefetch, so the loop is entered with no load outstanding and
+  // the compiler's count of outstanding loads at the loop head stays exact: each
+  // unpack then waits for its own chunk only, not for the one issued after it.
+  int t_0 = sg, t_p1 = sg;
   int t_m2 = 0, t_m1 = 0;
   uint64_t wpoll[RW];
 #pragma unroll
@@ -445,7 +447,7 @@ __global__ __launch_bounds__(kBlock) void tv_pipe_main(TvArgs a) {
       }
     }
     // ---- position i: unpack, then the poll for i - 1 and the loads of i + 2 ------
-    if (i < nl) {
+    if (i >= 0 && i < nl) {
       const char* rows[NR];
       fwd_rows<DT, NT, G>(a, t_0, rows);
       int lim_l = lim, tail_l = tail, vend_l = vend, V_l = V;
@@ -465,7 +467,7 @@ __global__ __launch_bounds__(kBlock) void tv_pipe_main(TvArgs a) {
     prefetch(rb, t_p2, i + 2 < nl);
     __builtin_amdgcn_sched_barrier(0);
 
-    if (i < nl) {
+    if (i >= 0 && i < nl) {
       // ---- pass 1 of position i ------------------------------------------------
       __builtin_amdgcn_s_setprio(1);
       float zl[NR];
@@ -478,8 +480,8 @@ __global__ __launch_bounds__(kBlock) void tv_pipe_main(TvArgs a) {
       }
       __builtin_amdgcn_s_setprio(0);
     }
-    if (i < nl || do2) __syncthreads();
-    if (i < nl) {
+    if ((i >= 0 && i < nl) || do2) __syncthreads();
+    if (i >= 0 && i < nl) {
       __builtin_amdgcn_s_setprio(3);
       const __amdgpu_buffer_rsrc_t rs = rsrc_rec(t_0);
 #pragma unroll
@@ -529,9 +531,9 @@ __global__ __launch_bounds__(kBlock) void tv_pipe_main(TvArgs a) {
     t_p1 = t_p2;
   };
 
-  // nl + 2 layers, rounded up to an even count so that both buffers keep their
-  // registers across iterations
-  for (int i = 0; i < nl + 2; i += 2) {
+  // nl + 4 layers from -2, rounded up to an even count so that both buffers keep
+  // their registers across iterations
+  for (int i = -2; i < nl + 2; i += 2) {
     layer(i, rawA);
     layer(i + 1, rawB);
   }

@@ -213,10 +213,12 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
     issue_seg_fixed<DT, NV, 2>(rb, rows, v0, last, live, row_bytes);
   };
   RawChunk<NV, 2> rawA, rawB;
-  // groups of items i, i + 1 of the current layer (past the end: an earlier item)
-  int g_0 = group_of(0), g_p1 = nl > 1 ? group_of(1) : g_0;
-  prefetch(rawA, g_0, true);
-  prefetch(rawB, g_p1, nl > 1);
+  // groups of items i, i + 1 of the current layer (past the end: an earlier item).
+  // Layers -2 and -1 only issue the loads of items 0 and 1, from the same code as
+  // every later prefetch, so the loop is entered with no load outstanding and the
+  // compiler's count of outstanding loads at the loop head stays exact: each unpack
+  // then waits for its own chunk only, not for the one issued after it.
+  int g_0 = group_of(0), g_p1 = g_0;
   int g_m2 = 0, g_m1 = 0;          // groups of items i - 2 and i - 1
   bool pair_m2 = false, pair_m1 = false;
   uint64_t wpoll = 0ull;                     // this lane's polled record word
@@ -238,6 +240,11 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
       if (wave == rp || (wave == rq && pair2)) {
         __builtin_amdgcn_s_setprio(3);
         const int row = wave == rp ? 0 : 1;
+        // Waiting for every load in flight first (the next item's chunk included)
+        // measured faster than testing the words as soon as their own load is back:
+        // the test comes later and finds a record missing less often, and a reload
+        // waits for those loads anyway.
+        wait_vmem_all();
         const Lse st = poll_row(wpoll, rsrc_rec(g_m2), C, kSt, row, a.err);
         if (lane == 0) lse_sh[i & 1][row] = lse_log2(st);
         if (TO && row == 1) {
@@ -391,7 +398,7 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
 
     // ---- item i: unpack, then the poll for item i - 1 and the loads of i + 2 ----
     const bool pair = is_pair(g_0);
-    if (i < nl) {
+    if (i >= 0 && i < nl) {
       const char* const rows[2] = {trow_of(g_0), drow_of(g_0)};
       // both rows always (a bonus item's second row is its target row again), so
       // that every load of the buffer is consumed before the buffer is refilled
@@ -413,7 +420,7 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
     prefetch(rb, g_p2, i + 2 < nl);
     __builtin_amdgcn_sched_barrier(0);
 
-    if (i < nl) {
+    if (i >= 0 && i < nl) {
       // ---- pass 1 of item i: wave partials, combined and published --------------
       // (raised priority up to the barrier: the combine and the next layer wait on it)
       __builtin_amdgcn_s_setprio(1);
@@ -487,9 +494,9 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
     g_p1 = g_p2;
   };
 
-  // nl + 2 layers, rounded up to an even count so that both halves of the loop
-  // body always run (the buffers then keep their registers across iterations)
-  for (int i = 0; i < nl + 2; i += 2) {
+  // nl + 4 layers from -2, rounded up to an even count so that both halves of the
+  // loop body always run (the buffers then keep their registers across iterations)
+  for (int i = -2; i < nl + 2; i += 2) {
     layer(i, rawA);
     layer(i + 1, rawB);
   }
