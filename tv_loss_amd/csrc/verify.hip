@@ -519,13 +519,8 @@ __device__ __forceinline__ int wave_inverse_cdf(const float (&v)[NV][PV], float 
     float s = 0.f;
 #pragma unroll
     for (int e = 0; e < PV; ++e) s += v[j][e];
-    float incl = s;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float n = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += n;
-    }
-    const float ex = __shfl_up(incl, 1, 64);
+    const float incl = wave_incl_sum(s);
+    const float ex = __shfl_up(incl, 1, 64);   // the previous lane's inclusive sum exactly
     float cum = base + (lane == 0 ? 0.f : ex);
 #pragma unroll
     for (int e = 0; e < PV; ++e) {
@@ -536,13 +531,10 @@ __device__ __forceinline__ int wave_inverse_cdf(const float (&v)[NV][PV], float 
         lastpos = idx;
       }
     }
-    base += __shfl(incl, 63, 64);
+    base += readlane_f(incl, 63);
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    best = min(best, __shfl_xor(best, o, 64));
-    lastpos = max(lastpos, __shfl_xor(lastpos, o, 64));
-  }
+  best = (int)wave_min_u32((uint32_t)best);
+  lastpos = (int)wave_max_u32((uint32_t)(lastpos + 1)) - 1;
   // blocks are scanned in order, so the smallest crossing index is the first one
   return best != 0x7fffffff ? best : lastpos;
 }
@@ -704,15 +696,10 @@ __global__ void verify_finish(VerifyArgs a) {
       blk += m;
       if (m > 0.f) last_pos = cc;
     }
-    float incl = blk;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float v = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += v;
-    }
+    const float incl = wave_incl_sum(blk);
     const float ex = __shfl_up(incl, 1, 64);
     const float excl = lane == 0 ? 0.f : ex;
-    sc.total = __shfl(incl, 63, 64);
+    sc.total = readlane_f(incl, 63);
     const float tt = up * sc.total;
     sc.owner = -1;
     sc.start = kNegInf;
@@ -728,13 +715,13 @@ __global__ void verify_finish(VerifyArgs a) {
         if (own < 0 && run + m > tt) { own = cc; st0 = run; }
         run += m;
       }
-      sc.owner = __shfl(own, ol, 64);
-      sc.start = __shfl(st0, ol, 64);
+      sc.owner = readlane_i(own, ol);
+      sc.start = readlane_f(st0, ol);
     }
     if (sc.owner < 0) {   // rounding left t past every boundary: last chunk with mass
       const uint64_t pos = __ballot(last_pos >= 0);
       ol = pos ? 63 - __builtin_clzll(pos) : 0;
-      sc.owner = pos ? __shfl(last_pos, ol, 64) : 0;
+      sc.owner = pos ? readlane_i(last_pos, ol) : 0;
       sc.start = kNegInf;
     }
     // the owner chunk's segment masses, from the lane that holds them
@@ -745,7 +732,7 @@ __global__ void verify_finish(VerifyArgs a) {
         float v = 0.f;
 #pragma unroll
         for (int i = 0; i < KC; ++i) v = i == oi ? seg[i][w] : v;
-        oseg[w] = __shfl(v, ol, 64);
+        oseg[w] = readlane_f(v, ol);
       }
     } else {
 #pragma unroll
