@@ -74,13 +74,23 @@ struct RowStats {
   Lse p, q;
 };
 
-__device__ __forceinline__ RowStats merge_records(__amdgpu_buffer_rsrc_t rs, int C, int st, bool pair) {
+// Words 0-2 of record `lane` (clamped into the row, so the loads are unconditional
+// and can go out early); lanes past the last record ignore them.
+struct RecWords {
+  uint64_t w0, w1, w2;
+};
+__device__ __forceinline__ RecWords rec_words(__amdgpu_buffer_rsrc_t rs, int C, int st) {
+  const int l = min((int)(threadIdx.x & 63), C - 1);
+  return RecWords{rec_load(rs, l * st), rec_load(rs, l * st + 8), rec_load(rs, l * st + 16)};
+}
+
+__device__ __forceinline__ RowStats merge_records(const RecWords& r, __amdgpu_buffer_rsrc_t rs, int C, int st,
+                                                  bool pair) {
   const int lane = threadIdx.x & 63;
   Lse a[2] = {lse_empty(), lse_empty()};
   if (lane < C) {
-    const uint64_t w0 = rec_load(rs, lane * st), w1 = rec_load(rs, lane * st + 8), w2 = rec_load(rs, lane * st + 16);
-    a[0] = Lse{unpack_lo(w0), unmark(unpack_hi(w0)), unpack_lo(w2)};
-    if (pair) a[1] = Lse{unpack_lo(w1), unmark(unpack_hi(w1)), 0.f};
+    a[0] = Lse{unpack_lo(r.w0), unmark(unpack_hi(r.w0)), unpack_lo(r.w2)};
+    if (pair) a[1] = Lse{unpack_lo(r.w1), unmark(unpack_hi(r.w1)), 0.f};
   }
   a[0] = lane_records(a[0], rs, C, st, 0, true);
   if (pair) a[1] = lane_records(a[1], rs, C, st, 1, false);
@@ -602,7 +612,9 @@ __global__ void verify_finish(VerifyArgs a) {
   const int C = a.sp.nchunks;
   const int G = a.G, G1 = G + 1;
   const int b = blockIdx.x;
-  const int k = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the row index is wave-uniform: kept in a scalar register, so the record
+  // descriptor built from it is scalar too
+  const int k = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int g = b * G1 + k;
   const bool pair = k < G;
   __shared__ int flag_sh[kMaxRowsPerSeq], token_sh[kMaxRowsPerSeq];
@@ -626,12 +638,32 @@ __global__ void verify_finish(VerifyArgs a) {
   for (int i = 0; i < KC; ++i)
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) seg[i][w] = 0.f;
+  // the given draft token's load goes out first, then the record words and the
+  // pass-2 words, then the loads of the token's two logits, so that the round trips
+  // overlap (all loads are unconditional, at clamped addresses, so none waits for
+  // another)
+  int y = 0;
+  if constexpr (!TO) y = a.tokens[b * G + min(k, G - 1)];
+  const RecWords rw = rec_words(rs, C, kSt);
+  uint64_t pw[KC][kWaves];
+#pragma unroll
+  for (int i = 0; i < KC; ++i)
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) pw[i][w] = p2[(int64_t)min(c0 + i, C - 1) * kWaves + w];
+  bool y_ok = false;
+  float ay = 0.f, by = 0.f;
+  if constexpr (!TO) {
+    y_ok = pair && y >= 0 && y < a.V;
+    const int yc = y_ok ? y : 0;
+    ay = load_one<DT>(trow, yc);
+    by = load_one<DT>(drow, yc);
+  }
 #pragma unroll
   for (int i = 0; i < KC; ++i) {
     if (c0 + i < c1) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const uint64_t v = p2[(int64_t)(c0 + i) * kWaves + w];
+        const uint64_t v = pw[i][w];
         seg[i][w] = to_pair ? p3[(int64_t)(c0 + i) * kWaves + w] : unpack_lo(v);
         om_sum += unpack_hi(v);
         tv_sum += unpack_lo(v);
@@ -645,14 +677,15 @@ __global__ void verify_finish(VerifyArgs a) {
       om_sum += unpack_hi(v);
       tv_sum += unpack_lo(v);
     }
-  // the draft token: given (rejection sampling) or the greedy one (target-only)
-  const int y = !pair ? 0 : TO ? (int)merge_argmax(rs, C, kSt) : a.tokens[b * G + k];
-  const bool y_ok = pair && y >= 0 && y < a.V;
-  const float ay = y_ok ? load_one<DT>(trow, y) : 0.f;
-  const float by = y_ok && !TO ? load_one<DT>(drow, y) : 0.f;
+  // target-only: the greedy draft token from the records, then p at it
+  if constexpr (TO) {
+    y = pair ? (int)merge_argmax(rs, C, kSt) : 0;
+    y_ok = pair && y >= 0 && y < a.V;
+    ay = y_ok ? load_one<DT>(trow, y) : 0.f;
+  }
 
   // ---- row statistics from the pass-1 records ---------------------------------
-  const RowStats st = merge_records(rs, C, kSt, pair);
+  const RowStats st = merge_records(rw, rs, C, kSt, pair);
   const float lse2_p = lse_log2(st.p);
   const float lse2_q = pair ? lse_log2(st.q) : 0.f;
   const bool bad_p = !(__builtin_isfinite(lse2_p));
