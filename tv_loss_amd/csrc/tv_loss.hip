@@ -59,7 +59,7 @@ __device__ __forceinline__ void fwd_rows(const TvArgs& a, int t, const char* (&r
 template <int DT, int NV, int NR>
 __device__ __forceinline__ void fwd_load(const TvArgs& a, const char* const (&rows)[NR], int c,
                                          float (&x)[NR][NV * Elem<DT>::kPerVec]) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int vpc = (int)a.sp.vec_per_chunk, nvec = (int)a.sp.nvec, nfull = (int)a.sp.nvec_full;
   const int vbeg = c * vpc;
   const int vend = min(vbeg + vpc, nvec);
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(kBlock) void tv_fwd_lse(TvArgs a) {
   constexpr int NE = NV * Elem<DT>::kPerVec;
   const int C = a.sp.nchunks;
   const int t = blockIdx.x / C, c = blockIdx.x - t * C;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   __shared__ float part_sh[NR][kWaves * 3];
   const char* rows[NR];
   fwd_rows<DT, FwdShape<G, SHARED>::NT, G>(a, t, rows);
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(kBlock) void tv_fwd_stats(TvArgs a) {
   constexpr int NE = NV * Elem<DT>::kPerVec;
   const int C = a.sp.nchunks;
   const int t = blockIdx.x / C, c = blockIdx.x - t * C;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   __shared__ float lse_sh[NR];
   __shared__ float acc_sh[2 * G][kWaves];
   const char* rows[NR];
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(64 * kFinishWaves) void tv_fwd_finish(TvArgs a) {
   constexpr int NT = FwdShape<G, SHARED>::NT;
   constexpr int NR = FwdShape<G, SHARED>::NR;
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * kFinishWaves + (threadIdx.x >> 6);
+  const int t = blockIdx.x * kFinishWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (t >= a.T) return;
   const int C = a.sp.nchunks;
   float lse2[NR];
@@ -232,7 +232,16 @@ __global__ __launch_bounds__(64 * kFinishWaves) void tv_fwd_finish(TvArgs a) {
 __global__ __launch_bounds__(kBlock) void tv_fwd_mean(TvArgs a) {
   __shared__ float lds[kWaves];
   float sum[1] = {0.f};
-  for (int i = threadIdx.x; i < a.T; i += kBlock) sum[0] += a.pos_ws[i];
+  // eight loads in flight per step, added in the same order as one at a time
+  int i = threadIdx.x;
+  for (; i + 7 * kBlock < a.T; i += 8 * kBlock) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = a.pos_ws[i + j * kBlock];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sum[0] += v[j];
+  }
+  for (; i < a.T; i += kBlock) sum[0] += a.pos_ws[i];
   block_sum<1>(sum, lds);
   for (int i = threadIdx.x; i < a.T; i += kBlock) a.pos_ws[i] = 0.f;
   if (threadIdx.x == 0) a.loss[0] = sum[0] / (float)a.T;
@@ -548,21 +557,28 @@ __global__ __launch_bounds__(64 * kFinishWaves) void tv_pipe_finish(TvArgs a) {
   constexpr int NR = FwdShape<G, SHARED>::NR;
   constexpr int kSt = NR * 8;
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * kFinishWaves + (threadIdx.x >> 6);
+  const int t = blockIdx.x * kFinishWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (t >= a.T) return;
   const int C = a.sp.nchunks;
   const __amdgpu_buffer_rsrc_t rs = rsrc_of(a.part1 + (int64_t)t * C * NR);
+  // every row's first record word and the first partials go out at once (clamped
+  // into the position, so the loads are unconditional); lanes past the last chunk
+  // ignore them
+  const int lc = min(lane, C - 1);
+  float* p2 = a.part2 + (int64_t)t * C * 2 * G;
+  uint64_t v[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) v[r] = rec_load(rs, lc * kSt + r * 8);
+  float pre[2 * G];
+#pragma unroll
+  for (int k = 0; k < 2 * G; ++k) pre[k] = p2[(int64_t)lc * 2 * G + k];
   float lse2[NR];
 #pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    const uint64_t v = lane < C ? rec_load(rs, lane * kSt + r * 8) : 0ull;
-    lse2[r] = lse_log2(poll_row(v, rs, C, kSt, r, a.err));
-  }
-  float* p2 = a.part2 + (int64_t)t * C * 2 * G;
+  for (int r = 0; r < NR; ++r) lse2[r] = lse_log2(poll_row(lane < C ? v[r] : 0ull, rs, C, kSt, r, a.err));
   float tot[2 * G];
 #pragma unroll
-  for (int k = 0; k < 2 * G; ++k) tot[k] = 0.f;
-  for (int cc = lane; cc < C; cc += 64) {
+  for (int k = 0; k < 2 * G; ++k) tot[k] = lane < C ? pre[k] : 0.f;
+  for (int cc = lane + 64; cc < C; cc += 64) {
 #pragma unroll
     for (int k = 0; k < 2 * G; ++k) tot[k] += p2[(int64_t)cc * 2 * G + k];
   }
@@ -899,7 +915,7 @@ __global__ __launch_bounds__(kBlock) void topk_fwd_lse(TvArgs a) {
   constexpr int NE = NV * Elem<DT>::kPerVec;
   const int C = a.sp.nchunks;
   const int t = blockIdx.x / C, c = blockIdx.x - t * C;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   __shared__ float part_sh[G][kWaves * 3];
   const char* db = reinterpret_cast<const char*>(a.draft);
   const char* rows[G];
@@ -927,7 +943,7 @@ __global__ __launch_bounds__(kBlock) void topk_fwd_lse(TvArgs a) {
 template <int DT, int G>
 __global__ __launch_bounds__(64 * kFinishWaves) void topk_fwd_finish(TvArgs a) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * kFinishWaves + (threadIdx.x >> 6);
+  const int t = blockIdx.x * kFinishWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (t >= a.T) return;
   const int C = a.sp.nchunks;
   const int K = a.K;

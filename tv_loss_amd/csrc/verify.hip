@@ -943,7 +943,7 @@ __global__ __launch_bounds__(kBlock) void gumbel_sample_chunks(const char* logit
                                                                uint64_t* keys) {
   constexpr int PV = Elem<DT>::kPerVec;
   const int r = blockIdx.x / nchunks, c = blockIdx.x - r * nchunks;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const char* row = logits + (int64_t)r * row_bytes;
   const int64_t nvec = (V + PV - 1) / PV;
   const uint64_t crow = offset + (uint64_t)r;
@@ -1006,7 +1006,7 @@ __global__ __launch_bounds__(kBlock) void gumbel_sample_chunks(const char* logit
 // as the verify kernels leave theirs, so that the two can share one.
 __global__ __launch_bounds__(kBlock) void gumbel_sample_finish(uint64_t* keys, int rows, int nchunks, int64_t V,
                                                                int32_t* tokens) {
-  const int r = blockIdx.x * kWaves + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int r = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (r >= rows) return;
   float m = kNegInf;
   uint32_t idx = 0xffffffffu;
