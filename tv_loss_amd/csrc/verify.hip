@@ -166,13 +166,24 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
   const int wp = (slot + c) & (kWaves - 1), wq = wp ^ 1;   // combine and publish p / q
   const int rp = wp ^ 2, rq = wp ^ 3;                     // poll p / q records
 
-  // item i of super-group sg is row w = sg + i S; rows are taken k-major (all
-  // k = 0 rows first), so every super-group sees the same mix of pair and bonus
-  // groups
+  // Items are rows w = 0 .. N - 1 taken k-major (all k = 0 rows first).  Super-
+  // groups late in launch order start late (their first loads queue behind those of
+  // the earlier ones; on a full chip the last ones trail the first by about three
+  // layers), so when every super-group has at least four items the middle and last
+  // thirds take one and two items fewer than the first third, each super-group a
+  // contiguous range of items; otherwise super-group sg takes w = sg + i S.
   if (sg >= a.ngroups) return;
-  const int nl = (a.ngroups - 1 - sg) / S + 1;
+  const int N = a.ngroups;
+  int nl = (N - 1 - sg) / S + 1, base = -1;
+  if (S >= 3 && N >= 4 * S) {
+    const int s1 = (S + 2) / 3, s2 = (2 * S + 2) / 3;
+    const int Sd = (S - s1) + (S - s2);                 // items the later thirds give up
+    const int H = (N + Sd) / S, R = N + Sd - H * S;
+    nl = H - (sg >= s1) - (sg >= s2) + (sg < R);
+    base = sg * H - max(0, sg - s1) - max(0, sg - s2) + min(sg, R);
+  }
   auto group_of = [&](int i) {
-    const int w = sg + i * S;
+    const int w = base >= 0 ? base + i : sg + i * S;
     const int k = fast_div(w, a.div_b);
     return (w - k * B) * G1 + k;
   };
