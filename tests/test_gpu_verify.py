@@ -91,6 +91,22 @@ def test_many_chunks_float32(V):
     compare_verify(out, oracle_verify(t, d, y, 8, 40), torch.float32)
 
 
+@pytest.mark.parametrize("extra", [-28, -4, 0, 4, 8])
+def test_item_split_around_four_items_per_super_group(extra):
+    """Super-groups take contiguous, unequal item ranges once every one of them has at
+    least four items (N >= 4 S), round-robin items below: V = 151936 (38 chunks per
+    row), N = B (G + 1) around four items per super-group of the full chip, every
+    output against the oracle."""
+    G, V = 3, 151936
+    smax = torch.cuda.get_device_properties(0).multi_processor_count * 4 // 38
+    B = max(1, smax + extra // 4)
+    w = dict(B=B, G=G, V=V, dtype=torch.bfloat16, kind="normal", scale=1.3, sigma=0.4, seed=17)
+    t, d, y = synthetic.verify_inputs(w, DEV, seed=B)
+    _say("item split", B, "x", G + 1, "items, super-groups at most", smax)
+    out = _run(t, d, y, seed=3, offset=B)
+    compare_verify(out, oracle_verify(t, d, y, 3, B), torch.bfloat16)
+
+
 def test_rollout_full():
     w = synthetic.VERIFY_WORKLOADS["rollout"]
     t, d, y = synthetic.verify_inputs(w, DEV)
