@@ -534,7 +534,7 @@ __device__ __forceinline__ void wave_pass1(float (&x)[R][NE], Lse (&out)[R], flo
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     ref[r] = M[r] > kNegInf ? M[r] * L : 0.f;   // 0 keeps -inf - ref = -inf
-    z0[r] = z1[r] = y0[r] = y1[r] = 0.f;
+    z0[r] = z1[r] = y0[r] = y1[r] = -0.f;   // -0 + x = x: the first additions fold away
   }
 #pragma unroll
   for (int i = 0; i < NE; ++i) {

@@ -291,7 +291,7 @@ __device__ __forceinline__ void lane_pass1(float (&x)[R][NE], float (&ref)[R], f
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     sh[r] = M[r] > kNegInf ? M[r] * L : 0.f;   // 0 keeps -inf - sh = -inf
-    z0[r] = z1[r] = 0.f;
+    z0[r] = z1[r] = -0.f;                       // -0 + e = e: the first addition folds away
   }
 #pragma unroll
   for (int i = 0; i < NE; ++i) {
@@ -403,7 +403,8 @@ __global__ __launch_bounds__(kBlock) void tv_pipe_main(TvArgs a) {
         const float la = href[rt] - lse_sh[par][rt];   // log2 sa (-inf: no p mass here)
         const float lb = href[rq] - lse_sh[par][rq];   // log2 sb
         const float lr = lb - la;
-        float al0 = 0.f, al1 = 0.f, s0_ = 0.f, s1_ = 0.f, scale = 0.f;
+        // sums start at -0, so that the first addition folds away (-0 + x = x)
+        float al0 = -0.f, al1 = -0.f, s0_ = -0.f, s1_ = -0.f, scale = 0.f;
         if (la == kNegInf || lb == kNegInf) {
           scale = 0.f;                                   // one of p, q has no mass here
         } else if (lr <= 0.f) {                          // p units

@@ -288,7 +288,7 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
         rm = sa * hz;
       } else if (la != kNegInf) {
         const float lr = href[1] - lse_sh[i & 1][1] - la;   // log2 of rho
-        float r0 = 0.f, r1 = 0.f;
+        float r0 = -0.f, r1 = -0.f;   // -0 + x = x: the first additions fold away
         if (!(lr > 64.f)) {
           const float rho = fast_exp2(lr);
 #pragma unroll
@@ -306,7 +306,7 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
           om = sa * fmaxf(hz - rw, 0.f);
         } else {
           const float rr = fast_exp2(-lr), sb = fast_exp2(href[1] - lse_sh[i & 1][1]);   // rr = 1 / rho
-          float o0 = 0.f, o1 = 0.f;
+          float o0 = -0.f, o1 = -0.f;
 #pragma unroll 1
           for (int qi = 0; qi < NQ; ++qi) {
             const float4 ea = held[0][qi][t], eb = held[1][qi][t];
@@ -386,7 +386,7 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
           const uint32_t ylo = (uint32_t)s0 * PV;
           float pex = sa * hz;
           if (la != kNegInf && yh >= ylo && yh - ylo < (uint32_t)(kSegVec * PV)) {
-            float m0 = 0.f, m1 = 0.f;
+            float m0 = -0.f, m1 = -0.f;
 #pragma unroll
             for (int qi = 0; qi < NQ; ++qi) {
               const float4 ea = held[0][qi][t];
