@@ -28,7 +28,20 @@
  *  - Workspaces: query the size, allocate it (256-byte aligned), and zero it
  *    once before its first use.  Each call leaves its workspace zeroed again when
  *    it completes, so one workspace can serve any sequence of calls on one
- *    stream.  Calls that use the same workspace concurrently race.
+ *    stream.  Calls that use the same workspace concurrently race.  A workspace
+ *    size depends on the device (how many workgroups it holds at once): size it on
+ *    the device that runs the calls.
+ *  - Co-residency: the verify calls and the single-read TV forward run persistent
+ *    grids whose workgroups exchange row statistics, so every workgroup of a grid
+ *    must be resident on the GPU at the same time.  The grid is sized from the
+ *    device's occupancy for an otherwise idle GPU; work from other streams or
+ *    processes that holds compute units can keep some workgroups waiting.  Every
+ *    such wait is bounded (one second by default, mtp_set_wait_limit): a wait
+ *    that gives up sets the workspace's error word (mtp_workspace_error) and the
+ *    affected rows report it -- verify rows get MTP_ROW_SYNC_TIMEOUT, NaN overlap
+ *    and TV, token -1 and a rejection; TV-loss positions get NaN alpha, S and
+ *    loss.  The call itself still returns MTP_OK (it has returned before the
+ *    kernels run).
  */
 #ifndef MTP_H
 #define MTP_H
@@ -58,6 +71,7 @@ typedef enum { MTP_F32 = 0, MTP_BF16 = 1 } mtp_dtype;
 #define MTP_ROW_BAD_TARGET 2      /* target row has no finite log-sum-exp                 */
 #define MTP_ROW_BAD_DRAFT 4       /* draft row has no finite log-sum-exp                  */
 #define MTP_ROW_RESIDUAL_EMPTY 8  /* max(0, p - q) has no mass: the row sampled from p    */
+#define MTP_ROW_SYNC_TIMEOUT 16   /* a bounded wait for the row's statistics gave up      */
 
 #define MTP_MAX_GAMMA 8
 
@@ -90,7 +104,11 @@ typedef enum { MTP_F32 = 0, MTP_BF16 = 1 } mtp_dtype;
  *   overlap, tv float [batch, gamma], entropy float [batch, gamma+1],
  *   row_status int32 [batch, gamma+1] (MTP_ROW_* bits).
  * Rows with MTP_ROW_BAD_TARGET / MTP_ROW_BAD_DRAFT give NaN statistics, token -1
- * and a rejection.  batch == 0 is a no-op.
+ * and a rejection; MTP_ROW_SYNC_TIMEOUT rows (see Co-residency above) give NaN
+ * overlap and TV, token -1 and a rejection (their entropy needs no exchange and
+ * stays valid).  The acceptance ratio is formed in float64 from the float32 row
+ * sums, and the inverse CDF's cumulative sums run in float64.
+ * batch == 0 is a no-op.
  * Limits: 1 <= gamma <= MTP_MAX_GAMMA, 1 <= vocab <= 2^30, strides >= vocab.
  */
 mtp_status mtp_verify_workspace_size(int32_t batch, int32_t gamma, int32_t vocab, mtp_dtype dtype,
@@ -296,9 +314,18 @@ mtp_status mtp_tv_topk_bwd(const int32_t* target_idx, const float* target_val, i
 
 /* ------------------------------------------------------------------------ */
 /* Error word of a workspace: non-zero if a kernel that used it hit its bounded
- * wait limit (the cluster exchange did not complete within one second).  Copies
- * the 32-bit word to host memory, synchronising `stream`. */
+ * wait limit (the exchange of row statistics between workgroups did not complete
+ * in time).  Copies the 32-bit word to host memory, synchronising `stream`.  The
+ * word stays set until the caller clears it. */
 mtp_status mtp_workspace_error(const void* workspace, uint32_t* host_word, void* stream);
+
+/* Diagnostics: the bound on every wait for row statistics exchanged between
+ * workgroups, in ticks of the GPU's 100 MHz constant clock (default 100000000 =
+ * one second), for the calls launched after it is set (process-wide).  0 makes a
+ * wait give up as soon as a record is missing, which exercises the failure
+ * reporting described under Co-residency without stalling any kernel.  Returns
+ * the previous bound. */
+uint64_t mtp_set_wait_limit(uint64_t ticks);
 
 const char* mtp_status_string(mtp_status s);
 const char* mtp_last_error(void);

@@ -86,6 +86,36 @@ def inverse_cdf(r, t):
     return v, lo, float(c[v])
 
 
+# READING (near-ties of the inverse CDF): a float32 evaluation carries rounding in
+# its cumulative sums, so where t lies within CDF_TIE_BAND * sum r of a boundary
+# C_v it may pick the token on the other side.  The band bounds that error; the
+# tokens it admits are listed exactly (cdf_allowed), so a flagged row still has
+# at most a few correct answers.
+CDF_TIE_BAND = 1e-6
+# READING: an acceptance decision whose |u - min(1, ratio)| is within this band may
+# go either way in a float evaluation of the ratio.
+ACCEPT_TIE_BAND = 1e-6
+
+
+def cdf_allowed(r, t, band):
+    """Every token an inverse CDF of r whose cumulative sums are each off by at most
+    `band` (absolute) may return for t: the v with r_v > 0 whose interval
+    [C_{v-1}, C_v) meets [t - band, t + band].  Contains inverse_cdf(r, t)'s token
+    (t < sum r); with a small band it adds only the nearest positive-mass token
+    across a boundary that t lies near.  Sorted int64 array."""
+    c = np.cumsum(r)
+    lo_edge = np.concatenate(([0.0], c[:-1]))
+    return np.flatnonzero((r > 0) & (lo_edge <= t + band) & (c > t - band))
+
+
+def cdf_tie_probability(r, band_rel):
+    """Upper bound on the chance, over t uniform on [0, sum r), that cdf_allowed
+    admits more than one token: every boundary between two positive-mass tokens
+    flags an interval of width 2 band around it (union bound)."""
+    n_pos = int(np.count_nonzero(r > 0))
+    return min(1.0, 2.0 * band_rel * max(n_pos - 1, 0))
+
+
 def accept_decision(u, logp_y, logq_y):
     """Accept iff u < min(1, p(y)/q(y)) (paperlayer Sec. 2 "Acceptance methods",
     App. G.1; rainbus "Rejection Sampling").
@@ -101,14 +131,19 @@ def accept_decision(u, logp_y, logq_y):
     return (1 if u < min(1.0, ratio) else 0), ratio
 
 
-def row_sample(p, q, u_prime, cdf_tie_band=1e-6):
+def row_sample(p, q, u_prime, cdf_tie_band=CDF_TIE_BAND, identical=False):
     """The token a row emits when it is the first rejection (or the bonus row).
 
     r = max(0, p - q) when q is given, else r = p (bonus row).  READING: if the
-    residual has no mass (p = q up to rounding) the row samples from p instead.
+    residual has no mass (p = q exactly) the row samples from p instead.
     t = u' * sum r; the token is inverse_cdf(r, t).
-    Returns (token, residual_was_empty, near_tie); near_tie is also set when the
-    residual mass is below cdf_tie_band (a float32 evaluation may find it empty).
+    Returns (token, residual_was_empty, allowed): `allowed` lists the tokens a
+    float32 evaluation may return (cdf_allowed with band cdf_tie_band * sum r).
+    READING: a residual whose mass is below cdf_tie_band is below what a float32
+    sum resolves: such an evaluation may find it empty (and sample p) or form it
+    from rounding noise, so every token with p > 0 is allowed there -- unless the
+    two rows are the same logits (`identical`), which any evaluation turns into the
+    same p and q, so that the residual is exactly empty there too.
     """
     empty = False
     near_empty = False
@@ -117,19 +152,66 @@ def row_sample(p, q, u_prime, cdf_tie_band=1e-6):
     else:
         r = residual(p, q)
         mass = float(np.sum(r))
-        # a float32 sum cannot tell a residual below ~1e-6 from an empty one
-        near_empty = mass < cdf_tie_band
+        near_empty = mass < cdf_tie_band and not identical
         if not mass > 0:
             empty = True
             r = p
     total = float(np.cumsum(r)[-1])
     t = u_prime * total
-    tok, lo, hi = inverse_cdf(r, t)
-    band = cdf_tie_band * total
-    return tok, empty, near_empty or (abs(t - lo) <= band) or (abs(t - hi) <= band)
+    tok, _, _ = inverse_cdf(r, t)
+    allowed = cdf_allowed(r, t, cdf_tie_band * total)
+    if near_empty:
+        allowed = np.flatnonzero(p > 0)
+    assert tok in allowed
+    return tok, empty, allowed
 
 
-def verify(target, draft, tokens, seed, offset, tie_band=1e-6, cdf_tie_band=1e-6):
+def _near_empty(p, q, cdf_tie_band, identical):
+    """The residual max(0, p - q) is below what a float32 sum resolves (see
+    row_sample)."""
+    return float(np.sum(residual(p, q))) < cdf_tie_band and not identical
+
+
+def _row_tie_bound(p, q, cdf_tie_band, identical=False):
+    """cdf_tie_probability of the distribution a row samples (1 for a near-empty
+    residual, whose row is always flagged)."""
+    if q is None:
+        return cdf_tie_probability(p, cdf_tie_band)
+    r = residual(p, q)
+    mass = float(np.sum(r))
+    if _near_empty(p, q, cdf_tie_band, identical):
+        return 1.0
+    return cdf_tie_probability(r if mass > 0 else p, cdf_tie_band)
+
+
+def _accept_tie_bound(ratio, tie_band):
+    """Chance, over u uniform on [0, 1), that |u - min(1, ratio)| <= tie_band."""
+    return min(1.0, tie_band if ratio >= 1.0 else 2.0 * tie_band)
+
+
+def _new_outputs(B, G, u, up):
+    G1 = G + 1
+    return dict(
+        accept=np.zeros((B, G), np.uint8), accepted_len=np.zeros(B, np.int32),
+        next_token=np.full(B, -1, np.int32), row_token=np.full((B, G1), -1, np.int32),
+        overlap=np.full((B, G), np.nan), tv=np.full((B, G), np.nan),
+        entropy=np.full((B, G1), np.nan), row_status=np.zeros((B, G1), np.int32),
+        ratio=np.full((B, G), np.nan), u=u, u_prime=up,
+        accept_tie=np.zeros((B, G), bool), accept_tie_bound=np.zeros((B, G)),
+        token_tie=np.zeros((B, G1), bool), token_tie_bound=np.zeros((B, G1)),
+        token_allowed=np.empty((B, G1), object), near_empty=np.zeros((B, G1), bool),
+        lse_p=np.full((B, G1), np.nan), lse_q=np.full((B, G), np.nan),
+    )
+
+
+def _set_token(out, b, k, tok, allowed, bound):
+    out["row_token"][b, k] = tok
+    out["token_allowed"][b, k] = allowed
+    out["token_tie"][b, k] = allowed.size > 1
+    out["token_tie_bound"][b, k] = bound
+
+
+def verify(target, draft, tokens, seed, offset, tie_band=ACCEPT_TIE_BAND, cdf_tie_band=CDF_TIE_BAND):
     """Rejection-sampling verification of gamma drafted tokens per sequence.
 
     target: float64 [B, gamma+1, V] -- target logits at the gamma draft positions
@@ -153,9 +235,11 @@ def verify(target, draft, tokens, seed, offset, tie_band=1e-6, cdf_tie_band=1e-6
          t = u'_k * sum r; token = inverse_cdf(r, t).
       8. next_token_b = row_token[b, n_b].
 
-    Near-ties: accept_tie marks |u - min(1, ratio)| <= tie_band; token_tie marks t
-    within cdf_tie_band * sum r of either boundary of the chosen token's interval.
-    There a float32 computation may legitimately decide the other way.
+    Near-ties: accept_tie marks |u - min(1, ratio)| <= tie_band, where a float
+    evaluation may decide the other way; token_allowed[b, k] lists every token a
+    float32 inverse CDF may return (row_sample), token_tie marks rows with more
+    than one.  accept_tie_bound / token_tie_bound are each flag's probability bound
+    over the uniforms, for bounding how many flags a batch may carry.
     """
     target = np.asarray(target, dtype=np.float64)
     draft = np.asarray(draft, dtype=np.float64)
@@ -167,34 +251,28 @@ def verify(target, draft, tokens, seed, offset, tie_band=1e-6, cdf_tie_band=1e-6
     pos = np.arange(B * G1, dtype=np.uint64).reshape(B, G1)
     u, up = verify_uniforms(seed, offset, pos)
 
-    out = dict(
-        accept=np.zeros((B, G), np.uint8), accepted_len=np.zeros(B, np.int32),
-        next_token=np.full(B, -1, np.int32), row_token=np.full((B, G1), -1, np.int32),
-        overlap=np.full((B, G), np.nan), tv=np.full((B, G), np.nan),
-        entropy=np.full((B, G1), np.nan), row_status=np.zeros((B, G1), np.int32),
-        ratio=np.full((B, G), np.nan), u=u, u_prime=up,
-        accept_tie=np.zeros((B, G), bool), token_tie=np.zeros((B, G1), bool),
-        lse_p=np.full((B, G1), np.nan), lse_q=np.full((B, G), np.nan),
-    )
+    out = _new_outputs(B, G, u, up)
     for b in range(B):
         for k in range(G1):
             logp, lse_p = log_softmax(target[b, k])
             out["lse_p"][b, k] = lse_p
             if logp is None:
                 out["row_status"][b, k] |= BAD_TARGET
+                out["token_allowed"][b, k] = np.array([-1])
             else:
                 out["entropy"][b, k] = entropy(logp)
             if k == G:                                   # bonus row: r = p
                 if logp is not None:
-                    tok, _, tie = row_sample(np.exp(logp), None, up[b, k], cdf_tie_band)
-                    out["row_token"][b, k] = tok
-                    out["token_tie"][b, k] = tie
+                    p = np.exp(logp)
+                    tok, _, allowed = row_sample(p, None, up[b, k], cdf_tie_band)
+                    _set_token(out, b, k, tok, allowed, _row_tie_bound(p, None, cdf_tie_band))
                 continue
             logq, lse_q = log_softmax(draft[b, k])
             out["lse_q"][b, k] = lse_q
             y = int(tokens[b, k])
             if logq is None:
                 out["row_status"][b, k] |= BAD_DRAFT
+                out["token_allowed"][b, k] = np.array([-1])
             if not (0 <= y < V):
                 out["row_status"][b, k] |= BAD_TOKEN
             if logp is None or logq is None:
@@ -207,11 +285,13 @@ def verify(target, draft, tokens, seed, offset, tie_band=1e-6, cdf_tie_band=1e-6
                 out["ratio"][b, k] = ratio
                 out["accept"][b, k] = flag
                 out["accept_tie"][b, k] = abs(u[b, k] - min(1.0, ratio)) <= tie_band
-            tok, empty, tie = row_sample(p, q, up[b, k], cdf_tie_band)
+                out["accept_tie_bound"][b, k] = _accept_tie_bound(ratio, tie_band)
+            same = bool(np.array_equal(target[b, k], draft[b, k]))
+            tok, empty, allowed = row_sample(p, q, up[b, k], cdf_tie_band, identical=same)
             if empty:
                 out["row_status"][b, k] |= RESIDUAL_EMPTY
-            out["row_token"][b, k] = tok
-            out["token_tie"][b, k] = tie
+            out["near_empty"][b, k] = _near_empty(p, q, cdf_tie_band, same)
+            _set_token(out, b, k, tok, allowed, _row_tie_bound(p, q, cdf_tie_band, same))
         n = 0
         while n < G and out["accept"][b, n] == 1:
             n += 1
@@ -228,7 +308,15 @@ def greedy_draft_token(draft_logits):
     return int(np.argmax(np.asarray(draft_logits, dtype=np.float64)))
 
 
-def target_only_row_sample(p, yhat, u_prime, cdf_tie_band=1e-6):
+def target_only_residual(p, yhat):
+    """p with the greedy token removed: the residual max(0, p - delta_yhat) of the
+    point-mass draft at yhat (see target_only_row_sample)."""
+    r = np.array(p, dtype=np.float64)
+    r[yhat] = 0.0
+    return r
+
+
+def target_only_row_sample(p, yhat, u_prime, cdf_tie_band=CDF_TIE_BAND):
     """The token a rejected target-only row emits.
 
     READING: the pages give target-only acceptance (probability p(yhat)) but not the
@@ -238,23 +326,25 @@ def target_only_row_sample(p, yhat, u_prime, cdf_tie_band=1e-6):
     is p with yhat removed, which keeps the emitted token's law exactly p.  If that
     residual has no mass (p(yhat) = 1) the row samples from p (flagged, as in
     row_sample).  t = u' * sum r; the token is inverse_cdf(r, t).
-    Returns (token, residual_was_empty, near_tie).
+    Returns (token, residual_was_empty, allowed) as row_sample does.
     """
-    r = np.array(p, dtype=np.float64)
-    r[yhat] = 0.0
+    r = target_only_residual(p, yhat)
     mass = float(np.sum(r))
-    near_empty = mass < cdf_tie_band
+    near_empty = 0.0 < mass < cdf_tie_band
     empty = not mass > 0
     if empty:
         r = np.asarray(p, dtype=np.float64)
     total = float(np.cumsum(r)[-1])
     t = u_prime * total
-    tok, lo, hi = inverse_cdf(r, t)
-    band = cdf_tie_band * total
-    return tok, empty, near_empty or (abs(t - lo) <= band) or (abs(t - hi) <= band)
+    tok, _, _ = inverse_cdf(r, t)
+    allowed = cdf_allowed(r, t, cdf_tie_band * total)
+    if near_empty:
+        allowed = np.flatnonzero(np.asarray(p) > 0)
+    assert tok in allowed
+    return tok, empty, allowed
 
 
-def verify_target_only(target, draft, seed, offset, tie_band=1e-6, cdf_tie_band=1e-6):
+def verify_target_only(target, draft, seed, offset, tie_band=ACCEPT_TIE_BAND, cdf_tie_band=CDF_TIE_BAND):
     """Target-only verification of gamma draft positions per sequence, with the
     rejection-sampling statistics and the RS/TO diagnostic.
 
@@ -286,32 +376,27 @@ def verify_target_only(target, draft, seed, offset, tie_band=1e-6, cdf_tie_band=
     pos = np.arange(B * G1, dtype=np.uint64).reshape(B, G1)
     u, up = verify_uniforms(seed, offset, pos)
 
-    out = dict(
-        accept=np.zeros((B, G), np.uint8), accepted_len=np.zeros(B, np.int32),
-        next_token=np.full(B, -1, np.int32), row_token=np.full((B, G1), -1, np.int32),
-        draft_token=np.full((B, G), -1, np.int32), p_yhat=np.full((B, G), np.nan),
-        rs_better=np.zeros((B, G), np.uint8), rs_tie=np.zeros((B, G), bool),
-        overlap=np.full((B, G), np.nan), tv=np.full((B, G), np.nan),
-        entropy=np.full((B, G1), np.nan), row_status=np.zeros((B, G1), np.int32),
-        u=u, u_prime=up,
-        accept_tie=np.zeros((B, G), bool), token_tie=np.zeros((B, G1), bool),
-    )
+    out = _new_outputs(B, G, u, up)
+    out.update(draft_token=np.full((B, G), -1, np.int32), p_yhat=np.full((B, G), np.nan),
+               rs_better=np.zeros((B, G), np.uint8), rs_tie=np.zeros((B, G), bool))
     for b in range(B):
         for k in range(G1):
             logp, _ = log_softmax(target[b, k])
             if logp is None:
                 out["row_status"][b, k] |= BAD_TARGET
+                out["token_allowed"][b, k] = np.array([-1])
             else:
                 out["entropy"][b, k] = entropy(logp)
             if k == G:                                   # bonus row: r = p
                 if logp is not None:
-                    tok, _, tie = row_sample(np.exp(logp), None, up[b, k], cdf_tie_band)
-                    out["row_token"][b, k] = tok
-                    out["token_tie"][b, k] = tie
+                    p = np.exp(logp)
+                    tok, _, allowed = row_sample(p, None, up[b, k], cdf_tie_band)
+                    _set_token(out, b, k, tok, allowed, _row_tie_bound(p, None, cdf_tie_band))
                 continue
             logq, _ = log_softmax(draft[b, k])
             if logq is None:
                 out["row_status"][b, k] |= BAD_DRAFT
+                out["token_allowed"][b, k] = np.array([-1])
             if logp is None or logq is None:
                 continue
             p, q = np.exp(logp), np.exp(logq)
@@ -321,16 +406,20 @@ def verify_target_only(target, draft, seed, offset, tie_band=1e-6, cdf_tie_band=
             out["p_yhat"][b, k] = py
             out["accept"][b, k] = 1 if u[b, k] < py else 0
             out["accept_tie"][b, k] = abs(u[b, k] - py) <= tie_band
+            out["accept_tie_bound"][b, k] = _accept_tie_bound(py, tie_band)
             out["overlap"][b, k] = overlap(p, q)
             tv = tv_distance(p, q)
             out["tv"][b, k] = tv
             out["rs_better"][b, k] = 1 if tv < 1.0 - py else 0
             out["rs_tie"][b, k] = abs(tv - (1.0 - py)) <= tie_band
-            tok, empty, tie = target_only_row_sample(p, yhat, up[b, k], cdf_tie_band)
+            tok, empty, allowed = target_only_row_sample(p, yhat, up[b, k], cdf_tie_band)
             if empty:
                 out["row_status"][b, k] |= RESIDUAL_EMPTY
-            out["row_token"][b, k] = tok
-            out["token_tie"][b, k] = tie
+            r = target_only_residual(p, yhat)
+            mass = float(np.sum(r))
+            out["near_empty"][b, k] = 0.0 < mass < cdf_tie_band
+            bound = 1.0 if out["near_empty"][b, k] else cdf_tie_probability(r if mass > 0 else p, cdf_tie_band)
+            _set_token(out, b, k, tok, allowed, bound)
         n = 0
         while n < G and out["accept"][b, n] == 1:
             n += 1
@@ -339,19 +428,26 @@ def verify_target_only(target, draft, seed, offset, tie_band=1e-6, cdf_tie_band=
     return out
 
 
-def gumbel_argmax(logw, U, gap_band=1e-4):
+# READING (near-ties of the Gumbel-max argmax): keys within this gap of the winner
+# (natural-log units) may be ordered differently by a float32 evaluation.
+GUMBEL_GAP_BAND = 1e-4
+
+
+def gumbel_argmax(logw, U, gap_band=GUMBEL_GAP_BAND):
     """argmax_v (log w_v + G_v) with G_v = -log(-log U_v): the Gumbel-max trick, a
     sample from w / sum w (paperlayer App. G.2 "Gumbel-Max Trick (vLLM)").  Entries
     with w_v = 0 (log w_v = -inf) never win.  READING: ties go to the smallest index.
-    Returns (token, near_tie): near_tie marks a runner-up key within gap_band of the
-    winner's, where a float32 evaluation of the keys may choose the other token.
+    Returns (token, allowed): `allowed` lists the tokens whose key lies within
+    gap_band of the winner's (the winner included), any of which a float32
+    evaluation of the keys may choose.
     """
     keys = np.asarray(logw, dtype=np.float64) - np.log(-np.log(np.asarray(U, dtype=np.float64)))
     tok = int(np.argmax(keys))
     top = keys[tok]
-    rest = np.delete(keys, tok)
-    near = bool(rest.size) and bool(np.max(rest) >= top - gap_band)
-    return tok, near
+    allowed = np.flatnonzero(np.isfinite(keys) & (keys >= top - gap_band))
+    if tok not in allowed:         # no finite key: argmax is index 0 of an all -inf row
+        allowed = np.array([tok])
+    return tok, allowed
 
 
 def gumbel_draft_tokens(draft, seed, offset, temperature=1.0):
@@ -359,18 +455,20 @@ def gumbel_draft_tokens(draft, seed, offset, temperature=1.0):
     (z_v / T + G_v) for each row of draft logits z [..., V] (App. G.2: argmax of
     log q / T + G, and log q differs from z / T by a constant).  Row r (in
     row-major order) uses element_uniforms(seed, offset, r, V).  Returns (tokens,
-    near_tie) of the leading shape."""
+    allowed) of the leading shape, `allowed` an object array of the tokens
+    gumbel_argmax admits per row."""
     z = np.asarray(draft, dtype=np.float64)
     lead, V = z.shape[:-1], z.shape[-1]
     flat = z.reshape(-1, V)
     tok = np.zeros(flat.shape[0], np.int32)
-    tie = np.zeros(flat.shape[0], bool)
+    allowed = np.empty(flat.shape[0], object)
     for r in range(flat.shape[0]):
-        tok[r], tie[r] = gumbel_argmax(flat[r] / temperature, element_uniforms(seed, offset, r, V))
-    return tok.reshape(lead), tie.reshape(lead)
+        tok[r], allowed[r] = gumbel_argmax(flat[r] / temperature, element_uniforms(seed, offset, r, V))
+    return tok.reshape(lead), allowed.reshape(lead)
 
 
-def verify_gumbel(target, draft, tokens, seed, offset, temperature=1.0, tie_band=1e-6, cdf_tie_band=1e-6):
+def verify_gumbel(target, draft, tokens, seed, offset, temperature=1.0, tie_band=ACCEPT_TIE_BAND,
+                  cdf_tie_band=CDF_TIE_BAND, gap_band=GUMBEL_GAP_BAND):
     """Rejection-sampling verification at temperature T with Gumbel-max sampling of
     the emitted tokens (paperlayer App. G.2, "Gumbel-Max Trick (vLLM)").
 
@@ -380,8 +478,13 @@ def verify_gumbel(target, draft, tokens, seed, offset, temperature=1.0, tie_band
       7. Row sample: r = max(0, p_k - q_k) (k < gamma) or p_gamma (bonus row); the
          token is gumbel_argmax(log r, U) with U = element_uniforms(seed, offset,
          b*(gamma+1) + k, V); an empty residual samples p the same way (flagged).
-    Acceptance uses the same u as verify; token_tie marks a near-tie of the keys
-    (or a residual below cdf_tie_band, as in row_sample).
+    Acceptance uses the same u as verify; token_allowed lists the tokens within the
+    key gap band of the winner (every token with p > 0 for a residual below
+    cdf_tie_band, as in row_sample).  token_tie_bound is e^gap_band - 1 per row: in
+    the exponential-race form of the trick the winner's clock T1 ~ Exp(sum w) and
+    the runner-up arrives an independent Exp(sum w - w_win) later (memoryless
+    clocks), so the chance that log T2 - log T1 < gap_band is at most
+    e^gap_band - 1.
     """
     target = np.asarray(target, dtype=np.float64) / temperature
     draft = np.asarray(draft, dtype=np.float64) / temperature
@@ -403,13 +506,14 @@ def verify_gumbel(target, draft, tokens, seed, offset, temperature=1.0, tie_band
                     continue
                 r = residual(p, np.exp(logq))
                 mass = float(np.sum(r))
-                near_empty = mass < cdf_tie_band
+                near_empty = _near_empty(p, np.exp(logq), cdf_tie_band, bool(np.array_equal(target[b, k], draft[b, k])))
                 if mass > 0:
                     w = r
             with np.errstate(divide="ignore"):
-                tok, near = gumbel_argmax(np.log(w), U)
-            out["row_token"][b, k] = tok
-            out["token_tie"][b, k] = near or near_empty
+                tok, allowed = gumbel_argmax(np.log(w), U, gap_band)
+            if near_empty:
+                allowed = np.flatnonzero(p > 0)
+            _set_token(out, b, k, tok, allowed, 1.0 if near_empty else float(np.expm1(gap_band)))
         n = out["accepted_len"][b]
         out["next_token"][b] = out["row_token"][b, n]
     return out

@@ -22,8 +22,8 @@ from scipy import special, stats
 import synthetic
 import tv_loss_amd as mtp
 from oracle import mtp as omtp
-from parity import (compare_target_only, compare_verify, oracle_target_only, oracle_verify, stat_close,
-                    to_f64)
+from parity import (check_tokens, compare_target_only, compare_verify, oracle_target_only, oracle_verify,
+                    stat_close, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -51,8 +51,10 @@ def _oracle(target, draft, tokens, T, seed, offset):
     return omtp.verify_gumbel(to_f64(target), to_f64(draft), tokens.cpu().numpy(), seed, offset, temperature=T)
 
 
-def _pad(t, d, V, dtype, fill=float("-inf")):
-    """Rows must start 16-byte aligned: pad the vocabulary dimension."""
+def _pad(t, d, V, dtype, fill=30.0):
+    """Rows must start 16-byte aligned: pad the vocabulary dimension, by default
+    with a large finite logit (exact in bf16), so a read past V would change every
+    statistic and token."""
     pv = 16 // (torch.finfo(dtype).bits // 8)
     pad = (-V) % pv
     if not pad:
@@ -65,11 +67,9 @@ def _pad(t, d, V, dtype, fill=float("-inf")):
 
 
 def _compare_sampler(tokens, draft, T, seed, offset):
-    ref, near = omtp.gumbel_draft_tokens(to_f64(draft), seed, offset, temperature=T)
-    got = tokens.cpu().numpy()
-    bad = (got != ref) & ~near
-    assert not bad.any(), f"sampler mismatch at {np.argwhere(bad)[:10]}: {got[bad][:10]} vs {ref[bad][:10]}"
-    return int(near.sum())
+    ref, allowed = omtp.gumbel_draft_tokens(to_f64(draft), seed, offset, temperature=T)
+    check_tokens(tokens.cpu().numpy(), ref, allowed)
+    return int(sum(a.size > 1 for a in allowed.ravel()))
 
 
 @pytest.mark.parametrize("T", [0.6, 1.0, 1.7])

@@ -40,8 +40,10 @@ def _say(*a):
     print(*a, flush=True)
 
 
-def _pad(t, d, V, dtype, fill=float("-inf")):
-    """Rows must start 16-byte aligned: pad the vocabulary dimension."""
+def _pad(t, d, V, dtype, fill=30.0):
+    """Rows must start 16-byte aligned: pad the vocabulary dimension, by default
+    with a large finite logit (exact in bf16), so a read past V would change every
+    statistic and token."""
     pv = 16 // (torch.finfo(dtype).bits // 8)
     pad = (-V) % pv
     if not pad:

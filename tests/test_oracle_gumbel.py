@@ -54,8 +54,33 @@ def test_gumbel_max_ties_and_zero_weights():
     U = np.full(6, 0.5)
     assert mtp.gumbel_argmax(np.log(np.array([1.0, 2.0, 2.0, 0.5, 2.0, 1.0])), U)[0] == 1
     assert mtp.gumbel_argmax(np.array([-np.inf, -np.inf, 0.0, -np.inf]), np.full(4, 0.999))[0] == 2
-    tok, near = mtp.gumbel_argmax(np.log(np.array([1.0, 1.0 + 1e-9])), np.full(2, 0.3))
-    assert tok == 1 and near
+    tok, allowed = mtp.gumbel_argmax(np.log(np.array([1.0, 1.0 + 1e-9])), np.full(2, 0.3))
+    assert tok == 1 and list(allowed) == [0, 1]
+    tok, allowed = mtp.gumbel_argmax(np.log(np.array([1.0, 2.0, 1.0])), np.array([0.3, 0.3, 0.9]))
+    assert list(allowed) == [tok]
+    tok, allowed = mtp.gumbel_argmax(np.full(3, -np.inf), np.full(3, 0.5))
+    assert tok == 0 and list(allowed) == [0]
+
+
+def test_gumbel_gap_probability_bound():
+    """The chance that the runner-up key lies within a gap g of the winner is at
+    most e^g - 1 (the bound verify_gumbel reports per row): Monte-Carlo over many
+    uniform vectors, for skewed weights, and for n equal weights, where the chance is
+    exactly (n - 1) c / (n + (n - 1) c) with c = e^g - 1 (the winner's clock is
+    Exp(n), the runner-up's lead an independent Exp(n - 1))."""
+    rng = np.random.default_rng(12)
+    g = 0.05
+    for w in (np.ones(40), np.exp(rng.normal(0, 2, 40))):
+        n, hits = 20000, 0
+        for r in range(n):
+            _, allowed = mtp.gumbel_argmax(np.log(w), element_uniforms(99, 1, r, w.size), gap_band=g)
+            hits += allowed.size > 1
+        bound = np.expm1(g)
+        assert hits / n <= bound + 5 * np.sqrt(bound / n)
+        if np.all(w == 1.0):
+            m = w.size
+            exact = (m - 1) * bound / (m + (m - 1) * bound)
+            assert abs(hits / n - exact) <= 5 * np.sqrt(exact / n)
 
 
 def test_tempered_verify_reduces_to_plain_verify_of_scaled_logits():

@@ -136,3 +136,27 @@ def test_repeated_indices_entry_by_entry_is_order_free():
     assert a[0] == pytest.approx(b[0], rel=1e-14)
     np.testing.assert_allclose(mtp.tv_topk_loss_grad(idx, val, dr), mtp.tv_topk_loss_grad(idx[:, perm], val[:, perm], dr),
                                rtol=1e-13, atol=1e-17)
+
+
+def test_indicator_margin_closed_form():
+    """tv_topk_indicator_margin = |log q(I_j) - log p_j| per entry, pinned by a closed
+    form: when the K target logits are the draft logits at their indices plus a
+    constant, the truncated target is q restricted to the entries and renormalised,
+    so every entry's margin is |log Q| with Q the draft mass on the entries; an
+    entry out of range gets inf."""
+    rng = np.random.default_rng(41)
+    T, G, V, K = 2, 2, 40, 7
+    dr = rng.normal(0, 1.2, (T, G, V))
+    idx = np.stack([np.stack([rng.choice(V, K, replace=False) for _ in range(G)]) for _ in range(T)])
+    val = np.take_along_axis(dr, idx, -1) + 3.25
+    idx = idx.copy()
+    idx[0, 1, 4] = V + 5
+    val[0, 1, 4] = 0.0
+    m = mtp.tv_topk_indicator_margin(idx, val, dr)
+    q = np.exp(dr - np.log(np.exp(dr).sum(-1, keepdims=True)))
+    for t in range(T):
+        for k in range(G):
+            ok = idx[t, k] < V
+            Q = q[t, k, idx[t, k][ok]].sum()
+            np.testing.assert_allclose(m[t, k][ok], abs(np.log(Q)), rtol=1e-10)
+            assert np.all(np.isinf(m[t, k][~ok]))

@@ -150,3 +150,26 @@ def test_row_without_a_finite_normaliser_is_a_data_error():
     assert np.allclose(saved[0], saved_ok[0]) and np.isclose(pos[0], pos_ok[0])
     g = mtp.tv_loss_grad(t_bad, d_bad)
     assert np.isnan(g[1]).all() and np.isfinite(g[0]).all()
+
+
+def test_indicator_margin_closed_forms():
+    """indicator_margin = |log q_v - log p_v| (the TV tests excuse indicator flips
+    where it is tiny), pinned by closed forms: a draft equal to the target shifted
+    by a constant has q = p (margin 0); a draft that raises one logit j by d has
+    log q_v - log p_v = -log(1 + p_j (e^d - 1)) off j and d plus that at j."""
+    rng = np.random.default_rng(40)
+    T, G, V = 2, 3, 50
+    tgt = rng.normal(0, 1.5, (T, V))
+    dr = tgt[:, None, :] + np.array([0.0, 2.5, -7.0])[None, :, None]
+    assert np.abs(mtp.indicator_margin(tgt, dr)).max() < 1e-12
+    j, d = 17, 0.8
+    dr = np.repeat(tgt[:, None, :], G, axis=1)
+    dr[:, 1, j] += d
+    m = mtp.indicator_margin(tgt, dr)
+    p = np.exp(tgt - np.log(np.exp(tgt).sum(-1, keepdims=True)))
+    shift = np.log1p(p[:, j] * np.expm1(d))
+    for t in range(T):
+        expect = np.full(V, shift[t])
+        expect[j] = abs(d - shift[t])
+        np.testing.assert_allclose(m[t, 1], expect, rtol=1e-10, atol=1e-13)
+        assert np.abs(m[t, 0]).max() < 1e-12 and np.abs(m[t, 2]).max() < 1e-12

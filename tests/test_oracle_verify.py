@@ -101,6 +101,94 @@ def test_inverse_cdf_rules():
     assert mtp.inverse_cdf(np.array([0, 0, 1.0, 0]), 0.999)[0] == 2
 
 
+def _perturbed_inverse_cdf(r, t, delta):
+    """Inverse CDF of r evaluated with every cumulative sum at a positive-mass token
+    moved by delta[v] (a zero-mass token repeats the previous sum, as any summation
+    does): the first positive-mass v whose perturbed sum exceeds t, else the last."""
+    last = None
+    c = np.cumsum(r)
+    for v in np.flatnonzero(r > 0):
+        last = v
+        if c[v] + delta[v] > t:
+            return int(v)
+    return int(last)
+
+
+def test_cdf_allowed_is_the_set_of_perturbed_inverse_cdf_tokens():
+    """Brute force on tiny rows: every inverse CDF whose cumulative sums each carry an
+    error of at most `band` returns a token of cdf_allowed (random perturbations,
+    also at the band's edges), and every token of cdf_allowed is returned by some
+    such perturbation (the set is tight)."""
+    rng = np.random.default_rng(21)
+    for trial in range(300):
+        V = int(rng.integers(1, 9))
+        r = rng.uniform(0, 1, V) * (rng.uniform(0, 1, V) < 0.7)
+        if not r.sum() > 0:
+            r[rng.integers(V)] = 1.0
+        if trial % 3 == 0:   # intervals narrower than the band
+            r = r * rng.uniform(0, 1e-3, V)
+        band = float(rng.choice([0.0, 1e-4, 0.05, 0.3])) * r.sum()
+        t = rng.uniform(0, r.sum())
+        if trial % 5 == 0:   # t exactly on a boundary
+            pos = np.cumsum(r)[r > 0]
+            t = float(pos[rng.integers(pos.size)]) if pos.size > 1 else t
+            t = min(t, np.nextafter(r.sum(), 0))
+        allowed = set(int(v) for v in mtp.cdf_allowed(r, t, band))
+        assert mtp.inverse_cdf(r, t)[0] in allowed
+        seen = set()
+        for _ in range(200):
+            delta = rng.choice([-band, band, 0.0], V) if rng.uniform() < 0.5 else rng.uniform(-band, band, V)
+            tok = _perturbed_inverse_cdf(r, t, delta)
+            assert tok in allowed, (r, t, band, delta, tok, allowed)
+            seen.add(tok)
+        c = np.cumsum(r)
+        for w in allowed:   # the perturbation that makes w the answer
+            delta = np.where(np.arange(V) < w, -band, band)
+            assert _perturbed_inverse_cdf(r, t, delta) == w
+            assert c[w] > t - band and (c[w - 1] if w else 0.0) <= t + band
+
+
+def test_cdf_tie_probability_bounds_the_flag_rate():
+    """Monte-Carlo over t uniform on [0, sum r): the share of t whose cdf_allowed has
+    more than one token is at most cdf_tie_probability, and equals it when every
+    interval is wider than two bands (the flagged bands around the boundaries do
+    not overlap)."""
+    rng = np.random.default_rng(22)
+    for V, band_rel, wide in ((40, 2e-3, True), (40, 2e-3, False), (300, 1e-4, True)):
+        r = rng.uniform(0.5, 1.5, V) if wide else np.exp(rng.normal(0, 3, V))
+        r[rng.integers(V)] = 0.0
+        bound = mtp.cdf_tie_probability(r, band_rel)
+        n = 20000
+        ts = rng.uniform(0, r.sum(), n)
+        hits = sum(mtp.cdf_allowed(r, t, band_rel * r.sum()).size > 1 for t in ts)
+        assert hits / n <= bound + 5 * np.sqrt(bound / n)
+        if wide:
+            assert abs(hits / n - bound) <= 5 * np.sqrt(bound / n)
+    assert mtp.cdf_tie_probability(np.array([0.0, 1.0, 0.0]), 0.1) == 0.0
+
+
+def test_row_sample_allowed_sets():
+    """row_sample's allowed set: the exact token alone away from boundaries; the
+    token on either side near one; every token with p > 0 for a residual whose mass
+    is below the band; an empty residual samples p, and only the rows made of the
+    same logits pin its token exactly."""
+    p = np.array([0.25, 0.25, 0.25, 0.25])
+    tok, empty, allowed = mtp.row_sample(p, None, 0.6)
+    assert tok == 2 and not empty and list(allowed) == [2]
+    tok, empty, allowed = mtp.row_sample(p, None, 0.5 + 1e-9)
+    assert tok == 2 and list(allowed) == [1, 2]
+    tok, empty, allowed = mtp.row_sample(p, None, 0.5 - 1e-9)
+    assert tok == 1 and list(allowed) == [1, 2]
+    q = p.copy()
+    tok, empty, allowed = mtp.row_sample(p, q, 0.3, identical=True)   # the same logits: exactly empty
+    assert empty and tok == 1 and list(allowed) == [1]
+    tok, empty, allowed = mtp.row_sample(p, q, 0.3)          # p = q from different logits
+    assert empty and tok == 1 and list(allowed) == [0, 1, 2, 3]
+    q = np.array([0.25 - 1e-8, 0.25 + 1e-8, 0.25, 0.25])   # residual of mass 1e-8 on token 0
+    tok, empty, allowed = mtp.row_sample(p, q, 0.3)
+    assert not empty and tok == 0 and list(allowed) == [0, 1, 2, 3]
+
+
 def _count_below(pred, n_bits=24):
     """Number of k in [0, 2^n) with pred(k * 2^-n) true, for a predicate true on a
     prefix of the grid (monotone decreasing in k): bisection over the oracle's own

@@ -11,6 +11,7 @@ ROW_BAD_TOKEN = 1
 ROW_BAD_TARGET = 2
 ROW_BAD_DRAFT = 4
 ROW_RESIDUAL_EMPTY = 8
+ROW_SYNC_TIMEOUT = 16
 
 MAX_GAMMA = 8
 
@@ -56,6 +57,7 @@ SIGNATURES = {
                                    _c.c_int32, _c.c_int32, _c.c_int32, _P, _P, _P, _c.c_int64, _c.c_int64, _c.c_int,
                                    _P]),
     "mtp_workspace_error": (_c.c_int, [_P, _c.POINTER(_c.c_uint32), _P]),
+    "mtp_set_wait_limit": (_c.c_uint64, [_c.c_uint64]),
     "mtp_status_string": (_c.c_char_p, [_c.c_int]),
     "mtp_last_error": (_c.c_char_p, []),
     "mtp_version": (_c.c_char_p, []),

@@ -3,6 +3,7 @@
 // Every argument check runs before the first HIP call, so a rejected call touches
 // neither the device nor any output.  The only global state is a per-device cache
 // of the compute-unit count and kernel occupancies, filled under a mutex.
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -15,6 +16,9 @@
 namespace {
 
 thread_local char g_err[512] = "";
+
+// Ticks of the 100 MHz counter after which a bounded wait gives up (process-wide).
+std::atomic<uint64_t> g_wait_limit{mtp::kDefaultWaitLimitTicks};
 
 mtp_status fail(mtp_status s, const char* fmt, ...) {
   va_list ap;
@@ -214,7 +218,9 @@ const char* mtp_status_string(mtp_status s) {
 
 const char* mtp_last_error(void) { return g_err; }
 
-const char* mtp_version(void) { return "libmtp 0.1 (gfx950)"; }
+const char* mtp_version(void) { return "libmtp 0.2 (gfx950)"; }
+
+uint64_t mtp_set_wait_limit(uint64_t ticks) { return g_wait_limit.exchange(ticks); }
 
 mtp_status mtp_verify_workspace_size(int32_t batch, int32_t gamma, int32_t vocab, mtp_dtype dtype,
                                      size_t* bytes) {
@@ -269,19 +275,15 @@ namespace {
 
 bool bad_temperature(float T) { return !(T > 0.f) || T == __builtin_inff(); }
 
-// The verify entry points: rejection sampling (draft_tokens given), target-only
-// (draft_token out) or rejection sampling at a temperature with Gumbel-max row
-// samples.  Argument errors return before any HIP call.
-mtp_status verify_impl(int mode, float temperature, const void* target, int64_t target_row_stride, const void* draft,
-                       int64_t draft_row_stride, mtp_dtype dtype, int32_t batch, int32_t gamma, int32_t vocab,
-                       const int32_t* draft_tokens, uint64_t seed, uint64_t offset, uint8_t* accept,
-                       int32_t* accepted_len, int32_t* next_token, int32_t* draft_token, float* p_yhat,
-                       uint8_t* rs_better, int32_t* row_token, float* overlap, float* tv, float* entropy,
-                       int32_t* row_status, void* workspace, size_t workspace_bytes, void* stream) {
+// Host-side checks of a verify call's arguments (no HIP call).
+mtp_status verify_check_args(int mode, float temperature, const void* target, int64_t target_row_stride,
+                             const void* draft, int64_t draft_row_stride, mtp_dtype dtype, int32_t batch,
+                             int32_t gamma, int32_t vocab, const int32_t* draft_tokens, const uint8_t* accept,
+                             const int32_t* accepted_len, const int32_t* next_token, const int32_t* draft_token) {
   mtp_status s = check_common(dtype, gamma, vocab);
   if (s) return s;
   if (batch < 0) return fail(MTP_ERR_SHAPE, "batch = %d is negative", batch);
-  if (batch == 0) return ok();
+  if (batch == 0) return MTP_OK;
   if (!target || !draft || !accept || !accepted_len || !next_token)
     return fail(MTP_ERR_NULL, "a required pointer (target, draft, accept, accepted_len, next_token) is NULL");
   const bool target_only = mode == mtp::kVerifyTargetOnly;
@@ -294,6 +296,23 @@ mtp_status verify_impl(int mode, float temperature, const void* target, int64_t 
   if ((s = check_row_base(draft, draft_row_stride, dtype, "draft"))) return s;
   if (mode == mtp::kVerifyGumbel && bad_temperature(temperature))
     return fail(MTP_ERR_SHAPE, "temperature %g is not a positive finite number", (double)temperature);
+  return MTP_OK;
+}
+
+// The verify entry points: rejection sampling (draft_tokens given), target-only
+// (draft_token out) or rejection sampling at a temperature with Gumbel-max row
+// samples.  Argument errors return before any HIP call.
+mtp_status verify_impl(int mode, float temperature, const void* target, int64_t target_row_stride, const void* draft,
+                       int64_t draft_row_stride, mtp_dtype dtype, int32_t batch, int32_t gamma, int32_t vocab,
+                       const int32_t* draft_tokens, uint64_t seed, uint64_t offset, uint8_t* accept,
+                       int32_t* accepted_len, int32_t* next_token, int32_t* draft_token, float* p_yhat,
+                       uint8_t* rs_better, int32_t* row_token, float* overlap, float* tv, float* entropy,
+                       int32_t* row_status, void* workspace, size_t workspace_bytes, void* stream) {
+  mtp_status s = verify_check_args(mode, temperature, target, target_row_stride, draft, draft_row_stride, dtype,
+                                   batch, gamma, vocab, draft_tokens, accept, accepted_len, next_token, draft_token);
+  if (s) return s;
+  if (batch == 0) return ok();
+  const bool target_only = mode == mtp::kVerifyTargetOnly;
   const VerifyLayout L = verify_layout(batch, gamma, vocab, dtype, mode);
   if ((s = check_workspace(workspace, workspace_bytes, L.total))) return s;
   if (L.ngroups > 0x7fffffffLL / 8) return fail(MTP_ERR_SHAPE, "batch * (gamma + 1) is too large");
@@ -322,6 +341,7 @@ mtp_status verify_impl(int mode, float temperature, const void* target, int64_t 
   a.part3 = target_only ? at<float>(workspace, L.part3) : nullptr;
   a.gkeys = mode == mtp::kVerifyGumbel ? at<uint64_t>(workspace, L.gkeys) : nullptr;
   a.inv_temp = mode == mtp::kVerifyGumbel ? 1.f / temperature : 1.f;
+  a.wait_limit = g_wait_limit.load(std::memory_order_relaxed);
   a.sp = L.sp;
   a.ngroups = (int)L.ngroups;
   a.sgroups = sgroups;
@@ -467,6 +487,7 @@ mtp_status mtp_tv_loss_fwd(const void* target, int64_t target_pos_stride, int64_
   a.pos_ws = at<float>(workspace, L.pos);
   a.sp = L.sp;
   a.sgroups = sgroups;
+  a.wait_limit = g_wait_limit.load(std::memory_order_relaxed);
   hipError_t e = pipe ? mtp::launch_tv_pipe_fwd(a, dtype, shared, (hipStream_t)stream)
                       : mtp::launch_tv_fwd(a, dtype, shared, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MTP_ERR_LAUNCH, "TV forward launch failed: %s", hipGetErrorString(e));

@@ -273,9 +273,10 @@ __device__ __forceinline__ void block_lse(Lse (&v)[N], float* scratch) {
 // partials with coherent stores, waits for them to complete (s_waitcnt), then
 // increments the cluster counter; a consumer polls the counter with coherent
 // loads and then reads the partials with coherent loads.  Waits are bounded by the
-// 100 MHz real-time counter so that no wave can spin forever; a timeout is
-// reported through `err` and the caller carries on.
-constexpr uint64_t kSpinLimitTicks = 100000000ull;   // 1 s
+// 100 MHz real-time counter (the limit is a kernel argument: 1 s by default) so
+// that no wave can spin forever; a timeout sets `err` and the caller carries on
+// with statistics it marks as NaN, so the affected rows are reported as failed.
+constexpr uint64_t kDefaultWaitLimitTicks = 100000000ull;   // 1 s of the 100 MHz counter
 constexpr uint32_t kErrSyncTimeout = 1u;
 
 __device__ __forceinline__ void st_coherent(float* p, float v) {
@@ -334,35 +335,6 @@ __device__ __forceinline__ void put_word(uint64_t* p, uint64_t w) {
 }
 __device__ __forceinline__ uint64_t get_word(const uint64_t* p) {
   return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// One wave polls the W-word records of chunks [c0, c0 + 64) (lane l: chunk c0 + l,
-// if < C) until all are non-zero, and returns this lane's words.  Bounded: on
-// timeout it flags `err` and returns what it has.
-template <int W>
-__device__ __forceinline__ void wave_poll(const uint64_t* rec, int c0, int C, uint64_t (&w)[W], uint32_t* err) {
-  const int lane = threadIdx.x & 63;
-  const int c = c0 + lane;
-  bool ready = !(c < C);          // lanes without a chunk are ready; ready lanes stop loading
-#pragma unroll
-  for (int i = 0; i < W; ++i) w[i] = 0ull;
-  uint64_t t0 = 0;
-  for (int it = 0;; ++it) {
-    if (!ready) {
-#pragma unroll
-      for (int i = 0; i < W; ++i) w[i] = get_word(rec + (int64_t)c * W + i);
-      ready = true;
-#pragma unroll
-      for (int i = 0; i < W; ++i) ready = ready && (w[i] != 0ull);
-    }
-    if (__ballot(!ready) == 0ull) return;
-    if (it == 0) t0 = __builtin_amdgcn_s_memrealtime();
-    __builtin_amdgcn_s_sleep(2);
-    if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimitTicks) {
-      if (lane == 0) __hip_atomic_fetch_or(err, kErrSyncTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return;
-    }
-  }
 }
 
 // Zero n 64-bit record words with the whole block.
@@ -764,27 +736,29 @@ __device__ __forceinline__ void rec_store(__amdgpu_buffer_rsrc_t r, int byte_off
 // Wait until word `word` of every record of a row is published (non-zero):
 // `v` is this lane's word of record `lane`, loaded earlier, and lanes still seeing
 // zero load again; records past the first 64 are loaded here.  `merge` folds each
-// lane's words in record order (first record, then l + 64, ...).  Bounded by the
-// spin limit (a timeout sets the error word and carries on).  The first 64 words are
-// tested before any load of this function is issued, so that test waits only for
-// the caller's load and not for the (in-order) loads the caller issued after it.
+// lane's words in record order (first record, then l + 64, ...).  Bounded by
+// `limit` ticks of the 100 MHz counter: a timeout sets the error word and returns
+// true (the same in every lane).  The first 64 words are tested before any load of
+// this function is issued, so that test waits only for the caller's load and not
+// for the (in-order) loads the caller issued after it.
 template <typename Fold>
-__device__ __forceinline__ void poll_words(uint64_t v, __amdgpu_buffer_rsrc_t rs, int C, int st, int word,
-                                           uint32_t* err, Fold fold) {
+__device__ __forceinline__ bool poll_words(uint64_t v, __amdgpu_buffer_rsrc_t rs, int C, int st, int word,
+                                           uint32_t* err, uint64_t limit, Fold fold) {
   const int lane = threadIdx.x & 63;
   uint64_t t0 = 0;
+  bool timed_out = false;
   auto settle = [&](int c, uint64_t& w) {
     bool ready = !(c < C) || w != 0ull;
-    while (__ballot(!ready) != 0ull) {
+    while (!timed_out && __ballot(!ready) != 0ull) {
       if (t0 == 0) t0 = __builtin_amdgcn_s_memrealtime();
       __builtin_amdgcn_s_sleep(1);
       if (!ready) {
         w = rec_load(rs, c * st + word * 8);
         ready = w != 0ull;
       }
-      if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimitTicks) {
+      if (__builtin_amdgcn_s_memrealtime() - t0 > limit) {
         if (lane == 0) __hip_atomic_fetch_or(err, kErrSyncTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
+        timed_out = true;
       }
     }
   };
@@ -796,19 +770,21 @@ __device__ __forceinline__ void poll_words(uint64_t v, __amdgpu_buffer_rsrc_t rs
     settle(c, v);
     if (c < C) fold(false, v);
   }
+  return timed_out;
 }
 
-// The row's merged log-sum-exp (no entropy moment) from word `word` of the records.
+// The row's merged log-sum-exp (no entropy moment) from word `word` of the records;
+// NaN if the wait timed out.
 __device__ __forceinline__ Lse poll_row(uint64_t v, __amdgpu_buffer_rsrc_t rs, int C, int st, int word,
-                                        uint32_t* err) {
+                                        uint32_t* err, uint64_t limit) {
   Lse acc = lse_empty();
-  poll_words(v, rs, C, st, word, err, [&](bool first, uint64_t w) {
+  const bool timed_out = poll_words(v, rs, C, st, word, err, limit, [&](bool first, uint64_t w) {
     const Lse r{unpack_lo(w), unmark(unpack_hi(w)), 0.f};
     acc = first ? r : lse_merge(acc, r);
   });
   Lse a[1] = {acc};
   wave_merge<1, 0>(a);
-  return a[0];
+  return timed_out ? lse_nan() : a[0];
 }
 
 // ---------------------------------------------------------------------------

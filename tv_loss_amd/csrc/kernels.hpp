@@ -27,6 +27,7 @@ constexpr int kRowBadToken = 1;
 constexpr int kRowBadTarget = 2;
 constexpr int kRowBadDraft = 4;
 constexpr int kRowResidualEmpty = 8;
+constexpr int kRowSyncTimeout = 16;
 
 // Division by a runtime-invariant d >= 1 for numerators 0 <= n < 2^31 with one
 // high multiply (Granlund and Montgomery, "Division by invariant integers using
@@ -64,6 +65,8 @@ struct VerifyArgs {
   int32_t* draft_token; float* p_yhat; uint8_t* rs_better;
   // Gumbel-max verify: 1 / temperature (1 otherwise)
   float inv_temp;
+  // bounded waits give up after this many ticks of the 100 MHz counter
+  uint64_t wait_limit;
   // workspace sections: error word, pass-1 records [group][chunk][3 or 4 words],
   // pass-2 sums [group][chunk][wave] = (residual or p mass, overlap) as two floats,
   // target-only: p mass without the greedy token [group][chunk][wave]; Gumbel-max:
@@ -115,6 +118,8 @@ struct TvArgs {
   // top-K path: the target of head k at position t is given by K entries, indices
   // idx and logits val at t*k_pos + k*k_head + j (k_head = 0: shared by the heads)
   const int32_t* idx; const float* val; int64_t k_pos, k_head; int K;
+  // bounded waits give up after this many ticks of the 100 MHz counter
+  uint64_t wait_limit;
 };
 
 constexpr int kTvSavedStride = 4;   // saved[t, k, :] = (lse_p, lse_q, alpha, S)

@@ -389,7 +389,7 @@ __global__ __launch_bounds__(kBlock) void tv_pipe_main(TvArgs a) {
         const int r = wave + j * kWaves;
         if (r < NR) {
           __builtin_amdgcn_s_setprio(3);
-          const Lse st = poll_row(wpoll[j], rsrc_rec(t_m2), C, kSt, r, a.err);
+          const Lse st = poll_row(wpoll[j], rsrc_rec(t_m2), C, kSt, r, a.err, a.wait_limit);
           if (lane == 0) lse_sh[par][r] = lse_log2(st);
           __builtin_amdgcn_s_setprio(0);
         }
@@ -575,7 +575,8 @@ __global__ __launch_bounds__(64 * kFinishWaves) void tv_pipe_finish(TvArgs a) {
   for (int k = 0; k < 2 * G; ++k) pre[k] = p2[(int64_t)lc * 2 * G + k];
   float lse2[NR];
 #pragma unroll
-  for (int r = 0; r < NR; ++r) lse2[r] = lse_log2(poll_row(lane < C ? v[r] : 0ull, rs, C, kSt, r, a.err));
+  for (int r = 0; r < NR; ++r)
+    lse2[r] = lse_log2(poll_row(lane < C ? v[r] : 0ull, rs, C, kSt, r, a.err, a.wait_limit));
   float tot[2 * G];
 #pragma unroll
   for (int k = 0; k < 2 * G; ++k) tot[k] = lane < C ? pre[k] : 0.f;

@@ -123,14 +123,17 @@ __device__ __forceinline__ void wave_argmax(float& m, uint32_t& idx) {
 
 // The chunk argmax words of a group merged over its C records, in record order per
 // lane then over the wave: the vocabulary index of the largest draft logit.
+// A wait that timed out gives kNoArgmax.
+constexpr uint32_t kNoArgmax = 0xffffffffu;
+
 __device__ __forceinline__ uint32_t poll_argmax(uint64_t v, __amdgpu_buffer_rsrc_t rs, int C, int st,
-                                                uint32_t* err) {
+                                                uint32_t* err, uint64_t limit) {
   float m = kNegInf;
   uint32_t idx = 0xffffffffu;
-  poll_words(v, rs, C, st, kArgmaxWord, err,
-             [&](bool, uint64_t w) { argmax_fold(m, idx, unpack_lo(w), argmax_index(w)); });
+  const bool timed_out = poll_words(v, rs, C, st, kArgmaxWord, err, limit,
+                                    [&](bool, uint64_t w) { argmax_fold(m, idx, unpack_lo(w), argmax_index(w)); });
   wave_argmax(m, idx);
-  return idx;
+  return timed_out ? kNoArgmax : idx;
 }
 
 __device__ __forceinline__ uint32_t merge_argmax(__amdgpu_buffer_rsrc_t rs, int C, int st) {
@@ -266,10 +269,12 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
         // the test comes later and finds a record missing less often, and a reload
         // waits for those loads anyway.
         wait_vmem_all();
-        const Lse st = poll_row(wpoll, rsrc_rec(g_m2), C, kSt, row, a.err);
+        // a wait that timed out gives NaN statistics (and no greedy token), which
+        // pass 2 turns into NaN partials: the finish reports such rows as failed
+        const Lse st = poll_row(wpoll, rsrc_rec(g_m2), C, kSt, row, a.err, a.wait_limit);
         if (lane == 0) lse_sh[i & 1][row] = lse_log2(st);
         if (TO && row == 1) {
-          const uint32_t yh = poll_argmax(wpoll_am, rsrc_rec(g_m2), C, kSt, a.err);
+          const uint32_t yh = poll_argmax(wpoll_am, rsrc_rec(g_m2), C, kSt, a.err, a.wait_limit);
           if (lane == 0) yhat_sh[i & 1] = yh;
         }
         __builtin_amdgcn_s_setprio(0);
@@ -322,6 +327,12 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
           om = sb * wave_total(o0 + o1);
         }
       }
+      // statistics that are NaN (a timed-out wait, or a row without a finite
+      // normaliser) make the partials NaN, whatever the sums above gave
+      const bool poison = !(lse_sh[i & 1][0] == lse_sh[i & 1][0]) ||
+                          (pair2 && !(lse_sh[i & 1][1] == lse_sh[i & 1][1])) ||
+                          (TO && pair2 && yhat_sh[i & 1] == kNoArgmax);
+      if (poison) rm = om = __builtin_nanf("");
       if (lane == 0) a.part2[((int64_t)g_m2 * C + c) * kWaves + wave] = pack2(rm, om);
       if constexpr (GM) {
         // Gumbel-max keys of this wave's segment, key = w / E (the exponential race,
@@ -526,33 +537,71 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
 // ---------------------------------------------------------------------------
 // verify_finish: one workgroup per sequence, wave k handles row (b, k).
 
+// The cumulative sums of the inverse CDF run in float64 (chunk, segment and
+// element prefixes alike): their rounding then stays far below that of the float32
+// masses they add up, so a token differs from the exact inverse CDF's only where t
+// lies within the masses' own rounding of a boundary.
+
+// A lane's double moved by a DPP control (both halves), 0 where there is no source.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ double dpp_or_zero_f64(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, ROW_MASK, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, ROW_MASK, 0xf, false);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Inclusive prefix sum over the wave in lane order (the float32 wave_incl_sum's
+// steps on doubles); lane 63 holds the total.
+__device__ __forceinline__ double wave_incl_sum_f64(double v) {
+  v += dpp_or_zero_f64<0x111>(v);
+  v += dpp_or_zero_f64<0x112>(v);
+  v += dpp_or_zero_f64<0x114>(v);
+  v += dpp_or_zero_f64<0x118>(v);
+  v += dpp_or_zero_f64<0x142, 0xa>(v);
+  v += dpp_or_zero_f64<0x143, 0xc>(v);
+  return v;
+}
+
+__device__ __forceinline__ double readlane_d(double v, int l) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// The previous lane's value (0 in lane 0).
+__device__ __forceinline__ double lane_before(double incl) {
+  const double ex = __shfl_up(incl, 1, 64);
+  return (threadIdx.x & 63) == 0 ? 0.0 : ex;
+}
+
 // Inverse CDF of one wave segment (NV blocks of 64 vectors, PV values per lane per
 // block, vocabulary order block-major then lane-major): the index (within the
 // segment) of the first value whose running mass exceeds t; if none, the last
 // index with positive mass; -1 if the segment has no mass.
 template <int NV, int PV>
-__device__ __forceinline__ int wave_inverse_cdf(const float (&v)[NV][PV], float t) {
+__device__ __forceinline__ int wave_inverse_cdf(const float (&v)[NV][PV], double t) {
   const int lane = threadIdx.x & 63;
-  float base = 0.f;
+  double base = 0.0;
   int best = 0x7fffffff, lastpos = -1;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    float s = 0.f;
+    double s = 0.0;
 #pragma unroll
-    for (int e = 0; e < PV; ++e) s += v[j][e];
-    const float incl = wave_incl_sum(s);
-    const float ex = __shfl_up(incl, 1, 64);   // the previous lane's inclusive sum exactly
-    float cum = base + (lane == 0 ? 0.f : ex);
+    for (int e = 0; e < PV; ++e) s += (double)v[j][e];
+    const double incl = wave_incl_sum_f64(s);
+    double cum = base + lane_before(incl);
 #pragma unroll
     for (int e = 0; e < PV; ++e) {
       if (v[j][e] > 0.f) {
-        cum += v[j][e];
+        cum += (double)v[j][e];
         const int idx = (j * 64 + lane) * PV + e;
         if (best == 0x7fffffff && cum > t) best = idx;
         lastpos = idx;
       }
     }
-    base += readlane_f(incl, 63);
+    base += readlane_d(incl, 63);
   }
   best = (int)wave_min_u32((uint32_t)best);
   lastpos = (int)wave_max_u32((uint32_t)(lastpos + 1)) - 1;
@@ -565,9 +614,9 @@ __device__ __forceinline__ int wave_inverse_cdf(const float (&v)[NV][PV], float 
 // index with mass, with start = -inf) and the mass before it.  Every lane of the
 // wave gets the same result.
 struct Scan {
-  float total;
+  double total;
   int owner;
-  float start;
+  double start;
 };
 
 template <typename MassFn>
@@ -575,33 +624,27 @@ __device__ __forceinline__ Scan wave_scan_owner(int n, float u_prime, MassFn mas
   const int lane = threadIdx.x & 63;
   const int K = (n + 63) / 64;
   const int c0 = lane * K, c1 = min(n, c0 + K);
-  float block = 0.f;
+  double block = 0.0;
   int last_pos = -1;
   for (int c = c0; c < c1; ++c) {
     const float m = mass(c);
-    block += m;
+    block += (double)m;
     if (m > 0.f) last_pos = c;
   }
-  float incl = block;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float v = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += v;
-  }
-  const float ex = __shfl_up(incl, 1, 64);
-  const float excl = lane == 0 ? 0.f : ex;
+  const double incl = wave_incl_sum_f64(block);
+  const double excl = lane_before(incl);
   Scan r;
-  r.total = __shfl(incl, 63, 64);
-  const float t = u_prime * r.total;
+  r.total = readlane_d(incl, 63);
+  const double t = (double)u_prime * r.total;
   r.owner = -1;
-  r.start = kNegInf;
+  r.start = -__builtin_huge_val();
   const uint64_t hit = __ballot(c0 < c1 && incl > t);
-  if (hit != 0ull && r.total > 0.f) {
+  if (hit != 0ull && r.total > 0.0) {
     const int l = __builtin_ctzll(hit);
-    float run = __shfl(excl, l, 64);
+    double run = readlane_d(excl, l);
     const int a0 = l * K, a1 = min(n, a0 + K);
     for (int c = a0; c < a1; ++c) {
-      const float m = mass(c);
+      const double m = (double)mass(c);
       if (r.owner < 0 && run + m > t) { r.owner = c; r.start = run; }
       run += m;
     }
@@ -609,7 +652,7 @@ __device__ __forceinline__ Scan wave_scan_owner(int n, float u_prime, MassFn mas
   if (r.owner < 0) {   // rounding left t past every boundary: last index with mass
     const uint64_t pos = __ballot(last_pos >= 0);
     r.owner = pos ? __shfl(last_pos, 63 - __builtin_clzll(pos), 64) : 0;
-    r.start = kNegInf;  // t - start = +inf: the owner takes its last positive element
+    r.start = -__builtin_huge_val();  // t - start = +inf: the owner takes its last positive element
   }
   return r;
 }
@@ -701,7 +744,12 @@ __global__ void verify_finish(VerifyArgs a) {
   const float lse2_q = pair ? lse_log2(st.q) : 0.f;
   const bool bad_p = !(__builtin_isfinite(lse2_p));
   const bool bad_q = pair && !(__builtin_isfinite(lse2_q));
-  const bool bad = bad_p || bad_q;
+  // the row's pass-2 partials: NaN (with finite statistics) where a bounded wait of
+  // the main kernel for the row statistics timed out
+  float ot[2] = {om_sum, tv_sum};
+  wave_reduce<false, 2>(ot);
+  const bool timed_out = !(bad_p || bad_q) && !(ot[0] == ot[0] && ot[1] == ot[1]);
+  const bool bad = bad_p || bad_q || timed_out;
   float u, up;
   row_uniforms(a.seed, a.offset, (uint64_t)g, &u, &up);
 
@@ -729,44 +777,43 @@ __global__ void verify_finish(VerifyArgs a) {
 
   float alpha = 0.f;
   bool empty_res = false;
-  Scan sc{0.f, 0, 0.f};
+  Scan sc{0.0, 0, 0.0};
   float oseg[kWaves] = {0.f, 0.f, 0.f, 0.f};   // segment masses of the owner chunk
   if (!bad && !GM) {
     // block sums in lane order, prefix over lanes, then the owner lane walks its block
-    float blk = 0.f;
+    double blk = 0.0;
     int last_pos = -1;
     for (int cc = c0; cc < c1; ++cc) {
       const float m = chunk_mass_own(cc);
-      blk += m;
+      blk += (double)m;
       if (m > 0.f) last_pos = cc;
     }
-    const float incl = wave_incl_sum(blk);
-    const float ex = __shfl_up(incl, 1, 64);
-    const float excl = lane == 0 ? 0.f : ex;
-    sc.total = readlane_f(incl, 63);
-    const float tt = up * sc.total;
+    const double incl = wave_incl_sum_f64(blk);
+    const double excl = lane_before(incl);
+    sc.total = readlane_d(incl, 63);
+    const double tt = (double)up * sc.total;
     sc.owner = -1;
-    sc.start = kNegInf;
+    sc.start = -__builtin_huge_val();
     int ol = -1;
     const uint64_t hit = __ballot(c0 < c1 && incl > tt);
-    if (hit != 0ull && sc.total > 0.f) {
+    if (hit != 0ull && sc.total > 0.0) {
       ol = __builtin_ctzll(hit);
-      float run = excl;
+      double run = excl;
       int own = -1;
-      float st0 = kNegInf;
+      double st0 = -__builtin_huge_val();
       for (int cc = c0; cc < c1; ++cc) {
-        const float m = chunk_mass_own(cc);
+        const double m = (double)chunk_mass_own(cc);
         if (own < 0 && run + m > tt) { own = cc; st0 = run; }
         run += m;
       }
       sc.owner = readlane_i(own, ol);
-      sc.start = readlane_f(st0, ol);
+      sc.start = readlane_d(st0, ol);
     }
     if (sc.owner < 0) {   // rounding left t past every boundary: last chunk with mass
       const uint64_t pos = __ballot(last_pos >= 0);
       ol = pos ? 63 - __builtin_clzll(pos) : 0;
       sc.owner = pos ? readlane_i(last_pos, ol) : 0;
-      sc.start = kNegInf;
+      sc.start = -__builtin_huge_val();
     }
     // the owner chunk's segment masses, from the lane that holds them
     const int oi = sc.owner - ol * K;
@@ -784,17 +831,15 @@ __global__ void verify_finish(VerifyArgs a) {
     }
   }
   if (!bad && pair) {
-    float ot[2] = {om_sum, tv_sum};
-    wave_reduce<false, 2>(ot);
     alpha = ot[0];
     tv_sum = ot[1];
-    if (GM ? !(tv_sum > 0.f) : !(sc.total > 0.f)) {   // the residual has no mass: sample from p
+    if (GM ? !(tv_sum > 0.f) : !(sc.total > 0.0)) {   // the residual has no mass: sample from p
       empty_res = true;
       if (!GM) sc = wave_scan_owner(C, up, pmass);
     }
   }
   // TV: the residual mass (the scan's total for rejection sampling)
-  const float r_tot = TO || GM ? tv_sum : pair && !empty_res ? sc.total : 0.f;
+  const float r_tot = TO || GM ? tv_sum : pair && !empty_res ? (float)sc.total : 0.f;
   const bool use_q = !TO && pair && !empty_res;
   const bool drop_y = to_pair && !empty_res && y_ok;   // target-only residual: p without y
 
@@ -849,13 +894,13 @@ __global__ void verify_finish(VerifyArgs a) {
           }
         }
     };
-    const float tl = up * sc.total - sc.start;
+    const double tl = (double)up * sc.total - sc.start;
     int os = -1;
-    float seg_start = kNegInf;
+    double seg_start = -__builtin_huge_val();
     float v[NV][PV];
     if (pair && empty_res) {
       // segment masses of p are not recorded for a pair row: measure them (rare)
-      float run = 0.f;
+      double run = 0.0;
       for (int s = 0; s < kWaves && os < 0; ++s) {
         seg_values(s, v);
         float m = 0.f;
@@ -863,18 +908,18 @@ __global__ void verify_finish(VerifyArgs a) {
         for (int j = 0; j < NV; ++j)
 #pragma unroll
           for (int e = 0; e < PV; ++e) m += v[j][e];
-        m = wave_total(m);
-        if (run + m > tl) { os = s; seg_start = run; }
-        run += m;
+        const double md = (double)wave_total(m);
+        if (run + md > tl) { os = s; seg_start = run; }
+        run += md;
       }
       if (os < 0) os = kWaves - 1;
     } else {
-      float run = 0.f;
+      double run = 0.0;
       int lastpos = 0;
 #pragma unroll
       for (int i = 0; i < kWaves; ++i) {
-        const float m = oseg[i];
-        if (m > 0.f) lastpos = i;
+        const double m = (double)oseg[i];
+        if (m > 0.0) lastpos = i;
         if (os < 0 && run + m > tl) { os = i; seg_start = run; }
         run += m;
       }
@@ -901,28 +946,39 @@ __global__ void verify_finish(VerifyArgs a) {
     int status = 0;
     if (bad_p) status |= kRowBadTarget;
     if (bad_q) status |= kRowBadDraft;
+    if (timed_out) status |= kRowSyncTimeout;
     if (empty_res) status |= kRowResidualEmpty;
     int flag = 0;
     const float nan = __builtin_nanf("");
     if (pair) {
+      // The acceptance ratio in float64 from the row statistics (ref, z) the main
+      // kernel summed in float32 with the same logit scale L: log2 p(y) / q(y) =
+      // (a_y - b_y) L - (lse2_p - lse2_q), lse2 = ref + log2 z.  Forming the two
+      // base-2 log-sum-exps (about 17 at V = 151936) in float32 would round each by
+      // up to 1e-6; in float64 the ratio keeps the accuracy of the float32 sums z.
+      const double Ld = (double)L;
+      const double l2p = bad ? 0.0 : (double)st.p.ref + log2((double)st.p.z);
       if (TO) {
         // target-only: accept the greedy token with probability p(y); the RS/TO
         // boundary TV < 1 - p(y)
-        const float py = y_ok && !bad ? fast_exp2(__builtin_fmaf(ay, L, -lse2_p)) : nan;
-        if (y_ok && !bad) flag = u < py ? 1 : 0;
+        const double pyd = exp2((double)ay * Ld - l2p);
+        const float py = y_ok && !bad ? (float)pyd : nan;
+        if (y_ok && !bad) flag = (double)u < pyd ? 1 : 0;
         a.draft_token[b * G + k] = y_ok && !bad ? y : -1;
         if (a.p_yhat) a.p_yhat[b * G + k] = py;
         if (a.rs_better) a.rs_better[b * G + k] = (uint8_t)(y_ok && !bad && r_tot < 1.f - py ? 1 : 0);
       } else if (!y_ok) {
         status |= kRowBadToken;
       } else if (!bad) {
-        const float d = __builtin_fmaf(ay, L, -lse2_p) - __builtin_fmaf(by, L, -lse2_q);
-        if (d == d) flag = u < fminf(1.f, fast_exp2(d)) ? 1 : 0;
+        const double l2q = (double)st.q.ref + log2((double)st.q.z);
+        const double d = ((double)ay - (double)by) * Ld - (l2p - l2q);
+        if (d == d) flag = (double)u < fmin(1.0, exp2(d)) ? 1 : 0;   // NaN (p(y) = q(y) = 0): reject
       }
       a.accept[b * G + k] = (uint8_t)flag;
       if (a.overlap) a.overlap[b * G + k] = bad ? nan : alpha;
       if (a.tv) a.tv[b * G + k] = bad ? nan : r_tot;
     }
+    // the entropy needs only the pass-1 records: valid after a timed-out wait too
     if (a.entropy) a.entropy[g] = bad_p ? nan : kLn2 * (fast_log2(st.p.z) - st.p.y / st.p.z);
     if (a.row_token) a.row_token[g] = token;
     if (a.row_status) a.row_status[g] = status;

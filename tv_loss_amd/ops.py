@@ -347,6 +347,12 @@ def workspace_error(ws):
     return word.value
 
 
+def set_wait_limit(ticks):
+    """Bound, in ticks of the GPU's 100 MHz clock, on every wait for row statistics
+    exchanged between workgroups, for calls launched afterwards (mtp_set_wait_limit);
+    returns the previous bound.  0 makes such waits give up at once."""
+    return int(load().mtp_set_wait_limit(ctypes.c_uint64(int(ticks))))
+
 
 def _check_temperature(temperature):
     t = float(temperature)
