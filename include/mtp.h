@@ -123,6 +123,28 @@ mtp_status mtp_verify(const void* target, int64_t target_row_stride,
                       int32_t* row_status,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* mtp_verify without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Arguments, outputs and results are those of mtp_verify.  The
+ * workspace is a file-scope device array of MTP_VERIFY_NOALLOC_SCRATCH_BYTES that
+ * each GPU holds from the first call on it until the process ends; calls whose
+ * workspace (mtp_verify_workspace_size) would be larger return MTP_ERR_WORKSPACE
+ * and write nothing.  The call allocates and frees nothing.  The first call on a
+ * device zeroes that device's array with a kernel on `stream` (it must not be
+ * captured in a graph: MTP_ERR_DEVICE); every call leaves the array zeroed again.
+ * All calls on one GPU share its array: calls that overlap on one GPU (other
+ * streams, other host threads) race.
+ */
+#define MTP_VERIFY_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+mtp_status mtp_verify_noalloc(const void* target, int64_t target_row_stride,
+                              const void* draft, int64_t draft_row_stride, mtp_dtype dtype,
+                              int32_t batch, int32_t gamma, int32_t vocab,
+                              const int32_t* draft_tokens, uint64_t seed, uint64_t offset,
+                              uint8_t* accept, int32_t* accepted_len, int32_t* next_token,
+                              int32_t* row_token, float* overlap, float* tv, float* entropy,
+                              int32_t* row_status, void* stream);
+
 /* The largest vocab that the verify entry points (all three) accept for dtype on
  * the current device: every row is cut into chunks of 4096 (bfloat16) or 3072
  * (float32) logits, one workgroup each, and all workgroups of a row must be

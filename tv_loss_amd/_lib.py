@@ -14,6 +14,7 @@ ROW_RESIDUAL_EMPTY = 8
 ROW_SYNC_TIMEOUT = 16
 
 MAX_GAMMA = 8
+VERIFY_NOALLOC_SCRATCH_BYTES = 16 << 20   # MTP_VERIFY_NOALLOC_SCRATCH_BYTES
 
 STATUS = {0: "MTP_OK", 1: "MTP_ERR_NULL", 2: "MTP_ERR_SHAPE", 3: "MTP_ERR_DTYPE", 4: "MTP_ERR_ALIGN",
           5: "MTP_ERR_WORKSPACE", 6: "MTP_ERR_DEVICE", 7: "MTP_ERR_LAUNCH"}
@@ -27,6 +28,8 @@ SIGNATURES = {
     "mtp_verify": (_c.c_int, [_P, _c.c_int64, _P, _c.c_int64, _c.c_int, _c.c_int32, _c.c_int32, _c.c_int32,
                               _P, _c.c_uint64, _c.c_uint64, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                               _c.c_size_t, _P]),
+    "mtp_verify_noalloc": (_c.c_int, [_P, _c.c_int64, _P, _c.c_int64, _c.c_int, _c.c_int32, _c.c_int32, _c.c_int32,
+                                      _P, _c.c_uint64, _c.c_uint64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "mtp_verify_max_vocab": (_c.c_int, [_c.c_int, _c.POINTER(_c.c_int32)]),
     "mtp_verify_target_only_workspace_size": (_c.c_int, [_c.c_int32, _c.c_int32, _c.c_int32, _c.c_int,
                                                          _c.POINTER(_c.c_size_t)]),

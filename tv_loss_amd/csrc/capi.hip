@@ -355,6 +355,55 @@ mtp_status verify_impl(int mode, float temperature, const void* target, int64_t 
 
 }  // namespace
 
+// ---- mtp_verify_noalloc: the verify workspace in a file-scope device array ----
+// For callers that cannot allocate device memory.  Each GPU holds its own copy of
+// `scratch` for the life of the process; host code never uses the array's name as
+// an address: hipGetSymbolAddress gives each device's copy once, and that pointer
+// is what the kernels get.  The verify kernels leave every word they use at zero
+// when a call completes, so the array only needs zeroing once per device.
+constexpr size_t kScratchBytes = MTP_VERIFY_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+__global__ void zero_scratch(uint64_t* p, size_t nwords) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nwords; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0ull;
+}
+
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch;   // device -> address of that device's `scratch`
+
+// This device's scratch address; on the first call on a device, looks it up and
+// zeroes the array on `stream` (a zero-fill kernel, not a memset node).
+mtp_status device_scratch(hipStream_t stream, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(MTP_ERR_DEVICE, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  auto it = g_scratch.find(dev);
+  if (it == g_scratch.end()) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess)
+      return fail(MTP_ERR_DEVICE, "cannot query the stream's capture status");
+    if (cs != hipStreamCaptureStatusNone)
+      return fail(MTP_ERR_DEVICE, "the first mtp_verify_noalloc call on a device zeroes its scratch array and "
+                                  "must not be captured");
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(MTP_ERR_DEVICE, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    hipLaunchKernelGGL(zero_scratch, dim3(1024), dim3(256), 0, stream, reinterpret_cast<uint64_t*>(p),
+                       kScratchBytes / 8);
+    const hipError_t le = hipGetLastError();
+    if (le != hipSuccess) return fail(MTP_ERR_LAUNCH, "zeroing the scratch array failed: %s", hipGetErrorString(le));
+    it = g_scratch.emplace(dev, p).first;
+  }
+  *out = it->second;
+  return MTP_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 mtp_status mtp_verify(const void* target, int64_t target_row_stride, const void* draft,
@@ -598,6 +647,28 @@ mtp_status mtp_tv_loss_bwd(const void* target, int64_t target_pos_stride, int64_
   hipError_t e = mtp::launch_tv_bwd(a, dtype, shared, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MTP_ERR_LAUNCH, "TV backward launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+mtp_status mtp_verify_noalloc(const void* target, int64_t target_row_stride, const void* draft,
+                              int64_t draft_row_stride, mtp_dtype dtype, int32_t batch, int32_t gamma,
+                              int32_t vocab, const int32_t* draft_tokens, uint64_t seed, uint64_t offset,
+                              uint8_t* accept, int32_t* accepted_len, int32_t* next_token, int32_t* row_token,
+                              float* overlap, float* tv, float* entropy, int32_t* row_status, void* stream) {
+  mtp_status s = verify_check_args(mtp::kVerifyRejection, 1.f, target, target_row_stride, draft, draft_row_stride,
+                                   dtype, batch, gamma, vocab, draft_tokens, accept, accepted_len, next_token,
+                                   nullptr);
+  if (s) return s;
+  if (batch == 0) return ok();
+  const size_t need = verify_layout(batch, gamma, vocab, dtype, mtp::kVerifyRejection).total;
+  if (need > kScratchBytes)
+    return fail(MTP_ERR_WORKSPACE,
+                "batch %d x (gamma %d + 1) rows of vocab %d need %zu bytes of scratch; mtp_verify_noalloc has %zu "
+                "(use mtp_verify with a workspace)", batch, gamma, vocab, need, kScratchBytes);
+  void* ws = nullptr;
+  if ((s = device_scratch((hipStream_t)stream, &ws))) return s;
+  return verify_impl(mtp::kVerifyRejection, 1.f, target, target_row_stride, draft, draft_row_stride, dtype, batch,
+                     gamma, vocab, draft_tokens, seed, offset, accept, accepted_len, next_token, nullptr, nullptr,
+                     nullptr, row_token, overlap, tv, entropy, row_status, ws, kScratchBytes, stream);
 }
 
 mtp_status mtp_workspace_error(const void* workspace, uint32_t* host_word, void* stream) {
