@@ -35,6 +35,21 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// x clamped to [0, 1]: folds into the producing instruction's output clamp (which
+// also turns a NaN into 0)
+__device__ __forceinline__ float clamp01(float x) { return __builtin_amdgcn_fmed3f(x, 0.f, 1.f); }
+
+// The reference of a pass-1 partial: m L rounded up, i.e. the float m * L when the
+// product rounded up or was exact, else the next float above it.  Every logit x <= m
+// then has x L - ref <= 0 exactly in the fused multiply-add, so e = 2^(x L - ref) <= 1
+// (the pass-2 sums rely on it: their maxima are [0, 1] output clamps).  -inf and
+// NaN pass through (m * L).
+__device__ __forceinline__ float ref_up(float m, float L) {
+  const float r = m * L;
+  if (!(__builtin_fmaf(m, L, -r) > 0.f)) return r;
+  const int b = __float_as_int(r);
+  return r > 0.f ? __int_as_float(b + 1) : r < 0.f ? __int_as_float(b - 1) : __int_as_float(1);
+}
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // Geometry of one row split into `nchunks` chunks of whole 16-byte vectors.
@@ -485,7 +500,7 @@ __device__ __forceinline__ Lse lse_nan() {
 // Log-sum-exp partials of R rows over a wave, the rows interleaved so that their
 // dependency chains overlap.  L converts logits to base-2 exponents: log2 e, or
 // log2 e / T for temperature T.  For row r the wave's largest logit M is the
-// reference (ref = M L), x[r] is overwritten with e = 2^(x L - ref) and the sums of
+// reference (ref = M L rounded up), x[r] is overwritten with e = 2^(x L - ref) <= 1 and the sums of
 // e, and for r < RY of e * (x L - ref) (the entropy moment), are taken over the
 // wave.  A wave holding only -inf gives the empty partial (ref = -inf, z = 0, e = 0);
 // a NaN gives z = NaN.  The entropy moment is
@@ -505,7 +520,7 @@ __device__ __forceinline__ void wave_pass1(float (&x)[R][NE], Lse (&out)[R], flo
   float ref[R], z0[R], z1[R], y0[R], y1[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    ref[r] = M[r] > kNegInf ? M[r] * L : 0.f;   // 0 keeps -inf - ref = -inf
+    ref[r] = M[r] > kNegInf ? ref_up(M[r], L) : 0.f;   // 0 keeps -inf - ref = -inf
     z0[r] = z1[r] = y0[r] = y1[r] = -0.f;   // -0 + x = x: the first additions fold away
   }
 #pragma unroll
@@ -544,7 +559,7 @@ __device__ __forceinline__ void wave_pass1(float (&x)[R][NE], Lse (&out)[R], flo
     }
   }
 #pragma unroll
-  for (int r = 0; r < R; ++r) out[r] = Lse{M[r] * L, Z[r], Y[r]};   // ref -inf when empty
+  for (int r = 0; r < R; ++r) out[r] = Lse{M[r] > kNegInf ? ref[r] : kNegInf, Z[r], Y[r]};   // ref -inf when empty
 }
 
 // Merge of per-lane partials of R rows into one per row, the same bits in every

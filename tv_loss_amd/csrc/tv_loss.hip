@@ -274,8 +274,9 @@ __global__ __launch_bounds__(kBlock) void tv_fwd_mean(TvArgs a) {
 constexpr int kPipeFloats = 64;   // logits per thread and position (all rows) in flight
 
 // Pass 1 of R rows with the sums left per lane: row r's reference is the wave's
-// largest logit M (ref = M L; -inf for a wave holding only -inf), x[r] is
-// overwritten with e = 2^(x L - ref) and z[r] is this lane's sum of its e values.
+// largest logit M (ref = M L rounded up, so e <= 1; -inf for a wave holding only
+// -inf), x[r] is overwritten with e = 2^(x L - ref) and z[r] is this lane's sum of
+// its e values.
 template <int NE, int R>
 __device__ __forceinline__ void lane_pass1(float (&x)[R][NE], float (&ref)[R], float (&z)[R], float L) {
   float M[R];
@@ -290,7 +291,7 @@ __device__ __forceinline__ void lane_pass1(float (&x)[R][NE], float (&ref)[R], f
   float sh[R], z0[R], z1[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    sh[r] = M[r] > kNegInf ? M[r] * L : 0.f;   // 0 keeps -inf - sh = -inf
+    sh[r] = M[r] > kNegInf ? ref_up(M[r], L) : 0.f;   // 0 keeps -inf - sh = -inf
     z0[r] = z1[r] = -0.f;                       // -0 + e = e: the first addition folds away
   }
 #pragma unroll
@@ -305,7 +306,7 @@ __device__ __forceinline__ void lane_pass1(float (&x)[R][NE], float (&ref)[R], f
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     z[r] = z0[r] + z1[r];
-    ref[r] = M[r] * L;
+    ref[r] = M[r] > kNegInf ? sh[r] : kNegInf;
   }
 }
 
@@ -319,7 +320,7 @@ template <int G, bool SHARED>
 constexpr bool pipe_fits() { return FwdShape<G, SHARED>::NR <= kTvPipeMaxRows; }
 
 template <int DT, int G, bool SHARED>
-__global__ __launch_bounds__(kBlock) void tv_pipe_main(TvArgs a) {
+__global__ __launch_bounds__(kBlock, 2) void tv_pipe_main(TvArgs a) {
   constexpr int NT = FwdShape<G, SHARED>::NT;
   constexpr int NR = FwdShape<G, SHARED>::NR;
   constexpr int PV = Elem<DT>::kPerVec;
@@ -396,52 +397,70 @@ __global__ __launch_bounds__(kBlock) void tv_pipe_main(TvArgs a) {
       }
       __syncthreads();
       // ---- pass 2 of position i - 2: overlap and S partials of every head ----
+      // In a wave's units p = sa e_p, q = sb e_q (e <= 1).  Working in q's units with
+      // rho = sa / sb, the residual of q over p, r = max(0, e_q - rho e_p) <= e_q <= 1,
+      // is one fused multiply-add with the [0, 1] output clamp, and
+      //   overlap = sum min(rho e_p, e_q) = zq - sum r,
+      //   S = sum_{q <= p} e_q = zq - sum_{r > 0} e_q,
+      // where zq is this lane's pass-1 sum of e_q (so disjoint supports give exactly
+      // 0 and identical rows exactly zq).  The indicator 1[r > 0] is r * 2^100
+      // clamped: 1 for every r >= 2^-100 (the rare r below it weigh under 2^-100 of
+      // the wave's largest q); a tie (r = 0) counts as q <= p.  Four operations per
+      // element and head.  When p outweighs q here by more than 2^100 (rho would
+      // overflow) the same sums run in p's units: r' = max(0, rho' e_q - e_p), rho' =
+      // sb / sa, overlap = rho' zq - sum r', S = rho' (zq - sum_{r' > 0} e_q).
+      constexpr float kIndScale = 0x1p100f;
       float res[2 * G];
 #pragma unroll
       for (int k = 0; k < G; ++k) {
         const int rt = SHARED ? 0 : k, rq = NT + k;
         const float la = href[rt] - lse_sh[par][rt];   // log2 sa (-inf: no p mass here)
         const float lb = href[rq] - lse_sh[par][rq];   // log2 sb
-        const float lr = lb - la;
+        const float zq = z_sh[par][rq][tid];           // this lane's pass-1 sum of e_q
         // sums start at -0, so that the first addition folds away (-0 + x = x)
-        float al0 = -0.f, al1 = -0.f, s0_ = -0.f, s1_ = -0.f, scale = 0.f;
+        float r0 = -0.f, r1 = -0.f, c0 = -0.f, c1 = -0.f;
+        float ov, sv;
         if (la == kNegInf || lb == kNegInf) {
-          scale = 0.f;                                   // one of p, q has no mass here
-        } else if (lr <= 0.f) {                          // p units
-          const float rho = fast_exp2(lr);
-          scale = fast_exp2(la);
+          ov = sv = 0.f;                                 // one of p, q has no mass here
+        } else if (la - lb <= 100.f) {                   // q units
+          const float rho = fast_exp2(la - lb);
 #pragma unroll
           for (int qi = 0; qi < NQ; ++qi) {
             const float4 ep4 = held[rt][qi][tid], eq4 = held[rq][qi][tid];
             const float ep[4] = {ep4.x, ep4.y, ep4.z, ep4.w}, eq[4] = {eq4.x, eq4.y, eq4.z, eq4.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float tq = rho * eq[e];
-              const float m = __builtin_elementwise_minimum(ep[e], tq);
-              const float sv = tq <= ep[e] ? tq : 0.f;
-              if (e & 1) { al1 += m; s1_ += sv; } else { al0 += m; s0_ += sv; }
+              const float r = clamp01(__builtin_fmaf(-rho, ep[e], eq[e]));
+              const float ind = clamp01(r * kIndScale);
+              if (e & 1) { r1 += r; c1 = __builtin_fmaf(ind, eq[e], c1); }
+              else { r0 += r; c0 = __builtin_fmaf(ind, eq[e], c0); }
             }
           }
-        } else if (lr > 0.f) {                           // q units
-          const float rho = fast_exp2(-lr);
-          scale = fast_exp2(lb);
-#pragma unroll
+          const float sb = fast_exp2(lb);
+          ov = sb * (zq - (r0 + r1));
+          sv = sb * (zq - (c0 + c1));
+        } else if (la - lb > 100.f) {                    // p units (q is comparatively tiny)
+          const float rho = fast_exp2(lb - la);
+#pragma unroll 1
           for (int qi = 0; qi < NQ; ++qi) {
             const float4 ep4 = held[rt][qi][tid], eq4 = held[rq][qi][tid];
             const float ep[4] = {ep4.x, ep4.y, ep4.z, ep4.w}, eq[4] = {eq4.x, eq4.y, eq4.z, eq4.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float tp = rho * ep[e];
-              const float m = __builtin_elementwise_minimum(tp, eq[e]);
-              const float sv = eq[e] <= tp ? eq[e] : 0.f;
-              if (e & 1) { al1 += m; s1_ += sv; } else { al0 += m; s0_ += sv; }
+              const float r = clamp01(__builtin_fmaf(rho, eq[e], -ep[e]));
+              const float ind = clamp01(r * kIndScale);
+              if (e & 1) { r1 += r; c1 = __builtin_fmaf(ind, eq[e], c1); }
+              else { r0 += r; c0 = __builtin_fmaf(ind, eq[e], c0); }
             }
           }
+          const float sa = fast_exp2(la);
+          ov = sa * (rho * zq - (r0 + r1));
+          sv = sa * rho * (zq - (c0 + c1));
         } else {
-          scale = __builtin_nanf("");                    // a NaN statistic propagates
+          ov = sv = __builtin_nanf("");                  // a NaN statistic propagates
         }
-        res[2 * k] = (al0 + al1) * scale;
-        res[2 * k + 1] = (s0_ + s1_) * scale;
+        res[2 * k] = ov;
+        res[2 * k + 1] = sv;
       }
 #pragma unroll
       for (int k = 0; k < 2 * G; ++k) red_sh[k][tid] = res[k];

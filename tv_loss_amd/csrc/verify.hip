@@ -282,7 +282,8 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
       __syncthreads();
       // ---- pass 2 of item i - 2 ------------------------------------------------
       // In this wave's e units p = sa e_p and q = sb e_q.  While rho = sb / sa is at
-      // most 2^64, max(0, p - q) = sa max(0, e_p - rho e_q) (one rounding) and the
+      // most 2^64, max(0, p - q) = sa max(0, e_p - rho e_q) (one fused multiply-add;
+      // e_p <= 1, so the max is the [0, 1] output clamp, free) and the
       // overlap is the wave's p mass minus the residual, both summed in pass 1's
       // order, so disjoint supports give an overlap of exactly 0.  A larger rho (q
       // outweighs p here by more than 2^64) works in q's units instead.
@@ -302,7 +303,7 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
             const float va[4] = {ea.x, ea.y, ea.z, ea.w}, vb[4] = {eb.x, eb.y, eb.z, eb.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float d = fmaxf(__builtin_fmaf(-rho, vb[e], va[e]), 0.f);
+              const float d = clamp01(__builtin_fmaf(-rho, vb[e], va[e]));   // <= va <= 1
               if (e & 1) r1 += d; else r0 += d;
             }
           }
@@ -318,7 +319,7 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
             const float va[4] = {ea.x, ea.y, ea.z, ea.w}, vb[4] = {eb.x, eb.y, eb.z, eb.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float d = fmaxf(__builtin_fmaf(rr, va[e], -vb[e]), 0.f);
+              const float d = clamp01(__builtin_fmaf(rr, va[e], -vb[e]));    // <= rr va <= 1
               const float m = __builtin_elementwise_minimum(rr * va[e], vb[e]);
               if (e & 1) { r1 += d; o1 += m; } else { r0 += d; o0 += m; }
             }
@@ -370,7 +371,7 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
               ep = tp ? E[e] : ep;
               ip = tp ? gi0 + e : ip;
               if (pair2) {
-                const float d = fmaxf(__builtin_fmaf(-fq, vb[e], fp * va[e]), 0.f);
+                const float d = clamp01(__builtin_fmaf(-fq, vb[e], fp * va[e]));   // <= fp va <= 1
                 const bool tr = d * er > nr * E[e];
                 nr = tr ? d : nr;
                 er = tr ? E[e] : er;
@@ -840,7 +841,7 @@ __global__ void verify_finish(VerifyArgs a) {
   }
   // TV: the residual mass (the scan's total for rejection sampling)
   const float r_tot = TO || GM ? tv_sum : pair && !empty_res ? (float)sc.total : 0.f;
-  const bool use_q = !TO && pair && !empty_res;
+  bool use_q = !TO && pair && !empty_res;
   const bool drop_y = to_pair && !empty_res && y_ok;   // target-only residual: p without y
 
   // ---- owner segment inside the owner chunk, then the inverse CDF in it ------
@@ -867,7 +868,8 @@ __global__ void verify_finish(VerifyArgs a) {
     if (!pair || empty_res) best(1);
     token = m > kNegInf && idx < (uint32_t)a.V ? (int)idx : -1;
   }
-  if (!bad && !GM) {
+  // the owner segment inside the owner chunk, then the inverse CDF in it
+  auto sample_owner = [&]() -> int {
     const int oc = sc.owner;
     const int vpc = (int)a.sp.vec_per_chunk, nvec = (int)a.sp.nvec, nfull = (int)a.sp.nvec_full;
     const int obeg = oc * vpc;
@@ -927,7 +929,19 @@ __global__ void verify_finish(VerifyArgs a) {
     }
     seg_values(os, v);
     const int loc = wave_inverse_cdf<NV, PV>(v, tl - seg_start);
-    if (loc >= 0) token = (obeg + os * kSegVec) * PV + loc;
+    return loc >= 0 ? (obeg + os * kSegVec) * PV + loc : -1;
+  };
+  if (!bad && !GM) {
+    token = sample_owner();
+    if (token < 0 && use_q) {
+      // a residual made of rounding alone (p and q equal up to float32 rounding):
+      // its mass from pass 2 was positive, but the owner segment's values, formed
+      // again from the logits, have none; the row samples p, like an empty residual
+      empty_res = true;
+      use_q = false;
+      sc = wave_scan_owner(C, up, pmass);
+      token = sample_owner();
+    }
   }
 
   // clear this row's records and pass-2 words for the next call (the wave has read
