@@ -571,10 +571,18 @@ __device__ __forceinline__ double readlane_d(double v, int l) {
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
-// The previous lane's value (0 in lane 0).
+// The previous lane's value (0 in lane 0): a DPP wave shift right by one lane.
 __device__ __forceinline__ double lane_before(double incl) {
-  const double ex = __shfl_up(incl, 1, 64);
-  return (threadIdx.x & 63) == 0 ? 0.0 : ex;
+  return dpp_or_zero_f64<0x138>(incl);
+}
+
+// log2 z for a positive float z, accurate to a few units of 2^-24 in absolute terms
+// even where log2 z is large: z = m 2^k with m in [1, 2) exactly, log2 z = k +
+// log2 m, the float32 log2 of m (a value in [0, 1)) carrying the only rounding.
+__device__ __forceinline__ double log2_split(float z) {
+  int k = 0;
+  const float m = 2.f * __builtin_frexpf(z, &k);   // z = m 2^(k - 1), m in [1, 2)
+  return (double)(k - 1) + (double)fast_log2(m);
 }
 
 // Inverse CDF of one wave segment (NV blocks of 64 vectors, PV values per lane per
@@ -970,23 +978,33 @@ __global__ void verify_finish(VerifyArgs a) {
       // (a_y - b_y) L - (lse2_p - lse2_q), lse2 = ref + log2 z.  Forming the two
       // base-2 log-sum-exps (about 17 at V = 151936) in float32 would round each by
       // up to 1e-6; in float64 the ratio keeps the accuracy of the float32 sums z.
+      // The acceptance test in the base-2 log domain, in float64, from the row
+      // statistics (ref, z) the main kernel summed with the same logit scale L:
+      //   u < p(y) / q(y)  <=>  log2 u < (a_y - b_y) L - (lse2_p - lse2_q),
+      // lse2 = ref + log2 z.  Taken in float32, the two base-2 log-sum-exps (about
+      // 17 at V = 151936) would each round by up to 1e-6; here every term keeps the
+      // accuracy of the float32 sums z (log2 z split into exponent and mantissa),
+      // and log2 u (u on a 2^-24 grid) carries one float32 rounding.  A ratio of at
+      // least 1 accepts outright (u < 1); u = 0 gives -inf (accept whenever p(y) > 0);
+      // a NaN difference (p(y) = q(y) = 0) rejects.
       const double Ld = (double)L;
-      const double l2p = bad ? 0.0 : (double)st.p.ref + log2((double)st.p.z);
+      const double l2p = bad ? 0.0 : (double)st.p.ref + log2_split(st.p.z);
+      const double lu = u > 0.f ? (double)fast_log2(u) : -__builtin_huge_val();
       if (TO) {
         // target-only: accept the greedy token with probability p(y); the RS/TO
         // boundary TV < 1 - p(y)
-        const double pyd = exp2((double)ay * Ld - l2p);
-        const float py = y_ok && !bad ? (float)pyd : nan;
-        if (y_ok && !bad) flag = (double)u < pyd ? 1 : 0;
+        const double lpy = (double)ay * Ld - l2p;
+        const float py = y_ok && !bad ? fast_exp2((float)lpy) : nan;
+        if (y_ok && !bad) flag = lpy >= 0.0 || lu < lpy ? 1 : 0;   // p(y) = 1: u < 1 always
         a.draft_token[b * G + k] = y_ok && !bad ? y : -1;
         if (a.p_yhat) a.p_yhat[b * G + k] = py;
         if (a.rs_better) a.rs_better[b * G + k] = (uint8_t)(y_ok && !bad && r_tot < 1.f - py ? 1 : 0);
       } else if (!y_ok) {
         status |= kRowBadToken;
       } else if (!bad) {
-        const double l2q = (double)st.q.ref + log2((double)st.q.z);
+        const double l2q = (double)st.q.ref + log2_split(st.q.z);
         const double d = ((double)ay - (double)by) * Ld - (l2p - l2q);
-        if (d == d) flag = (double)u < fmin(1.0, exp2(d)) ? 1 : 0;   // NaN (p(y) = q(y) = 0): reject
+        if (d == d) flag = d >= 0.0 || lu < d ? 1 : 0;   // ratio >= 1: u < 1 always
       }
       a.accept[b * G + k] = (uint8_t)flag;
       if (a.overlap) a.overlap[b * G + k] = bad ? nan : alpha;
