@@ -292,6 +292,30 @@ mtp_status mtp_tv_loss_bwd(const void* target, int64_t target_pos_stride, int64_
                            mtp_dtype grad_dtype, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* End-to-end TV loss, forward and backward in one sweep (paperlayer App. F "Fused
+ * TV Loss Kernel": the backward reuses what the forward computed; rainbus "Method
+ * steps": the fused kernel keeps the memory peak down), for when the upstream
+ * gradient g = grad_loss[0] (device float [1]) is known before the call.
+ * Outputs: loss, pos_loss, saved as mtp_tv_loss_fwd; grad as mtp_tv_loss_bwd with
+ * the same g.  Each logit is read once and each gradient element written once;
+ * the indicator of the gradient is the one S uses (on float32 probabilities), so
+ * the saved statistics are exactly those the gradient was formed with.  Shapes
+ * the one-sweep kernel does not take (more than 5 rows per position, gamma > 4, or
+ * a vocabulary whose chunks cannot all be resident) run mtp_tv_loss_fwd then
+ * mtp_tv_loss_bwd on the same workspace.  Arguments and limits as for those calls;
+ * workspace: mtp_tv_loss_fwd_bwd_workspace_size bytes, zeroed once, left zeroed.
+ */
+mtp_status mtp_tv_loss_fwd_bwd_workspace_size(int32_t T, int32_t gamma, int32_t vocab, mtp_dtype dtype,
+                                              int32_t shared_target, size_t* bytes);
+
+mtp_status mtp_tv_loss_fwd_bwd(const void* target, int64_t target_pos_stride, int64_t target_head_stride,
+                               const void* draft, int64_t draft_pos_stride, int64_t draft_head_stride,
+                               mtp_dtype dtype, int32_t T, int32_t gamma, int32_t vocab, const float* grad_loss,
+                               float* loss, float* pos_loss, float* saved,
+                               void* grad, int64_t grad_pos_stride, int64_t grad_head_stride,
+                               mtp_dtype grad_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* End-to-end TV loss with top-K targets (paperlayer App. F "Fused TV Loss
  * Kernel": an optional top-K path keeps O(K) of the target instead of O(V)).
  *

@@ -52,6 +52,11 @@ SIGNATURES = {
     "mtp_tv_loss_bwd": (_c.c_int, [_P, _c.c_int64, _c.c_int64, _P, _c.c_int64, _c.c_int64, _c.c_int,
                                    _c.c_int32, _c.c_int32, _c.c_int32, _P, _P, _P, _c.c_int64, _c.c_int64,
                                    _c.c_int, _P]),
+    "mtp_tv_loss_fwd_bwd_workspace_size": (_c.c_int, [_c.c_int32, _c.c_int32, _c.c_int32, _c.c_int, _c.c_int32,
+                                                      _c.POINTER(_c.c_size_t)]),
+    "mtp_tv_loss_fwd_bwd": (_c.c_int, [_P, _c.c_int64, _c.c_int64, _P, _c.c_int64, _c.c_int64, _c.c_int,
+                                       _c.c_int32, _c.c_int32, _c.c_int32, _P, _P, _P, _P, _P, _c.c_int64,
+                                       _c.c_int64, _c.c_int, _P, _c.c_size_t, _P]),
     "mtp_tv_topk_workspace_size": (_c.c_int, [_c.c_int32, _c.c_int32, _c.c_int32, _c.c_int,
                                               _c.POINTER(_c.c_size_t)]),
     "mtp_tv_topk_fwd": (_c.c_int, [_P, _P, _c.c_int64, _c.c_int64, _c.c_int32, _P, _c.c_int64, _c.c_int64, _c.c_int,

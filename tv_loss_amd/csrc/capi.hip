@@ -100,6 +100,11 @@ mtp_status tv_pipe_capacity(int dt, int G, bool shared, int64_t* per_gpu) {
                   [&](int* n) { return mtp::tv_pipe_occupancy(dt, G, shared, n); }, per_gpu);
 }
 
+mtp_status tv_fused_capacity(int dt, int gdt, int G, bool shared, int64_t* per_gpu) {
+  return capacity(2000 + dt * 256 + gdt * 128 + G * 2 + (shared ? 1 : 0),
+                  [&](int* n) { return mtp::tv_fused_occupancy(dt, gdt, G, shared, n); }, per_gpu);
+}
+
 // ---- workspace layouts --------------------------------------------------------
 struct VerifyLayout {
   size_t err, part1, part2, part3, gkeys, total;
@@ -154,6 +159,40 @@ size_t tv_workspace_bytes(int32_t T, int32_t G, int32_t V, mtp_dtype dt, bool sh
   if (mtp::tv_pipe_vec_per_thread(dt, G, shared) > 0) {
     const size_t p = tv_layout(T, G, V, dt, shared, true).total;
     b = p > b ? p : b;
+  }
+  return b;
+}
+
+// The fused forward + backward: error word, normaliser records part1
+// [t][chunk][rows], overlap / S records part3 [t][chunk][gamma], per-position
+// losses [t]; the single-read forward's chunking.
+struct FusedLayout {
+  size_t err, part1, part3, pos, total;
+  mtp::RowSplit sp;
+};
+
+FusedLayout fused_layout(int32_t T, int32_t G, int32_t V, mtp_dtype dt, bool shared) {
+  FusedLayout L{};
+  L.sp = mtp::make_split(V, per_vec(dt), mtp::tv_pipe_vec_per_thread(dt, G, shared), false);
+  const int64_t C = L.sp.nchunks;
+  size_t off = 0;
+  L.err = off; off = align256(off + 4);
+  L.part1 = off; off = align256(off + (size_t)T * C * mtp::tv_fwd_part1_words(G, shared) * 8);
+  L.part3 = off; off = align256(off + (size_t)T * C * G * 8);
+  L.pos = off; off = align256(off + (size_t)T * 4);
+  L.total = off;
+  return L;
+}
+
+bool fused_shape(int32_t G, bool shared) { return G <= mtp::kWaves && mtp::tv_pipe_vec_per_thread(MTP_BF16, G, shared) > 0; }
+
+// Bytes a fused call may need: its own layout or, for the shapes it hands to the
+// forward and backward calls, theirs.
+size_t fused_workspace_bytes(int32_t T, int32_t G, int32_t V, mtp_dtype dt, bool shared) {
+  size_t b = tv_workspace_bytes(T, G, V, dt, shared);
+  if (fused_shape(G, shared)) {
+    const size_t f = fused_layout(T, G, V, dt, shared).total;
+    b = f > b ? f : b;
   }
   return b;
 }
@@ -669,6 +708,75 @@ mtp_status mtp_verify_noalloc(const void* target, int64_t target_row_stride, con
   return verify_impl(mtp::kVerifyRejection, 1.f, target, target_row_stride, draft, draft_row_stride, dtype, batch,
                      gamma, vocab, draft_tokens, seed, offset, accept, accepted_len, next_token, nullptr, nullptr,
                      nullptr, row_token, overlap, tv, entropy, row_status, ws, kScratchBytes, stream);
+}
+
+mtp_status mtp_tv_loss_fwd_bwd_workspace_size(int32_t T, int32_t gamma, int32_t vocab, mtp_dtype dtype,
+                                              int32_t shared_target, size_t* bytes) {
+  if (!bytes) return fail(MTP_ERR_NULL, "bytes is NULL");
+  mtp_status s = check_common(dtype, gamma, vocab);
+  if (s) return s;
+  if (T < 1) return fail(MTP_ERR_SHAPE, "T = %d must be >= 1", T);
+  *bytes = fused_workspace_bytes(T, gamma, vocab, dtype, shared_target != 0);
+  return ok();
+}
+
+mtp_status mtp_tv_loss_fwd_bwd(const void* target, int64_t target_pos_stride, int64_t target_head_stride,
+                               const void* draft, int64_t draft_pos_stride, int64_t draft_head_stride,
+                               mtp_dtype dtype, int32_t T, int32_t gamma, int32_t vocab, const float* grad_loss,
+                               float* loss, float* pos_loss, float* saved, void* grad, int64_t grad_pos_stride,
+                               int64_t grad_head_stride, mtp_dtype grad_dtype, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  mtp_status s = check_tv_inputs(target, target_pos_stride, target_head_stride, draft, draft_pos_stride,
+                                 draft_head_stride, dtype, T, gamma, vocab);
+  if (s) return s;
+  if (grad_dtype != MTP_F32 && grad_dtype != MTP_BF16)
+    return fail(MTP_ERR_DTYPE, "unknown grad dtype code %d", (int)grad_dtype);
+  if (!loss || !saved || !grad_loss || !grad) return fail(MTP_ERR_NULL, "loss, saved, grad_loss or grad is NULL");
+  if (grad_pos_stride < 0 || grad_head_stride < 0) return fail(MTP_ERR_SHAPE, "negative grad stride");
+  if ((s = check_row_base(grad, grad_pos_stride, grad_dtype, "grad position"))) return s;
+  if ((s = check_row_base(grad, grad_head_stride, grad_dtype, "grad head"))) return s;
+  const bool shared = target_head_stride == 0;
+  if ((s = check_workspace(workspace, workspace_bytes, fused_workspace_bytes(T, gamma, vocab, dtype, shared)))) return s;
+  // one sweep when the shape fits the fused kernel and every chunk of a row can be
+  // resident at once; otherwise the forward call, then the backward call
+  bool fused = false;
+  int sgroups = 0, layers = 0;
+  FusedLayout L{};
+  if (fused_shape(gamma, shared)) {
+    int64_t per_gpu = 0;
+    if ((s = tv_fused_capacity(dtype, grad_dtype, gamma, shared, &per_gpu))) return s;
+    L = fused_layout(T, gamma, vocab, dtype, shared);
+    if ((int64_t)L.sp.nchunks <= per_gpu && (int64_t)T * L.sp.nchunks <= 0x7fffffffLL) {
+      fused = true;
+      plan_layers(per_gpu, L.sp.nchunks, T, &sgroups, &layers);
+    }
+  }
+  if (!fused) {
+    if ((s = mtp_tv_loss_fwd(target, target_pos_stride, target_head_stride, draft, draft_pos_stride,
+                             draft_head_stride, dtype, T, gamma, vocab, loss, pos_loss, saved, workspace,
+                             workspace_bytes, stream)))
+      return s;
+    return mtp_tv_loss_bwd(target, target_pos_stride, target_head_stride, draft, draft_pos_stride,
+                           draft_head_stride, dtype, T, gamma, vocab, saved, grad_loss, grad, grad_pos_stride,
+                           grad_head_stride, grad_dtype, stream);
+  }
+  mtp::TvArgs a{};
+  a.target = target; a.t_pos = target_pos_stride; a.t_head = target_head_stride;
+  a.draft = draft; a.d_pos = draft_pos_stride; a.d_head = draft_head_stride;
+  a.T = T; a.G = gamma; a.V = vocab;
+  a.loss = loss; a.pos_loss = pos_loss; a.saved = saved;
+  a.grad_loss = grad_loss;
+  a.grad = grad; a.g_pos = grad_pos_stride; a.g_head = grad_head_stride; a.grad_dt = grad_dtype;
+  a.err = at<uint32_t>(workspace, L.err);
+  a.part1 = at<uint64_t>(workspace, L.part1);
+  a.part3 = at<uint64_t>(workspace, L.part3);
+  a.pos_ws = at<float>(workspace, L.pos);
+  a.sp = L.sp;
+  a.sgroups = sgroups;
+  a.wait_limit = g_wait_limit.load(std::memory_order_relaxed);
+  hipError_t e = mtp::launch_tv_fused(a, dtype, shared, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MTP_ERR_LAUNCH, "fused TV loss launch failed: %s", hipGetErrorString(e));
+  return ok();
 }
 
 mtp_status mtp_workspace_error(const void* workspace, uint32_t* host_word, void* stream) {

@@ -111,8 +111,9 @@ struct TvArgs {
   const float* saved_in; const float* grad_loss;
   void* grad; int64_t g_pos, g_head; int grad_dt;
   // forward workspace: error word, log-sum-exp partials [t][chunk][rows] as
-  // (ref, z), overlap and S partials [t][chunk][2 gamma], per-position losses [t]
-  uint32_t* err; uint64_t* part1; float* part2; float* pos_ws;
+  // (ref, z), overlap and S partials [t][chunk][2 gamma], per-position losses [t];
+  // the fused forward + backward also: overlap / S records [t][chunk][gamma]
+  uint32_t* err; uint64_t* part1; float* part2; float* pos_ws; uint64_t* part3;
   RowSplit sp;
   int sgroups;   // single-read forward: super-groups of sp.nchunks workgroups, all resident
   // top-K path: the target of head k at position t is given by K entries, indices
@@ -136,6 +137,12 @@ constexpr int kTvPipeMaxRows = 5;
 int tv_pipe_vec_per_thread(int dt, int G, bool shared);
 hipError_t tv_pipe_occupancy(int dt, int G, bool shared, int* blocks_per_cu);
 hipError_t launch_tv_pipe_fwd(const TvArgs& a, int dt, bool shared, hipStream_t stream);
+// fused forward + backward (same shapes as the single-read forward): launch (main,
+// finish, mean) and main-kernel occupancy; the workspace holds the normaliser
+// records part1 [t][chunk][rows], the overlap / S records part3 [t][chunk][gamma]
+// and the per-position losses
+hipError_t tv_fused_occupancy(int dt, int grad_dt, int G, bool shared, int* blocks_per_cu);
+hipError_t launch_tv_fused(const TvArgs& a, int dt, bool shared, hipStream_t stream);
 int tv_bwd_vec_per_thread(int dt);   // top-K backward
 int tv_bwd_full_vec_per_thread(int dt, int G, bool shared);
 hipError_t launch_tv_bwd(const TvArgs& a, int dt, bool shared, hipStream_t stream);

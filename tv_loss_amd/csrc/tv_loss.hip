@@ -403,13 +403,14 @@ __global__ __launch_bounds__(kBlock, 2) void tv_pipe_main(TvArgs a) {
       //   overlap = sum min(rho e_p, e_q) = zq - sum r,
       //   S = sum_{q <= p} e_q = zq - sum_{r > 0} e_q,
       // where zq is this lane's pass-1 sum of e_q (so disjoint supports give exactly
-      // 0 and identical rows exactly zq).  The indicator 1[r > 0] is r * 2^100
-      // clamped: 1 for every r >= 2^-100 (the rare r below it weigh under 2^-100 of
-      // the wave's largest q); a tie (r = 0) counts as q <= p.  Four operations per
-      // element and head.  When p outweighs q here by more than 2^100 (rho would
+      // 0 and identical rows exactly zq).  The indicator 1[r > 0] is r * 2^126
+      // clamped: exactly 1 for every normal r (only a subnormal r, a difference
+      // below 2^-126 of the wave's largest q, gives a fraction); a tie (r = 0)
+      // counts as q <= p.  Four operations per element and head.  When p outweighs
+      // q here by more than 2^100 (rho would
       // overflow) the same sums run in p's units: r' = max(0, rho' e_q - e_p), rho' =
       // sb / sa, overlap = rho' zq - sum r', S = rho' (zq - sum_{r' > 0} e_q).
-      constexpr float kIndScale = 0x1p100f;
+      constexpr float kIndScale = 0x1p126f;
       float res[2 * G];
 #pragma unroll
       for (int k = 0; k < G; ++k) {
@@ -751,6 +752,404 @@ __global__ __launch_bounds__(kBlock) void tv_bwd_kernel(TvArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Fused forward + backward (paperlayer App. F "Fused TV Loss Kernel": the backward
+// reuses quantities the forward computed; rainbus "Method steps": the fused
+// kernel keeps the memory peak down).  With the upstream scalar g known before
+// the call, one sweep over the logits gives the loss, the saved statistics and
+// the gradient: every logit is read once and every gradient element written once.
+//
+// The single-read forward's pipeline (super-groups of C workgroups, chunk c of
+// every row of a position per workgroup, records of the row normalisers, pass 2
+// from the e values held on chip two layers after pass 1) gains a second exchange
+// and a gradient phase.  Layer i:
+//   * gradient of position i - 3: every wave reads the position's overlap and S
+//     totals (merged by the waves from the chunks' records in one fixed order),
+//     forms the end-to-end weights and writes g_v = w q_v (1[q_v <= p_v] - S) for
+//     its segment of every head from the values s_v it kept since pass 2;
+//   * pass 2 of position i - 2 (as in the forward) also keeps, per draft element,
+//     s_v = +e_q where q_v <= p_v and -e_q where q_v > p_v (e_q in the wave's q
+//     units sb): the gradient needs q_v = sb |s_v| and the indicator, the sign;
+//     the chunk's overlap and S partials (summed over the waves) are published
+//     at once as one self-announcing record per head;
+//   * the e values of position i - 1 move to LDS, position i is unpacked, the
+//     record polls of positions i - 1 (normalisers) and i - 2 (overlap, S) and
+//     the loads of position i + 1 go out, pass 1 of position i and its records.
+// The overlap/S records of a position are polled a layer after they are
+// published and used a layer later; the s values live in registers for one
+// layer.  tv_fused_finish (one wave per position) writes the saved statistics
+// and l_t from the same records, merged in the same order, and clears them.
+template <int G>
+struct FusedRec {
+  // record word of (chunk, head): (overlap partial, S partial with the sign bit as
+  // a marker: S >= 0, so a published word is never zero)
+  static constexpr int kStride = G * 8;
+};
+
+// The overlap and S totals of head k from the chunks' records: lane l folds record
+// l, then l + 64, ... in that order, then the wave sums the lanes (the same bits in
+// every lane and every workgroup).  `v` is this lane's first word, loaded earlier.
+// NaN totals if the wait timed out.
+template <int G>
+__device__ __forceinline__ void fused_totals(uint64_t v, __amdgpu_buffer_rsrc_t rs, int C, int k, uint32_t* err,
+                                             uint64_t limit, float& alpha, float& S) {
+  float ac = 0.f, sc = 0.f;
+  const bool timed_out = poll_words(v, rs, C, FusedRec<G>::kStride, k, err, limit, [&](bool first, uint64_t w) {
+    const float aw = unpack_lo(w), sw = unmark(unpack_hi(w));
+    ac = first ? aw : ac + aw;
+    sc = first ? sw : sc + sw;
+  });
+  if ((threadIdx.x & 63) >= C) ac = sc = 0.f;
+  float t[2] = {ac, sc};
+  wave_reduce<false, 2>(t);
+  alpha = timed_out ? __builtin_nanf("") : t[0];
+  S = timed_out ? __builtin_nanf("") : t[1];
+}
+
+// This thread's gradient values of one head's segment (NV vectors of PV values,
+// vector v0 + 64 j), stored to row `row`: full vectors as one 16-byte (bf16) or
+// PV/4 16-byte (fp32) non-temporal stores, the row's partial last vector element by
+// element; vectors past the chunk or the row are skipped.
+template <int GDT, int NV, int PV>
+__device__ __forceinline__ void fused_store(char* row, int v0, int vend, const RowSplit& sp, int64_t V,
+                                            const float (&g)[NV * PV]) {
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int vi = v0 + j * 64;
+    if (vi < vend) store_grad<GDT, PV>(row, vi, sp, V, g + j * PV);
+  }
+}
+
+template <int DT, int GDT, int G, bool SHARED>
+__global__ __launch_bounds__(kBlock, 2) void tv_fused_main(TvArgs a) {
+  constexpr int NT = FwdShape<G, SHARED>::NT;
+  constexpr int NR = FwdShape<G, SHARED>::NR;
+  constexpr int PV = Elem<DT>::kPerVec;
+  constexpr int NV = pipe_nv<NR>(PV);
+  constexpr int NE = NV * PV;
+  constexpr int NQ = NE / 4;
+  constexpr int kSegVec = NV * 64;
+  constexpr int RW = (NR + kWaves - 1) / kWaves;
+  constexpr int kSt = NR * 8;
+  constexpr int kSt2 = FusedRec<G>::kStride;
+  static_assert(G <= kWaves, "one wave per head merges the overlap / S records");
+  const int C = a.sp.nchunks;
+  const int slot = blockIdx.x;
+  const int sg = slot / C, c = slot - sg * C;
+  const int S = a.sgroups;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  if (sg >= a.T) return;
+  const int nl = (a.T - 1 - sg) / S + 1;
+  auto pos_of = [&](int i) { return sg + i * S; };
+  auto rsrc_rec = [&](int t) { return rsrc_of(a.part1 + (int64_t)t * C * NR); };
+  auto rsrc_rec2 = [&](int t) { return rsrc_of(a.part3 + (int64_t)t * C * G); };
+
+  const int vpc = (int)a.sp.vec_per_chunk, nvec = (int)a.sp.nvec, nfull = (int)a.sp.nvec_full;
+  const int vbeg = c * vpc;
+  const int vend = min(vbeg + vpc, nvec);
+  const int s0 = vbeg + wave * kSegVec;
+  const int v0 = s0 + lane;
+  const int lim = min(vend, nfull);
+  const bool full = s0 + kSegVec <= lim;
+  const int last = nfull - 1;
+  const int tail = nfull;
+  const int V = (int)a.V;
+  const int row_bytes = (int)min(a.V * Elem<DT>::kBytes, (int64_t)0x7fffffff);
+  const float gscale = -a.grad_loss[0] / (float)a.T;
+  char* gb = reinterpret_cast<char*>(a.grad);
+  constexpr int gbytes = GDT == kBF16 ? 2 : 4;
+
+  __shared__ float4 held[NR][NQ][kBlock];      // e values of the position two layers back
+  __shared__ float ref_sh[2][NR][kWaves];       // pass-1 wave references, by layer parity
+  __shared__ float z_sh[2][NR][kBlock];         // pass-1 lane sums in their wave's units
+  __shared__ float lse_sh[NR];                  // row log2-sum-exps of the position in pass 2
+  __shared__ float red_sh[2 * G][kBlock];       // pass-2 lane partials (overlap, S per head)
+  __shared__ float tot_sh[2 * G];               // overlap and S totals of the gradient's position
+
+  auto prefetch = [&](int t, bool live, RawChunk<NV, NR>& rb) {
+    const char* rows[NR];
+    fwd_rows<DT, NT, G>(a, t, rows);
+    issue_seg_fixed<DT, NV, NR>(rb, rows, v0, last, live, row_bytes);
+  };
+  RawChunk<NV, NR> raw;
+  uint64_t wpoll[RW], wpoll2 = 0ull;
+#pragma unroll
+  for (int j = 0; j < RW; ++j) wpoll[j] = 0ull;
+  float x[NR][NE];
+  float xref[NR], href[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) xref[r] = href[r] = 0.f;
+  float sv[G][NE];   // signed q values kept from pass 2 for the gradient
+  float sbg[G];      // their q units (log2) per head
+#pragma unroll
+  for (int k = 0; k < G; ++k) sbg[k] = 0.f;
+
+  // Layer -1 only issues the loads of position 0 (from the same code as every
+  // later prefetch); layer i unpacks position i, whose loads went out a layer ago.
+  for (int i = -1; i < nl + 3; ++i) {
+    const bool dog = i >= 3 && i - 3 < nl;   // gradient of position i - 3
+    const bool do2 = i >= 2 && i - 2 < nl;   // pass 2 of position i - 2
+    const bool do1 = i >= 0 && i < nl;       // pass 1 of position i
+    const int t_g = pos_of(i - 3), t_2 = pos_of(i - 2), t_1 = pos_of(i - 1), t_0 = pos_of(i);
+    // ---- record polls issued a layer ago: overlap / S totals, row normalisers --
+    if (dog || do2) {
+      __builtin_amdgcn_s_setprio(3);
+      if (dog && wave < G) {
+        float al, s;
+        fused_totals<G>(wpoll2, rsrc_rec2(t_g), C, wave, a.err, a.wait_limit, al, s);
+        if (lane == 0) {
+          tot_sh[2 * wave] = al;
+          tot_sh[2 * wave + 1] = s;
+        }
+      }
+      if (do2) {
+#pragma unroll
+        for (int j = 0; j < RW; ++j) {
+          const int r = wave + j * kWaves;
+          if (r < NR) {
+            const Lse st = poll_row(wpoll[j], rsrc_rec(t_2), C, kSt, r, a.err, a.wait_limit);
+            if (lane == 0) lse_sh[r] = lse_log2(st);
+          }
+        }
+      }
+      __builtin_amdgcn_s_setprio(0);
+      __syncthreads();
+    }
+    // ---- gradient of position i - 3 ------------------------------------------
+    if (dog) {
+      float al[G], Sk[G];
+#pragma unroll
+      for (int k = 0; k < G; ++k) {
+        const float ov = tot_sh[2 * k];   // NaN (a row without a normaliser) stays NaN
+        al[k] = ov != ov ? ov : fminf(fmaxf(ov, 0.f), 1.f);
+        Sk[k] = tot_sh[2 * k + 1];
+      }
+#pragma unroll
+      for (int k = 0; k < G; ++k) {
+        // w_k = -(g / T) sum_{m >= k} prod_{j <= m, j != k} alpha_j
+        float wsum = 0.f;
+#pragma unroll
+        for (int m = k; m < G; ++m) {
+          float prod = 1.f;
+#pragma unroll
+          for (int j = 0; j <= m; ++j)
+            if (j != k) prod *= al[j];
+          wsum += prod;
+        }
+        const float qs = gscale * wsum * fast_exp2(sbg[k]);   // w sb
+        const float cp = qs * (1.f - Sk[k]), cn = qs * Sk[k];
+        float gv[NE];
+#pragma unroll
+        for (int e = 0; e < NE; ++e) gv[e] = sv[k][e] * (sv[k][e] >= 0.f ? cp : cn);
+        char* grow = gb + ((int64_t)t_g * a.g_pos + (int64_t)k * a.g_head) * gbytes;
+        fused_store<GDT, NV, PV>(grow, v0, vend, a.sp, a.V, gv);
+      }
+    }
+    // ---- pass 2 of position i - 2 ---------------------------------------------
+    if (do2) {
+      constexpr float kIndScale = 0x1p126f;
+      float res[2 * G];
+#pragma unroll
+      for (int k = 0; k < G; ++k) {
+        const int rt = SHARED ? 0 : k, rq = NT + k;
+        const float la = href[rt] - lse_sh[rt];   // log2 sa (-inf: no p mass here)
+        const float lb = href[rq] - lse_sh[rq];   // log2 sb
+        const float zq = z_sh[i & 1][rq][tid];
+        float r0 = -0.f, r1 = -0.f, c0 = -0.f, c1 = -0.f;
+        float ov, svp;
+        sbg[k] = lb;
+        if (lb == kNegInf) {                             // no q mass here: no gradient
+          ov = svp = 0.f;
+#pragma unroll
+          for (int e = 0; e < NE; ++e) sv[k][e] = 0.f;
+        } else if (la == kNegInf) {                      // no p mass: every q > p
+          ov = svp = 0.f;
+#pragma unroll
+          for (int qi = 0; qi < NQ; ++qi) {
+            const float4 eq4 = held[rq][qi][tid];
+            sv[k][4 * qi] = -eq4.x; sv[k][4 * qi + 1] = -eq4.y; sv[k][4 * qi + 2] = -eq4.z; sv[k][4 * qi + 3] = -eq4.w;
+          }
+        } else if (la - lb <= 100.f) {                   // q units
+          const float rho = fast_exp2(la - lb);
+#pragma unroll
+          for (int qi = 0; qi < NQ; ++qi) {
+            const float4 ep4 = held[rt][qi][tid], eq4 = held[rq][qi][tid];
+            const float ep[4] = {ep4.x, ep4.y, ep4.z, ep4.w}, eq[4] = {eq4.x, eq4.y, eq4.z, eq4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float r = clamp01(__builtin_fmaf(-rho, ep[e], eq[e]));
+              const float ind = clamp01(r * kIndScale);   // 1[q > p]
+              sv[k][4 * qi + e] = __builtin_fmaf(-2.f * ind, eq[e], eq[e]);
+              if (e & 1) { r1 += r; c1 = __builtin_fmaf(ind, eq[e], c1); }
+              else { r0 += r; c0 = __builtin_fmaf(ind, eq[e], c0); }
+            }
+          }
+          const float sb = fast_exp2(lb);
+          ov = sb * (zq - (r0 + r1));
+          svp = sb * (zq - (c0 + c1));
+        } else if (la - lb > 100.f) {                    // p units (q is comparatively tiny)
+          const float rho = fast_exp2(lb - la);
+#pragma unroll
+          for (int qi = 0; qi < NQ; ++qi) {
+            const float4 ep4 = held[rt][qi][tid], eq4 = held[rq][qi][tid];
+            const float ep[4] = {ep4.x, ep4.y, ep4.z, ep4.w}, eq[4] = {eq4.x, eq4.y, eq4.z, eq4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float r = clamp01(__builtin_fmaf(rho, eq[e], -ep[e]));
+              const float ind = clamp01(r * kIndScale);
+              sv[k][4 * qi + e] = __builtin_fmaf(-2.f * ind, eq[e], eq[e]);
+              if (e & 1) { r1 += r; c1 = __builtin_fmaf(ind, eq[e], c1); }
+              else { r0 += r; c0 = __builtin_fmaf(ind, eq[e], c0); }
+            }
+          }
+          const float sa = fast_exp2(la);
+          ov = sa * (rho * zq - (r0 + r1));
+          svp = sa * rho * (zq - (c0 + c1));
+        } else {
+          ov = svp = __builtin_nanf("");                 // a NaN statistic propagates
+#pragma unroll
+          for (int e = 0; e < NE; ++e) sv[k][e] = __builtin_nanf("");
+        }
+        res[2 * k] = ov;
+        res[2 * k + 1] = svp;
+      }
+#pragma unroll
+      for (int k = 0; k < 2 * G; ++k) red_sh[k][tid] = res[k];
+      __syncthreads();
+      // the chunk's overlap and S partials: wave k sums head k over the four
+      // waves' lanes (in a fixed order) and publishes them as one record word
+      if (wave < G) {
+        float v[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float* rr = red_sh[2 * wave + h];
+          v[h] = (rr[lane] + rr[lane + 64]) + (rr[lane + 128] + rr[lane + 192]);
+        }
+        wave_reduce<false, 2>(v);
+        if (lane == 0) rec_store(rsrc_rec2(t_2), c * kSt2 + wave * 8, pack2(v[0], mark(v[1])));
+      }
+    }
+    // ---- position i - 1 moves to LDS (own slots only) --------------------------
+    if (i >= 1 && i - 1 < nl) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+#pragma unroll
+        for (int qi = 0; qi < NQ; ++qi)
+          held[r][qi][tid] = make_float4(x[r][4 * qi], x[r][4 * qi + 1], x[r][4 * qi + 2], x[r][4 * qi + 3]);
+        href[r] = xref[r];
+      }
+    }
+    // ---- position i: unpack; record polls; the loads of position i + 1 --------
+    if (do1) {
+      const char* rows[NR];
+      fwd_rows<DT, NT, G>(a, t_0, rows);
+      int lim_l = lim, tail_l = tail, vend_l = vend, V_l = V;
+      asm volatile("" : "+s"(lim_l), "+s"(tail_l), "+s"(vend_l), "+s"(V_l));
+      unpack_seg<DT, NV, NR>(raw, rows, v0, full, lim_l, tail_l, vend_l, V_l, x);
+    }
+    if (i >= 1 && i <= nl && lane < C) {
+      const __amdgpu_buffer_rsrc_t rs = rsrc_rec(t_1);
+#pragma unroll
+      for (int j = 0; j < RW; ++j) {
+        const int r = wave + j * kWaves;
+        if (r < NR) wpoll[j] = rec_load(rs, lane * kSt + r * 8);
+      }
+    }
+    if (do2 && wave < G && lane < C) wpoll2 = rec_load(rsrc_rec2(t_2), lane * kSt2 + wave * 8);
+    __builtin_amdgcn_sched_barrier(0);
+    prefetch(i + 1 < nl ? pos_of(i + 1) : sg, i + 1 < nl, raw);
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- pass 1 of position i ------------------------------------------------
+    if (do1) {
+      __builtin_amdgcn_s_setprio(1);
+      float zl[NR];
+      lane_pass1<NE, NR>(x, xref, zl, kLog2e);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) z_sh[i & 1][r][tid] = zl[r];
+      if (lane == 0) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) ref_sh[i & 1][r][wave] = xref[r];
+      }
+      __builtin_amdgcn_s_setprio(0);
+      __syncthreads();
+      __builtin_amdgcn_s_setprio(3);
+      const __amdgpu_buffer_rsrc_t rs = rsrc_rec(t_0);
+#pragma unroll
+      for (int j = 0; j < RW; ++j) {
+        const int r = wave + j * kWaves;
+        if (r < NR) {
+          float rf[kWaves], R = kNegInf;
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w) {
+            rf[w] = ref_sh[i & 1][r][w];
+            R = fmaximum(R, rf[w]);
+          }
+          const float Rf = finite_ref(R);
+          float zs = 0.f;
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w)
+            zs = __builtin_fmaf(z_sh[i & 1][r][w * 64 + lane], fast_exp2(rf[w] - Rf), zs);
+          const float Z = wave_total(zs);
+          if (lane == 0) rec_store(rs, c * kSt + r * 8, pack2(R, mark(Z)));
+        }
+      }
+      __builtin_amdgcn_s_setprio(0);
+    }
+  }
+}
+
+// One wave per position: row log-sum-exps from the normaliser records, overlap and
+// S totals from the overlap / S records (merged as the main kernel merged them, so
+// the saved statistics are the ones its gradient used), l_t; clears the records.
+template <int G, bool SHARED>
+__global__ __launch_bounds__(64 * kFinishWaves) void tv_fused_finish(TvArgs a) {
+  constexpr int NT = FwdShape<G, SHARED>::NT;
+  constexpr int NR = FwdShape<G, SHARED>::NR;
+  constexpr int kSt = NR * 8;
+  constexpr int kSt2 = FusedRec<G>::kStride;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kFinishWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const int C = a.sp.nchunks;
+  const __amdgpu_buffer_rsrc_t rs = rsrc_of(a.part1 + (int64_t)t * C * NR);
+  const __amdgpu_buffer_rsrc_t rs2 = rsrc_of(a.part3 + (int64_t)t * C * G);
+  const int lc = min(lane, C - 1);
+  uint64_t v[NR], v2[G];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) v[r] = rec_load(rs, lc * kSt + r * 8);
+#pragma unroll
+  for (int k = 0; k < G; ++k) v2[k] = rec_load(rs2, lc * kSt2 + k * 8);
+  float lse2[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+    lse2[r] = lse_log2(poll_row(lane < C ? v[r] : 0ull, rs, C, kSt, r, a.err, a.wait_limit));
+  float al[G], Sk[G];
+#pragma unroll
+  for (int k = 0; k < G; ++k) fused_totals<G>(lane < C ? v2[k] : 0ull, rs2, C, k, a.err, a.wait_limit, al[k], Sk[k]);
+  uint64_t* rec = a.part1 + (int64_t)t * C * NR;
+  for (int i = lane; i < C * NR; i += 64) rec[i] = 0ull;
+  uint64_t* rec2 = a.part3 + (int64_t)t * C * G;
+  for (int i = lane; i < C * G; i += 64) rec2[i] = 0ull;
+  if (lane == 0) {
+    float prod = 1.f, l = 0.f;
+    float* sv = a.saved + (int64_t)t * G * kTvSavedStride;
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const float ov = al[k];
+      const float alc = ov != ov ? ov : fminf(fmaxf(ov, 0.f), 1.f);
+      prod *= alc;
+      l -= prod;
+      sv[k * kTvSavedStride + 0] = lse2[SHARED ? 0 : k] * kLn2;
+      sv[k * kTvSavedStride + 1] = lse2[NT + k] * kLn2;
+      sv[k * kTvSavedStride + 2] = alc;
+      sv[k * kTvSavedStride + 3] = Sk[k];
+    }
+    if (a.pos_loss) a.pos_loss[t] = l;
+    a.pos_ws[t] = l;
+  }
+}
+
+// ---------------------------------------------------------------------------
 template <int DT, bool SHARED, int G>
 static hipError_t launch_fwd_g(const TvArgs& a, hipStream_t stream) {
   const int64_t grid = (int64_t)a.T * a.sp.nchunks;
@@ -845,6 +1244,60 @@ hipError_t tv_pipe_occupancy(int dt, int G, bool shared, int* blocks_per_cu) {
 
 hipError_t launch_tv_pipe_fwd(const TvArgs& a, int dt, bool shared, hipStream_t stream) {
   return pipe_any(dt, shared, a.G, &a, stream, nullptr);
+}
+
+// ---- fused forward + backward: launch, occupancy ------------------------------
+template <int DT, int GDT, bool SHARED, int G>
+static hipError_t fused_g(const TvArgs* a, hipStream_t stream, int* occ) {
+  if constexpr (!pipe_fits<G, SHARED>() || G > kWaves) {
+    if (occ) *occ = 0;
+    return hipErrorInvalidValue;
+  } else {
+    if (!a) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, tv_fused_main<DT, GDT, G, SHARED>, kBlock, 0);
+    const int64_t grid = (int64_t)a->sgroups * a->sp.nchunks;
+    hipLaunchKernelGGL((tv_fused_main<DT, GDT, G, SHARED>), dim3((unsigned)grid), dim3(kBlock), 0, stream, *a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((tv_fused_finish<G, SHARED>), dim3((unsigned)((a->T + kFinishWaves - 1) / kFinishWaves)),
+                       dim3(64 * kFinishWaves), 0, stream, *a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(tv_fwd_mean, dim3(1), dim3(kBlock), 0, stream, *a);
+    return hipGetLastError();
+  }
+}
+
+template <int DT, int GDT, bool SHARED>
+static hipError_t fused_dispatch(int G, const TvArgs* a, hipStream_t stream, int* occ) {
+  switch (G) {
+    case 1: return fused_g<DT, GDT, SHARED, 1>(a, stream, occ);
+    case 2: return fused_g<DT, GDT, SHARED, 2>(a, stream, occ);
+    case 3: return fused_g<DT, GDT, SHARED, 3>(a, stream, occ);
+    case 4: return fused_g<DT, GDT, SHARED, 4>(a, stream, occ);
+  }
+  if (occ) *occ = 0;
+  return hipErrorInvalidValue;
+}
+
+static hipError_t fused_any(int dt, int gdt, bool shared, int G, const TvArgs* a, hipStream_t stream, int* occ) {
+  if (dt == kBF16) {
+    if (gdt == kBF16)
+      return shared ? fused_dispatch<kBF16, kBF16, true>(G, a, stream, occ)
+                    : fused_dispatch<kBF16, kBF16, false>(G, a, stream, occ);
+    return shared ? fused_dispatch<kBF16, kF32, true>(G, a, stream, occ)
+                  : fused_dispatch<kBF16, kF32, false>(G, a, stream, occ);
+  }
+  if (gdt == kBF16)
+    return shared ? fused_dispatch<kF32, kBF16, true>(G, a, stream, occ)
+                  : fused_dispatch<kF32, kBF16, false>(G, a, stream, occ);
+  return shared ? fused_dispatch<kF32, kF32, true>(G, a, stream, occ) : fused_dispatch<kF32, kF32, false>(G, a, stream, occ);
+}
+
+hipError_t tv_fused_occupancy(int dt, int grad_dt, int G, bool shared, int* blocks_per_cu) {
+  return fused_any(dt, grad_dt, shared, G, nullptr, nullptr, blocks_per_cu);
+}
+
+hipError_t launch_tv_fused(const TvArgs& a, int dt, bool shared, hipStream_t stream) {
+  return fused_any(dt, a.grad_dt, shared, a.G, &a, stream, nullptr);
 }
 
 template <int G>

@@ -232,6 +232,36 @@ def tv_loss_bwd(target, draft, saved, grad_loss, grad_dtype=None, out=None):
     return out
 
 
+def tv_loss_fwd_bwd(target, draft, grad_loss, grad_dtype=None, out=None):
+    """End-to-end TV loss forward and backward in one sweep (mtp_tv_loss_fwd_bwd),
+    with the upstream gradient grad_loss (float [1]) given up front.  Returns (loss
+    [1], pos_loss [T], saved [T, gamma, 4], grad [T, gamma, V] in grad_dtype,
+    default the draft's dtype)."""
+    lib = load()
+    _require_cuda(target, draft, grad_loss)
+    T, G, V, t_pos, t_head = _tv_layout(target, draft)
+    dev = draft.device
+    dt = _dtype_code(draft)
+    grad_dtype = grad_dtype or draft.dtype
+    if out is None:
+        out = torch.empty((T, G, V), dtype=grad_dtype, device=dev)
+    if out.stride(2) != 1 or tuple(out.shape) != (T, G, V):
+        raise ValueError("grad output must be [T, gamma, V] with unit stride along V")
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    pos_loss = torch.empty(T, dtype=torch.float32, device=dev)
+    saved = torch.empty((T, G, 4), dtype=torch.float32, device=dev)
+    grad_loss = grad_loss.reshape(1).to(torch.float32).contiguous()
+    nbytes = ctypes.c_size_t()
+    check(lib.mtp_tv_loss_fwd_bwd_workspace_size(T, G, V, dt, int(t_head == 0), ctypes.byref(nbytes)))
+    ws = workspace(dev, nbytes.value)
+    with torch.cuda.device(dev):
+        check(lib.mtp_tv_loss_fwd_bwd(_ptr(target), t_pos, t_head, _ptr(draft), draft.stride(0), draft.stride(1),
+                                      dt, T, G, V, _ptr(grad_loss), _ptr(loss), _ptr(pos_loss), _ptr(saved),
+                                      _ptr(out), out.stride(0), out.stride(1), _DTYPES[out.dtype],
+                                      _ptr(ws), ws.numel(), _stream(dev)))
+    return loss, pos_loss, saved, out
+
+
 class TVLoss(torch.autograd.Function):
     """L = mean_t -sum_k prod_{j<=k} alpha_{t,j}; gradient to the draft logits only
     (the target distribution is detached)."""
@@ -512,6 +542,11 @@ class TVPlan:
                               self.ws.numel(), s)
         self._bwd = common + (_ptr(self.saved), _ptr(self.grad_loss), _ptr(self.grad), self.grad.stride(0),
                               self.grad.stride(1), _DTYPES[self.grad.dtype], s)
+        check(self.lib.mtp_tv_loss_fwd_bwd_workspace_size(T, G, V, dt, int(t_head == 0), ctypes.byref(nbytes)))
+        self.ws_fused = workspace(dev, nbytes.value) if nbytes.value > self.ws.numel() else self.ws
+        self._fused = common + (_ptr(self.grad_loss), _ptr(self.loss), _ptr(self.pos_loss), _ptr(self.saved),
+                                _ptr(self.grad), self.grad.stride(0), self.grad.stride(1),
+                                _DTYPES[self.grad.dtype], _ptr(self.ws_fused), self.ws_fused.numel(), s)
 
     def forward(self):
         st = self.lib.mtp_tv_loss_fwd(*self._fwd)
@@ -521,6 +556,13 @@ class TVPlan:
 
     def backward(self):
         st = self.lib.mtp_tv_loss_bwd(*self._bwd)
+        if st:
+            check(st)
+        return self.grad
+
+    def fused(self):
+        """Forward and backward in one sweep (loss, saved statistics and gradient)."""
+        st = self.lib.mtp_tv_loss_fwd_bwd(*self._fused)
         if st:
             check(st)
         return self.grad
@@ -548,6 +590,11 @@ class TVTopKPlan:
                               self.ws.numel(), s)
         self._bwd = common + (_ptr(self.saved), _ptr(self.grad_loss), _ptr(self.grad), self.grad.stride(0),
                               self.grad.stride(1), _DTYPES[self.grad.dtype], s)
+        check(self.lib.mtp_tv_loss_fwd_bwd_workspace_size(T, G, V, dt, int(t_head == 0), ctypes.byref(nbytes)))
+        self.ws_fused = workspace(dev, nbytes.value) if nbytes.value > self.ws.numel() else self.ws
+        self._fused = common + (_ptr(self.grad_loss), _ptr(self.loss), _ptr(self.pos_loss), _ptr(self.saved),
+                                _ptr(self.grad), self.grad.stride(0), self.grad.stride(1),
+                                _DTYPES[self.grad.dtype], _ptr(self.ws_fused), self.ws_fused.numel(), s)
 
     def forward(self):
         st = self.lib.mtp_tv_topk_fwd(*self._fwd)
