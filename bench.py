@@ -10,7 +10,8 @@ accepted lengths and next tokens.
 
 Also reported (`tv_loss`): end-to-end TV loss forward + backward on T = 8192
 positions x 3 heads, V = 151936 (bf16 in, bf16 gradient out), as algorithmic GB/s
-against the 8 TB/s HBM peak; (`long_tail`) verify on 512 x 4 positions at V = 2^18
+against the 8 TB/s HBM peak, by the forward and backward calls and (`tv_fused`) by
+the one call that does both in one sweep; (`long_tail`) verify on 512 x 4 positions at V = 2^18
 with Zipf-like logits; (`entropy_sweep`) verify on the 15 temperature x noise cells
 (128 sequences each), with each cell's acceptance rate, mean accepted length and
 mean target entropy; (`target_only`) target-only verify of the rollout workload;
@@ -19,7 +20,10 @@ Gumbel-max draft sampler on the rollout's draft rows; (`tv_topk`) the TV loss
 forward + backward with top-K targets (K = 256) on the TV workload.
 
 `roofline` uses per-launch HIP events recorded on the stream the kernels run on;
-`cpu_baseline` times the float64 oracle on a bounded sample of the same workload.
+`cpu_baseline` times the float64 oracle on a bounded sample of the same workload
+(and of the TV, long-tail and entropy-sweep workloads in their lines); each
+entropy-sweep cell also reports the oracle's acceptance rate, mean accepted length
+and mean entropy on a seeded sample of its sequences beside the GPU's.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -34,6 +38,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "draft positions verified/sec at V=151936, γ=3; TV fwd+bwd GB/s vs HBM peak"
 HBM_PEAK_GBS = 8000.0
+C3_SAMPLE = 16   # sequences per entropy-sweep cell run through the oracle beside the GPU
 EXTRAS = ("tv_topk", "target_only", "gumbel", "long_tail", "entropy_sweep", "stream_context")
 
 
@@ -148,6 +153,35 @@ def time_verify(mtp, torch, w, steps, warmup, nsets, target_only=False, temperat
     return wall, kernel_ms, plans
 
 
+def time_tv_fused(mtp, torch, w, steps, warmup):
+    """mtp_tv_loss_fwd_bwd on the TV workload: per-call HIP events and the wall time
+    of the same calls back to back."""
+    import synthetic
+    t, d = synthetic.tv_inputs(w, "cuda:0")
+    plan = mtp.TVPlan(t, d, grad_dtype=torch.bfloat16)
+    for _ in range(warmup):
+        plan.fused()
+    torch.cuda.synchronize()
+    check_waits(mtp, plan.ws_fused)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        plan.fused()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        plan.fused()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    check_waits(mtp, plan.ws_fused)
+    ms = [a.elapsed_time(b) for a, b in ev]
+    loss = plan.loss.item()
+    del plan, t, d
+    torch.cuda.empty_cache()
+    return wall, ms, loss
+
+
 def time_tv(mtp, torch, w, steps, warmup, topk=None):
     import synthetic
     dev = "cuda:0"
@@ -181,38 +215,100 @@ def time_tv(mtp, torch, w, steps, warmup, topk=None):
     return wall, fwd, bwd, loss
 
 
-def cpu_baseline(torch, w, seconds):
-    """The float64 oracle, untuned, on whole sequences of the rollout workload until
-    about `seconds` of CPU time: draft positions per second on this host."""
+def _f64(torch, x):
+    """bf16 tensor on the GPU -> float64 NumPy array (exact)."""
     import numpy as np
 
+    from oracle.bf16 import bf16_bits_to_f64
+    return bf16_bits_to_f64(x.cpu().view(torch.int16).numpy().view(np.uint16))
+
+
+class _one_core:
+    """Pin this thread to a single CPU for a timed oracle loop."""
+
+    def __enter__(self):
+        self.old = os.sched_getaffinity(0) if hasattr(os, "sched_getaffinity") else None
+        if self.old:
+            os.sched_setaffinity(0, {min(self.old)})
+        return self
+
+    def __exit__(self, *exc):
+        if self.old:
+            os.sched_setaffinity(0, self.old)
+
+
+def cpu_baseline(torch, w, seconds, nseq=16):
+    """The float64 oracle, untuned, on whole sequences of a verify workload (the
+    first `nseq` sequences, cycled) until about `seconds` of CPU time: returns
+    (sequences done, wall seconds)."""
     import synthetic
     from oracle import mtp as omtp
-    from oracle.bf16 import bf16_bits_to_f64
-    t, d, y = synthetic.verify_inputs(w, "cuda:0", B=16)
-    tb = bf16_bits_to_f64(t.cpu().view(torch.int16).numpy().view(np.uint16))
-    db = bf16_bits_to_f64(d.cpu().view(torch.int16).numpy().view(np.uint16))
-    yb = y.cpu().numpy()
+    t, d, y = synthetic.verify_inputs(w, "cuda:0", B=nseq)
+    tb, db, yb = _f64(torch, t), _f64(torch, d), y.cpu().numpy()
     G1 = w["G"] + 1
-    # one core: this thread pinned to a single CPU for the timed loop
-    old = os.sched_getaffinity(0) if hasattr(os, "sched_getaffinity") else None
-    if old:
-        os.sched_setaffinity(0, {min(old)})
     n = 0
-    t0 = time.process_time()
-    w0 = time.perf_counter()
-    try:
+    with _one_core():
+        t0 = time.process_time()
+        w0 = time.perf_counter()
         while True:
             b = n % tb.shape[0]
             omtp.verify(tb[b:b + 1], db[b:b + 1], yb[b:b + 1], w["seed"], b * G1)
             n += 1
             if time.process_time() - t0 >= seconds:
                 break
-    finally:
         wall = time.perf_counter() - w0
-        if old:
-            os.sched_setaffinity(0, old)
     return n, wall
+
+
+def cpu_tv_baseline(torch, w, seconds):
+    """The float64 oracle, untuned, on the first positions of the TV workload, one
+    position at a time (statistics, position loss and gradient, with the gradient
+    scale of the full mean), until about `seconds` of CPU time: returns (positions
+    done, wall seconds)."""
+    import synthetic
+    from oracle import mtp as omtp
+    P = 64
+    t, d = synthetic.tv_inputs(w, "cuda:0", T=P)
+    tb, db = _f64(torch, t), _f64(torch, d)
+    scale = 1.0 / w["T"]
+    n = 0
+    with _one_core():
+        t0 = time.process_time()
+        w0 = time.perf_counter()
+        while True:
+            i = n % P
+            omtp.tv_loss(tb[i:i + 1], db[i:i + 1])
+            omtp.tv_loss_grad(tb[i:i + 1], db[i:i + 1], scale)
+            n += 1
+            if time.process_time() - t0 >= seconds:
+                break
+        wall = time.perf_counter() - w0
+    return n, wall
+
+
+def oracle_cell(torch, w, seqs):
+    """The oracle's acceptance rate, mean accepted length and mean target entropy
+    on the given sequences of a verify workload (its own seed, offsets b (gamma+1)),
+    and the wall seconds it took on one core."""
+    import numpy as np
+
+    import synthetic
+    from oracle import mtp as omtp
+    t, d, y = synthetic.verify_inputs(w, "cuda:0")
+    G1 = w["G"] + 1
+    acc, n, H = [], [], []
+    with _one_core():
+        w0 = time.perf_counter()
+        for b in seqs:
+            r = omtp.verify(_f64(torch, t[b:b + 1]), _f64(torch, d[b:b + 1]), y[b:b + 1].cpu().numpy(),
+                            w["seed"], b * G1)
+            acc.append(np.asarray(r["accept"], dtype=np.float64).ravel())
+            n.append(float(np.asarray(r["accepted_len"]).ravel()[0]))
+            H.append(np.asarray(r["entropy"], dtype=np.float64).ravel())
+        wall = time.perf_counter() - w0
+    del t, d, y
+    return {"accept_rate": float(np.concatenate(acc).mean()), "mean_accepted_len": float(np.mean(n)),
+            "mean_entropy": float(np.concatenate(H).mean())}, wall
 
 
 def stream_context(torch, nbytes=1 << 31, reps=10):
@@ -268,6 +364,8 @@ def main():
         sys.exit(2)
 
     import torch
+
+    import numpy as np
 
     import synthetic
     import tv_loss_amd as mtp
@@ -345,6 +443,44 @@ def main():
         log(f"tv loss: fwd {fm:.3f} ms ({fwd_bytes / fm / 1e6:.0f} GB/s), bwd {bm:.3f} ms "
             f"({bwd_bytes / bm / 1e6:.0f} GB/s), total {gbs:.0f} GB/s")
 
+        # forward and backward in one sweep (mtp_tv_loss_fwd_bwd): every logit read
+        # once, the gradient written once
+        fwall, fms, floss = time_tv_fused(mtp, torch, tw, tv_steps, max(1, min(3, args.warmup)))
+        fused_bytes = T * (1 + TG) * TV * 2 + T * TG * TV * 2
+        fmean = sum(fms) / len(fms)
+        fgbs = fused_bytes / (fmean * 1e-3) / 1e9
+        result["tv_fused"] = {
+            "workload": "e2e TV loss forward + backward in one call (mtp_tv_loss_fwd_bwd) on the tv_loss workload: "
+                        "T=8192 x gamma=3, V=151936, bf16 in, bf16 grad out",
+            "value": fgbs, "unit": "GB/s", "ms": fmean, "ms_two_calls": fm + bm,
+            "wall_ms_per_step": fwall / tv_steps * 1e3, "steps": tv_steps, "loss": floss,
+            "roofline": {"bound": "hbm", "achieved": fgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": fgbs / HBM_PEAK_GBS,
+                         "traffic": profiled_traffic("tv_fused_T8192x3_V151936_bf16.md", TV_SOURCES),
+                         "kernel": "tv_fused_main + tv_fused_finish + tv_fwd_mean",
+                         "valu_busy_pct": profiled_valu_busy(["void mtp::tv_fused_main<1, 1, 3, true>(mtp::TvArgs)"]),
+                         "bytes_per_launch": fused_bytes},
+        }
+        log(f"tv loss fused: {fmean:.3f} ms ({fgbs:.0f} GB/s of {fused_bytes / 1e9:.2f} GB) against "
+            f"{fm + bm:.3f} ms for the two calls")
+
+        if not args.no_cpu_baseline:
+            n, cwall = cpu_tv_baseline(torch, tw, args.cpu_seconds)
+            per_pos = (fwd_bytes + bwd_bytes) / T
+            est = cwall / n * T
+            result["tv_loss"]["cpu_baseline"] = {
+                "value": n * per_pos / cwall / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"the first {min(n, 64)} positions of the workload, cycled: {n} positions (forward "
+                          f"statistics, position loss and gradient) through the float64 NumPy oracle on one CPU "
+                          f"in {cwall:.1f} s; GB/s counts the two calls' bytes per position; extrapolated to "
+                          f"all {T} positions: {est:.0f} s per step",
+                "extrapolated_s_per_step": est}
+            result["tv_fused"]["cpu_baseline"] = dict(
+                result["tv_loss"]["cpu_baseline"], value=n * (fused_bytes / T) / cwall / 1e9,
+                sample=result["tv_loss"]["cpu_baseline"]["sample"].replace("the two calls' bytes",
+                                                                          "the one call's bytes"))
+            log(f"cpu oracle tv: {n} positions in {cwall:.1f} s, {est:.0f} s per full step extrapolated")
+
     if "tv_topk" in extras:
         # the top-K path on the same workload: each position's target reduced to its
         # 256 largest logits (indices + float32 values, shared by the heads)
@@ -387,8 +523,20 @@ def main():
                          "unit": "GB/s", "frac": alg_bytes / (omean * 1e-3) / 1e9 / HBM_PEAK_GBS,
                          "bytes_per_launch": alg_bytes},
         }
-        log(f"verify target-only: {omean * 1e3:.2f} us per call, accept rate {to_acc:.3f}, "
-            f"RS better on {rs_share:.3f} of positions")
+        # a low-temperature cell (tau = 0.25, sigma = 1), where p(yhat) is large and the
+        # draft far from the target: positions on both sides of the RS/TO boundary
+        lw = synthetic.sweep_cell(0, 2)
+        lwall, lkms, plans = time_verify(mtp, torch, lw, max(5, args.steps // 10), 2, 1, target_only=True)
+        out = plans[0].run(seed=lw["seed"], offset=0)
+        result["target_only"]["low_tau_cell"] = {
+            "workload": "target-only verify of the entropy-sweep cell tau=0.25, sigma=1.0 (128 sequences x "
+                        "gamma=3, V=151936, bf16)",
+            "accept_rate": out["accept"].float().mean().item(),
+            "rs_better_share": out["rs_better"].float().mean().item(),
+            "kernel_us_mean": sum(lkms) / len(lkms) * 1e3}
+        del plans, out
+        log(f"verify target-only at tau=0.25: accept rate {result['target_only']['low_tau_cell']['accept_rate']:.3f}, "
+            f"RS better on {result['target_only']['low_tau_cell']['rs_better_share']:.3f} of positions")
     if "gumbel" in extras:
         # rejection sampling at temperature 0.7 with Gumbel-max row samples, and the
         # Gumbel-max draft sampler on the rollout's draft rows
@@ -447,10 +595,18 @@ def main():
         }
         log(f"verify long tail: {lpos / lmean / 1e3:.3f} M positions/s, {lmean * 1e3:.1f} us per call, "
             f"{lbytes / lmean / 1e6:.0f} GB/s")
+        if not args.no_cpu_baseline:
+            n, cwall = cpu_baseline(torch, lw, args.cpu_seconds / 2, nseq=8)
+            result["long_tail"]["cpu_baseline"] = {
+                "value": n * lw["G"] / cwall, "unit": "draft positions/s", "cores": 1, "kind": "oracle",
+                "sample": f"the first 8 sequences of the workload, cycled: {n} sequences ({n * lw['G']} draft "
+                          f"positions) through the float64 NumPy oracle on one CPU in {cwall:.1f} s"}
+            log(f"cpu oracle long tail: {n * lw['G'] / cwall:.1f} positions/s")
 
     if "entropy_sweep" in extras:
         # the 15 cells of the entropy sweep
         cells = []
+        oracle_seqs, oracle_wall = 0, 0.0
         for it in range(len(synthetic.SWEEP_TAUS)):
             for isg in range(len(synthetic.SWEEP_SIGMAS)):
                 cw = synthetic.sweep_cell(it, isg)
@@ -459,11 +615,26 @@ def main():
                 acc = out["accept"].float().mean().item()
                 mean_n = out["accepted_len"].float().mean().item()
                 ent = out["entropy"].float().mean().item()
-                del plans, out
                 cm = sum(ckms) / len(ckms)
-                cells.append({"tau": synthetic.SWEEP_TAUS[it], "sigma": synthetic.SWEEP_SIGMAS[isg],
-                              "us_per_call": cm * 1e3, "positions_per_s": cw["B"] * cw["G"] / (cm * 1e-3),
-                              "accept_rate": acc, "mean_accepted_len": mean_n, "mean_entropy": ent})
+                cell = {"tau": synthetic.SWEEP_TAUS[it], "sigma": synthetic.SWEEP_SIGMAS[isg],
+                        "us_per_call": cm * 1e3, "positions_per_s": cw["B"] * cw["G"] / (cm * 1e-3),
+                        "accept_rate": acc, "mean_accepted_len": mean_n, "mean_entropy": ent}
+                if not args.no_cpu_baseline:
+                    # the same statistics on a seeded sample of sequences, from the GPU
+                    # call above and from the oracle
+                    seqs = sorted(np.random.default_rng(1000 + 10 * it + isg).choice(cw["B"], C3_SAMPLE,
+                                                                                    replace=False).tolist())
+                    ref, owall = oracle_cell(torch, cw, seqs)
+                    cell["sample"] = {
+                        "sequences": seqs,
+                        "gpu": {"accept_rate": out["accept"][seqs].float().mean().item(),
+                                "mean_accepted_len": out["accepted_len"][seqs].float().mean().item(),
+                                "mean_entropy": out["entropy"][seqs].float().mean().item()},
+                        "oracle": ref}
+                    oracle_seqs += len(seqs)
+                    oracle_wall += owall
+                del plans, out
+                cells.append(cell)
         torch.cuda.empty_cache()
         _, cbytes = verify_bytes(128, 3, 151936, 2)
         cmean = sum(c["us_per_call"] for c in cells) / len(cells)
@@ -476,6 +647,13 @@ def main():
                          "bytes_per_launch": cbytes},
             "cells": cells,
         }
+        if oracle_seqs:
+            result["entropy_sweep"]["cpu_baseline"] = {
+                "value": oracle_seqs * 3 / oracle_wall, "unit": "draft positions/s", "cores": 1, "kind": "oracle",
+                "sample": f"{C3_SAMPLE} seeded sequences of each cell ({oracle_seqs} sequences, "
+                          f"{oracle_seqs * 3} draft positions) through the float64 NumPy oracle on one CPU in "
+                          f"{oracle_wall:.1f} s; each cell's 'sample' holds the oracle's and the GPU's acceptance "
+                          f"rate, mean accepted length and mean entropy on them"}
         log(f"verify entropy sweep: {cmean:.1f} us per call on average over 15 cells")
 
     if not args.no_cpu_baseline:

@@ -87,10 +87,14 @@ def inverse_cdf(r, t):
 
 
 # READING (near-ties of the inverse CDF): a float32 evaluation carries rounding in
-# its cumulative sums, so where t lies within CDF_TIE_BAND * sum r of a boundary
-# C_v it may pick the token on the other side.  The band bounds that error; the
-# tokens it admits are listed exactly (cdf_allowed), so a flagged row still has
-# at most a few correct answers.
+# its cumulative sums, so where t lies within a band of a boundary C_v it may pick
+# the token on the other side.  Each residual entry max(0, p_v - q_v) is formed
+# from operands of size up to p_v, so the rounding of the cumulative sums is of the
+# order of 2^-24 times the p mass they span, however small the residual is: the
+# band is CDF_TIE_BAND * M, M = sum of p_v over the tokens with r_v > 0 (M = sum r
+# for a row sampled from p itself, or p without one token).  The tokens it admits
+# are listed exactly (cdf_allowed), so a flagged row still has at most a few
+# correct answers.
 CDF_TIE_BAND = 1e-6
 # READING: an acceptance decision whose |u - min(1, ratio)| is within this band may
 # go either way in a float evaluation of the ratio.
@@ -108,12 +112,30 @@ def cdf_allowed(r, t, band):
     return np.flatnonzero((r > 0) & (lo_edge <= t + band) & (c > t - band))
 
 
-def cdf_tie_probability(r, band_rel):
-    """Upper bound on the chance, over t uniform on [0, sum r), that cdf_allowed
-    admits more than one token: every boundary between two positive-mass tokens
-    flags an interval of width 2 band around it (union bound)."""
-    n_pos = int(np.count_nonzero(r > 0))
-    return min(1.0, 2.0 * band_rel * max(n_pos - 1, 0))
+def cdf_tie_probability(r, band):
+    """The chance, over t uniform on [0, sum r), that cdf_allowed(r, t, band)
+    admits more than one token: t lies within `band` (absolute) of a boundary
+    between two positive-mass tokens, i.e. in [b - band, b + band) for such a
+    boundary b.  The union of those windows is measured exactly: the boundaries
+    are sorted, so each window adds what lies beyond the end of the one before."""
+    r = np.asarray(r, dtype=np.float64)
+    c = np.cumsum(r)
+    total = float(c[-1]) if c.size else 0.0
+    pos = np.flatnonzero(r > 0)
+    if not total > 0 or pos.size < 2:
+        return 0.0
+    b = c[pos[:-1]]
+    lo = np.clip(b - band, 0.0, total)
+    hi = np.clip(b + band, 0.0, total)
+    prev_hi = np.concatenate(([0.0], hi[:-1]))
+    covered = float(np.sum(np.maximum(hi - np.maximum(lo, prev_hi), 0.0)))
+    return min(1.0, covered / total)
+
+
+def support_mass(p, r):
+    """M = sum of p_v over the tokens with r_v > 0: the size of the operands the
+    residual's entries on its support are formed from (see CDF_TIE_BAND)."""
+    return float(np.sum(np.where(np.asarray(r) > 0, p, 0.0)))
 
 
 def accept_decision(u, logp_y, logq_y):
@@ -138,7 +160,8 @@ def row_sample(p, q, u_prime, cdf_tie_band=CDF_TIE_BAND, identical=False):
     residual has no mass (p = q exactly) the row samples from p instead.
     t = u' * sum r; the token is inverse_cdf(r, t).
     Returns (token, residual_was_empty, allowed): `allowed` lists the tokens a
-    float32 evaluation may return (cdf_allowed with band cdf_tie_band * sum r).
+    float32 evaluation may return (cdf_allowed with band cdf_tie_band * M, M the
+    p mass on the support of r).
     READING: a residual whose mass is below cdf_tie_band is below what a float32
     sum resolves: such an evaluation may find it empty (and sample p) or form it
     from rounding noise, so every token with p > 0 is allowed there -- unless the
@@ -159,7 +182,7 @@ def row_sample(p, q, u_prime, cdf_tie_band=CDF_TIE_BAND, identical=False):
     total = float(np.cumsum(r)[-1])
     t = u_prime * total
     tok, _, _ = inverse_cdf(r, t)
-    allowed = cdf_allowed(r, t, cdf_tie_band * total)
+    allowed = cdf_allowed(r, t, cdf_tie_band * support_mass(p, r))
     if near_empty:
         allowed = np.flatnonzero(p > 0)
     assert tok in allowed
@@ -176,12 +199,13 @@ def _row_tie_bound(p, q, cdf_tie_band, identical=False):
     """cdf_tie_probability of the distribution a row samples (1 for a near-empty
     residual, whose row is always flagged)."""
     if q is None:
-        return cdf_tie_probability(p, cdf_tie_band)
+        return cdf_tie_probability(p, cdf_tie_band * support_mass(p, p))
     r = residual(p, q)
     mass = float(np.sum(r))
     if _near_empty(p, q, cdf_tie_band, identical):
         return 1.0
-    return cdf_tie_probability(r if mass > 0 else p, cdf_tie_band)
+    r = r if mass > 0 else p
+    return cdf_tie_probability(r, cdf_tie_band * support_mass(p, r))
 
 
 def _accept_tie_bound(ratio, tie_band):
@@ -337,7 +361,7 @@ def target_only_row_sample(p, yhat, u_prime, cdf_tie_band=CDF_TIE_BAND):
     total = float(np.cumsum(r)[-1])
     t = u_prime * total
     tok, _, _ = inverse_cdf(r, t)
-    allowed = cdf_allowed(r, t, cdf_tie_band * total)
+    allowed = cdf_allowed(r, t, cdf_tie_band * support_mass(p, r))
     if near_empty:
         allowed = np.flatnonzero(np.asarray(p) > 0)
     assert tok in allowed
@@ -418,7 +442,8 @@ def verify_target_only(target, draft, seed, offset, tie_band=ACCEPT_TIE_BAND, cd
             r = target_only_residual(p, yhat)
             mass = float(np.sum(r))
             out["near_empty"][b, k] = 0.0 < mass < cdf_tie_band
-            bound = 1.0 if out["near_empty"][b, k] else cdf_tie_probability(r if mass > 0 else p, cdf_tie_band)
+            rs = r if mass > 0 else p
+            bound = 1.0 if out["near_empty"][b, k] else cdf_tie_probability(rs, cdf_tie_band * support_mass(p, rs))
             _set_token(out, b, k, tok, allowed, bound)
         n = 0
         while n < G and out["accept"][b, n] == 1:

@@ -225,3 +225,16 @@ def test_autograd_wrapper():
     ref = mtp.tv_topk_bwd(i, v, d, saved, torch.tensor([2.5], device=DEV))
     torch.cuda.synchronize()
     assert torch.equal(z.grad, ref)
+
+
+def test_plan_matches_the_functional_calls():
+    w = dict(synthetic.TV_WORKLOADS["tv_loss"], T=16, V=20000)
+    i, v, d = synthetic.topk_inputs(w, 128, DEV, seed=3)
+    plan = mtp.TVTopKPlan(i, v, d, grad_dtype=torch.bfloat16)
+    loss, pos, saved = mtp.tv_topk_fwd(i, v, d)
+    g = mtp.tv_topk_bwd(i, v, d, saved, torch.ones(1, device=DEV), grad_dtype=torch.bfloat16)
+    plan.forward()
+    plan.backward()
+    torch.cuda.synchronize()
+    assert torch.equal(plan.saved, saved) and torch.equal(plan.loss, loss)
+    assert torch.equal(plan.grad, g)

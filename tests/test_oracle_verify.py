@@ -148,23 +148,51 @@ def test_cdf_allowed_is_the_set_of_perturbed_inverse_cdf_tokens():
             assert c[w] > t - band and (c[w - 1] if w else 0.0) <= t + band
 
 
-def test_cdf_tie_probability_bounds_the_flag_rate():
+def test_cdf_tie_probability_is_the_flag_rate():
     """Monte-Carlo over t uniform on [0, sum r): the share of t whose cdf_allowed has
-    more than one token is at most cdf_tie_probability, and equals it when every
-    interval is wider than two bands (the flagged bands around the boundaries do
-    not overlap)."""
+    more than one token equals cdf_tie_probability, for wide intervals (windows
+    apart), heavy-tailed ones (windows overlapping: most intervals are narrower
+    than a band) and zeros between positive tokens."""
     rng = np.random.default_rng(22)
-    for V, band_rel, wide in ((40, 2e-3, True), (40, 2e-3, False), (300, 1e-4, True)):
+    for V, band_rel, wide in ((40, 2e-3, True), (40, 2e-3, False), (300, 1e-4, True), (200, 5e-3, False)):
         r = rng.uniform(0.5, 1.5, V) if wide else np.exp(rng.normal(0, 3, V))
-        r[rng.integers(V)] = 0.0
-        bound = mtp.cdf_tie_probability(r, band_rel)
+        r[rng.integers(V, size=3)] = 0.0
+        band = band_rel * r.sum()
+        prob = mtp.cdf_tie_probability(r, band)
         n = 20000
         ts = rng.uniform(0, r.sum(), n)
-        hits = sum(mtp.cdf_allowed(r, t, band_rel * r.sum()).size > 1 for t in ts)
-        assert hits / n <= bound + 5 * np.sqrt(bound / n)
-        if wide:
-            assert abs(hits / n - bound) <= 5 * np.sqrt(bound / n)
+        hits = sum(mtp.cdf_allowed(r, t, band).size > 1 for t in ts)
+        assert abs(hits / n - prob) <= 5 * np.sqrt(prob * (1 - prob) / n) + 1e-4, (V, hits / n, prob)
     assert mtp.cdf_tie_probability(np.array([0.0, 1.0, 0.0]), 0.1) == 0.0
+
+
+def test_cdf_tie_probability_closed_forms():
+    """Four unit intervals (boundaries 1, 2, 3 on [0, 4)): windows of half-width
+    0.25 are apart, 3 x 0.5 / 4; of half-width 0.6 they merge into [0.4, 3.6),
+    3.2 / 4; of half-width 2 they cover everything.  Zeros between the tokens
+    change nothing."""
+    r = np.ones(4)
+    assert mtp.cdf_tie_probability(r, 0.25) == pytest.approx(0.375)
+    assert mtp.cdf_tie_probability(r, 0.6) == pytest.approx(0.8)
+    assert mtp.cdf_tie_probability(r, 2.0) == pytest.approx(1.0)
+    assert mtp.cdf_tie_probability(np.array([1.0, 0.0, 1.0, 0.0, 0.0, 1.0, 1.0]), 0.25) == pytest.approx(0.375)
+
+
+def test_cdf_band_scales_with_the_p_mass_of_the_support():
+    """The band of a residual row is CDF_TIE_BAND times the p mass on the
+    residual's support, not times the residual's own mass: r = (1e-3, 1e-3, 0)
+    from p = (0.3, 0.3, 0.4) has M = 0.6, a band of 6e-7 around the boundary at
+    1e-3, so t = 1e-3 + 4e-7 admits both tokens and t = 1e-3 + 8e-7 only the
+    second."""
+    p = np.array([0.3, 0.3, 0.4])
+    q = np.array([0.3 - 1e-3, 0.3 - 1e-3, 0.4 + 2e-3])
+    assert mtp.support_mass(p, mtp.residual(p, q)) == pytest.approx(0.6)
+    tok, empty, allowed = mtp.row_sample(p, q, (1e-3 + 4e-7) / 2e-3)
+    assert tok == 1 and not empty and list(allowed) == [0, 1]
+    tok, empty, allowed = mtp.row_sample(p, q, (1e-3 + 8e-7) / 2e-3)
+    assert tok == 1 and list(allowed) == [1]
+    tok, empty, allowed = mtp.row_sample(p, q, (1e-3 - 4e-7) / 2e-3)
+    assert tok == 0 and list(allowed) == [0, 1]
 
 
 def test_row_sample_allowed_sets():

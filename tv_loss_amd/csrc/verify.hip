@@ -221,7 +221,8 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
   __shared__ float4 held[2][NQ][kBlock];
   // double-buffered by layer parity: a wave may run one layer ahead of another
   __shared__ float part_sh[2][2][kWaves * 3];
-  __shared__ float lse_sh[2][2];
+  // row statistics (ref, z) of the item in pass 2, the normaliser being 2^ref z
+  __shared__ float2 st_sh[2][2];
   // target-only: per-wave argmax of the draft logits (pass 1), the row's argmax (pass 2)
   __shared__ float am_sh[2][kWaves];
   __shared__ uint32_t ai_sh[2][kWaves];
@@ -272,7 +273,7 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
         // a wait that timed out gives NaN statistics (and no greedy token), which
         // pass 2 turns into NaN partials: the finish reports such rows as failed
         const Lse st = poll_row(wpoll, rsrc_rec(g_m2), C, kSt, row, a.err, a.wait_limit);
-        if (lane == 0) lse_sh[i & 1][row] = lse_log2(st);
+        if (lane == 0) st_sh[i & 1][row] = make_float2(st.ref, st.z);
         if (TO && row == 1) {
           const uint32_t yh = poll_argmax(wpoll_am, rsrc_rec(g_m2), C, kSt, a.err, a.wait_limit);
           if (lane == 0) yhat_sh[i & 1] = yh;
@@ -281,22 +282,35 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
       }
       __syncthreads();
       // ---- pass 2 of item i - 2 ------------------------------------------------
-      // In this wave's e units p = sa e_p and q = sb e_q.  While rho = sb / sa is at
+      // In this wave's e units p = sa e_p and q = sb e_q, sa = 2^(href_p - ref_p) / z_p
+      // and sb likewise.  The difference of references is exact for every wave whose
+      // largest logit is near the row's (two floats within a factor of 2), so the
+      // ratio rho = sb / sa = 2^(dq - dp) z_p / z_q carries three roundings.  (Through
+      // the logarithms ref + log2 z instead, rho would inherit their rounding, about
+      // 2^-24 times their size: an error common to every element that the
+      // cancellation in p - q magnifies in the residual's shape.)  While rho is at
       // most 2^64, max(0, p - q) = sa max(0, e_p - rho e_q) (one fused multiply-add;
-      // e_p <= 1, so the max is the [0, 1] output clamp, free) and the
-      // overlap is the wave's p mass minus the residual, both summed in pass 1's
-      // order, so disjoint supports give an overlap of exactly 0.  A larger rho (q
-      // outweighs p here by more than 2^64) works in q's units instead.
-      const float la = href[0] - lse_sh[i & 1][0];   // log2 of sa (-inf: no p mass here)
-      const float sa = fast_exp2(la);
+      // e_p <= 1, so the max is the [0, 1] output clamp, free) and the overlap is the
+      // wave's p mass minus the residual, both summed in pass 1's order, so disjoint
+      // supports give an overlap of exactly 0.  A larger rho (q outweighs p here by
+      // more than 2^64) works in q's units instead.
+      const float2 sp = st_sh[i & 1][0];
+      const float dp = href[0] - sp.x;   // -inf: no p mass here
+      const float sa = fast_exp2(dp) / sp.y;
+      // log2 of sa for the Gumbel-max keys (whose comparisons within the row cancel
+      // the log2 z_p term) and the target-only test below
+      const float la = dp - fast_log2(sp.y);
       float rm = 0.f, om = 0.f;
       if (!pair2) {
         rm = sa * hz;
-      } else if (la != kNegInf) {
-        const float lr = href[1] - lse_sh[i & 1][1] - la;   // log2 of rho
+      } else if (dp != kNegInf) {
+        const float2 sq = st_sh[i & 1][1];
+        const float dq = href[1] - sq.x;
+        const float zr = sp.y / sq.y;                  // z_p / z_q
+        const float lr = dq - dp + fast_log2(zr);      // log2 of rho, for the range test
         float r0 = -0.f, r1 = -0.f;   // -0 + x = x: the first additions fold away
         if (!(lr > 64.f)) {
-          const float rho = fast_exp2(lr);
+          const float rho = fast_exp2(dq - dp) * zr;
 #pragma unroll
           for (int qi = 0; qi < NQ; ++qi) {
             const float4 ea = held[0][qi][t], eb = held[1][qi][t];
@@ -311,7 +325,7 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
           rm = sa * rw;
           om = sa * fmaxf(hz - rw, 0.f);
         } else {
-          const float rr = fast_exp2(-lr), sb = fast_exp2(href[1] - lse_sh[i & 1][1]);   // rr = 1 / rho
+          const float rr = fast_exp2(dp - dq) / zr, sb = fast_exp2(dq) / sq.y;   // rr = 1 / rho
           float o0 = -0.f, o1 = -0.f;
 #pragma unroll 1
           for (int qi = 0; qi < NQ; ++qi) {
@@ -330,8 +344,7 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
       }
       // statistics that are NaN (a timed-out wait, or a row without a finite
       // normaliser) make the partials NaN, whatever the sums above gave
-      const bool poison = !(lse_sh[i & 1][0] == lse_sh[i & 1][0]) ||
-                          (pair2 && !(lse_sh[i & 1][1] == lse_sh[i & 1][1])) ||
+      const bool poison = !(sp.y == sp.y) || (pair2 && !(st_sh[i & 1][1].y == st_sh[i & 1][1].y)) ||
                           (TO && pair2 && yhat_sh[i & 1] == kNoArgmax);
       if (poison) rm = om = __builtin_nanf("");
       if (lane == 0) a.part2[((int64_t)g_m2 * C + c) * kWaves + wave] = pack2(rm, om);
@@ -346,9 +359,13 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
         float lr = la;   // log2 of the residual's unit
         if (la != kNegInf) {
           const uint64_t crow = a.offset + (uint64_t)g_m2;
-          const float lb = href[1] - lse_sh[i & 1][1];
+          const float2 sq = st_sh[i & 1][1];
+          const float dq = href[1] - sq.x;
+          const float zr = sp.y / sq.y;                // z_p / z_q
+          const float lb = dq - fast_log2(sq.y);
           const bool p_units = !(lb - la > 64.f);
-          const float fq = p_units ? fast_exp2(lb - la) : 1.f, fp = p_units ? 1.f : fast_exp2(la - lb);
+          // rho = sb / sa as in the residual above
+          const float fq = p_units ? fast_exp2(dq - dp) * zr : 1.f, fp = p_units ? 1.f : fast_exp2(dp - dq) / zr;
           lr = p_units ? la : lb;
           // one 16-byte slot at a time: the Philox rounds would otherwise hold the
           // registers that the items in flight need
@@ -877,6 +894,7 @@ __global__ void verify_finish(VerifyArgs a) {
     token = m > kNegInf && idx < (uint32_t)a.V ? (int)idx : -1;
   }
   // the owner segment inside the owner chunk, then the inverse CDF in it
+  const float zr = pair ? st.p.z / st.q.z : 1.f, rzp = 1.f / st.p.z;
   auto sample_owner = [&]() -> int {
     const int oc = sc.owner;
     const int vpc = (int)a.sp.vec_per_chunk, nvec = (int)a.sp.nvec, nfull = (int)a.sp.nvec_full;
@@ -895,11 +913,14 @@ __global__ void verify_finish(VerifyArgs a) {
       for (int j = 0; j < NV; ++j)
 #pragma unroll
         for (int e = 0; e < PV; ++e) {
-          const float p = fast_exp2(__builtin_fmaf(x[0][j * PV + e], L, -lse2_p));
           if (use_q) {
-            const float q = fast_exp2(__builtin_fmaf(x[1][j * PV + e], L, -lse2_q));
-            v[j][e] = fmaxf(p - q, 0.f);
+            // in the row's units e = 2^(x L - ref): max(0, p - q) = max(0, e_p - zr e_q) / z_p,
+            // zr = z_p / z_q, the ratio pass 2 forms the residual with
+            const float ep = fast_exp2(__builtin_fmaf(x[0][j * PV + e], L, -st.p.ref));
+            const float eq = fast_exp2(__builtin_fmaf(x[1][j * PV + e], L, -st.q.ref));
+            v[j][e] = fmaxf(__builtin_fmaf(-zr, eq, ep), 0.f) * rzp;
           } else {
+            const float p = fast_exp2(__builtin_fmaf(x[0][j * PV + e], L, -lse2_p));
             v[j][e] = drop_y && (s0 + lane + j * 64) * PV + e == y ? 0.f : p;
           }
         }

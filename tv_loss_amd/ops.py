@@ -590,11 +590,6 @@ class TVTopKPlan:
                               self.ws.numel(), s)
         self._bwd = common + (_ptr(self.saved), _ptr(self.grad_loss), _ptr(self.grad), self.grad.stride(0),
                               self.grad.stride(1), _DTYPES[self.grad.dtype], s)
-        check(self.lib.mtp_tv_loss_fwd_bwd_workspace_size(T, G, V, dt, int(t_head == 0), ctypes.byref(nbytes)))
-        self.ws_fused = workspace(dev, nbytes.value) if nbytes.value > self.ws.numel() else self.ws
-        self._fused = common + (_ptr(self.grad_loss), _ptr(self.loss), _ptr(self.pos_loss), _ptr(self.saved),
-                                _ptr(self.grad), self.grad.stride(0), self.grad.stride(1),
-                                _DTYPES[self.grad.dtype], _ptr(self.ws_fused), self.ws_fused.numel(), s)
 
     def forward(self):
         st = self.lib.mtp_tv_topk_fwd(*self._fwd)
@@ -611,4 +606,4 @@ class TVTopKPlan:
 
 __all__ = ["verify", "verify_max_vocab", "verify_target_only", "verify_gumbel", "gumbel_sample", "tv_loss_fwd", "tv_loss_bwd",
            "tv_loss", "TVLoss", "tv_topk_fwd", "tv_topk_bwd", "tv_topk_loss", "TVTopKLoss", "MtpError",
-           "workspace", "workspace_error", "VerifyPlan", "TVPlan", "TVTopKPlan"]
+           "workspace", "workspace_error", "VerifyPlan", "TVPlan", "TVTopKPlan", "tv_loss_fwd_bwd", "set_wait_limit"]
