@@ -39,18 +39,23 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // also turns a NaN into 0)
 __device__ __forceinline__ float clamp01(float x) { return __builtin_amdgcn_fmed3f(x, 0.f, 1.f); }
 
-// The reference of a pass-1 partial: m L rounded up, i.e. the float m * L when the
-// product rounded up or was exact, else the next float above it.  Every logit x <= m
-// then has x L - ref <= 0 exactly in the fused multiply-add, so e = 2^(x L - ref) <= 1
-// (the pass-2 sums rely on it: their maxima are [0, 1] output clamps).  -inf and
-// NaN pass through (m * L).
+// The reference of a pass-1 partial: m L moved up past its rounding.  r = fl(m L)
+// lies within half a unit in the last place of the exact product, and
+// fl(r + |r| 2^-23) lies one or two units above r (toward +inf for either sign), so
+// every logit x <= m has x L - ref < 0 exactly in the fused multiply-add and
+// e = 2^(x L - ref) <= 1 (the pass-2 sums rely on it: their maxima are [0, 1] output
+// clamps).  Where |r| < 2^-103 the increment underflows and x L - ref is within a
+// subnormal of 0, whose exp2 is 1 in float32.  +-inf and NaN pass through.
 __device__ __forceinline__ float ref_up(float m, float L) {
   const float r = m * L;
-  if (!(__builtin_fmaf(m, L, -r) > 0.f)) return r;
-  const int b = __float_as_int(r);
-  return r > 0.f ? __int_as_float(b + 1) : r < 0.f ? __int_as_float(b - 1) : __int_as_float(1);
+  return __builtin_fmaf(__builtin_fabsf(r), 0x1p-23f, r);
 }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// The ratio z_a / z_b of two normalisers from the reciprocal rz_b = 1 / z_b (one
+// unit of rounding), and exactly 1 for equal normalisers, so that two rows of the
+// same logits get exactly the same units (p = q exactly there).
+__device__ __forceinline__ float z_ratio(float za, float zb, float rzb) { return za == zb ? 1.f : za * rzb; }
 
 // Geometry of one row split into `nchunks` chunks of whole 16-byte vectors.
 struct RowSplit {

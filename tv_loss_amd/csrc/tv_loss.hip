@@ -357,7 +357,7 @@ __global__ __launch_bounds__(kBlock, 2) void tv_pipe_main(TvArgs a) {
   __shared__ float4 held[NR][NQ][kBlock];      // e values of the position two layers back
   __shared__ float ref_sh[2][NR][kWaves];       // pass-1 wave references, by layer parity
   __shared__ float z_sh[2][NR][kBlock];         // pass-1 lane sums in their wave's units
-  __shared__ float lse_sh[2][NR];               // row log2-sum-exps of the position in pass 2
+  __shared__ float st_sh[2][NR][3];             // row normalisers 2^ref z of the position in pass 2: (ref, z, 1/z)
   __shared__ float red_sh[2 * G][kBlock];       // pass-2 lane partials (overlap, S per head)
 
   auto prefetch = [&](RawChunk<NV, NR>& rb, int t, bool live) {
@@ -391,7 +391,11 @@ __global__ __launch_bounds__(kBlock, 2) void tv_pipe_main(TvArgs a) {
         if (r < NR) {
           __builtin_amdgcn_s_setprio(3);
           const Lse st = poll_row(wpoll[j], rsrc_rec(t_m2), C, kSt, r, a.err, a.wait_limit);
-          if (lane == 0) lse_sh[par][r] = lse_log2(st);
+          if (lane == 0) {
+            st_sh[par][r][0] = st.ref;
+            st_sh[par][r][1] = st.z;
+            st_sh[par][r][2] = __builtin_amdgcn_rcpf(st.z);
+          }
           __builtin_amdgcn_s_setprio(0);
         }
       }
@@ -407,24 +411,31 @@ __global__ __launch_bounds__(kBlock, 2) void tv_pipe_main(TvArgs a) {
       // clamped: exactly 1 for every normal r (only a subnormal r, a difference
       // below 2^-126 of the wave's largest q, gives a fraction); a tie (r = 0)
       // counts as q <= p.  Four operations per element and head.  When p outweighs
-      // q here by more than 2^100 (rho would
-      // overflow) the same sums run in p's units: r' = max(0, rho' e_q - e_p), rho' =
-      // sb / sa, overlap = rho' zq - sum r', S = rho' (zq - sum_{r' > 0} e_q).
+      // q here by more than 2^100 the same sums run in p's units: r' = max(0, rho'
+      // e_q - e_p), rho' = sb / sa, overlap = rho' zq - sum r', S = rho' (zq -
+      // sum_{r' > 0} e_q).  The units come from the rows' normalisers 2^ref z:
+      // sa = 2^(href_p - ref_p) / z_p, sb likewise, so rho = 2^(dp - dq) z_q / z_p
+      // carries a few roundings of its own (the differences of references are exact
+      // for every wave near the row's largest logit), not those of the normalisers'
+      // logarithms, which the cancellation in min(p, q) would magnify.
       constexpr float kIndScale = 0x1p126f;
       float res[2 * G];
 #pragma unroll
       for (int k = 0; k < G; ++k) {
         const int rt = SHARED ? 0 : k, rq = NT + k;
-        const float la = href[rt] - lse_sh[par][rt];   // log2 sa (-inf: no p mass here)
-        const float lb = href[rq] - lse_sh[par][rq];   // log2 sb
+        const float* const stp = st_sh[par][rt];
+        const float* const stq = st_sh[par][rq];
+        const float dp = href[rt] - stp[0];            // -inf: no p mass here
+        const float dq = href[rq] - stq[0];            // -inf: no q mass here
         const float zq = z_sh[par][rq][tid];           // this lane's pass-1 sum of e_q
         // sums start at -0, so that the first addition folds away (-0 + x = x)
         float r0 = -0.f, r1 = -0.f, c0 = -0.f, c1 = -0.f;
         float ov, sv;
-        if (la == kNegInf || lb == kNegInf) {
+        const float rho_q = fast_exp2(dp - dq) * z_ratio(stq[1], stp[1], stp[2]);   // sa / sb; NaN for a bad row
+        if (dp == kNegInf || dq == kNegInf) {
           ov = sv = 0.f;                                 // one of p, q has no mass here
-        } else if (la - lb <= 100.f) {                   // q units
-          const float rho = fast_exp2(la - lb);
+        } else if (rho_q <= 0x1p100f) {                  // q units
+          const float rho = rho_q;
 #pragma unroll
           for (int qi = 0; qi < NQ; ++qi) {
             const float4 ep4 = held[rt][qi][tid], eq4 = held[rq][qi][tid];
@@ -437,11 +448,11 @@ __global__ __launch_bounds__(kBlock, 2) void tv_pipe_main(TvArgs a) {
               else { r0 += r; c0 = __builtin_fmaf(ind, eq[e], c0); }
             }
           }
-          const float sb = fast_exp2(lb);
+          const float sb = fast_exp2(dq) * stq[2];
           ov = sb * (zq - (r0 + r1));
           sv = sb * (zq - (c0 + c1));
-        } else if (la - lb > 100.f) {                    // p units (q is comparatively tiny)
-          const float rho = fast_exp2(lb - la);
+        } else if (rho_q > 0x1p100f) {                   // p units (q is comparatively tiny)
+          const float rho = fast_exp2(dq - dp) * z_ratio(stp[1], stq[1], stq[2]);
 #pragma unroll 1
           for (int qi = 0; qi < NQ; ++qi) {
             const float4 ep4 = held[rt][qi][tid], eq4 = held[rq][qi][tid];
@@ -454,7 +465,7 @@ __global__ __launch_bounds__(kBlock, 2) void tv_pipe_main(TvArgs a) {
               else { r0 += r; c0 = __builtin_fmaf(ind, eq[e], c0); }
             }
           }
-          const float sa = fast_exp2(la);
+          const float sa = fast_exp2(dp) * stp[2];
           ov = sa * (rho * zq - (r0 + r1));
           sv = sa * rho * (zq - (c0 + c1));
         } else {
@@ -862,7 +873,7 @@ __global__ __launch_bounds__(kBlock, 2) void tv_fused_main(TvArgs a) {
   __shared__ float4 held[NR][NQ][kBlock];      // e values of the position two layers back
   __shared__ float ref_sh[2][NR][kWaves];       // pass-1 wave references, by layer parity
   __shared__ float z_sh[2][NR][kBlock];         // pass-1 lane sums in their wave's units
-  __shared__ float lse_sh[NR];                  // row log2-sum-exps of the position in pass 2
+  __shared__ float st_sh[NR][3];                // row normalisers 2^ref z of the position in pass 2: (ref, z, 1/z)
   __shared__ float red_sh[2 * G][kBlock];       // pass-2 lane partials (overlap, S per head)
   __shared__ float tot_sh[2 * G];               // overlap and S totals of the gradient's position
 
@@ -908,7 +919,11 @@ __global__ __launch_bounds__(kBlock, 2) void tv_fused_main(TvArgs a) {
           const int r = wave + j * kWaves;
           if (r < NR) {
             const Lse st = poll_row(wpoll[j], rsrc_rec(t_2), C, kSt, r, a.err, a.wait_limit);
-            if (lane == 0) lse_sh[r] = lse_log2(st);
+            if (lane == 0) {
+              st_sh[r][0] = st.ref;
+              st_sh[r][1] = st.z;
+              st_sh[r][2] = __builtin_amdgcn_rcpf(st.z);
+            }
           }
         }
       }
@@ -936,7 +951,7 @@ __global__ __launch_bounds__(kBlock, 2) void tv_fused_main(TvArgs a) {
             if (j != k) prod *= al[j];
           wsum += prod;
         }
-        const float qs = gscale * wsum * fast_exp2(sbg[k]);   // w sb
+        const float qs = gscale * wsum * sbg[k];   // w sb
         const float cp = qs * (1.f - Sk[k]), cn = qs * Sk[k];
         float gv[NE];
 #pragma unroll
@@ -952,25 +967,28 @@ __global__ __launch_bounds__(kBlock, 2) void tv_fused_main(TvArgs a) {
 #pragma unroll
       for (int k = 0; k < G; ++k) {
         const int rt = SHARED ? 0 : k, rq = NT + k;
-        const float la = href[rt] - lse_sh[rt];   // log2 sa (-inf: no p mass here)
-        const float lb = href[rq] - lse_sh[rq];   // log2 sb
+        // units as in the single-read forward: sa = 2^(href_p - ref_p) / z_p, sb likewise
+        const float dp = href[rt] - st_sh[rt][0];        // -inf: no p mass here
+        const float dq = href[rq] - st_sh[rq][0];        // -inf: no q mass here
         const float zq = z_sh[i & 1][rq][tid];
         float r0 = -0.f, r1 = -0.f, c0 = -0.f, c1 = -0.f;
         float ov, svp;
-        sbg[k] = lb;
-        if (lb == kNegInf) {                             // no q mass here: no gradient
+        const float sb = fast_exp2(dq) * st_sh[rq][2];
+        const float rho_q = fast_exp2(dp - dq) * z_ratio(st_sh[rq][1], st_sh[rt][1], st_sh[rt][2]);   // sa / sb; NaN for a bad row
+        sbg[k] = sb;
+        if (dq == kNegInf) {                             // no q mass here: no gradient
           ov = svp = 0.f;
 #pragma unroll
           for (int e = 0; e < NE; ++e) sv[k][e] = 0.f;
-        } else if (la == kNegInf) {                      // no p mass: every q > p
+        } else if (dp == kNegInf) {                      // no p mass: every q > p
           ov = svp = 0.f;
 #pragma unroll
           for (int qi = 0; qi < NQ; ++qi) {
             const float4 eq4 = held[rq][qi][tid];
             sv[k][4 * qi] = -eq4.x; sv[k][4 * qi + 1] = -eq4.y; sv[k][4 * qi + 2] = -eq4.z; sv[k][4 * qi + 3] = -eq4.w;
           }
-        } else if (la - lb <= 100.f) {                   // q units
-          const float rho = fast_exp2(la - lb);
+        } else if (rho_q <= 0x1p100f) {                  // q units
+          const float rho = rho_q;
 #pragma unroll
           for (int qi = 0; qi < NQ; ++qi) {
             const float4 ep4 = held[rt][qi][tid], eq4 = held[rq][qi][tid];
@@ -984,11 +1002,10 @@ __global__ __launch_bounds__(kBlock, 2) void tv_fused_main(TvArgs a) {
               else { r0 += r; c0 = __builtin_fmaf(ind, eq[e], c0); }
             }
           }
-          const float sb = fast_exp2(lb);
           ov = sb * (zq - (r0 + r1));
           svp = sb * (zq - (c0 + c1));
-        } else if (la - lb > 100.f) {                    // p units (q is comparatively tiny)
-          const float rho = fast_exp2(lb - la);
+        } else if (rho_q > 0x1p100f) {                   // p units (q is comparatively tiny)
+          const float rho = fast_exp2(dq - dp) * z_ratio(st_sh[rt][1], st_sh[rq][1], st_sh[rq][2]);
 #pragma unroll
           for (int qi = 0; qi < NQ; ++qi) {
             const float4 ep4 = held[rt][qi][tid], eq4 = held[rq][qi][tid];
@@ -1002,7 +1019,7 @@ __global__ __launch_bounds__(kBlock, 2) void tv_fused_main(TvArgs a) {
               else { r0 += r; c0 = __builtin_fmaf(ind, eq[e], c0); }
             }
           }
-          const float sa = fast_exp2(la);
+          const float sa = fast_exp2(dp) * st_sh[rt][2];
           ov = sa * (rho * zq - (r0 + r1));
           svp = sa * rho * (zq - (c0 + c1));
         } else {

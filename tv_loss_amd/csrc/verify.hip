@@ -221,8 +221,8 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
   __shared__ float4 held[2][NQ][kBlock];
   // double-buffered by layer parity: a wave may run one layer ahead of another
   __shared__ float part_sh[2][2][kWaves * 3];
-  // row statistics (ref, z) of the item in pass 2, the normaliser being 2^ref z
-  __shared__ float2 st_sh[2][2];
+  // row statistics of the item in pass 2, the normaliser being 2^ref z: (ref, z, 1/z)
+  __shared__ float st_sh[2][2][3];
   // target-only: per-wave argmax of the draft logits (pass 1), the row's argmax (pass 2)
   __shared__ float am_sh[2][kWaves];
   __shared__ uint32_t ai_sh[2][kWaves];
@@ -273,7 +273,11 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
         // a wait that timed out gives NaN statistics (and no greedy token), which
         // pass 2 turns into NaN partials: the finish reports such rows as failed
         const Lse st = poll_row(wpoll, rsrc_rec(g_m2), C, kSt, row, a.err, a.wait_limit);
-        if (lane == 0) st_sh[i & 1][row] = make_float2(st.ref, st.z);
+        if (lane == 0) {
+          st_sh[i & 1][row][0] = st.ref;
+          st_sh[i & 1][row][1] = st.z;
+          st_sh[i & 1][row][2] = __builtin_amdgcn_rcpf(st.z);
+        }
         if (TO && row == 1) {
           const uint32_t yh = poll_argmax(wpoll_am, rsrc_rec(g_m2), C, kSt, a.err, a.wait_limit);
           if (lane == 0) yhat_sh[i & 1] = yh;
@@ -285,32 +289,32 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
       // In this wave's e units p = sa e_p and q = sb e_q, sa = 2^(href_p - ref_p) / z_p
       // and sb likewise.  The difference of references is exact for every wave whose
       // largest logit is near the row's (two floats within a factor of 2), so the
-      // ratio rho = sb / sa = 2^(dq - dp) z_p / z_q carries three roundings.  (Through
-      // the logarithms ref + log2 z instead, rho would inherit their rounding, about
-      // 2^-24 times their size: an error common to every element that the
-      // cancellation in p - q magnifies in the residual's shape.)  While rho is at
-      // most 2^64, max(0, p - q) = sa max(0, e_p - rho e_q) (one fused multiply-add;
-      // e_p <= 1, so the max is the [0, 1] output clamp, free) and the overlap is the
-      // wave's p mass minus the residual, both summed in pass 1's order, so disjoint
-      // supports give an overlap of exactly 0.  A larger rho (q outweighs p here by
-      // more than 2^64) works in q's units instead.
-      const float2 sp = st_sh[i & 1][0];
-      const float dp = href[0] - sp.x;   // -inf: no p mass here
-      const float sa = fast_exp2(dp) / sp.y;
+      // ratio rho = sb / sa = 2^(dq - dp) z_p / z_q carries a few roundings of its own
+      // (the reciprocal 1 / z_q to within one unit).  (Through the logarithms
+      // ref + log2 z instead, rho would inherit their rounding, about 2^-24 times
+      // their size: an error common to every element that the cancellation in p - q
+      // magnifies in the residual's shape.)  While rho is at most 2^64,
+      // max(0, p - q) = sa max(0, e_p - rho e_q) (one fused multiply-add; e_p <= 1,
+      // so the max is the [0, 1] output clamp, free) and the overlap is the wave's p
+      // mass minus the residual, both summed in pass 1's order, so disjoint supports
+      // give an overlap of exactly 0.  A larger rho (q outweighs p here by more than
+      // 2^64) works in q's units instead.
+      const float* const sp = st_sh[i & 1][0];
+      const float* const sq = st_sh[i & 1][1];
+      const float dp = href[0] - sp[0];   // -inf: no p mass here
+      const float sa = fast_exp2(dp) * sp[2];
       // log2 of sa for the Gumbel-max keys (whose comparisons within the row cancel
       // the log2 z_p term) and the target-only test below
-      const float la = dp - fast_log2(sp.y);
+      const float la = dp - fast_log2(sp[1]);
       float rm = 0.f, om = 0.f;
       if (!pair2) {
         rm = sa * hz;
       } else if (dp != kNegInf) {
-        const float2 sq = st_sh[i & 1][1];
-        const float dq = href[1] - sq.x;
-        const float zr = sp.y / sq.y;                  // z_p / z_q
-        const float lr = dq - dp + fast_log2(zr);      // log2 of rho, for the range test
+        const float dq = href[1] - sq[0];
+        const float zr = z_ratio(sp[1], sq[1], sq[2]);   // z_p / z_q
+        const float rho = fast_exp2(dq - dp) * zr;     // +inf past 2^128
         float r0 = -0.f, r1 = -0.f;   // -0 + x = x: the first additions fold away
-        if (!(lr > 64.f)) {
-          const float rho = fast_exp2(dq - dp) * zr;
+        if (!(rho > 0x1p64f)) {
 #pragma unroll
           for (int qi = 0; qi < NQ; ++qi) {
             const float4 ea = held[0][qi][t], eb = held[1][qi][t];
@@ -325,7 +329,7 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
           rm = sa * rw;
           om = sa * fmaxf(hz - rw, 0.f);
         } else {
-          const float rr = fast_exp2(dp - dq) / zr, sb = fast_exp2(dq) / sq.y;   // rr = 1 / rho
+          const float rr = fast_exp2(dp - dq) * z_ratio(sq[1], sp[1], sp[2]), sb = fast_exp2(dq) * sq[2];   // rr = 1 / rho
           float o0 = -0.f, o1 = -0.f;
 #pragma unroll 1
           for (int qi = 0; qi < NQ; ++qi) {
@@ -344,7 +348,7 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
       }
       // statistics that are NaN (a timed-out wait, or a row without a finite
       // normaliser) make the partials NaN, whatever the sums above gave
-      const bool poison = !(sp.y == sp.y) || (pair2 && !(st_sh[i & 1][1].y == st_sh[i & 1][1].y)) ||
+      const bool poison = !(sp[1] == sp[1]) || (pair2 && !(sq[1] == sq[1])) ||
                           (TO && pair2 && yhat_sh[i & 1] == kNoArgmax);
       if (poison) rm = om = __builtin_nanf("");
       if (lane == 0) a.part2[((int64_t)g_m2 * C + c) * kWaves + wave] = pack2(rm, om);
@@ -359,13 +363,12 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
         float lr = la;   // log2 of the residual's unit
         if (la != kNegInf) {
           const uint64_t crow = a.offset + (uint64_t)g_m2;
-          const float2 sq = st_sh[i & 1][1];
-          const float dq = href[1] - sq.x;
-          const float zr = sp.y / sq.y;                // z_p / z_q
-          const float lb = dq - fast_log2(sq.y);
+          const float dq = href[1] - sq[0];
+          const float lb = dq - fast_log2(sq[1]);
           const bool p_units = !(lb - la > 64.f);
           // rho = sb / sa as in the residual above
-          const float fq = p_units ? fast_exp2(dq - dp) * zr : 1.f, fp = p_units ? 1.f : fast_exp2(dp - dq) / zr;
+          const float fq = p_units ? fast_exp2(dq - dp) * z_ratio(sp[1], sq[1], sq[2]) : 1.f,
+                      fp = p_units ? 1.f : fast_exp2(dp - dq) * z_ratio(sq[1], sp[1], sp[2]);
           lr = p_units ? la : lb;
           // one 16-byte slot at a time: the Philox rounds would otherwise hold the
           // registers that the items in flight need
@@ -456,7 +459,8 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
       // segment path are derived there, not kept live across the loop
       int lim_l = lim, tail_l = tail, vend_l = vend, V_l = V;
       asm volatile("" : "+s"(lim_l), "+s"(tail_l), "+s"(vend_l), "+s"(V_l));
-      unpack_seg<DT, NV, 2>(rb, rows, v0, full, lim_l, tail_l, vend_l, V_l, x, 2);
+      // a bonus item's second row (its target row again) is loaded but not unpacked
+      unpack_seg<DT, NV, 2>(rb, rows, v0, full, lim_l, tail_l, vend_l, V_l, x, pair ? 2 : 1);
     }
     // the poll goes out before the prefetch, so that waiting for it (a layer
     // later) does not wait for the prefetch
@@ -894,7 +898,8 @@ __global__ void verify_finish(VerifyArgs a) {
     token = m > kNegInf && idx < (uint32_t)a.V ? (int)idx : -1;
   }
   // the owner segment inside the owner chunk, then the inverse CDF in it
-  const float zr = pair ? st.p.z / st.q.z : 1.f, rzp = 1.f / st.p.z;
+  const float zr = pair ? z_ratio(st.p.z, st.q.z, __builtin_amdgcn_rcpf(st.q.z)) : 1.f,
+              rzp = __builtin_amdgcn_rcpf(st.p.z);
   auto sample_owner = [&]() -> int {
     const int oc = sc.owner;
     const int vpc = (int)a.sp.vec_per_chunk, nvec = (int)a.sp.nvec, nfull = (int)a.sp.nvec_full;
