@@ -53,7 +53,11 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* Status and dtype codes are plain 32-bit integers (any value may be passed in:
+ * unknown dtype codes are rejected with MTP_ERR_DTYPE, unknown status codes have
+ * a status string), named by the constants below. */
+typedef int32_t mtp_status;
+enum {
   MTP_OK = 0,
   MTP_ERR_NULL = 1,       /* a required pointer is NULL                          */
   MTP_ERR_SHAPE = 2,      /* a size or stride is out of range                    */
@@ -62,9 +66,10 @@ typedef enum {
   MTP_ERR_WORKSPACE = 5,  /* workspace NULL, misaligned or smaller than required */
   MTP_ERR_DEVICE = 6,     /* a HIP device query failed                           */
   MTP_ERR_LAUNCH = 7      /* a kernel launch failed                              */
-} mtp_status;
+};
 
-typedef enum { MTP_F32 = 0, MTP_BF16 = 1 } mtp_dtype;
+typedef int32_t mtp_dtype;
+enum { MTP_F32 = 0, MTP_BF16 = 1 };
 
 /* row_status bits (per verify row) */
 #define MTP_ROW_BAD_TOKEN 1       /* draft token outside [0, V): counted as a rejection    */
@@ -372,6 +377,20 @@ mtp_status mtp_workspace_error(const void* workspace, uint32_t* host_word, void*
  * reporting described under Co-residency without stalling any kernel.  Returns
  * the previous bound. */
 uint64_t mtp_set_wait_limit(uint64_t ticks);
+
+/* Diagnostics: the number of 16-byte vectors per chunk of the persistent grids
+ * (the verify calls, the single-read TV forward and mtp_tv_loss_fwd_bwd), for the
+ * calls and workspace-size queries made after it is set (process-wide).  A chunk
+ * is one workgroup's share of a row; by default it is the workgroup's full reach
+ * (4096 bfloat16 or 3072 float32 logits for verify).  A smaller count, down to one
+ * vector, spreads a short row over many workgroups, so that their exchange of row
+ * statistics (records past the first 64 per row, many super-groups of few items,
+ * workgroups covering their chunk in part) runs at small vocabularies; results
+ * are the same up to rounding.  The co-residency bound applies to the chunk count,
+ * so the largest vocabulary shrinks with the chunk (mtp_verify_max_vocab reports
+ * it).  0 or a negative count restores the default.  Size workspaces after setting
+ * it.  Returns the previous count (0 for the default). */
+int32_t mtp_set_chunk_vectors(int32_t vectors);
 
 const char* mtp_status_string(mtp_status s);
 const char* mtp_last_error(void);

@@ -254,3 +254,22 @@ def test_python_binding_refuses_cpu_tensors():
     t = torch.zeros(1, 4, 16)
     with pytest.raises(ValueError):
         tv_loss_amd.verify(t, t[:, :3], torch.zeros(1, 3, dtype=torch.int32), 0)
+
+
+def test_chunk_vectors_hook_resizes_the_persistent_layouts():
+    """mtp_set_chunk_vectors returns the previous count and changes the chunking,
+    hence the workspace sizes, of the verify and single-read TV layouts; 0 or a
+    negative count restores the default."""
+    lib = tv_loss_amd.load()
+    n0, n1 = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.mtp_verify_workspace_size(4, 3, 20000, 1, ctypes.byref(n0)) == 0
+    try:
+        assert lib.mtp_set_chunk_vectors(3) == 0
+        assert lib.mtp_verify_workspace_size(4, 3, 20000, 1, ctypes.byref(n1)) == 0
+        # 2500 vectors: 834 chunks of 3 instead of 5 of 512; records and pass-2 words grow
+        assert n1.value > 100 * n0.value // 2
+        assert lib.mtp_set_chunk_vectors(-5) == 3
+        assert lib.mtp_verify_workspace_size(4, 3, 20000, 1, ctypes.byref(n1)) == 0
+        assert n1.value == n0.value
+    finally:
+        lib.mtp_set_chunk_vectors(0)

@@ -66,6 +66,7 @@ SIGNATURES = {
                                    _P]),
     "mtp_workspace_error": (_c.c_int, [_P, _c.POINTER(_c.c_uint32), _P]),
     "mtp_set_wait_limit": (_c.c_uint64, [_c.c_uint64]),
+    "mtp_set_chunk_vectors": (_c.c_int32, [_c.c_int32]),
     "mtp_status_string": (_c.c_char_p, [_c.c_int]),
     "mtp_last_error": (_c.c_char_p, []),
     "mtp_version": (_c.c_char_p, []),

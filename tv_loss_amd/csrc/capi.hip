@@ -19,6 +19,9 @@ thread_local char g_err[512] = "";
 
 // Ticks of the 100 MHz counter after which a bounded wait gives up (process-wide).
 std::atomic<uint64_t> g_wait_limit{mtp::kDefaultWaitLimitTicks};
+// Vectors per chunk of the persistent kernels (0: each kernel's own chunk of
+// kBlock x vectors-per-thread; process-wide, diagnostics only).
+std::atomic<int32_t> g_chunk_vectors{0};
 
 mtp_status fail(mtp_status s, const char* fmt, ...) {
   va_list ap;
@@ -106,6 +109,20 @@ mtp_status tv_fused_capacity(int dt, int gdt, int G, bool shared, int64_t* per_g
 }
 
 // ---- workspace layouts --------------------------------------------------------
+// The chunking of a persistent kernel (verify, single-read and fused TV): whole
+// chunks of kBlock * nv vectors, or fewer vectors per chunk under the diagnostic
+// cap, the kernels' workgroups then covering the chunk in part (lanes past its end
+// read nothing).
+mtp::RowSplit persistent_split(int64_t V, int pv, int nv) {
+  mtp::RowSplit sp = mtp::make_split(V, pv, nv, false);
+  const int32_t cap = g_chunk_vectors.load(std::memory_order_relaxed);
+  if (cap > 0 && cap < sp.vec_per_chunk) {
+    sp.vec_per_chunk = cap;
+    sp.nchunks = (int)((sp.nvec + cap - 1) / cap);
+  }
+  return sp;
+}
+
 struct VerifyLayout {
   size_t err, part1, part2, part3, gkeys, total;
   mtp::RowSplit sp;
@@ -114,7 +131,7 @@ struct VerifyLayout {
 
 VerifyLayout verify_layout(int32_t B, int32_t G, int32_t V, mtp_dtype dt, int mode) {
   VerifyLayout L{};
-  L.sp = mtp::make_split(V, per_vec(dt), mtp::verify_vec_per_thread(dt), false);
+  L.sp = persistent_split(V, per_vec(dt), mtp::verify_vec_per_thread(dt));
   L.ngroups = (int64_t)B * (G + 1);
   const int64_t C = L.sp.nchunks;
   size_t off = 0;
@@ -140,8 +157,8 @@ struct TvLayout {
 // forward's chunking.
 TvLayout tv_layout(int32_t T, int32_t G, int32_t V, mtp_dtype dt, bool shared, bool pipe) {
   TvLayout L{};
-  const int nv = pipe ? mtp::tv_pipe_vec_per_thread(dt, G, shared) : mtp::tv_fwd_vec_per_thread(dt, G, shared);
-  L.sp = mtp::make_split(V, per_vec(dt), nv, false);
+  L.sp = pipe ? persistent_split(V, per_vec(dt), mtp::tv_pipe_vec_per_thread(dt, G, shared))
+              : mtp::make_split(V, per_vec(dt), mtp::tv_fwd_vec_per_thread(dt, G, shared), false);
   const int64_t C = L.sp.nchunks;
   size_t off = 0;
   L.err = off; off = align256(off + 4);
@@ -173,7 +190,7 @@ struct FusedLayout {
 
 FusedLayout fused_layout(int32_t T, int32_t G, int32_t V, mtp_dtype dt, bool shared) {
   FusedLayout L{};
-  L.sp = mtp::make_split(V, per_vec(dt), mtp::tv_pipe_vec_per_thread(dt, G, shared), false);
+  L.sp = persistent_split(V, per_vec(dt), mtp::tv_pipe_vec_per_thread(dt, G, shared));
   const int64_t C = L.sp.nchunks;
   size_t off = 0;
   L.err = off; off = align256(off + 4);
@@ -261,6 +278,8 @@ const char* mtp_version(void) { return "libmtp 0.2 (gfx950)"; }
 
 uint64_t mtp_set_wait_limit(uint64_t ticks) { return g_wait_limit.exchange(ticks); }
 
+int32_t mtp_set_chunk_vectors(int32_t vectors) { return g_chunk_vectors.exchange(vectors > 0 ? vectors : 0); }
+
 mtp_status mtp_verify_workspace_size(int32_t batch, int32_t gamma, int32_t vocab, mtp_dtype dtype,
                                      size_t* bytes) {
   if (!bytes) return fail(MTP_ERR_NULL, "bytes is NULL");
@@ -291,8 +310,11 @@ mtp_status mtp_verify_max_vocab(mtp_dtype dtype, int32_t* vocab) {
     if (s) return s;
     cap = per_gpu < cap ? per_gpu : cap;
   }
-  // every chunk holds kBlock * vec_per_thread vectors; the last may be partial
-  const int64_t per_chunk = (int64_t)mtp::kBlock * mtp::verify_vec_per_thread(dtype) * per_vec(dtype);
+  // every chunk holds kBlock * vec_per_thread vectors (or the diagnostic cap); the
+  // last may be partial
+  const int32_t vcap = g_chunk_vectors.load(std::memory_order_relaxed);
+  const int64_t nat = (int64_t)mtp::kBlock * mtp::verify_vec_per_thread(dtype);
+  const int64_t per_chunk = (vcap > 0 && vcap < nat ? vcap : nat) * per_vec(dtype);
   const int64_t v = cap * per_chunk;
   *vocab = (int32_t)(v < kMaxVocab ? v : kMaxVocab);
   return ok();

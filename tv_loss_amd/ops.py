@@ -43,6 +43,15 @@ def workspace(device, nbytes):
     return ws
 
 
+def _grad_buffer(T, G, V, dtype, device):
+    """A [T, gamma, V] gradient whose rows start 16 bytes apart (the kernels store
+    whole 16-byte vectors): a view of a buffer padded past V when V is ragged."""
+    per = 16 // torch.empty((), dtype=dtype).element_size()
+    Vp = (V + per - 1) // per * per
+    buf = torch.empty((T, G, Vp), dtype=dtype, device=device)
+    return buf[..., :V] if Vp != V else buf
+
+
 def _require_cuda(*ts):
     for t in ts:
         if not t.is_cuda:
@@ -219,7 +228,7 @@ def tv_loss_bwd(target, draft, saved, grad_loss, grad_dtype=None, out=None):
     dt = _dtype_code(draft)
     grad_dtype = grad_dtype or draft.dtype
     if out is None:
-        out = torch.empty((T, G, V), dtype=grad_dtype, device=dev)
+        out = _grad_buffer(T, G, V, grad_dtype, dev)
     if out.stride(2) != 1 or tuple(out.shape) != (T, G, V):
         raise ValueError("grad output must be [T, gamma, V] with unit stride along V")
     gdt = _DTYPES[out.dtype]
@@ -244,7 +253,7 @@ def tv_loss_fwd_bwd(target, draft, grad_loss, grad_dtype=None, out=None):
     dt = _dtype_code(draft)
     grad_dtype = grad_dtype or draft.dtype
     if out is None:
-        out = torch.empty((T, G, V), dtype=grad_dtype, device=dev)
+        out = _grad_buffer(T, G, V, grad_dtype, dev)
     if out.stride(2) != 1 or tuple(out.shape) != (T, G, V):
         raise ValueError("grad output must be [T, gamma, V] with unit stride along V")
     loss = torch.empty(1, dtype=torch.float32, device=dev)
@@ -337,7 +346,7 @@ def tv_topk_bwd(target_idx, target_val, draft, saved, grad_loss, grad_dtype=None
     dt = _dtype_code(draft)
     grad_dtype = grad_dtype or draft.dtype
     if out is None:
-        out = torch.empty((T, G, V), dtype=grad_dtype, device=dev)
+        out = _grad_buffer(T, G, V, grad_dtype, dev)
     if out.stride(2) != 1 or tuple(out.shape) != (T, G, V):
         raise ValueError("grad output must be [T, gamma, V] with unit stride along V")
     gdt = _DTYPES[out.dtype]
@@ -382,6 +391,13 @@ def set_wait_limit(ticks):
     exchanged between workgroups, for calls launched afterwards (mtp_set_wait_limit);
     returns the previous bound.  0 makes such waits give up at once."""
     return int(load().mtp_set_wait_limit(ctypes.c_uint64(int(ticks))))
+
+
+def set_chunk_vectors(vectors):
+    """Diagnostics: 16-byte vectors per chunk of the persistent verify and TV grids
+    (mtp_set_chunk_vectors; 0 restores each kernel's own chunk).  Returns the
+    previous count."""
+    return int(load().mtp_set_chunk_vectors(int(vectors)))
 
 
 def _check_temperature(temperature):
@@ -532,7 +548,7 @@ class TVPlan:
         dt = _dtype_code(draft)
         self.loss, self.pos_loss, self.saved = tv_loss_fwd(target, draft)
         self.grad_loss = torch.ones(1, dtype=torch.float32, device=dev)
-        self.grad = torch.empty((T, G, V), dtype=grad_dtype or draft.dtype, device=dev)
+        self.grad = _grad_buffer(T, G, V, grad_dtype or draft.dtype, dev)
         nbytes = ctypes.c_size_t()
         check(self.lib.mtp_tv_loss_workspace_size(T, G, V, dt, int(t_head == 0), ctypes.byref(nbytes)))
         self.ws = workspace(dev, nbytes.value)
@@ -579,7 +595,7 @@ class TVTopKPlan:
         dt = _dtype_code(draft)
         self.loss, self.pos_loss, self.saved = tv_topk_fwd(target_idx, target_val, draft)
         self.grad_loss = torch.ones(1, dtype=torch.float32, device=dev)
-        self.grad = torch.empty((T, G, V), dtype=grad_dtype or draft.dtype, device=dev)
+        self.grad = _grad_buffer(T, G, V, grad_dtype or draft.dtype, dev)
         nbytes = ctypes.c_size_t()
         check(self.lib.mtp_tv_topk_workspace_size(T, G, V, dt, ctypes.byref(nbytes)))
         self.ws = workspace(dev, nbytes.value)
@@ -606,4 +622,5 @@ class TVTopKPlan:
 
 __all__ = ["verify", "verify_max_vocab", "verify_target_only", "verify_gumbel", "gumbel_sample", "tv_loss_fwd", "tv_loss_bwd",
            "tv_loss", "TVLoss", "tv_topk_fwd", "tv_topk_bwd", "tv_topk_loss", "TVTopKLoss", "MtpError",
-           "workspace", "workspace_error", "VerifyPlan", "TVPlan", "TVTopKPlan", "tv_loss_fwd_bwd", "set_wait_limit"]
+           "workspace", "workspace_error", "VerifyPlan", "TVPlan", "TVTopKPlan", "tv_loss_fwd_bwd", "set_wait_limit",
+           "set_chunk_vectors"]
