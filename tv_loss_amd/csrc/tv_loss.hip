@@ -779,9 +779,12 @@ __global__ __launch_bounds__(kBlock) void tv_bwd_kernel(TvArgs a) {
 //     its segment of every head from the values s_v it kept since pass 2;
 //   * pass 2 of position i - 2 (as in the forward) also keeps, per draft element,
 //     s_v = +e_q where q_v <= p_v and -e_q where q_v > p_v (e_q in the wave's q
-//     units sb): the gradient needs q_v = sb |s_v| and the indicator, the sign;
-//     the chunk's overlap and S partials (summed over the waves) are published
-//     at once as one self-announcing record per head;
+//     units sb): the gradient needs q_v = sb |s_v| and the indicator, the sign.
+//     The test is r > 0 for the residual r = max(0, e_q - rho e_p) (a compare
+//     and a select; a tie counts as q <= p), and S comes from the sum of the s
+//     values: S = sb (zq + sum s) / 2.  The chunk's overlap and S partials (summed
+//     over the waves) are published at once as one self-announcing record per
+//     head;
 //   * the e values of position i - 1 move to LDS, position i is unpacked, the
 //     record polls of positions i - 1 (normalisers) and i - 2 (overlap, S) and
 //     the loads of position i + 1 go out, pass 1 of position i and its records.
@@ -962,7 +965,6 @@ __global__ __launch_bounds__(kBlock, 2) void tv_fused_main(TvArgs a) {
     }
     // ---- pass 2 of position i - 2 ---------------------------------------------
     if (do2) {
-      constexpr float kIndScale = 0x1p126f;
       float res[2 * G];
 #pragma unroll
       for (int k = 0; k < G; ++k) {
@@ -996,14 +998,15 @@ __global__ __launch_bounds__(kBlock, 2) void tv_fused_main(TvArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const float r = clamp01(__builtin_fmaf(-rho, ep[e], eq[e]));
-              const float ind = clamp01(r * kIndScale);   // 1[q > p]
-              sv[k][4 * qi + e] = __builtin_fmaf(-2.f * ind, eq[e], eq[e]);
-              if (e & 1) { r1 += r; c1 = __builtin_fmaf(ind, eq[e], c1); }
-              else { r0 += r; c0 = __builtin_fmaf(ind, eq[e], c0); }
+              const float s = r > 0.f ? -eq[e] : eq[e];   // q > p: -e_q, else e_q
+              sv[k][4 * qi + e] = s;
+              if (e & 1) { r1 += r; c1 += s; }
+              else { r0 += r; c0 += s; }
             }
           }
+          // sum s = sum_{q <= p} e_q - sum_{q > p} e_q, so S = sb (zq + sum s) / 2
           ov = sb * (zq - (r0 + r1));
-          svp = sb * (zq - (c0 + c1));
+          svp = 0.5f * sb * (zq + (c0 + c1));
         } else if (rho_q > 0x1p100f) {                   // p units (q is comparatively tiny)
           const float rho = fast_exp2(dq - dp) * z_ratio(st_sh[rt][1], st_sh[rq][1], st_sh[rq][2]);
 #pragma unroll
@@ -1013,15 +1016,15 @@ __global__ __launch_bounds__(kBlock, 2) void tv_fused_main(TvArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const float r = clamp01(__builtin_fmaf(rho, eq[e], -ep[e]));
-              const float ind = clamp01(r * kIndScale);
-              sv[k][4 * qi + e] = __builtin_fmaf(-2.f * ind, eq[e], eq[e]);
-              if (e & 1) { r1 += r; c1 = __builtin_fmaf(ind, eq[e], c1); }
-              else { r0 += r; c0 = __builtin_fmaf(ind, eq[e], c0); }
+              const float s = r > 0.f ? -eq[e] : eq[e];
+              sv[k][4 * qi + e] = s;
+              if (e & 1) { r1 += r; c1 += s; }
+              else { r0 += r; c0 += s; }
             }
           }
           const float sa = fast_exp2(dp) * st_sh[rt][2];
           ov = sa * (rho * zq - (r0 + r1));
-          svp = sa * rho * (zq - (c0 + c1));
+          svp = 0.5f * sa * rho * (zq + (c0 + c1));
         } else {
           ov = svp = __builtin_nanf("");                 // a NaN statistic propagates
 #pragma unroll
