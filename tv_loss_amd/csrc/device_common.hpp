@@ -818,12 +818,13 @@ __device__ __forceinline__ P4 philox4x32_10(P4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     if (r) { k0 += W0; k1 += W1; }
-    // each 32 x 32 -> 64-bit product is one v_mad_u64_u32
+    // each 32 x 32 -> 64-bit product is one v_mad_u64_u32, each three-way
+    // exclusive or one v_bitop3_b32 (truth table 0x96: a ^ b ^ c)
     const uint64_t p0 = (uint64_t)M0 * c.x[0], p1 = (uint64_t)M1 * c.x[2];
     P4 n;
-    n.x[0] = (uint32_t)(p1 >> 32) ^ c.x[1] ^ k0;
+    n.x[0] = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c.x[1], k0, 0x96);
     n.x[1] = (uint32_t)p1;
-    n.x[2] = (uint32_t)(p0 >> 32) ^ c.x[3] ^ k1;
+    n.x[2] = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c.x[3], k1, 0x96);
     n.x[3] = (uint32_t)p0;
     c = n;
   }
@@ -845,22 +846,18 @@ __device__ __forceinline__ void row_uniforms(uint64_t seed, uint64_t offset, uin
 // base-2 units: E = -log2 U = -ln U / ln 2, U = (k + 1/2) 2^-24 with k = word >> 8
 // of Philox at counter (c, 1 + v4, 0), key = seed.  The Gumbel noise is -ln(-ln U),
 // so argmax_v (ln w_v + G_v) = argmax_v w_v / E_v = argmax_v (log2 w_v - log2 E_v)
-// (the exponential race).  E is formed from whichever of U and 1 - U is exact in
-// float32: U = (2k + 1) 2^-25 below 1/2; from 1/2 up, e = 1 - U = (2^25 - 2k - 1)
-// 2^-25 and -log2(1 - e) = -log2(y) e / (1 - y) with y = 1 - e rounded (the log1p
-// identity of Goldberg, "What every computer scientist should know about
-// floating-point arithmetic", Theorem 4; 1 - y is exact), or e / ln 2 when y rounds
-// to 1.  The smallest E (U near 1, the likely winners) thus keeps full relative
-// accuracy.
+// (the exponential race).  The smallest E (U near 1, the likely winners) keep their
+// relative accuracy: where e = 1 - U = (2^25 - 2k - 1) 2^-25 is below 2^-5 (exact in
+// float32 there), E comes from the series -log2(1 - e) = (e / ln 2)(1 + e/2 + e^2/3 +
+// e^3/4 + ...) cut after e^3/4 (relative error below e^4 / 5 < 2^-22); elsewhere
+// from log2 of U rounded to float32 (U has 25 significant bits above 1/2), an error
+// of at most 2^-24 / ln 2 in log2 U, below 2e-6 relative to E >= 0.045.
 __device__ __forceinline__ float expo_of_word(uint32_t w) {
-  const uint32_t k = w >> 8;
-  const bool low = k < (1u << 23);
-  const float e = (float)((1u << 25) - 2u * k - 1u) * 0x1p-25f;
-  const float y = 1.f - e;
-  const float z = low ? (float)(2u * k + 1u) * 0x1p-25f : y;
-  const float f = low ? 1.f : e * __builtin_amdgcn_rcpf(1.f - y);
-  const float E = -fast_log2(z) * f;
-  return !low && y == 1.f ? e * kLog2e : E;
+  const float kf = (float)(w >> 8);
+  const float e = __builtin_fmaf(-kf, 0x1p-24f, 1.f - 0x1p-25f);   // 1 - U, exact below 1/2
+  const float U = __builtin_fmaf(kf, 0x1p-24f, 0x1p-25f);          // exact below 1/2
+  const float s = __builtin_fmaf(e, __builtin_fmaf(e, __builtin_fmaf(e, 0.25f, 1.f / 3.f), 0.5f), 1.f);
+  return e < 0x1p-5f ? e * kLog2e * s : -fast_log2(U);
 }
 
 __device__ __forceinline__ void expo4(uint64_t seed, uint64_t c, uint32_t v4, float (&E)[4]) {
