@@ -1,6 +1,7 @@
 """The C-ABI calls under HIP graph capture: no call allocates, frees or issues a
-memset, so a captured verify (all three modes), sampler and TV-loss forward +
-backward replay to the eager results.  Every graph is replayed several times
+memset, so a captured verify (all three modes), sampler and TV-loss calls (forward,
+backward, the top-K pair and the fused forward + backward) replay to the eager
+results.  Every graph is replayed several times
 with eager calls of the same entry points (on the same workspace) and host
 synchronisations in between, and every replay is compared with the eager run."""
 import ctypes
@@ -110,7 +111,8 @@ def test_verify_modes_and_sampler_replay_to_the_eager_results():
     assert int(torch.count_nonzero(ws)) == 0
 
 
-def test_tv_loss_forward_backward_replay_to_the_eager_results():
+def test_tv_loss_calls_replay_to_the_eager_results():
+    """Forward, backward, the top-K pair and the fused call in one graph."""
     lib = mtp.load()
     w = dict(T=64, G=3, V=40000, dtype=torch.bfloat16, scale=1.2, sigma=0.3, shared=True, seed=11)
     t, d = synthetic.tv_inputs(w, DEV)
@@ -120,7 +122,9 @@ def test_tv_loss_forward_backward_replay_to_the_eager_results():
     n1, n2 = ctypes.c_size_t(), ctypes.c_size_t()
     _check(lib.mtp_tv_loss_workspace_size(T, G, V, dt, 1, ctypes.byref(n1)))
     _check(lib.mtp_tv_topk_workspace_size(T, G, V, dt, ctypes.byref(n2)))
-    ws = torch.zeros(max(n1.value, n2.value), dtype=torch.uint8, device=DEV)
+    n3 = ctypes.c_size_t()
+    _check(lib.mtp_tv_loss_fwd_bwd_workspace_size(T, G, V, dt, 1, ctypes.byref(n3)))
+    ws = torch.zeros(max(n1.value, n2.value, n3.value), dtype=torch.uint8, device=DEV)
     gl = torch.ones(1, device=DEV)
 
     def alloc():
@@ -128,7 +132,10 @@ def test_tv_loss_forward_backward_replay_to_the_eager_results():
                     saved=torch.empty((T, G, 4), device=DEV),
                     grad=torch.empty((T, G, V), dtype=torch.bfloat16, device=DEV),
                     kloss=torch.empty(1, device=DEV), ksaved=torch.empty((T, G, 4), device=DEV),
-                    kgrad=torch.empty((T, G, V), dtype=torch.float32, device=DEV))
+                    kgrad=torch.empty((T, G, V), dtype=torch.float32, device=DEV),
+                    floss=torch.empty(1, device=DEV), fpos=torch.empty(T, device=DEV),
+                    fsaved=torch.empty((T, G, 4), device=DEV),
+                    fgrad=torch.empty((T, G, V), dtype=torch.bfloat16, device=DEV))
 
     def calls(o, stream):
         s = P(stream.cuda_stream)
@@ -140,6 +147,9 @@ def test_tv_loss_forward_backward_replay_to_the_eager_results():
                                    T, G, V, _p(o["kloss"]), None, _p(o["ksaved"]), _p(ws), ws.numel(), s))
         _check(lib.mtp_tv_topk_bwd(_p(i), _p(v), i.stride(0), 0, i.shape[1], _p(d), d.stride(0), d.stride(1), dt,
                                    T, G, V, _p(o["ksaved"]), _p(gl), _p(o["kgrad"]), V * G, V, _lib.MTP_F32, s))
+        _check(lib.mtp_tv_loss_fwd_bwd(_p(t), t.stride(0), 0, _p(d), d.stride(0), d.stride(1), dt, T, G, V, _p(gl),
+                                       _p(o["floss"]), _p(o["fpos"]), _p(o["fsaved"]), _p(o["fgrad"]), V * G, V,
+                                       _lib.MTP_BF16, _p(ws), ws.numel(), s))
 
     side = torch.cuda.Stream()
     eager = alloc()
