@@ -305,8 +305,9 @@ mtp_status mtp_tv_loss_bwd(const void* target, int64_t target_pos_stride, int64_
  * the same g.  Each logit is read once and each gradient element written once;
  * the indicator of the gradient is the one S uses (on float32 probabilities), so
  * the saved statistics are exactly those the gradient was formed with.  Shapes
- * the one-sweep kernel does not take (more than 5 rows per position, gamma > 4, or
- * a vocabulary whose chunks cannot all be resident) run mtp_tv_loss_fwd then
+ * the one-sweep kernel does not take (more than 5 rows per position, gamma > 4, a
+ * vocabulary whose chunks cannot all be resident, or gamma = 1 with bfloat16
+ * logits and gradient, where the two calls are faster) run mtp_tv_loss_fwd then
  * mtp_tv_loss_bwd on the same workspace.  Arguments and limits as for those calls;
  * workspace: mtp_tv_loss_fwd_bwd_workspace_size bytes, zeroed once, left zeroed.
  */
