@@ -39,8 +39,9 @@ def _run(t, d, g, outs=None):
     loss, pos, saved, gb = mtp.tv_loss_fwd_bwd(t, d, gl, grad_dtype=torch.bfloat16, out=ob)
     loss2, pos2, saved2, gf = mtp.tv_loss_fwd_bwd(t, d, gl, grad_dtype=torch.float32, out=of)
     torch.cuda.synchronize()
-    # the float32-gradient call computed the same forward
-    assert torch.equal(torch.nan_to_num(saved), torch.nan_to_num(saved2))
+    # the float32-gradient call computed the same forward (bit for bit when both calls
+    # take the same path; gamma = 1 with bf16 logits and gradient takes the two calls)
+    assert torch.allclose(torch.nan_to_num(saved), torch.nan_to_num(saved2), rtol=1e-6, atol=1e-7)
     return loss, pos, saved, gb, gf
 
 
