@@ -502,10 +502,14 @@ def verify_gumbel(target, draft, tokens, seed, offset, temperature=1.0, tie_band
          temperature scales both the target and the cached draft logits.
       7. Row sample: r = max(0, p_k - q_k) (k < gamma) or p_gamma (bonus row); the
          token is gumbel_argmax(log r, U) with U = element_uniforms(seed, offset,
-         b*(gamma+1) + k, V); an empty residual samples p the same way (flagged).
+         b*(gamma+1) + k, V).  READING: the pages leave the empty residual open; a
+         row whose residual is empty samples p by the inverse CDF with its u'
+         (row_sample of p, flagged) -- any exact sample of p keeps the law; the
+         inverse CDF needs no key of p for rows that have a residual.
     Acceptance uses the same u as verify; token_allowed lists the tokens within the
     key gap band of the winner (every token with p > 0 for a residual below
-    cdf_tie_band, as in row_sample).  token_tie_bound is e^gap_band - 1 per row: in
+    cdf_tie_band, as in row_sample; the CDF near-ties for an empty residual's inverse
+    CDF).  token_tie_bound is e^gap_band - 1 per Gumbel-max row: in
     the exponential-race form of the trick the winner's clock T1 ~ Exp(sum w) and
     the runner-up arrives an independent Exp(sum w - w_win) later (memoryless
     clocks), so the chance that log T2 - log T1 < gap_band is at most
@@ -521,7 +525,6 @@ def verify_gumbel(target, draft, tokens, seed, offset, temperature=1.0, tie_band
             logp, _ = log_softmax(target[b, k])
             if logp is None:
                 continue
-            U = element_uniforms(seed, offset, b * G1 + k, V)
             p = np.exp(logp)
             near_empty = False
             w = p
@@ -532,13 +535,19 @@ def verify_gumbel(target, draft, tokens, seed, offset, temperature=1.0, tie_band
                 r = residual(p, np.exp(logq))
                 mass = float(np.sum(r))
                 near_empty = _near_empty(p, np.exp(logq), cdf_tie_band, bool(np.array_equal(target[b, k], draft[b, k])))
-                if mass > 0:
-                    w = r
-            with np.errstate(divide="ignore"):
-                tok, allowed = gumbel_argmax(np.log(w), U, gap_band)
+                w = r if mass > 0 else None
+            if w is None:      # empty residual: the inverse CDF of p with the row's u'
+                tok, _, allowed = row_sample(p, None, out["u_prime"][b, k], cdf_tie_band)
+                bound = _row_tie_bound(p, None, cdf_tie_band)
+            else:
+                U = element_uniforms(seed, offset, b * G1 + k, V)
+                with np.errstate(divide="ignore"):
+                    tok, allowed = gumbel_argmax(np.log(w), U, gap_band)
+                bound = float(np.expm1(gap_band))
             if near_empty:
                 allowed = np.flatnonzero(p > 0)
-            _set_token(out, b, k, tok, allowed, 1.0 if near_empty else float(np.expm1(gap_band)))
+                bound = 1.0
+            _set_token(out, b, k, tok, allowed, bound)
         n = out["accepted_len"][b]
         out["next_token"][b] = out["row_token"][b, n]
     return out

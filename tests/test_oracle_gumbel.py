@@ -7,7 +7,8 @@ oracle/philox.py), none of which re-types it:
 * the Gumbel-max trick samples w / sum w (paperlayer App. G.2): chi-square over
   independent rows; zero weights never win; ties go to the smallest index;
 * the tempered verify reduces to the plain verify of logits divided by T (accept
-  flags, overlap, TV, entropy), an empty residual samples p, and the first
+  flags, overlap, TV, entropy), an empty residual samples p by the inverse CDF
+  with the row's u' (numpy's searchsorted on SciPy's softmax), and the first
   emitted token of the full pipeline follows the tempered p (chi-square);
 * the Gumbel-max draft tokens follow the tempered q (chi-square).
 """
@@ -99,16 +100,24 @@ def test_tempered_verify_reduces_to_plain_verify_of_scaled_logits():
 
 
 def test_identical_rows_sample_p():
+    """An empty residual (the same logits on both sides) samples the tempered p by
+    the inverse CDF with the row's u' (the smallest v whose cumulative probability
+    exceeds u'); a bonus row takes the Gumbel-max of p."""
     rng = np.random.default_rng(9)
     B, G, V = 4, 2, 64
     tgt = rng.normal(0, 1, (B, G + 1, V))
     out = mtp.verify_gumbel(tgt, tgt[:, :G].copy(), np.zeros((B, G), int), seed=2, offset=0, temperature=0.8)
     assert np.all(out["row_status"][:, :G] & mtp.RESIDUAL_EMPTY)
+    _, up = verify_uniforms(2, 0, np.arange(B * (G + 1), dtype=np.uint64).reshape(B, G + 1))
     for b in range(B):
-        for k in range(G):
+        for k in range(G + 1):
             logp = special.log_softmax(tgt[b, k] / 0.8)
-            U = element_uniforms(2, 0, b * (G + 1) + k, V)
-            assert out["row_token"][b, k] == int(np.argmax(logp - np.log(-np.log(U))))
+            if k < G:
+                want = int(np.searchsorted(np.cumsum(np.exp(logp)), up[b, k], side="right"))
+            else:
+                U = element_uniforms(2, 0, b * (G + 1) + k, V)
+                want = int(np.argmax(logp - np.log(-np.log(U))))
+            assert out["row_token"][b, k] == want, (b, k)
 
 
 def test_first_emitted_token_follows_tempered_p():

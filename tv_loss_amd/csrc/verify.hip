@@ -42,6 +42,8 @@
 // acceptance flag needs p(y) and q(y) only.  The sequence's accepted length and
 // next token are formed in LDS.  It also clears what the main kernel wrote, so the
 // workspace is all zeros again when the call ends.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -354,10 +356,12 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
       if (lane == 0) a.part2[((int64_t)g_m2 * C + c) * kWaves + wave] = pack2(rm, om);
       if constexpr (GM) {
         // Gumbel-max keys of this wave's segment, key = w / E (the exponential race,
-        // E the element's exponential variate): w = the residual (pair rows) and w =
-        // p.  Each thread keeps its best of each as a (numerator, E) pair compared by
-        // cross-multiplication, in increasing index order (strict >, so the smaller
-        // index stays on equal keys); the wave then compares log2 keys.
+        // E the element's exponential variate): w = the residual for a pair row, w = p
+        // for a bonus row (a pair row whose residual turns out empty samples p by the
+        // inverse CDF in the finish instead).  Each thread keeps its best as a
+        // (numerator, E) pair compared by cross-multiplication, in increasing index
+        // order (strict >, so the smaller index stays on equal keys); the wave then
+        // compares log2 keys.
         float np = 0.f, ep = 1.f, nr = 0.f, er = 1.f;
         uint32_t ip = 0xffffffffu, ir = 0xffffffffu;
         float lr = la;   // log2 of the residual's unit
@@ -372,33 +376,41 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
           lr = p_units ? la : lb;
           // one 16-byte slot at a time: the Philox rounds would otherwise hold the
           // registers that the items in flight need
+          auto keys = [&](auto kind) __attribute__((always_inline)) {
+            constexpr int K = decltype(kind)::value;   // 0: p, 1: residual in p's units, 2: in q's
 #pragma unroll 1
-          for (int qi = 0; qi < NQ; ++qi) {
-            const float4 ea = held[0][qi][t];
-            const float va[4] = {ea.x, ea.y, ea.z, ea.w};
-            float vb[4] = {0.f, 0.f, 0.f, 0.f};
-            if (pair2) {
-              const float4 eb = held[1][qi][t];
-              vb[0] = eb.x; vb[1] = eb.y; vb[2] = eb.z; vb[3] = eb.w;
-            }
-            const uint32_t gi0 = (uint32_t)(v0 + (4 * qi / PV) * 64) * PV + (4 * qi) % PV;   // 4-aligned
-            float E[4];
-            expo4(a.seed, crow, gi0 >> 2, E);
+            for (int qi = 0; qi < NQ; ++qi) {
+              const float4 ea = held[0][qi][t];
+              const float va[4] = {ea.x, ea.y, ea.z, ea.w};
+              float vb[4] = {0.f, 0.f, 0.f, 0.f};
+              if constexpr (K > 0) {
+                const float4 eb = held[1][qi][t];
+                vb[0] = eb.x; vb[1] = eb.y; vb[2] = eb.z; vb[3] = eb.w;
+              }
+              const uint32_t gi0 = (uint32_t)(v0 + (4 * qi / PV) * 64) * PV + (4 * qi) % PV;   // 4-aligned
+              float E[4];
+              expo4(a.seed, crow, gi0 >> 2, E);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const bool tp = va[e] * ep > np * E[e];
-              np = tp ? va[e] : np;
-              ep = tp ? E[e] : ep;
-              ip = tp ? gi0 + e : ip;
-              if (pair2) {
-                const float d = clamp01(__builtin_fmaf(-fq, vb[e], fp * va[e]));   // <= fp va <= 1
-                const bool tr = d * er > nr * E[e];
-                nr = tr ? d : nr;
-                er = tr ? E[e] : er;
-                ir = tr ? gi0 + e : ir;
+              for (int e = 0; e < 4; ++e) {
+                if constexpr (K == 0) {
+                  const bool tp = va[e] * ep > np * E[e];
+                  np = tp ? va[e] : np;
+                  ep = tp ? E[e] : ep;
+                  ip = tp ? gi0 + e : ip;
+                } else {
+                  // <= fp va <= 1; fp = 1 in p's units
+                  const float d = clamp01(__builtin_fmaf(-fq, vb[e], K == 1 ? va[e] : fp * va[e]));
+                  const bool tr = d * er > nr * E[e];
+                  nr = tr ? d : nr;
+                  er = tr ? E[e] : er;
+                  ir = tr ? gi0 + e : ir;
+                }
               }
             }
-          }
+          };
+          if (!pair2) keys(std::integral_constant<int, 0>{});
+          else if (p_units) keys(std::integral_constant<int, 1>{});
+          else keys(std::integral_constant<int, 2>{});
         }
         float kp = np > 0.f ? la + fast_log2(np) - fast_log2(ep) : kNegInf;
         float kr = nr > 0.f ? lr + fast_log2(nr) - fast_log2(er) : kNegInf;
@@ -876,8 +888,9 @@ __global__ void verify_finish(VerifyArgs a) {
   // ---- owner segment inside the owner chunk, then the inverse CDF in it ------
   int token = -1;
   if (GM && !bad) {
-    // Gumbel-max: the largest key over the row's waves, of the residual unless it is
-    // empty (or no residual key is finite), else of p (a bonus row's keys are p's)
+    // Gumbel-max: the largest key over the row's waves, of the residual for a pair
+    // row (unless it is empty or no residual key is finite: then the inverse CDF of
+    // p below), of p for a bonus row
     const uint64_t* gk = a.gkeys + (int64_t)g * C * kWaves * 2;
     float m = kNegInf;
     uint32_t idx = 0xffffffffu;
@@ -894,8 +907,8 @@ __global__ void verify_finish(VerifyArgs a) {
       best(0);
       empty_res = !(m > kNegInf);
     }
-    if (!pair || empty_res) best(1);
-    token = m > kNegInf && idx < (uint32_t)a.V ? (int)idx : -1;
+    if (!pair) best(1);
+    token = !(pair && empty_res) && m > kNegInf && idx < (uint32_t)a.V ? (int)idx : -1;
   }
   // the owner segment inside the owner chunk, then the inverse CDF in it
   const float zr = pair ? z_ratio(st.p.z, st.q.z, __builtin_amdgcn_rcpf(st.q.z)) : 1.f,
@@ -965,6 +978,13 @@ __global__ void verify_finish(VerifyArgs a) {
     const int loc = wave_inverse_cdf<NV, PV>(v, tl - seg_start);
     return loc >= 0 ? (obeg + os * kSegVec) * PV + loc : -1;
   };
+  if (GM && !bad && pair && empty_res) {
+    // a Gumbel-max pair row whose residual is empty samples p by the inverse CDF
+    // with the row's u' (the main kernel forms p's keys for bonus rows only)
+    use_q = false;
+    sc = wave_scan_owner(C, up, pmass);
+    token = sample_owner();
+  }
   if (!bad && !GM) {
     token = sample_owner();
     if (token < 0 && use_q) {
