@@ -408,7 +408,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": profiled_traffic("verify_rollout_64x3_V151936_bf16.md", VERIFY_SOURCES),
-                     "kernel": "verify_main + verify_finish (one mtp_verify call)", "bytes_per_launch": alg_bytes,
+                     "kernel": "verify_main (one mtp_verify call: layers and finish in one launch)", "bytes_per_launch": alg_bytes,
                      "kernel_us_mean": kmean * 1e3, "kernel_us_median": ksorted[len(ksorted) // 2] * 1e3,
                      "kernel_us_p10": pct(kms, 0.1) * 1e3, "kernel_us_p90": pct(kms, 0.9) * 1e3,
                      "valu_busy_pct": profiled_valu_busy(["void mtp::verify_main<1, 2, 0>(mtp::VerifyArgs)"])},

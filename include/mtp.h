@@ -41,7 +41,11 @@
  *    affected rows report it -- verify rows get MTP_ROW_SYNC_TIMEOUT, NaN overlap
  *    and TV, token -1 and a rejection; TV-loss positions get NaN alpha, S and
  *    loss.  The call itself still returns MTP_OK (it has returned before the
- *    kernels run).
+ *    kernels run).  The verify calls finish each sequence in the same grid, in a
+ *    workgroup whose own share is done; its wait for the sequence's rows is bounded
+ *    by the larger of that limit and one second.  If that wait gives up (some
+ *    workgroup of the grid could not run for that long), workspace words written
+ *    after it may stay set: zero the workspace again before reusing it.
  */
 #ifndef MTP_H
 #define MTP_H

@@ -12,36 +12,36 @@
 // r = max(0, p - q) for k < gamma and r = p for the bonus row; the sequence emits
 // the sample of row n_b, n_b being the number of leading accepts.
 //
-// Two kernels.
-//
-// verify_main streams every logit once.  A "group" is one row of one sequence:
-// (target row, draft row) for k < gamma, or the bonus target row alone.  Each
-// group is split along the vocabulary into C chunks of 4096 elements (3072 for
-// fp32); C workgroups form a super-group that walks a list of groups ("layers"),
-// chunk c of every group going to workgroup c, and each wave of a workgroup owns a
-// contiguous segment of the chunk.  All super-groups are resident at once.  The two
-// passes over a chunk are software-pipelined across layers, so that no workgroup
-// waits on its cluster:
+// One kernel, verify_main.  It streams every logit once.  A "group" is one row of
+// one sequence: (target row, draft row) for k < gamma, or the bonus target row
+// alone.  Each group is split along the vocabulary into C chunks of 4096 elements
+// (3072 for fp32); C workgroups form a super-group that walks a list of groups
+// ("layers"), chunk c of every group going to workgroup c, and each wave of a
+// workgroup owns a contiguous segment of the chunk.  All super-groups are resident
+// at once.  The two passes over a chunk are software-pipelined across layers, so
+// that no workgroup waits on its cluster:
 //   layer i:  row statistics and pass 2 of group i - 2: its C records were polled
 //             a layer ago; merged in one fixed order they give the row
 //             log-sum-exps, and each wave sums r = p - min(p, q) and min(p, q)
 //             (p alone for a bonus row) over its segment from the e values held
-//             in LDS;
+//             in LDS, and publishes them as a self-announcing pass-2 word;
 //             group i - 1's e values move from registers to LDS;
 //             unpack the chunk of group i (its loads went out two layers ago),
 //             poll group i - 1's records and issue the loads of group i + 2;
 //             pass 1 on group i: per-wave log-sum-exp partials (both rows, plus
 //             the entropy moment of the target), combined over the workgroup and
 //             published as one self-announcing record.
-// Records use device-scope loads and stores, so a super-group may span XCDs.
+// Records and pass-2 words use device-scope loads and stores, so a super-group may
+// span XCDs.
 //
-// verify_finish runs one workgroup per sequence, one wave per row.  A wave merges
-// the row's records again (lse, entropy), scans the chunk masses, then the segment
-// masses of the owner chunk in vocabulary order, re-reads the single 1024-element
-// segment holding t = u' * sum r and finishes the inverse CDF in it.  The row's
-// acceptance flag needs p(y) and q(y) only.  The sequence's accepted length and
-// next token are formed in LDS.  It also clears what the main kernel wrote, so the
-// workspace is all zeros again when the call ends.
+// The finish runs in the same kernel: a workgroup whose layers are done takes a
+// sequence, one wave per row.  A wave waits for the row's records and merges them
+// (lse, entropy, the acceptance test, which needs p(y) and q(y) only), then waits
+// for its pass-2 words, scans the chunk masses, then the segment masses of the
+// owner chunk in vocabulary order, re-reads the single 1024-element segment
+// holding t = u' * sum r and finishes the inverse CDF in it.  The sequence's
+// accepted length and next token are formed in LDS.  It also clears what the
+// layers wrote for the row, so the workspace is all zeros again when the call ends.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -151,6 +151,15 @@ __device__ __forceinline__ uint32_t merge_argmax(__amdgpu_buffer_rsrc_t rs, int 
 }
 
 // ---------------------------------------------------------------------------
+template <int DT, int NV, int MODE>
+__device__ __forceinline__ void finish_row(const VerifyArgs& a, int b, int k, int* flag_sh, int* token_sh,
+                                           uint64_t limit);
+
+// The finish's waits are for the other workgroups' last layers (not for a record
+// of the exchange), so they are bounded by at least this many ticks of the 100 MHz
+// counter (one second), whatever the exchange's own bound.
+constexpr uint64_t kFinishWaitFloor = 100000000ull;
+
 template <int DT, int NV, int MODE>
 __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(VerifyArgs a) {
   constexpr bool TO = MODE == kVerifyTargetOnly, GM = MODE == kVerifyGumbel;
@@ -353,7 +362,8 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
       const bool poison = !(sp[1] == sp[1]) || (pair2 && !(sq[1] == sq[1])) ||
                           (TO && pair2 && yhat_sh[i & 1] == kNoArgmax);
       if (poison) rm = om = __builtin_nanf("");
-      if (lane == 0) a.part2[((int64_t)g_m2 * C + c) * kWaves + wave] = pack2(rm, om);
+      // (om >= 0 or NaN carries the sign bit as a marker: a published word is non-zero)
+      if (lane == 0) put_word(a.part2 + ((int64_t)g_m2 * C + c) * kWaves + wave, pack2(rm, mark(om)));
       if constexpr (GM) {
         // Gumbel-max keys of this wave's segment, key = w / E (the exponential race,
         // E the element's exponential variate): w = the residual for a pair row, w = p
@@ -418,8 +428,8 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
         if (pair2) wave_argmax(kr, ir);
         if (lane == 0) {
           uint64_t* gk = a.gkeys + (((int64_t)g_m2 * C + c) * kWaves + wave) * 2;
-          gk[0] = pack_argmax(kr, ir);
-          gk[1] = pack_argmax(kp, ip);
+          put_word(gk, pack_argmax(kr, ir));
+          put_word(gk + 1, pack_argmax(kp, ip));
         }
       }
       if constexpr (TO) {
@@ -445,7 +455,7 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
             }
             pex = sa * wave_total(m0 + m1);
           }
-          if (lane == 0) a.part3[((int64_t)g_m2 * C + c) * kWaves + wave] = pex;
+          if (lane == 0) st_coherent(a.part3 + ((int64_t)g_m2 * C + c) * kWaves + wave, mark(pex));
         }
       }
     }
@@ -566,10 +576,31 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
     layer(i, rawA);
     layer(i + 1, rawB);
   }
+
+  // ---- the finish: the workgroup j places from the end of the grid (j = S C - 1 -
+  // blockIdx.x), its layers done, finishes sequences j, j + S C, ...: wave w takes
+  // rows w, w + kWaves, ... of the sequence, then thread 0 forms the accepted length
+  // and the next token.  With the item split above the last super-groups have the
+  // fewest items and end first, so their workgroups merge a sequence's records
+  // while the other super-groups still run, and wait only for its pass-2 words.
+  __shared__ int flag_sh[kMaxRowsPerSeq], token_sh[kMaxRowsPerSeq];
+  const uint64_t flimit = a.wait_limit > kFinishWaitFloor ? a.wait_limit : kFinishWaitFloor;
+  for (int b = S * C - 1 - slot; b < B; b += S * C) {
+    for (int k = wave; k < G1; k += kWaves) finish_row<DT, NV, MODE>(a, b, k, flag_sh, token_sh, flimit);
+    __syncthreads();
+    if (t == 0) {
+      int n = 0;
+      while (n < G && flag_sh[n] == 1) ++n;
+      a.accepted_len[b] = n;
+      a.next_token[b] = token_sh[n];
+    }
+    __syncthreads();
+  }
 }
 
 // ---------------------------------------------------------------------------
-// verify_finish: one workgroup per sequence, wave k handles row (b, k).
+// The finish of a sequence: the main kernel's workgroups run it once their layers
+// are done, one wave per row.
 
 // The cumulative sums of the inverse CDF run in float64 (chunk, segment and
 // element prefixes alike): their rounding then stays far below that of the float32
@@ -621,29 +652,42 @@ __device__ __forceinline__ double log2_split(float z) {
 // Inverse CDF of one wave segment (NV blocks of 64 vectors, PV values per lane per
 // block, vocabulary order block-major then lane-major): the index (within the
 // segment) of the first value whose running mass exceeds t; if none, the last
-// index with positive mass; -1 if the segment has no mass.
+// index with positive mass; -1 if the segment has no mass.  The running masses are
+// float64 sums: each lane's prefixes of its PV values (a tree, log2 PV deep), the
+// wave's exclusive prefix of the lane totals, and the blocks before; the blocks'
+// wave scans are independent of each other.
 template <int NV, int PV>
 __device__ __forceinline__ int wave_inverse_cdf(const float (&v)[NV][PV], double t) {
   const int lane = threadIdx.x & 63;
+  double pre[NV][PV], incl[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+#pragma unroll
+    for (int e = 0; e < PV; ++e) pre[j][e] = (double)v[j][e];
+    // in place, highest index first, so each step reads the previous step's values
+#pragma unroll
+    for (int d = 1; d < PV; d *= 2)
+#pragma unroll
+      for (int e = PV - 1; e >= d; --e) pre[j][e] += pre[j][e - d];
+  }
+#pragma unroll
+  for (int j = 0; j < NV; ++j) incl[j] = wave_incl_sum_f64(pre[j][PV - 1]);
   double base = 0.0;
   int best = 0x7fffffff, lastpos = -1;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    double s = 0.0;
+    const double cum0 = base + lane_before(incl[j]);
+    // the running masses only grow, so the lane's first crossing is the smallest
+    // index that crosses: scanned downwards, the last one found
+    int bj = 0x7fffffff;
 #pragma unroll
-    for (int e = 0; e < PV; ++e) s += (double)v[j][e];
-    const double incl = wave_incl_sum_f64(s);
-    double cum = base + lane_before(incl);
+    for (int e = PV - 1; e >= 0; --e)
+      if (v[j][e] > 0.f && cum0 + pre[j][e] > t) bj = (j * 64 + lane) * PV + e;
+    best = min(best, bj);
 #pragma unroll
-    for (int e = 0; e < PV; ++e) {
-      if (v[j][e] > 0.f) {
-        cum += (double)v[j][e];
-        const int idx = (j * 64 + lane) * PV + e;
-        if (best == 0x7fffffff && cum > t) best = idx;
-        lastpos = idx;
-      }
-    }
-    base += readlane_d(incl, 63);
+    for (int e = 0; e < PV; ++e)
+      if (v[j][e] > 0.f) lastpos = (j * 64 + lane) * PV + e;
+    base += readlane_d(incl[j], 63);
   }
   best = (int)wave_min_u32((uint32_t)best);
   lastpos = (int)wave_max_u32((uint32_t)(lastpos + 1)) - 1;
@@ -699,21 +743,26 @@ __device__ __forceinline__ Scan wave_scan_owner(int n, float u_prime, MassFn mas
   return r;
 }
 
+// Row (b, k) of the finish, by one wave (k wave-uniform, so the record descriptor
+// built from it is scalar).  It first waits until every word the row needs is
+// published: the pass-2 words of all its chunks and waves (written last, each after
+// its workgroup had polled the row's records), the records themselves, and the
+// Gumbel-max keys or the masses without the greedy token.  The wait is bounded by
+// `limit` ticks; one that gives up sets the error word and reports the row as timed
+// out.  Writes the row's outputs and its acceptance flag and token to flag_sh[k],
+// token_sh[k].
 template <int DT, int NV, int MODE>
-__global__ void verify_finish(VerifyArgs a) {
+__device__ __forceinline__ void finish_row(const VerifyArgs& a, int b, int k, int* flag_sh, int* token_sh,
+                                           uint64_t limit) {
   constexpr bool TO = MODE == kVerifyTargetOnly, GM = MODE == kVerifyGumbel;
   constexpr int PV = Elem<DT>::kPerVec;
   constexpr int kSegVec = NV * 64;
   constexpr int KC = 2;   // chunks per lane whose pass-2 words are kept in registers
   const int C = a.sp.nchunks;
   const int G = a.G, G1 = G + 1;
-  const int b = blockIdx.x;
-  // the row index is wave-uniform: kept in a scalar register, so the record
-  // descriptor built from it is scalar too
-  const int k = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63;
   const int g = b * G1 + k;
   const bool pair = k < G;
-  __shared__ int flag_sh[kMaxRowsPerSeq], token_sh[kMaxRowsPerSeq];
 
   const char* trow = reinterpret_cast<const char*>(a.target) + (int64_t)g * a.t_stride * Elem<DT>::kBytes;
   const char* drow = reinterpret_cast<const char*>(a.draft) + (int64_t)(b * G + (pair ? k : 0)) * a.d_stride * Elem<DT>::kBytes;
@@ -725,7 +774,6 @@ __global__ void verify_finish(VerifyArgs a) {
   float* p3 = TO ? a.part3 + (int64_t)g * C * kWaves : nullptr;
   const bool to_pair = TO && pair;
 
-  // ---- everything that does not depend on the row statistics goes out first ----
   // lane l owns chunks [l K, l K + K); the pass-2 words of its first KC are kept
   const int K = (C + 63) / 64;
   const int c0 = lane * K, c1 = min(C, c0 + K);
@@ -734,34 +782,112 @@ __global__ void verify_finish(VerifyArgs a) {
   for (int i = 0; i < KC; ++i)
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) seg[i][w] = 0.f;
-  // the given draft token's load goes out first, then the record words and the
-  // pass-2 words, then the loads of the token's two logits, so that the round trips
-  // overlap (all loads are unconditional, at clamped addresses, so none waits for
-  // another)
+  // the given draft token and its two logits do not depend on the other
+  // workgroups: their loads go out before the wait
   int y = 0;
-  if constexpr (!TO) y = a.tokens[b * G + min(k, G - 1)];
-  const RecWords rw = rec_words(rs, C, kSt);
-  uint64_t pw[KC][kWaves];
-#pragma unroll
-  for (int i = 0; i < KC; ++i)
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) pw[i][w] = p2[(int64_t)min(c0 + i, C - 1) * kWaves + w];
   bool y_ok = false;
   float ay = 0.f, by = 0.f;
   if constexpr (!TO) {
+    y = a.tokens[b * G + min(k, G - 1)];
     y_ok = pair && y >= 0 && y < a.V;
     const int yc = y_ok ? y : 0;
     ay = load_one<DT>(trow, yc);
     by = load_one<DT>(drow, yc);
   }
+  float u, up;
+  row_uniforms(a.seed, a.offset, (uint64_t)g, &u, &up);
+
+  // A bounded wait: `test` loads words and tells whether this lane's are all
+  // published; a timeout sets the error word and returns true.
+  auto wait_words = [&](auto&& test) -> bool {
+    uint64_t t0 = 0;
+    for (;;) {
+      const bool ready = test();
+      if (__ballot(!ready) == 0ull) return false;
+      const uint64_t now = __builtin_amdgcn_s_memrealtime();
+      if (t0 == 0) t0 = now;
+      if (now - t0 > limit) {
+        if (lane == 0) __hip_atomic_fetch_or(a.err, kErrSyncTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return true;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  };
+
+  // ---- phase 1: the records, complete some two layers before the pass-2 words:
+  // the row statistics and the acceptance test's log ratio ----------------------
+  RecWords rw;
+  const bool wto_rec = wait_words([&]() {
+    rw = rec_words(rs, C, kSt);   // record `lane`'s words, kept
+    bool ready = lane >= C || (rw.w0 != 0ull && rw.w1 != 0ull && rw.w2 != 0ull);
+    if (to_pair && lane < C) ready &= rec_load(rs, lane * kSt + kArgmaxWord * 8) != 0ull;
+    for (int cc = lane + 64; cc < C; cc += 64) {
+#pragma unroll
+      for (int w = 0; w < 3; ++w) ready &= rec_load(rs, cc * kSt + w * 8) != 0ull;
+      if (to_pair) ready &= rec_load(rs, cc * kSt + kArgmaxWord * 8) != 0ull;
+    }
+    return ready;
+  });
+  const RowStats st = merge_records(rw, rs, C, kSt, pair);
+  const float lse2_p = lse_log2(st.p);
+  const float lse2_q = pair ? lse_log2(st.q) : 0.f;
+  const bool bad_p = !wto_rec && !(__builtin_isfinite(lse2_p));
+  const bool bad_q = !wto_rec && pair && !(__builtin_isfinite(lse2_q));
+  const bool stats_ok = !wto_rec && !bad_p && !bad_q;
+  // target-only: the greedy draft token from the records, then p at it
+  if constexpr (TO) {
+    y = pair ? (int)merge_argmax(rs, C, kSt) : 0;
+    y_ok = pair && y >= 0 && y < a.V;
+    ay = y_ok ? load_one<DT>(trow, y) : 0.f;
+  }
+  // The acceptance test in the base-2 log domain, in float64, from the row
+  // statistics (ref, z) the main kernel summed with the same logit scale L:
+  //   u < p(y) / q(y)  <=>  log2 u < (a_y - b_y) L - (lse2_p - lse2_q),
+  // lse2 = ref + log2 z.  Taken in float32, the two base-2 log-sum-exps (about
+  // 17 at V = 151936) would each round by up to 1e-6; here every term keeps the
+  // accuracy of the float32 sums z (log2 z split into exponent and mantissa),
+  // and log2 u (u on a 2^-24 grid) carries one float32 rounding.  Target-only
+  // verify tests log2 u < log2 p(y) = a_y L - lse2_p instead.
+  const double Ld = (double)L;
+  const double l2p = stats_ok ? (double)st.p.ref + log2_split(st.p.z) : 0.0;
+  const double lu = u > 0.f ? (double)fast_log2(u) : -__builtin_huge_val();
+  double lratio = 0.0;
+  if (TO) lratio = (double)ay * Ld - l2p;
+  else if (pair && stats_ok)
+    lratio = ((double)ay - (double)by) * Ld - (l2p - ((double)st.q.ref + log2_split(st.q.z)));
+
+  // ---- phase 2: the pass-2 words, and the Gumbel-max keys or the masses without
+  // the greedy token; each poll keeps the pass-2 words of the lane's first KC chunks
+  // and only tests the others (they are read again below) -------------------------
+  const uint64_t* gk = GM ? a.gkeys + (int64_t)g * C * kWaves * 2 : nullptr;
+  uint64_t pw[KC][kWaves];
+  const bool wto_p2 = wait_words([&]() {
+    bool ready = true;
+#pragma unroll
+    for (int i = 0; i < KC; ++i)
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        pw[i][w] = get_word(p2 + (int64_t)min(c0 + i, C - 1) * kWaves + w);
+        ready &= !(c0 + i < c1) || pw[i][w] != 0ull;
+      }
+    for (int cc = c0 + KC; cc < c1; ++cc)
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) ready &= get_word(p2 + (int64_t)cc * kWaves + w) != 0ull;
+    if (to_pair)
+      for (int i = lane; i < C * kWaves; i += 64) ready &= __float_as_uint(ld_coherent(p3 + i)) != 0u;
+    if (GM)
+      for (int i = lane; i < C * kWaves * 2; i += 64) ready &= get_word(gk + i) != 0ull;
+    return ready;
+  });
+  const bool wto = wto_rec || wto_p2;
 #pragma unroll
   for (int i = 0; i < KC; ++i) {
     if (c0 + i < c1) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
         const uint64_t v = pw[i][w];
-        seg[i][w] = to_pair ? p3[(int64_t)(c0 + i) * kWaves + w] : unpack_lo(v);
-        om_sum += unpack_hi(v);
+        seg[i][w] = to_pair ? unmark(ld_coherent(p3 + (int64_t)(c0 + i) * kWaves + w)) : unpack_lo(v);
+        om_sum += unmark(unpack_hi(v));
         tv_sum += unpack_lo(v);
       }
     }
@@ -769,35 +895,15 @@ __global__ void verify_finish(VerifyArgs a) {
   for (int cc = c0 + KC; cc < c1; ++cc)
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const uint64_t v = p2[(int64_t)cc * kWaves + w];
-      om_sum += unpack_hi(v);
+      const uint64_t v = get_word(p2 + (int64_t)cc * kWaves + w);
+      om_sum += unmark(unpack_hi(v));
       tv_sum += unpack_lo(v);
     }
-  // target-only: the greedy draft token from the records, then p at it
-  if constexpr (TO) {
-    y = pair ? (int)merge_argmax(rs, C, kSt) : 0;
-    y_ok = pair && y >= 0 && y < a.V;
-    ay = y_ok ? load_one<DT>(trow, y) : 0.f;
-  }
-
-  // ---- row statistics from the pass-1 records ---------------------------------
-  const RowStats st = merge_records(rw, rs, C, kSt, pair);
-  const float lse2_p = lse_log2(st.p);
-  const float lse2_q = pair ? lse_log2(st.q) : 0.f;
-  const bool bad_p = !(__builtin_isfinite(lse2_p));
-  const bool bad_q = pair && !(__builtin_isfinite(lse2_q));
-  // the row's pass-2 partials: NaN (with finite statistics) where a bounded wait of
-  // the main kernel for the row statistics timed out
-  float ot[2] = {om_sum, tv_sum};
-  wave_reduce<false, 2>(ot);
-  const bool timed_out = !(bad_p || bad_q) && !(ot[0] == ot[0] && ot[1] == ot[1]);
-  const bool bad = bad_p || bad_q || timed_out;
-  float u, up;
-  row_uniforms(a.seed, a.offset, (uint64_t)g, &u, &up);
 
   // chunk mass (residual, or p for a bonus row) and its segment masses
   auto seg_mass = [&](int cc, int w) {   // any chunk, from memory
-    return to_pair ? p3[(int64_t)cc * kWaves + w] : unpack_lo(p2[(int64_t)cc * kWaves + w]);
+    return to_pair ? unmark(ld_coherent(p3 + (int64_t)cc * kWaves + w))
+                   : unpack_lo(get_word(p2 + (int64_t)cc * kWaves + w));
   };
   auto chunk_mass_own = [&](int cc) {    // a chunk of this lane's block
     const int i = cc - c0;
@@ -811,17 +917,13 @@ __global__ void verify_finish(VerifyArgs a) {
     }
     return m;
   };
-  auto pmass = [&](int cc) {   // mass of p in chunk cc, from its record
-    const uint64_t w0 = rec_load(rs, cc * kSt);
-    const float z = unmark(unpack_hi(w0));
-    return z > 0.f ? z * fast_exp2(unpack_lo(w0) - lse2_p) : 0.f;
-  };
-
-  float alpha = 0.f;
+  // ---- the chunk scan: it needs only the pass-2 masses and u', so it runs before
+  // the row statistics are merged (on whatever the masses hold: a row found bad
+  // below discards it) ------------------------------------------------------------
   bool empty_res = false;
   Scan sc{0.0, 0, 0.0};
   float oseg[kWaves] = {0.f, 0.f, 0.f, 0.f};   // segment masses of the owner chunk
-  if (!bad && !GM) {
+  if constexpr (!GM) {
     // block sums in lane order, prefix over lanes, then the owner lane walks its block
     double blk = 0.0;
     int last_pos = -1;
@@ -872,6 +974,51 @@ __global__ void verify_finish(VerifyArgs a) {
       for (int w = 0; w < kWaves; ++w) oseg[w] = seg_mass(sc.owner, w);
     }
   }
+  // Where the residual has mass, and for a bonus row, the owner segment follows from
+  // the owner chunk's segment masses: its loads go out before the statistics merge.
+  const int vpc = (int)a.sp.vec_per_chunk, nvec = (int)a.sp.nvec, nfull = (int)a.sp.nvec_full;
+  auto pick_segment = [&](double tl, int& os, double& seg_start) {
+    os = -1;
+    seg_start = -__builtin_huge_val();
+    double run = 0.0;
+    int lastpos = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+      const double m = (double)oseg[i];
+      if (m > 0.0) lastpos = i;
+      if (os < 0 && run + m > tl) { os = i; seg_start = run; }
+      run += m;
+    }
+    if (os < 0) os = lastpos;
+  };
+  auto issue_segment = [&](int oc, int sgm, bool q_rows, RawChunk<NV, 2>& raw) {
+    const int s0 = oc * vpc + sgm * kSegVec;
+    const char* const rows[2] = {trow, q_rows ? drow : trow};
+    issue_seg<DT, NV, 2>(raw, rows, s0 + lane, nfull - 1);
+  };
+  const bool pre = !GM && !(pair && !(sc.total > 0.0));
+  RawChunk<NV, 2> raw_pre;
+  int os_pre = 0;
+  double start_pre = 0.0;
+  if (pre) {
+    pick_segment((double)up * sc.total - sc.start, os_pre, start_pre);
+    issue_segment(sc.owner, os_pre, !TO && pair, raw_pre);
+  }
+
+  // the row's pass-2 partials: NaN (with finite statistics) where a bounded wait of
+  // a workgroup for the row statistics timed out
+  float ot[2] = {om_sum, tv_sum};
+  wave_reduce<false, 2>(ot);
+  const bool timed_out = wto || (!(bad_p || bad_q) && !(ot[0] == ot[0] && ot[1] == ot[1]));
+  const bool bad = bad_p || bad_q || timed_out;
+
+  auto pmass = [&](int cc) {   // mass of p in chunk cc, from its record
+    const uint64_t w0 = rec_load(rs, cc * kSt);
+    const float z = unmark(unpack_hi(w0));
+    return z > 0.f ? z * fast_exp2(unpack_lo(w0) - lse2_p) : 0.f;
+  };
+
+  float alpha = 0.f;
   if (!bad && pair) {
     alpha = ot[0];
     tv_sum = ot[1];
@@ -891,14 +1038,13 @@ __global__ void verify_finish(VerifyArgs a) {
     // Gumbel-max: the largest key over the row's waves, of the residual for a pair
     // row (unless it is empty or no residual key is finite: then the inverse CDF of
     // p below), of p for a bonus row
-    const uint64_t* gk = a.gkeys + (int64_t)g * C * kWaves * 2;
     float m = kNegInf;
     uint32_t idx = 0xffffffffu;
     auto best = [&](int slot) {
       m = kNegInf;
       idx = 0xffffffffu;
       for (int i = lane; i < C * kWaves; i += 64) {
-        const uint64_t w = gk[i * 2 + slot];
+        const uint64_t w = get_word(gk + i * 2 + slot);
         argmax_fold(m, idx, unpack_lo(w), argmax_index(w));
       }
       wave_argmax(m, idx);
@@ -913,18 +1059,19 @@ __global__ void verify_finish(VerifyArgs a) {
   // the owner segment inside the owner chunk, then the inverse CDF in it
   const float zr = pair ? z_ratio(st.p.z, st.q.z, __builtin_amdgcn_rcpf(st.q.z)) : 1.f,
               rzp = __builtin_amdgcn_rcpf(st.p.z);
-  auto sample_owner = [&]() -> int {
+  // have_raw: the owner segment and its loads are the ones issued above
+  auto sample_owner = [&](bool have_raw) -> int {
     const int oc = sc.owner;
-    const int vpc = (int)a.sp.vec_per_chunk, nvec = (int)a.sp.nvec, nfull = (int)a.sp.nvec_full;
     const int obeg = oc * vpc;
     const int oend = min(obeg + vpc, nvec);
     const int lim = min(oend, nfull);
     // this lane's values of wave segment s: p, or max(0, p - q) for a non-empty residual
-    auto seg_values = [&](int s, float (&v)[NV][PV]) {
+    auto seg_values = [&](int s, float (&v)[NV][PV], bool use_pre) {
       const int s0 = obeg + s * kSegVec;
       const char* const rows[2] = {trow, use_q ? drow : trow};
       RawChunk<NV, 2> raw;
-      issue_seg<DT, NV, 2>(raw, rows, s0 + lane, nfull - 1);
+      if (use_pre) raw = raw_pre;
+      else issue_segment(oc, s, use_q, raw);
       float x[2][NV * PV];
       unpack_seg<DT, NV, 2>(raw, rows, s0 + lane, s0 + kSegVec <= lim, lim, nfull, oend, (int)a.V, x);
 #pragma unroll
@@ -951,7 +1098,7 @@ __global__ void verify_finish(VerifyArgs a) {
       // segment masses of p are not recorded for a pair row: measure them (rare)
       double run = 0.0;
       for (int s = 0; s < kWaves && os < 0; ++s) {
-        seg_values(s, v);
+        seg_values(s, v, false);
         float m = 0.f;
 #pragma unroll
         for (int j = 0; j < NV; ++j)
@@ -962,19 +1109,14 @@ __global__ void verify_finish(VerifyArgs a) {
         run += md;
       }
       if (os < 0) os = kWaves - 1;
+      have_raw = false;
+    } else if (have_raw) {
+      os = os_pre;
+      seg_start = start_pre;
     } else {
-      double run = 0.0;
-      int lastpos = 0;
-#pragma unroll
-      for (int i = 0; i < kWaves; ++i) {
-        const double m = (double)oseg[i];
-        if (m > 0.0) lastpos = i;
-        if (os < 0 && run + m > tl) { os = i; seg_start = run; }
-        run += m;
-      }
-      if (os < 0) os = lastpos;
+      pick_segment(tl, os, seg_start);
     }
-    seg_values(os, v);
+    seg_values(os, v, have_raw);
     const int loc = wave_inverse_cdf<NV, PV>(v, tl - seg_start);
     return loc >= 0 ? (obeg + os * kSegVec) * PV + loc : -1;
   };
@@ -983,10 +1125,10 @@ __global__ void verify_finish(VerifyArgs a) {
     // with the row's u' (the main kernel forms p's keys for bonus rows only)
     use_q = false;
     sc = wave_scan_owner(C, up, pmass);
-    token = sample_owner();
+    token = sample_owner(false);
   }
   if (!bad && !GM) {
-    token = sample_owner();
+    token = sample_owner(pre);
     if (token < 0 && use_q) {
       // a residual made of rounding alone (p and q equal up to float32 rounding):
       // its mass from pass 2 was positive, but the owner segment's values, formed
@@ -994,7 +1136,7 @@ __global__ void verify_finish(VerifyArgs a) {
       empty_res = true;
       use_q = false;
       sc = wave_scan_owner(C, up, pmass);
-      token = sample_owner();
+      token = sample_owner(false);
     }
   }
 
@@ -1004,11 +1146,11 @@ __global__ void verify_finish(VerifyArgs a) {
 #pragma unroll
     for (int w = 0; w < kSt / 8; ++w) rec_store(rs, cc * kSt + w * 8, 0ull);
   }
-  for (int i = lane; i < C * kWaves; i += 64) p2[i] = 0ull;
+  for (int i = lane; i < C * kWaves; i += 64) put_word(p2 + i, 0ull);
   if (to_pair)
-    for (int i = lane; i < C * kWaves; i += 64) p3[i] = 0.f;
+    for (int i = lane; i < C * kWaves; i += 64) st_coherent(p3 + i, 0.f);
   if (GM)
-    for (int i = lane; i < C * kWaves * 2; i += 64) a.gkeys[(int64_t)g * C * kWaves * 2 + i] = 0ull;
+    for (int i = lane; i < C * kWaves * 2; i += 64) put_word(a.gkeys + (int64_t)g * C * kWaves * 2 + i, 0ull);
 
   if (lane == 0) {
     int status = 0;
@@ -1019,27 +1161,10 @@ __global__ void verify_finish(VerifyArgs a) {
     int flag = 0;
     const float nan = __builtin_nanf("");
     if (pair) {
-      // The acceptance ratio in float64 from the row statistics (ref, z) the main
-      // kernel summed in float32 with the same logit scale L: log2 p(y) / q(y) =
-      // (a_y - b_y) L - (lse2_p - lse2_q), lse2 = ref + log2 z.  Forming the two
-      // base-2 log-sum-exps (about 17 at V = 151936) in float32 would round each by
-      // up to 1e-6; in float64 the ratio keeps the accuracy of the float32 sums z.
-      // The acceptance test in the base-2 log domain, in float64, from the row
-      // statistics (ref, z) the main kernel summed with the same logit scale L:
-      //   u < p(y) / q(y)  <=>  log2 u < (a_y - b_y) L - (lse2_p - lse2_q),
-      // lse2 = ref + log2 z.  Taken in float32, the two base-2 log-sum-exps (about
-      // 17 at V = 151936) would each round by up to 1e-6; here every term keeps the
-      // accuracy of the float32 sums z (log2 z split into exponent and mantissa),
-      // and log2 u (u on a 2^-24 grid) carries one float32 rounding.  A ratio of at
-      // least 1 accepts outright (u < 1); u = 0 gives -inf (accept whenever p(y) > 0);
-      // a NaN difference (p(y) = q(y) = 0) rejects.
-      const double Ld = (double)L;
-      const double l2p = bad ? 0.0 : (double)st.p.ref + log2_split(st.p.z);
-      const double lu = u > 0.f ? (double)fast_log2(u) : -__builtin_huge_val();
       if (TO) {
         // target-only: accept the greedy token with probability p(y); the RS/TO
         // boundary TV < 1 - p(y)
-        const double lpy = (double)ay * Ld - l2p;
+        const double lpy = lratio;
         const float py = y_ok && !bad ? fast_exp2((float)lpy) : nan;
         if (y_ok && !bad) flag = lpy >= 0.0 || lu < lpy ? 1 : 0;   // p(y) = 1: u < 1 always
         a.draft_token[b * G + k] = y_ok && !bad ? y : -1;
@@ -1048,27 +1173,20 @@ __global__ void verify_finish(VerifyArgs a) {
       } else if (!y_ok) {
         status |= kRowBadToken;
       } else if (!bad) {
-        const double l2q = (double)st.q.ref + log2_split(st.q.z);
-        const double d = ((double)ay - (double)by) * Ld - (l2p - l2q);
+        const double d = lratio;
         if (d == d) flag = d >= 0.0 || lu < d ? 1 : 0;   // ratio >= 1: u < 1 always
       }
       a.accept[b * G + k] = (uint8_t)flag;
       if (a.overlap) a.overlap[b * G + k] = bad ? nan : alpha;
       if (a.tv) a.tv[b * G + k] = bad ? nan : r_tot;
     }
-    // the entropy needs only the pass-1 records: valid after a timed-out wait too
-    if (a.entropy) a.entropy[g] = bad_p ? nan : kLn2 * (fast_log2(st.p.z) - st.p.y / st.p.z);
+    // the entropy needs only the pass-1 records: valid after a timed-out wait for
+    // the pass-2 words too
+    if (a.entropy) a.entropy[g] = bad_p || wto_rec ? nan : kLn2 * (fast_log2(st.p.z) - st.p.y / st.p.z);
     if (a.row_token) a.row_token[g] = token;
     if (a.row_status) a.row_status[g] = status;
     flag_sh[k] = flag;
     token_sh[k] = token;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int n = 0;
-    while (n < G && flag_sh[n] == 1) ++n;
-    a.accepted_len[b] = n;
-    a.next_token[b] = token_sh[n];
   }
 }
 
@@ -1195,9 +1313,6 @@ template <int DT, int NV, int MODE>
 static hipError_t launch(const VerifyArgs& a, hipStream_t stream) {
   const int64_t grid = (int64_t)a.sgroups * a.sp.nchunks;
   hipLaunchKernelGGL((verify_main<DT, NV, MODE>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((verify_finish<DT, NV, MODE>), dim3((unsigned)a.B), dim3(64 * (a.G + 1)), 0, stream, a);
   return hipGetLastError();
 }
 
