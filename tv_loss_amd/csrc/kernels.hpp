@@ -52,6 +52,35 @@ __device__ __forceinline__ int fast_div(int n, const FastDiv& f) {
   return (int)((__umulhi((uint32_t)n, f.lo) + (uint32_t)n * f.hi) >> f.s);
 }
 
+// Contiguous item ranges for S persistent super-groups of C workgroups each.  The
+// grid's workgroups reach the compute units in launch order, one per unit and
+// dispatch round, so super-group s (workgroups sC .. sC + C - 1) has its last
+// workgroup in round r(s) = ((s + 1) C - 1) / W, W the workgroups per round (the
+// compute-unit count).  Waves of a later round lose issue arbitration to the older
+// ones on their unit and run measurably slower, so the host gives the super-groups
+// of round r `items` items each, except the last `short_by` of them, which take one
+// fewer (plan_round_split).  Returns the first item of super-group s (the total for
+// s = S).
+constexpr int kMaxRounds = 8;
+struct RoundSplit {
+  int W;                       // workgroups per round; 0: strided items; -1: split by thirds
+  int rounds;
+  int items[kMaxRounds], short_by[kMaxRounds];
+};
+
+__device__ __forceinline__ int round_first_sg(int r, int C, int W) { return (r * W + C) / C - 1; }
+
+__device__ __forceinline__ int round_split_base(const RoundSplit& rs, int s, int S, int C) {
+  int base = 0;
+  for (int r = 0; r < rs.rounds; ++r) {
+    const int lo = min(S, round_first_sg(r, C, rs.W)), hi = min(S, round_first_sg(r + 1, C, rs.W));
+    const int full = (hi - lo) - rs.short_by[r];   // super-groups of the round with all items
+    const int k = min(max(s, lo), hi) - lo;        // super-groups of the round before s
+    base += k * rs.items[r] - max(0, k - full);
+  }
+  return base;
+}
+
 struct VerifyArgs {
   const void* target; int64_t t_stride;   // row (b, k) of [B, G+1, V] at (b*(G+1)+k)*t_stride
   const void* draft;  int64_t d_stride;   // row (b, k) of [B, G, V]   at (b*G+k)*d_stride
@@ -76,6 +105,7 @@ struct VerifyArgs {
   int ngroups;
   int sgroups, layers;   // super-groups (all co-resident), groups per super-group
   FastDiv div_b, div_g1; // division by B and by gamma + 1
+  RoundSplit split;      // contiguous item ranges per super-group (see verify_main)
 };
 
 // Verify modes: rejection sampling with inverse-CDF samples; target-only (greedy

@@ -180,16 +180,22 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
   const int wp = (slot + c) & (kWaves - 1), wq = wp ^ 1;   // combine and publish p / q
   const int rp = wp ^ 2, rq = wp ^ 3;                     // poll p / q records
 
-  // Items are rows w = 0 .. N - 1 taken k-major (all k = 0 rows first).  Super-
-  // groups late in launch order start late (their first loads queue behind those of
-  // the earlier ones; on a full chip the last ones trail the first by about three
-  // layers), so when every super-group has at least four items the middle and last
-  // thirds take one and two items fewer than the first third, each super-group a
-  // contiguous range of items; otherwise super-group sg takes w = sg + i S.
+  // Items are rows w = 0 .. N - 1 taken k-major (all k = 0 rows first), each
+  // super-group a contiguous range, by one of two splits the host picks:
+  //  - by dispatch round (round_split_base), when the super-groups have many items
+  //    each: what a later round loses per item then adds up over the layers;
+  //  - with few items each, the middle and last thirds of the super-groups take one
+  //    and two items fewer than the first: the last ones end well before the others
+  //    and, as they host the finish (below), have the rows' statistics merged by
+  //    the time the last pass-2 words arrive.
+  // With fewer than four items per super-group, super-group sg takes w = sg + i S.
   if (sg >= a.ngroups) return;
   const int N = a.ngroups;
   int nl = (N - 1 - sg) / S + 1, base = -1;
-  if (S >= 3 && N >= 4 * S) {
+  if (a.split.W > 0) {
+    base = round_split_base(a.split, sg, S, C);
+    nl = round_split_base(a.split, sg + 1, S, C) - base;
+  } else if (a.split.W < 0) {
     const int s1 = (S + 2) / 3, s2 = (2 * S + 2) / 3;
     const int Sd = (S - s1) + (S - s2);                 // items the later thirds give up
     const int H = (N + Sd) / S, R = N + Sd - H * S;
@@ -850,11 +856,17 @@ __device__ __forceinline__ void finish_row(const VerifyArgs& a, int b, int k, in
   // verify tests log2 u < log2 p(y) = a_y L - lse2_p instead.
   const double Ld = (double)L;
   const double l2p = stats_ok ? (double)st.p.ref + log2_split(st.p.z) : 0.0;
-  const double lu = u > 0.f ? (double)fast_log2(u) : -__builtin_huge_val();
+  double lu = u > 0.f ? (double)fast_log2(u) : -__builtin_huge_val();
   double lratio = 0.0;
   if (TO) lratio = (double)ay * Ld - l2p;
   else if (pair && stats_ok)
     lratio = ((double)ay - (double)by) * Ld - (l2p - ((double)st.q.ref + log2_split(st.q.z)));
+  // the entropy needs only the pass-1 records: valid after a timed-out wait for the
+  // pass-2 words too
+  const float entropy = bad_p || wto_rec ? __builtin_nanf("") : kLn2 * (fast_log2(st.p.z) - st.p.y / st.p.z);
+  // formed here, while the other workgroups still run, not where they are used
+  float ent_v = entropy;
+  asm volatile("" : "+v"(lratio), "+v"(lu), "+v"(up), "+v"(ent_v));
 
   // ---- phase 2: the pass-2 words, and the Gumbel-max keys or the masses without
   // the greedy token; each poll keeps the pass-2 words of the lane's first KC chunks
@@ -1140,18 +1152,6 @@ __device__ __forceinline__ void finish_row(const VerifyArgs& a, int b, int k, in
     }
   }
 
-  // clear this row's records and pass-2 words for the next call (the wave has read
-  // them all): a call leaves every workspace word it wrote at zero
-  for (int cc = lane; cc < C; cc += 64) {
-#pragma unroll
-    for (int w = 0; w < kSt / 8; ++w) rec_store(rs, cc * kSt + w * 8, 0ull);
-  }
-  for (int i = lane; i < C * kWaves; i += 64) put_word(p2 + i, 0ull);
-  if (to_pair)
-    for (int i = lane; i < C * kWaves; i += 64) st_coherent(p3 + i, 0.f);
-  if (GM)
-    for (int i = lane; i < C * kWaves * 2; i += 64) put_word(a.gkeys + (int64_t)g * C * kWaves * 2 + i, 0ull);
-
   if (lane == 0) {
     int status = 0;
     if (bad_p) status |= kRowBadTarget;
@@ -1180,14 +1180,24 @@ __device__ __forceinline__ void finish_row(const VerifyArgs& a, int b, int k, in
       if (a.overlap) a.overlap[b * G + k] = bad ? nan : alpha;
       if (a.tv) a.tv[b * G + k] = bad ? nan : r_tot;
     }
-    // the entropy needs only the pass-1 records: valid after a timed-out wait for
-    // the pass-2 words too
-    if (a.entropy) a.entropy[g] = bad_p || wto_rec ? nan : kLn2 * (fast_log2(st.p.z) - st.p.y / st.p.z);
+    if (a.entropy) a.entropy[g] = ent_v;
     if (a.row_token) a.row_token[g] = token;
     if (a.row_status) a.row_status[g] = status;
     flag_sh[k] = flag;
     token_sh[k] = token;
   }
+  // clear this row's records and pass-2 words for the next call (the wave has read
+  // them all): a call leaves every workspace word it wrote at zero.  Last, so that
+  // nothing in the row waits for these stores to complete
+  for (int cc = lane; cc < C; cc += 64) {
+#pragma unroll
+    for (int w = 0; w < kSt / 8; ++w) rec_store(rs, cc * kSt + w * 8, 0ull);
+  }
+  for (int i = lane; i < C * kWaves; i += 64) put_word(p2 + i, 0ull);
+  if (to_pair)
+    for (int i = lane; i < C * kWaves; i += 64) st_coherent(p3 + i, 0.f);
+  if (GM)
+    for (int i = lane; i < C * kWaves * 2; i += 64) put_word(a.gkeys + (int64_t)g * C * kWaves * 2 + i, 0ull);
 }
 
 // ---------------------------------------------------------------------------
