@@ -107,6 +107,9 @@ int device_cus() {
 // Measured on MI355X (four verify workgroups per compute unit): each later dispatch
 // round takes about 6 % longer per item.
 constexpr double kVerifyRoundCost = 0.06;
+// ... and for the fused TV forward + backward (two workgroups per compute unit:
+// 4.81 -> 4.70 ms on T = 8192; the single-read forward measured no faster with it)
+constexpr double kTvRoundCost = 0.08;
 
 // Item counts per dispatch round for S super-groups of C workgroups, W per round,
 // N items, an item of round r costing 1 + cost r: the smallest end time T at which
@@ -681,7 +684,7 @@ mtp_status mtp_tv_loss_fwd(const void* target, int64_t target_pos_stride, int64_
   a.part2 = at<float>(workspace, L.part2);
   a.pos_ws = at<float>(workspace, L.pos);
   a.sp = L.sp;
-  a.sgroups = sgroups;
+  a.sgroups = sgroups;   // positions strided (a split by dispatch round measured no faster)
   a.wait_limit = g_wait_limit.load(std::memory_order_relaxed);
   hipError_t e = pipe ? mtp::launch_tv_pipe_fwd(a, dtype, shared, (hipStream_t)stream)
                       : mtp::launch_tv_fwd(a, dtype, shared, (hipStream_t)stream);
@@ -884,6 +887,8 @@ mtp_status mtp_tv_loss_fwd_bwd(const void* target, int64_t target_pos_stride, in
   a.pos_ws = at<float>(workspace, L.pos);
   a.sp = L.sp;
   a.sgroups = sgroups;
+  if (T >= 16 * (int64_t)sgroups)
+    a.split = plan_round_split(sgroups, L.sp.nchunks, T, device_cus(), kTvRoundCost);
   a.wait_limit = g_wait_limit.load(std::memory_order_relaxed);
   hipError_t e = mtp::launch_tv_fused(a, dtype, shared, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MTP_ERR_LAUNCH, "fused TV loss launch failed: %s", hipGetErrorString(e));

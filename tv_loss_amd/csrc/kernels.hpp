@@ -146,6 +146,7 @@ struct TvArgs {
   uint32_t* err; uint64_t* part1; float* part2; float* pos_ws; uint64_t* part3;
   RowSplit sp;
   int sgroups;   // single-read forward: super-groups of sp.nchunks workgroups, all resident
+  RoundSplit split;   // their contiguous position ranges (split.W = 0: t = sg + i sgroups)
   // top-K path: the target of head k at position t is given by K entries, indices
   // idx and logits val at t*k_pos + k*k_head + j (k_head = 0: shared by the heads)
   const int32_t* idx; const float* val; int64_t k_pos, k_head; int K;

@@ -337,8 +337,14 @@ __global__ __launch_bounds__(kBlock, 2) void tv_pipe_main(TvArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int tid = threadIdx.x;
   if (sg >= a.T) return;
-  const int nl = (a.T - 1 - sg) / S + 1;
-  auto pos_of = [&](int i) { return sg + i * S; };
+  // positions t = sg + i S, or the contiguous range the host sized for this
+  // super-group's dispatch round (round_split_base)
+  int nl = (a.T - 1 - sg) / S + 1, base = -1;
+  if (a.split.W > 0) {
+    base = round_split_base(a.split, sg, S, C);
+    nl = round_split_base(a.split, sg + 1, S, C) - base;
+  }
+  auto pos_of = [&](int i) { return base >= 0 ? base + i : sg + i * S; };
   auto rsrc_rec = [&](int t) { return rsrc_of(a.part1 + (int64_t)t * C * NR); };
 
   const int vpc = (int)a.sp.vec_per_chunk, nvec = (int)a.sp.nvec, nfull = (int)a.sp.nvec_full;
@@ -853,8 +859,14 @@ __global__ __launch_bounds__(kBlock, 2) void tv_fused_main(TvArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int tid = threadIdx.x;
   if (sg >= a.T) return;
-  const int nl = (a.T - 1 - sg) / S + 1;
-  auto pos_of = [&](int i) { return sg + i * S; };
+  // positions t = sg + i S, or the contiguous range the host sized for this
+  // super-group's dispatch round (round_split_base)
+  int nl = (a.T - 1 - sg) / S + 1, base = -1;
+  if (a.split.W > 0) {
+    base = round_split_base(a.split, sg, S, C);
+    nl = round_split_base(a.split, sg + 1, S, C) - base;
+  }
+  auto pos_of = [&](int i) { return base >= 0 ? base + i : sg + i * S; };
   auto rsrc_rec = [&](int t) { return rsrc_of(a.part1 + (int64_t)t * C * NR); };
   auto rsrc_rec2 = [&](int t) { return rsrc_of(a.part3 + (int64_t)t * C * G); };
 
