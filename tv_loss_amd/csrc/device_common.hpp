@@ -846,18 +846,19 @@ __device__ __forceinline__ void row_uniforms(uint64_t seed, uint64_t offset, uin
 // base-2 units: E = -log2 U = -ln U / ln 2, U = (k + 1/2) 2^-24 with k = word >> 8
 // of Philox at counter (c, 1 + v4, 0), key = seed.  The Gumbel noise is -ln(-ln U),
 // so argmax_v (ln w_v + G_v) = argmax_v w_v / E_v = argmax_v (log2 w_v - log2 E_v)
-// (the exponential race).  The smallest E (U near 1, the likely winners) keep their
-// relative accuracy: where e = 1 - U = (2^25 - 2k - 1) 2^-25 is below 2^-5 (exact in
-// float32 there), E comes from the series -log2(1 - e) = (e / ln 2)(1 + e/2 + e^2/3 +
-// e^3/4 + ...) cut after e^3/4 (relative error below e^4 / 5 < 2^-22); elsewhere
-// from log2 of U rounded to float32 (U has 25 significant bits above 1/2), an error
-// of at most 2^-24 / ln 2 in log2 U, below 2e-6 relative to E >= 0.045.
+// (the exponential race).  U has 25 significant bits above 1/2, so float32 rounds
+// it (U_r); the rounding d = U - U_r comes back exactly from one fused multiply-add
+// (k 2^-24 - U_r is a small multiple of 2^-25) and one addition, and
+//   E = -log2 U_r - log2(1 + d / U_r) = -log2 U_r - d log2(e) + eps,
+// |eps| <= |d| log2(e) (1 - U_r) / U_r + d^2 / U_r^2, below 1e-7 relative to E for
+// every U (|d| <= 2^-25; E ~ (1 - U) log2(e) near 1).  The hardware base-2 log keeps
+// about 1e-7 of relative accuracy down to U = 1 - 2^-24, where E is smallest and
+// the likely winners are, so E is within a few 1e-7 relative of -log2 U throughout.
 __device__ __forceinline__ float expo_of_word(uint32_t w) {
   const float kf = (float)(w >> 8);
-  const float e = __builtin_fmaf(-kf, 0x1p-24f, 1.f - 0x1p-25f);   // 1 - U, exact below 1/2
-  const float U = __builtin_fmaf(kf, 0x1p-24f, 0x1p-25f);          // exact below 1/2
-  const float s = __builtin_fmaf(e, __builtin_fmaf(e, __builtin_fmaf(e, 0.25f, 1.f / 3.f), 0.5f), 1.f);
-  return e < 0x1p-5f ? e * kLog2e * s : -fast_log2(U);
+  const float Ur = __builtin_fmaf(kf, 0x1p-24f, 0x1p-25f);          // U rounded once
+  const float d = __builtin_fmaf(kf, 0x1p-24f, -Ur) + 0x1p-25f;       // U - U_r, exact
+  return __builtin_fmaf(-d, kLog2e, -fast_log2(Ur));
 }
 
 __device__ __forceinline__ void expo4(uint64_t seed, uint64_t c, uint32_t v4, float (&E)[4]) {
