@@ -79,7 +79,7 @@ def test_ragged_vocab(V, G, B, dtype):
 def test_many_chunks_float32(V):
     """More than 64 (V = 262144) and more than 128 (V = 400003) chunks per row for
     float32 rows: records beyond the first 64 per lane batch, and chunk masses the
-    finish kernel re-reads instead of keeping in registers."""
+    finish re-reads instead of keeping in registers."""
     B, G = 2, 2
     w = dict(B=B, G=G, V=V, dtype=torch.float32, kind="normal", scale=1.2, sigma=0.5, seed=13)
     t, d, y = synthetic.verify_inputs(w, DEV, seed=V)
