@@ -929,9 +929,8 @@ __device__ __forceinline__ void finish_row(const VerifyArgs& a, int b, int k, in
     }
     return m;
   };
-  // ---- the chunk scan: it needs only the pass-2 masses and u', so it runs before
-  // the row statistics are merged (on whatever the masses hold: a row found bad
-  // below discards it) ------------------------------------------------------------
+  // ---- the chunk scan: it needs only the pass-2 masses and u', so it runs as soon
+  // as they are in, on whatever they hold (a row found bad below discards it) ------
   bool empty_res = false;
   Scan sc{0.0, 0, 0.0};
   float oseg[kWaves] = {0.f, 0.f, 0.f, 0.f};   // segment masses of the owner chunk
@@ -987,7 +986,8 @@ __device__ __forceinline__ void finish_row(const VerifyArgs& a, int b, int k, in
     }
   }
   // Where the residual has mass, and for a bonus row, the owner segment follows from
-  // the owner chunk's segment masses: its loads go out before the statistics merge.
+  // the owner chunk's segment masses: its loads go out right away, ahead of the
+  // checks below.
   const int vpc = (int)a.sp.vec_per_chunk, nvec = (int)a.sp.nvec, nfull = (int)a.sp.nvec_full;
   auto pick_segment = [&](double tl, int& os, double& seg_start) {
     os = -1;
