@@ -48,8 +48,11 @@ def _clear_error(ws):
 
 
 def test_verify_reports_timed_out_rows(zero_wait_limit):
+    # the full rollout batch: with about ten items per super-group, a large share of
+    # the record polls find a record not yet published (a few polls of a smaller
+    # batch may all find their records in place, and then nothing gives up)
     w = synthetic.VERIFY_WORKLOADS["rollout"]
-    t, d, y = synthetic.verify_inputs(w, DEV, B=16)
+    t, d, y = synthetic.verify_inputs(w, DEV, B=64)
     print("verify with wait limit 0", flush=True)
     out = mtp.verify(t, d, y, seed=2, offset=0)
     torch.cuda.synchronize()
