@@ -680,7 +680,7 @@ __device__ __forceinline__ void issue_seg_fixed(RawChunk<NV, R>& raw, const char
 template <int DT, int NV, int R>
 __device__ __forceinline__ void unpack_seg(const RawChunk<NV, R>& raw, const char* const (&rows)[R], int v0,
                                            bool full, int lim, int tail, int cend, int V,
-                                           float (&x)[R][NV * Elem<DT>::kPerVec], int nrows = R) {
+                                           float (&x)[R][NV * Elem<DT>::kPerVec]) {
   constexpr int PV = Elem<DT>::kPerVec;
   constexpr uint32_t kMasked = DT == kBF16 ? 0xFF80FF80u : 0xFF800000u;
   auto put = [&](int r, int j, int w, uint32_t word) {
@@ -696,7 +696,6 @@ __device__ __forceinline__ void unpack_seg(const RawChunk<NV, R>& raw, const cha
     for (int j = 0; j < NV; ++j)
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        if (r >= nrows) break;
 #pragma unroll
         for (int w = 0; w < 4; ++w) put(r, j, w, raw.v[r][j][w]);
       }
@@ -708,7 +707,6 @@ __device__ __forceinline__ void unpack_seg(const RawChunk<NV, R>& raw, const cha
     const bool ok = v0 + j * 64 < lim;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      if (r >= nrows) break;
 #pragma unroll
       for (int w = 0; w < 4; ++w) put(r, j, w, ok ? raw.v[r][j][w] : kMasked);
     }
@@ -719,7 +717,6 @@ __device__ __forceinline__ void unpack_seg(const RawChunk<NV, R>& raw, const cha
       if (v0 + j * 64 == tail) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          if (r >= nrows) break;
 #pragma unroll
           for (int e = 0; e < PV; ++e) {
             const int idx = tail * PV + e;

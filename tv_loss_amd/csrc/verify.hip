@@ -481,14 +481,16 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
     const bool pair = is_pair(g_0);
     if (i >= 0 && i < nl) {
       const char* const rows[2] = {trow_of(g_0), drow_of(g_0)};
-      // both rows always (a bonus item's second row is its target row again), so
-      // that every load of the buffer is consumed before the buffer is refilled
-      // the bounds pass through an empty asm so that the masks of the partial
-      // segment path are derived there, not kept live across the loop
+      // both rows always (a bonus item's second row is its target row again, which
+      // pass 1 then ignores), so that every load of the buffer is consumed before
+      // the buffer is refilled and x[1] has one definition on every path (a
+      // bonus-only branch around its unpack costs more register copies at the join
+      // than the unpack saves); the bounds pass through an empty asm so that the
+      // masks of the partial segment path are derived there, not kept live across
+      // the loop
       int lim_l = lim, tail_l = tail, vend_l = vend, V_l = V;
       asm volatile("" : "+s"(lim_l), "+s"(tail_l), "+s"(vend_l), "+s"(V_l));
-      // a bonus item's second row (its target row again) is loaded but not unpacked
-      unpack_seg<DT, NV, 2>(rb, rows, v0, full, lim_l, tail_l, vend_l, V_l, x, pair ? 2 : 1);
+      unpack_seg<DT, NV, 2>(rb, rows, v0, full, lim_l, tail_l, vend_l, V_l, x);
     }
     // the poll goes out before the prefetch, so that waiting for it (a layer
     // later) does not wait for the prefetch
