@@ -745,7 +745,7 @@ __device__ __forceinline__ Scan wave_scan_owner(int n, float u_prime, MassFn mas
   }
   if (r.owner < 0) {   // rounding left t past every boundary: last index with mass
     const uint64_t pos = __ballot(last_pos >= 0);
-    r.owner = pos ? __shfl(last_pos, 63 - __builtin_clzll(pos), 64) : 0;
+    r.owner = pos ? readlane_i(last_pos, 63 - __builtin_clzll(pos)) : 0;
     r.start = -__builtin_huge_val();  // t - start = +inf: the owner takes its last positive element
   }
   return r;
@@ -765,7 +765,7 @@ __device__ __forceinline__ void finish_row(const VerifyArgs& a, int b, int k, in
   constexpr bool TO = MODE == kVerifyTargetOnly, GM = MODE == kVerifyGumbel;
   constexpr int PV = Elem<DT>::kPerVec;
   constexpr int kSegVec = NV * 64;
-  constexpr int KC = 2;   // chunks per lane whose pass-2 words are kept in registers
+  constexpr int KC = 1;   // chunks per lane whose pass-2 words are kept in registers
   const int C = a.sp.nchunks;
   const int G = a.G, G1 = G + 1;
   const int lane = threadIdx.x & 63;
@@ -1195,7 +1195,8 @@ __device__ __forceinline__ void finish_row(const VerifyArgs& a, int b, int k, in
 #pragma unroll
     for (int w = 0; w < kSt / 8; ++w) rec_store(rs, cc * kSt + w * 8, 0ull);
   }
-  for (int i = lane; i < C * kWaves; i += 64) put_word(p2 + i, 0ull);
+  const __amdgpu_buffer_rsrc_t rs2 = rsrc_of(p2);   // 32-bit offsets: no 64-bit address per lane
+  for (int i = lane; i < C * kWaves; i += 64) rec_store(rs2, i * 8, 0ull);
   if (to_pair)
     for (int i = lane; i < C * kWaves; i += 64) st_coherent(p3 + i, 0.f);
   if (GM)
