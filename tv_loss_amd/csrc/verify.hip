@@ -778,6 +778,10 @@ __device__ __forceinline__ void finish_row(const VerifyArgs& a, int b, int k, in
   const float L = GM ? kLog2e * a.inv_temp : kLog2e;   // logit -> base-2 exponent scale
   const __amdgpu_buffer_rsrc_t rs = rsrc_of(a.part1 + (int64_t)g * C * (kSt / 8));
   uint64_t* p2 = a.part2 + (int64_t)g * C * kWaves;
+  // the row's pass-2 words through a buffer descriptor: 32-bit offsets, so that no
+  // 64-bit address per lane stays live through the finish
+  const __amdgpu_buffer_rsrc_t rs2 = rsrc_of(p2);
+  auto p2_word = [&](int i) { return rec_load(rs2, i * 8); };
   // target-only pair rows sample p without the greedy token: its per-wave masses
   float* p3 = TO ? a.part3 + (int64_t)g * C * kWaves : nullptr;
   const bool to_pair = TO && pair;
@@ -881,12 +885,12 @@ __device__ __forceinline__ void finish_row(const VerifyArgs& a, int b, int k, in
     for (int i = 0; i < KC; ++i)
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        pw[i][w] = get_word(p2 + (int64_t)min(c0 + i, C - 1) * kWaves + w);
+        pw[i][w] = p2_word(min(c0 + i, C - 1) * kWaves + w);
         ready &= !(c0 + i < c1) || pw[i][w] != 0ull;
       }
     for (int cc = c0 + KC; cc < c1; ++cc)
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) ready &= get_word(p2 + (int64_t)cc * kWaves + w) != 0ull;
+      for (int w = 0; w < kWaves; ++w) ready &= p2_word(cc * kWaves + w) != 0ull;
     if (to_pair)
       for (int i = lane; i < C * kWaves; i += 64) ready &= __float_as_uint(ld_coherent(p3 + i)) != 0u;
     if (GM)
@@ -909,7 +913,7 @@ __device__ __forceinline__ void finish_row(const VerifyArgs& a, int b, int k, in
   for (int cc = c0 + KC; cc < c1; ++cc)
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const uint64_t v = get_word(p2 + (int64_t)cc * kWaves + w);
+      const uint64_t v = p2_word(cc * kWaves + w);
       om_sum += unmark(unpack_hi(v));
       tv_sum += unpack_lo(v);
     }
@@ -917,7 +921,7 @@ __device__ __forceinline__ void finish_row(const VerifyArgs& a, int b, int k, in
   // chunk mass (residual, or p for a bonus row) and its segment masses
   auto seg_mass = [&](int cc, int w) {   // any chunk, from memory
     return to_pair ? unmark(ld_coherent(p3 + (int64_t)cc * kWaves + w))
-                   : unpack_lo(get_word(p2 + (int64_t)cc * kWaves + w));
+                   : unpack_lo(p2_word(cc * kWaves + w));
   };
   auto chunk_mass_own = [&](int cc) {    // a chunk of this lane's block
     const int i = cc - c0;
@@ -1195,7 +1199,6 @@ __device__ __forceinline__ void finish_row(const VerifyArgs& a, int b, int k, in
 #pragma unroll
     for (int w = 0; w < kSt / 8; ++w) rec_store(rs, cc * kSt + w * 8, 0ull);
   }
-  const __amdgpu_buffer_rsrc_t rs2 = rsrc_of(p2);   // 32-bit offsets: no 64-bit address per lane
   for (int i = lane; i < C * kWaves; i += 64) rec_store(rs2, i * 8, 0ull);
   if (to_pair)
     for (int i = lane; i < C * kWaves; i += 64) st_coherent(p3 + i, 0.f);
