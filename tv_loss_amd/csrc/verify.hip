@@ -275,13 +275,18 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
   // i - 1's records and the loads of item i + 2 (into the same buffer) go out, pass
   // 1 of item i.
   auto layer = [&](int i, RawChunk<NV, 2>& rb) __attribute__((always_inline)) {
+    // this wave's role, derived again in every layer (opaque to the compiler), so
+    // that the role tests are not hoisted out of the loop as 64-bit masks that
+    // would hold scalar registers through it: 0 combines p, 1 q; 2 polls p, 3 q
+    int role = wave ^ wp;
+    asm volatile("" : "+s"(role));
     // ---- row statistics of item i - 2 (polled a layer ago) ---------------------
     if (i >= 2 && i - 2 < nl) {
       const bool pair2 = pair_m2;
       // the bookkeeping waves run at raised priority: the layer waits for them
-      if (wave == rp || (wave == rq && pair2)) {
+      if (role == 2 || (role == 3 && pair2)) {
         __builtin_amdgcn_s_setprio(3);
-        const int row = wave == rp ? 0 : 1;
+        const int row = role == 2 ? 0 : 1;
         // Waiting for every load in flight first (the next item's chunk included)
         // measured faster than testing the words as soon as their own load is back:
         // the test comes later and finds a record missing less often, and a reload
@@ -494,10 +499,10 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
     }
     // the poll goes out before the prefetch, so that waiting for it (a layer
     // later) does not wait for the prefetch
-    if (i >= 1 && i <= nl && (wave == rp || wave == rq) && lane < C) {
+    if (i >= 1 && i <= nl && role >= 2 && lane < C) {
       const __amdgpu_buffer_rsrc_t rs = rsrc_rec(g_m1);
-      wpoll = rec_load(rs, lane * kSt + (wave == rp ? 0 : 8));
-      if (TO && wave == rq) wpoll_am = rec_load(rs, lane * kSt + kArgmaxWord * 8);
+      wpoll = rec_load(rs, lane * kSt + (role == 2 ? 0 : 8));
+      if (TO && role == 3) wpoll_am = rec_load(rs, lane * kSt + kArgmaxWord * 8);
     }
     __builtin_amdgcn_sched_barrier(0);
     const int g_p2 = i + 2 < nl ? group_of(i + 2) : g_0;
@@ -545,15 +550,15 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
       }
       __builtin_amdgcn_s_setprio(0);
       __syncthreads();
-      if (wave == wp || wave == wq) __builtin_amdgcn_s_setprio(3);
-      if (wave == wp) {
+      if (role < 2) __builtin_amdgcn_s_setprio(3);
+      if (role == 0) {
         const Lse p = merge_lds<kWaves, true>(part_sh[i & 1][0]);
         if (lane == 0) {
           const __amdgpu_buffer_rsrc_t rs = rsrc_rec(g_0);
           rec_store(rs, c * kSt, pack2(p.ref, mark(p.z)));
           rec_store(rs, c * kSt + 16, pack2(p.y, 1.f));
         }
-      } else if (wave == wq) {
+      } else if (role == 1) {
         const Lse q = merge_lds<kWaves, false>(part_sh[i & 1][1]);
         if (lane == 0) {
           const __amdgpu_buffer_rsrc_t rs = rsrc_rec(g_0);
