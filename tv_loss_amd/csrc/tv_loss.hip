@@ -388,12 +388,17 @@ __global__ __launch_bounds__(kBlock, 2) void tv_pipe_main(TvArgs a) {
 
   auto layer = [&](int i, RawChunk<NV, NR>& rb) __attribute__((always_inline)) {
     const int par = i & 1;
+    // the wave index passes through an empty asm in every layer, so that the tests
+    // on it are made here instead of being hoisted out of the loop as 64-bit masks
+    // that hold scalar registers through it
+    int wv = wave;
+    asm volatile("" : "+s"(wv));
     const bool do2 = i >= 2 && i - 2 < nl;
     // ---- row statistics of position i - 2 (polled a layer ago) ---------------
     if (do2) {
 #pragma unroll
       for (int j = 0; j < RW; ++j) {
-        const int r = wave + j * kWaves;
+        const int r = wv + j * kWaves;
         if (r < NR) {
           __builtin_amdgcn_s_setprio(3);
           const Lse st = poll_row(wpoll[j], rsrc_rec(t_m2), C, kSt, r, a.err, a.wait_limit);
@@ -505,7 +510,7 @@ __global__ __launch_bounds__(kBlock, 2) void tv_pipe_main(TvArgs a) {
       const __amdgpu_buffer_rsrc_t rs = rsrc_rec(t_m1);
 #pragma unroll
       for (int j = 0; j < RW; ++j) {
-        const int r = wave + j * kWaves;
+        const int r = wv + j * kWaves;
         if (r < NR) wpoll[j] = rec_load(rs, lane * kSt + r * 8);
       }
     }
@@ -523,7 +528,7 @@ __global__ __launch_bounds__(kBlock, 2) void tv_pipe_main(TvArgs a) {
       for (int r = 0; r < NR; ++r) z_sh[par][r][tid] = zl[r];
       if (lane == 0) {
 #pragma unroll
-        for (int r = 0; r < NR; ++r) ref_sh[par][r][wave] = xref[r];
+        for (int r = 0; r < NR; ++r) ref_sh[par][r][wv] = xref[r];
       }
       __builtin_amdgcn_s_setprio(0);
     }
@@ -533,7 +538,7 @@ __global__ __launch_bounds__(kBlock, 2) void tv_pipe_main(TvArgs a) {
       const __amdgpu_buffer_rsrc_t rs = rsrc_rec(t_0);
 #pragma unroll
       for (int j = 0; j < RW; ++j) {
-        const int r = wave + j * kWaves;
+        const int r = wv + j * kWaves;
         if (r < NR) {
           // row r over the workgroup: each lane rescales its four waves' sums to the
           // largest reference, then one wave sum
@@ -559,14 +564,14 @@ __global__ __launch_bounds__(kBlock, 2) void tv_pipe_main(TvArgs a) {
       float v[KW];
 #pragma unroll
       for (int j = 0; j < KW; ++j) {
-        const int k = min(wave + j * kWaves, 2 * G - 1);
+        const int k = min(wv + j * kWaves, 2 * G - 1);
         v[j] = (red_sh[k][lane] + red_sh[k][lane + 64]) + (red_sh[k][lane + 128] + red_sh[k][lane + 192]);
       }
       wave_reduce<false, KW>(v);
       if (lane == 0) {
 #pragma unroll
         for (int j = 0; j < KW; ++j) {
-          const int k = wave + j * kWaves;
+          const int k = wv + j * kWaves;
           if (k < 2 * G) a.part2[((int64_t)t_m2 * C + c) * 2 * G + k] = v[j];
         }
       }

@@ -278,8 +278,8 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
     // this wave's role, derived again in every layer (opaque to the compiler), so
     // that the role tests are not hoisted out of the loop as 64-bit masks that
     // would hold scalar registers through it: 0 combines p, 1 q; 2 polls p, 3 q
-    int role = wave ^ wp;
-    asm volatile("" : "+s"(role));
+    int role = wave ^ wp, c_l = c;
+    asm volatile("" : "+s"(role), "+s"(c_l));
     // ---- row statistics of item i - 2 (polled a layer ago) ---------------------
     if (i >= 2 && i - 2 < nl) {
       const bool pair2 = pair_m2;
@@ -374,7 +374,7 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
                           (TO && pair2 && yhat_sh[i & 1] == kNoArgmax);
       if (poison) rm = om = __builtin_nanf("");
       // (om >= 0 or NaN carries the sign bit as a marker: a published word is non-zero)
-      if (lane == 0) put_word(a.part2 + ((int64_t)g_m2 * C + c) * kWaves + wave, pack2(rm, mark(om)));
+      if (lane == 0) put_word(a.part2 + ((int64_t)g_m2 * C + c_l) * kWaves + wave, pack2(rm, mark(om)));
       if constexpr (GM) {
         // Gumbel-max keys of this wave's segment, key = w / E (the exponential race,
         // E the element's exponential variate): w = the residual for a pair row, w = p
@@ -555,20 +555,20 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
         const Lse p = merge_lds<kWaves, true>(part_sh[i & 1][0]);
         if (lane == 0) {
           const __amdgpu_buffer_rsrc_t rs = rsrc_rec(g_0);
-          rec_store(rs, c * kSt, pack2(p.ref, mark(p.z)));
-          rec_store(rs, c * kSt + 16, pack2(p.y, 1.f));
+          rec_store(rs, c_l * kSt, pack2(p.ref, mark(p.z)));
+          rec_store(rs, c_l * kSt + 16, pack2(p.y, 1.f));
         }
       } else if (role == 1) {
         const Lse q = merge_lds<kWaves, false>(part_sh[i & 1][1]);
         if (lane == 0) {
           const __amdgpu_buffer_rsrc_t rs = rsrc_rec(g_0);
-          rec_store(rs, c * kSt + 8, pack2(q.ref, mark(q.z)));
+          rec_store(rs, c_l * kSt + 8, pack2(q.ref, mark(q.z)));
           if (TO && pair) {   // the chunk's argmax over the four waves
             float m = am_sh[i & 1][0];
             uint32_t idx = ai_sh[i & 1][0];
 #pragma unroll
             for (int w = 1; w < kWaves; ++w) argmax_fold(m, idx, am_sh[i & 1][w], ai_sh[i & 1][w]);
-            rec_store(rs, c * kSt + kArgmaxWord * 8, pack_argmax(m, idx));
+            rec_store(rs, c_l * kSt + kArgmaxWord * 8, pack_argmax(m, idx));
           }
         }
       }
