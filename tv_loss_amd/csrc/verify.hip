@@ -770,7 +770,10 @@ __device__ __forceinline__ void finish_row(const VerifyArgs& a, int b, int k, in
   constexpr bool TO = MODE == kVerifyTargetOnly, GM = MODE == kVerifyGumbel;
   constexpr int PV = Elem<DT>::kPerVec;
   constexpr int kSegVec = NV * 64;
-  constexpr int KC = 1;   // chunks per lane whose pass-2 words are kept in registers
+  // chunks per lane whose pass-2 words are kept in registers: one (rows of up to 64
+  // chunks, 262,144 bf16 logits, have no more per lane; a lane's further chunks are
+  // read again from memory), as more registers here spill the finish's live values
+  constexpr int KC = 1;
   const int C = a.sp.nchunks;
   const int G = a.G, G1 = G + 1;
   const int lane = threadIdx.x & 63;
