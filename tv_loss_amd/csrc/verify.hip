@@ -395,11 +395,11 @@ __global__ __launch_bounds__(kBlock, kVerifyBlocksPerCU) void verify_main(Verify
           const float fq = p_units ? fast_exp2(dq - dp) * z_ratio(sp[1], sq[1], sq[2]) : 1.f,
                       fp = p_units ? 1.f : fast_exp2(dp - dq) * z_ratio(sq[1], sp[1], sp[2]);
           lr = p_units ? la : lb;
-          // one 16-byte slot at a time: the Philox rounds would otherwise hold the
-          // registers that the items in flight need
+          // two 16-byte slots at a time: unrolled further, the Philox rounds would
+          // hold the registers that the items in flight need (scratch spills)
           auto keys = [&](auto kind) __attribute__((always_inline)) {
             constexpr int K = decltype(kind)::value;   // 0: p, 1: residual in p's units, 2: in q's
-#pragma unroll 1
+#pragma unroll 2
             for (int qi = 0; qi < NQ; ++qi) {
               const float4 ea = held[0][qi][t];
               const float va[4] = {ea.x, ea.y, ea.z, ea.w};
