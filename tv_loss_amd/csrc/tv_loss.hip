@@ -411,6 +411,10 @@ __global__ __launch_bounds__(kBlock, 2) void tv_pipe_main(TvArgs a) {
         }
       }
       __syncthreads();
+      // pass 2 runs at raised priority (2), then the move and the unpack (1): the
+      // other workgroup on the SIMD then fills the gaps with its own work instead of
+      // delaying this layer's critical steps (pass 1 runs at 1, the record work at 3)
+      __builtin_amdgcn_s_setprio(2);
       // ---- pass 2 of position i - 2: overlap and S partials of every head ----
       // In a wave's units p = sa e_p, q = sb e_q (e <= 1).  Working in q's units with
       // rho = sa / sb, the residual of q over p, r = max(0, e_q - rho e_p) <= e_q <= 1,
@@ -488,6 +492,7 @@ __global__ __launch_bounds__(kBlock, 2) void tv_pipe_main(TvArgs a) {
 #pragma unroll
       for (int k = 0; k < 2 * G; ++k) red_sh[k][tid] = res[k];
     }
+    __builtin_amdgcn_s_setprio(1);
     // ---- position i - 1 moves to LDS (own slots only) --------------------------
     if (i >= 1 && i - 1 < nl) {
 #pragma unroll
@@ -514,6 +519,7 @@ __global__ __launch_bounds__(kBlock, 2) void tv_pipe_main(TvArgs a) {
         if (r < NR) wpoll[j] = rec_load(rs, lane * kSt + r * 8);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
     const int t_p2 = i + 2 < nl ? pos_of(i + 2) : t_0;
     prefetch(rb, t_p2, i + 2 < nl);
