@@ -411,9 +411,9 @@ __global__ __launch_bounds__(kBlock, 2) void tv_pipe_main(TvArgs a) {
         }
       }
       __syncthreads();
-      // pass 2 runs at raised priority (2), then the move and the unpack (1): the
-      // other workgroup on the SIMD then fills the gaps with its own work instead of
-      // delaying this layer's critical steps (pass 1 runs at 1, the record work at 3)
+      // pass 2 runs at raised priority (2), then the move and the unpack (1); pass 1
+      // runs at 1 and the record work at 3 (measured faster than pass 2, the move and
+      // the unpack at the base priority, and than pass 2 at 3 or pass 1 at 2)
       __builtin_amdgcn_s_setprio(2);
       // ---- pass 2 of position i - 2: overlap and S partials of every head ----
       // In a wave's units p = sa e_p, q = sb e_q (e <= 1).  Working in q's units with
