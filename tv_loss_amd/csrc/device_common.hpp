@@ -91,16 +91,14 @@ struct RawChunk {
   u32x4 v[R][NV];
 };
 
-// Only the first `nrows` rows (a wave-uniform count, default R) are loaded.
 template <int DT, int NV, int R>
 __device__ __forceinline__ void issue_rows(RawChunk<NV, R>& raw, const char* const (&rows)[R], int64_t vbeg,
-                                           const RowSplit& sp, int nrows = R) {
+                                           const RowSplit& sp) {
   const int tid = threadIdx.x;
   if (sp.nvec_full > 0) {
     const int64_t last = sp.nvec_full - 1;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      if (r >= nrows) break;
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
         const int64_t vi = min(vbeg + (int64_t)j * kBlock + tid, last);
@@ -118,7 +116,7 @@ __device__ __forceinline__ void issue_rows(RawChunk<NV, R>& raw, const char* con
 template <int DT, int NV, int R>
 __device__ __forceinline__ void unpack_rows(const RawChunk<NV, R>& raw, const char* const (&rows)[R], int64_t vbeg,
                                             int64_t vend, const RowSplit& sp, int64_t V,
-                                            float (&x)[R][NV * Elem<DT>::kPerVec], int nrows = R) {
+                                            float (&x)[R][NV * Elem<DT>::kPerVec]) {
   constexpr int PV = Elem<DT>::kPerVec;
   // a masked word reads as -inf in every element it holds
   constexpr uint32_t kMasked = DT == kBF16 ? 0xFF80FF80u : 0xFF800000u;
@@ -129,7 +127,6 @@ __device__ __forceinline__ void unpack_rows(const RawChunk<NV, R>& raw, const ch
     const bool full = vi < vend && vi < sp.nvec_full;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      if (r >= nrows) break;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const uint32_t word = full ? raw.v[r][j][w] : kMasked;
@@ -150,7 +147,6 @@ __device__ __forceinline__ void unpack_rows(const RawChunk<NV, R>& raw, const ch
       if (vbeg + (int64_t)j * kBlock + tid == tail) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          if (r >= nrows) break;
 #pragma unroll
           for (int e = 0; e < PV; ++e) {
             const int64_t idx = tail * PV + e;
@@ -635,8 +631,7 @@ constexpr int kStreamCpol = 2;
 // may exceed the 2^31 bytes one descriptor spans); a vector clamped below that
 // start gives a negative offset, which the descriptor's bound turns into zeros.
 template <int DT, int NV, int R>
-__device__ __forceinline__ void issue_seg(RawChunk<NV, R>& raw, const char* const (&rows)[R], int v0, int last,
-                                          int nrows = R) {
+__device__ __forceinline__ void issue_seg(RawChunk<NV, R>& raw, const char* const (&rows)[R], int v0, int last) {
   if (last >= 0) {
     const int vb = __builtin_amdgcn_readfirstlane(v0 - (int)(threadIdx.x & 63));
 #pragma unroll
@@ -644,7 +639,6 @@ __device__ __forceinline__ void issue_seg(RawChunk<NV, R>& raw, const char* cons
       const int off = (min(v0 + j * 64, last) - vb) * 16;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        if (r >= nrows) break;
         raw.v[r][j] = __builtin_amdgcn_raw_buffer_load_b128(
             __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(rows[r]) + (int64_t)vb * 16, 0, 0x7fffffff, 0x00020000),
             off, 0, kStreamCpol);
