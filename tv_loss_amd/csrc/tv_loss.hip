@@ -412,8 +412,9 @@ __global__ __launch_bounds__(kBlock, 2) void tv_pipe_main(TvArgs a) {
       }
       __syncthreads();
       // pass 2 runs at raised priority (2), then the move and the unpack (1); pass 1
-      // runs at 1 and the record work at 3 (measured faster than pass 2, the move and
-      // the unpack at the base priority, and than pass 2 at 3 or pass 1 at 2)
+      // runs at the base priority and the record work at 3 (measured faster than
+      // pass 2, the move and the unpack at the base priority, than pass 2 at 3, and
+      // than pass 1 at 1 or 2)
       __builtin_amdgcn_s_setprio(2);
       // ---- pass 2 of position i - 2: overlap and S partials of every head ----
       // In a wave's units p = sa e_p, q = sb e_q (e <= 1).  Working in q's units with
@@ -526,8 +527,7 @@ __global__ __launch_bounds__(kBlock, 2) void tv_pipe_main(TvArgs a) {
     __builtin_amdgcn_sched_barrier(0);
 
     if (i >= 0 && i < nl) {
-      // ---- pass 1 of position i ------------------------------------------------
-      __builtin_amdgcn_s_setprio(1);
+      // ---- pass 1 of position i (base priority) ------------------------------
       float zl[NR];
       lane_pass1<NE, NR>(x, xref, zl, kLog2e);
 #pragma unroll
@@ -536,7 +536,6 @@ __global__ __launch_bounds__(kBlock, 2) void tv_pipe_main(TvArgs a) {
 #pragma unroll
         for (int r = 0; r < NR; ++r) ref_sh[par][r][wv] = xref[r];
       }
-      __builtin_amdgcn_s_setprio(0);
     }
     if ((i >= 0 && i < nl) || do2) __syncthreads();
     if (i >= 0 && i < nl) {
