@@ -1268,8 +1268,15 @@ __global__ __launch_bounds__(kBlock) void gumbel_sample_chunks(const char* logit
       float E[4];
       expo4(seed, crow, (uint32_t)(v * PV / 4 + h), E);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        argmax_fold(km, ki, __builtin_fmaf(x[4 * h + e], L, -fast_log2(E[e])), (uint32_t)(v * PV + 4 * h + e));
+      for (int e = 0; e < 4; ++e) {
+        // the thread visits its elements in increasing index order, so a strict >
+        // keeps the smaller index on equal keys (and a NaN key never wins); a row
+        // whose keys are all -inf yields no token, whatever index is kept
+        const float kv = __builtin_fmaf(x[4 * h + e], L, -fast_log2(E[e]));
+        const bool tk = kv > km;
+        km = tk ? kv : km;
+        ki = tk ? (uint32_t)(v * PV + 4 * h + e) : ki;
+      }
     }
   }
   wave_argmax(km, ki);
