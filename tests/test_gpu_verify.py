@@ -1,7 +1,7 @@
 """GPU parity of mtp_verify against the float64 oracle, on identical seeded inputs.
 
-Sizes: the tiny float32 workload; ragged vocabularies spanning several 8192-element
-chunks with a partial last vector; the full rollout workload (64 x 4 rows of
+Sizes: the tiny float32 workload; ragged vocabularies spanning several chunks (4096
+bfloat16 or 3072 float32 logits each) with a partial last vector; the full rollout workload (64 x 4 rows of
 151936, every row checked); 64 sampled sequences of the long-tail workload (512 x 5
 rows of 262144, the last super-group's included) and 16 of each of the 15
 entropy-sweep cells; edge cases; determinism and
